@@ -1,0 +1,508 @@
+"""STAR-KV decode path, step by step, on the CPU (NumPy, fp64 unless a step fixes
+another precision).  TEST INFRASTRUCTURE ONLY -- see ``oracle/__init__.py``.
+
+Sources (the STAR-KV summary page, "STAR-KV: Low-Rank KV Cache Compression via
+Soft Thresholding for Adaptive Rank Control"):
+
+* Methodology section 1, Adaptive Rank Selection: thresholds act on the singular
+  values of the key and value projections, one threshold per block and head; at
+  inference the thresholds become hard and the projections are truncated.
+  -> :func:`select_rank`, :func:`kept_spectrum`, :func:`factor_pair`.
+* Methodology section 2, Hybrid Decomposition: keys are factored head by head
+  (HD), values jointly over the concatenated heads (JD); the reconstruction
+  matrices are fused by reordering the operations.
+  -> :func:`build_layer`, :func:`reconstruct`, :func:`attention`,
+  :func:`attention_latent`.
+* Methodology section 3, Low-Rank-Aware Mixed-Precision Quantisation: leading
+  (outlier) channels of the latent get more bits than the rest; the abstract adds
+  that the quantiser uses data statistics.
+  -> :func:`channel_qmax`, :func:`calibrate_scales`, :func:`quantize`.
+* Problem Statement: the cache holds the projected hidden states (the latent)
+  instead of K and V.  -> :func:`latent`, the cache byte format.
+
+Readings where the pages are silent (each also listed in the design notes):
+the kept singular values are shrunk by tau (``shrink=True``) or kept as they
+are (``shrink=False``); a channel survives only if ``s > tau`` (strict); the
+singular values live in the down-projection ``A = U diag(s')``, ``B = V^T``; the
+leading ceil(r/4) channels of each latent segment are int8 (qmax 127), the rest
+int4 (qmax 7); quantisation is symmetric with per-channel fp16 scales
+``fp16(fp32(absmax)/qmax)`` from calibration tokens, ``code = clamp(rne(x/s))``
+with an IEEE fp32 division, and a zero scale gives code 0; the latent is the
+fp32 accumulator value; the softmax scale is ``1/sqrt(d_h)``; query ``j`` of a
+chunk of ``n_q`` sees the tokens at positions ``<= T - n_q + j``; query head
+``h`` reads KV head ``h // (H_q/H_kv)``; there is no positional rotation.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import List, Sequence, Tuple
+
+import numpy as np
+
+LOG2E = math.log2(math.e)
+TT = 32  # tokens per value tile in the cache byte format
+
+
+# ---------------------------------------------------------------------------
+# precision helpers (the oracle's own; nothing shared with the GPU side)
+
+def round_bf16(x) -> np.ndarray:
+    """Round float32 values to the nearest bfloat16 (ties to even); float32 out."""
+    u = np.ascontiguousarray(np.asarray(x, dtype=np.float32)).view(np.uint32).astype(np.uint64)
+    keep = u >> 16
+    rem = u & 0xFFFF
+    up = (rem > 0x8000) | ((rem == 0x8000) & ((keep & 1) == 1))
+    r = ((keep + up.astype(np.uint64)) << 16).astype(np.uint32)
+    return r.view(np.float32).reshape(np.shape(x))
+
+
+def round_dtype(x, dtype: str) -> np.ndarray:
+    x32 = np.asarray(x, dtype=np.float32)
+    if dtype == "f32":
+        return x32.copy()
+    if dtype == "bf16":
+        return round_bf16(x32)
+    raise ValueError(dtype)
+
+
+# ---------------------------------------------------------------------------
+# O1: rank selection (Methodology section 1: hard threshold at inference)
+
+def select_rank(s, tau) -> int:
+    """Number of singular values strictly above the threshold, compared in fp32."""
+    s32 = np.asarray(s, dtype=np.float32)
+    return int(np.count_nonzero(s32 > np.float32(tau)))
+
+
+def kept_spectrum(s, tau, shrink: bool = True) -> np.ndarray:
+    """Singular values that the truncated factors carry (fp32).
+
+    shrink=True: the soft threshold ``max(s - tau, 0)`` (one fp32 subtraction);
+    shrink=False: the values themselves (plain truncation).
+    """
+    s32 = np.asarray(s, dtype=np.float32)
+    if not shrink:
+        return s32.copy()
+    return np.maximum(s32 - np.float32(tau), np.float32(0.0)).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# O2: factor build (truncated SVD factors; singular values in the down-projection)
+
+def factor_pair(U, s, V, tau, shrink: bool = True, dtype: str = "f32"):
+    """W = U diag(s) V^T  ->  A (d x r) = U[:, :r] diag(s'[:r]),  B (r x n) = V[:, :r]^T.
+
+    A is one fp32 multiply per element, then rounded to ``dtype``; B is V^T rounded.
+    """
+    r = select_rank(s, tau)
+    sp = kept_spectrum(s, tau, shrink)[:r]
+    U32 = np.asarray(U, dtype=np.float32)[:, :r]
+    A = round_dtype(U32 * sp[None, :], dtype)
+    B = round_dtype(np.asarray(V, dtype=np.float32)[:, :r].T, dtype)
+    return A, B
+
+
+@dataclasses.dataclass
+class Layer:
+    ranks: np.ndarray  # [H_kv] key ranks
+    r_v: int
+    A_cat: np.ndarray  # [d, sum(ranks) + r_v]  (natural channel order: key heads, then value)
+    B_k: np.ndarray  # [sum(ranks), d_h]       (rows of head g at key offset of g)
+    B_v: np.ndarray  # [r_v, H_kv * d_h]
+    H_q: int
+    H_kv: int
+    d_h: int
+    latent: str
+    dtype: str
+
+    @property
+    def key_offsets(self) -> np.ndarray:
+        return np.concatenate([[0], np.cumsum(self.ranks)]).astype(np.int64)
+
+    @property
+    def n_key(self) -> int:
+        return int(np.sum(self.ranks))
+
+    @property
+    def n_lat(self) -> int:
+        return self.n_key + self.r_v
+
+
+def build_layer(U_k, s_k, V_k, tau_k, U_v, s_v, V_v, tau_v, H_q: int, latent: str,
+                dtype: str, shrink: bool = True) -> Layer:
+    """Hybrid decomposition: per-head (HD) key factors, joint (JD) value factors."""
+    H_kv, d, d_h = np.shape(U_k)
+    As, Bs, ranks = [], [], []
+    for g in range(H_kv):
+        A, B = factor_pair(U_k[g], s_k[g], V_k[g], tau_k[g], shrink, dtype)
+        As.append(A)
+        Bs.append(B)
+        ranks.append(A.shape[1])
+    A_v, B_v = factor_pair(U_v, s_v, V_v, tau_v, shrink, dtype)
+    A_cat = np.concatenate(As + [A_v], axis=1)
+    B_k = np.concatenate(Bs, axis=0) if Bs else np.zeros((0, d_h), np.float32)
+    return Layer(np.asarray(ranks, dtype=np.int64), A_v.shape[1], A_cat, B_k, B_v,
+                 H_q, H_kv, d_h, latent, dtype)
+
+
+# ---------------------------------------------------------------------------
+# mixed precision split (Methodology section 3; leading channels get more bits)
+
+def mix84_split(r: int) -> Tuple[int, int]:
+    """(int8 channels, int4 channels) of a latent segment of rank r: the leading
+    ceil(r/4) channels are int8, the rest int4."""
+    n8 = -(-int(r) // 4)
+    return n8, int(r) - n8
+
+
+def channel_qmax(layer: Layer) -> np.ndarray:
+    """qmax per latent channel in natural order (127 for int8, 7 for int4)."""
+    q = []
+    for r in list(layer.ranks) + [layer.r_v]:
+        n8, n4 = mix84_split(int(r))
+        q += [127] * n8 + [7] * n4
+    return np.asarray(q, dtype=np.int64)
+
+
+# ---------------------------------------------------------------------------
+# O3 / O4 / O5: calibration, latent projection, quantisation
+
+def latent(X, A_cat) -> np.ndarray:
+    """The latent the cache stores before rounding: fp32 of the exact product X @ A."""
+    return (np.asarray(X, np.float64) @ np.asarray(A_cat, np.float64)).astype(np.float32)
+
+
+def calibrate_scales(X_cal, A_cat, qmax) -> np.ndarray:
+    """Per-channel fp16 scale from calibration statistics: fp16(fp32(absmax) / qmax)."""
+    L = np.asarray(X_cal, np.float64) @ np.asarray(A_cat, np.float64)
+    amax = np.max(np.abs(L), axis=0).astype(np.float32) if L.shape[0] else np.zeros(L.shape[1], np.float32)
+    return (amax / np.asarray(qmax, dtype=np.float32)).astype(np.float16)
+
+
+def quantize(x32, scales_f16, qmax) -> np.ndarray:
+    """code = clamp(rne(x / s), -qmax, qmax) with an fp32 IEEE division; s == 0 gives 0."""
+    x32 = np.asarray(x32, dtype=np.float32)
+    s32 = np.asarray(scales_f16, dtype=np.float16).astype(np.float32)
+    qm = np.asarray(qmax, dtype=np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        y = x32 / s32
+    c = np.clip(np.rint(y), -qm, qm)
+    c = np.where(s32 == 0, 0.0, c)
+    return c.astype(np.int64)
+
+
+def dequantize(codes, scales_f16) -> np.ndarray:
+    """x_hat = code * s (fp64)."""
+    return np.asarray(codes, np.float64) * np.asarray(scales_f16, dtype=np.float16).astype(np.float64)
+
+
+def stored_latent(x32, latent_kind: str) -> np.ndarray:
+    """Unquantised cache value: the fp32 latent itself or its bf16 rounding (float32 out)."""
+    if latent_kind == "f32":
+        return np.asarray(x32, dtype=np.float32).copy()
+    if latent_kind == "bf16":
+        return round_bf16(x32)
+    raise ValueError(latent_kind)
+
+
+# ---------------------------------------------------------------------------
+# O6: the cache byte format (as the library header documents it)
+
+def _ceil_to(x: int, m: int) -> int:
+    return -(-int(x) // m) * m
+
+
+@dataclasses.dataclass
+class CacheFormat:
+    """Byte layout of one layer's cache.
+
+    mix84 key row (one per token): an int8 region of K8 bytes holding, head after
+    head, the leading ceil(r_g/4) channels of each head's key latent (two's
+    complement), zero-padded to a multiple of 16; then an int4 region of K4/2
+    bytes holding, head after head, the remaining channels, two per byte (the
+    even-indexed one in the low nibble, two's complement nibbles), zero-padded
+    to a multiple of 32 nibbles.
+    mix84 value tile (32 tokens): V8 byte-rows, one per int8 channel (zero-padded
+    to a multiple of 32 rows), then V4/2 byte-rows, one per pair of int4 channels
+    (low nibble = even channel, padded to a multiple of 64 channels); byte t of a
+    row is token t of the tile.
+    f32/bf16: key row = the key latent in channel order, padded to 16 bytes;
+    value tile = r_v (padded to a multiple of 32) element-rows of 32 tokens.
+    """
+
+    latent: str
+    ranks: Tuple[int, ...]
+    r_v: int
+
+    @property
+    def elem(self) -> int:
+        return {"f32": 4, "bf16": 2, "mix84": 1}[self.latent]
+
+    # key side
+    @property
+    def n8(self) -> List[int]:
+        return [mix84_split(r)[0] for r in self.ranks]
+
+    @property
+    def n4(self) -> List[int]:
+        return [mix84_split(r)[1] for r in self.ranks]
+
+    @property
+    def K8(self) -> int:
+        return _ceil_to(sum(self.n8), 16)
+
+    @property
+    def K4(self) -> int:
+        return _ceil_to(sum(self.n4), 32)
+
+    @property
+    def k_row_bytes(self) -> int:
+        if self.latent == "mix84":
+            return self.K8 + self.K4 // 2
+        return _ceil_to(sum(self.ranks) * self.elem, 16)
+
+    # value side
+    @property
+    def V8(self) -> int:
+        return _ceil_to(mix84_split(self.r_v)[0], 32)
+
+    @property
+    def V4(self) -> int:
+        return _ceil_to(mix84_split(self.r_v)[1], 64)
+
+    @property
+    def v_rows(self) -> int:
+        """Rows of a value tile (byte-rows for mix84, element-rows otherwise)."""
+        if self.latent == "mix84":
+            return self.V8 + self.V4 // 2
+        return _ceil_to(self.r_v, 32)
+
+    @property
+    def v_tile_bytes(self) -> int:
+        return self.v_rows * TT * self.elem
+
+
+def pack_key_rows(vals, fmt: CacheFormat) -> np.ndarray:
+    """Key latent rows [T, sum(r)] (codes for mix84, values otherwise) -> bytes [T, k_row_bytes]."""
+    vals = np.asarray(vals)
+    T = vals.shape[0]
+    out = np.zeros((T, fmt.k_row_bytes), dtype=np.uint8)
+    if fmt.latent != "mix84":
+        if fmt.latent == "f32":
+            raw = np.ascontiguousarray(vals, dtype=np.float32).view(np.uint8).reshape(T, -1)
+        else:
+            raw = (round_bf16(vals).view(np.uint32) >> 16).astype(np.uint16).view(np.uint8).reshape(T, -1)
+        out[:, : raw.shape[1]] = raw
+        return out
+    koff = np.concatenate([[0], np.cumsum(fmt.ranks)])
+    o8 = np.concatenate([[0], np.cumsum(fmt.n8)])
+    o4 = np.concatenate([[0], np.cumsum(fmt.n4)])
+    for g, r in enumerate(fmt.ranks):
+        n8, n4 = fmt.n8[g], fmt.n4[g]
+        seg = vals[:, koff[g]: koff[g] + r].astype(np.int64)
+        out[:, o8[g]: o8[g] + n8] = (seg[:, :n8] & 0xFF).astype(np.uint8)
+        for k in range(n4):
+            u = o4[g] + k
+            nib = (seg[:, n8 + k] & 0xF).astype(np.uint8)
+            col = fmt.K8 + u // 2
+            out[:, col] |= nib if u % 2 == 0 else (nib << 4)
+    return out
+
+
+def unpack_key_rows(rows, fmt: CacheFormat) -> np.ndarray:
+    rows = np.asarray(rows, dtype=np.uint8)
+    T = rows.shape[0]
+    nk = sum(fmt.ranks)
+    if fmt.latent == "f32":
+        return rows[:, : nk * 4].copy().view(np.float32).reshape(T, nk)
+    if fmt.latent == "bf16":
+        b = rows[:, : nk * 2].copy().view(np.uint16).reshape(T, nk)
+        return (b.astype(np.uint32) << 16).view(np.float32)
+    out = np.zeros((T, nk), dtype=np.int64)
+    koff = np.concatenate([[0], np.cumsum(fmt.ranks)])
+    o8 = np.concatenate([[0], np.cumsum(fmt.n8)])
+    o4 = np.concatenate([[0], np.cumsum(fmt.n4)])
+    for g, r in enumerate(fmt.ranks):
+        n8, n4 = fmt.n8[g], fmt.n4[g]
+        out[:, koff[g]: koff[g] + n8] = rows[:, o8[g]: o8[g] + n8].view(np.int8)
+        for k in range(n4):
+            u = o4[g] + k
+            byte = rows[:, fmt.K8 + u // 2].astype(np.int64)
+            nib = (byte >> (4 * (u % 2))) & 0xF
+            out[:, koff[g] + n8 + k] = np.where(nib >= 8, nib - 16, nib)
+    return out
+
+
+def pack_value_tiles(vals, fmt: CacheFormat, n_tiles: int) -> np.ndarray:
+    """Value latent [T, r_v] -> tiles [n_tiles, v_rows, 32 * elem] (tokens >= T are zero)."""
+    vals = np.asarray(vals)
+    T = vals.shape[0]
+    out = np.zeros((n_tiles, fmt.v_rows, TT * fmt.elem), dtype=np.uint8)
+    if fmt.latent != "mix84":
+        if fmt.latent == "f32":
+            ev = np.zeros((n_tiles * TT, fmt.v_rows), dtype=np.float32)
+            ev[:T, : fmt.r_v] = vals
+            raw = ev.reshape(n_tiles, TT, fmt.v_rows).transpose(0, 2, 1).copy().view(np.uint8)
+        else:
+            ev = np.zeros((n_tiles * TT, fmt.v_rows), dtype=np.uint16)
+            ev[:T, : fmt.r_v] = (round_bf16(vals).view(np.uint32) >> 16).astype(np.uint16)
+            raw = ev.reshape(n_tiles, TT, fmt.v_rows).transpose(0, 2, 1).copy().view(np.uint8)
+        return raw.reshape(n_tiles, fmt.v_rows, TT * fmt.elem)
+    n8, n4 = mix84_split(fmt.r_v)
+    c = np.zeros((n_tiles * TT, fmt.r_v), dtype=np.int64)
+    c[:T] = vals
+    byrow = np.zeros((n_tiles * TT, fmt.v_rows), dtype=np.uint8)
+    byrow[:, :n8] = (c[:, :n8] & 0xFF).astype(np.uint8)
+    for k in range(n4):
+        nib = (c[:, n8 + k] & 0xF).astype(np.uint8)
+        byrow[:, fmt.V8 + k // 2] |= nib if k % 2 == 0 else (nib << 4)
+    return byrow.reshape(n_tiles, TT, fmt.v_rows).transpose(0, 2, 1).copy()
+
+
+def unpack_value_tiles(tiles, fmt: CacheFormat, T: int) -> np.ndarray:
+    tiles = np.asarray(tiles, dtype=np.uint8)
+    n_tiles = tiles.shape[0]
+    if fmt.latent == "f32":
+        v = tiles.copy().view(np.float32).reshape(n_tiles, fmt.v_rows, TT)
+        return v.transpose(0, 2, 1).reshape(n_tiles * TT, fmt.v_rows)[:T, : fmt.r_v].copy()
+    if fmt.latent == "bf16":
+        v = tiles.copy().view(np.uint16).reshape(n_tiles, fmt.v_rows, TT)
+        v = v.transpose(0, 2, 1).reshape(n_tiles * TT, fmt.v_rows)[:T, : fmt.r_v]
+        return (v.astype(np.uint32) << 16).view(np.float32)
+    n8, n4 = mix84_split(fmt.r_v)
+    by = tiles.transpose(0, 2, 1).reshape(n_tiles * TT, fmt.v_rows)[:T]
+    out = np.zeros((T, fmt.r_v), dtype=np.int64)
+    out[:, :n8] = by[:, :n8].view(np.int8)
+    for k in range(n4):
+        nib = (by[:, fmt.V8 + k // 2].astype(np.int64) >> (4 * (k % 2))) & 0xF
+        out[:, n8 + k] = np.where(nib >= 8, nib - 16, nib)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# O7: reconstruct dense K and V from the (dequantised) latent
+
+def reconstruct(xk_hat, xv_hat, layer: Layer) -> Tuple[np.ndarray, np.ndarray]:
+    """K_g = L_g B_g (head-wise), V = C_v B_v (joint) -> both [T, H_kv, d_h] fp64."""
+    xk_hat = np.asarray(xk_hat, np.float64)
+    T = xk_hat.shape[0]
+    K = np.zeros((T, layer.H_kv, layer.d_h))
+    off = layer.key_offsets
+    Bk = np.asarray(layer.B_k, np.float64)
+    for g in range(layer.H_kv):
+        K[:, g, :] = xk_hat[:, off[g]: off[g + 1]] @ Bk[off[g]: off[g + 1]]
+    V = (np.asarray(xv_hat, np.float64) @ np.asarray(layer.B_v, np.float64)).reshape(T, layer.H_kv, layer.d_h)
+    return K, V
+
+
+# ---------------------------------------------------------------------------
+# O8: dense attention of the decode queries over the reconstructed cache
+
+def attention(q, K, V, n_q: int) -> np.ndarray:
+    """q [n_q, H_q, d_h]; K, V [T, H_kv, d_h]; causal over the last n_q positions.
+
+    Query j sits at position T - n_q + j and sees positions <= that; query head h
+    reads KV head h // (H_q / H_kv); scores are scaled by 1/sqrt(d_h).
+    """
+    q = np.asarray(q, np.float64)
+    T, H_kv, d_h = K.shape
+    H_q = q.shape[1]
+    G = H_q // H_kv
+    out = np.zeros((n_q, H_q, d_h))
+    for j in range(n_q):
+        pos = T - n_q + j
+        for h in range(H_q):
+            g = h // G
+            s = (K[: pos + 1, g, :] @ q[j, h]) / math.sqrt(d_h)
+            p = np.exp(s - np.max(s))
+            out[j, h] = (p @ V[: pos + 1, g, :]) / np.sum(p)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# O9: the same attention computed in the latent space (operations reordered)
+
+def attention_latent(q, xk_hat, xv_hat, layer: Layer, n_q: int) -> np.ndarray:
+    """q is projected into each key head's latent (q B_g^T), scored against the latent
+    keys; the probabilities weight the joint value latent, which is then up-projected
+    per head with the head's slice of B_v."""
+    q = np.asarray(q, np.float64)
+    xk_hat = np.asarray(xk_hat, np.float64)
+    xv_hat = np.asarray(xv_hat, np.float64)
+    T = xk_hat.shape[0]
+    G = layer.H_q // layer.H_kv
+    off = layer.key_offsets
+    Bk = np.asarray(layer.B_k, np.float64)
+    Bv = np.asarray(layer.B_v, np.float64)
+    d_h = layer.d_h
+    out = np.zeros((n_q, layer.H_q, d_h))
+    for j in range(n_q):
+        pos = T - n_q + j
+        for h in range(layer.H_q):
+            g = h // G
+            qt = Bk[off[g]: off[g + 1]] @ q[j, h]
+            s = (xk_hat[: pos + 1, off[g]: off[g + 1]] @ qt) / math.sqrt(d_h)
+            p = np.exp(s - np.max(s))
+            z = p @ xv_hat[: pos + 1]
+            out[j, h] = (z @ Bv[:, g * d_h: (g + 1) * d_h]) / np.sum(p)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# split-K over the context: partial softmax states and their log-sum-exp merge
+
+def partial_state(s, values) -> Tuple[float, float, np.ndarray]:
+    """(max, sum of exp(s - max), sum of exp(s - max) * values) over one token range."""
+    s = np.asarray(s, np.float64)
+    m = float(np.max(s))
+    e = np.exp(s - m)
+    return m, float(np.sum(e)), e @ np.asarray(values, np.float64)
+
+
+def lse_merge(parts: Sequence[Tuple[float, float, np.ndarray]]) -> np.ndarray:
+    """Merge partial states: m = max m_i, l = sum e^(m_i - m) l_i, acc likewise; -> acc / l."""
+    m = max(p[0] for p in parts)
+    l = sum(math.exp(p[0] - m) * p[1] for p in parts)
+    acc = sum(math.exp(p[0] - m) * p[2] for p in parts)
+    return acc / l
+
+
+# ---------------------------------------------------------------------------
+# the whole path for one sequence
+
+@dataclasses.dataclass
+class SequenceCache:
+    """The oracle's cache of one sequence: integer codes (mix84) or stored values."""
+
+    key: np.ndarray  # [T, sum(r)]
+    value: np.ndarray  # [T, r_v]
+
+
+def compress(X, layer: Layer, scales=None) -> SequenceCache:
+    """Project hidden states X [T, d] into the latent and quantise / round it."""
+    x = latent(X, layer.A_cat)
+    nk = layer.n_key
+    if layer.latent == "mix84":
+        codes = quantize(x, scales, channel_qmax(layer))
+        return SequenceCache(codes[:, :nk], codes[:, nk:])
+    v = stored_latent(x, layer.latent)
+    return SequenceCache(v[:, :nk], v[:, nk:])
+
+
+def dequantized(cache: SequenceCache, layer: Layer, scales=None) -> Tuple[np.ndarray, np.ndarray]:
+    nk = layer.n_key
+    if layer.latent == "mix84":
+        s = np.asarray(scales, dtype=np.float16)
+        return dequantize(cache.key, s[:nk]), dequantize(cache.value, s[nk:])
+    return np.asarray(cache.key, np.float64), np.asarray(cache.value, np.float64)
+
+
+def decode(q, cache: SequenceCache, layer: Layer, n_q: int, scales=None, mode: str = "reconstruct") -> np.ndarray:
+    """Decode attention of one sequence; ``mode`` = "reconstruct" (O7 + O8) or "latent" (O9)."""
+    xk, xv = dequantized(cache, layer, scales)
+    if mode == "latent":
+        return attention_latent(q, xk, xv, layer, n_q)
+    K, V = reconstruct(xk, xv, layer)
+    return attention(q, K, V, n_q)
