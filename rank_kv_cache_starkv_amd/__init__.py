@@ -1,0 +1,282 @@
+"""Python binding of libstarkv: decode attention over a low-rank, mixed-precision KV cache.
+
+Argument marshalling only.  Every step of the path runs in libstarkv's HIP kernels;
+PyTorch provides device memory and the stream.  There is no CPU fallback: if the
+library is not built, :func:`lib` raises.
+
+Typical use (one layer)::
+
+    layer = Layer(H_q, H_kv, d_h, d, "bf16", "mix84", s_k, tau_k, s_v, tau_v)
+    layer.build_factors(U_k, V_k, U_v, V_v)      # fp32 SVD factors on the device
+    layer.calibrate(X_cal)                       # per-channel fp16 scales (mix84)
+    cache = layer.new_cache(B, T_max)
+    layer.append(cache, X_new, lens)             # project + quantise new tokens
+    out = layer.decode(cache, q, lens)           # attention read from the latent
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libstarkv.so")
+
+F32, BF16 = 0, 1
+LATENT = {"f32": 0, "bf16": 1, "mix84": 2}
+DTYPE = {"f32": F32, "bf16": BF16}
+TILE_TOKENS = 32
+MAX_BATCH = 128
+
+STATUS = {0: "ok", -1: "EINVAL", -2: "ENOMEM", -3: "ECAPACITY", -4: "EUNSUPPORTED", -5: "EWORKSPACE",
+          -6: "EHIP", -7: "ESTATE"}
+
+
+class StarKVError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {STATUS.get(status, status)} ({status})")
+        self.status = status
+
+
+class _Desc(ctypes.Structure):
+    _fields_ = [("H_q", ctypes.c_int), ("H_kv", ctypes.c_int), ("d_h", ctypes.c_int), ("d", ctypes.c_int),
+                ("dtype", ctypes.c_int), ("latent", ctypes.c_int), ("shrink", ctypes.c_int), ("n_v", ctypes.c_int),
+                ("s_k", ctypes.POINTER(ctypes.c_float)), ("tau_k", ctypes.POINTER(ctypes.c_float)),
+                ("s_v", ctypes.POINTER(ctypes.c_float)), ("tau_v", ctypes.c_float)]
+
+
+class _Info(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in ("H_q", "H_kv", "d_h", "d", "dtype", "latent", "n_key", "r_v", "n_lat",
+                                            "k_row_bytes", "v_tile_rows", "v_tile_bytes", "K8", "K4", "V8", "V4")] + \
+               [(n, ctypes.c_size_t) for n in ("a_bytes", "bk_bytes", "bv_bytes", "scale_bytes")]
+
+
+class _Cache(ctypes.Structure):
+    _fields_ = [("k_rows", ctypes.c_void_p), ("v_tiles", ctypes.c_void_p), ("B", ctypes.c_int),
+                ("T_max", ctypes.c_int)]
+
+
+EXPORTS = ["starkv_abi_version", "starkv_status_string", "starkv_layer_create", "starkv_layer_destroy",
+           "starkv_layer_get_info", "starkv_layer_ranks", "starkv_build_factors", "starkv_bind_factors",
+           "starkv_calibrate", "starkv_bind_scales", "starkv_cache_bytes", "starkv_compress_append",
+           "starkv_decode_workspace_bytes", "starkv_decode_attention", "starkv_reconstruct"]
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libstarkv (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"libstarkv is not built ({LIB_PATH} missing); run __graft_entry__.build()")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, ci, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    L.starkv_abi_version.restype = ci
+    L.starkv_status_string.restype = ctypes.c_char_p
+    L.starkv_status_string.argtypes = [ci]
+    L.starkv_layer_create.argtypes = [ctypes.POINTER(_Desc), ctypes.POINTER(vp)]
+    L.starkv_layer_destroy.argtypes = [vp]
+    L.starkv_layer_get_info.argtypes = [vp, ctypes.POINTER(_Info)]
+    L.starkv_layer_ranks.argtypes = [vp, ctypes.POINTER(ctypes.c_int32)]
+    L.starkv_build_factors.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.starkv_bind_factors.argtypes = [vp, vp, vp, vp]
+    L.starkv_calibrate.argtypes = [vp, vp, ci, vp, vp]
+    L.starkv_bind_scales.argtypes = [vp, vp]
+    L.starkv_cache_bytes.argtypes = [vp, ci, ci, ctypes.POINTER(sz), ctypes.POINTER(sz)]
+    L.starkv_compress_append.argtypes = [vp, ctypes.POINTER(_Cache), vp, ci, ci, ctypes.POINTER(ctypes.c_int32), vp]
+    L.starkv_decode_workspace_bytes.argtypes = [vp, ci, ci, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(sz)]
+    L.starkv_decode_attention.argtypes = [vp, ctypes.POINTER(_Cache), vp, ci, ci, ctypes.POINTER(ctypes.c_int32),
+                                          vp, vp, sz, vp]
+    L.starkv_reconstruct.argtypes = [vp, ctypes.POINTER(_Cache), ci, ci, ci, vp, vp, vp]
+    for name in EXPORTS:
+        if name not in ("starkv_abi_version", "starkv_status_string"):
+            getattr(L, name).restype = ci
+    _lib = L
+    return L
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise StarKVError(status, what)
+
+
+def _f32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float32))
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def _ptr(t) -> int:
+    return int(t.data_ptr())
+
+
+def _stream(stream=None) -> int:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+class Cache:
+    """Caller-owned cache buffers of one layer (torch uint8 tensors on the device)."""
+
+    def __init__(self, k_rows, v_tiles, B: int, T_max: int):
+        self.k_rows = k_rows
+        self.v_tiles = v_tiles
+        self.B = B
+        self.T_max = T_max
+
+    def struct(self) -> _Cache:
+        return _Cache(_ptr(self.k_rows), _ptr(self.v_tiles), self.B, self.T_max)
+
+    def seq(self, b: int) -> "Cache":
+        """A one-sequence view of sequence b (same memory)."""
+        kb = self.k_rows.numel() // self.B
+        vb = self.v_tiles.numel() // self.B
+        return Cache(self.k_rows[b * kb:(b + 1) * kb], self.v_tiles[b * vb:(b + 1) * vb], 1, self.T_max)
+
+
+class Layer:
+    """One decoder layer's low-rank, quantised KV cache path (a libstarkv layer handle)."""
+
+    def __init__(self, H_q: int, H_kv: int, d_h: int, d: int, dtype: str, latent: str, s_k, tau_k, s_v, tau_v,
+                 shrink: bool = True, device: Optional[str] = None):
+        self._lib = lib()
+        self.dtype = dtype
+        self.latent = latent
+        self._s_k = _f32(s_k).reshape(H_kv, d_h)
+        self._tau_k = _f32(tau_k).reshape(H_kv)
+        self._s_v = _f32(s_v).reshape(-1)
+        desc = _Desc(H_q, H_kv, d_h, d, DTYPE[dtype], LATENT[latent], 1 if shrink else 0, len(self._s_v),
+                     self._s_k.ctypes.data_as(ctypes.POINTER(ctypes.c_float)),
+                     self._tau_k.ctypes.data_as(ctypes.POINTER(ctypes.c_float)),
+                     self._s_v.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), float(np.float32(tau_v)))
+        h = ctypes.c_void_p()
+        _check(self._lib.starkv_layer_create(ctypes.byref(desc), ctypes.byref(h)), "starkv_layer_create")
+        self._h = h
+        info = _Info()
+        _check(self._lib.starkv_layer_get_info(h, ctypes.byref(info)), "starkv_layer_get_info")
+        self.info = {f: getattr(info, f) for f, _ in _Info._fields_}
+        r = np.zeros(H_kv + 1, dtype=np.int32)
+        _check(self._lib.starkv_layer_ranks(h, r.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))), "starkv_layer_ranks")
+        self.ranks = r[:H_kv].copy()
+        self.r_v = int(r[H_kv])
+        self.H_q, self.H_kv, self.d_h, self.d = H_q, H_kv, d_h, d
+        self.A_t = self.B_k = self.B_vt = self.scales = None
+        self._ws = None
+
+    # -- lifecycle
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None and self._h.value:
+            self._lib.starkv_layer_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def torch_dtype(self):
+        import torch
+        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+
+    # -- factors and scales
+    def build_factors(self, U_k, V_k, U_v, V_v, stream=None):
+        """Truncated factors from fp32 device SVD factors; returns (A_t, B_k, B_vt)."""
+        import torch
+        dev = U_k.device
+        n_lat, n_key = self.info["n_lat"], self.info["n_key"]
+        self.A_t = torch.empty((n_lat, self.d), dtype=self.torch_dtype, device=dev)
+        self.B_k = torch.empty((n_key, self.d_h), dtype=self.torch_dtype, device=dev)
+        self.B_vt = torch.empty((self.H_kv * self.d_h, self.r_v), dtype=self.torch_dtype, device=dev)
+        for t in (U_k, V_k, U_v, V_v):
+            assert t.dtype == torch.float32 and t.is_contiguous() and t.is_cuda
+        _check(self._lib.starkv_build_factors(self._h, _ptr(U_k), _ptr(V_k), _ptr(U_v), _ptr(V_v), _ptr(self.A_t),
+                                              _ptr(self.B_k), _ptr(self.B_vt), _stream(stream)), "starkv_build_factors")
+        return self.A_t, self.B_k, self.B_vt
+
+    def bind_factors(self, A_t, B_k, B_vt) -> None:
+        self.A_t, self.B_k, self.B_vt = A_t, B_k, B_vt
+        _check(self._lib.starkv_bind_factors(self._h, _ptr(A_t), _ptr(B_k), _ptr(B_vt)), "starkv_bind_factors")
+
+    def calibrate(self, X_cal, stream=None):
+        """Per-channel fp16 scales from calibration hidden states [n_cal, d] (mix84)."""
+        import torch
+        assert X_cal.dtype == self.torch_dtype and X_cal.is_contiguous()
+        self.scales = torch.empty((self.info["n_lat"],), dtype=torch.float16, device=X_cal.device)
+        _check(self._lib.starkv_calibrate(self._h, _ptr(X_cal), int(X_cal.shape[0]), _ptr(self.scales),
+                                          _stream(stream)), "starkv_calibrate")
+        return self.scales
+
+    def bind_scales(self, scales) -> None:
+        self.scales = scales
+        _check(self._lib.starkv_bind_scales(self._h, _ptr(scales)), "starkv_bind_scales")
+
+    # -- cache
+    def cache_bytes(self, B: int, T_max: int) -> Tuple[int, int]:
+        kb, vb = ctypes.c_size_t(), ctypes.c_size_t()
+        _check(self._lib.starkv_cache_bytes(self._h, B, T_max, ctypes.byref(kb), ctypes.byref(vb)), "starkv_cache_bytes")
+        return kb.value, vb.value
+
+    def new_cache(self, B: int, T_max: int, device="cuda", zero: bool = False) -> Cache:
+        import torch
+        T_max = -(-T_max // TILE_TOKENS) * TILE_TOKENS
+        kb, vb = self.cache_bytes(B, T_max)
+        mk = torch.zeros if zero else torch.empty
+        return Cache(mk((kb,), dtype=torch.uint8, device=device), mk((vb,), dtype=torch.uint8, device=device), B, T_max)
+
+    def append(self, cache: Cache, X_new, lens: Sequence[int], stream=None) -> None:
+        """Project X_new [B, n_new, d] into the latent and store it after position lens[b]."""
+        assert X_new.dtype == self.torch_dtype and X_new.is_contiguous() and X_new.dim() == 3
+        B, n_new = int(X_new.shape[0]), int(X_new.shape[1])
+        L = _i32(lens)
+        cs = cache.struct()
+        _check(self._lib.starkv_compress_append(self._h, ctypes.byref(cs), _ptr(X_new), B, n_new,
+                                                L.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), _stream(stream)),
+               "starkv_compress_append")
+
+    # -- decode
+    def workspace_bytes(self, B: int, n_q: int, lens: Sequence[int]) -> int:
+        L = _i32(lens)
+        n = ctypes.c_size_t()
+        _check(self._lib.starkv_decode_workspace_bytes(self._h, B, n_q, L.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                                       ctypes.byref(n)), "starkv_decode_workspace_bytes")
+        return n.value
+
+    def decode(self, cache: Cache, q, lens: Sequence[int], out=None, ws=None, stream=None):
+        """Attention of q [B, n_q, H_q, d_h] over the cache (lens include the n_q query tokens)."""
+        import torch
+        assert q.dtype == self.torch_dtype and q.is_contiguous() and q.dim() == 4
+        B, n_q = int(q.shape[0]), int(q.shape[1])
+        L = _i32(lens)
+        need = self.workspace_bytes(B, n_q, L)
+        if ws is None:
+            if self._ws is None or self._ws.numel() < need:
+                self._ws = torch.empty((max(need, 256),), dtype=torch.uint8, device=q.device)
+            ws = self._ws
+        if out is None:
+            out = torch.empty_like(q)
+        cs = cache.struct()
+        _check(self._lib.starkv_decode_attention(self._h, ctypes.byref(cs), _ptr(q), B, n_q,
+                                                 L.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), _ptr(out), _ptr(ws),
+                                                 int(ws.numel() * ws.element_size()), _stream(stream)),
+               "starkv_decode_attention")
+        return out
+
+    def reconstruct(self, cache: Cache, b: int, t0: int, t1: int, stream=None):
+        """Dense K, V [t1 - t0, H_kv, d_h] rebuilt from the latent of sequence b."""
+        import torch
+        K = torch.empty((t1 - t0, self.H_kv, self.d_h), dtype=self.torch_dtype, device=cache.k_rows.device)
+        V = torch.empty_like(K)
+        cs = cache.struct()
+        _check(self._lib.starkv_reconstruct(self._h, ctypes.byref(cs), b, t0, t1, _ptr(K), _ptr(V), _stream(stream)),
+               "starkv_reconstruct")
+        return K, V

@@ -1,0 +1,218 @@
+// Latent projection of hidden states (x = X A, fp32 accumulation on MFMA) with two epilogues:
+//   append    -- quantise / round and store the new tokens into the cache
+//                (STAR-KV summary page, Problem Statement: the cache holds the projected
+//                hidden states; Methodology section 3: leading channels int8, the rest int4)
+//   calibrate -- per-channel absmax of the calibration latent, then the fp16 scales
+//                (abstract: the quantiser uses data statistics)
+//
+// GEMM shape: rows = tokens, columns = cache slots (the key-row slots then the value slots,
+// in cache order, so that the two nibbles of an int4 byte are adjacent columns), K = d.
+// Workgroup tile 64 x 64, four waves of 32 x 32 (v_mfma_f32_32x32x16_bf16, or 32x32x2_f32).
+#include "device_common.h"
+#include "starkv_internal.h"
+
+namespace skv {
+
+struct GemmArgs {
+  const void* X;        // [M][d]
+  const void* A_t;      // [n_lat][d]
+  const int* slot_chan; // [NS]
+  int M, d, NS;
+  int key_slots, K8, V8;
+  int latent;
+  // append
+  int n_new, T_max, k_row_bytes, v_rows;
+  uint8_t* k_rows;
+  uint8_t* v_tiles;
+  const uint16_t* scales;
+  int lens[kMaxB];
+  // calibrate
+  uint32_t* absmax;
+};
+
+template <int DT>
+__device__ __forceinline__ void load_frag8(const void* base, size_t elem_off, bool ok, u32x4& lo, u32x4& hi) {
+  // 8 consecutive elements: bf16 -> lo holds all 8; f32 -> lo elements 0..3, hi 4..7
+  if (!ok) {
+    lo = u32x4{0, 0, 0, 0};
+    hi = lo;
+    return;
+  }
+  if (DT == STARKV_BF16) {
+    lo = ld16((const uint16_t*)base + elem_off);
+    hi = u32x4{0, 0, 0, 0};
+  } else {
+    const float* p = (const float*)base + elem_off;
+    lo = ld16(p);
+    hi = ld16(p + 4);
+  }
+}
+
+template <int DT, int MODE>
+__global__ __launch_bounds__(256) void k_latent_gemm(GemmArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const int wm = wave & 1, wn = wave >> 1;
+  const int m0 = blockIdx.x * 64 + wm * 32;
+  const int s0 = blockIdx.y * 64 + wn * 32;
+  const int r = lane & 31, q = lane >> 5;
+
+  const int arow = m0 + r;
+  const bool a_ok = arow < a.M;
+  const int bslot = s0 + r;
+  const int bchan = (bslot < a.NS) ? a.slot_chan[bslot] : -1;
+  const bool b_ok = bchan >= 0;
+  const size_t a_base = (size_t)(a_ok ? arow : 0) * a.d;
+  const size_t b_base = (size_t)(b_ok ? bchan : 0) * a.d;
+
+  f32x16 acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+
+  for (int k0 = 0; k0 < a.d; k0 += 16) {
+    u32x4 alo, ahi, blo, bhi;
+    load_frag8<DT>(a.X, a_base + k0 + 8 * q, a_ok, alo, ahi);
+    load_frag8<DT>(a.A_t, b_base + k0 + 8 * q, b_ok, blo, bhi);
+    if (DT == STARKV_BF16) {
+      acc = mfma32_bf16(as_bf16x8(alo), as_bf16x8(blo), acc);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc = mfma32_f32(__uint_as_float(alo[e]), __uint_as_float(blo[e]), acc);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc = mfma32_f32(__uint_as_float(ahi[e]), __uint_as_float(bhi[e]), acc);
+    }
+  }
+
+  // result: lane holds column n = r (slot s0 + r), rows d32_row(v, q)
+  const int slot = s0 + r;
+  const int chan = (slot < a.NS) ? a.slot_chan[slot] : -1;
+
+  if (MODE == 1) {
+    // calibrate: absmax of this column over the 32 rows (rows >= M hold 0)
+    float m = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) m = fmaxf(m, fabsf(acc[v]));
+    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    if (q == 0 && chan >= 0) atomicMax(a.absmax + chan, __float_as_uint(m));
+    return;
+  }
+
+  const bool is_key = slot < a.key_slots;
+  if (a.latent == STARKV_LATENT_MIX84) {
+    int qmax;
+    if (is_key) qmax = slot < a.K8 ? 127 : 7;
+    else qmax = (slot - a.key_slots) < a.V8 ? 127 : 7;
+    const float sc = chan >= 0 ? f16_to_f32(a.scales[chan]) : 0.f;
+    const bool nib = qmax == 7;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int m = m0 + d32_row(v, q);
+      int code = 0;
+      if (sc != 0.f) {
+        const float y = acc[v] / sc;  // IEEE fp32 division
+        float rq = __builtin_rintf(y);
+        rq = fminf(fmaxf(rq, -(float)qmax), (float)qmax);
+        code = (int)rq;
+      }
+      const int partner = __shfl_xor(code, 1, 64);
+      if (m >= a.M || slot >= a.NS) continue;
+      const int b = m / a.n_new, i = m - b * a.n_new;
+      const int pos = a.lens[b] + i;
+      if (is_key) {
+        uint8_t* row = a.k_rows + ((size_t)b * a.T_max + pos) * a.k_row_bytes;
+        if (!nib) row[slot] = (uint8_t)(code & 0xFF);
+        else if ((slot & 1) == 0) row[a.K8 + (slot - a.K8) / 2] = (uint8_t)((code & 0xF) | ((partner & 0xF) << 4));
+      } else {
+        const int u = slot - a.key_slots;
+        uint8_t* tile = a.v_tiles + ((size_t)b * (a.T_max / kTT) + pos / kTT) * a.v_rows * kTT;
+        if (!nib) tile[(size_t)u * kTT + pos % kTT] = (uint8_t)(code & 0xFF);
+        else if ((u & 1) == 0)
+          tile[(size_t)(a.V8 + (u - a.V8) / 2) * kTT + pos % kTT] = (uint8_t)((code & 0xF) | ((partner & 0xF) << 4));
+      }
+    }
+    return;
+  }
+
+  // unquantised latent: fp32 or bf16 elements
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int m = m0 + d32_row(v, q);
+    if (m >= a.M || slot >= a.NS) continue;
+    const int b = m / a.n_new, i = m - b * a.n_new;
+    const int pos = a.lens[b] + i;
+    const float x = acc[v];
+    if (is_key) {
+      uint8_t* row = a.k_rows + ((size_t)b * a.T_max + pos) * a.k_row_bytes;
+      if (a.latent == STARKV_LATENT_F32) ((float*)row)[slot] = x;
+      else ((uint16_t*)row)[slot] = f32_to_bf16(x);
+    } else {
+      const int u = slot - a.key_slots;
+      uint8_t* tile = a.v_tiles + ((size_t)b * (a.T_max / kTT) + pos / kTT) * a.v_rows * kTT * (a.latent == STARKV_LATENT_F32 ? 4 : 2);
+      if (a.latent == STARKV_LATENT_F32) ((float*)tile)[(size_t)u * kTT + pos % kTT] = x;
+      else ((uint16_t*)tile)[(size_t)u * kTT + pos % kTT] = f32_to_bf16(x);
+    }
+  }
+}
+
+__global__ void k_fill_u32(uint32_t* p, int n, uint32_t v) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+__global__ __launch_bounds__(256) void k_finish_scales(const uint32_t* __restrict__ absmax, const int* __restrict__ src,
+                                                       const int* __restrict__ n8, int n8v, int H_kv, int n_lat,
+                                                       uint16_t* __restrict__ scales) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= n_lat) return;
+  const int s = src[c];
+  const int g = s >> 16, k = s & 0xFFFF;
+  const bool is8 = (g < H_kv) ? (k < n8[g]) : (k < n8v);
+  const float q = is8 ? 127.f : 7.f;
+  scales[c] = f32_to_f16(__uint_as_float(absmax[c]) / q);
+}
+
+static void fill_common(const Layer& L, GemmArgs& a, const void* X, int M) {
+  a.X = X;
+  a.A_t = L.A_t;
+  a.slot_chan = L.d_slot_chan;
+  a.M = M;
+  a.d = L.d;
+  a.NS = L.key_slots + L.val_slots;
+  a.key_slots = L.key_slots;
+  a.K8 = L.K8;
+  a.V8 = L.V8;
+  a.latent = L.latent;
+}
+
+hipError_t launch_calibrate(const Layer& L, const void* X_cal, int n_cal, uint16_t* scales_out, hipStream_t s) {
+  hipLaunchKernelGGL(k_fill_u32, dim3((L.n_lat + 255) / 256), dim3(256), 0, s, L.d_absmax, L.n_lat, 0u);
+  GemmArgs a = {};
+  fill_common(L, a, X_cal, n_cal);
+  a.absmax = L.d_absmax;
+  dim3 grid((n_cal + 63) / 64, (a.NS + 63) / 64);
+  if (L.dtype == STARKV_BF16) hipLaunchKernelGGL((k_latent_gemm<STARKV_BF16, 1>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((k_latent_gemm<STARKV_F32, 1>), grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_finish_scales, dim3((L.n_lat + 255) / 256), dim3(256), 0, s, (const uint32_t*)L.d_absmax,
+                     (const int*)L.d_src, (const int*)L.d_n8, L.n8v, L.H_kv, L.n_lat, scales_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_append(const Layer& L, const starkv_cache& c, const void* X_new, int B, int n_new,
+                         const int32_t* lens, hipStream_t s) {
+  GemmArgs a = {};
+  fill_common(L, a, X_new, B * n_new);
+  a.n_new = n_new;
+  a.T_max = c.T_max;
+  a.k_row_bytes = L.k_row_bytes;
+  a.v_rows = L.v_rows;
+  a.k_rows = (uint8_t*)c.k_rows;
+  a.v_tiles = (uint8_t*)c.v_tiles;
+  a.scales = L.scales;
+  for (int b = 0; b < B; ++b) a.lens[b] = lens[b];
+  dim3 grid((B * n_new + 63) / 64, (a.NS + 63) / 64);
+  if (L.dtype == STARKV_BF16) hipLaunchKernelGGL((k_latent_gemm<STARKV_BF16, 0>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((k_latent_gemm<STARKV_F32, 0>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace skv

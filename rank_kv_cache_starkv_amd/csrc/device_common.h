@@ -1,0 +1,97 @@
+// Device-side helpers shared by the libstarkv kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define SKV_LOG2E 1.4426950408889634f
+
+namespace skv {
+
+// ---- scalar conversions (all round-to-nearest-even) ----
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
+__device__ __forceinline__ float f16_to_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+__device__ __forceinline__ uint16_t f32_to_f16(float x) { return __builtin_bit_cast(uint16_t, (_Float16)x); }
+
+// ---- wave helpers ----
+// Wave index within the workgroup, provably uniform to the compiler: branches on values
+// derived from it become scalar branches.  This matters around MFMA instructions, which
+// do not honour EXEC: an MFMA left in an exec-masked (linearised) branch still executes.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+__device__ __forceinline__ float wave_max_xor(float v, int mask) { return fmaxf(v, __shfl_xor(v, mask, 64)); }
+__device__ __forceinline__ float wave_sum_xor(float v, int mask) { return v + __shfl_xor(v, mask, 64); }
+
+// ---- 16-byte loads/stores ----
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ __forceinline__ u32x2 ld8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
+__device__ __forceinline__ void st8(void* p, u32x2 v) { *reinterpret_cast<u32x2*>(p) = v; }
+
+// signed nibble / byte extraction
+__device__ __forceinline__ int sbyte(uint32_t w, int i) { return (int)(w << (24 - 8 * i)) >> 24; }
+__device__ __forceinline__ int snib(uint32_t w, int i) { return (int)(w << (28 - 4 * i)) >> 28; }
+
+// int4 group of 16 channels (8 bytes, channel 2k in the low nibble of byte k) -> 16 int8 in the
+// order [0,2,4,...,14, 1,3,...,15] as offset binary (code + 8); see the key-score bias term.
+__device__ __forceinline__ i32x4 unpack_int4_group(u32x2 w) {
+  uint32_t a = w[0] ^ 0x88888888u, b = w[1] ^ 0x88888888u;
+  i32x4 r;
+  r[0] = (int)(a & 0x0F0F0F0Fu);
+  r[1] = (int)(b & 0x0F0F0F0Fu);
+  r[2] = (int)((a >> 4) & 0x0F0F0F0Fu);
+  r[3] = (int)((b >> 4) & 0x0F0F0F0Fu);
+  return r;
+}
+
+// position within a 16-slot int4 group of fragment element e (see unpack_int4_group)
+__device__ __forceinline__ int int4_perm16(int e) { return e < 8 ? 2 * e : 2 * (e - 8) + 1; }
+
+// ---- MFMA wrappers ----
+__device__ __forceinline__ f32x4 mfma16_f16(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32_f16(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ i32x4 mfma16_i8(i32x4 a, i32x4 b, i32x4 c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32_f32(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
+
+// Row of a 32x32 MFMA result held in register v of a lane in half q (= lane / 32).
+__device__ __forceinline__ int d32_row(int v, int q) { return 8 * (v >> 2) + 4 * q + (v & 3); }
+
+// binary search: largest b in [0, n) with off[b] <= x  (off ascending, off[0] == 0)
+__device__ __forceinline__ int find_segment(const int* off, int n, int x) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (off[mid] <= x) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+}  // namespace skv

@@ -1,0 +1,218 @@
+// Layer setup: rank selection, cache layout, device tables, and the factor-build kernels.
+//
+// STAR-KV summary page, Methodology section 1 (thresholds on the singular values,
+// hard at inference, projections truncated) and section 2 (keys head by head,
+// values jointly); section 3 for the leading-channel split of the latent.
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "device_common.h"
+#include "starkv_internal.h"
+
+namespace skv {
+
+static int ceil_to(int x, int m) { return (x + m - 1) / m * m; }
+
+int layer_init(const starkv_layer_desc& d, Layer* L) {
+  L->H_q = d.H_q;
+  L->H_kv = d.H_kv;
+  L->d_h = d.d_h;
+  L->d = d.d;
+  L->dtype = d.dtype;
+  L->latent = d.latent;
+  L->shrink = d.shrink;
+  L->n_v = d.n_v;
+  L->G = d.H_q / d.H_kv;
+  // rank selection: strict comparison in fp32; kept values shrunk by tau (or not)
+  L->rk.assign(d.H_kv, 0);
+  L->sp_k.assign((size_t)d.H_kv * d.d_h, 0.f);
+  for (int g = 0; g < d.H_kv; ++g) {
+    const float tau = d.tau_k[g];
+    int r = 0;
+    for (int i = 0; i < d.d_h; ++i) {
+      const float s = d.s_k[(size_t)g * d.d_h + i];
+      if (s > tau) ++r;
+      L->sp_k[(size_t)g * d.d_h + i] = d.shrink ? std::max(s - tau, 0.0f) : s;
+    }
+    L->rk[g] = r;
+  }
+  int rv = 0;
+  L->sp_v.assign(d.n_v, 0.f);
+  for (int i = 0; i < d.n_v; ++i) {
+    if (d.s_v[i] > d.tau_v) ++rv;
+    L->sp_v[i] = d.shrink ? std::max(d.s_v[i] - d.tau_v, 0.0f) : d.s_v[i];
+  }
+  L->r_v = rv;
+  L->n_key = 0;
+  L->koff.assign(d.H_kv + 1, 0);
+  for (int g = 0; g < d.H_kv; ++g) {
+    L->koff[g + 1] = L->koff[g] + L->rk[g];
+  }
+  L->n_key = L->koff[d.H_kv];
+  L->n_lat = L->n_key + L->r_v;
+  if (L->n_key == 0 || L->r_v == 0) return STARKV_EUNSUPPORTED;
+
+  // cache layout
+  L->n8.assign(d.H_kv, 0);
+  L->n4.assign(d.H_kv, 0);
+  L->off8.assign(d.H_kv + 1, 0);
+  L->off4.assign(d.H_kv + 1, 0);
+  if (L->mix()) {
+    for (int g = 0; g < d.H_kv; ++g) {
+      L->n8[g] = (L->rk[g] + 3) / 4;
+      L->n4[g] = L->rk[g] - L->n8[g];
+      L->off8[g + 1] = L->off8[g] + L->n8[g];
+      L->off4[g + 1] = L->off4[g] + L->n4[g];
+    }
+    L->K8 = ceil_to(L->off8[d.H_kv], 16);
+    L->K4 = ceil_to(L->off4[d.H_kv], 32);
+    L->k_row_bytes = L->K8 + L->K4 / 2;
+    L->n8v = (L->r_v + 3) / 4;
+    L->n4v = L->r_v - L->n8v;
+    L->V8 = ceil_to(L->n8v, 32);
+    L->V4 = ceil_to(L->n4v, 64);
+    L->v_rows = L->V8 + L->V4 / 2;
+    L->elem = 1;
+    L->key_slots = L->K8 + L->K4;
+    L->val_slots = L->V8 + L->V4;
+    L->key_kt = 64;
+    L->key_kpos = L->K8 + L->K4;
+  } else {
+    L->elem = (L->latent == STARKV_LATENT_F32) ? 4 : 2;
+    L->k_row_bytes = ceil_to(L->n_key * L->elem, 16);
+    L->key_slots = L->k_row_bytes / L->elem;
+    L->v_rows = ceil_to(L->r_v, 32);
+    L->val_slots = L->v_rows;
+    L->key_kt = 32;
+    L->key_kpos = L->key_slots;
+  }
+  L->v_tile_bytes = L->v_rows * kTT * L->elem;
+  return STARKV_OK;
+}
+
+int layer_upload_tables(Layer* L) {
+  const int NS = L->key_slots + L->val_slots;
+  std::vector<int> slot_chan(NS, -1);
+  if (L->mix()) {
+    for (int g = 0; g < L->H_kv; ++g) {
+      for (int k = 0; k < L->n8[g]; ++k) slot_chan[L->off8[g] + k] = L->koff[g] + k;
+      for (int k = 0; k < L->n4[g]; ++k) slot_chan[L->K8 + L->off4[g] + k] = L->koff[g] + L->n8[g] + k;
+    }
+    for (int k = 0; k < L->n8v; ++k) slot_chan[L->key_slots + k] = L->n_key + k;
+    for (int k = 0; k < L->n4v; ++k) slot_chan[L->key_slots + L->V8 + k] = L->n_key + L->n8v + k;
+  } else {
+    for (int c = 0; c < L->n_key; ++c) slot_chan[c] = c;
+    for (int k = 0; k < L->r_v; ++k) slot_chan[L->key_slots + k] = L->n_key + k;
+  }
+  std::vector<float> sp(L->n_lat);
+  std::vector<int> src(L->n_lat);
+  for (int g = 0; g < L->H_kv; ++g)
+    for (int k = 0; k < L->rk[g]; ++k) {
+      sp[L->koff[g] + k] = L->sp_k[(size_t)g * L->d_h + k];
+      src[L->koff[g] + k] = (g << 16) | k;
+    }
+  for (int k = 0; k < L->r_v; ++k) {
+    sp[L->n_key + k] = L->sp_v[k];
+    src[L->n_key + k] = (L->H_kv << 16) | k;
+  }
+  const int H = L->H_kv;
+  // one allocation: slot_chan | koff(H+1) | n8(H) | off8(H+1) | off4(H+1) | sp | src | absmax
+  size_t n_int = (size_t)NS + (H + 1) + H + (H + 1) + (H + 1);
+  size_t bytes = n_int * 4 + (size_t)L->n_lat * 4 * 3;
+  std::vector<uint8_t> host(bytes, 0);
+  size_t o = 0;
+  auto put = [&](const void* p, size_t nb) { memcpy(host.data() + o, p, nb); o += nb; };
+  put(slot_chan.data(), NS * 4);
+  put(L->koff.data(), (H + 1) * 4);
+  put(L->n8.data(), H * 4);
+  put(L->off8.data(), (H + 1) * 4);
+  put(L->off4.data(), (H + 1) * 4);
+  put(sp.data(), L->n_lat * 4);
+  put(src.data(), L->n_lat * 4);
+  void* dev = nullptr;
+  if (hipMalloc(&dev, bytes) != hipSuccess) return STARKV_ENOMEM;
+  if (hipMemcpy(dev, host.data(), bytes, hipMemcpyHostToDevice) != hipSuccess) {
+    (void)hipFree(dev);
+    return STARKV_EHIP;
+  }
+  L->dev_tables = dev;
+  uint8_t* b = (uint8_t*)dev;
+  o = 0;
+  L->d_slot_chan = (int*)(b + o); o += NS * 4;
+  L->d_koff = (int*)(b + o); o += (H + 1) * 4;
+  L->d_n8 = (int*)(b + o); o += H * 4;
+  L->d_off8 = (int*)(b + o); o += (H + 1) * 4;
+  L->d_off4 = (int*)(b + o); o += (H + 1) * 4;
+  L->d_sp = (float*)(b + o); o += L->n_lat * 4;
+  L->d_src = (int*)(b + o); o += L->n_lat * 4;
+  L->d_absmax = (uint32_t*)(b + o);
+  return STARKV_OK;
+}
+
+// ---------------------------------------------------------------------------
+// factor build: A^T[c][i] = rne(U[i][k] * s'[c]), B_k[c][e] = rne(V_g[e][k]), B_v^T[j][k] = rne(V_v[j][k])
+
+template <typename T>
+__device__ __forceinline__ void store_dt(T* p, size_t i, float x);
+template <>
+__device__ __forceinline__ void store_dt<float>(float* p, size_t i, float x) { p[i] = x; }
+template <>
+__device__ __forceinline__ void store_dt<uint16_t>(uint16_t* p, size_t i, float x) { p[i] = f32_to_bf16(x); }
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_build_a(const float* __restrict__ U_k, const float* __restrict__ U_v,
+                                                 const float* __restrict__ sp, const int* __restrict__ src,
+                                                 T* __restrict__ A_t, int d, int d_h, int n_v, int H_kv) {
+  const int c = blockIdx.y;
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= d) return;
+  const int s = src[c];
+  const int g = s >> 16, k = s & 0xFFFF;
+  const float u = (g < H_kv) ? U_k[((size_t)g * d + i) * d_h + k] : U_v[(size_t)i * n_v + k];
+  store_dt<T>(A_t, (size_t)c * d + i, __fmul_rn(u, sp[c]));
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_build_bk(const float* __restrict__ V_k, const int* __restrict__ src,
+                                                  T* __restrict__ B_k, int n_key, int d_h) {
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= n_key * d_h) return;
+  const int c = idx / d_h, e = idx % d_h;
+  const int s = src[c];
+  const int g = s >> 16, k = s & 0xFFFF;
+  store_dt<T>(B_k, idx, V_k[((size_t)g * d_h + e) * d_h + k]);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_build_bv(const float* __restrict__ V_v, T* __restrict__ B_vt, int rows,
+                                                  int r_v, int n_v) {
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (size_t)rows * r_v) return;
+  const size_t j = idx / r_v, k = idx % r_v;
+  store_dt<T>(B_vt, idx, V_v[j * n_v + k]);
+}
+
+template <typename T>
+static hipError_t build_factors_t(const Layer& L, const float* U_k, const float* V_k, const float* U_v,
+                                  const float* V_v, void* A_t, void* B_k, void* B_vt, hipStream_t s) {
+  dim3 ga((L.d + 255) / 256, L.n_lat);
+  hipLaunchKernelGGL(k_build_a<T>, ga, dim3(256), 0, s, U_k, U_v, L.d_sp, L.d_src, (T*)A_t, L.d, L.d_h, L.n_v,
+                     L.H_kv);
+  const int nbk = L.n_key * L.d_h;
+  hipLaunchKernelGGL(k_build_bk<T>, dim3((nbk + 255) / 256), dim3(256), 0, s, V_k, L.d_src, (T*)B_k, L.n_key,
+                     L.d_h);
+  const size_t nbv = (size_t)L.H_kv * L.d_h * L.r_v;
+  hipLaunchKernelGGL(k_build_bv<T>, dim3((unsigned)((nbv + 255) / 256)), dim3(256), 0, s, V_v, (T*)B_vt,
+                     L.H_kv * L.d_h, L.r_v, L.n_v);
+  return hipGetLastError();
+}
+
+hipError_t launch_build_factors(const Layer& L, const float* U_k, const float* V_k, const float* U_v,
+                                const float* V_v, void* A_t, void* B_k, void* B_vt, hipStream_t s) {
+  if (L.dtype == STARKV_F32) return build_factors_t<float>(L, U_k, V_k, U_v, V_v, A_t, B_k, B_vt, s);
+  return build_factors_t<uint16_t>(L, U_k, V_k, U_v, V_v, A_t, B_k, B_vt, s);
+}
+
+}  // namespace skv

@@ -1,0 +1,125 @@
+// Host-side state of a libstarkv layer and the launch descriptors of its kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <vector>
+
+#include "../../include/starkv.h"
+
+namespace skv {
+
+constexpr int kTT = STARKV_TILE_TOKENS;  // tokens per value tile
+constexpr int kTC = 64;                  // tokens per score chunk
+constexpr int kMaxB = STARKV_MAX_BATCH;
+constexpr int kMaxCT = STARKV_MAX_QROWS / 16;  // 16-row column tiles of the key-score GEMM
+constexpr int kMaxKT = 48;                     // K-tiles per column tile
+constexpr int kMaxSplitsPerSeq = 64;
+
+// Per-KV-head tables on the device (int32 each, H_kv entries unless noted).
+struct HeadTables {
+  const int* koff;   // [H_kv + 1] first natural key channel of head g
+  const int* n8;     // mix84: int8 channels of head g
+  const int* off8;   // mix84: first int8 slot of head g
+  const int* off4;   // mix84: first int4 slot of head g (relative to K8)
+};
+
+struct Layer {
+  // description
+  int H_q = 0, H_kv = 0, d_h = 0, d = 0, dtype = 0, latent = 0, shrink = 1, n_v = 0;
+  int G = 1;
+  std::vector<int> rk;      // key ranks
+  int r_v = 0;
+  std::vector<float> sp_k;  // [H_kv][d_h] kept singular values (s' or s)
+  std::vector<float> sp_v;  // [n_v]
+  // layout
+  int n_key = 0, n_lat = 0;
+  std::vector<int> koff, n8, n4, off8, off4;
+  int K8 = 0, K4 = 0, V8 = 0, V4 = 0, n8v = 0, n4v = 0;
+  int elem = 1;             // bytes per cache element (1 for mix84 codes)
+  int k_row_bytes = 0, v_rows = 0, v_tile_bytes = 0;
+  int key_slots = 0, val_slots = 0;  // columns of the append GEMM
+  int key_kt = 0;           // K-positions per key-score K-tile (64 for int8 MFMA, 32 otherwise)
+  int key_kpos = 0;         // key K-positions (slots) of the key row
+  // device tables (owned)
+  void* dev_tables = nullptr;
+  int* d_slot_chan = nullptr;  // [key_slots + val_slots] natural channel of each GEMM column or -1
+  int* d_koff = nullptr;
+  int* d_n8 = nullptr;
+  int* d_off8 = nullptr;
+  int* d_off4 = nullptr;
+  float* d_sp = nullptr;       // [n_lat] kept singular value of each natural channel
+  int* d_src = nullptr;        // [n_lat] (head << 16) | local index; head = H_kv for values
+  uint32_t* d_absmax = nullptr;  // [n_lat] calibration scratch
+  // bound buffers (borrowed)
+  const void* A_t = nullptr;
+  const void* B_k = nullptr;
+  const void* B_vt = nullptr;
+  const uint16_t* scales = nullptr;
+
+  HeadTables heads() const { return HeadTables{d_koff, d_n8, d_off8, d_off4}; }
+  bool mix() const { return latent == STARKV_LATENT_MIX84; }
+};
+
+// ---------------------------------------------------------------------------
+// decode plan (host-built per call, passed by value to the kernels)
+
+struct DecodeGeom {
+  int B, n_q, M_q, M_pad, nct, G, d_h, H_q, H_kv;
+  int n_key, r_v, K8, K4, key_kt, key_kpos, k_row_bytes, v_rows, v_tile_bytes, T_max;
+  int latent, dtype;
+  float qscale;  // log2(e) / sqrt(d_h)
+};
+
+struct KtList {
+  uint8_t n[kMaxCT];
+  uint8_t kt[kMaxCT][kMaxKT];
+};
+
+struct SeqTable {
+  int lens[kMaxB];
+  int chunk_off[kMaxB + 1];
+  int split_off[kMaxB + 1];
+};
+
+struct DecodeWs {
+  // all device pointers into the caller's workspace
+  void* qfrag;      // [B][nct][kMaxKT? -> nkt_max][2048 bytes]
+  float* rowp;      // [B][M_pad][4]  (rho, bias_hi, bias_lo, 0)
+  void* p;          // [total_chunks][M_pad][kTC] probabilities (f16 / bf16 / f32)
+  float* cm;        // [total_chunks][M_pad] chunk max (log2 units)
+  float* cl;        // [total_chunks][M_pad] chunk sum
+  float* zp;        // [total_splits][M_pad][r_v] value-latent partials
+  float* sm;        // [total_splits][M_pad] split max
+  float* sl;        // [total_splits][M_pad] split sum
+  int nkt_max;
+  int total_chunks, total_splits;
+  int cps;          // score chunks per value split
+  int blocks_per_wg;  // value blocks (waves) per value WG
+};
+
+struct DecodePlan {
+  DecodeGeom g;
+  DecodeWs ws;
+  size_t ws_bytes;
+};
+
+int plan_decode(const Layer& L, int B, int n_q, const int32_t* lens, int T_max, void* ws_base, DecodePlan* plan,
+                KtList* kts, SeqTable* seq);
+
+hipError_t launch_decode(const Layer& L, const DecodePlan& plan, const KtList& kts, const SeqTable& seq,
+                         const void* q, void* out, const void* k_rows, const void* v_tiles, hipStream_t s);
+
+hipError_t launch_build_factors(const Layer& L, const float* U_k, const float* V_k, const float* U_v,
+                                const float* V_v, void* A_t, void* B_k, void* B_vt, hipStream_t s);
+
+hipError_t launch_calibrate(const Layer& L, const void* X_cal, int n_cal, uint16_t* scales_out, hipStream_t s);
+
+hipError_t launch_append(const Layer& L, const starkv_cache& c, const void* X_new, int B, int n_new,
+                         const int32_t* lens, hipStream_t s);
+
+hipError_t launch_reconstruct(const Layer& L, const starkv_cache& c, int b, int t0, int t1, void* K_out,
+                              void* V_out, hipStream_t s);
+
+}  // namespace skv

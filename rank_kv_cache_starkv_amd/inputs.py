@@ -256,6 +256,15 @@ def x_prefill(w: Workload, b: int, t0: int, t1: int, layer: int = 0) -> np.ndarr
     return gaussian(rng, (t1 - t0, w.d))
 
 
+def x_prefill_chunks(w: Workload, b: int, T: int, chunk: int, layer: int = 0):
+    """Yield (t0, t1, X[t0:t1]) over tokens [0, T) of sequence ``b`` from one stream
+    (the same values :func:`x_prefill` gives for any range)."""
+    rng = rng_for(w.cfg_id, layer, "x_prefill", b)
+    for t0 in range(0, T, chunk):
+        t1 = min(T, t0 + chunk)
+        yield t0, t1, gaussian(rng, (t1 - t0, w.d))
+
+
 def x_calibration(w: Workload, layer: int = 0) -> np.ndarray:
     return gaussian(rng_for(w.cfg_id, layer, "x_cal"), (w.n_cal, w.d))
 

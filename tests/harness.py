@@ -1,0 +1,205 @@
+"""Shared setup of parity runs: the same seeded inputs go to libstarkv (GPU) and to the
+CPU oracle; nothing computed on the GPU is ever fed to the oracle.
+
+A run builds one layer on both sides, fills the cache by compress_append (prefill, then
+the workload's own append step), and decodes.  ``exact=True`` applies the exact-latent
+conditioning (A snapped per channel to 8 significant bits, X to multiples of 1/16), under
+which every fp32 partial sum of X A is exact in any order, so latents, scales and codes
+must agree bit for bit.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import sys
+import time
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+import torch
+
+import rank_kv_cache_starkv_amd as S
+from oracle import starkv_oracle as O
+from rank_kv_cache_starkv_amd import inputs as I
+
+DEV = "cuda:0"
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(x: np.ndarray, dtype: str) -> torch.Tensor:
+    """float32 host values (already representable in dtype) -> device tensor of dtype."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if dtype == "f32":
+        return torch.from_numpy(x).to(DEV)
+    bits = I.to_bf16_bits(x)
+    return torch.from_numpy(bits.view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def from_dev(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
+
+
+def dev_bits(t: torch.Tensor) -> np.ndarray:
+    if t.dtype == torch.float32:
+        return t.detach().cpu().numpy().view(np.uint32)
+    if t.dtype in (torch.bfloat16, torch.float16):
+        return t.detach().cpu().view(torch.int16).numpy().view(np.uint16)
+    raise TypeError(t.dtype)
+
+
+def f32_bits(x: np.ndarray, dtype: str) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    return x.view(np.uint32) if dtype == "f32" else (x.view(np.uint32) >> 16).astype(np.uint16)
+
+
+@dataclasses.dataclass
+class Run:
+    w: I.Workload
+    lf: I.LayerFactors
+    OL: O.Layer
+    GL: S.Layer
+    exact: bool
+    scales_o: Optional[np.ndarray] = None  # oracle scales (float16)
+    cache: Optional[S.Cache] = None
+    lens0: Optional[np.ndarray] = None
+    lens: Optional[np.ndarray] = None
+    oracle_seqs: Sequence[int] = ()
+    ocache: Dict[int, O.SequenceCache] = dataclasses.field(default_factory=dict)
+    fmt: Optional[O.CacheFormat] = None
+
+
+def make_layer(w: I.Workload, exact: bool = False, layer: int = 0) -> Run:
+    lf = I.layer_factors(w, layer)
+    OL = O.build_layer(lf.U_k, lf.s_k, lf.V_k, lf.tau_k, lf.U_v, lf.s_v, lf.V_v, lf.tau_v, w.H_q, w.latent, w.dtype)
+    GL = S.Layer(w.H_q, w.H_kv, w.d_h, w.d, w.dtype, w.latent, lf.s_k, lf.tau_k, lf.s_v, lf.tau_v)
+    dev = [torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV) for a in (lf.U_k, lf.V_k, lf.U_v, lf.V_v)]
+    GL.build_factors(*dev)
+    torch.cuda.synchronize()
+    run = Run(w, lf, OL, GL, exact)
+    run.fmt = O.CacheFormat(w.latent, tuple(int(r) for r in OL.ranks), OL.r_v)
+    if exact:
+        At = I.snap_columns(OL.A_cat.T)
+        OL.A_cat = np.ascontiguousarray(At.T)
+        GL.A_t.copy_(to_dev(At, w.dtype))
+    return run
+
+
+def calibrate(run: Run) -> None:
+    w = run.w
+    if w.latent != "mix84":
+        return
+    Xc = I.x_calibration(w)
+    Xc = I.snap_hidden(Xc) if run.exact else I.as_dtype(Xc, w.dtype)
+    run.GL.calibrate(to_dev(Xc, w.dtype))
+    run.scales_o = O.calibrate_scales(Xc, run.OL.A_cat, O.channel_qmax(run.OL))
+    torch.cuda.synchronize()
+
+
+def hidden(run: Run, X: np.ndarray) -> np.ndarray:
+    return I.snap_hidden(X) if run.exact else I.as_dtype(X, run.w.dtype)
+
+
+def prefill(run: Run, lens0: Sequence[int], oracle_seqs: Sequence[int], T_max: Optional[int] = None,
+            chunk: int = 2048, fast_fill: bool = False) -> None:
+    """Fill sequence b with lens0[b] prefill tokens.  Sequences outside ``oracle_seqs`` may be
+    filled from torch's GPU generator (``fast_fill``): nothing checks their contents."""
+    w = run.w
+    lens0 = np.asarray(lens0, dtype=np.int32)
+    B = len(lens0)
+    T_max = T_max or int(lens0.max()) + max(w.n_append, 1)
+    run.cache = run.GL.new_cache(B, T_max)
+    run.lens0 = lens0
+    run.oracle_seqs = list(oracle_seqs)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(1234)
+    for b in range(B):
+        view = run.cache.seq(b)
+        Xs = []
+        if b in run.oracle_seqs or not fast_fill:
+            for t0, t1, X in I.x_prefill_chunks(w, b, int(lens0[b]), chunk):
+                X = hidden(run, X)
+                if b in run.oracle_seqs:
+                    Xs.append(X)
+                run.GL.append(view, to_dev(X, w.dtype)[None].contiguous(), [t0])
+        else:
+            for t0 in range(0, int(lens0[b]), chunk):
+                t1 = min(int(lens0[b]), t0 + chunk)
+                Xd = torch.randn((t1 - t0, w.d), generator=gen, device=DEV, dtype=torch.float32)
+                if run.exact:
+                    Xd = torch.clamp(torch.round(Xd * 16), -255, 255) / 16
+                Xd = Xd.to(run.GL.torch_dtype)
+                run.GL.append(view, Xd[None].contiguous(), [t0])
+        if b in run.oracle_seqs:
+            Xall = np.concatenate(Xs, axis=0) if Xs else np.zeros((0, w.d), np.float32)
+            run.ocache[b] = O.compress(Xall, run.OL, run.scales_o)
+    torch.cuda.synchronize()
+    run.lens = lens0.copy()
+
+
+def append_step(run: Run, n_new: int, step: int = 0) -> np.ndarray:
+    """The workload's own append: n_new tokens for every sequence at its current length."""
+    w = run.w
+    B = len(run.lens)
+    Xn = hidden(run, I.x_new(dataclasses.replace(w, B=B), n_new, step=step))
+    run.GL.append(run.cache, to_dev(Xn, w.dtype), run.lens)
+    for b in run.oracle_seqs:
+        oc = O.compress(Xn[b], run.OL, run.scales_o)
+        old = run.ocache[b]
+        run.ocache[b] = O.SequenceCache(np.concatenate([old.key, oc.key]), np.concatenate([old.value, oc.value]))
+    run.lens = run.lens + n_new
+    torch.cuda.synchronize()
+    return Xn
+
+
+def gpu_seq_cache(run: Run, b: int):
+    """(key rows bytes [len, k_row_bytes], value tiles bytes [n_tiles, rows, 32*elem]) of sequence b."""
+    fmt = run.fmt
+    T = int(run.lens[b])
+    kb = run.cache.k_rows.numel() // run.cache.B
+    vb = run.cache.v_tiles.numel() // run.cache.B
+    k = run.cache.k_rows[b * kb:(b + 1) * kb].view(run.cache.T_max, fmt.k_row_bytes)[:T].cpu().numpy()
+    nt = -(-T // O.TT)
+    v = run.cache.v_tiles[b * vb:(b + 1) * vb].view(run.cache.T_max // O.TT, fmt.v_rows, O.TT * fmt.elem)[:nt]
+    return k, v.cpu().numpy()
+
+
+def oracle_seq_bytes(run: Run, b: int):
+    fmt = run.fmt
+    oc = run.ocache[b]
+    T = oc.key.shape[0]
+    return O.pack_key_rows(oc.key, fmt), O.pack_value_tiles(oc.value, fmt, -(-T // O.TT))
+
+
+def queries(run: Run, scale: float = 1.0, step: int = 0) -> np.ndarray:
+    w = run.w
+    q = I.queries(dataclasses.replace(w, B=len(run.lens)), step=step, scale=scale)
+    return I.as_dtype(q, w.dtype)
+
+
+def decode(run: Run, q: np.ndarray) -> torch.Tensor:
+    out = run.GL.decode(run.cache, to_dev(q, run.w.dtype), run.lens)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_decode(run: Run, q: np.ndarray, b: int, mode: str = "reconstruct") -> np.ndarray:
+    return O.decode(q[b].astype(np.float64), run.ocache[b], run.OL, run.w.n_q, run.scales_o, mode=mode)
+
+
+def check_output(w: I.Workload, got: np.ndarray, ref: np.ndarray, what: str) -> float:
+    """f32 workloads: max |err| <= 1e-4; bf16 workloads: max |err| / max |ref| <= 2e-2."""
+    err = float(np.max(np.abs(got - ref)))
+    if w.dtype == "f32":
+        log(f"  {what}: max|err| = {err:.3e} (bound 1e-4)")
+        assert err <= 1e-4, (what, err)
+        return err
+    rel = err / float(np.max(np.abs(ref)))
+    big = np.abs(ref) > 0.1 * np.max(np.abs(ref))
+    elem = float(np.max(np.abs(got - ref)[big] / np.abs(ref)[big])) if big.any() else 0.0
+    log(f"  {what}: normwise rel = {rel:.3e} (bound 2e-2), max|err| = {err:.3e}, elementwise rel (|ref|>10% max) = {elem:.3e}")
+    assert rel <= 2e-2, (what, rel)
+    return rel

@@ -1,0 +1,154 @@
+"""Host-side checks of libstarkv (no GPU needed): exports, rank selection, layout,
+argument validation and workspace sizing, called through the C ABI."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import rank_kv_cache_starkv_amd as S
+from oracle import starkv_oracle as O
+from rank_kv_cache_starkv_amd import inputs as I
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "starkv.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(starkv_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    assert os.path.exists(S.LIB_PATH), "build libstarkv first (__graft_entry__.build())"
+    out = subprocess.run(["nm", "-D", "--defined-only", S.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\b(starkv_\w+)\b", out))
+    decl = declared_functions()
+    assert len(decl) >= 15
+    missing = [f for f in decl if f not in exported]
+    assert not missing, missing
+    assert sorted(decl) == sorted(S.EXPORTS)
+    L = S.lib()
+    for f in decl:
+        assert hasattr(L, f)
+
+
+def test_abi_version_and_status_strings():
+    L = S.lib()
+    assert L.starkv_abi_version() == 1
+    for st in (0, -1, -2, -3, -4, -5, -6, -7):
+        assert L.starkv_status_string(st).decode() not in ("", "unknown status")
+    assert L.starkv_status_string(-99).decode() == "unknown status"
+
+
+def _layer(cfg, **kw):
+    w = I.WORKLOADS[cfg]
+    s_k, tau_k, s_v, tau_v, ranks = I.layer_spectra(w)
+    args = dict(H_q=w.H_q, H_kv=w.H_kv, d_h=w.d_h, d=w.d, dtype=w.dtype, latent=w.latent, s_k=s_k, tau_k=tau_k,
+                s_v=s_v, tau_v=tau_v)
+    args.update(kw)
+    return w, S.Layer(**args), ranks
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
+def test_ranks_and_layout_match_oracle(cfg):
+    w, layer, ranks = _layer(cfg)
+    s_k, tau_k, s_v, tau_v, _ = I.layer_spectra(w)
+    exp = [O.select_rank(s_k[g], tau_k[g]) for g in range(w.H_kv)]
+    assert list(layer.ranks) == exp == list(ranks)
+    assert layer.r_v == O.select_rank(s_v, tau_v) == w.r_v
+    fmt = O.CacheFormat(w.latent, tuple(exp), layer.r_v)
+    inf = layer.info
+    assert inf["k_row_bytes"] == fmt.k_row_bytes
+    assert inf["v_tile_rows"] == fmt.v_rows
+    assert inf["v_tile_bytes"] == fmt.v_tile_bytes
+    assert inf["n_key"] == sum(exp) and inf["n_lat"] == sum(exp) + w.r_v
+    if w.latent == "mix84":
+        assert (inf["K8"], inf["K4"], inf["V8"], inf["V4"]) == (fmt.K8, fmt.K4, fmt.V8, fmt.V4)
+    kb, vb = layer.cache_bytes(w.B, 4096)
+    assert kb == w.B * 4096 * fmt.k_row_bytes and vb == w.B * 128 * fmt.v_tile_bytes
+    layer.close()
+
+
+def test_shrink_flag_and_tie():
+    # hard truncation keeps the same rank; a tie s == tau drops the channel (strict >)
+    s_k = np.array([[3.0, 2.0, 1.0, 0.5] * 4], np.float32)
+    s_k = np.sort(s_k, axis=1)[:, ::-1].copy()
+    for shrink in (True, False):
+        layer = S.Layer(1, 1, 16, 16, "f32", "f32", s_k, [2.0], np.linspace(2, 1, 16), 1.5, shrink=shrink)
+        assert layer.ranks[0] == 4 and layer.r_v == 8
+        layer.close()
+    layer = S.Layer(1, 1, 16, 16, "f32", "f32", s_k, [0.0], np.linspace(2, 1, 16), 0.0)
+    assert layer.ranks[0] == 16 and layer.r_v == 16  # tau = 0 keeps every rank
+    layer.close()
+
+
+def test_create_validation():
+    w = I.WORKLOADS[0]
+    s_k, tau_k, s_v, tau_v, _ = I.layer_spectra(w)
+
+    def status(**kw):
+        args = dict(H_q=w.H_q, H_kv=w.H_kv, d_h=w.d_h, d=w.d, dtype="f32", latent="f32", s_k=s_k, tau_k=tau_k,
+                    s_v=s_v, tau_v=tau_v)
+        args.update(kw)
+        try:
+            S.Layer(**args).close()
+            return 0
+        except S.StarKVError as e:
+            return e.status
+
+    assert status() == 0
+    assert status(H_q=6) == -1  # H_q % H_kv != 0
+    assert status(tau_k=np.array([np.nan, 0.1, 0.1, 0.1], np.float32)) == -1
+    assert status(tau_v=-1.0) == -1
+    assert status(dtype="bf16", latent="f32") == -4
+    assert status(dtype="f32", latent="mix84") == -4
+    assert status(d=250) == -4  # d not a multiple of 16
+    assert status(tau_v=100.0) == -4  # r_v == 0
+    assert status(tau_k=np.full(4, 100.0, np.float32)) == -4  # every key rank 0
+
+
+def test_hot_calls_reject_bad_arguments_without_launching():
+    w, layer, _ = _layer(2)
+    L = S.lib()
+    h = layer._h
+    lens = np.full(w.B, 100, np.int32)
+    lp = lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    fake = ctypes.c_void_p(0x1000)
+    cache = S._Cache(0x1000, 0x2000, w.B, 4096)
+    # no factors bound yet -> ESTATE (after the argument checks pass)
+    assert L.starkv_compress_append(h, ctypes.byref(cache), fake, w.B, 1, lp, None) == -7
+    assert L.starkv_decode_attention(h, ctypes.byref(cache), fake, w.B, 1, lp, fake, ctypes.c_void_p(0x1000),
+                                     1 << 30, None) == -7
+    # argument errors
+    assert L.starkv_compress_append(h, ctypes.byref(cache), fake, w.B, 5000, lp, None) == -3  # capacity
+    assert L.starkv_compress_append(h, ctypes.byref(cache), fake, 0, 1, lp, None) == -1
+    assert L.starkv_compress_append(h, ctypes.byref(cache), fake, 129, 1, lp, None) == -4
+    assert L.starkv_compress_append(h, ctypes.byref(cache), fake, w.B, 0, lp, None) == 0  # no-op
+    bad = S._Cache(0x1000, 0x2000, w.B, 100)  # T_max not a multiple of 32
+    assert L.starkv_compress_append(h, ctypes.byref(bad), fake, w.B, 1, lp, None) == -1
+    assert L.starkv_decode_attention(h, ctypes.byref(cache), fake, w.B, 0, lp, fake, fake, 1 << 30, None) == -1
+    big = np.full(w.B, 5000, np.int32)
+    assert L.starkv_decode_attention(h, ctypes.byref(cache), fake, w.B, 1,
+                                     big.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), fake, fake, 1 << 30, None) == -3
+    assert L.starkv_decode_attention(h, ctypes.byref(cache), fake, w.B, 9, lp, fake, fake, 1 << 30, None) == -4  # 32*9 rows
+    assert L.starkv_reconstruct(h, ctypes.byref(cache), w.B, 0, 1, fake, fake, None) == -1
+    assert L.starkv_reconstruct(h, ctypes.byref(cache), 0, 5, 4, fake, fake, None) == -1
+    assert L.starkv_calibrate(h, fake, 4, fake, None) == -7
+    layer.close()
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
+def test_workspace_sizing(cfg):
+    w, layer, _ = _layer(cfg)
+    lens = I.context_lengths(w) + w.n_append
+    n = layer.workspace_bytes(w.B, w.n_q, lens)
+    M_pad = -(-w.H_q * w.n_q // 32) * 32
+    chunks = int(np.sum(-(-lens // 64)))
+    esz = 4 if w.latent == "f32" else 2
+    assert n >= chunks * M_pad * 64 * esz  # the probability buffer alone
+    assert n % 256 == 0
+    layer.close()

@@ -1,0 +1,202 @@
+"""GPU parity: libstarkv on the MI355X against the CPU oracle (same seeded inputs).
+
+Bars: ranks, factor bits, scales and cache bytes bit-exact (exact-latent conditioning);
+decode outputs within max|err| <= 1e-4 (fp32 workload) or normwise relative 2e-2 (bf16
+workloads); the same call twice gives bit-identical outputs.
+"""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import starkv_oracle as O
+from rank_kv_cache_starkv_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from tests import harness as H  # noqa: E402
+else:  # collected on CPU-only machines but never run there (marked gpu)
+    H = None
+
+
+# ---------------------------------------------------------------- factors and ranks, full shapes
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
+def test_ranks_and_factor_bits(cfg):
+    w = I.WORKLOADS[cfg]
+    H.log(f"[factors] cfg={cfg} {w.name}")
+    run = H.make_layer(w, exact=False)
+    assert list(run.GL.ranks) == list(map(int, run.OL.ranks)), "ranks"
+    assert run.GL.r_v == run.OL.r_v
+    np.testing.assert_array_equal(H.dev_bits(run.GL.A_t), H.f32_bits(run.OL.A_cat.T, w.dtype))
+    np.testing.assert_array_equal(H.dev_bits(run.GL.B_k), H.f32_bits(run.OL.B_k, w.dtype))
+    np.testing.assert_array_equal(H.dev_bits(run.GL.B_vt), H.f32_bits(run.OL.B_v.T, w.dtype))
+    fmt = run.fmt
+    assert run.GL.info["k_row_bytes"] == fmt.k_row_bytes and run.GL.info["v_tile_rows"] == fmt.v_rows
+
+
+# ---------------------------------------------------------------- reduced-size workloads, every element
+
+def mini(cfg):
+    w = I.WORKLOADS[cfg]
+    lens = {0: [256], 1: [300, 129], 2: [250, 70], 3: [1000], 4: [100, 33, 257]}[cfg]
+    return w, lens
+
+
+def _run_mini(cfg, exact, q_scale=1.0):
+    w, lens0 = mini(cfg)
+    w = dataclasses.replace(w, B=len(lens0))
+    H.log(f"[mini] cfg={cfg} {w.name} exact={exact} lens0={lens0} n_append={w.n_append} q_scale={q_scale}")
+    run = H.make_layer(w, exact=exact)
+    H.calibrate(run)
+    if exact and w.latent == "mix84":
+        np.testing.assert_array_equal(H.dev_bits(run.GL.scales), run.scales_o.view(np.uint16))
+    H.prefill(run, lens0, oracle_seqs=range(len(lens0)))
+    if w.n_append:
+        H.append_step(run, w.n_append)
+    return w, run
+
+
+def _compare_cache(run, exact):
+    w = run.w
+    for b in run.oracle_seqs:
+        gk, gv = H.gpu_seq_cache(run, b)
+        ok, ov = H.oracle_seq_bytes(run, b)
+        T = int(run.lens[b])
+        if exact:
+            np.testing.assert_array_equal(gk, ok)
+            # value tiles: compare the columns of tokens < T only
+            for t in range(0, T, O.TT):
+                n = min(O.TT, T - t) * run.fmt.elem
+                np.testing.assert_array_equal(gv[t // O.TT, :, :n], ov[t // O.TT, :, :n])
+        else:
+            kc = O.unpack_key_rows(gk, run.fmt)
+            vc = O.unpack_value_tiles(gv, run.fmt, T)
+            okc, ovc = run.ocache[b].key, run.ocache[b].value
+            if w.latent == "mix84":
+                dk, dv = np.abs(kc - okc), np.abs(vc - ovc)
+                H.log(f"  seq {b}: natural-run code mismatches key {int((dk > 0).sum())}/{dk.size}, "
+                      f"value {int((dv > 0).sum())}/{dv.size}")
+                assert dk.max() <= 1 and dv.max() <= 1
+                assert (dk > 0).mean() < 1e-3 and (dv > 0).mean() < 1e-3
+            else:
+                tol = 1e-5 if w.latent == "f32" else 2 ** -7
+                np.testing.assert_allclose(kc, okc, rtol=tol, atol=tol * np.abs(okc).max())
+                np.testing.assert_allclose(vc, ovc, rtol=tol, atol=tol * np.abs(ovc).max())
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("exact", [True, False])
+def test_mini_parity(cfg, exact):
+    w, run = _run_mini(cfg, exact)
+    _compare_cache(run, exact)
+    q = H.queries(run)
+    out = H.decode(run, q)
+    out2 = H.decode(run, q)
+    assert torch.equal(out.view(torch.int16) if out.dtype != torch.float32 else out.view(torch.int32),
+                       out2.view(torch.int16) if out2.dtype != torch.float32 else out2.view(torch.int32)), "determinism"
+    got = H.from_dev(out)
+    for b in run.oracle_seqs:
+        ref = H.oracle_decode(run, q, b)
+        H.check_output(w, got[b], ref, f"seq {b} len {int(run.lens[b])}")
+
+
+@pytest.mark.parametrize("cfg", [0, 2, 4])
+@pytest.mark.parametrize("q_scale", [30.0, 300.0])
+def test_mini_softmax_stress(cfg, q_scale):
+    w, run = _run_mini(cfg, exact=True)
+    q = H.queries(run, scale=q_scale)
+    got = H.from_dev(H.decode(run, q))
+    for b in run.oracle_seqs:
+        H.check_output(w, got[b], H.oracle_decode(run, q, b), f"q x{q_scale} seq {b}")
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2])
+def test_reconstruct(cfg):
+    w, run = _run_mini(cfg, exact=True)
+    b = 0
+    T = int(run.lens[b])
+    t0, t1 = 3, T
+    K, V = run.GL.reconstruct(run.cache, b, t0, t1)
+    torch.cuda.synchronize()
+    xk, xv = O.dequantized(run.ocache[b], run.OL, run.scales_o)
+    Kr, Vr = O.reconstruct(xk[t0:t1], xv[t0:t1], run.OL)
+    for got, ref, name in ((H.from_dev(K), Kr, "K"), (H.from_dev(V), Vr, "V")):
+        err = np.max(np.abs(got - ref)) / np.max(np.abs(ref))
+        H.log(f"  reconstruct {name}: normwise rel {err:.3e}")
+        assert err <= (1e-5 if w.dtype == "f32" else 2 ** -8)
+
+
+# ---------------------------------------------------------------- edge cases
+
+def test_edge_lengths_and_tails():
+    """Lengths equal to n_q, to one tile, just over a chunk, and a cache with no slack."""
+    w = dataclasses.replace(I.WORKLOADS[4], B=5)
+    lens0 = [0, 28, 60, 61, 125]  # + 4 appended: 4, 32, 64, 65, 129
+    run = H.make_layer(w, exact=True)
+    H.calibrate(run)
+    H.prefill(run, lens0, oracle_seqs=range(5), T_max=160)
+    H.append_step(run, 4)
+    _compare_cache(run, True)
+    q = H.queries(run)
+    got = H.from_dev(H.decode(run, q))
+    for b in range(5):
+        H.check_output(w, got[b], H.oracle_decode(run, q, b), f"len {int(run.lens[b])}")
+
+
+def test_append_noop_and_capacity():
+    import rank_kv_cache_starkv_amd as S
+    w = dataclasses.replace(I.WORKLOADS[0], B=1)
+    run = H.make_layer(w)
+    H.prefill(run, [64], oracle_seqs=[0], T_max=64)
+    before = run.cache.k_rows.clone()
+    run.GL.append(run.cache, torch.zeros((1, 0, w.d), device=H.DEV), [64])  # n_new = 0: no-op
+    torch.cuda.synchronize()
+    assert torch.equal(before, run.cache.k_rows)
+    with pytest.raises(S.StarKVError) as e:
+        run.GL.append(run.cache, torch.zeros((1, 1, w.d), device=H.DEV), [64])
+    assert e.value.status == -3
+    q = torch.zeros((1, 1, w.H_q, w.d_h), device=H.DEV)
+    with pytest.raises(S.StarKVError) as e:
+        run.GL.decode(run.cache, q, [65])
+    assert e.value.status == -3
+    with pytest.raises(S.StarKVError) as e:
+        run.GL.decode(run.cache, q, [64], ws=torch.empty(256, dtype=torch.uint8, device=H.DEV))
+    assert e.value.status == -5
+
+
+# ---------------------------------------------------------------- full-size workloads, sampled sequences
+
+def _full(cfg):
+    w = I.WORKLOADS[cfg]
+    lens0 = I.context_lengths(w)
+    if cfg == 4:
+        order = np.argsort(lens0)
+        sample = [int(order[0]), int(order[len(order) // 2])]
+    else:
+        sample = [0] if w.B == 1 else [0, w.B - 1]
+    H.log(f"[full] cfg={cfg} {w.name} B={w.B} lens0 in [{lens0.min()}, {lens0.max()}] oracle seqs {sample}")
+    run = H.make_layer(w, exact=True)
+    H.calibrate(run)
+    if w.latent == "mix84":
+        np.testing.assert_array_equal(H.dev_bits(run.GL.scales), run.scales_o.view(np.uint16))
+    H.prefill(run, lens0, oracle_seqs=sample, fast_fill=True)
+    if w.n_append:
+        H.append_step(run, w.n_append)
+    return w, run
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+def test_full_size_sampled(cfg):
+    w, run = _full(cfg)
+    _compare_cache(run, True)
+    q = H.queries(run)
+    out = H.decode(run, q)
+    got = H.from_dev(out)
+    assert np.all(np.isfinite(got))
+    for b in run.oracle_seqs:
+        ref = H.oracle_decode(run, q, b, mode="latent")
+        H.check_output(w, got[b], ref, f"seq {b} len {int(run.lens[b])}")
