@@ -1,0 +1,315 @@
+"""Benchmark of one decode step over a low-rank, quantised KV cache on one MI355X.
+
+A step is one pass of the hot path for one decoder layer: compress_append of the step's
+n_q new tokens per sequence (latent projection + quantise/round + pack), then decode
+attention read directly from the latent cache (query projection, key scores and softmax
+statistics, P.C_v, split merge and up-projection).  Inputs are resident in HBM before
+timing starts.  Steps rotate over distinct layers (own factors, own cache) totalling more
+than 1 GiB, so every step reads cold HBM rather than the 256 MB Infinity Cache.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1] [--no-cpu]
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "low-rank KV decode attention queries/s + achieved HBM GB/s vs ~8 TB/s peak"
+HBM_PEAK_GBPS = 8000.0
+MIN_ROTATION_BYTES = 1 << 30
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def to_dev_bf16(x: np.ndarray, dev: str):
+    import torch
+    from rank_kv_cache_starkv_amd import inputs as I
+    return torch.from_numpy(I.to_bf16_bits(x).view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+def algorithmic_bytes(w, ranks, r_v, lens, n_q):
+    """Bytes the method must move per step (each latent once, factors once, q, out, X_new, A)."""
+    elem = {"f32": 4, "bf16": 2}[w.dtype]
+    if w.latent == "mix84":
+        n8 = [-(-int(r) // 4) for r in ranks]
+        key_tok = sum(n8) + (sum(int(r) for r in ranks) - sum(n8)) / 2.0
+        n8v = -(-r_v // 4)
+        val_tok = n8v + (r_v - n8v) / 2.0
+        scale_k, scale_v = 2 * int(sum(ranks)), 2 * r_v
+    else:
+        le = 4 if w.latent == "f32" else 2
+        key_tok, val_tok = le * float(sum(ranks)), le * float(r_v)
+        scale_k = scale_v = 0
+    n_key = int(sum(ranks))
+    tokens = float(np.sum(lens))
+    qo = w.B * n_q * w.H_q * w.d_h * elem
+    b = {
+        "decode_qproj": qo + n_key * w.d_h * elem + scale_k,
+        "decode_scores": tokens * key_tok,
+        "decode_values": tokens * val_tok,
+        "decode_merge": r_v * w.H_kv * w.d_h * elem + qo + scale_v,
+        "append": w.B * n_q * w.d * elem + (n_key + r_v) * w.d * elem + w.B * n_q * (key_tok + val_tok)
+        + scale_k + scale_v,
+    }
+    b["decode"] = b["decode_qproj"] + b["decode_scores"] + b["decode_values"] + b["decode_merge"]
+    b["step"] = b["decode"] + b["append"]
+    return b
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "rank_kv_cache_starkv_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counters, if taken on the current kernels."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+    except Exception:
+        return None
+    e = d.get(workload, {}).get(kernel)
+    if not e or e.get("source_hash") != source_hash():
+        return None
+    return float(e["bytes_per_launch"])
+
+
+def cpu_baseline(w, lf, lens, n_q, X0, Xcal, q_step, X_step, budget_s: float):
+    """The CPU oracle (NumPy fp64) on one sequence: one decode step = append n_q tokens +
+    attention, repeated until ``budget_s`` of CPU time is used."""
+    from oracle import starkv_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:
+        cores = os.cpu_count() or 1
+    OL = O.build_layer(lf.U_k, lf.s_k, lf.V_k, lf.tau_k, lf.U_v, lf.s_v, lf.V_v, lf.tau_v, w.H_q, w.latent, w.dtype)
+    scales = O.calibrate_scales(Xcal, OL.A_cat, O.channel_qmax(OL)) if w.latent == "mix84" else None
+    t_setup = time.perf_counter()
+    base = O.compress(X0, OL, scales)
+    log(f"[cpu] oracle prefill of sequence 0 ({X0.shape[0]} tokens): {time.perf_counter() - t_setup:.1f} s")
+    reps, spent = 0, 0.0
+    while spent < budget_s and reps < 50:
+        t0 = time.perf_counter()
+        new = O.compress(X_step[0], OL, scales)
+        cache = O.SequenceCache(np.concatenate([base.key, new.key]), np.concatenate([base.value, new.value]))
+        O.decode(q_step[0].astype(np.float64), cache, OL, n_q, scales)
+        spent += time.perf_counter() - t0
+        reps += 1
+    qps = reps * n_q / spent
+    return {"value": qps, "unit": "queries/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"sequence 0 of {w.B} (context {int(lens[0])}), {reps} decode steps "
+                      f"(append {n_q} token(s) + attention), {spent:.1f} s; GPU value is all {w.B} sequences"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=1, help="workload id (0-4); 1 is the headline")
+    ap.add_argument("--layers", type=int, default=0, help="layers to rotate (0: enough for 1 GiB)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the build targets a single "
+              f"MI355X; multi-GPU sharding is described in DESIGN.md, not built)", file=sys.stderr)
+        return 2
+
+    import torch
+    import rank_kv_cache_starkv_amd as S
+    from rank_kv_cache_starkv_amd import inputs as I
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    w = I.WORKLOADS[args.workload]
+    n_q = w.n_q
+    lens = I.context_lengths(w) + w.n_append  # lengths at decode (include the n_q step tokens)
+    if not w.ragged:
+        lens = np.full(w.B, w.T, np.int32)
+    lens = lens.astype(np.int32)
+    lens_pre = (lens - n_q).astype(np.int32)  # each step appends at lens_pre and attends over lens
+    T_max = int(-(-int(lens.max()) // 32) * 32)
+    tdt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+
+    t0 = time.perf_counter()
+    lf = I.layer_factors(w, 0)
+    log(f"[setup] workload {w.cfg_id} {w.name}: host factors {time.perf_counter() - t0:.1f} s")
+    U = [torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev) for a in (lf.U_k, lf.V_k, lf.U_v, lf.V_v)]
+    Xcal = I.as_dtype(I.x_calibration(w), w.dtype) if w.latent == "mix84" else None
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(2606_08382)
+
+    def new_layer():
+        L = S.Layer(w.H_q, w.H_kv, w.d_h, w.d, w.dtype, w.latent, lf.s_k, lf.tau_k, lf.s_v, lf.tau_v)
+        L.build_factors(*U)
+        if Xcal is not None:
+            L.calibrate(to_dev_bf16(Xcal, dev) if w.dtype == "bf16" else torch.from_numpy(Xcal).to(dev))
+        return L
+
+    probe = new_layer()
+    kb, vb = probe.cache_bytes(w.B, T_max)
+    inf = probe.info
+    per_layer = kb + vb + inf["a_bytes"] + inf["bk_bytes"] + inf["bv_bytes"]
+    n_layers = args.layers or max(2, math.ceil(MIN_ROTATION_BYTES / per_layer))
+    log(f"[setup] {n_layers} layers x {per_layer / 2**20:.0f} MiB (cache {(kb + vb) / 2**20:.0f} MiB), T_max {T_max}")
+
+    # host-generated prefill of sequence 0 of layer 0 (the CPU baseline attends over the same tokens)
+    X0 = I.as_dtype(I.x_prefill(w, 0, 0, int(lens_pre[0])), w.dtype)
+    layers, caches = [], []
+    t0 = time.perf_counter()
+    for li in range(n_layers):
+        L = probe if li == 0 else new_layer()
+        c = L.new_cache(w.B, T_max)
+        for b in range(w.B):
+            n = int(lens_pre[b])
+            view = c.seq(b)
+            for s0 in range(0, n, 4096):
+                s1 = min(n, s0 + 4096)
+                if li == 0 and b == 0:
+                    X = (to_dev_bf16(X0[s0:s1], dev) if w.dtype == "bf16" else torch.from_numpy(X0[s0:s1]).to(dev))
+                else:
+                    X = torch.randn((s1 - s0, w.d), generator=gen, device=dev, dtype=torch.float32).to(tdt)
+                L.append(view, X[None].contiguous(), [s0])
+        layers.append(L)
+        caches.append(c)
+    torch.cuda.synchronize()
+    t_prefill = time.perf_counter() - t0
+    log(f"[setup] prefill {n_layers} layers ({n_layers * int(lens_pre.sum())} tokens): {t_prefill:.1f} s")
+
+    q_np = I.as_dtype(I.queries(w), w.dtype)
+    X_np = I.as_dtype(I.x_new(w, n_q), w.dtype)
+    q = to_dev_bf16(q_np, dev) if w.dtype == "bf16" else torch.from_numpy(q_np).to(dev)
+    X_step = to_dev_bf16(X_np, dev) if w.dtype == "bf16" else torch.from_numpy(X_np).to(dev)
+    ws_bytes = max(L.workspace_bytes(w.B, n_q, lens) for L in layers)
+    ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
+    outs = [torch.empty_like(q) for _ in range(n_layers)]
+
+    def step(i):
+        li = i % n_layers
+        layers[li].append(caches[li], X_step, lens_pre)
+        layers[li].decode(caches[li], q, lens, out=outs[li], ws=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # eager: one host call per append / decode
+    t_host = time.perf_counter()
+    ev0.record()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    ev1.record()
+    t_host = time.perf_counter() - t_host
+    torch.cuda.synchronize()
+    ms_step_eager = ev0.elapsed_time(ev1) / args.steps
+    log(f"[time] eager: {ms_step_eager * 1000:.2f} us/step (host issue {t_host / args.steps * 1e6:.1f} us/step)")
+
+    # graph: one rotation over the layers captured once and replayed (no host work per step)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        for li in range(n_layers):
+            step(li)
+        side.synchronize()
+        with torch.cuda.graph(graph, stream=side):
+            for li in range(n_layers):
+                step(li)
+    torch.cuda.synchronize()
+    reps = max(1, -(-args.steps // n_layers))
+    for _ in range(2):
+        graph.replay()
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(reps):
+        graph.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    n_steps = reps * n_layers
+    ms_total = ev0.elapsed_time(ev1)
+    ms_step = ms_total / n_steps
+    log(f"[time] graph: {n_steps} steps: {ms_total:.3f} ms, {ms_step * 1000:.2f} us/step")
+
+    # second pass with per-kernel events (same steps, same stream)
+    S.profile_enable(True)
+    S.profile_read(reset=True)
+    for i in range(args.steps):
+        step(args.warmup + args.steps + i)
+    torch.cuda.synchronize()
+    prof = S.profile_read(reset=True)
+    S.profile_enable(False)
+    kern_us = {k: 1000.0 * ms / n for k, (n, ms) in prof.items()}
+    for k, us in sorted(kern_us.items()):
+        log(f"[kernel] {k:14s} {us:9.2f} us/launch ({prof[k][0]} launches)")
+
+    ab = algorithmic_bytes(w, probe.ranks, probe.r_v, lens, n_q)
+    dom = max((k for k in kern_us if k.startswith("decode_")), key=lambda k: kern_us[k])
+    achieved = ab[dom] / (kern_us[dom] * 1e-6) / 1e9
+    traffic = traffic_for(dom, w.name)
+    qps = w.B * n_q / (ms_step * 1e-3)
+    dec_us = sum(us for k, us in kern_us.items() if k.startswith("decode_"))
+    result = {
+        "metric": METRIC,
+        "value": qps,
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": n_steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f32": "f32", "bf16": "bf16", "mix84": "int8/int4 codes, f16 MFMA, fp32 accumulate"}[w.latent],
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.B, "context": int(lens.max()) if not w.ragged else "ragged",
+                   "context_tokens": int(lens.sum()), "queries_per_seq": n_q, "H_q": w.H_q, "H_kv": w.H_kv,
+                   "d_h": w.d_h, "hidden": w.d, "key_rank_sum": int(np.sum(probe.ranks)), "value_rank": probe.r_v,
+                   "latent": w.latent, "layers_rotated": n_layers},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                     "alg_bytes_per_launch": ab[dom], "us_per_launch": kern_us[dom]},
+        "timing": "HIP graph of one rotation over the layers, replayed; events on the replay stream",
+        "ms_per_step_eager": ms_step_eager,
+        "step_hbm_gbps": ab["step"] / (ms_step * 1e-3) / 1e9,
+        "step_frac": ab["step"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "decode_kernels_us": dec_us,
+        "decode_hbm_gbps": ab["decode"] / (dec_us * 1e-6) / 1e9,
+        "kv_tokens_per_s": float(lens.sum()) / (ms_step * 1e-3),
+        "kernel_us": kern_us,
+        "alg_bytes": ab,
+    }
+    if not args.no_cpu:
+        t0 = time.perf_counter()
+        result["cpu_baseline"] = cpu_baseline(w, lf, lens, n_q, X0, Xcal, q_np, X_np, args.cpu_budget)
+        log(f"[cpu] {time.perf_counter() - t0:.1f} s")
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

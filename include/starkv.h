@@ -257,6 +257,21 @@ int starkv_decode_attention(const starkv_layer* layer, const starkv_cache* cache
 int starkv_reconstruct(const starkv_layer* layer, const starkv_cache* cache, int b, int t0, int t1,
                        void* K_out, void* V_out, hipStream_t stream);
 
+/* Per-kernel timing of the library's own launches, for measurement (not part of the
+ * method).  While enabled, each kernel launch is bracketed by two HIP events recorded on
+ * the launch's stream.  starkv_profile_read waits for the recorded events, adds their
+ * durations into per-kernel totals, and copies up to max_entries totals into out (host);
+ * *n_entries receives the number of distinct kernels.  reset != 0 clears the totals
+ * afterwards.  Process-wide; thread-safe.  Errors: EHIP if an event query fails. */
+typedef struct starkv_kernel_time {
+  char name[32];
+  int launches;
+  double total_ms;
+} starkv_kernel_time;
+
+int starkv_profile_enable(int on);
+int starkv_profile_read(starkv_kernel_time* out, int max_entries, int* n_entries, int reset);
+
 #ifdef __cplusplus
 }
 #endif

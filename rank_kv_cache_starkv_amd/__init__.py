@@ -54,6 +54,10 @@ class _Info(ctypes.Structure):
                [(n, ctypes.c_size_t) for n in ("a_bytes", "bk_bytes", "bv_bytes", "scale_bytes")]
 
 
+class _KernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 32), ("launches", ctypes.c_int), ("total_ms", ctypes.c_double)]
+
+
 class _Cache(ctypes.Structure):
     _fields_ = [("k_rows", ctypes.c_void_p), ("v_tiles", ctypes.c_void_p), ("B", ctypes.c_int),
                 ("T_max", ctypes.c_int)]
@@ -62,7 +66,8 @@ class _Cache(ctypes.Structure):
 EXPORTS = ["starkv_abi_version", "starkv_status_string", "starkv_layer_create", "starkv_layer_destroy",
            "starkv_layer_get_info", "starkv_layer_ranks", "starkv_build_factors", "starkv_bind_factors",
            "starkv_calibrate", "starkv_bind_scales", "starkv_cache_bytes", "starkv_compress_append",
-           "starkv_decode_workspace_bytes", "starkv_decode_attention", "starkv_reconstruct"]
+           "starkv_decode_workspace_bytes", "starkv_decode_attention", "starkv_reconstruct",
+           "starkv_profile_enable", "starkv_profile_read"]
 
 _lib = None
 
@@ -93,11 +98,26 @@ def lib() -> ctypes.CDLL:
     L.starkv_decode_attention.argtypes = [vp, ctypes.POINTER(_Cache), vp, ci, ci, ctypes.POINTER(ctypes.c_int32),
                                           vp, vp, sz, vp]
     L.starkv_reconstruct.argtypes = [vp, ctypes.POINTER(_Cache), ci, ci, ci, vp, vp, vp]
+    L.starkv_profile_enable.argtypes = [ci]
+    L.starkv_profile_read.argtypes = [ctypes.POINTER(_KernelTime), ci, ctypes.POINTER(ci), ci]
     for name in EXPORTS:
         if name not in ("starkv_abi_version", "starkv_status_string"):
             getattr(L, name).restype = ci
     _lib = L
     return L
+
+
+def profile_enable(on: bool = True) -> None:
+    """Bracket every libstarkv kernel launch with HIP events on its stream (measurement only)."""
+    _check(lib().starkv_profile_enable(1 if on else 0), "starkv_profile_enable")
+
+
+def profile_read(reset: bool = True) -> dict:
+    """{kernel name: (launches, total ms)} of the launches timed since the last reset."""
+    buf = (_KernelTime * 64)()
+    n = ctypes.c_int()
+    _check(lib().starkv_profile_read(buf, 64, ctypes.byref(n), 1 if reset else 0), "starkv_profile_read")
+    return {buf[i].name.decode(): (buf[i].launches, buf[i].total_ms) for i in range(min(n.value, 64))}
 
 
 def _check(status: int, what: str) -> None:

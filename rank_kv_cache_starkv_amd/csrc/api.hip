@@ -5,6 +5,7 @@
 #include <new>
 
 #include "device_common.h"
+#include "profile.h"
 #include "starkv_internal.h"
 
 namespace skv {
@@ -280,6 +281,15 @@ int starkv_reconstruct(const starkv_layer* l, const starkv_cache* c, int b, int 
   st = check_bound(l->L, true);
   if (st != STARKV_OK) return st;
   return hip_status(skv::launch_reconstruct(l->L, *c, b, t0, t1, K_out, V_out, stream));
+  SKV_GUARD_END
+}
+
+int starkv_profile_enable(int on) { return skv::profile_enable(on); }
+
+int starkv_profile_read(starkv_kernel_time* out, int max_entries, int* n_entries, int reset) {
+  SKV_GUARD_BEGIN
+  if (max_entries < 0 || (max_entries > 0 && !out)) return STARKV_EINVAL;
+  return skv::profile_read(out, max_entries, n_entries, reset) == 0 ? STARKV_OK : STARKV_EHIP;
   SKV_GUARD_END
 }
 

@@ -9,6 +9,7 @@
 // in cache order, so that the two nibbles of an int4 byte are adjacent columns), K = d.
 // Workgroup tile 64 x 64, four waves of 32 x 32 (v_mfma_f32_32x32x16_bf16, or 32x32x2_f32).
 #include "device_common.h"
+#include "profile.h"
 #include "starkv_internal.h"
 
 namespace skv {
@@ -210,6 +211,7 @@ hipError_t launch_append(const Layer& L, const starkv_cache& c, const void* X_ne
   a.scales = L.scales;
   for (int b = 0; b < B; ++b) a.lens[b] = lens[b];
   dim3 grid((B * n_new + 63) / 64, (a.NS + 63) / 64);
+  ProfScope ps("append", s);
   if (L.dtype == STARKV_BF16) hipLaunchKernelGGL((k_latent_gemm<STARKV_BF16, 0>), grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL((k_latent_gemm<STARKV_F32, 0>), grid, dim3(256), 0, s, a);
   return hipGetLastError();

@@ -17,6 +17,7 @@
 #include <cstdlib>
 
 #include "device_common.h"
+#include "profile.h"
 #include "starkv_internal.h"
 
 namespace skv {
@@ -840,12 +841,15 @@ hipError_t launch_decode(const Layer& L, const DecodePlan& plan, const KtList& k
   qa.nkt_max = w.nkt_max;
   qa.kts = kts;
   dim3 gq(g.nct, g.B);
+  {
+  ProfScope ps("decode_qproj", s);
   if (L.dtype == STARKV_F32) {
     hipLaunchKernelGGL((k_qproj<STARKV_F32, STARKV_LATENT_F32>), gq, dim3(256), 0, s, qa);
   } else if (L.latent == STARKV_LATENT_BF16) {
     hipLaunchKernelGGL((k_qproj<STARKV_BF16, STARKV_LATENT_BF16>), gq, dim3(256), 0, s, qa);
   } else {
     hipLaunchKernelGGL((k_qproj<STARKV_BF16, STARKV_LATENT_MIX84>), gq, dim3(256), 0, s, qa);
+  }
   }
   // 2. scores
   ScoreArgs sa;
@@ -860,12 +864,15 @@ hipError_t launch_decode(const Layer& L, const DecodePlan& plan, const KtList& k
   sa.kts = kts;
   sa.seq = seq;
   const int W = std::min(g.nct, 4);
+  {
+  ProfScope ps("decode_scores", s);
   if (L.latent == STARKV_LATENT_MIX84)
     hipLaunchKernelGGL(k_scores<STARKV_LATENT_MIX84>, dim3(w.total_chunks), dim3(64 * W), 0, s, sa);
   else if (L.latent == STARKV_LATENT_BF16)
     hipLaunchKernelGGL(k_scores<STARKV_LATENT_BF16>, dim3(w.total_chunks), dim3(64 * W), 0, s, sa);
   else
     hipLaunchKernelGGL(k_scores<STARKV_LATENT_F32>, dim3(w.total_chunks), dim3(64 * W), 0, s, sa);
+  }
   // 3. values
   ValueArgs va;
   va.v_tiles = (const uint8_t*)v_tiles;
@@ -886,9 +893,12 @@ hipError_t launch_decode(const Layer& L, const DecodePlan& plan, const KtList& k
   const int nmt = g.M_pad / 32;
   dim3 gv((va.NB + va.bpw - 1) / va.bpw, w.total_splits);
   dim3 bv(64 * va.bpw);
+  {
+  ProfScope ps("decode_values", s);
   if (L.latent == STARKV_LATENT_MIX84) launch_values_nmt<STARKV_LATENT_MIX84>(nmt, gv, bv, s, va);
   else if (L.latent == STARKV_LATENT_BF16) launch_values_nmt<STARKV_LATENT_BF16>(nmt, gv, bv, s, va);
   else launch_values_nmt<STARKV_LATENT_F32>(nmt, gv, bv, s, va);
+  }
   // 4. merge + up-projection
   MergeArgs ma;
   ma.zp = w.zp;
@@ -901,8 +911,11 @@ hipError_t launch_decode(const Layer& L, const DecodePlan& plan, const KtList& k
   ma.seq = seq;
   const int Rg = g.B * g.G * g.n_q;
   dim3 gm(g.H_kv, (Rg + 15) / 16);
+  {
+  ProfScope ps("decode_merge", s);
   if (L.dtype == STARKV_F32) hipLaunchKernelGGL(k_merge<STARKV_F32>, gm, dim3(256), 0, s, ma);
   else hipLaunchKernelGGL(k_merge<STARKV_BF16>, gm, dim3(256), 0, s, ma);
+  }
   return hipGetLastError();
 }
 

@@ -200,3 +200,38 @@ def test_full_size_sampled(cfg):
     for b in run.oracle_seqs:
         ref = H.oracle_decode(run, q, b, mode="latent")
         H.check_output(w, got[b], ref, f"seq {b} len {int(run.lens[b])}")
+
+
+# ---------------------------------------------------------------- graph capture of a decode step
+
+def test_graph_replay_matches_eager():
+    """One decode step (append + attention) captured in a HIP graph: every replay, with eager
+    work and synchronisations in between, gives the eager result bit for bit."""
+    w, run = _run_mini(2, exact=True)
+    q = H.to_dev(H.queries(run), w.dtype)
+    Xn = H.to_dev(H.hidden(run, I.x_new(dataclasses.replace(w, B=len(run.lens)), 1, step=7)), w.dtype)
+    lens_pre = run.lens.copy()
+    lens = lens_pre + 1
+    ws = torch.empty((run.GL.workspace_bytes(len(lens), w.n_q, lens),), dtype=torch.uint8, device=H.DEV)
+    out = torch.empty_like(q)
+    run.GL.append(run.cache, Xn, lens_pre)
+    run.GL.decode(run.cache, q, lens, out=out, ws=ws)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            run.GL.append(run.cache, Xn, lens_pre)
+            run.GL.decode(run.cache, q, lens, out=out, ws=ws)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        out.zero_()
+        ws.fill_(0xAB)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {rep}"
+        # eager work between replays
+        run.GL.decode(run.cache, q, lens, out=torch.empty_like(q))
+        torch.cuda.synchronize()
