@@ -61,11 +61,12 @@ def algorithmic_bytes(w, ranks, r_v, lens, n_q):
         "decode_qproj": qo + n_key * w.d_h * elem + scale_k,
         "decode_scores": tokens * key_tok,
         "decode_values": tokens * val_tok,
-        "decode_merge": r_v * w.H_kv * w.d_h * elem + qo + scale_v,
+        "decode_zmerge": scale_v,
+        "decode_upproj": r_v * w.H_kv * w.d_h * elem + qo,
         "append": w.B * n_q * w.d * elem + (n_key + r_v) * w.d * elem + w.B * n_q * (key_tok + val_tok)
         + scale_k + scale_v,
     }
-    b["decode"] = b["decode_qproj"] + b["decode_scores"] + b["decode_values"] + b["decode_merge"]
+    b["decode"] = sum(v for k, v in b.items() if k.startswith("decode_"))
     b["step"] = b["decode"] + b["append"]
     return b
 

@@ -152,9 +152,10 @@ const char* starkv_status_string(int status);
  * Host only: the layer's small device tables (channel maps, calibration
  * scratch) are allocated on the current device by the first
  * starkv_build_factors / starkv_bind_factors call.
- * Errors: EINVAL (null, non-positive sizes, H_q % H_kv != 0, n_v < 1, NaN or
- * negative thresholds), EUNSUPPORTED (dtype/latent combination, a rank of 0
- * for every key head, r_v == 0, sizes over the limits), ENOMEM, EHIP.
+ * Errors: EINVAL (null, non-positive sizes, H_q % H_kv != 0, n_v < 1 or above
+ * min(d, H_kv*d_h), NaN or negative thresholds), EUNSUPPORTED (dtype/latent
+ * combination, d not a multiple of 16, d_h not a multiple of 32 or above 256,
+ * every key rank 0, r_v == 0, n_lat above 8192), ENOMEM.
  */
 int starkv_layer_create(const starkv_layer_desc* desc, starkv_layer** out);
 

@@ -78,7 +78,7 @@ int starkv_layer_create(const starkv_layer_desc* d, starkv_layer** out) {
   // supported combinations and sizes
   if (d->latent == STARKV_LATENT_F32 && d->dtype != STARKV_F32) return STARKV_EUNSUPPORTED;
   if (d->latent != STARKV_LATENT_F32 && d->dtype != STARKV_BF16) return STARKV_EUNSUPPORTED;
-  if (d->d % 16 != 0 || d->d_h % 16 != 0 || d->d_h > 256) return STARKV_EUNSUPPORTED;
+  if (d->d % 16 != 0 || d->d_h % 32 != 0 || d->d_h > 256) return STARKV_EUNSUPPORTED;
   if (d->n_v > d->d || d->n_v > d->H_kv * d->d_h) return STARKV_EINVAL;
   starkv_layer* l = new starkv_layer();
   int st = skv::layer_init(*d, &l->L);

@@ -49,6 +49,139 @@ __device__ __forceinline__ void load_frag8(const void* base, size_t elem_off, bo
   }
 }
 
+// Store R latent values of one cache slot (column) for R token rows: quantise/pack (mix84) or
+// round (bf16) or store (f32).  For int4 slots the even-slot lane of each lane pair writes the
+// byte holding both nibbles (the partner slot is in lane ^ 1, same rows); every lane of the wave
+// must call this together.
+template <int R>
+__device__ __forceinline__ void store_latent(const GemmArgs& a, int slot, int chan, const float* xs, const int* ms) {
+  const bool is_key = slot < a.key_slots;
+  if (a.latent == STARKV_LATENT_MIX84) {
+    int qmax;
+    if (is_key) qmax = slot < a.K8 ? 127 : 7;
+    else qmax = (slot - a.key_slots) < a.V8 ? 127 : 7;
+    const float sc = chan >= 0 ? f16_to_f32(a.scales[chan]) : 0.f;
+    const bool nib = qmax == 7;
+#pragma unroll
+    for (int v = 0; v < R; ++v) {
+      const int m = ms[v];
+      int code = 0;
+      if (sc != 0.f) {
+        const float y = xs[v] / sc;  // IEEE fp32 division
+        float rq = __builtin_rintf(y);
+        rq = fminf(fmaxf(rq, -(float)qmax), (float)qmax);
+        code = (int)rq;
+      }
+      const int partner = __shfl_xor(code, 1, 64);
+      if (m >= a.M || slot >= a.NS) continue;
+      const int b = m / a.n_new, i = m - b * a.n_new;
+      const int pos = a.lens[b] + i;
+      if (is_key) {
+        uint8_t* row = a.k_rows + ((size_t)b * a.T_max + pos) * a.k_row_bytes;
+        if (!nib) row[slot] = (uint8_t)(code & 0xFF);
+        else if ((slot & 1) == 0) row[a.K8 + (slot - a.K8) / 2] = (uint8_t)((code & 0xF) | ((partner & 0xF) << 4));
+      } else {
+        const int u = slot - a.key_slots;
+        uint8_t* tile = a.v_tiles + ((size_t)b * (a.T_max / kTT) + pos / kTT) * a.v_rows * kTT;
+        if (!nib) tile[(size_t)u * kTT + pos % kTT] = (uint8_t)(code & 0xFF);
+        else if ((u & 1) == 0)
+          tile[(size_t)(a.V8 + (u - a.V8) / 2) * kTT + pos % kTT] = (uint8_t)((code & 0xF) | ((partner & 0xF) << 4));
+      }
+    }
+    return;
+  }
+  // unquantised latent: fp32 or bf16 elements
+#pragma unroll
+  for (int v = 0; v < R; ++v) {
+    const int m = ms[v];
+    if (m >= a.M || slot >= a.NS) continue;
+    const int b = m / a.n_new, i = m - b * a.n_new;
+    const int pos = a.lens[b] + i;
+    const float x = xs[v];
+    if (is_key) {
+      uint8_t* row = a.k_rows + ((size_t)b * a.T_max + pos) * a.k_row_bytes;
+      if (a.latent == STARKV_LATENT_F32) ((float*)row)[slot] = x;
+      else ((uint16_t*)row)[slot] = f32_to_bf16(x);
+    } else {
+      const int u = slot - a.key_slots;
+      uint8_t* tile = a.v_tiles + ((size_t)b * (a.T_max / kTT) + pos / kTT) * a.v_rows * kTT * (a.latent == STARKV_LATENT_F32 ? 4 : 2);
+      if (a.latent == STARKV_LATENT_F32) ((float*)tile)[(size_t)u * kTT + pos % kTT] = x;
+      else ((uint16_t*)tile)[(size_t)u * kTT + pos % kTT] = f32_to_bf16(x);
+    }
+  }
+}
+
+// Few-token append (M <= 16 rows): the work is reading A once.  Workgroup = 16 cache slots
+// x all rows; the 8 waves split K = d and their 16x16 partial results are summed through LDS;
+// loads run 4 K-steps deep.  16x16x32 bf16 MFMA (16x16x4 f32 for the fp32 path).
+template <int DT>
+__global__ __launch_bounds__(512) void k_latent_gemm_skinny(GemmArgs a) {
+  constexpr int KU = 4;
+  __shared__ float red[7][4][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const int n = lane & 15, q = lane >> 4;
+  const int s0 = blockIdx.x * 16;
+  const bool a_ok = n < a.M;
+  const int bslot = s0 + n;
+  const int bchan = (bslot < a.NS) ? a.slot_chan[bslot] : -1;
+  const bool b_ok = bchan >= 0;
+  const size_t a_base = (size_t)(a_ok ? n : 0) * a.d;
+  const size_t b_base = (size_t)(b_ok ? bchan : 0) * a.d;
+  const int ksteps = a.d / 32;
+  const int per = (ksteps + 7) / 8;
+  const int k_beg = wave * per, k_end = min(ksteps, k_beg + per);
+  f32x4 acc = {0, 0, 0, 0};
+  for (int k0 = k_beg; k0 < k_end; k0 += KU) {
+    u32x4 av[KU][2], bv[KU][2];
+#pragma unroll
+    for (int j = 0; j < KU; ++j) {
+      const bool on = k0 + j < k_end;
+      const size_t ko = (size_t)(k0 + j) * 32 + 8 * q;
+      if (DT == STARKV_BF16) {
+        av[j][0] = (on && a_ok) ? ld16((const uint16_t*)a.X + a_base + ko) : u32x4{0, 0, 0, 0};
+        bv[j][0] = (on && b_ok) ? ld16((const uint16_t*)a.A_t + b_base + ko) : u32x4{0, 0, 0, 0};
+      } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          av[j][h] = (on && a_ok) ? ld16((const float*)a.X + a_base + ko + 4 * h) : u32x4{0, 0, 0, 0};
+          bv[j][h] = (on && b_ok) ? ld16((const float*)a.A_t + b_base + ko + 4 * h) : u32x4{0, 0, 0, 0};
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < KU; ++j) {
+      if (DT == STARKV_BF16) {
+        acc = mfma16_bf16(as_bf16x8(av[j][0]), as_bf16x8(bv[j][0]), acc);
+      } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc = mfma16_f32(__uint_as_float(av[j][h][e]), __uint_as_float(bv[j][h][e]), acc);
+      }
+    }
+  }
+  if (wave > 0) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) red[wave - 1][v][lane] = acc[v];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  float xs[4];
+  int ms[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    float x = acc[v];
+#pragma unroll
+    for (int w = 0; w < 7; ++w) x += red[w][v][lane];
+    xs[v] = x;
+    ms[v] = 4 * q + v;  // D row = token row; D column = n
+  }
+  const int slot = s0 + n;
+  const int chan = (slot < a.NS) ? a.slot_chan[slot] : -1;
+  store_latent<4>(a, slot, chan, xs, ms);
+}
+
 template <int DT, int MODE>
 __global__ __launch_bounds__(256) void k_latent_gemm(GemmArgs a) {
   const int lane = threadIdx.x & 63;
@@ -98,61 +231,14 @@ __global__ __launch_bounds__(256) void k_latent_gemm(GemmArgs a) {
     return;
   }
 
-  const bool is_key = slot < a.key_slots;
-  if (a.latent == STARKV_LATENT_MIX84) {
-    int qmax;
-    if (is_key) qmax = slot < a.K8 ? 127 : 7;
-    else qmax = (slot - a.key_slots) < a.V8 ? 127 : 7;
-    const float sc = chan >= 0 ? f16_to_f32(a.scales[chan]) : 0.f;
-    const bool nib = qmax == 7;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int m = m0 + d32_row(v, q);
-      int code = 0;
-      if (sc != 0.f) {
-        const float y = acc[v] / sc;  // IEEE fp32 division
-        float rq = __builtin_rintf(y);
-        rq = fminf(fmaxf(rq, -(float)qmax), (float)qmax);
-        code = (int)rq;
-      }
-      const int partner = __shfl_xor(code, 1, 64);
-      if (m >= a.M || slot >= a.NS) continue;
-      const int b = m / a.n_new, i = m - b * a.n_new;
-      const int pos = a.lens[b] + i;
-      if (is_key) {
-        uint8_t* row = a.k_rows + ((size_t)b * a.T_max + pos) * a.k_row_bytes;
-        if (!nib) row[slot] = (uint8_t)(code & 0xFF);
-        else if ((slot & 1) == 0) row[a.K8 + (slot - a.K8) / 2] = (uint8_t)((code & 0xF) | ((partner & 0xF) << 4));
-      } else {
-        const int u = slot - a.key_slots;
-        uint8_t* tile = a.v_tiles + ((size_t)b * (a.T_max / kTT) + pos / kTT) * a.v_rows * kTT;
-        if (!nib) tile[(size_t)u * kTT + pos % kTT] = (uint8_t)(code & 0xFF);
-        else if ((u & 1) == 0)
-          tile[(size_t)(a.V8 + (u - a.V8) / 2) * kTT + pos % kTT] = (uint8_t)((code & 0xF) | ((partner & 0xF) << 4));
-      }
-    }
-    return;
-  }
-
-  // unquantised latent: fp32 or bf16 elements
+  float xs[16];
+  int ms[16];
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
-    const int m = m0 + d32_row(v, q);
-    if (m >= a.M || slot >= a.NS) continue;
-    const int b = m / a.n_new, i = m - b * a.n_new;
-    const int pos = a.lens[b] + i;
-    const float x = acc[v];
-    if (is_key) {
-      uint8_t* row = a.k_rows + ((size_t)b * a.T_max + pos) * a.k_row_bytes;
-      if (a.latent == STARKV_LATENT_F32) ((float*)row)[slot] = x;
-      else ((uint16_t*)row)[slot] = f32_to_bf16(x);
-    } else {
-      const int u = slot - a.key_slots;
-      uint8_t* tile = a.v_tiles + ((size_t)b * (a.T_max / kTT) + pos / kTT) * a.v_rows * kTT * (a.latent == STARKV_LATENT_F32 ? 4 : 2);
-      if (a.latent == STARKV_LATENT_F32) ((float*)tile)[(size_t)u * kTT + pos % kTT] = x;
-      else ((uint16_t*)tile)[(size_t)u * kTT + pos % kTT] = f32_to_bf16(x);
-    }
+    xs[v] = acc[v];
+    ms[v] = m0 + d32_row(v, q);
   }
+  store_latent<16>(a, slot, chan, xs, ms);
 }
 
 __global__ void k_fill_u32(uint32_t* p, int n, uint32_t v) {
@@ -210,10 +296,16 @@ hipError_t launch_append(const Layer& L, const starkv_cache& c, const void* X_ne
   a.v_tiles = (uint8_t*)c.v_tiles;
   a.scales = L.scales;
   for (int b = 0; b < B; ++b) a.lens[b] = lens[b];
-  dim3 grid((B * n_new + 63) / 64, (a.NS + 63) / 64);
   ProfScope ps("append", s);
-  if (L.dtype == STARKV_BF16) hipLaunchKernelGGL((k_latent_gemm<STARKV_BF16, 0>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((k_latent_gemm<STARKV_F32, 0>), grid, dim3(256), 0, s, a);
+  if (B * n_new <= 16 && L.d % 32 == 0) {
+    dim3 grid((a.NS + 15) / 16);
+    if (L.dtype == STARKV_BF16) hipLaunchKernelGGL(k_latent_gemm_skinny<STARKV_BF16>, grid, dim3(512), 0, s, a);
+    else hipLaunchKernelGGL(k_latent_gemm_skinny<STARKV_F32>, grid, dim3(512), 0, s, a);
+  } else {
+    dim3 grid((B * n_new + 63) / 64, (a.NS + 63) / 64);
+    if (L.dtype == STARKV_BF16) hipLaunchKernelGGL((k_latent_gemm<STARKV_BF16, 0>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_latent_gemm<STARKV_F32, 0>), grid, dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 

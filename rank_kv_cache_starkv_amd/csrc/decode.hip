@@ -89,7 +89,15 @@ int plan_decode(const Layer& L, int B, int n_q, const int32_t* lens, int T_max, 
   int bpw = NB >= 16 ? 4 : (NB >= 8 ? 2 : 1);
   bpw = env_int("STARKV_BPW", bpw);
   if (bpw < 1 || bpw > 4) bpw = 4;
-  const int n_slices = ceil_div(NB, bpw);
+  int n_slices = ceil_div(NB, bpw);
+  DecodeWs& w = P->ws;
+  // one-M-tile value kernel: slices of up to nbw8 one-N-tile blocks and nbw4 int4 blocks
+  w.nbw8 = std::min(4, std::max(1, env_int("STARKV_NBW8", 4)));
+  w.nbw4 = std::min(2, std::max(1, env_int("STARKV_NBW4", 2)));
+  const int nb8 = L.mix() ? L.V8 / 32 : NB;
+  w.n_sl8 = ceil_div(nb8, w.nbw8);
+  w.n_sl4 = L.mix() ? ceil_div(NB - nb8, w.nbw4) : 0;
+  if (g.M_pad == 32) n_slices = w.n_sl8 + w.n_sl4;
   int total_chunks = 0, max_chunks = 0;
   seq->chunk_off[0] = 0;
   for (int b = 0; b < B; ++b) {
@@ -99,7 +107,9 @@ int plan_decode(const Layer& L, int B, int n_q, const int32_t* lens, int T_max, 
     total_chunks += nc;
     max_chunks = std::max(max_chunks, nc);
   }
-  int cps = std::max(1, (total_chunks * n_slices) / 512);
+  // splits: aim at ~320 value workgroups, at least 8 tiles (two per wave) per split
+  const int target_wg = env_int("STARKV_VALUE_WGS", 320);
+  int cps = std::max(8, ceil_div(total_chunks, std::max(1, target_wg / n_slices)));
   cps = std::max(cps, ceil_div(max_chunks, kMaxSplitsPerSeq));
   const int cps_env = env_int("STARKV_CPS", 0);
   if (cps_env > 0) cps = std::max(cps_env, ceil_div(max_chunks, kMaxSplitsPerSeq));
@@ -112,7 +122,6 @@ int plan_decode(const Layer& L, int B, int n_q, const int32_t* lens, int T_max, 
   }
 
   // workspace
-  DecodeWs& w = P->ws;
   const int esz_p = L.latent == STARKV_LATENT_F32 ? 4 : 2;
   size_t o = 0;
   const size_t o_qfrag = o; o = align256(o + (size_t)B * g.nct * nkt_max * 2048);
@@ -123,6 +132,7 @@ int plan_decode(const Layer& L, int B, int n_q, const int32_t* lens, int T_max, 
   const size_t o_zp = o; o = align256(o + (size_t)total_splits * g.M_pad * L.r_v * 4);
   const size_t o_sm = o; o = align256(o + (size_t)total_splits * g.M_pad * 4);
   const size_t o_sl = o; o = align256(o + (size_t)total_splits * g.M_pad * 4);
+  const size_t o_zt = o; o = align256(o + (size_t)B * g.M_pad * L.r_v * 4);
   P->ws_bytes = o;
   uint8_t* base = (uint8_t*)ws_base;
   w.qfrag = base + o_qfrag;
@@ -133,6 +143,7 @@ int plan_decode(const Layer& L, int B, int n_q, const int32_t* lens, int T_max, 
   w.zp = (float*)(base + o_zp);
   w.sm = (float*)(base + o_sm);
   w.sl = (float*)(base + o_sl);
+  w.zt = (float*)(base + o_zt);
   w.nkt_max = nkt_max;
   w.total_chunks = total_chunks;
   w.total_splits = total_splits;
@@ -162,156 +173,194 @@ __device__ __forceinline__ float ldx(const void* p, size_t i) {
   return bf16_to_f32(((const uint16_t*)p)[i]);
 }
 
+// One workgroup per (sequence, KV head g): the rows of g (its G query heads x n_q queries)
+// are complete here, so the per-row quantisation scale is local.  Each row owns the 16-byte
+// fragment chunks of its column in every K-tile of its column tile; the workgroup writes
+// exactly those chunks (zeros outside g's segment), so no two workgroups write the same bytes.
 template <int DT, int LAT>
 __global__ __launch_bounds__(256) void k_qproj(QprojArgs a) {
-  constexpr int RMAX = 256;
-  __shared__ float qh[16][RMAX];
-  __shared__ float rho_s[16];
-  __shared__ int seg_g[16];
-  const int ct = blockIdx.x, b = blockIdx.y;
-  const int tid = threadIdx.x;
+  constexpr int RB = 8;     // rows per batch
+  constexpr int RMAX = 256; // max rank (<= d_h <= 256)
+  __shared__ float qrow[RB][RMAX];
+  __shared__ float qh[RB][RMAX];
+  __shared__ int8_t hi8[RB][RMAX];
+  __shared__ int8_t lo8[RB][RMAX];
+  __shared__ float rho_s[RB];
   const DecodeGeom& g = a.g;
+  const int gk = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int rph = g.G * g.n_q;
-  if (tid < 16) {
-    const int i = ct * 16 + tid;
-    seg_g[tid] = (i < g.M_q) ? i / rph : -1;
-  }
-  __syncthreads();
-  // q^ = (q B_g^T) * scale * log2(e)/sqrt(d_h) over each row's segment
-  for (int idx = tid; idx < 16 * RMAX; idx += 256) {
-    const int n = idx / RMAX, k = idx % RMAX;
-    const int gg = seg_g[n];
-    float val = 0.f;
-    if (gg >= 0) {
-      const int c0 = a.heads.koff[gg];
-      const int r = a.heads.koff[gg + 1] - c0;
-      if (k < r) {
-        const int i = ct * 16 + n;
-        const int hh = (i % rph) / g.n_q, j = i % g.n_q;
-        const int h = gg * g.G + hh;
-        const size_t qoff = (((size_t)b * g.n_q + j) * g.H_q + h) * g.d_h;
+  const int c0 = a.heads.koff[gk];
+  const int r = a.heads.koff[gk + 1] - c0;
+  const int n8g = (LAT == STARKV_LATENT_MIX84) ? a.heads.n8[gk] : 0;
+  const int o8 = (LAT == STARKV_LATENT_MIX84) ? a.heads.off8[gk] : 0;
+  const int o4 = (LAT == STARKV_LATENT_MIX84) ? a.heads.off4[gk] : 0;
+
+  for (int rb0 = 0; rb0 < rph; rb0 += RB) {
+    const int nrows = min(RB, rph - rb0);
+    __syncthreads();
+    // query rows of this batch into LDS (fp32)
+    for (int idx = tid; idx < nrows * g.d_h; idx += 256) {
+      const int n = idx / g.d_h, e = idx % g.d_h;
+      const int i = gk * rph + rb0 + n;
+      const int hh = (i % rph) / g.n_q, j = i % g.n_q;
+      const int h = gk * g.G + hh;
+      qrow[n][e] = ldx<DT>(a.q, (((size_t)b * g.n_q + j) * g.H_q + h) * g.d_h + e);
+    }
+    __syncthreads();
+    // q^[n][k] = (q_n . B_k[c0 + k]) * scale * log2(e)/sqrt(d_h): 4 lanes per dot product
+    for (int p0 = 0; p0 < nrows * r; p0 += 64) {
+      const int p = p0 + (tid >> 2), sub = tid & 3;
+      float acc = 0.f;
+      if (p < nrows * r) {
+        const int n = p / r, k = p % r;
         const size_t boff = (size_t)(c0 + k) * g.d_h;
-        float acc = 0.f;
-        for (int e = 0; e < g.d_h; ++e) acc = fmaf(ldx<DT>(a.q, qoff + e), ldx<DT>(a.B_k, boff + e), acc);
+        for (int e0 = 8 * sub; e0 < g.d_h; e0 += 32) {
+          if (DT == STARKV_F32) {
+            const u32x4 v0 = ld16((const float*)a.B_k + boff + e0);
+            const u32x4 v1 = ld16((const float*)a.B_k + boff + e0 + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              acc = fmaf(qrow[n][e0 + e], __uint_as_float(v0[e]), acc);
+              acc = fmaf(qrow[n][e0 + 4 + e], __uint_as_float(v1[e]), acc);
+            }
+          } else {
+            const u32x4 v = ld16((const uint16_t*)a.B_k + boff + e0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              acc = fmaf(qrow[n][e0 + 2 * e], bf16_to_f32((uint16_t)(v[e] & 0xFFFF)), acc);
+              acc = fmaf(qrow[n][e0 + 2 * e + 1], bf16_to_f32((uint16_t)(v[e] >> 16)), acc);
+            }
+          }
+        }
+      }
+      acc += __shfl_xor(acc, 1, 64);
+      acc += __shfl_xor(acc, 2, 64);
+      if (p < nrows * r && sub == 0) {
+        const int n = p / r, k = p % r;
         float sc = 1.f;
         if (LAT == STARKV_LATENT_MIX84) sc = f16_to_f32(a.scales[c0 + k]);
-        val = acc * sc * g.qscale;
+        qh[n][k] = acc * sc * g.qscale;
       }
     }
-    qh[n][k] = val;
-  }
-  __syncthreads();
-  if (LAT == STARKV_LATENT_MIX84 && tid < 16) {
-    const int gg = seg_g[tid];
-    float amax = 0.f;
-    if (gg >= 0) {
-      const int r = a.heads.koff[gg + 1] - a.heads.koff[gg];
-      for (int k = 0; k < r; ++k) amax = fmaxf(amax, fabsf(qh[tid][k]));
-    }
-    rho_s[tid] = amax > 0.f ? amax / 127.f : 1.f;
-  }
-  __syncthreads();
-  // hi/lo split per element; int8 keeps rho * (hi + lo/254), bf16 keeps hi + lo
-  __shared__ int8_t hi8[16][RMAX];
-  __shared__ int8_t lo8[16][RMAX];
-  for (int idx = tid; idx < 16 * RMAX; idx += 256) {
-    const int n = idx / RMAX, k = idx % RMAX;
-    const float x = qh[n][k];
+    __syncthreads();
+    // per-row scale (int8 path): rho = max|q^| / 127, one wave per row
     if (LAT == STARKV_LATENT_MIX84) {
-      const float rho = rho_s[n];
-      float hi = fminf(fmaxf(__builtin_rintf(x / rho), -127.f), 127.f);
-      float lo = fminf(fmaxf(__builtin_rintf((x - hi * rho) * (254.f / rho)), -127.f), 127.f);
-      hi8[n][k] = (int8_t)hi;
-      lo8[n][k] = (int8_t)lo;
-    }
-  }
-  __syncthreads();
-  // row parameters
-  if (tid < 16) {
-    const int i = ct * 16 + tid;
-    const int gg = seg_g[tid];
-    if (gg >= 0) {
-      float bh = 0.f, bl = 0.f;
-      if (LAT == STARKV_LATENT_MIX84) {
-        const int r = a.heads.koff[gg + 1] - a.heads.koff[gg];
-        int sh = 0, sl = 0;
-        for (int k = a.heads.n8[gg]; k < r; ++k) {
-          sh += hi8[tid][k];
-          sl += lo8[tid][k];
-        }
-        bh = (float)(8 * sh);
-        bl = (float)(8 * sl);
-      }
-      float* rp = a.rowp + ((size_t)b * g.M_pad + i) * 4;
-      rp[0] = LAT == STARKV_LATENT_MIX84 ? rho_s[tid] : 1.f;
-      rp[1] = bh;
-      rp[2] = bl;
-      rp[3] = 0.f;
-    }
-  }
-  // fragments
-  const int wave = wave_id(), lane = tid & 63;
-  const int n = lane & 15, qq = lane >> 4;
-  const int gg = seg_g[n];
-  const int nkt = a.kts.n[ct];
-  for (int jt = wave; jt < nkt; jt += 4) {
-    const int kt = a.kts.kt[ct][jt];
-    uint8_t* frag = a.qfrag + (((size_t)b * g.nct + ct) * a.nkt_max + jt) * 2048;
-    if (LAT == STARKV_LATENT_MIX84) {
-      const int P0 = kt * 64 + 16 * qq;
-      uint32_t wh[4] = {0, 0, 0, 0}, wl[4] = {0, 0, 0, 0};
-      if (gg >= 0 && P0 < g.K8 + g.K4) {
-        const int c0 = a.heads.koff[gg];
-        const int n8g = a.heads.n8[gg];
-        const int n4g = (a.heads.koff[gg + 1] - c0) - n8g;
-        const int o8 = a.heads.off8[gg], o4 = a.heads.off4[gg];
+      for (int n = wave; n < nrows; n += 4) {
+        float m = 0.f;
+        for (int k = lane; k < r; k += 64) m = fmaxf(m, fabsf(qh[n][k]));
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          int k = -1;
-          if (P0 < g.K8) {
-            const int slot = P0 + e;
-            if (slot >= o8 && slot < o8 + n8g) k = slot - o8;
+        for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+        if (lane == 0) rho_s[n] = m > 0.f ? m / 127.f : 1.f;
+      }
+      __syncthreads();
+      for (int idx = tid; idx < nrows * r; idx += 256) {
+        const int n = idx / r, k = idx % r;
+        const float rho = rho_s[n], x = qh[n][k];
+        const float hi = fminf(fmaxf(__builtin_rintf(x / rho), -127.f), 127.f);
+        const float lo = fminf(fmaxf(__builtin_rintf((x - hi * rho) * (254.f / rho)), -127.f), 127.f);
+        hi8[n][k] = (int8_t)hi;
+        lo8[n][k] = (int8_t)lo;
+      }
+      __syncthreads();
+    }
+    // row parameters: rho and the int4 offset-binary bias terms 8 * sum(int4 codes' weights)
+    for (int n = wave; n < nrows; n += 4) {
+      int sh = 0, sl = 0;
+      if (LAT == STARKV_LATENT_MIX84)
+        for (int k = n8g + lane; k < r; k += 64) {
+          sh += hi8[n][k];
+          sl += lo8[n][k];
+        }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        sh += __shfl_xor(sh, o, 64);
+        sl += __shfl_xor(sl, o, 64);
+      }
+      if (lane == 0) {
+        const int i = gk * rph + rb0 + n;
+        float* rp = a.rowp + ((size_t)b * g.M_pad + i) * 4;
+        rp[0] = LAT == STARKV_LATENT_MIX84 ? rho_s[n] : 1.f;
+        rp[1] = (float)(8 * sh);
+        rp[2] = (float)(8 * sl);
+        rp[3] = 0.f;
+      }
+    }
+    // fragment chunks of these rows: (row, K-tile, 16-position group qq)
+    for (int n = 0; n < nrows; ++n) {
+      const int i = gk * rph + rb0 + n;
+      const int ct = i >> 4, col = i & 15;
+      const int nkt = a.kts.n[ct];
+      for (int item = tid; item < nkt * 4; item += 256) {
+        const int jt = item >> 2, qq = item & 3;
+        const int kt = a.kts.kt[ct][jt];
+        const int ln = col + 16 * qq;  // fragment lane holding this chunk
+        uint8_t* frag = a.qfrag + (((size_t)b * g.nct + ct) * a.nkt_max + jt) * 2048;
+        if (LAT == STARKV_LATENT_MIX84) {
+          const int P0 = kt * 64 + 16 * qq;
+          uint32_t wh[4] = {0, 0, 0, 0}, wl[4] = {0, 0, 0, 0};
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            int k = -1;
+            if (P0 < g.K8) {
+              const int slot = P0 + e;
+              if (slot >= o8 && slot < o8 + n8g) k = slot - o8;
+            } else if (P0 < g.K8 + g.K4) {
+              const int u = P0 - g.K8 + int4_perm16(e);
+              if (u >= o4 && u < o4 + (r - n8g)) k = n8g + (u - o4);
+            }
+            if (k >= 0) {
+              wh[e >> 2] |= ((uint32_t)(uint8_t)hi8[n][k]) << (8 * (e & 3));
+              wl[e >> 2] |= ((uint32_t)(uint8_t)lo8[n][k]) << (8 * (e & 3));
+            }
+          }
+          st16(frag + ln * 16, u32x4{wh[0], wh[1], wh[2], wh[3]});
+          st16(frag + 1024 + ln * 16, u32x4{wl[0], wl[1], wl[2], wl[3]});
+        } else {
+          const int P0 = kt * 32 + 8 * qq;
+          float v[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int k = P0 + e - c0;
+            v[e] = (k >= 0 && k < r) ? qh[n][k] : 0.f;
+          }
+          if (LAT == STARKV_LATENT_F32) {
+            st16(frag + ln * 32, u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                                       __float_as_uint(v[3])});
+            st16(frag + ln * 32 + 16, u32x4{__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]),
+                                            __float_as_uint(v[7])});
           } else {
-            const int u = P0 - g.K8 + int4_perm16(e);
-            if (u >= o4 && u < o4 + n4g) k = n8g + (u - o4);
-          }
-          if (k >= 0) {
-            wh[e >> 2] |= ((uint32_t)(uint8_t)hi8[n][k]) << (8 * (e & 3));
-            wl[e >> 2] |= ((uint32_t)(uint8_t)lo8[n][k]) << (8 * (e & 3));
+            uint32_t wh[4], wl[4];
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+              const uint16_t h0 = f32_to_bf16(v[2 * e2]), h1 = f32_to_bf16(v[2 * e2 + 1]);
+              const uint16_t l0 = f32_to_bf16(v[2 * e2] - bf16_to_f32(h0));
+              const uint16_t l1 = f32_to_bf16(v[2 * e2 + 1] - bf16_to_f32(h1));
+              wh[e2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+              wl[e2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+            }
+            st16(frag + ln * 16, u32x4{wh[0], wh[1], wh[2], wh[3]});
+            st16(frag + 1024 + ln * 16, u32x4{wl[0], wl[1], wl[2], wl[3]});
           }
         }
       }
-      st16(frag + lane * 16, u32x4{wh[0], wh[1], wh[2], wh[3]});
-      st16(frag + 1024 + lane * 16, u32x4{wl[0], wl[1], wl[2], wl[3]});
-    } else {
-      const int P0 = kt * 32 + 8 * qq;
-      float v[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        v[e] = 0.f;
-        if (gg >= 0) {
-          const int k = P0 + e - a.heads.koff[gg];
-          const int r = a.heads.koff[gg + 1] - a.heads.koff[gg];
-          if (k >= 0 && k < r) v[e] = qh[n][k];
+    }
+  }
+  // the last head also zeroes the chunks of the padding rows of the last column tile
+  if (gk == g.H_kv - 1) {
+    for (int i = g.M_q; i < g.nct * 16; ++i) {
+      const int ct = i >> 4, col = i & 15;
+      const int nkt = a.kts.n[ct];
+      for (int item = tid; item < nkt * 4; item += 256) {
+        const int jt = item >> 2, qq = item & 3, ln = col + 16 * qq;
+        uint8_t* frag = a.qfrag + (((size_t)b * g.nct + ct) * a.nkt_max + jt) * 2048;
+        if (LAT == STARKV_LATENT_F32) {
+          st16(frag + ln * 32, u32x4{0, 0, 0, 0});
+          st16(frag + ln * 32 + 16, u32x4{0, 0, 0, 0});
+        } else {
+          st16(frag + ln * 16, u32x4{0, 0, 0, 0});
+          st16(frag + 1024 + ln * 16, u32x4{0, 0, 0, 0});
         }
-      }
-      if (LAT == STARKV_LATENT_F32) {
-        st16(frag + lane * 32, u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
-                                     __float_as_uint(v[3])});
-        st16(frag + lane * 32 + 16, u32x4{__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]),
-                                          __float_as_uint(v[7])});
-      } else {
-        uint32_t wh[4], wl[4];
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-          const uint16_t h0 = f32_to_bf16(v[2 * e2]), h1 = f32_to_bf16(v[2 * e2 + 1]);
-          const uint16_t l0 = f32_to_bf16(v[2 * e2] - bf16_to_f32(h0));
-          const uint16_t l1 = f32_to_bf16(v[2 * e2 + 1] - bf16_to_f32(h1));
-          wh[e2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-          wl[e2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
-        }
-        st16(frag + lane * 16, u32x4{wh[0], wh[1], wh[2], wh[3]});
-        st16(frag + 1024 + lane * 16, u32x4{wl[0], wl[1], wl[2], wl[3]});
       }
     }
   }
@@ -329,24 +378,34 @@ struct ScoreArgs {
   float* cl;
   DecodeGeom g;
   int nkt_max;
+  int nch_wg;        // 64-token chunks per workgroup
+  int total_chunks;
   KtList kts;
   SeqTable seq;
 };
 
+// Workgroup = 4 waves over `nch_wg` consecutive 64-token chunks (global chunk numbering, so a
+// workgroup may span sequences); work unit = (column tile ct, chunk).  Per unit the loop runs
+// K-tile outer / 16-token tile inner, so each query fragment is loaded once per unit.
+// Workgroup = 4 waves over `nch_wg` consecutive 32-token chunks (global chunk numbering, so a
+// workgroup may span sequences); work unit = (column tile ct, chunk) = 2 MFMA row tiles of 16
+// tokens.  Per unit the K-tiles are walked four at a time: the loads of four K-tiles (query
+// fragments and key rows) are issued before their MFMAs, to keep enough bytes in flight.
 template <int LAT>
 __global__ __launch_bounds__(256) void k_scores(ScoreArgs a) {
+  constexpr int KU = 4;  // K-tiles in flight
   const DecodeGeom& g = a.g;
-  const int cg = blockIdx.x;
-  const int b = find_segment(a.seq.chunk_off, g.B, cg);
-  const int c = cg - a.seq.chunk_off[b];
-  const int t0 = c * kTC;
-  const int len = a.seq.lens[b];
   const int lane = threadIdx.x & 63, wave = wave_id();
-  const int W = blockDim.x >> 6;
   const int n = lane & 15, qq = lane >> 4;
-  const uint8_t* kbase = a.k_rows + (size_t)b * g.T_max * g.k_row_bytes;
-
-  for (int ct = wave; ct < g.nct; ct += W) {
+  const int units = g.nct * a.nch_wg;
+  for (int u = wave; u < units; u += 4) {
+    const int ct = u % g.nct;
+    const int cg = blockIdx.x * a.nch_wg + u / g.nct;  // global chunk
+    if (cg >= a.total_chunks) break;
+    const int b = find_segment(a.seq.chunk_off, g.B, cg);
+    const int t0 = (cg - a.seq.chunk_off[b]) * kTC;
+    const int len = a.seq.lens[b];
+    const uint8_t* kbase = a.k_rows + (size_t)b * g.T_max * g.k_row_bytes;
     const int i = ct * 16 + n;  // query row of this lane's result column
     const bool rowvalid = i < g.M_q;
     const int pos = len - g.n_q + (i % g.n_q);
@@ -359,73 +418,116 @@ __global__ __launch_bounds__(256) void k_scores(ScoreArgs a) {
     }
     const int nkt = a.kts.n[ct];
     const uint8_t* fbase = a.qfrag + ((size_t)b * g.nct + ct) * a.nkt_max * 2048;
-    float s2[4][4];
+    const uint8_t* rowp[2];
+    bool tok_ok[2];
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      const int tok = t0 + tt * 16 + n;  // A-fragment row (token) of this lane
-      const bool tok_ok = tok < len;
-      const uint8_t* row = kbase + (size_t)(tok_ok ? tok : 0) * g.k_row_bytes;
-      if (LAT == STARKV_LATENT_MIX84) {
-        i32x4 ah = {0, 0, 0, 0}, al = {0, 0, 0, 0};
-        for (int jt = 0; jt < nkt; ++jt) {
-          const int kt = a.kts.kt[ct][jt];
-          const i32x4 fh = __builtin_bit_cast(i32x4, ld16(fbase + jt * 2048 + lane * 16));
-          const i32x4 fl = __builtin_bit_cast(i32x4, ld16(fbase + jt * 2048 + 1024 + lane * 16));
+    for (int tt = 0; tt < 2; ++tt) {
+      const int tok = t0 + tt * 16 + n;
+      tok_ok[tt] = tok < len;
+      rowp[tt] = kbase + (size_t)(tok_ok[tt] ? tok : 0) * g.k_row_bytes;
+    }
+    float s2[2][4];
+    if (LAT == STARKV_LATENT_MIX84) {
+      i32x4 ah[2], al[2];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) ah[tt] = al[tt] = i32x4{0, 0, 0, 0};
+      for (int jt0 = 0; jt0 < nkt; jt0 += KU) {
+        i32x4 fh[KU], fl[KU], av[KU][2];
+#pragma unroll
+        for (int j = 0; j < KU; ++j) {
+          const bool on = jt0 + j < nkt;
+          const int kt = on ? a.kts.kt[ct][jt0 + j] : 0;
           const int P0 = kt * 64 + 16 * qq;
-          i32x4 av = {0, 0, 0, 0};
-          if (tok_ok) {
-            if (P0 < g.K8) av = __builtin_bit_cast(i32x4, ld16(row + P0));
-            else if (P0 < g.K8 + g.K4) av = unpack_int4_group(ld8(row + g.K8 + (P0 - g.K8) / 2));
+          fh[j] = on ? __builtin_bit_cast(i32x4, ld16(fbase + (jt0 + j) * 2048 + lane * 16)) : i32x4{0, 0, 0, 0};
+          fl[j] = on ? __builtin_bit_cast(i32x4, ld16(fbase + (jt0 + j) * 2048 + 1024 + lane * 16)) : i32x4{0, 0, 0, 0};
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) {
+            i32x4 v = {0, 0, 0, 0};
+            if (on && tok_ok[tt]) {
+              if (P0 < g.K8) v = __builtin_bit_cast(i32x4, ld16(rowp[tt] + P0));
+              else if (P0 < g.K8 + g.K4) v = unpack_int4_group(ld8(rowp[tt] + g.K8 + (P0 - g.K8) / 2));
+            }
+            av[j][tt] = v;
           }
-          ah = mfma16_i8(av, fh, ah);
-          al = mfma16_i8(av, fl, al);
         }
+#pragma unroll
+        for (int j = 0; j < KU; ++j)
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) {
+            ah[tt] = mfma16_i8(av[j][tt], fh[j], ah[tt]);
+            al[tt] = mfma16_i8(av[j][tt], fl[j], al[tt]);
+          }
+      }
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int v = 0; v < 4; ++v)
-          s2[tt][v] = rho * (float)(ah[v] - (int)bh) + (rho * (1.f / 254.f)) * (float)(al[v] - (int)bl);
-      } else if (LAT == STARKV_LATENT_BF16) {
-        f32x4 acc = {0, 0, 0, 0};
-        for (int jt = 0; jt < nkt; ++jt) {
-          const int kt = a.kts.kt[ct][jt];
-          const u32x4 fh = ld16(fbase + jt * 2048 + lane * 16);
-          const u32x4 fl = ld16(fbase + jt * 2048 + 1024 + lane * 16);
+          s2[tt][v] = rho * (float)(ah[tt][v] - (int)bh) + (rho * (1.f / 254.f)) * (float)(al[tt][v] - (int)bl);
+    } else if (LAT == STARKV_LATENT_BF16) {
+      f32x4 acc[2];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) acc[tt] = f32x4{0, 0, 0, 0};
+      for (int jt0 = 0; jt0 < nkt; jt0 += KU) {
+        u32x4 fh[KU], fl[KU], av[KU][2];
+#pragma unroll
+        for (int j = 0; j < KU; ++j) {
+          const bool on = jt0 + j < nkt;
+          const int kt = on ? a.kts.kt[ct][jt0 + j] : 0;
           const int P0 = kt * 32 + 8 * qq;
-          u32x4 av = {0, 0, 0, 0};
-          if (tok_ok && P0 < g.key_kpos) av = ld16(row + 2 * P0);
-          acc = mfma16_bf16(as_bf16x8(av), as_bf16x8(fh), acc);
-          acc = mfma16_bf16(as_bf16x8(av), as_bf16x8(fl), acc);
+          fh[j] = on ? ld16(fbase + (jt0 + j) * 2048 + lane * 16) : u32x4{0, 0, 0, 0};
+          fl[j] = on ? ld16(fbase + (jt0 + j) * 2048 + 1024 + lane * 16) : u32x4{0, 0, 0, 0};
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt)
+            av[j][tt] = (on && tok_ok[tt] && P0 < g.key_kpos) ? ld16(rowp[tt] + 2 * P0) : u32x4{0, 0, 0, 0};
         }
 #pragma unroll
-        for (int v = 0; v < 4; ++v) s2[tt][v] = acc[v];
-      } else {
-        f32x4 acc = {0, 0, 0, 0};
-        for (int jt = 0; jt < nkt; ++jt) {
-          const int kt = a.kts.kt[ct][jt];
-          const u32x4 f0 = ld16(fbase + jt * 2048 + lane * 32);
-          const u32x4 f1 = ld16(fbase + jt * 2048 + lane * 32 + 16);
-          const int P0 = kt * 32 + 8 * qq;
-          u32x4 a0 = {0, 0, 0, 0}, a1 = {0, 0, 0, 0};
-          if (tok_ok && P0 < g.key_kpos) a0 = ld16(row + 4 * P0);
-          if (tok_ok && P0 + 4 < g.key_kpos) a1 = ld16(row + 4 * P0 + 16);
+        for (int j = 0; j < KU; ++j)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc = mfma16_f32(__uint_as_float(a0[e]), __uint_as_float(f0[e]), acc);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc = mfma16_f32(__uint_as_float(a1[e]), __uint_as_float(f1[e]), acc);
-        }
-#pragma unroll
-        for (int v = 0; v < 4; ++v) s2[tt][v] = acc[v];
+          for (int tt = 0; tt < 2; ++tt) {
+            acc[tt] = mfma16_bf16(as_bf16x8(av[j][tt]), as_bf16x8(fh[j]), acc[tt]);
+            acc[tt] = mfma16_bf16(as_bf16x8(av[j][tt]), as_bf16x8(fl[j]), acc[tt]);
+          }
       }
-      // lane holds D[token 4*qq + v][column n]
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) s2[tt][v] = acc[tt][v];
+    } else {
+      f32x4 acc[2];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) acc[tt] = f32x4{0, 0, 0, 0};
+      for (int jt = 0; jt < nkt; ++jt) {
+        const int kt = a.kts.kt[ct][jt];
+        const u32x4 f0 = ld16(fbase + jt * 2048 + lane * 32);
+        const u32x4 f1 = ld16(fbase + jt * 2048 + lane * 32 + 16);
+        const int P0 = kt * 32 + 8 * qq;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const u32x4 a0 = (tok_ok[tt] && P0 < g.key_kpos) ? ld16(rowp[tt] + 4 * P0) : u32x4{0, 0, 0, 0};
+          const u32x4 a1 = (tok_ok[tt] && P0 + 4 < g.key_kpos) ? ld16(rowp[tt] + 4 * P0 + 16) : u32x4{0, 0, 0, 0};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[tt] = mfma16_f32(__uint_as_float(a0[e]), __uint_as_float(f0[e]), acc[tt]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[tt] = mfma16_f32(__uint_as_float(a1[e]), __uint_as_float(f1[e]), acc[tt]);
+        }
+      }
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) s2[tt][v] = acc[tt][v];
+    }
+    // lane holds D[token 4*qq + v][column n] of each 16-token tile: mask, chunk max and sum
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int t = t0 + tt * 16 + 4 * qq + v;
         const bool ok = rowvalid && t < len && t <= pos;
         s2[tt][v] = ok ? s2[tt][v] : -INFINITY;
       }
-    }
     float m = -INFINITY;
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
+    for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int v = 0; v < 4; ++v) m = fmaxf(m, s2[tt][v]);
     m = wave_max_xor(m, 16);
@@ -433,7 +535,7 @@ __global__ __launch_bounds__(256) void k_scores(ScoreArgs a) {
     float l = 0.f;
     const size_t prow = ((size_t)cg * g.M_pad + i) * kTC;
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
+    for (int tt = 0; tt < 2; ++tt) {
       float e4[4];
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
@@ -477,6 +579,7 @@ struct ValueArgs {
   DecodeGeom g;
   SeqTable seq;
   int cps, bpw, NB, V8, n8v, n4v;
+  int n_sl8, nbw8, nbw4;  // one-M-tile kernel: slices of one-N-tile blocks, blocks per slice
 };
 
 // 8 tokens of one channel (int8 codes in 8 bytes) -> f16x8
@@ -500,8 +603,15 @@ __device__ __forceinline__ void deq_i4x8(uint32_t w0, uint32_t w1, f16x8& ev, f1
   }
 }
 
+// Workgroup = (slice of `bpw` value blocks, split of one sequence); wave = one value block
+// (32 byte-rows of the value tiles).  The split's 32-token tiles are walked U at a time: the
+// value rows, probabilities and chunk statistics of U tiles are loaded before their MFMAs.
 template <int LAT, int NMT>
 __global__ __launch_bounds__(256) void k_values(ValueArgs a) {
+  constexpr int U = (LAT == STARKV_LATENT_F32) ? 1 : (NMT >= 3 ? 1 : (NMT == 2 ? 2 : 4));
+  constexpr int esz = LAT == STARKV_LATENT_F32 ? 4 : (LAT == STARKV_LATENT_BF16 ? 2 : 1);
+  constexpr int NV = esz == 1 ? 1 : (esz == 2 ? 2 : 4);  // 16-byte value loads per lane per tile
+  constexpr int NP = LAT == STARKV_LATENT_F32 ? 2 : 1;   // 16-byte probability loads per lane per K-step
   const DecodeGeom& g = a.g;
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int nb = blockIdx.x * a.bpw + wave;  // value block of this wave (wave-uniform)
@@ -515,9 +625,8 @@ __global__ __launch_bounds__(256) void k_values(ValueArgs a) {
   const int len = a.seq.lens[b];
   const int r = lane & 31, q = lane >> 5;
   const bool is4 = (LAT == STARKV_LATENT_MIX84) && (nb >= a.V8 / 32);
-  constexpr int esz = LAT == STARKV_LATENT_F32 ? 4 : (LAT == STARKV_LATENT_BF16 ? 2 : 1);
 
-  // split max per row held by this lane (as an A-fragment row)
+  // split max of the rows this lane feeds as A-fragment rows
   float Ms[NMT], lsum[NMT];
 #pragma unroll
   for (int mt = 0; mt < NMT; ++mt) {
@@ -537,38 +646,51 @@ __global__ __launch_bounds__(256) void k_values(ValueArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[mt][nt][v] = 0.f;
 
-  const uint8_t* vb = a.v_tiles + (size_t)b * (g.T_max / kTT) * g.v_tile_bytes;
-  for (int c = c_lo; c < c_hi; ++c) {
-    const size_t cgl = (size_t)(cbase + c);
-    float alpha[NMT];
+  const uint8_t* vb = a.v_tiles + (size_t)b * (g.T_max / kTT) * g.v_tile_bytes + (size_t)(nb * 32 + r) * kTT * esz;
+  for (int c0 = c_lo; c0 < c_hi; c0 += U) {
+    u32x4 vr[U][NV];
+    u32x4 pr[U][NMT][2][NP];
+    float cmv[U][NMT], clv[U][NMT];
+    // ---- loads of U tiles
 #pragma unroll
-    for (int mt = 0; mt < NMT; ++mt) {
-      const int row = mt * 32 + r;
-      float al = 0.f;
-      if (row < g.M_q) {
-        const float m = a.cm[cgl * g.M_pad + row];
-        if (m != -INFINITY) al = __builtin_amdgcn_exp2f(m - Ms[mt]);
-        lsum[mt] += al * a.cl[cgl * g.M_pad + row];
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + u;
+      const bool on = c < c_hi;  // uniform
+      const size_t cgl = (size_t)(cbase + (on ? c : c_lo));
+      const uint8_t* trow = vb + (size_t)(on ? c : c_lo) * g.v_tile_bytes;
+#pragma unroll
+      for (int k = 0; k < NV; ++k) vr[u][k] = on ? ld16(trow + 16 * NV * q + 16 * k) : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt) {
+        const int row = mt * 32 + r;
+        const bool rok = on && row < g.M_q;
+        cmv[u][mt] = rok ? a.cm[cgl * g.M_pad + row] : -INFINITY;
+        clv[u][mt] = rok ? a.cl[cgl * g.M_pad + row] : 0.f;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int k = 0; k < NP; ++k) {
+            const size_t pe = (cgl * g.M_pad + row) * kTC + 16 * q + 8 * h + 4 * k;
+            pr[u][mt][h][k] = rok ? (LAT == STARKV_LATENT_F32 ? ld16((const float*)a.p + pe)
+                                                              : ld16((const uint16_t*)a.p + pe))
+                                  : u32x4{0, 0, 0, 0};
+          }
       }
-      alpha[mt] = al;
     }
+    // ---- compute
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int tt0 = c * kTC + half * 32;
-      if (tt0 >= len) break;
-      const uint8_t* trow = vb + (size_t)(tt0 / kTT) * g.v_tile_bytes + (size_t)(nb * 32 + r) * kTT * esz;
-      // this lane's 16 tokens: tt0 + 16q .. +15
-      u32x4 vraw[4];
-      if (esz == 1) {
-        vraw[0] = ld16(trow + 16 * q);
-      } else if (esz == 2) {
-        vraw[0] = ld16(trow + 32 * q);
-        vraw[1] = ld16(trow + 32 * q + 16);
-      } else {
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + u;
+      if (c >= c_hi) break;
+      const int tt0 = c * kTC;
+      float alpha[NMT];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) vraw[k] = ld16(trow + 64 * q + 16 * k);
+      for (int mt = 0; mt < NMT; ++mt) {
+        const float m = cmv[u][mt];
+        alpha[mt] = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - Ms[mt]);
+        lsum[mt] += alpha[mt] * clv[u][mt];
       }
-      if (esz > 1 && tt0 + 32 > len) {
+      if (esz > 1 && tt0 + kTT > len) {
         // zero the elements of tokens at or past the length (their bits may be anything)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
@@ -576,62 +698,50 @@ __global__ __launch_bounds__(256) void k_values(ValueArgs a) {
           if (t >= len) {
             if (esz == 2) {
               const uint32_t keep = (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
-              vraw[e >> 3][(e >> 1) & 3] = vraw[e >> 3][(e >> 1) & 3] & keep;
+              vr[u][e >> 3][(e >> 1) & 3] = vr[u][e >> 3][(e >> 1) & 3] & keep;
             } else {
-              vraw[e >> 2][e & 3] = 0u;
+              vr[u][e >> 2][e & 3] = 0u;
             }
           }
         }
       }
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const int tk = 32 * half + 16 * q + 8 * h;  // token offset inside the chunk
         // value fragments of this K-step (8 tokens of one channel, or of a channel pair)
         f16x8 v_lo, v_hi;
         if (LAT == STARKV_LATENT_MIX84) {
-          const uint32_t w0 = vraw[0][2 * h], w1 = vraw[0][2 * h + 1];
+          const uint32_t w0 = vr[u][0][2 * h], w1 = vr[u][0][2 * h + 1];
           if (is4) deq_i4x8(w0, w1, v_lo, v_hi);
           else v_lo = deq_i8x8(w0, w1);
         }
 #pragma unroll
         for (int mt = 0; mt < NMT; ++mt) {
-          const int row = mt * 32 + r;
-          const bool rok = row < g.M_q;
           if (LAT == STARKV_LATENT_F32) {
-            const float* pp = (const float*)a.p + (cgl * g.M_pad + row) * kTC + tk;
-            u32x4 p0 = {0, 0, 0, 0}, p1 = {0, 0, 0, 0};
-            if (rok) {
-              p0 = ld16(pp);
-              p1 = ld16(pp + 4);
-            }
-            const u32x4 v0 = vraw[2 * h], v1 = vraw[2 * h + 1];
+            const u32x4 p0 = pr[u][mt][h][0], p1 = pr[u][mt][h][NP - 1];
+            const u32x4 v0 = vr[u][2 * h], v1 = vr[u][2 * h + 1];
 #pragma unroll
             for (int e = 0; e < 4; ++e)
               acc[mt][0] = mfma32_f32(__uint_as_float(p0[e]) * alpha[mt], __uint_as_float(v0[e]), acc[mt][0]);
 #pragma unroll
             for (int e = 0; e < 4; ++e)
               acc[mt][0] = mfma32_f32(__uint_as_float(p1[e]) * alpha[mt], __uint_as_float(v1[e]), acc[mt][0]);
-          } else {
-            const uint16_t* pp = (const uint16_t*)a.p + (cgl * g.M_pad + row) * kTC + tk;
-            u32x4 praw = {0, 0, 0, 0};
-            if (rok) praw = ld16(pp);
-            if (LAT == STARKV_LATENT_BF16) {
-              u32x4 ps;
+          } else if (LAT == STARKV_LATENT_BF16) {
+            const u32x4 praw = pr[u][mt][h][0];
+            u32x4 ps;
 #pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const float x0 = bf16_to_f32((uint16_t)(praw[e] & 0xFFFF)) * alpha[mt];
-                const float x1 = bf16_to_f32((uint16_t)(praw[e] >> 16)) * alpha[mt];
-                ps[e] = (uint32_t)f32_to_bf16(x0) | ((uint32_t)f32_to_bf16(x1) << 16);
-              }
-              acc[mt][0] = mfma32_bf16(as_bf16x8(ps), as_bf16x8(vraw[h]), acc[mt][0]);
-            } else {
-              f16x8 ps;
-              const f16x8 pin = as_f16x8(praw);
-#pragma unroll
-              for (int e = 0; e < 8; ++e) ps[e] = (_Float16)((float)pin[e] * alpha[mt]);
-              acc[mt][0] = mfma32_f16(ps, v_lo, acc[mt][0]);
-              if (is4) acc[mt][1] = mfma32_f16(ps, v_hi, acc[mt][1]);
+            for (int e = 0; e < 4; ++e) {
+              const float x0 = bf16_to_f32((uint16_t)(praw[e] & 0xFFFF)) * alpha[mt];
+              const float x1 = bf16_to_f32((uint16_t)(praw[e] >> 16)) * alpha[mt];
+              ps[e] = (uint32_t)f32_to_bf16(x0) | ((uint32_t)f32_to_bf16(x1) << 16);
             }
+            acc[mt][0] = mfma32_bf16(as_bf16x8(ps), as_bf16x8(vr[u][h]), acc[mt][0]);
+          } else {
+            const f16x8 pin = as_f16x8(pr[u][mt][h][0]);
+            f16x8 ps;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ps[e] = (_Float16)((float)pin[e] * alpha[mt]);
+            acc[mt][0] = mfma32_f16(ps, v_lo, acc[mt][0]);
+            if (is4) acc[mt][1] = mfma32_f16(ps, v_hi, acc[mt][1]);
           }
         }
       }
@@ -679,6 +789,206 @@ __global__ __launch_bounds__(256) void k_values(ValueArgs a) {
   }
 }
 
+// One M-tile (at most 32 query rows per sequence): workgroup = (slice of value blocks of one
+// kind, split of one sequence); the four waves take interleaved 32-token tiles of the split and
+// each covers every block of the slice, so a probability fragment feeds up to four N-tiles.
+// The waves' accumulators and softmax sums are added through LDS at the end.
+// Slices [0, n_sl8) hold blocks of one N-tile (int8, bf16 or fp32 rows), slices [n_sl8, ...)
+// int4 blocks (two N-tiles each: even and odd channels of the byte pairs).
+template <int LAT>
+__global__ __launch_bounds__(256) void k_values1(ValueArgs a) {
+  constexpr int esz = LAT == STARKV_LATENT_F32 ? 4 : (LAT == STARKV_LATENT_BF16 ? 2 : 1);
+  constexpr int NV = esz == 1 ? 1 : (esz == 2 ? 2 : 4);
+  constexpr int NP = LAT == STARKV_LATENT_F32 ? 2 : 1;
+  constexpr int U = LAT == STARKV_LATENT_F32 ? 1 : (LAT == STARKV_LATENT_BF16 ? 2 : 4);
+  constexpr int NBMAX = 4;
+  __shared__ float sred[3][4][16][64];
+  __shared__ float smax[4][32];
+  __shared__ float ssum[4][32];
+  const DecodeGeom& g = a.g;
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int r = lane & 31, q = lane >> 5;
+  const int slice = blockIdx.x;
+  const bool is4 = (LAT == STARKV_LATENT_MIX84) && slice >= a.n_sl8;  // workgroup-uniform
+  int nb0, nb_end;
+  if (!is4) {
+    nb0 = slice * a.nbw8;
+    nb_end = min(nb0 + a.nbw8, LAT == STARKV_LATENT_MIX84 ? a.V8 / 32 : a.NB);
+  } else {
+    nb0 = a.V8 / 32 + (slice - a.n_sl8) * a.nbw4;
+    nb_end = min(nb0 + a.nbw4, a.NB);
+  }
+  const int nblk = nb_end - nb0;
+  const int sg = blockIdx.y;
+  const int b = find_segment(a.seq.split_off, g.B, sg);
+  const int s = sg - a.seq.split_off[b];
+  const int cbase = a.seq.chunk_off[b];
+  const int nch = a.seq.chunk_off[b + 1] - cbase;
+  const int c_lo = s * a.cps, c_hi = min(c_lo + a.cps, nch);
+  const int len = a.seq.lens[b];
+  const bool rok = r < g.M_q;
+
+  // split max of row r, shared by the waves
+  float m = -INFINITY;
+  if (rok)
+    for (int c = c_lo + wave; c < c_hi; c += 4) m = fmaxf(m, a.cm[(size_t)(cbase + c) * g.M_pad + r]);
+  if (q == 0) smax[wave][r] = m;
+  __syncthreads();
+  const float Ms = fmaxf(fmaxf(smax[0][r], smax[1][r]), fmaxf(smax[2][r], smax[3][r]));
+  float lsum = 0.f;
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[t][v] = 0.f;
+
+  const uint8_t* vb = a.v_tiles + (size_t)b * (g.T_max / kTT) * g.v_tile_bytes;
+  for (int c0 = c_lo + wave; c0 < c_hi; c0 += 4 * U) {
+    u32x4 vr[U][NBMAX][NV];
+    u32x4 pr[U][2][NP];
+    float cmv[U], clv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + 4 * u;
+      const bool on = c < c_hi;  // wave-uniform
+      const int cc = on ? c : c_lo;
+      const size_t cgl = (size_t)(cbase + cc);
+#pragma unroll
+      for (int j = 0; j < NBMAX; ++j) {
+        const bool bon = on && j < nblk;
+        const uint8_t* trow = vb + (size_t)cc * g.v_tile_bytes + (size_t)((nb0 + (bon ? j : 0)) * 32 + r) * kTT * esz;
+#pragma unroll
+        for (int k = 0; k < NV; ++k) vr[u][j][k] = bon ? ld16(trow + 16 * NV * q + 16 * k) : u32x4{0, 0, 0, 0};
+      }
+      const bool pon = on && rok;
+      cmv[u] = pon ? a.cm[cgl * g.M_pad + r] : -INFINITY;
+      clv[u] = pon ? a.cl[cgl * g.M_pad + r] : 0.f;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int k = 0; k < NP; ++k) {
+          const size_t pe = (cgl * g.M_pad + r) * kTC + 16 * q + 8 * h + 4 * k;
+          pr[u][h][k] = pon ? (LAT == STARKV_LATENT_F32 ? ld16((const float*)a.p + pe) : ld16((const uint16_t*)a.p + pe))
+                            : u32x4{0, 0, 0, 0};
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + 4 * u;
+      if (c >= c_hi) break;
+      const int tt0 = c * kTC;
+      const float alpha = (cmv[u] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(cmv[u] - Ms);
+      lsum += alpha * clv[u];
+      if (esz > 1 && tt0 + kTT > len) {
+#pragma unroll
+        for (int j = 0; j < NBMAX; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int t = tt0 + 16 * q + e;
+            if (t >= len) {
+              if (esz == 2) {
+                const uint32_t keep = (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+                vr[u][j][e >> 3][(e >> 1) & 3] = vr[u][j][e >> 3][(e >> 1) & 3] & keep;
+              } else {
+                vr[u][j][e >> 2][e & 3] = 0u;
+              }
+            }
+          }
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (LAT == STARKV_LATENT_F32) {
+          const u32x4 p0 = pr[u][h][0], p1 = pr[u][h][NP - 1];
+#pragma unroll
+          for (int j = 0; j < NBMAX; ++j) {
+            if (j >= nblk) continue;
+            const u32x4 v0 = vr[u][j][2 * h], v1 = vr[u][j][2 * h + 1];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              acc[j] = mfma32_f32(__uint_as_float(p0[e]) * alpha, __uint_as_float(v0[e]), acc[j]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              acc[j] = mfma32_f32(__uint_as_float(p1[e]) * alpha, __uint_as_float(v1[e]), acc[j]);
+          }
+        } else if (LAT == STARKV_LATENT_BF16) {
+          const u32x4 praw = pr[u][h][0];
+          u32x4 ps;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float x0 = bf16_to_f32((uint16_t)(praw[e] & 0xFFFF)) * alpha;
+            const float x1 = bf16_to_f32((uint16_t)(praw[e] >> 16)) * alpha;
+            ps[e] = (uint32_t)f32_to_bf16(x0) | ((uint32_t)f32_to_bf16(x1) << 16);
+          }
+#pragma unroll
+          for (int j = 0; j < NBMAX; ++j) {
+            if (j >= nblk) continue;
+            acc[j] = mfma32_bf16(as_bf16x8(ps), as_bf16x8(vr[u][j][h]), acc[j]);
+          }
+        } else {
+          const f16x8 pin = as_f16x8(pr[u][h][0]);
+          f16x8 ps;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ps[e] = (_Float16)((float)pin[e] * alpha);
+          if (!is4) {
+#pragma unroll
+            for (int j = 0; j < NBMAX; ++j) {
+              if (j >= nblk) continue;
+              acc[j] = mfma32_f16(ps, deq_i8x8(vr[u][j][0][2 * h], vr[u][j][0][2 * h + 1]), acc[j]);
+            }
+          } else {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              if (j >= nblk) continue;
+              f16x8 ev, od;
+              deq_i4x8(vr[u][j][0][2 * h], vr[u][j][0][2 * h + 1], ev, od);
+              acc[2 * j] = mfma32_f16(ps, ev, acc[2 * j]);
+              acc[2 * j + 1] = mfma32_f16(ps, od, acc[2 * j + 1]);
+            }
+          }
+        }
+      }
+    }
+  }
+  // add the four waves' accumulators and sums
+  const int ntile = is4 ? 2 * nblk : nblk;
+  if (wave > 0) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if (t >= ntile) continue;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) sred[wave - 1][t][v][lane] = acc[t][v];
+    }
+  }
+  if (q == 0) ssum[wave][r] = lsum;
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    if (t >= ntile) continue;
+    int vc;
+    bool cok;
+    if (!is4) {
+      vc = (nb0 + t) * 32 + r;
+      cok = vc < (LAT == STARKV_LATENT_MIX84 ? a.n8v : g.r_v);
+    } else {
+      const int w = 2 * ((nb0 + t / 2 - a.V8 / 32) * 32 + r) + (t & 1);
+      cok = w < a.n4v;
+      vc = a.n8v + w;
+    }
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const float z = acc[t][v] + sred[0][t][v][lane] + sred[1][t][v][lane] + sred[2][t][v][lane];
+      const int row = d32_row(v, q);
+      if (cok && row < g.M_q) a.zp[((size_t)sg * g.M_pad + row) * g.r_v + vc] = z;
+    }
+  }
+  if (slice == 0 && q == 0 && rok) {
+    a.sm[(size_t)sg * g.M_pad + r] = Ms;
+    a.sl[(size_t)sg * g.M_pad + r] = ssum[0][r] + ssum[1][r] + ssum[2][r] + ssum[3][r];
+  }
+}
+
 // ===========================================================================
 // merge + up-projection: out = (sum_s w_s z_s) * scale_v B_v^g / l
 
@@ -686,6 +996,7 @@ struct MergeArgs {
   const float* zp;
   const float* sm;
   const float* sl;
+  float* zt;                // [B][M_pad][r_v] merged, scaled, normalised value latent
   const void* B_vt;
   const uint16_t* vscales;  // value-channel scales (mix84) or null
   void* out;
@@ -693,120 +1004,151 @@ struct MergeArgs {
   SeqTable seq;
 };
 
-template <int DT>
-__global__ __launch_bounds__(256) void k_merge(MergeArgs a) {
+// Split merge (log-sum-exp): for sequence b and row i, M = max_s m_s, w_s = 2^(m_s - M),
+// l = sum_s w_s l_s, and z~[c] = (sum_s w_s z_s[c]) * scale_c / l.  Workgroup = 4 rows x 64
+// channels of one sequence; one thread per (row, channel).
+__global__ __launch_bounds__(256) void k_zmerge(MergeArgs a) {
   const DecodeGeom& g = a.g;
-  const int gk = blockIdx.x;  // KV head
+  __shared__ float wts[4][kMaxSplitsPerSeq];
+  __shared__ float invl[4];
+  const int b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int rn = tid >> 6, cn = tid & 63;
+  const int i = blockIdx.y * 4 + rn;
+  const int c = blockIdx.x * 64 + cn;
+  const int s0 = a.seq.split_off[b], ns = a.seq.split_off[b + 1] - s0;
+  if (cn == 0) {
+    float il = 0.f;
+    if (i < g.M_q) {
+      float M = -INFINITY;
+      for (int s = 0; s < ns; ++s) M = fmaxf(M, a.sm[(size_t)(s0 + s) * g.M_pad + i]);
+      float l = 0.f;
+      for (int s = 0; s < ns; ++s) {
+        const float ms = a.sm[(size_t)(s0 + s) * g.M_pad + i];
+        const float wgt = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+        wts[rn][s] = wgt;
+        l += wgt * a.sl[(size_t)(s0 + s) * g.M_pad + i];
+      }
+      il = 1.f / l;
+    }
+    invl[rn] = il;
+  }
+  __syncthreads();
+  if (i >= g.M_q || c >= g.r_v) return;
+  float z = 0.f;
+  for (int s = 0; s < ns; ++s) z = fmaf(wts[rn][s], a.zp[((size_t)(s0 + s) * g.M_pad + i) * g.r_v + c], z);
+  float sc = invl[rn];
+  if (a.vscales) sc *= f16_to_f32(a.vscales[c]);
+  a.zt[((size_t)b * g.M_pad + i) * g.r_v + c] = z * sc;
+}
+
+// Up-projection out_i = z~_i B_v^g for the rows of KV head g.  Workgroup = (g, 32-column slice
+// of d_h, 16-row tile of g's rows over all sequences); the four waves split K = r_v and their
+// partial outputs are added through LDS.  bf16: z~ split into hi + lo bf16 parts (two MFMAs).
+template <int DT>
+__global__ __launch_bounds__(256) void k_upproj(MergeArgs a) {
+  const DecodeGeom& g = a.g;
+  const int nsl_n = g.d_h / 32;
+  const int gk = blockIdx.x / nsl_n, nsl = blockIdx.x % nsl_n;
   const int rph = g.G * g.n_q;
   const int Rg = g.B * rph;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
-  __shared__ float wts[16][kMaxSplitsPerSeq];
-  __shared__ float invl[16];
-  __shared__ int rb[16], ri[16];
-  __shared__ float zf[16][33];
-  __shared__ uint16_t zh[16][40], zl[16][40];
-  if (tid < 16) {
-    const int rr = blockIdx.y * 16 + tid;
-    int bb = -1, ii = 0;
-    if (rr < Rg) {
-      bb = rr / rph;
-      ii = gk * rph + rr % rph;
-    }
-    rb[tid] = bb;
-    ri[tid] = ii;
-    if (bb >= 0) {
-      const int s0 = a.seq.split_off[bb], ns = a.seq.split_off[bb + 1] - s0;
-      float M = -INFINITY;
-      for (int s = 0; s < ns; ++s) M = fmaxf(M, a.sm[(size_t)(s0 + s) * g.M_pad + ii]);
-      float l = 0.f;
-      for (int s = 0; s < ns; ++s) {
-        const float ms = a.sm[(size_t)(s0 + s) * g.M_pad + ii];
-        const float w = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms - M);
-        wts[tid][s] = w;
-        l += w * a.sl[(size_t)(s0 + s) * g.M_pad + ii];
+  const int n = lane & 15, qq = lane >> 4;
+  __shared__ float red[3][2][4][64];
+  const int rr = blockIdx.y * 16 + n;  // A-fragment row of this lane
+  const bool rv = rr < Rg;
+  const int bb = rv ? rr / rph : 0;
+  const int ii = gk * rph + (rv ? rr % rph : 0);
+  const float* zr = a.zt + ((size_t)bb * g.M_pad + ii) * g.r_v;
+  const bool vec = (g.r_v & 7) == 0;
+  const int nch = (g.r_v + 31) / 32;
+  const int per = (nch + 3) / 4;
+  const int k_beg = wave * per * 32, k_end = min(g.r_v, (wave + 1) * per * 32);
+  f32x4 acc[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
+  for (int kc = k_beg; kc < k_end; kc += 32) {
+    const int c = kc + 8 * qq;
+    float z[8];
+    if (rv && vec && c + 8 <= g.r_v) {
+      const u32x4 v0 = ld16(zr + c), v1 = ld16(zr + c + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        z[e] = __uint_as_float(v0[e]);
+        z[4 + e] = __uint_as_float(v1[e]);
       }
-      invl[tid] = 1.f / l;
     } else {
-      invl[tid] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) z[e] = (rv && c + e < g.r_v) ? zr[c + e] : 0.f;
     }
+    u32x4 ah, al;
+    if (DT != STARKV_F32) {
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const uint16_t h0 = f32_to_bf16(z[2 * e2]), h1 = f32_to_bf16(z[2 * e2 + 1]);
+        const uint16_t l0 = f32_to_bf16(z[2 * e2] - bf16_to_f32(h0));
+        const uint16_t l1 = f32_to_bf16(z[2 * e2 + 1] - bf16_to_f32(h1));
+        ah[e2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        al[e2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int col = gk * g.d_h + (2 * nsl + t) * 16 + n;  // B_v^T row
+      if (DT == STARKV_F32) {
+        const float* bp = (const float*)a.B_vt + (size_t)col * g.r_v;
+        float bv[8];
+        if (vec && c + 8 <= g.r_v) {
+          const u32x4 v0 = ld16(bp + c), v1 = ld16(bp + c + 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            bv[e] = __uint_as_float(v0[e]);
+            bv[4 + e] = __uint_as_float(v1[e]);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) bv[e] = (c + e < g.r_v) ? bp[c + e] : 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[t] = mfma16_f32(z[e], bv[e], acc[t]);
+      } else {
+        const uint16_t* bp = (const uint16_t*)a.B_vt + (size_t)col * g.r_v;
+        u32x4 bw;
+        if (vec && c + 8 <= g.r_v) {
+          bw = ld16(bp + c);
+        } else {
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2) {
+            const uint32_t b0 = (c + 2 * e2 < g.r_v) ? bp[c + 2 * e2] : 0u;
+            const uint32_t b1 = (c + 2 * e2 + 1 < g.r_v) ? bp[c + 2 * e2 + 1] : 0u;
+            bw[e2] = b0 | (b1 << 16);
+          }
+        }
+        acc[t] = mfma16_bf16(as_bf16x8(ah), as_bf16x8(bw), acc[t]);
+        acc[t] = mfma16_bf16(as_bf16x8(al), as_bf16x8(bw), acc[t]);
+      }
+    }
+  }
+  if (wave > 0) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) red[wave - 1][t][v][lane] = acc[t][v];
   }
   __syncthreads();
-  const int n_nt = g.d_h / 16;
-  f32x4 acc[4];
+  if (wave != 0) return;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) acc[k] = f32x4{0, 0, 0, 0};
-  const int n = lane & 15, qq = lane >> 4;
-  for (int kc = 0; kc < g.r_v; kc += 32) {
-    // merged, scaled, normalised value latent tile [16 rows][32 channels]
-    for (int idx = tid; idx < 16 * 32; idx += 256) {
-      const int rr = idx >> 5, cc = idx & 31;
-      const int bb = rb[rr];
-      float z = 0.f;
-      if (bb >= 0 && kc + cc < g.r_v) {
-        const int s0 = a.seq.split_off[bb], ns = a.seq.split_off[bb + 1] - s0;
-        for (int s = 0; s < ns; ++s) z += wts[rr][s] * a.zp[((size_t)(s0 + s) * g.M_pad + ri[rr]) * g.r_v + kc + cc];
-        if (a.vscales) z *= f16_to_f32(a.vscales[kc + cc]);
-        z *= invl[rr];
-      }
-      if (DT == STARKV_F32) {
-        zf[rr][cc] = z;
-      } else {
-        const uint16_t hb = f32_to_bf16(z);
-        zh[rr][cc] = hb;
-        zl[rr][cc] = f32_to_bf16(z - bf16_to_f32(hb));
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int nt = wave + 4 * k;
-      if (nt >= n_nt) break;
-      const size_t brow = (size_t)(gk * g.d_h + nt * 16 + n) * g.r_v;
-      if (DT == STARKV_F32) {
-        const float* bp = (const float*)a.B_vt + brow;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int cch = kc + 8 * qq + e;
-          const float bv = (cch < g.r_v) ? bp[cch] : 0.f;
-          acc[k] = mfma16_f32(zf[n][8 * qq + e], bv, acc[k]);
-        }
-      } else {
-        const uint16_t* bp = (const uint16_t*)a.B_vt + brow;
-        uint32_t bw[4], ah[4], al[4];
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-          const int c0 = kc + 8 * qq + 2 * e2;
-          const uint32_t b0 = (c0 < g.r_v) ? bp[c0] : 0u;
-          const uint32_t b1 = (c0 + 1 < g.r_v) ? bp[c0 + 1] : 0u;
-          bw[e2] = b0 | (b1 << 16);
-          ah[e2] = (uint32_t)zh[n][8 * qq + 2 * e2] | ((uint32_t)zh[n][8 * qq + 2 * e2 + 1] << 16);
-          al[e2] = (uint32_t)zl[n][8 * qq + 2 * e2] | ((uint32_t)zl[n][8 * qq + 2 * e2 + 1] << 16);
-        }
-        const bf16x8 B8 = as_bf16x8(u32x4{bw[0], bw[1], bw[2], bw[3]});
-        acc[k] = mfma16_bf16(as_bf16x8(u32x4{ah[0], ah[1], ah[2], ah[3]}), B8, acc[k]);
-        acc[k] = mfma16_bf16(as_bf16x8(u32x4{al[0], al[1], al[2], al[3]}), B8, acc[k]);
-      }
-    }
-    __syncthreads();
-  }
-  // lane holds D[row 4*qq + v][col n] of each N-tile
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int nt = wave + 4 * k;
-    if (nt >= n_nt) break;
+  for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const int rr = 4 * qq + v;
-      const int bb = rb[rr];
-      if (bb < 0) continue;
-      const int ii = ri[rr] - gk * rph;
-      const int hh = ii / g.n_q, j = ii % g.n_q;
+      const float o = acc[t][v] + red[0][t][v][lane] + red[1][t][v][lane] + red[2][t][v][lane];
+      const int orow = blockIdx.y * 16 + 4 * qq + v;  // D row = row within the tile; D column = n
+      if (orow >= Rg) continue;
+      const int ob = orow / rph, iw = orow % rph;
+      const int hh = iw / g.n_q, j = iw % g.n_q;
       const int h = gk * g.G + hh;
-      const size_t o = (((size_t)bb * g.n_q + j) * g.H_q + h) * g.d_h + nt * 16 + n;
-      if (DT == STARKV_F32) ((float*)a.out)[o] = acc[k][v];
-      else ((uint16_t*)a.out)[o] = f32_to_bf16(acc[k][v]);
+      const size_t off = (((size_t)ob * g.n_q + j) * g.H_q + h) * g.d_h + (2 * nsl + t) * 16 + n;
+      if (DT == STARKV_F32) ((float*)a.out)[off] = o;
+      else ((uint16_t*)a.out)[off] = f32_to_bf16(o);
     }
-  }
 }
 
 // ===========================================================================
@@ -840,7 +1182,7 @@ hipError_t launch_decode(const Layer& L, const DecodePlan& plan, const KtList& k
   qa.g = g;
   qa.nkt_max = w.nkt_max;
   qa.kts = kts;
-  dim3 gq(g.nct, g.B);
+  dim3 gq(g.H_kv, g.B);
   {
   ProfScope ps("decode_qproj", s);
   if (L.dtype == STARKV_F32) {
@@ -863,15 +1205,18 @@ hipError_t launch_decode(const Layer& L, const DecodePlan& plan, const KtList& k
   sa.nkt_max = w.nkt_max;
   sa.kts = kts;
   sa.seq = seq;
-  const int W = std::min(g.nct, 4);
+  // enough chunks per workgroup that every one of its 4 waves has a (column tile, chunk) unit
+  sa.nch_wg = std::max(1, 4 / std::min(g.nct, 4));
+  sa.total_chunks = w.total_chunks;
+  const int n_wg = (w.total_chunks + sa.nch_wg - 1) / sa.nch_wg;
   {
   ProfScope ps("decode_scores", s);
   if (L.latent == STARKV_LATENT_MIX84)
-    hipLaunchKernelGGL(k_scores<STARKV_LATENT_MIX84>, dim3(w.total_chunks), dim3(64 * W), 0, s, sa);
+    hipLaunchKernelGGL(k_scores<STARKV_LATENT_MIX84>, dim3(n_wg), dim3(256), 0, s, sa);
   else if (L.latent == STARKV_LATENT_BF16)
-    hipLaunchKernelGGL(k_scores<STARKV_LATENT_BF16>, dim3(w.total_chunks), dim3(64 * W), 0, s, sa);
+    hipLaunchKernelGGL(k_scores<STARKV_LATENT_BF16>, dim3(n_wg), dim3(256), 0, s, sa);
   else
-    hipLaunchKernelGGL(k_scores<STARKV_LATENT_F32>, dim3(w.total_chunks), dim3(64 * W), 0, s, sa);
+    hipLaunchKernelGGL(k_scores<STARKV_LATENT_F32>, dim3(n_wg), dim3(256), 0, s, sa);
   }
   // 3. values
   ValueArgs va;
@@ -890,31 +1235,47 @@ hipError_t launch_decode(const Layer& L, const DecodePlan& plan, const KtList& k
   va.V8 = L.V8;
   va.n8v = L.n8v;
   va.n4v = L.n4v;
+  va.n_sl8 = w.n_sl8;
+  va.nbw8 = w.nbw8;
+  va.nbw4 = w.nbw4;
   const int nmt = g.M_pad / 32;
-  dim3 gv((va.NB + va.bpw - 1) / va.bpw, w.total_splits);
-  dim3 bv(64 * va.bpw);
   {
   ProfScope ps("decode_values", s);
-  if (L.latent == STARKV_LATENT_MIX84) launch_values_nmt<STARKV_LATENT_MIX84>(nmt, gv, bv, s, va);
-  else if (L.latent == STARKV_LATENT_BF16) launch_values_nmt<STARKV_LATENT_BF16>(nmt, gv, bv, s, va);
-  else launch_values_nmt<STARKV_LATENT_F32>(nmt, gv, bv, s, va);
+  if (nmt == 1) {
+    dim3 gv(w.n_sl8 + w.n_sl4, w.total_splits);
+    if (L.latent == STARKV_LATENT_MIX84) hipLaunchKernelGGL(k_values1<STARKV_LATENT_MIX84>, gv, dim3(256), 0, s, va);
+    else if (L.latent == STARKV_LATENT_BF16) hipLaunchKernelGGL(k_values1<STARKV_LATENT_BF16>, gv, dim3(256), 0, s, va);
+    else hipLaunchKernelGGL(k_values1<STARKV_LATENT_F32>, gv, dim3(256), 0, s, va);
+  } else {
+    dim3 gv((va.NB + va.bpw - 1) / va.bpw, w.total_splits);
+    dim3 bv(64 * va.bpw);
+    if (L.latent == STARKV_LATENT_MIX84) launch_values_nmt<STARKV_LATENT_MIX84>(nmt, gv, bv, s, va);
+    else if (L.latent == STARKV_LATENT_BF16) launch_values_nmt<STARKV_LATENT_BF16>(nmt, gv, bv, s, va);
+    else launch_values_nmt<STARKV_LATENT_F32>(nmt, gv, bv, s, va);
+  }
   }
   // 4. merge + up-projection
   MergeArgs ma;
   ma.zp = w.zp;
   ma.sm = w.sm;
   ma.sl = w.sl;
+  ma.zt = w.zt;
   ma.B_vt = L.B_vt;
   ma.vscales = L.mix() ? L.scales + L.n_key : nullptr;
   ma.out = out;
   ma.g = g;
   ma.seq = seq;
-  const int Rg = g.B * g.G * g.n_q;
-  dim3 gm(g.H_kv, (Rg + 15) / 16);
   {
-  ProfScope ps("decode_merge", s);
-  if (L.dtype == STARKV_F32) hipLaunchKernelGGL(k_merge<STARKV_F32>, gm, dim3(256), 0, s, ma);
-  else hipLaunchKernelGGL(k_merge<STARKV_BF16>, gm, dim3(256), 0, s, ma);
+  ProfScope ps("decode_zmerge", s);
+  dim3 gz((g.r_v + 63) / 64, (g.M_q + 3) / 4, g.B);
+  hipLaunchKernelGGL(k_zmerge, gz, dim3(256), 0, s, ma);
+  }
+  const int Rg = g.B * g.G * g.n_q;
+  dim3 gm(g.H_kv * (g.d_h / 32), (Rg + 15) / 16);
+  {
+  ProfScope ps("decode_upproj", s);
+  if (L.dtype == STARKV_F32) hipLaunchKernelGGL(k_upproj<STARKV_F32>, gm, dim3(256), 0, s, ma);
+  else hipLaunchKernelGGL(k_upproj<STARKV_BF16>, gm, dim3(256), 0, s, ma);
   }
   return hipGetLastError();
 }

@@ -11,7 +11,7 @@
 namespace skv {
 
 constexpr int kTT = STARKV_TILE_TOKENS;  // tokens per value tile
-constexpr int kTC = 64;                  // tokens per score chunk
+constexpr int kTC = 32;                  // tokens per score chunk (= one value tile)
 constexpr int kMaxB = STARKV_MAX_BATCH;
 constexpr int kMaxCT = STARKV_MAX_QROWS / 16;  // 16-row column tiles of the key-score GEMM
 constexpr int kMaxKT = 48;                     // K-tiles per column tile
@@ -93,10 +93,13 @@ struct DecodeWs {
   float* zp;        // [total_splits][M_pad][r_v] value-latent partials
   float* sm;        // [total_splits][M_pad] split max
   float* sl;        // [total_splits][M_pad] split sum
+  float* zt;        // [B][M_pad][r_v] merged value latent (scaled, normalised)
   int nkt_max;
   int total_chunks, total_splits;
   int cps;          // score chunks per value split
-  int blocks_per_wg;  // value blocks (waves) per value WG
+  int blocks_per_wg;  // value blocks (waves) per value WG (several query-row tiles)
+  int n_sl8, n_sl4;   // one-row-tile value kernel: slices of one-N-tile blocks / of int4 blocks
+  int nbw8, nbw4;     // blocks per slice of each kind
 };
 
 struct DecodePlan {

@@ -75,14 +75,14 @@ def test_ranks_and_layout_match_oracle(cfg):
 
 def test_shrink_flag_and_tie():
     # hard truncation keeps the same rank; a tie s == tau drops the channel (strict >)
-    s_k = np.array([[3.0, 2.0, 1.0, 0.5] * 4], np.float32)
+    s_k = np.array([[3.0, 2.0, 1.0, 0.5] * 8], np.float32)
     s_k = np.sort(s_k, axis=1)[:, ::-1].copy()
     for shrink in (True, False):
-        layer = S.Layer(1, 1, 16, 16, "f32", "f32", s_k, [2.0], np.linspace(2, 1, 16), 1.5, shrink=shrink)
-        assert layer.ranks[0] == 4 and layer.r_v == 8
+        layer = S.Layer(1, 1, 32, 32, "f32", "f32", s_k, [2.0], np.linspace(2, 1, 32), 1.5, shrink=shrink)
+        assert layer.ranks[0] == 8 and layer.r_v == 16
         layer.close()
-    layer = S.Layer(1, 1, 16, 16, "f32", "f32", s_k, [0.0], np.linspace(2, 1, 16), 0.0)
-    assert layer.ranks[0] == 16 and layer.r_v == 16  # tau = 0 keeps every rank
+    layer = S.Layer(1, 1, 32, 32, "f32", "f32", s_k, [0.0], np.linspace(2, 1, 32), 0.0)
+    assert layer.ranks[0] == 32 and layer.r_v == 32  # tau = 0 keeps every rank
     layer.close()
 
 
@@ -107,6 +107,7 @@ def test_create_validation():
     assert status(dtype="bf16", latent="f32") == -4
     assert status(dtype="f32", latent="mix84") == -4
     assert status(d=250) == -4  # d not a multiple of 16
+    assert status(d_h=48, s_k=np.ones((4, 48), np.float32)) == -4  # d_h not a multiple of 32
     assert status(tau_v=100.0) == -4  # r_v == 0
     assert status(tau_k=np.full(4, 100.0, np.float32)) == -4  # every key rank 0
 

@@ -235,3 +235,21 @@ def test_graph_replay_matches_eager():
         # eager work between replays
         run.GL.decode(run.cache, q, lens, out=torch.empty_like(q))
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2])
+@pytest.mark.parametrize("n_new", [1, 2])
+def test_append_few_tokens(cfg, n_new):
+    """Appends of one or two tokens per sequence (the per-step append) on top of a prefill:
+    cache bytes bit-exact against the oracle (exact-latent conditioning)."""
+    w = dataclasses.replace(I.WORKLOADS[cfg], B=3)
+    run = H.make_layer(w, exact=True)
+    H.calibrate(run)
+    H.prefill(run, [40, 31, 64], oracle_seqs=range(3), T_max=128)
+    H.append_step(run, n_new, step=3)
+    H.append_step(run, n_new, step=4)
+    _compare_cache(run, True)
+    q = H.queries(run)
+    got = H.from_dev(H.decode(run, q))
+    for b in range(3):
+        H.check_output(w, got[b], H.oracle_decode(run, q, b), f"len {int(run.lens[b])}")
