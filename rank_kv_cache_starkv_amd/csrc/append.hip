@@ -113,10 +113,10 @@ __device__ __forceinline__ void store_latent(const GemmArgs& a, int slot, int ch
 
 // Few-token append (M <= 16 rows): the work is reading A once.  Workgroup = 16 cache slots
 // x all rows; the 8 waves split K = d and their 16x16 partial results are summed through LDS;
-// loads run 4 K-steps deep.  16x16x32 bf16 MFMA (16x16x4 f32 for the fp32 path).
+// loads run 8 K-steps deep.  16x16x32 bf16 MFMA (16x16x4 f32 for the fp32 path).
 template <int DT>
 __global__ __launch_bounds__(512) void k_latent_gemm_skinny(GemmArgs a) {
-  constexpr int KU = 4;
+  constexpr int KU = 8;
   __shared__ float red[7][4][64];
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();

@@ -13,6 +13,8 @@
 // rows, K = key-row slots (the query fragments are zero outside their head's segment).
 #include <math.h>
 
+#include <string.h>
+
 #include <algorithm>
 #include <cstdlib>
 
@@ -58,6 +60,7 @@ int plan_decode(const Layer& L, int B, int n_q, const int32_t* lens, int T_max, 
   g.qscale = (float)(1.4426950408889634 / sqrt((double)L.d_h));
 
   // K-tiles touched by every 16-row column tile (block-diagonal query fragments)
+  memset(kts, 0, sizeof(*kts));
   const int rows_per_head = L.G * n_q;
   int nkt_max = 1;
   for (int ct = 0; ct < g.nct; ++ct) {
@@ -100,15 +103,17 @@ int plan_decode(const Layer& L, int B, int n_q, const int32_t* lens, int T_max, 
   if (g.M_pad == 32) n_slices = w.n_sl8 + w.n_sl4;
   int total_chunks = 0, max_chunks = 0;
   seq->chunk_off[0] = 0;
+  seq->blk_off[0] = 0;
   for (int b = 0; b < B; ++b) {
     seq->lens[b] = lens[b];
     const int nc = ceil_div(lens[b], kTC);
     seq->chunk_off[b + 1] = seq->chunk_off[b] + nc;
+    seq->blk_off[b + 1] = seq->blk_off[b] + ceil_div(nc, 4);
     total_chunks += nc;
     max_chunks = std::max(max_chunks, nc);
   }
-  // splits: aim at ~320 value workgroups, at least 8 tiles (two per wave) per split
-  const int target_wg = env_int("STARKV_VALUE_WGS", 320);
+  // splits: aim at ~512 value workgroups (two per CU), at least 8 tiles (two per wave) per split
+  const int target_wg = env_int("STARKV_VALUE_WGS", 512);
   int cps = std::max(8, ceil_div(total_chunks, std::max(1, target_wg / n_slices)));
   cps = std::max(cps, ceil_div(max_chunks, kMaxSplitsPerSeq));
   const int cps_env = env_int("STARKV_CPS", 0);
@@ -208,40 +213,48 @@ __global__ __launch_bounds__(256) void k_qproj(QprojArgs a) {
       qrow[n][e] = ldx<DT>(a.q, (((size_t)b * g.n_q + j) * g.H_q + h) * g.d_h + e);
     }
     __syncthreads();
-    // q^[n][k] = (q_n . B_k[c0 + k]) * scale * log2(e)/sqrt(d_h): 4 lanes per dot product
-    for (int p0 = 0; p0 < nrows * r; p0 += 64) {
-      const int p = p0 + (tid >> 2), sub = tid & 3;
+    // q^[n][k] = (q_n . B_k[c0 + k]) * scale * log2(e)/sqrt(d_h): one lane per dot product,
+    // the B_k row read with 16-byte loads all issued before the FMAs
+    for (int p = tid; p < nrows * r; p += 256) {
+      const int n = p / r, k = p % r;
+      const size_t boff = (size_t)(c0 + k) * g.d_h;
       float acc = 0.f;
-      if (p < nrows * r) {
-        const int n = p / r, k = p % r;
-        const size_t boff = (size_t)(c0 + k) * g.d_h;
-        for (int e0 = 8 * sub; e0 < g.d_h; e0 += 32) {
-          if (DT == STARKV_F32) {
-            const u32x4 v0 = ld16((const float*)a.B_k + boff + e0);
-            const u32x4 v1 = ld16((const float*)a.B_k + boff + e0 + 4);
+      for (int e0 = 0; e0 < g.d_h; e0 += 64) {
+        u32x4 bv[8];
+        if (DT == STARKV_F32) {
+#pragma unroll
+          for (int x = 0; x < 8; ++x) bv[x] = (e0 + 4 * x < g.d_h) ? ld16((const float*)a.B_k + boff + e0 + 4 * x) : u32x4{0, 0, 0, 0};
+#pragma unroll
+          for (int x = 0; x < 8; ++x)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (e0 + 4 * x + e < g.d_h) acc = fmaf(qrow[n][e0 + 4 * x + e], __uint_as_float(bv[x][e]), acc);
+          // second half of the 64-element step
+#pragma unroll
+          for (int x = 0; x < 8; ++x) bv[x] = (e0 + 32 + 4 * x < g.d_h) ? ld16((const float*)a.B_k + boff + e0 + 32 + 4 * x) : u32x4{0, 0, 0, 0};
+#pragma unroll
+          for (int x = 0; x < 8; ++x)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (e0 + 32 + 4 * x + e < g.d_h) acc = fmaf(qrow[n][e0 + 32 + 4 * x + e], __uint_as_float(bv[x][e]), acc);
+        } else {
+#pragma unroll
+          for (int x = 0; x < 8; ++x) bv[x] = (e0 + 8 * x < g.d_h) ? ld16((const uint16_t*)a.B_k + boff + e0 + 8 * x) : u32x4{0, 0, 0, 0};
+#pragma unroll
+          for (int x = 0; x < 8; ++x)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              acc = fmaf(qrow[n][e0 + e], __uint_as_float(v0[e]), acc);
-              acc = fmaf(qrow[n][e0 + 4 + e], __uint_as_float(v1[e]), acc);
+              const int ee = e0 + 8 * x + 2 * e;
+              if (ee < g.d_h) {
+                acc = fmaf(qrow[n][ee], bf16_to_f32((uint16_t)(bv[x][e] & 0xFFFF)), acc);
+                acc = fmaf(qrow[n][ee + 1], bf16_to_f32((uint16_t)(bv[x][e] >> 16)), acc);
+              }
             }
-          } else {
-            const u32x4 v = ld16((const uint16_t*)a.B_k + boff + e0);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              acc = fmaf(qrow[n][e0 + 2 * e], bf16_to_f32((uint16_t)(v[e] & 0xFFFF)), acc);
-              acc = fmaf(qrow[n][e0 + 2 * e + 1], bf16_to_f32((uint16_t)(v[e] >> 16)), acc);
-            }
-          }
         }
       }
-      acc += __shfl_xor(acc, 1, 64);
-      acc += __shfl_xor(acc, 2, 64);
-      if (p < nrows * r && sub == 0) {
-        const int n = p / r, k = p % r;
-        float sc = 1.f;
-        if (LAT == STARKV_LATENT_MIX84) sc = f16_to_f32(a.scales[c0 + k]);
-        qh[n][k] = acc * sc * g.qscale;
-      }
+      float sc = 1.f;
+      if (LAT == STARKV_LATENT_MIX84) sc = f16_to_f32(a.scales[c0 + k]);
+      qh[n][k] = acc * sc * g.qscale;
     }
     __syncthreads();
     // per-row scale (int8 path): rho = max|q^| / 127, one wave per row
@@ -387,12 +400,252 @@ struct ScoreArgs {
 // Workgroup = 4 waves over `nch_wg` consecutive 64-token chunks (global chunk numbering, so a
 // workgroup may span sequences); work unit = (column tile ct, chunk).  Per unit the loop runs
 // K-tile outer / 16-token tile inner, so each query fragment is loaded once per unit.
+// Workgroup = (sequence, column tile ct, block of 128 tokens = four 32-token chunks).  The four
+// waves split the K-tiles of ct (wave w takes K-tiles w, w+4, ...) and keep their query
+// fragments in registers for the whole block; each wave computes partial scores of the 8
+// 16-token tiles over its K-tiles (loads of 4 tiles x 4 K-tiles in flight), the partials are
+// added through LDS, and wave w then finishes chunk w: mask, chunk max and sum, p~ = 2^(s - m).
+template <int LAT>
+__global__ __launch_bounds__(256) void k_scores(ScoreArgs a) {
+  constexpr int KW = kMaxKT / 4;  // K-tiles per wave (max)
+  constexpr int FR = LAT == STARKV_LATENT_F32 ? 2 : 2;  // 16-byte fragment loads per K-tile
+  __shared__ float part[4][8][4][64];  // [wave][token tile][D element][lane]
+  const DecodeGeom& g = a.g;
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int n = lane & 15, qq = lane >> 4;
+  const int ct = blockIdx.x % g.nct;
+  const int gblk = blockIdx.x / g.nct;
+  const int b = find_segment(a.seq.blk_off, g.B, gblk);
+  const int t_blk = (gblk - a.seq.blk_off[b]) * 128;
+  const int len = a.seq.lens[b];
+  const uint8_t* kbase = a.k_rows + (size_t)b * g.T_max * g.k_row_bytes;
+  const int nkt = a.kts.n[ct];
+  const int nkw = nkt > wave ? (nkt - wave + 3) / 4 : 0;  // K-tiles of this wave (uniform)
+  const uint8_t* fbase = a.qfrag + ((size_t)b * g.nct + ct) * a.nkt_max * 2048;
+
+  // query fragments of this wave's K-tiles
+  u32x4 fr[KW][FR];
+  int p0[KW];
+#pragma unroll
+  for (int j = 0; j < KW; ++j) {
+    const bool on = j < nkw;
+    const int jt = wave + 4 * (on ? j : 0);
+    const int kt = a.kts.kt[ct][jt];
+    p0[j] = (LAT == STARKV_LATENT_MIX84 ? kt * 64 + 16 * qq : kt * 32 + 8 * qq);
+    const uint8_t* f = fbase + (size_t)jt * 2048;
+#pragma unroll
+    for (int k = 0; k < FR; ++k) {
+      const int off = LAT == STARKV_LATENT_F32 ? lane * 32 + 16 * k : 1024 * k + lane * 16;
+      fr[j][k] = on ? ld16(f + off) : u32x4{0, 0, 0, 0};
+    }
+  }
+  float rho = 1.f;
+  if (LAT == STARKV_LATENT_MIX84) {
+    const int i = ct * 16 + n;
+    if (i < g.M_q) rho = a.rowp[((size_t)b * g.M_pad + i) * 4];
+  }
+
+  // partial scores of the 8 token tiles over this wave's K-tiles, four tiles at a time
+#pragma unroll
+  for (int tg = 0; tg < 2; ++tg) {
+    float sp[4][4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sp[t][v] = 0.f;
+    const uint8_t* rowp[4];
+    bool tok_ok[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int tok = t_blk + (tg * 4 + t) * 16 + n;
+      tok_ok[t] = tok < len;
+      rowp[t] = kbase + (size_t)(tok_ok[t] ? tok : 0) * g.k_row_bytes;
+    }
+    for (int j0 = 0; j0 < nkw; j0 += 4) {
+      if (LAT == STARKV_LATENT_MIX84) {
+        i32x4 av[4][4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int j = j0 + jj;
+          const bool on = j < nkw;
+          int P0 = 0;
+#pragma unroll
+          for (int x = 0; x < KW; ++x)
+            if (x == j) P0 = p0[x];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            i32x4 v = {0, 0, 0, 0};
+            if (on && tok_ok[t]) {
+              if (P0 < g.K8) v = __builtin_bit_cast(i32x4, ld16(rowp[t] + P0));
+              else if (P0 < g.K8 + g.K4) v = unpack_int4_group(ld8(rowp[t] + g.K8 + (P0 - g.K8) / 2));
+            }
+            av[jj][t] = v;
+          }
+        }
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          i32x4 fh = {0, 0, 0, 0}, fl = {0, 0, 0, 0};
+#pragma unroll
+          for (int x = 0; x < KW; ++x)
+            if (x == j0 + jj) {
+              fh = __builtin_bit_cast(i32x4, fr[x][0]);
+              fl = __builtin_bit_cast(i32x4, fr[x][1]);
+            }
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const i32x4 h = mfma16_i8(av[jj][t], fh, i32x4{0, 0, 0, 0});
+            const i32x4 l = mfma16_i8(av[jj][t], fl, i32x4{0, 0, 0, 0});
+#pragma unroll
+            for (int v = 0; v < 4; ++v) sp[t][v] += rho * (float)h[v] + (rho * (1.f / 254.f)) * (float)l[v];
+          }
+        }
+      } else if (LAT == STARKV_LATENT_BF16) {
+        u32x4 av[4][4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int j = j0 + jj;
+          const bool on = j < nkw;
+          int P0 = 0;
+#pragma unroll
+          for (int x = 0; x < KW; ++x)
+            if (x == j) P0 = p0[x];
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            av[jj][t] = (on && tok_ok[t] && P0 < g.key_kpos) ? ld16(rowp[t] + 2 * P0) : u32x4{0, 0, 0, 0};
+        }
+        f32x4 acc[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[t] = f32x4{sp[t][0], sp[t][1], sp[t][2], sp[t][3]};
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          u32x4 fh = {0, 0, 0, 0}, fl = {0, 0, 0, 0};
+#pragma unroll
+          for (int x = 0; x < KW; ++x)
+            if (x == j0 + jj) {
+              fh = fr[x][0];
+              fl = fr[x][1];
+            }
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            acc[t] = mfma16_bf16(as_bf16x8(av[jj][t]), as_bf16x8(fh), acc[t]);
+            acc[t] = mfma16_bf16(as_bf16x8(av[jj][t]), as_bf16x8(fl), acc[t]);
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) sp[t][v] = acc[t][v];
+      } else {
+        f32x4 acc[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[t] = f32x4{sp[t][0], sp[t][1], sp[t][2], sp[t][3]};
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int j = j0 + jj;
+          if (j >= nkw) continue;
+          int P0 = 0;
+          u32x4 f0 = {0, 0, 0, 0}, f1 = {0, 0, 0, 0};
+#pragma unroll
+          for (int x = 0; x < KW; ++x)
+            if (x == j) {
+              P0 = p0[x];
+              f0 = fr[x][0];
+              f1 = fr[x][1];
+            }
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const u32x4 a0 = (tok_ok[t] && P0 < g.key_kpos) ? ld16(rowp[t] + 4 * P0) : u32x4{0, 0, 0, 0};
+            const u32x4 a1 = (tok_ok[t] && P0 + 4 < g.key_kpos) ? ld16(rowp[t] + 4 * P0 + 16) : u32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[t] = mfma16_f32(__uint_as_float(a0[e]), __uint_as_float(f0[e]), acc[t]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[t] = mfma16_f32(__uint_as_float(a1[e]), __uint_as_float(f1[e]), acc[t]);
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) sp[t][v] = acc[t][v];
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) part[wave][tg * 4 + t][v][lane] = sp[t][v];
+  }
+  __syncthreads();
+
+  // wave w finishes chunk w of the block (token tiles 2w, 2w + 1)
+  const int t0 = t_blk + 32 * wave;
+  const int nch_b = a.seq.chunk_off[b + 1] - a.seq.chunk_off[b];
+  const int cidx = t0 / kTC;
+  if (cidx >= nch_b) return;
+  const int cg = a.seq.chunk_off[b] + cidx;
+  const int i = ct * 16 + n;
+  const bool rowvalid = i < g.M_q;
+  const int pos = len - g.n_q + (i % g.n_q);
+  float bias = 0.f;
+  if (LAT == STARKV_LATENT_MIX84 && rowvalid) {
+    const float* rp = a.rowp + ((size_t)b * g.M_pad + i) * 4;
+    bias = rp[0] * (rp[1] + rp[2] * (1.f / 254.f));
+  }
+  float s2[2][4];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int ti = 2 * wave + tt;
+      float x = part[0][ti][v][lane] + part[1][ti][v][lane] + part[2][ti][v][lane] + part[3][ti][v][lane];
+      x -= bias;
+      const int t = t0 + tt * 16 + 4 * qq + v;
+      const bool ok = rowvalid && t < len && t <= pos;
+      s2[tt][v] = ok ? x : -INFINITY;
+    }
+  float m = -INFINITY;
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) m = fmaxf(m, s2[tt][v]);
+  m = wave_max_xor(m, 16);
+  m = wave_max_xor(m, 32);
+  float l = 0.f;
+  const size_t prow = ((size_t)cg * g.M_pad + i) * kTC;
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    float e4[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      e4[v] = (s2[tt][v] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s2[tt][v] - m);
+      l += e4[v];
+    }
+    const size_t off = prow + tt * 16 + 4 * qq;
+    if (LAT == STARKV_LATENT_F32) {
+      st16((float*)a.p + off, u32x4{__float_as_uint(e4[0]), __float_as_uint(e4[1]), __float_as_uint(e4[2]),
+                                    __float_as_uint(e4[3])});
+    } else if (LAT == STARKV_LATENT_BF16) {
+      const uint32_t w0 = (uint32_t)f32_to_bf16(e4[0]) | ((uint32_t)f32_to_bf16(e4[1]) << 16);
+      const uint32_t w1 = (uint32_t)f32_to_bf16(e4[2]) | ((uint32_t)f32_to_bf16(e4[3]) << 16);
+      st8((uint16_t*)a.p + off, u32x2{w0, w1});
+    } else {
+      const uint32_t w0 = (uint32_t)f32_to_f16(e4[0]) | ((uint32_t)f32_to_f16(e4[1]) << 16);
+      const uint32_t w1 = (uint32_t)f32_to_f16(e4[2]) | ((uint32_t)f32_to_f16(e4[3]) << 16);
+      st8((uint16_t*)a.p + off, u32x2{w0, w1});
+    }
+  }
+  l = wave_sum_xor(l, 16);
+  l = wave_sum_xor(l, 32);
+  if (qq == 0) {
+    a.cm[(size_t)cg * g.M_pad + i] = m;
+    a.cl[(size_t)cg * g.M_pad + i] = l;
+  }
+}
+
 // Workgroup = 4 waves over `nch_wg` consecutive 32-token chunks (global chunk numbering, so a
 // workgroup may span sequences); work unit = (column tile ct, chunk) = 2 MFMA row tiles of 16
 // tokens.  Per unit the K-tiles are walked four at a time: the loads of four K-tiles (query
 // fragments and key rows) are issued before their MFMAs, to keep enough bytes in flight.
 template <int LAT>
-__global__ __launch_bounds__(256) void k_scores(ScoreArgs a) {
+__global__ __launch_bounds__(256) void k_scores_chunk(ScoreArgs a) {
   constexpr int KU = 4;  // K-tiles in flight
   const DecodeGeom& g = a.g;
   const int lane = threadIdx.x & 63, wave = wave_id();
@@ -1035,8 +1288,18 @@ __global__ __launch_bounds__(256) void k_zmerge(MergeArgs a) {
   }
   __syncthreads();
   if (i >= g.M_q || c >= g.r_v) return;
+  const float* zc = a.zp + ((size_t)s0 * g.M_pad + i) * g.r_v + c;
+  const size_t zs = (size_t)g.M_pad * g.r_v;
   float z = 0.f;
-  for (int s = 0; s < ns; ++s) z = fmaf(wts[rn][s], a.zp[((size_t)(s0 + s) * g.M_pad + i) * g.r_v + c], z);
+  int s = 0;
+  for (; s + 4 <= ns; s += 4) {
+    const float z0 = zc[(s + 0) * zs], z1 = zc[(s + 1) * zs], z2 = zc[(s + 2) * zs], z3 = zc[(s + 3) * zs];
+    z = fmaf(wts[rn][s], z0, z);
+    z = fmaf(wts[rn][s + 1], z1, z);
+    z = fmaf(wts[rn][s + 2], z2, z);
+    z = fmaf(wts[rn][s + 3], z3, z);
+  }
+  for (; s < ns; ++s) z = fmaf(wts[rn][s], zc[s * zs], z);
   float sc = invl[rn];
   if (a.vscales) sc *= f16_to_f32(a.vscales[c]);
   a.zt[((size_t)b * g.M_pad + i) * g.r_v + c] = z * sc;
@@ -1065,65 +1328,82 @@ __global__ __launch_bounds__(256) void k_upproj(MergeArgs a) {
   const int per = (nch + 3) / 4;
   const int k_beg = wave * per * 32, k_end = min(g.r_v, (wave + 1) * per * 32);
   f32x4 acc[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
-  for (int kc = k_beg; kc < k_end; kc += 32) {
-    const int c = kc + 8 * qq;
-    float z[8];
-    if (rv && vec && c + 8 <= g.r_v) {
-      const u32x4 v0 = ld16(zr + c), v1 = ld16(zr + c + 4);
+  constexpr int KU = 8;  // 32-channel chunks in flight
+  for (int kc0 = k_beg; kc0 < k_end; kc0 += 32 * KU) {
+    float z[KU][8];
+    u32x4 bw[KU][2][DT == STARKV_F32 ? 2 : 1];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        z[e] = __uint_as_float(v0[e]);
-        z[4 + e] = __uint_as_float(v1[e]);
-      }
-    } else {
+    for (int u = 0; u < KU; ++u) {
+      const int c = kc0 + 32 * u + 8 * qq;
+      const bool on = kc0 + 32 * u < k_end;
+      if (on && rv && vec && c + 8 <= g.r_v) {
+        const u32x4 v0 = ld16(zr + c), v1 = ld16(zr + c + 4);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) z[e] = (rv && c + e < g.r_v) ? zr[c + e] : 0.f;
-    }
-    u32x4 ah, al;
-    if (DT != STARKV_F32) {
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        const uint16_t h0 = f32_to_bf16(z[2 * e2]), h1 = f32_to_bf16(z[2 * e2 + 1]);
-        const uint16_t l0 = f32_to_bf16(z[2 * e2] - bf16_to_f32(h0));
-        const uint16_t l1 = f32_to_bf16(z[2 * e2 + 1] - bf16_to_f32(h1));
-        ah[e2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-        al[e2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int col = gk * g.d_h + (2 * nsl + t) * 16 + n;  // B_v^T row
-      if (DT == STARKV_F32) {
-        const float* bp = (const float*)a.B_vt + (size_t)col * g.r_v;
-        float bv[8];
-        if (vec && c + 8 <= g.r_v) {
-          const u32x4 v0 = ld16(bp + c), v1 = ld16(bp + c + 4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            bv[e] = __uint_as_float(v0[e]);
-            bv[4 + e] = __uint_as_float(v1[e]);
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) bv[e] = (c + e < g.r_v) ? bp[c + e] : 0.f;
+        for (int e = 0; e < 4; ++e) {
+          z[u][e] = __uint_as_float(v0[e]);
+          z[u][4 + e] = __uint_as_float(v1[e]);
         }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[t] = mfma16_f32(z[e], bv[e], acc[t]);
       } else {
-        const uint16_t* bp = (const uint16_t*)a.B_vt + (size_t)col * g.r_v;
-        u32x4 bw;
-        if (vec && c + 8 <= g.r_v) {
-          bw = ld16(bp + c);
-        } else {
 #pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2) {
-            const uint32_t b0 = (c + 2 * e2 < g.r_v) ? bp[c + 2 * e2] : 0u;
-            const uint32_t b1 = (c + 2 * e2 + 1 < g.r_v) ? bp[c + 2 * e2 + 1] : 0u;
-            bw[e2] = b0 | (b1 << 16);
+        for (int e = 0; e < 8; ++e) z[u][e] = (on && rv && c + e < g.r_v) ? zr[c + e] : 0.f;
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int col = gk * g.d_h + (2 * nsl + t) * 16 + n;  // B_v^T row
+        if (DT == STARKV_F32) {
+          const float* bp = (const float*)a.B_vt + (size_t)col * g.r_v;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            u32x4 v;
+            if (on && vec && c + 8 <= g.r_v) {
+              v = ld16(bp + c + 4 * h);
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[e] = (on && c + 4 * h + e < g.r_v) ? __float_as_uint(bp[c + 4 * h + e]) : 0u;
+            }
+            bw[u][t][h] = v;
           }
+        } else {
+          const uint16_t* bp = (const uint16_t*)a.B_vt + (size_t)col * g.r_v;
+          u32x4 v;
+          if (on && vec && c + 8 <= g.r_v) {
+            v = ld16(bp + c);
+          } else {
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+              const uint32_t b0 = (on && c + 2 * e2 < g.r_v) ? bp[c + 2 * e2] : 0u;
+              const uint32_t b1 = (on && c + 2 * e2 + 1 < g.r_v) ? bp[c + 2 * e2 + 1] : 0u;
+              v[e2] = b0 | (b1 << 16);
+            }
+          }
+          bw[u][t][0] = v;
         }
-        acc[t] = mfma16_bf16(as_bf16x8(ah), as_bf16x8(bw), acc[t]);
-        acc[t] = mfma16_bf16(as_bf16x8(al), as_bf16x8(bw), acc[t]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < KU; ++u) {
+      if (DT == STARKV_F32) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[t] = mfma16_f32(z[u][4 * h + e], __uint_as_float(bw[u][t][h][e]), acc[t]);
+      } else {
+        u32x4 ah, al;
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const uint16_t h0 = f32_to_bf16(z[u][2 * e2]), h1 = f32_to_bf16(z[u][2 * e2 + 1]);
+          const uint16_t l0 = f32_to_bf16(z[u][2 * e2] - bf16_to_f32(h0));
+          const uint16_t l1 = f32_to_bf16(z[u][2 * e2 + 1] - bf16_to_f32(h1));
+          ah[e2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+          al[e2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          acc[t] = mfma16_bf16(as_bf16x8(ah), as_bf16x8(bw[u][t][0]), acc[t]);
+          acc[t] = mfma16_bf16(as_bf16x8(al), as_bf16x8(bw[u][t][0]), acc[t]);
+        }
       }
     }
   }
@@ -1205,18 +1485,24 @@ hipError_t launch_decode(const Layer& L, const DecodePlan& plan, const KtList& k
   sa.nkt_max = w.nkt_max;
   sa.kts = kts;
   sa.seq = seq;
-  // enough chunks per workgroup that every one of its 4 waves has a (column tile, chunk) unit
-  sa.nch_wg = std::max(1, 4 / std::min(g.nct, 4));
   sa.total_chunks = w.total_chunks;
-  const int n_wg = (w.total_chunks + sa.nch_wg - 1) / sa.nch_wg;
   {
   ProfScope ps("decode_scores", s);
-  if (L.latent == STARKV_LATENT_MIX84)
-    hipLaunchKernelGGL(k_scores<STARKV_LATENT_MIX84>, dim3(n_wg), dim3(256), 0, s, sa);
-  else if (L.latent == STARKV_LATENT_BF16)
-    hipLaunchKernelGGL(k_scores<STARKV_LATENT_BF16>, dim3(n_wg), dim3(256), 0, s, sa);
-  else
-    hipLaunchKernelGGL(k_scores<STARKV_LATENT_F32>, dim3(n_wg), dim3(256), 0, s, sa);
+  if (L.latent == STARKV_LATENT_MIX84) {
+    // int8/int4 keys: work unit = (column tile, 32-token chunk), enough chunks per workgroup
+    // that each of its four waves has a unit
+    sa.nch_wg = std::max(1, 4 / std::min(g.nct, 4));
+    const int n_wg = (w.total_chunks + sa.nch_wg - 1) / sa.nch_wg;
+    hipLaunchKernelGGL(k_scores_chunk<STARKV_LATENT_MIX84>, dim3(n_wg), dim3(256), 0, s, sa);
+  } else {
+    // bf16/fp32 keys (many K-tiles per column tile): K split over the waves of a 128-token block
+    sa.nch_wg = 4;
+    const int n_wg = seq.blk_off[g.B] * g.nct;
+    if (L.latent == STARKV_LATENT_BF16)
+      hipLaunchKernelGGL(k_scores<STARKV_LATENT_BF16>, dim3(n_wg), dim3(256), 0, s, sa);
+    else
+      hipLaunchKernelGGL(k_scores<STARKV_LATENT_F32>, dim3(n_wg), dim3(256), 0, s, sa);
+  }
   }
   // 3. values
   ValueArgs va;

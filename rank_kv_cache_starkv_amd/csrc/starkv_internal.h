@@ -14,7 +14,7 @@ constexpr int kTT = STARKV_TILE_TOKENS;  // tokens per value tile
 constexpr int kTC = 32;                  // tokens per score chunk (= one value tile)
 constexpr int kMaxB = STARKV_MAX_BATCH;
 constexpr int kMaxCT = STARKV_MAX_QROWS / 16;  // 16-row column tiles of the key-score GEMM
-constexpr int kMaxKT = 48;                     // K-tiles per column tile
+constexpr int kMaxKT = 32;                     // K-tiles per column tile
 constexpr int kMaxSplitsPerSeq = 64;
 
 // Per-KV-head tables on the device (int32 each, H_kv entries unless noted).
@@ -79,8 +79,9 @@ struct KtList {
 
 struct SeqTable {
   int lens[kMaxB];
-  int chunk_off[kMaxB + 1];
-  int split_off[kMaxB + 1];
+  int chunk_off[kMaxB + 1];  // prefix of 32-token chunks per sequence
+  int split_off[kMaxB + 1];  // prefix of value splits per sequence
+  int blk_off[kMaxB + 1];    // prefix of 128-token score blocks per sequence
 };
 
 struct DecodeWs {
