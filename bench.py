@@ -9,11 +9,20 @@ than 1 GiB, so every step reads cold HBM rather than the 256 MB Infinity Cache.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1] [--no-cpu]
 Prints one JSON line on stdout; progress goes to stderr.
+
+Two helper modes serve the HBM-traffic figures:
+  --copy-probe       copies 1 GiB between two device buffers a few times (a plain copy
+                     kernel of known size, run under rocprofv3 --pmc to calibrate counters);
+  --pmc-summary F W CF CW  reads four rocprofv3 --pmc output folders (FETCH_SIZE and
+                     WRITE_SIZE of a bench run, then of the copy probe), prints a summary and
+                     records bytes per launch of each step kernel in profiles/traffic.json.
 """
 
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
 import hashlib
 import json
 import math
@@ -95,6 +104,87 @@ def traffic_for(kernel: str, workload: str):
     return float(e["bytes_per_launch"])
 
 
+KERNEL_KEYS = (("k_qproj", "decode_qproj"), ("k_scores", "decode_scores"), ("k_values", "decode_values"),
+               ("k_zmerge", "decode_zmerge"), ("k_upproj", "decode_upproj"), ("k_latent_gemm", "append"))
+
+
+COPY_PROBE_MIB = 1024
+
+
+def copy_probe(mib: int = COPY_PROBE_MIB) -> int:
+    """A plain device-to-device copy of known size, for calibrating the traffic counters."""
+    import torch
+    n = mib << 20
+    src = torch.ones((n,), dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "launches": 5}))
+    return 0
+
+
+def _pmc_rows(folder: str):
+    files = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {folder}")
+    rows = {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            key = (f, int(r["Dispatch_Id"]))
+            e = rows.setdefault(key, {"name": r["Kernel_Name"], "grid": int(r["Grid_Size"]), "v": 0.0})
+            e["v"] += float(r["Counter_Value"])  # KiB; summed over the counter's instances
+    return [rows[k] for k in sorted(rows)]
+
+
+def _step_kernels(rows):
+    """Per-launch counter values of the step kernels, keyed like the bench's kernel timers:
+    only dispatches after the first query projection (prefill launches come before it)."""
+    first = next((i for i, r in enumerate(rows) if "k_qproj" in r["name"]), None)
+    out = {}
+    if first is None:
+        return out
+    # the step's append precedes its query projection
+    for r in rows[max(0, first - 1):]:
+        for pat, key in KERNEL_KEYS:
+            if pat in r["name"]:
+                out.setdefault(key, []).append(r["v"])
+    return out
+
+
+def pmc_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, workload: str) -> int:
+    def copy_kib(folder):
+        vals = [r["v"] for r in _pmc_rows(folder) if "copy" in r["name"].lower()]
+        return float(np.median(vals)), len(vals)
+    cf, ncf = copy_kib(copy_fetch_dir)
+    cw, ncw = copy_kib(copy_write_dir)
+    copy_bytes = float(COPY_PROBE_MIB << 20)
+    f_fetch = copy_bytes / (cf * 1024.0)
+    f_write = copy_bytes / (cw * 1024.0)
+    fk = _step_kernels(_pmc_rows(fetch_dir))
+    wk = _step_kernels(_pmc_rows(write_dir))
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    d = json.load(open(path)) if os.path.exists(path) else {}
+    ent = d.setdefault(workload, {})
+    h = source_hash()
+    print(f"copy probe {copy_bytes / 2**20:.0f} MiB: FETCH_SIZE {cf:.0f} KiB ({ncf} launches) -> factor {f_fetch:.3f}; "
+          f"WRITE_SIZE {cw:.0f} KiB ({ncw} launches) -> factor {f_write:.3f}")
+    print(f"workload {workload}, kernel sources {h}")
+    print("| kernel | launches | FETCH_SIZE KiB/launch | WRITE_SIZE KiB/launch | calibrated HBM MB/launch |")
+    print("|---|---|---|---|---|")
+    for key in [k for _, k in KERNEL_KEYS]:
+        if key not in fk or key not in wk:
+            continue
+        fv, wv = float(np.mean(fk[key])), float(np.mean(wk[key]))
+        tb = f_fetch * fv * 1024.0 + f_write * wv * 1024.0
+        print(f"| {key} | {len(fk[key])} | {fv:.1f} | {wv:.1f} | {tb / 1e6:.3f} |")
+        ent[key] = {"bytes_per_launch": tb, "fetch_kib": fv, "write_kib": wv, "fetch_factor": f_fetch,
+                    "write_factor": f_write, "source_hash": h}
+    json.dump(d, open(path, "w"), indent=1, sort_keys=True)
+    return 0
+
+
 def cpu_baseline(w, lf, lens, n_q, X0, Xcal, q_step, X_step, budget_s: float):
     """The CPU oracle (NumPy fp64) on one sequence: one decode step = append n_q tokens +
     attention, repeated until ``budget_s`` of CPU time is used."""
@@ -110,7 +200,7 @@ def cpu_baseline(w, lf, lens, n_q, X0, Xcal, q_step, X_step, budget_s: float):
     base = O.compress(X0, OL, scales)
     log(f"[cpu] oracle prefill of sequence 0 ({X0.shape[0]} tokens): {time.perf_counter() - t_setup:.1f} s")
     reps, spent = 0, 0.0
-    while spent < budget_s and reps < 50:
+    while spent < budget_s:
         t0 = time.perf_counter()
         new = O.compress(X_step[0], OL, scales)
         cache = O.SequenceCache(np.concatenate([base.key, new.key]), np.concatenate([base.value, new.value]))
@@ -132,7 +222,14 @@ def main() -> int:
     ap.add_argument("--layers", type=int, default=0, help="layers to rotate (0: enough for 1 GiB)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-probe", action="store_true", help=f"copy {COPY_PROBE_MIB} MiB device to device")
+    ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"))
     args = ap.parse_args()
+    if args.pmc_summary:
+        from rank_kv_cache_starkv_amd import inputs as I
+        return pmc_summary(*args.pmc_summary, I.WORKLOADS[args.workload].name)
+    if args.copy_probe:
+        return copy_probe()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the build targets a single "
               f"MI355X; multi-GPU sharding is described in DESIGN.md, not built)", file=sys.stderr)

@@ -95,7 +95,7 @@ int plan_decode(const Layer& L, int B, int n_q, const int32_t* lens, int T_max, 
   int n_slices = ceil_div(NB, bpw);
   DecodeWs& w = P->ws;
   // one-M-tile value kernel: slices of up to nbw8 one-N-tile blocks and nbw4 int4 blocks
-  w.nbw8 = std::min(4, std::max(1, env_int("STARKV_NBW8", 4)));
+  w.nbw8 = std::min(4, std::max(1, env_int("STARKV_NBW8", 2)));
   w.nbw4 = std::min(2, std::max(1, env_int("STARKV_NBW4", 2)));
   const int nb8 = L.mix() ? L.V8 / 32 : NB;
   w.n_sl8 = ceil_div(nb8, w.nbw8);
