@@ -20,6 +20,7 @@ struct GemmArgs {
   const int* slot_chan; // [NS]
   int M, d, NS;
   int key_slots, K8, V8;
+  int n_key, r_v;
   int latent;
   // append
   int n_new, T_max, k_row_bytes, v_rows;
@@ -111,51 +112,69 @@ __device__ __forceinline__ void store_latent(const GemmArgs& a, int slot, int ch
   }
 }
 
-// Few-token append (M <= 16 rows): the work is reading A once.  Workgroup = 16 cache slots
-// x all rows; the 8 waves split K = d and their 16x16 partial results are summed through LDS;
-// loads run 8 K-steps deep.  16x16x32 bf16 MFMA (16x16x4 f32 for the fp32 path).
+// Natural latent channel of GEMM column `slot`, or -1 for a padding column.  Unquantised
+// latents keep the natural order (key channels, padding to the row size, value channels), so
+// the channel follows from the slot; the int8/int4 layout reorders channels (table lookup).
+__device__ __forceinline__ int slot_channel(const GemmArgs& a, int slot) {
+  if (slot >= a.NS) return -1;
+  if (a.latent == STARKV_LATENT_MIX84) return a.slot_chan[slot];
+  if (slot < a.n_key) return slot;
+  if (slot < a.key_slots) return -1;
+  const int u = slot - a.key_slots;
+  return u < a.r_v ? a.n_key + u : -1;
+}
+
+// Few-token append (M <= 16 rows): the work is reading A once.  Workgroup = 16 cache slots x
+// all rows; the 8 waves split K = d and their 16x16 partial results are summed through LDS.
+// A wave issues KU K-steps of loads before its MFMAs; every load is unconditional (rows past M
+// read row 0 and are never stored; K-steps past the wave's range repeat its last one with the
+// A_t operand zeroed; padding columns read channel 0 with the A_t operand zeroed).
+// 16x16x32 bf16 MFMA (16x16x4 f32 for the fp32 path).
 template <int DT>
 __global__ __launch_bounds__(512) void k_latent_gemm_skinny(GemmArgs a) {
-  constexpr int KU = 8;
+  constexpr int KU = DT == STARKV_BF16 ? 16 : 8;
+  constexpr int NL = DT == STARKV_BF16 ? 1 : 2;  // 16-byte loads per operand per K-step
   __shared__ float red[7][4][64];
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   const int n = lane & 15, q = lane >> 4;
   const int s0 = blockIdx.x * 16;
-  const bool a_ok = n < a.M;
   const int bslot = s0 + n;
-  const int bchan = (bslot < a.NS) ? a.slot_chan[bslot] : -1;
+  const int bchan = slot_channel(a, bslot);
   const bool b_ok = bchan >= 0;
-  const size_t a_base = (size_t)(a_ok ? n : 0) * a.d;
+  const size_t a_base = (size_t)(n < a.M ? n : 0) * a.d;
   const size_t b_base = (size_t)(b_ok ? bchan : 0) * a.d;
   const int ksteps = a.d / 32;
   const int per = (ksteps + 7) / 8;
   const int k_beg = wave * per, k_end = min(ksteps, k_beg + per);
   f32x4 acc = {0, 0, 0, 0};
   for (int k0 = k_beg; k0 < k_end; k0 += KU) {
-    u32x4 av[KU][2], bv[KU][2];
+    u32x4 av[KU][NL], bv[KU][NL];
 #pragma unroll
     for (int j = 0; j < KU; ++j) {
-      const bool on = k0 + j < k_end;
-      const size_t ko = (size_t)(k0 + j) * 32 + 8 * q;
-      if (DT == STARKV_BF16) {
-        av[j][0] = (on && a_ok) ? ld16((const uint16_t*)a.X + a_base + ko) : u32x4{0, 0, 0, 0};
-        bv[j][0] = (on && b_ok) ? ld16((const uint16_t*)a.A_t + b_base + ko) : u32x4{0, 0, 0, 0};
-      } else {
+      const size_t ko = (size_t)min(k0 + j, k_end - 1) * 32 + 8 * q;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          av[j][h] = (on && a_ok) ? ld16((const float*)a.X + a_base + ko + 4 * h) : u32x4{0, 0, 0, 0};
-          bv[j][h] = (on && b_ok) ? ld16((const float*)a.A_t + b_base + ko + 4 * h) : u32x4{0, 0, 0, 0};
+      for (int h = 0; h < NL; ++h) {
+        if (DT == STARKV_BF16) {
+          av[j][h] = ld16((const uint16_t*)a.X + a_base + ko);
+          bv[j][h] = ld16((const uint16_t*)a.A_t + b_base + ko);
+        } else {
+          av[j][h] = ld16((const float*)a.X + a_base + ko + 4 * h);
+          bv[j][h] = ld16((const float*)a.A_t + b_base + ko + 4 * h);
         }
       }
     }
+    __builtin_amdgcn_sched_barrier(0);  // keep every load of the batch ahead of the MFMAs
 #pragma unroll
     for (int j = 0; j < KU; ++j) {
+      const bool live = b_ok && k0 + j < k_end;
+#pragma unroll
+      for (int h = 0; h < NL; ++h) bv[j][h] = live ? bv[j][h] : u32x4{0, 0, 0, 0};
       if (DT == STARKV_BF16) {
         acc = mfma16_bf16(as_bf16x8(av[j][0]), as_bf16x8(bv[j][0]), acc);
       } else {
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < NL; ++h)
 #pragma unroll
           for (int e = 0; e < 4; ++e) acc = mfma16_f32(__uint_as_float(av[j][h][e]), __uint_as_float(bv[j][h][e]), acc);
       }
@@ -177,9 +196,7 @@ __global__ __launch_bounds__(512) void k_latent_gemm_skinny(GemmArgs a) {
     xs[v] = x;
     ms[v] = 4 * q + v;  // D row = token row; D column = n
   }
-  const int slot = s0 + n;
-  const int chan = (slot < a.NS) ? a.slot_chan[slot] : -1;
-  store_latent<4>(a, slot, chan, xs, ms);
+  store_latent<4>(a, bslot, bchan, xs, ms);
 }
 
 template <int DT, int MODE>
@@ -194,7 +211,7 @@ __global__ __launch_bounds__(256) void k_latent_gemm(GemmArgs a) {
   const int arow = m0 + r;
   const bool a_ok = arow < a.M;
   const int bslot = s0 + r;
-  const int bchan = (bslot < a.NS) ? a.slot_chan[bslot] : -1;
+  const int bchan = slot_channel(a, bslot);
   const bool b_ok = bchan >= 0;
   const size_t a_base = (size_t)(a_ok ? arow : 0) * a.d;
   const size_t b_base = (size_t)(b_ok ? bchan : 0) * a.d;
@@ -219,7 +236,7 @@ __global__ __launch_bounds__(256) void k_latent_gemm(GemmArgs a) {
 
   // result: lane holds column n = r (slot s0 + r), rows d32_row(v, q)
   const int slot = s0 + r;
-  const int chan = (slot < a.NS) ? a.slot_chan[slot] : -1;
+  const int chan = slot_channel(a, slot);
 
   if (MODE == 1) {
     // calibrate: absmax of this column over the 32 rows (rows >= M hold 0)
@@ -268,6 +285,8 @@ static void fill_common(const Layer& L, GemmArgs& a, const void* X, int M) {
   a.key_slots = L.key_slots;
   a.K8 = L.K8;
   a.V8 = L.V8;
+  a.n_key = L.n_key;
+  a.r_v = L.r_v;
   a.latent = L.latent;
 }
 
@@ -296,16 +315,18 @@ hipError_t launch_append(const Layer& L, const starkv_cache& c, const void* X_ne
   a.v_tiles = (uint8_t*)c.v_tiles;
   a.scales = L.scales;
   for (int b = 0; b < B; ++b) a.lens[b] = lens[b];
-  ProfScope ps("append", s);
+  ProfScope ps("append");
+  hipError_t e;
   if (B * n_new <= 16 && L.d % 32 == 0) {
-    dim3 grid((a.NS + 15) / 16);
-    if (L.dtype == STARKV_BF16) hipLaunchKernelGGL(k_latent_gemm_skinny<STARKV_BF16>, grid, dim3(512), 0, s, a);
-    else hipLaunchKernelGGL(k_latent_gemm_skinny<STARKV_F32>, grid, dim3(512), 0, s, a);
+    const dim3 grid((a.NS + 15) / 16);
+    if (L.dtype == STARKV_BF16) e = launch_k(ps, k_latent_gemm_skinny<STARKV_BF16>, grid, dim3(512), s, a);
+    else e = launch_k(ps, k_latent_gemm_skinny<STARKV_F32>, grid, dim3(512), s, a);
   } else {
-    dim3 grid((B * n_new + 63) / 64, (a.NS + 63) / 64);
-    if (L.dtype == STARKV_BF16) hipLaunchKernelGGL((k_latent_gemm<STARKV_BF16, 0>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((k_latent_gemm<STARKV_F32, 0>), grid, dim3(256), 0, s, a);
+    const dim3 grid((B * n_new + 63) / 64, (a.NS + 63) / 64);
+    if (L.dtype == STARKV_BF16) e = launch_k(ps, k_latent_gemm<STARKV_BF16, 0>, grid, dim3(256), s, a);
+    else e = launch_k(ps, k_latent_gemm<STARKV_F32, 0>, grid, dim3(256), s, a);
   }
+  if (e != hipSuccess) return e;
   return hipGetLastError();
 }
 

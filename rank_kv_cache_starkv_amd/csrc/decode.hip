@@ -55,6 +55,7 @@ int plan_decode(const Layer& L, int B, int n_q, const int32_t* lens, int T_max, 
   g.v_rows = L.v_rows;
   g.v_tile_bytes = L.v_tile_bytes;
   g.T_max = T_max;
+  g.rv_ld = ceil_div(L.r_v, 32) * 32;
   g.latent = L.latent;
   g.dtype = L.dtype;
   g.qscale = (float)(1.4426950408889634 / sqrt((double)L.d_h));
@@ -95,8 +96,11 @@ int plan_decode(const Layer& L, int B, int n_q, const int32_t* lens, int T_max, 
   int n_slices = ceil_div(NB, bpw);
   DecodeWs& w = P->ws;
   // one-M-tile value kernel: slices of up to nbw8 one-N-tile blocks and nbw4 int4 blocks
-  w.nbw8 = std::min(4, std::max(1, env_int("STARKV_NBW8", 2)));
-  w.nbw4 = std::min(2, std::max(1, env_int("STARKV_NBW4", 2)));
+  {
+    const int v8 = env_int("STARKV_NBW8", 2), v4 = env_int("STARKV_NBW4", 2);
+    w.nbw8 = v8 >= 4 ? 4 : (v8 >= 2 ? 2 : 1);
+    w.nbw4 = v4 >= 2 ? 2 : 1;
+  }
   const int nb8 = L.mix() ? L.V8 / 32 : NB;
   w.n_sl8 = ceil_div(nb8, w.nbw8);
   w.n_sl4 = L.mix() ? ceil_div(NB - nb8, w.nbw4) : 0;
@@ -134,10 +138,10 @@ int plan_decode(const Layer& L, int B, int n_q, const int32_t* lens, int T_max, 
   const size_t o_p = o; o = align256(o + (size_t)total_chunks * g.M_pad * kTC * esz_p);
   const size_t o_cm = o; o = align256(o + (size_t)total_chunks * g.M_pad * 4);
   const size_t o_cl = o; o = align256(o + (size_t)total_chunks * g.M_pad * 4);
-  const size_t o_zp = o; o = align256(o + (size_t)total_splits * g.M_pad * L.r_v * 4);
-  const size_t o_sm = o; o = align256(o + (size_t)total_splits * g.M_pad * 4);
+  const size_t o_gmax = o; o = align256(o + (size_t)B * g.M_pad * kMaxSlots * 4);
+  const size_t o_zp = o; o = align256(o + (size_t)total_splits * g.M_pad * g.rv_ld * 4);
   const size_t o_sl = o; o = align256(o + (size_t)total_splits * g.M_pad * 4);
-  const size_t o_zt = o; o = align256(o + (size_t)B * g.M_pad * L.r_v * 4);
+  const size_t o_zt = o; o = align256(o + (size_t)B * g.M_pad * g.rv_ld * 4);
   P->ws_bytes = o;
   uint8_t* base = (uint8_t*)ws_base;
   w.qfrag = base + o_qfrag;
@@ -145,8 +149,8 @@ int plan_decode(const Layer& L, int B, int n_q, const int32_t* lens, int T_max, 
   w.p = base + o_p;
   w.cm = (float*)(base + o_cm);
   w.cl = (float*)(base + o_cl);
+  w.gmax = (int*)(base + o_gmax);
   w.zp = (float*)(base + o_zp);
-  w.sm = (float*)(base + o_sm);
   w.sl = (float*)(base + o_sl);
   w.zt = (float*)(base + o_zt);
   w.nkt_max = nkt_max;
@@ -167,6 +171,7 @@ struct QprojArgs {
   HeadTables heads;
   uint8_t* qfrag;
   float* rowp;
+  int* gmax;
   DecodeGeom g;
   int nkt_max;
   KtList kts;
@@ -200,6 +205,10 @@ __global__ __launch_bounds__(256) void k_qproj(QprojArgs a) {
   const int n8g = (LAT == STARKV_LATENT_MIX84) ? a.heads.n8[gk] : 0;
   const int o8 = (LAT == STARKV_LATENT_MIX84) ? a.heads.off8[gk] : 0;
   const int o4 = (LAT == STARKV_LATENT_MIX84) ? a.heads.off4[gk] : 0;
+
+  // the running-maximum slots of this head's rows start at -inf (the key-score kernel raises them)
+  for (int idx = tid; idx < rph * kMaxSlots; idx += 256)
+    a.gmax[((size_t)b * g.M_pad + gk * rph + idx / kMaxSlots) * kMaxSlots + idx % kMaxSlots] = ord_key(-INFINITY);
 
   for (int rb0 = 0; rb0 < rph; rb0 += RB) {
     const int nrows = min(RB, rph - rb0);
@@ -389,6 +398,7 @@ struct ScoreArgs {
   void* p;
   float* cm;
   float* cl;
+  int* gmax;
   DecodeGeom g;
   int nkt_max;
   int nch_wg;        // 64-token chunks per workgroup
@@ -637,6 +647,7 @@ __global__ __launch_bounds__(256) void k_scores(ScoreArgs a) {
   if (qq == 0) {
     a.cm[(size_t)cg * g.M_pad + i] = m;
     a.cl[(size_t)cg * g.M_pad + i] = l;
+    if (rowvalid) atomicMax(a.gmax + ((size_t)b * g.M_pad + i) * kMaxSlots + cidx % kMaxSlots, ord_key(m));
   }
 }
 
@@ -814,6 +825,8 @@ __global__ __launch_bounds__(256) void k_scores_chunk(ScoreArgs a) {
     if (qq == 0) {
       a.cm[(size_t)cg * g.M_pad + i] = m;
       a.cl[(size_t)cg * g.M_pad + i] = l;
+      if (rowvalid)
+        atomicMax(a.gmax + ((size_t)b * g.M_pad + i) * kMaxSlots + (t0 / kTC) % kMaxSlots, ord_key(m));
     }
   }
 }
@@ -826,14 +839,27 @@ struct ValueArgs {
   const void* p;
   const float* cm;
   const float* cl;
+  const int* gmax;
   float* zp;
-  float* sm;
   float* sl;
   DecodeGeom g;
   SeqTable seq;
   int cps, bpw, NB, V8, n8v, n4v;
-  int n_sl8, nbw8, nbw4;  // one-M-tile kernel: slices of one-N-tile blocks, blocks per slice
+  int n_sl8;  // one-M-tile kernel: slices of one-N-tile blocks (the rest hold int4 blocks)
+  int n_sl, n_splits;  // one-M-tile kernel: slices per split, splits in all
 };
+
+// Row maximum of the base-2 logits of query row `row` (index into [B][M_pad]) over its slots.
+__device__ __forceinline__ float row_max(const int* gmax, size_t row) {
+  const int* p = gmax + row * kMaxSlots;
+  int m = ord_key(-INFINITY);
+#pragma unroll
+  for (int k = 0; k < kMaxSlots / 4; ++k) {
+    const u32x4 v = ld16(p + 4 * k);
+    m = max(m, max(max((int)v[0], (int)v[1]), max((int)v[2], (int)v[3])));
+  }
+  return ord_val(m);
+}
 
 // 8 tokens of one channel (int8 codes in 8 bytes) -> f16x8
 __device__ __forceinline__ f16x8 deq_i8x8(uint32_t w0, uint32_t w1) {
@@ -879,15 +905,12 @@ __global__ __launch_bounds__(256) void k_values(ValueArgs a) {
   const int r = lane & 31, q = lane >> 5;
   const bool is4 = (LAT == STARKV_LATENT_MIX84) && (nb >= a.V8 / 32);
 
-  // split max of the rows this lane feeds as A-fragment rows
+  // row maximum (over the whole sequence) of the rows this lane feeds as A-fragment rows
   float Ms[NMT], lsum[NMT];
 #pragma unroll
   for (int mt = 0; mt < NMT; ++mt) {
-    const int row = mt * 32 + r;
-    float m = -INFINITY;
-    if (row < g.M_q)
-      for (int c = c_lo; c < c_hi; ++c) m = fmaxf(m, a.cm[(size_t)(cbase + c) * g.M_pad + row]);
-    Ms[mt] = m;
+    const int row = min(mt * 32 + r, g.M_q - 1);
+    Ms[mt] = row_max(a.gmax, (size_t)b * g.M_pad + row);
     lsum[mt] = 0.f;
   }
 
@@ -1027,17 +1050,14 @@ __global__ __launch_bounds__(256) void k_values(ValueArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int row = mt * 32 + d32_row(v, q);
-        if (row < g.M_q) a.zp[((size_t)sg * g.M_pad + row) * g.r_v + vc] = acc[mt][nt][v];
+        if (row < g.M_q) a.zp[((size_t)sg * g.M_pad + row) * g.rv_ld + vc] = acc[mt][nt][v];
       }
   }
   if (blockIdx.x == 0 && wave == 0 && q == 0) {
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) {
       const int row = mt * 32 + r;
-      if (row < g.M_q) {
-        a.sm[(size_t)sg * g.M_pad + row] = Ms[mt];
-        a.sl[(size_t)sg * g.M_pad + row] = lsum[mt];
-      }
+      if (row < g.M_q) a.sl[(size_t)sg * g.M_pad + row] = lsum[mt];
     }
   }
 }
@@ -1045,34 +1065,36 @@ __global__ __launch_bounds__(256) void k_values(ValueArgs a) {
 // One M-tile (at most 32 query rows per sequence): workgroup = (slice of value blocks of one
 // kind, split of one sequence); the four waves take interleaved 32-token tiles of the split and
 // each covers every block of the slice, so a probability fragment feeds up to four N-tiles.
-// The waves' accumulators and softmax sums are added through LDS at the end.
-// Slices [0, n_sl8) hold blocks of one N-tile (int8, bf16 or fp32 rows), slices [n_sl8, ...)
-// int4 blocks (two N-tiles each: even and odd channels of the byte pairs).
+// Slices [0, n_sl8) hold NBW8 blocks of one N-tile each (int8, bf16 or fp32 rows), slices
+// [n_sl8, ...) NBW4 int4 blocks (two N-tiles each: even and odd channels of the byte pairs).
+// Each wave double-buffers its tile loads in registers: the loads of the next U tiles are issued
+// before the MFMAs of the current U, and every load is unconditional (addresses of tiles past
+// the wave's last one are clamped to it; those tiles are loaded but never used).  The waves'
+// accumulators and probability sums are added through LDS at the end.
 template <int LAT>
-__global__ __launch_bounds__(256) void k_values1(ValueArgs a) {
-  constexpr int esz = LAT == STARKV_LATENT_F32 ? 4 : (LAT == STARKV_LATENT_BF16 ? 2 : 1);
-  constexpr int NV = esz == 1 ? 1 : (esz == 2 ? 2 : 4);
-  constexpr int NP = LAT == STARKV_LATENT_F32 ? 2 : 1;
-  constexpr int U = LAT == STARKV_LATENT_F32 ? 1 : (LAT == STARKV_LATENT_BF16 ? 2 : 4);
-  constexpr int NBMAX = 4;
-  __shared__ float sred[3][4][16][64];
-  __shared__ float smax[4][32];
-  __shared__ float ssum[4][32];
+struct VLayout {
+  static constexpr int esz = LAT == STARKV_LATENT_F32 ? 4 : (LAT == STARKV_LATENT_BF16 ? 2 : 1);
+  static constexpr int NV = esz == 1 ? 1 : (esz == 2 ? 2 : 4);  // 16-byte value loads per lane per block
+  static constexpr int NP = LAT == STARKV_LATENT_F32 ? 2 : 1;   // 16-byte probability loads per half
+};
+
+template <int LAT, int NBW>
+struct VTile {
+  u32x4 v[NBW][VLayout<LAT>::NV];
+  u32x4 p[2][VLayout<LAT>::NP];
+  float cm, cl;
+};
+
+template <int LAT, int NBW, bool IS4>
+__device__ __forceinline__ void values1_run(const ValueArgs& a, int slice, int sg, int nb0, int nblk,
+                                            float* sred, float (*ssum)[32]) {
+  using VL = VLayout<LAT>;
+  constexpr int NT = IS4 ? 2 * NBW : NBW;  // accumulator tiles
+  constexpr int TU = NBW * VL::NV + 2 * VL::NP;  // 16-byte loads per lane per tile
+  constexpr int U = TU <= 6 ? 2 : 1;       // tiles per pipeline stage
   const DecodeGeom& g = a.g;
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int r = lane & 31, q = lane >> 5;
-  const int slice = blockIdx.x;
-  const bool is4 = (LAT == STARKV_LATENT_MIX84) && slice >= a.n_sl8;  // workgroup-uniform
-  int nb0, nb_end;
-  if (!is4) {
-    nb0 = slice * a.nbw8;
-    nb_end = min(nb0 + a.nbw8, LAT == STARKV_LATENT_MIX84 ? a.V8 / 32 : a.NB);
-  } else {
-    nb0 = a.V8 / 32 + (slice - a.n_sl8) * a.nbw4;
-    nb_end = min(nb0 + a.nbw4, a.NB);
-  }
-  const int nblk = nb_end - nb0;
-  const int sg = blockIdx.y;
   const int b = find_segment(a.seq.split_off, g.B, sg);
   const int s = sg - a.seq.split_off[b];
   const int cbase = a.seq.chunk_off[b];
@@ -1080,148 +1102,148 @@ __global__ __launch_bounds__(256) void k_values1(ValueArgs a) {
   const int c_lo = s * a.cps, c_hi = min(c_lo + a.cps, nch);
   const int len = a.seq.lens[b];
   const bool rok = r < g.M_q;
-
-  // split max of row r, shared by the waves
-  float m = -INFINITY;
-  if (rok)
-    for (int c = c_lo + wave; c < c_hi; c += 4) m = fmaxf(m, a.cm[(size_t)(cbase + c) * g.M_pad + r]);
-  if (q == 0) smax[wave][r] = m;
-  __syncthreads();
-  const float Ms = fmaxf(fmaxf(smax[0][r], smax[1][r]), fmaxf(smax[2][r], smax[3][r]));
-  float lsum = 0.f;
-
-  f32x16 acc[4];
+  const size_t prow = (size_t)(rok ? r : 0);
+  const float M = row_max(a.gmax, (size_t)b * g.M_pad + prow);
+  // tiles of this wave: chunks c_lo + wave + 4k, k < ntw (wave-uniform)
+  const int ntw = c_lo + wave < c_hi ? (c_hi - c_lo - wave + 3) / 4 : 0;
+  const uint8_t* vb = a.v_tiles + (size_t)b * (g.T_max / kTT) * g.v_tile_bytes + 16 * VL::NV * q;
+  int boff[NBW];
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+  for (int j = 0; j < NBW; ++j) boff[j] = ((nb0 + (j < nblk ? j : 0)) * 32 + r) * kTT * VL::esz;
+
+  f32x16 acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[t][v] = 0.f;
+  float lsum = 0.f;
 
-  const uint8_t* vb = a.v_tiles + (size_t)b * (g.T_max / kTT) * g.v_tile_bytes;
-  for (int c0 = c_lo + wave; c0 < c_hi; c0 += 4 * U) {
-    u32x4 vr[U][NBMAX][NV];
-    u32x4 pr[U][2][NP];
-    float cmv[U], clv[U];
+  auto load = [&](VTile<LAT, NBW>& t, int k) {
+    const int c = c_lo + wave + 4 * min(k, ntw - 1);
+    const uint8_t* tb = vb + (size_t)c * g.v_tile_bytes;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int c = c0 + 4 * u;
-      const bool on = c < c_hi;  // wave-uniform
-      const int cc = on ? c : c_lo;
-      const size_t cgl = (size_t)(cbase + cc);
+    for (int j = 0; j < NBW; ++j)
 #pragma unroll
-      for (int j = 0; j < NBMAX; ++j) {
-        const bool bon = on && j < nblk;
-        const uint8_t* trow = vb + (size_t)cc * g.v_tile_bytes + (size_t)((nb0 + (bon ? j : 0)) * 32 + r) * kTT * esz;
+      for (int x = 0; x < VL::NV; ++x) t.v[j][x] = ld16(tb + boff[j] + 16 * x);
+    const size_t cr = (size_t)(cbase + c) * g.M_pad + prow;
 #pragma unroll
-        for (int k = 0; k < NV; ++k) vr[u][j][k] = bon ? ld16(trow + 16 * NV * q + 16 * k) : u32x4{0, 0, 0, 0};
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int x = 0; x < VL::NP; ++x) {
+        const size_t pe = cr * kTC + 16 * q + 8 * h + 4 * x;
+        t.p[h][x] = LAT == STARKV_LATENT_F32 ? ld16((const float*)a.p + pe) : ld16((const uint16_t*)a.p + pe);
       }
-      const bool pon = on && rok;
-      cmv[u] = pon ? a.cm[cgl * g.M_pad + r] : -INFINITY;
-      clv[u] = pon ? a.cl[cgl * g.M_pad + r] : 0.f;
+    t.cm = a.cm[cr];
+    t.cl = a.cl[cr];
+  };
+
+  auto compute = [&](VTile<LAT, NBW>& t, int k) {
+    if (k >= ntw) return;  // uniform
+    const int tt0 = (c_lo + wave + 4 * k) * kTC;
+    // rows past M_q read row 0's statistics; their results are never stored
+    const float alpha = (t.cm == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(t.cm - M);
+    lsum += alpha * t.cl;
+    if (VL::esz > 1 && tt0 + kTT > len) {
+      // zero the elements of tokens at or past the length (their bits may be anything)
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int j = 0; j < NBW; ++j)
 #pragma unroll
-        for (int k = 0; k < NP; ++k) {
-          const size_t pe = (cgl * g.M_pad + r) * kTC + 16 * q + 8 * h + 4 * k;
-          pr[u][h][k] = pon ? (LAT == STARKV_LATENT_F32 ? ld16((const float*)a.p + pe) : ld16((const uint16_t*)a.p + pe))
-                            : u32x4{0, 0, 0, 0};
+        for (int e = 0; e < 16; ++e) {
+          const int tok = tt0 + 16 * q + e;
+          if (tok >= len) {
+            if (VL::esz == 2) {
+              const uint32_t keep = (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+              t.v[j][e >> 3][(e >> 1) & 3] &= keep;
+            } else {
+              t.v[j][e >> 2][e & 3] = 0u;
+            }
+          }
         }
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int c = c0 + 4 * u;
-      if (c >= c_hi) break;
-      const int tt0 = c * kTC;
-      const float alpha = (cmv[u] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(cmv[u] - Ms);
-      lsum += alpha * clv[u];
-      if (esz > 1 && tt0 + kTT > len) {
+    for (int h = 0; h < 2; ++h) {
+      if (LAT == STARKV_LATENT_F32) {
+        const u32x4 p0 = t.p[h][0], p1 = t.p[h][VL::NP - 1];
 #pragma unroll
-        for (int j = 0; j < NBMAX; ++j)
+        for (int j = 0; j < NBW; ++j) {
+          if (j >= nblk) continue;
+          const u32x4 v0 = t.v[j][2 * h], v1 = t.v[j][(2 * h + 1) % VL::NV];
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int t = tt0 + 16 * q + e;
-            if (t >= len) {
-              if (esz == 2) {
-                const uint32_t keep = (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
-                vr[u][j][e >> 3][(e >> 1) & 3] = vr[u][j][e >> 3][(e >> 1) & 3] & keep;
-              } else {
-                vr[u][j][e >> 2][e & 3] = 0u;
-              }
-            }
-          }
-      }
+          for (int e = 0; e < 4; ++e)
+            acc[j] = mfma32_f32(__uint_as_float(p0[e]) * alpha, __uint_as_float(v0[e]), acc[j]);
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        if (LAT == STARKV_LATENT_F32) {
-          const u32x4 p0 = pr[u][h][0], p1 = pr[u][h][NP - 1];
+          for (int e = 0; e < 4; ++e)
+            acc[j] = mfma32_f32(__uint_as_float(p1[e]) * alpha, __uint_as_float(v1[e]), acc[j]);
+        }
+      } else if (LAT == STARKV_LATENT_BF16) {
+        const u32x4 praw = t.p[h][0];
+        u32x4 ps;
 #pragma unroll
-          for (int j = 0; j < NBMAX; ++j) {
-            if (j >= nblk) continue;
-            const u32x4 v0 = vr[u][j][2 * h], v1 = vr[u][j][2 * h + 1];
+        for (int e = 0; e < 4; ++e) {
+          const float x0 = bf16_to_f32((uint16_t)(praw[e] & 0xFFFF)) * alpha;
+          const float x1 = bf16_to_f32((uint16_t)(praw[e] >> 16)) * alpha;
+          ps[e] = (uint32_t)f32_to_bf16(x0) | ((uint32_t)f32_to_bf16(x1) << 16);
+        }
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              acc[j] = mfma32_f32(__uint_as_float(p0[e]) * alpha, __uint_as_float(v0[e]), acc[j]);
+        for (int j = 0; j < NBW; ++j) {
+          if (j >= nblk) continue;
+          acc[j] = mfma32_bf16(as_bf16x8(ps), as_bf16x8(t.v[j][h % VL::NV]), acc[j]);
+        }
+      } else {
+        const f16x8 pin = as_f16x8(t.p[h][0]);
+        f16x8 ps;
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              acc[j] = mfma32_f32(__uint_as_float(p1[e]) * alpha, __uint_as_float(v1[e]), acc[j]);
-          }
-        } else if (LAT == STARKV_LATENT_BF16) {
-          const u32x4 praw = pr[u][h][0];
-          u32x4 ps;
+        for (int e = 0; e < 8; ++e) ps[e] = (_Float16)((float)pin[e] * alpha);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float x0 = bf16_to_f32((uint16_t)(praw[e] & 0xFFFF)) * alpha;
-            const float x1 = bf16_to_f32((uint16_t)(praw[e] >> 16)) * alpha;
-            ps[e] = (uint32_t)f32_to_bf16(x0) | ((uint32_t)f32_to_bf16(x1) << 16);
-          }
-#pragma unroll
-          for (int j = 0; j < NBMAX; ++j) {
-            if (j >= nblk) continue;
-            acc[j] = mfma32_bf16(as_bf16x8(ps), as_bf16x8(vr[u][j][h]), acc[j]);
-          }
-        } else {
-          const f16x8 pin = as_f16x8(pr[u][h][0]);
-          f16x8 ps;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) ps[e] = (_Float16)((float)pin[e] * alpha);
-          if (!is4) {
-#pragma unroll
-            for (int j = 0; j < NBMAX; ++j) {
-              if (j >= nblk) continue;
-              acc[j] = mfma32_f16(ps, deq_i8x8(vr[u][j][0][2 * h], vr[u][j][0][2 * h + 1]), acc[j]);
-            }
+        for (int j = 0; j < NBW; ++j) {
+          if (j >= nblk) continue;
+          if (!IS4) {
+            acc[j] = mfma32_f16(ps, deq_i8x8(t.v[j][0][2 * h], t.v[j][0][2 * h + 1]), acc[j]);
           } else {
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-              if (j >= nblk) continue;
-              f16x8 ev, od;
-              deq_i4x8(vr[u][j][0][2 * h], vr[u][j][0][2 * h + 1], ev, od);
-              acc[2 * j] = mfma32_f16(ps, ev, acc[2 * j]);
-              acc[2 * j + 1] = mfma32_f16(ps, od, acc[2 * j + 1]);
-            }
+            f16x8 ev, od;
+            deq_i4x8(t.v[j][0][2 * h], t.v[j][0][2 * h + 1], ev, od);
+            acc[(2 * j) % NT] = mfma32_f16(ps, ev, acc[(2 * j) % NT]);
+            acc[(2 * j + 1) % NT] = mfma32_f16(ps, od, acc[(2 * j + 1) % NT]);
           }
         }
       }
+    }
+  };
+
+  if (ntw > 0) {
+    VTile<LAT, NBW> ta[U], tb[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) load(ta[u], u);
+    for (int k0 = 0; k0 < ntw; k0 += 2 * U) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) load(tb[u], k0 + U + u);
+#pragma unroll
+      for (int u = 0; u < U; ++u) compute(ta[u], k0 + u);
+      if (k0 + U >= ntw) break;
+#pragma unroll
+      for (int u = 0; u < U; ++u) load(ta[u], k0 + 2 * U + u);
+#pragma unroll
+      for (int u = 0; u < U; ++u) compute(tb[u], k0 + U + u);
     }
   }
-  // add the four waves' accumulators and sums
-  const int ntile = is4 ? 2 * nblk : nblk;
-  if (wave > 0) {
+
+  // add the four waves' accumulators and sums: every wave parks its accumulators in LDS, then
+  // wave w adds and stores elements v = 4w .. 4w + 3 of every tile
+  const int ntile = IS4 ? 2 * nblk : nblk;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      if (t >= ntile) continue;
+  for (int t = 0; t < NT; ++t) {
+    if (t >= ntile) continue;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) sred[wave - 1][t][v][lane] = acc[t][v];
-    }
+    for (int v = 0; v < 16; ++v) sred[((wave * NT + t) * 16 + v) * 64 + lane] = acc[t][v];
   }
   if (q == 0) ssum[wave][r] = lsum;
   __syncthreads();
-  if (wave != 0) return;
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
+  for (int t = 0; t < NT; ++t) {
     if (t >= ntile) continue;
     int vc;
     bool cok;
-    if (!is4) {
+    if (!IS4) {
       vc = (nb0 + t) * 32 + r;
       cok = vc < (LAT == STARKV_LATENT_MIX84 ? a.n8v : g.r_v);
     } else {
@@ -1230,228 +1252,260 @@ __global__ __launch_bounds__(256) void k_values1(ValueArgs a) {
       vc = a.n8v + w;
     }
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const float z = acc[t][v] + sred[0][t][v][lane] + sred[1][t][v][lane] + sred[2][t][v][lane];
+    for (int vv = 0; vv < 4; ++vv) {
+      const int v = 4 * wave + vv;
+      float z = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) z += sred[((w * NT + t) * 16 + v) * 64 + lane];
       const int row = d32_row(v, q);
-      if (cok && row < g.M_q) a.zp[((size_t)sg * g.M_pad + row) * g.r_v + vc] = z;
+      if (cok && row < g.M_q) a.zp[((size_t)sg * g.M_pad + row) * g.rv_ld + vc] = z;
     }
   }
-  if (slice == 0 && q == 0 && rok) {
-    a.sm[(size_t)sg * g.M_pad + r] = Ms;
+  if (slice == 0 && wave == 0 && q == 0 && rok)
     a.sl[(size_t)sg * g.M_pad + r] = ssum[0][r] + ssum[1][r] + ssum[2][r] + ssum[3][r];
+}
+
+// Grid: one dimension of n_sl x (n_splits rounded up to 8) workgroups.  Workgroups are handed to
+// the eight XCDs in turn (id mod 8), so the k-th workgroup of XCD x takes slice k mod n_sl of
+// split 8 (k / n_sl) + x: all slices of a split run on one XCD and share its L2 copy of the
+// split's probabilities.
+template <int LAT, int NBW8, int NBW4>
+__global__ __launch_bounds__(256) void k_values1(ValueArgs a) {
+  // room for four accumulator tiles per wave whatever the instance needs: at 64 KiB of LDS at
+  // most two workgroups share a CU, so the 2-per-CU grids spread evenly over the CUs
+  __shared__ float sred[4 * 4 * 16 * 64];
+  __shared__ float ssum[4][32];
+  const int xcd = blockIdx.x & 7, k = blockIdx.x >> 3;
+  const int slice = k % a.n_sl;
+  const int sg = 8 * (k / a.n_sl) + xcd;
+  if (sg >= a.n_splits) return;
+  if (LAT == STARKV_LATENT_MIX84 && slice >= a.n_sl8) {
+    const int nb0 = a.V8 / 32 + (slice - a.n_sl8) * NBW4;
+    values1_run<LAT, NBW4, true>(a, slice, sg, nb0, min(NBW4, a.NB - nb0), sred, ssum);
+  } else {
+    const int nb0 = slice * NBW8;
+    const int nbe = LAT == STARKV_LATENT_MIX84 ? a.V8 / 32 : a.NB;
+    values1_run<LAT, NBW8, false>(a, slice, sg, nb0, min(NBW8, nbe - nb0), sred, ssum);
   }
 }
 
 // ===========================================================================
-// merge + up-projection: out = (sum_s w_s z_s) * scale_v B_v^g / l
+// merge + up-projection: out = (sum_s z_s) * scale_v B_v^g / (sum_s l_s)
 
 struct MergeArgs {
   const float* zp;
-  const float* sm;
   const float* sl;
-  float* zt;                // [B][M_pad][r_v] merged, scaled, normalised value latent
-  const void* B_vt;
-  const uint16_t* vscales;  // value-channel scales (mix84) or null
+  float* zt;                // [B][M_pad][rv_ld] merged, scaled, normalised value latent
+  const void* B_vt;         // [H_kv * d_h][r_v]
+  const uint16_t* vscales;  // [r_v] f16 (mix84) or null
   void* out;
   DecodeGeom g;
   SeqTable seq;
 };
 
-// Split merge (log-sum-exp): for sequence b and row i, M = max_s m_s, w_s = 2^(m_s - M),
-// l = sum_s w_s l_s, and z~[c] = (sum_s w_s z_s[c]) * scale_c / l.  Workgroup = 4 rows x 64
-// channels of one sequence; one thread per (row, channel).
+// Split merge.  Every split of a sequence weighted its tiles against the same row maximum (the
+// whole sequence's), so the merge is a plain sum, taken in split order: z~[c] = (sum_s z_s[c]) *
+// scale_c / (sum_s l_s), and zero in the padding channels [r_v, rv_ld).  Workgroup = 4 rows x
+// 256 channels of one sequence; a thread takes 4 channels with 16-byte loads of every split.
 __global__ __launch_bounds__(256) void k_zmerge(MergeArgs a) {
   const DecodeGeom& g = a.g;
-  __shared__ float wts[4][kMaxSplitsPerSeq];
-  __shared__ float invl[4];
   const int b = blockIdx.z;
   const int tid = threadIdx.x;
-  const int rn = tid >> 6, cn = tid & 63;
-  const int i = blockIdx.y * 4 + rn;
-  const int c = blockIdx.x * 64 + cn;
+  const int i = blockIdx.y * 4 + (tid >> 6);
+  const int c = blockIdx.x * 256 + (tid & 63) * 4;
+  if (i >= g.M_q || c >= g.rv_ld) return;
   const int s0 = a.seq.split_off[b], ns = a.seq.split_off[b + 1] - s0;
-  if (cn == 0) {
-    float il = 0.f;
-    if (i < g.M_q) {
-      float M = -INFINITY;
-      for (int s = 0; s < ns; ++s) M = fmaxf(M, a.sm[(size_t)(s0 + s) * g.M_pad + i]);
-      float l = 0.f;
-      for (int s = 0; s < ns; ++s) {
-        const float ms = a.sm[(size_t)(s0 + s) * g.M_pad + i];
-        const float wgt = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms - M);
-        wts[rn][s] = wgt;
-        l += wgt * a.sl[(size_t)(s0 + s) * g.M_pad + i];
-      }
-      il = 1.f / l;
+  const float* zc = a.zp + ((size_t)s0 * g.M_pad + i) * g.rv_ld + c;
+  const float* lc = a.sl + (size_t)s0 * g.M_pad + i;
+  const size_t zs = (size_t)g.M_pad * g.rv_ld;
+  float z[4] = {0.f, 0.f, 0.f, 0.f};
+  float l = 0.f;
+  for (int s = 0; s < ns; s += 8) {
+    u32x4 v[8];
+    float lv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int ss = min(s + u, ns - 1);
+      v[u] = ld16(zc + (size_t)ss * zs);
+      lv[u] = lc[(size_t)ss * g.M_pad];
     }
-    invl[rn] = il;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (s + u < ns) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) z[e] += __uint_as_float(v[u][e]);
+        l += lv[u];
+      }
+    }
   }
-  __syncthreads();
-  if (i >= g.M_q || c >= g.r_v) return;
-  const float* zc = a.zp + ((size_t)s0 * g.M_pad + i) * g.r_v + c;
-  const size_t zs = (size_t)g.M_pad * g.r_v;
-  float z = 0.f;
-  int s = 0;
-  for (; s + 4 <= ns; s += 4) {
-    const float z0 = zc[(s + 0) * zs], z1 = zc[(s + 1) * zs], z2 = zc[(s + 2) * zs], z3 = zc[(s + 3) * zs];
-    z = fmaf(wts[rn][s], z0, z);
-    z = fmaf(wts[rn][s + 1], z1, z);
-    z = fmaf(wts[rn][s + 2], z2, z);
-    z = fmaf(wts[rn][s + 3], z3, z);
+  const float il = 1.f / l;
+  u32x4 o;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int ce = c + e;
+    float sc = il;
+    if (a.vscales) sc *= f16_to_f32(a.vscales[min(ce, g.r_v - 1)]);
+    o[e] = __float_as_uint(ce < g.r_v ? z[e] * sc : 0.f);
   }
-  for (; s < ns; ++s) z = fmaf(wts[rn][s], zc[s * zs], z);
-  float sc = invl[rn];
-  if (a.vscales) sc *= f16_to_f32(a.vscales[c]);
-  a.zt[((size_t)b * g.M_pad + i) * g.r_v + c] = z * sc;
+  st16(a.zt + ((size_t)b * g.M_pad + i) * g.rv_ld + c, o);
 }
 
-// Up-projection out_i = z~_i B_v^g for the rows of KV head g.  Workgroup = (g, 32-column slice
-// of d_h, 16-row tile of g's rows over all sequences); the four waves split K = r_v and their
-// partial outputs are added through LDS.  bf16: z~ split into hi + lo bf16 parts (two MFMAs).
-template <int DT>
+// Up-projection out_i = z~_i B_v^g for the rows of KV head g.  Workgroup = (g, 16-column slice of
+// d_h, 16-row tile of g's rows over all sequences); the four waves split K = rv_ld in 32-channel
+// chunks and add their partial outputs through LDS.  Every load is unconditional: rows past the
+// tile's end read its last row (their outputs are not stored), chunks past a wave's range repeat
+// its last chunk (not used), and channels at or past r_v are zero in z~ and masked in B_v.
+// bf16: z~ split into hi + lo bf16 parts (two MFMAs).  VEC: r_v % 8 == 0, so 8 channels of a
+// B_v^T row are one 16-byte load; otherwise they are loaded one by one.
+template <int DT, bool VEC>
 __global__ __launch_bounds__(256) void k_upproj(MergeArgs a) {
   const DecodeGeom& g = a.g;
-  const int nsl_n = g.d_h / 32;
+  const int nsl_n = g.d_h / 16;
   const int gk = blockIdx.x / nsl_n, nsl = blockIdx.x % nsl_n;
   const int rph = g.G * g.n_q;
   const int Rg = g.B * rph;
-  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int n = lane & 15, qq = lane >> 4;
-  __shared__ float red[3][2][4][64];
-  const int rr = blockIdx.y * 16 + n;  // A-fragment row of this lane
-  const bool rv = rr < Rg;
-  const int bb = rv ? rr / rph : 0;
-  const int ii = gk * rph + (rv ? rr % rph : 0);
-  const float* zr = a.zt + ((size_t)bb * g.M_pad + ii) * g.r_v;
-  const bool vec = (g.r_v & 7) == 0;
-  const int nch = (g.r_v + 31) / 32;
-  const int per = (nch + 3) / 4;
-  const int k_beg = wave * per * 32, k_end = min(g.r_v, (wave + 1) * per * 32);
-  f32x4 acc[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
+  __shared__ float red[3][4][64];
+  const int rr = min((int)blockIdx.y * 16 + n, Rg - 1);  // A-fragment row of this lane
+  const int bb = rr / rph;
+  const int ii = gk * rph + rr % rph;
+  const float* zr = a.zt + ((size_t)bb * g.M_pad + ii) * g.rv_ld + 8 * qq;
+  const int col = gk * g.d_h + nsl * 16 + n;  // B_v^T row of this lane's output column
+  const int nchk = g.rv_ld / 32;
+  const int per = (nchk + 3) / 4;
+  const int k_beg = wave * per, k_end = min(nchk, k_beg + per);
+  f32x4 acc = {0, 0, 0, 0};
   constexpr int KU = 8;  // 32-channel chunks in flight
-  for (int kc0 = k_beg; kc0 < k_end; kc0 += 32 * KU) {
-    float z[KU][8];
-    u32x4 bw[KU][2][DT == STARKV_F32 ? 2 : 1];
+  for (int kc0 = k_beg; kc0 < k_end; kc0 += KU) {
+    u32x4 z[KU][2];
+    u32x4 bw[KU][DT == STARKV_F32 ? 2 : 1];
 #pragma unroll
     for (int u = 0; u < KU; ++u) {
-      const int c = kc0 + 32 * u + 8 * qq;
-      const bool on = kc0 + 32 * u < k_end;
-      if (on && rv && vec && c + 8 <= g.r_v) {
-        const u32x4 v0 = ld16(zr + c), v1 = ld16(zr + c + 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          z[u][e] = __uint_as_float(v0[e]);
-          z[u][4 + e] = __uint_as_float(v1[e]);
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) z[u][e] = (on && rv && c + e < g.r_v) ? zr[c + e] : 0.f;
-      }
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int col = gk * g.d_h + (2 * nsl + t) * 16 + n;  // B_v^T row
-        if (DT == STARKV_F32) {
-          const float* bp = (const float*)a.B_vt + (size_t)col * g.r_v;
+      const bool live = kc0 + u < k_end;  // a repeated chunk contributes zero (B masked)
+      const int c = 32 * min(kc0 + u, k_end - 1) + 8 * qq;  // first channel of this lane's 8
+      z[u][0] = ld16(zr + 32 * min(kc0 + u, k_end - 1));
+      z[u][1] = ld16(zr + 32 * min(kc0 + u, k_end - 1) + 4);
+      if (DT == STARKV_F32) {
+        const float* bp = (const float*)a.B_vt + (size_t)col * g.r_v;
+        if (VEC) {
+          const bool ok = live && c < g.r_v;
+          const int cc = ok ? c : 0;
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
-            u32x4 v;
-            if (on && vec && c + 8 <= g.r_v) {
-              v = ld16(bp + c + 4 * h);
-            } else {
-#pragma unroll
-              for (int e = 0; e < 4; ++e) v[e] = (on && c + 4 * h + e < g.r_v) ? __float_as_uint(bp[c + 4 * h + e]) : 0u;
-            }
-            bw[u][t][h] = v;
+            const u32x4 v = ld16(bp + cc + 4 * h);
+            bw[u][h % 2] = ok ? v : u32x4{0, 0, 0, 0};
           }
         } else {
-          const uint16_t* bp = (const uint16_t*)a.B_vt + (size_t)col * g.r_v;
-          u32x4 v;
-          if (on && vec && c + 8 <= g.r_v) {
-            v = ld16(bp + c);
-          } else {
 #pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) {
-              const uint32_t b0 = (on && c + 2 * e2 < g.r_v) ? bp[c + 2 * e2] : 0u;
-              const uint32_t b1 = (on && c + 2 * e2 + 1 < g.r_v) ? bp[c + 2 * e2 + 1] : 0u;
-              v[e2] = b0 | (b1 << 16);
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int ce = c + 4 * h + e;
+              const float x = bp[min(ce, g.r_v - 1)];
+              bw[u][h % 2][e] = (live && ce < g.r_v) ? __float_as_uint(x) : 0u;
             }
+        }
+      } else {
+        const uint16_t* bp = (const uint16_t*)a.B_vt + (size_t)col * g.r_v;
+        if (VEC) {
+          const bool ok = live && c < g.r_v;
+          const u32x4 v = ld16(bp + (ok ? c : 0));
+          bw[u][0] = ok ? v : u32x4{0, 0, 0, 0};
+        } else {
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2) {
+            const int ce = c + 2 * e2;
+            const uint32_t b0 = bp[min(ce, g.r_v - 1)], b1 = bp[min(ce + 1, g.r_v - 1)];
+            bw[u][0][e2] = (live && ce < g.r_v ? b0 : 0u) | ((live && ce + 1 < g.r_v ? b1 : 0u) << 16);
           }
-          bw[u][t][0] = v;
         }
       }
     }
+    __builtin_amdgcn_sched_barrier(0);  // keep every load of the batch ahead of the MFMAs
 #pragma unroll
     for (int u = 0; u < KU; ++u) {
       if (DT == STARKV_F32) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[t] = mfma16_f32(z[u][4 * h + e], __uint_as_float(bw[u][t][h][e]), acc[t]);
+          for (int e = 0; e < 4; ++e)
+            acc = mfma16_f32(__uint_as_float(z[u][h][e]), __uint_as_float(bw[u][h % 2][e]), acc);
       } else {
         u32x4 ah, al;
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
-          const uint16_t h0 = f32_to_bf16(z[u][2 * e2]), h1 = f32_to_bf16(z[u][2 * e2 + 1]);
-          const uint16_t l0 = f32_to_bf16(z[u][2 * e2] - bf16_to_f32(h0));
-          const uint16_t l1 = f32_to_bf16(z[u][2 * e2 + 1] - bf16_to_f32(h1));
+          const float z0 = __uint_as_float(z[u][e2 >> 1][2 * (e2 & 1)]);
+          const float z1 = __uint_as_float(z[u][e2 >> 1][2 * (e2 & 1) + 1]);
+          const uint16_t h0 = f32_to_bf16(z0), h1 = f32_to_bf16(z1);
+          const uint16_t l0 = f32_to_bf16(z0 - bf16_to_f32(h0));
+          const uint16_t l1 = f32_to_bf16(z1 - bf16_to_f32(h1));
           ah[e2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
           al[e2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
         }
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          acc[t] = mfma16_bf16(as_bf16x8(ah), as_bf16x8(bw[u][t][0]), acc[t]);
-          acc[t] = mfma16_bf16(as_bf16x8(al), as_bf16x8(bw[u][t][0]), acc[t]);
-        }
+        acc = mfma16_bf16(as_bf16x8(ah), as_bf16x8(bw[u][0]), acc);
+        acc = mfma16_bf16(as_bf16x8(al), as_bf16x8(bw[u][0]), acc);
       }
     }
   }
   if (wave > 0) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) red[wave - 1][t][v][lane] = acc[t][v];
+    for (int v = 0; v < 4; ++v) red[wave - 1][v][lane] = acc[v];
   }
   __syncthreads();
   if (wave != 0) return;
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const float o = acc[t][v] + red[0][t][v][lane] + red[1][t][v][lane] + red[2][t][v][lane];
-      const int orow = blockIdx.y * 16 + 4 * qq + v;  // D row = row within the tile; D column = n
-      if (orow >= Rg) continue;
-      const int ob = orow / rph, iw = orow % rph;
-      const int hh = iw / g.n_q, j = iw % g.n_q;
-      const int h = gk * g.G + hh;
-      const size_t off = (((size_t)ob * g.n_q + j) * g.H_q + h) * g.d_h + (2 * nsl + t) * 16 + n;
-      if (DT == STARKV_F32) ((float*)a.out)[off] = o;
-      else ((uint16_t*)a.out)[off] = f32_to_bf16(o);
-    }
+  for (int v = 0; v < 4; ++v) {
+    const float o = acc[v] + red[0][v][lane] + red[1][v][lane] + red[2][v][lane];
+    const int orow = blockIdx.y * 16 + 4 * qq + v;  // D row = row within the tile; D column = n
+    if (orow >= Rg) continue;
+    const int ob = orow / rph, iw = orow % rph;
+    const int hh = iw / g.n_q, j = iw % g.n_q;
+    const int h = gk * g.G + hh;
+    const size_t off = (((size_t)ob * g.n_q + j) * g.H_q + h) * g.d_h + nsl * 16 + n;
+    if (DT == STARKV_F32) ((float*)a.out)[off] = o;
+    else ((uint16_t*)a.out)[off] = f32_to_bf16(o);
+  }
 }
 
 // ===========================================================================
 
 template <int LAT>
-static void launch_values_nmt(int nmt, dim3 grid, dim3 block, hipStream_t s, const ValueArgs& va) {
+static hipError_t launch_values_nmt(const ProfScope& ps, int nmt, dim3 grid, dim3 block, hipStream_t s,
+                                    const ValueArgs& va) {
   switch (nmt) {
-    case 1: hipLaunchKernelGGL((k_values<LAT, 1>), grid, block, 0, s, va); break;
-    case 2: hipLaunchKernelGGL((k_values<LAT, 2>), grid, block, 0, s, va); break;
-    case 3: hipLaunchKernelGGL((k_values<LAT, 3>), grid, block, 0, s, va); break;
-    case 4: hipLaunchKernelGGL((k_values<LAT, 4>), grid, block, 0, s, va); break;
-    case 5: hipLaunchKernelGGL((k_values<LAT, 5>), grid, block, 0, s, va); break;
-    case 6: hipLaunchKernelGGL((k_values<LAT, 6>), grid, block, 0, s, va); break;
-    case 7: hipLaunchKernelGGL((k_values<LAT, 7>), grid, block, 0, s, va); break;
-    default: hipLaunchKernelGGL((k_values<LAT, 8>), grid, block, 0, s, va); break;
+    case 1: return launch_k(ps, k_values<LAT, 1>, grid, block, s, va);
+    case 2: return launch_k(ps, k_values<LAT, 2>, grid, block, s, va);
+    case 3: return launch_k(ps, k_values<LAT, 3>, grid, block, s, va);
+    case 4: return launch_k(ps, k_values<LAT, 4>, grid, block, s, va);
+    case 5: return launch_k(ps, k_values<LAT, 5>, grid, block, s, va);
+    case 6: return launch_k(ps, k_values<LAT, 6>, grid, block, s, va);
+    case 7: return launch_k(ps, k_values<LAT, 7>, grid, block, s, va);
+    default: return launch_k(ps, k_values<LAT, 8>, grid, block, s, va);
   }
+}
+
+template <int LAT>
+static hipError_t launch_values1(const ProfScope& ps, int nbw8, int nbw4, dim3 grid, hipStream_t s,
+                                 const ValueArgs& va) {
+  const dim3 blk(256);
+  if (LAT != STARKV_LATENT_MIX84) nbw4 = 1;
+  if (nbw4 == 1) {
+    if (nbw8 == 1) return launch_k(ps, k_values1<LAT, 1, 1>, grid, blk, s, va);
+    if (nbw8 == 2) return launch_k(ps, k_values1<LAT, 2, 1>, grid, blk, s, va);
+    return launch_k(ps, k_values1<LAT, 4, 1>, grid, blk, s, va);
+  }
+  if (nbw8 == 1) return launch_k(ps, k_values1<LAT, 1, 2>, grid, blk, s, va);
+  if (nbw8 == 2) return launch_k(ps, k_values1<LAT, 2, 2>, grid, blk, s, va);
+  return launch_k(ps, k_values1<LAT, 4, 2>, grid, blk, s, va);
 }
 
 hipError_t launch_decode(const Layer& L, const DecodePlan& plan, const KtList& kts, const SeqTable& seq,
                          const void* q, void* out, const void* k_rows, const void* v_tiles, hipStream_t s) {
   const DecodeGeom& g = plan.g;
   const DecodeWs& w = plan.ws;
-  // 1. query fragments
+  hipError_t e = hipSuccess;
+  // 1. query fragments (and the running-maximum slots set to -inf)
   QprojArgs qa;
   qa.q = q;
   qa.B_k = L.B_k;
@@ -1459,19 +1513,17 @@ hipError_t launch_decode(const Layer& L, const DecodePlan& plan, const KtList& k
   qa.heads = L.heads();
   qa.qfrag = (uint8_t*)w.qfrag;
   qa.rowp = w.rowp;
+  qa.gmax = w.gmax;
   qa.g = g;
   qa.nkt_max = w.nkt_max;
   qa.kts = kts;
-  dim3 gq(g.H_kv, g.B);
   {
-  ProfScope ps("decode_qproj", s);
-  if (L.dtype == STARKV_F32) {
-    hipLaunchKernelGGL((k_qproj<STARKV_F32, STARKV_LATENT_F32>), gq, dim3(256), 0, s, qa);
-  } else if (L.latent == STARKV_LATENT_BF16) {
-    hipLaunchKernelGGL((k_qproj<STARKV_BF16, STARKV_LATENT_BF16>), gq, dim3(256), 0, s, qa);
-  } else {
-    hipLaunchKernelGGL((k_qproj<STARKV_BF16, STARKV_LATENT_MIX84>), gq, dim3(256), 0, s, qa);
-  }
+    ProfScope ps("decode_qproj");
+    const dim3 gq(g.H_kv, g.B);
+    if (L.dtype == STARKV_F32) e = launch_k(ps, k_qproj<STARKV_F32, STARKV_LATENT_F32>, gq, dim3(256), s, qa);
+    else if (L.latent == STARKV_LATENT_BF16) e = launch_k(ps, k_qproj<STARKV_BF16, STARKV_LATENT_BF16>, gq, dim3(256), s, qa);
+    else e = launch_k(ps, k_qproj<STARKV_BF16, STARKV_LATENT_MIX84>, gq, dim3(256), s, qa);
+    if (e != hipSuccess) return e;
   }
   // 2. scores
   ScoreArgs sa;
@@ -1481,28 +1533,28 @@ hipError_t launch_decode(const Layer& L, const DecodePlan& plan, const KtList& k
   sa.p = w.p;
   sa.cm = w.cm;
   sa.cl = w.cl;
+  sa.gmax = w.gmax;
   sa.g = g;
   sa.nkt_max = w.nkt_max;
   sa.kts = kts;
   sa.seq = seq;
   sa.total_chunks = w.total_chunks;
   {
-  ProfScope ps("decode_scores", s);
-  if (L.latent == STARKV_LATENT_MIX84) {
-    // int8/int4 keys: work unit = (column tile, 32-token chunk), enough chunks per workgroup
-    // that each of its four waves has a unit
-    sa.nch_wg = std::max(1, 4 / std::min(g.nct, 4));
-    const int n_wg = (w.total_chunks + sa.nch_wg - 1) / sa.nch_wg;
-    hipLaunchKernelGGL(k_scores_chunk<STARKV_LATENT_MIX84>, dim3(n_wg), dim3(256), 0, s, sa);
-  } else {
-    // bf16/fp32 keys (many K-tiles per column tile): K split over the waves of a 128-token block
-    sa.nch_wg = 4;
-    const int n_wg = seq.blk_off[g.B] * g.nct;
-    if (L.latent == STARKV_LATENT_BF16)
-      hipLaunchKernelGGL(k_scores<STARKV_LATENT_BF16>, dim3(n_wg), dim3(256), 0, s, sa);
-    else
-      hipLaunchKernelGGL(k_scores<STARKV_LATENT_F32>, dim3(n_wg), dim3(256), 0, s, sa);
-  }
+    ProfScope ps("decode_scores");
+    if (L.latent == STARKV_LATENT_MIX84) {
+      // int8/int4 keys: work unit = (column tile, 32-token chunk), enough chunks per workgroup
+      // that each of its four waves has a unit
+      sa.nch_wg = std::max(1, 4 / std::min(g.nct, 4));
+      const int n_wg = (w.total_chunks + sa.nch_wg - 1) / sa.nch_wg;
+      e = launch_k(ps, k_scores_chunk<STARKV_LATENT_MIX84>, dim3(n_wg), dim3(256), s, sa);
+    } else {
+      // bf16/fp32 keys (many K-tiles per column tile): K split over the waves of a 128-token block
+      sa.nch_wg = 4;
+      const int n_wg = seq.blk_off[g.B] * g.nct;
+      if (L.latent == STARKV_LATENT_BF16) e = launch_k(ps, k_scores<STARKV_LATENT_BF16>, dim3(n_wg), dim3(256), s, sa);
+      else e = launch_k(ps, k_scores<STARKV_LATENT_F32>, dim3(n_wg), dim3(256), s, sa);
+    }
+    if (e != hipSuccess) return e;
   }
   // 3. values
   ValueArgs va;
@@ -1510,8 +1562,8 @@ hipError_t launch_decode(const Layer& L, const DecodePlan& plan, const KtList& k
   va.p = w.p;
   va.cm = w.cm;
   va.cl = w.cl;
+  va.gmax = w.gmax;
   va.zp = w.zp;
-  va.sm = w.sm;
   va.sl = w.sl;
   va.g = g;
   va.seq = seq;
@@ -1522,28 +1574,28 @@ hipError_t launch_decode(const Layer& L, const DecodePlan& plan, const KtList& k
   va.n8v = L.n8v;
   va.n4v = L.n4v;
   va.n_sl8 = w.n_sl8;
-  va.nbw8 = w.nbw8;
-  va.nbw4 = w.nbw4;
   const int nmt = g.M_pad / 32;
   {
-  ProfScope ps("decode_values", s);
-  if (nmt == 1) {
-    dim3 gv(w.n_sl8 + w.n_sl4, w.total_splits);
-    if (L.latent == STARKV_LATENT_MIX84) hipLaunchKernelGGL(k_values1<STARKV_LATENT_MIX84>, gv, dim3(256), 0, s, va);
-    else if (L.latent == STARKV_LATENT_BF16) hipLaunchKernelGGL(k_values1<STARKV_LATENT_BF16>, gv, dim3(256), 0, s, va);
-    else hipLaunchKernelGGL(k_values1<STARKV_LATENT_F32>, gv, dim3(256), 0, s, va);
-  } else {
-    dim3 gv((va.NB + va.bpw - 1) / va.bpw, w.total_splits);
-    dim3 bv(64 * va.bpw);
-    if (L.latent == STARKV_LATENT_MIX84) launch_values_nmt<STARKV_LATENT_MIX84>(nmt, gv, bv, s, va);
-    else if (L.latent == STARKV_LATENT_BF16) launch_values_nmt<STARKV_LATENT_BF16>(nmt, gv, bv, s, va);
-    else launch_values_nmt<STARKV_LATENT_F32>(nmt, gv, bv, s, va);
-  }
+    ProfScope ps("decode_values");
+    if (nmt == 1) {
+      va.n_sl = w.n_sl8 + w.n_sl4;
+      va.n_splits = w.total_splits;
+      const dim3 gv(va.n_sl * ((w.total_splits + 7) / 8 * 8));
+      if (L.latent == STARKV_LATENT_MIX84) e = launch_values1<STARKV_LATENT_MIX84>(ps, w.nbw8, w.nbw4, gv, s, va);
+      else if (L.latent == STARKV_LATENT_BF16) e = launch_values1<STARKV_LATENT_BF16>(ps, w.nbw8, w.nbw4, gv, s, va);
+      else e = launch_values1<STARKV_LATENT_F32>(ps, w.nbw8, w.nbw4, gv, s, va);
+    } else {
+      const dim3 gv((va.NB + va.bpw - 1) / va.bpw, w.total_splits);
+      const dim3 bv(64 * va.bpw);
+      if (L.latent == STARKV_LATENT_MIX84) e = launch_values_nmt<STARKV_LATENT_MIX84>(ps, nmt, gv, bv, s, va);
+      else if (L.latent == STARKV_LATENT_BF16) e = launch_values_nmt<STARKV_LATENT_BF16>(ps, nmt, gv, bv, s, va);
+      else e = launch_values_nmt<STARKV_LATENT_F32>(ps, nmt, gv, bv, s, va);
+    }
+    if (e != hipSuccess) return e;
   }
   // 4. merge + up-projection
   MergeArgs ma;
   ma.zp = w.zp;
-  ma.sm = w.sm;
   ma.sl = w.sl;
   ma.zt = w.zt;
   ma.B_vt = L.B_vt;
@@ -1552,16 +1604,23 @@ hipError_t launch_decode(const Layer& L, const DecodePlan& plan, const KtList& k
   ma.g = g;
   ma.seq = seq;
   {
-  ProfScope ps("decode_zmerge", s);
-  dim3 gz((g.r_v + 63) / 64, (g.M_q + 3) / 4, g.B);
-  hipLaunchKernelGGL(k_zmerge, gz, dim3(256), 0, s, ma);
+    ProfScope ps("decode_zmerge");
+    const dim3 gz((g.rv_ld + 255) / 256, (g.M_q + 3) / 4, g.B);
+    e = launch_k(ps, k_zmerge, gz, dim3(256), s, ma);
+    if (e != hipSuccess) return e;
   }
-  const int Rg = g.B * g.G * g.n_q;
-  dim3 gm(g.H_kv * (g.d_h / 32), (Rg + 15) / 16);
   {
-  ProfScope ps("decode_upproj", s);
-  if (L.dtype == STARKV_F32) hipLaunchKernelGGL(k_upproj<STARKV_F32>, gm, dim3(256), 0, s, ma);
-  else hipLaunchKernelGGL(k_upproj<STARKV_BF16>, gm, dim3(256), 0, s, ma);
+    ProfScope ps("decode_upproj");
+    const int Rg = g.B * g.G * g.n_q;
+    const dim3 gm(g.H_kv * (g.d_h / 16), (Rg + 15) / 16);
+    const bool vec = (g.r_v & 7) == 0;
+    if (L.dtype == STARKV_F32)
+      e = vec ? launch_k(ps, k_upproj<STARKV_F32, true>, gm, dim3(256), s, ma)
+              : launch_k(ps, k_upproj<STARKV_F32, false>, gm, dim3(256), s, ma);
+    else
+      e = vec ? launch_k(ps, k_upproj<STARKV_BF16, true>, gm, dim3(256), s, ma)
+              : launch_k(ps, k_upproj<STARKV_BF16, false>, gm, dim3(256), s, ma);
+    if (e != hipSuccess) return e;
   }
   return hipGetLastError();
 }

@@ -1,6 +1,7 @@
-// Per-kernel event timing: when enabled, each kernel launch of the library is bracketed by
-// two HIP events recorded on the launch's own stream.  Reading the totals synchronises on
-// those events.  Off by default; enabling it adds two event records per launch.
+// Per-kernel timing: when enabled, each kernel launch of the library is made with
+// hipExtLaunchKernel and two events that take the kernel's own start and end timestamps (the
+// same interval a kernel trace reports).  Reading the totals synchronises on those events.
+// Off by default.
 #include <string.h>
 
 #include <mutex>
@@ -39,20 +40,22 @@ hipEvent_t take_event() {
 }
 }  // namespace
 
-ProfScope::ProfScope(const char* name, hipStream_t s) : name_(name), s_(s), a_(nullptr) {
+ProfScope::ProfScope(const char* name) : name_(name), a_(nullptr), b_(nullptr) {
   std::lock_guard<std::mutex> lk(g_mu);
   if (!g_on) return;
   a_ = take_event();
-  if (a_) (void)hipEventRecord((hipEvent_t)a_, s);
+  b_ = take_event();
+  if (!a_ || !b_) {
+    if (a_) g_pool.push_back(a_);
+    if (b_) g_pool.push_back(b_);
+    a_ = b_ = nullptr;
+  }
 }
 
 ProfScope::~ProfScope() {
   if (!a_) return;
   std::lock_guard<std::mutex> lk(g_mu);
-  hipEvent_t b = take_event();
-  if (!b) return;
-  (void)hipEventRecord(b, s_);
-  g_pending.push_back(Pending{name_, (hipEvent_t)a_, b});
+  g_pending.push_back(Pending{name_, a_, b_});
 }
 
 int profile_enable(int on) {
