@@ -54,8 +54,16 @@ __device__ __forceinline__ void load_frag8(const void* base, size_t elem_off, bo
 // round (bf16) or store (f32).  For int4 slots the even-slot lane of each lane pair writes the
 // byte holding both nibbles (the partner slot is in lane ^ 1, same rows); every lane of the wave
 // must call this together.
+// Cache position of token row m of the appended block (0 for rows past M).
+__device__ __forceinline__ int row_pos(const GemmArgs& a, int m) {
+  if (m >= a.M) return 0;
+  const int b = m / a.n_new;
+  return a.lens[b] + (m - b * a.n_new);
+}
+
 template <int R>
-__device__ __forceinline__ void store_latent(const GemmArgs& a, int slot, int chan, const float* xs, const int* ms) {
+__device__ __forceinline__ void store_latent(const GemmArgs& a, int slot, int chan, const float* xs, const int* ms,
+                                             const int* ps) {
   const bool is_key = slot < a.key_slots;
   if (a.latent == STARKV_LATENT_MIX84) {
     int qmax;
@@ -75,8 +83,8 @@ __device__ __forceinline__ void store_latent(const GemmArgs& a, int slot, int ch
       }
       const int partner = __shfl_xor(code, 1, 64);
       if (m >= a.M || slot >= a.NS) continue;
-      const int b = m / a.n_new, i = m - b * a.n_new;
-      const int pos = a.lens[b] + i;
+      const int b = m / a.n_new;
+      const int pos = ps[v];
       if (is_key) {
         uint8_t* row = a.k_rows + ((size_t)b * a.T_max + pos) * a.k_row_bytes;
         if (!nib) row[slot] = (uint8_t)(code & 0xFF);
@@ -96,8 +104,8 @@ __device__ __forceinline__ void store_latent(const GemmArgs& a, int slot, int ch
   for (int v = 0; v < R; ++v) {
     const int m = ms[v];
     if (m >= a.M || slot >= a.NS) continue;
-    const int b = m / a.n_new, i = m - b * a.n_new;
-    const int pos = a.lens[b] + i;
+    const int b = m / a.n_new;
+    const int pos = ps[v];
     const float x = xs[v];
     if (is_key) {
       uint8_t* row = a.k_rows + ((size_t)b * a.T_max + pos) * a.k_row_bytes;
@@ -124,29 +132,45 @@ __device__ __forceinline__ int slot_channel(const GemmArgs& a, int slot) {
   return u < a.r_v ? a.n_key + u : -1;
 }
 
-// Few-token append (M <= 16 rows): the work is reading A once.  Workgroup = 16 cache slots x
-// all rows; the 8 waves split K = d and their 16x16 partial results are summed through LDS.
-// A wave issues KU K-steps of loads before its MFMAs; every load is unconditional (rows past M
-// read row 0 and are never stored; K-steps past the wave's range repeat its last one with the
-// A_t operand zeroed; padding columns read channel 0 with the A_t operand zeroed).
+// Few-token append (M <= 16 rows): the work is reading A once.  Workgroup = SW cache slots x all
+// rows; the 8 waves split K = d and their 16x16 partial results are summed through LDS.
+//   SW = 16 (M <= 16): MFMA row i = token i, column j = slot j.
+//   SW = 8 (M <= 8): twice as many workgroups, so that every CU streams A.  Row i and column j
+//     of the 16x16 tile take token i % 8 and slot j % 8 over K-half i / 8 (resp. j / 8); the tile
+//     holds the two half-K partials of (token, slot) at (i, j) and (i + 8, j + 8), which are added
+//     with a cross-lane read.
+// A wave issues all its K-steps of loads before its MFMAs; every load is unconditional (rows
+// past M read row 0 and are never stored; padding slots read channel 0 with the A_t operand
+// zeroed).  The cache positions of the output rows are fetched at the start.
 // 16x16x32 bf16 MFMA (16x16x4 f32 for the fp32 path).
-template <int DT>
+template <int DT, int SW>
 __global__ __launch_bounds__(512) void k_latent_gemm_skinny(GemmArgs a) {
-  constexpr int KU = DT == STARKV_BF16 ? 16 : 8;
+  constexpr bool HALF = SW == 8;
+  constexpr int KU = DT == STARKV_BF16 ? (HALF ? 8 : 16) : (HALF ? 4 : 8);
   constexpr int NL = DT == STARKV_BF16 ? 1 : 2;  // 16-byte loads per operand per K-step
   __shared__ float red[7][4][64];
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   const int n = lane & 15, q = lane >> 4;
-  const int s0 = blockIdx.x * 16;
-  const int bslot = s0 + n;
+  const int s0 = blockIdx.x * SW;
+  const int bslot = s0 + (HALF ? (n & 7) : n);
   const int bchan = slot_channel(a, bslot);
   const bool b_ok = bchan >= 0;
-  const size_t a_base = (size_t)(n < a.M ? n : 0) * a.d;
-  const size_t b_base = (size_t)(b_ok ? bchan : 0) * a.d;
-  const int ksteps = a.d / 32;
-  const int per = (ksteps + 7) / 8;
-  const int k_beg = wave * per, k_end = min(ksteps, k_beg + per);
+  const int tok = HALF ? (n & 7) : n;
+  const int khalf = HALF ? (n >> 3) : 0;
+  const int kst_all = HALF ? a.d / 64 : a.d / 32;  // K-steps of this lane's K range
+  const size_t koff = (size_t)khalf * (a.d / 2);
+  const size_t a_base = (size_t)(tok < a.M ? tok : 0) * a.d + koff;
+  const size_t b_base = (size_t)(b_ok ? bchan : 0) * a.d + koff;
+  // output rows of this lane (wave 0 stores them): token 4q + v
+  int ms[4], ps[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    ms[v] = (HALF && (q >= 2 || n >= 8)) ? a.M : 4 * q + v;
+    ps[v] = row_pos(a, ms[v]);
+  }
+  const int per = (kst_all + 7) / 8;
+  const int k_beg = wave * per, k_end = min(kst_all, k_beg + per);
   f32x4 acc = {0, 0, 0, 0};
   for (int k0 = k_beg; k0 < k_end; k0 += KU) {
     u32x4 av[KU][NL], bv[KU][NL];
@@ -187,16 +211,16 @@ __global__ __launch_bounds__(512) void k_latent_gemm_skinny(GemmArgs a) {
   __syncthreads();
   if (wave != 0) return;
   float xs[4];
-  int ms[4];
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     float x = acc[v];
 #pragma unroll
     for (int w = 0; w < 7; ++w) x += red[w][v][lane];
-    xs[v] = x;
-    ms[v] = 4 * q + v;  // D row = token row; D column = n
+    // second K-half of (token 4q + v, slot n): D element (4q + 8 + v, n + 8) in lane + 40
+    if (HALF) x += __shfl(x, (lane + 40) & 63, 64);
+    xs[v] = x;  // D row = token row; D column = n
   }
-  store_latent<4>(a, bslot, bchan, xs, ms);
+  store_latent<4>(a, bslot, bchan, xs, ms, ps);
 }
 
 template <int DT, int MODE>
@@ -255,7 +279,10 @@ __global__ __launch_bounds__(256) void k_latent_gemm(GemmArgs a) {
     xs[v] = acc[v];
     ms[v] = m0 + d32_row(v, q);
   }
-  store_latent<16>(a, slot, chan, xs, ms);
+  int ps[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) ps[v] = row_pos(a, ms[v]);
+  store_latent<16>(a, slot, chan, xs, ms, ps);
 }
 
 __global__ void k_fill_u32(uint32_t* p, int n, uint32_t v) {
@@ -317,10 +344,14 @@ hipError_t launch_append(const Layer& L, const starkv_cache& c, const void* X_ne
   for (int b = 0; b < B; ++b) a.lens[b] = lens[b];
   ProfScope ps("append");
   hipError_t e;
-  if (B * n_new <= 16 && L.d % 32 == 0) {
+  if (B * n_new <= 8 && L.d % 64 == 0) {
+    const dim3 grid((a.NS + 7) / 8);
+    if (L.dtype == STARKV_BF16) e = launch_k(ps, k_latent_gemm_skinny<STARKV_BF16, 8>, grid, dim3(512), s, a);
+    else e = launch_k(ps, k_latent_gemm_skinny<STARKV_F32, 8>, grid, dim3(512), s, a);
+  } else if (B * n_new <= 16 && L.d % 32 == 0) {
     const dim3 grid((a.NS + 15) / 16);
-    if (L.dtype == STARKV_BF16) e = launch_k(ps, k_latent_gemm_skinny<STARKV_BF16>, grid, dim3(512), s, a);
-    else e = launch_k(ps, k_latent_gemm_skinny<STARKV_F32>, grid, dim3(512), s, a);
+    if (L.dtype == STARKV_BF16) e = launch_k(ps, k_latent_gemm_skinny<STARKV_BF16, 16>, grid, dim3(512), s, a);
+    else e = launch_k(ps, k_latent_gemm_skinny<STARKV_F32, 16>, grid, dim3(512), s, a);
   } else {
     const dim3 grid((B * n_new + 63) / 64, (a.NS + 63) / 64);
     if (L.dtype == STARKV_BF16) e = launch_k(ps, k_latent_gemm<STARKV_BF16, 0>, grid, dim3(256), s, a);

@@ -191,7 +191,9 @@ template <int DT, int LAT>
 __global__ __launch_bounds__(256) void k_qproj(QprojArgs a) {
   constexpr int RB = 8;     // rows per batch
   constexpr int RMAX = 256; // max rank (<= d_h <= 256)
-  __shared__ float qrow[RB][RMAX];
+  constexpr int CH = DT == STARKV_F32 ? 64 : 128;  // elements of d_h per load round
+  constexpr int EPL = DT == STARKV_F32 ? 4 : 8;    // elements per 16-byte load
+  constexpr int NX = CH / EPL;                       // 16-byte loads per operand per round
   __shared__ float qh[RB][RMAX];
   __shared__ int8_t hi8[RB][RMAX];
   __shared__ int8_t lo8[RB][RMAX];
@@ -200,65 +202,60 @@ __global__ __launch_bounds__(256) void k_qproj(QprojArgs a) {
   const int gk = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int rph = g.G * g.n_q;
+  const int rpg = (rph + (int)gridDim.z - 1) / (int)gridDim.z;  // rows of this workgroup
+  const int r_lo = blockIdx.z * rpg, r_hi = min(rph, r_lo + rpg);
   const int c0 = a.heads.koff[gk];
   const int r = a.heads.koff[gk + 1] - c0;
   const int n8g = (LAT == STARKV_LATENT_MIX84) ? a.heads.n8[gk] : 0;
   const int o8 = (LAT == STARKV_LATENT_MIX84) ? a.heads.off8[gk] : 0;
   const int o4 = (LAT == STARKV_LATENT_MIX84) ? a.heads.off4[gk] : 0;
 
-  // the running-maximum slots of this head's rows start at -inf (the key-score kernel raises them)
-  for (int idx = tid; idx < rph * kMaxSlots; idx += 256)
-    a.gmax[((size_t)b * g.M_pad + gk * rph + idx / kMaxSlots) * kMaxSlots + idx % kMaxSlots] = ord_key(-INFINITY);
+  // the running-maximum slots of these rows start at -inf (the key-score kernel raises them)
+  for (int idx = tid; idx < (r_hi - r_lo) * kMaxSlots; idx += 256)
+    a.gmax[((size_t)b * g.M_pad + gk * rph + r_lo + idx / kMaxSlots) * kMaxSlots + idx % kMaxSlots] =
+        ord_key(-INFINITY);
 
-  for (int rb0 = 0; rb0 < rph; rb0 += RB) {
-    const int nrows = min(RB, rph - rb0);
+  for (int rb0 = r_lo; rb0 < r_hi; rb0 += RB) {
+    const int nrows = min(RB, r_hi - rb0);
     __syncthreads();
-    // query rows of this batch into LDS (fp32)
-    for (int idx = tid; idx < nrows * g.d_h; idx += 256) {
-      const int n = idx / g.d_h, e = idx % g.d_h;
-      const int i = gk * rph + rb0 + n;
-      const int hh = (i % rph) / g.n_q, j = i % g.n_q;
-      const int h = gk * g.G + hh;
-      qrow[n][e] = ldx<DT>(a.q, (((size_t)b * g.n_q + j) * g.H_q + h) * g.d_h + e);
-    }
-    __syncthreads();
-    // q^[n][k] = (q_n . B_k[c0 + k]) * scale * log2(e)/sqrt(d_h): one lane per dot product,
-    // the B_k row read with 16-byte loads all issued before the FMAs
+    // q^[n][k] = (q_n . B_k[c0 + k]) * scale * log2(e)/sqrt(d_h): one lane per dot product; the
+    // q row and the B_k row are loaded together (CH elements per round, unconditional loads at
+    // clamped offsets, masked in the FMAs)
     for (int p = tid; p < nrows * r; p += 256) {
       const int n = p / r, k = p % r;
+      const int i = gk * rph + rb0 + n;
+      const int hh = (i % rph) / g.n_q, j = i % g.n_q;
+      const size_t qoff = (((size_t)b * g.n_q + j) * g.H_q + gk * g.G + hh) * g.d_h;
       const size_t boff = (size_t)(c0 + k) * g.d_h;
       float acc = 0.f;
-      for (int e0 = 0; e0 < g.d_h; e0 += 64) {
-        u32x4 bv[8];
-        if (DT == STARKV_F32) {
+      for (int e0 = 0; e0 < g.d_h; e0 += CH) {
+        u32x4 qv[NX], bv[NX];
 #pragma unroll
-          for (int x = 0; x < 8; ++x) bv[x] = (e0 + 4 * x < g.d_h) ? ld16((const float*)a.B_k + boff + e0 + 4 * x) : u32x4{0, 0, 0, 0};
+        for (int x = 0; x < NX; ++x) {
+          const int ee = min(e0 + x * EPL, g.d_h - EPL);
+          if (DT == STARKV_F32) {
+            qv[x] = ld16((const float*)a.q + qoff + ee);
+            bv[x] = ld16((const float*)a.B_k + boff + ee);
+          } else {
+            qv[x] = ld16((const uint16_t*)a.q + qoff + ee);
+            bv[x] = ld16((const uint16_t*)a.B_k + boff + ee);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int x = 0; x < 8; ++x)
+        for (int x = 0; x < NX; ++x) {
+          const bool live = e0 + x * EPL < g.d_h;
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (e0 + 4 * x + e < g.d_h) acc = fmaf(qrow[n][e0 + 4 * x + e], __uint_as_float(bv[x][e]), acc);
-          // second half of the 64-element step
-#pragma unroll
-          for (int x = 0; x < 8; ++x) bv[x] = (e0 + 32 + 4 * x < g.d_h) ? ld16((const float*)a.B_k + boff + e0 + 32 + 4 * x) : u32x4{0, 0, 0, 0};
-#pragma unroll
-          for (int x = 0; x < 8; ++x)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (e0 + 32 + 4 * x + e < g.d_h) acc = fmaf(qrow[n][e0 + 32 + 4 * x + e], __uint_as_float(bv[x][e]), acc);
-        } else {
-#pragma unroll
-          for (int x = 0; x < 8; ++x) bv[x] = (e0 + 8 * x < g.d_h) ? ld16((const uint16_t*)a.B_k + boff + e0 + 8 * x) : u32x4{0, 0, 0, 0};
-#pragma unroll
-          for (int x = 0; x < 8; ++x)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int ee = e0 + 8 * x + 2 * e;
-              if (ee < g.d_h) {
-                acc = fmaf(qrow[n][ee], bf16_to_f32((uint16_t)(bv[x][e] & 0xFFFF)), acc);
-                acc = fmaf(qrow[n][ee + 1], bf16_to_f32((uint16_t)(bv[x][e] >> 16)), acc);
-              }
+          for (int e = 0; e < 4; ++e) {
+            if (DT == STARKV_F32) {
+              acc = fmaf(live ? __uint_as_float(qv[x][e]) : 0.f, __uint_as_float(bv[x][e]), acc);
+            } else {
+              acc = fmaf(live ? bf16_to_f32((uint16_t)(qv[x][e] & 0xFFFF)) : 0.f,
+                         bf16_to_f32((uint16_t)(bv[x][e] & 0xFFFF)), acc);
+              acc = fmaf(live ? bf16_to_f32((uint16_t)(qv[x][e] >> 16)) : 0.f,
+                         bf16_to_f32((uint16_t)(bv[x][e] >> 16)), acc);
             }
+          }
         }
       }
       float sc = 1.f;
@@ -369,7 +366,7 @@ __global__ __launch_bounds__(256) void k_qproj(QprojArgs a) {
     }
   }
   // the last head also zeroes the chunks of the padding rows of the last column tile
-  if (gk == g.H_kv - 1) {
+  if (gk == g.H_kv - 1 && blockIdx.z == 0) {
     for (int i = g.M_q; i < g.nct * 16; ++i) {
       const int ct = i >> 4, col = i & 15;
       const int nkt = a.kts.n[ct];
@@ -1519,7 +1516,10 @@ hipError_t launch_decode(const Layer& L, const DecodePlan& plan, const KtList& k
   qa.kts = kts;
   {
     ProfScope ps("decode_qproj");
-    const dim3 gq(g.H_kv, g.B);
+    // (KV head, sequence, row group); few heads x sequences: spread a head's rows over workgroups
+    const int rph = g.G * g.n_q;
+    const int nrg = std::min(rph, std::max(1, ceil_div(256, g.H_kv * g.B)));
+    const dim3 gq(g.H_kv, g.B, nrg);
     if (L.dtype == STARKV_F32) e = launch_k(ps, k_qproj<STARKV_F32, STARKV_LATENT_F32>, gq, dim3(256), s, qa);
     else if (L.latent == STARKV_LATENT_BF16) e = launch_k(ps, k_qproj<STARKV_BF16, STARKV_LATENT_BF16>, gq, dim3(256), s, qa);
     else e = launch_k(ps, k_qproj<STARKV_BF16, STARKV_LATENT_MIX84>, gq, dim3(256), s, qa);
