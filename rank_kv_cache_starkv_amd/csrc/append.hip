@@ -54,11 +54,13 @@ __device__ __forceinline__ void load_frag8(const void* base, size_t elem_off, bo
 // round (bf16) or store (f32).  For int4 slots the even-slot lane of each lane pair writes the
 // byte holding both nibbles (the partner slot is in lane ^ 1, same rows); every lane of the wave
 // must call this together.
-// Cache position of token row m of the appended block (0 for rows past M).
+// Cache position of token row m of the appended block (0 for rows past M); no branch, the length
+// read at a clamped index.
 __device__ __forceinline__ int row_pos(const GemmArgs& a, int m) {
-  if (m >= a.M) return 0;
-  const int b = m / a.n_new;
-  return a.lens[b] + (m - b * a.n_new);
+  const int mc = min(m, a.M - 1);
+  const int b = mc / a.n_new;
+  const int pos = a.lens[b] + (mc - b * a.n_new);
+  return m < a.M ? pos : 0;
 }
 
 template <int R>
@@ -131,6 +133,19 @@ __device__ __forceinline__ int slot_channel(const GemmArgs& a, int slot) {
   const int u = slot - a.key_slots;
   return u < a.r_v ? a.n_key + u : -1;
 }
+// The same without branches (selects only, the table read at a clamped index), so that a
+// kernel's prologue does not wait on argument loads one branch at a time.
+template <bool MIX>
+__device__ __forceinline__ int slot_channel_nb(const GemmArgs& a, int slot) {
+  int ch;
+  if (MIX) {
+    ch = a.slot_chan[min(slot, a.NS - 1)];
+  } else {
+    const int u = slot - a.key_slots;
+    ch = slot < a.n_key ? slot : ((slot >= a.key_slots && u < a.r_v) ? a.n_key + u : -1);
+  }
+  return slot < a.NS ? ch : -1;
+}
 
 // Few-token append (M <= 16 rows): the work is reading A once.  Workgroup = SW cache slots x all
 // rows; the 8 waves split K = d and their 16x16 partial results are summed through LDS.
@@ -143,7 +158,7 @@ __device__ __forceinline__ int slot_channel(const GemmArgs& a, int slot) {
 // past M read row 0 and are never stored; padding slots read channel 0 with the A_t operand
 // zeroed).  The cache positions of the output rows are fetched at the start.
 // 16x16x32 bf16 MFMA (16x16x4 f32 for the fp32 path).
-template <int DT, int SW>
+template <int DT, int SW, bool MIX>
 __global__ __launch_bounds__(512) void k_latent_gemm_skinny(GemmArgs a) {
   constexpr bool HALF = SW == 8;
   constexpr int KU = DT == STARKV_BF16 ? (HALF ? 8 : 16) : (HALF ? 4 : 8);
@@ -154,7 +169,7 @@ __global__ __launch_bounds__(512) void k_latent_gemm_skinny(GemmArgs a) {
   const int n = lane & 15, q = lane >> 4;
   const int s0 = blockIdx.x * SW;
   const int bslot = s0 + (HALF ? (n & 7) : n);
-  const int bchan = slot_channel(a, bslot);
+  const int bchan = slot_channel_nb<MIX>(a, bslot);
   const bool b_ok = bchan >= 0;
   const int tok = HALF ? (n & 7) : n;
   const int khalf = HALF ? (n >> 3) : 0;
@@ -344,14 +359,23 @@ hipError_t launch_append(const Layer& L, const starkv_cache& c, const void* X_ne
   for (int b = 0; b < B; ++b) a.lens[b] = lens[b];
   ProfScope ps("append");
   hipError_t e;
+  const bool mix = L.mix();
   if (B * n_new <= 8 && L.d % 64 == 0) {
     const dim3 grid((a.NS + 7) / 8);
-    if (L.dtype == STARKV_BF16) e = launch_k(ps, k_latent_gemm_skinny<STARKV_BF16, 8>, grid, dim3(512), s, a);
-    else e = launch_k(ps, k_latent_gemm_skinny<STARKV_F32, 8>, grid, dim3(512), s, a);
+    if (L.dtype == STARKV_BF16)
+      e = mix ? launch_k(ps, k_latent_gemm_skinny<STARKV_BF16, 8, true>, grid, dim3(512), s, a)
+              : launch_k(ps, k_latent_gemm_skinny<STARKV_BF16, 8, false>, grid, dim3(512), s, a);
+    else
+      e = mix ? launch_k(ps, k_latent_gemm_skinny<STARKV_F32, 8, true>, grid, dim3(512), s, a)
+              : launch_k(ps, k_latent_gemm_skinny<STARKV_F32, 8, false>, grid, dim3(512), s, a);
   } else if (B * n_new <= 16 && L.d % 32 == 0) {
     const dim3 grid((a.NS + 15) / 16);
-    if (L.dtype == STARKV_BF16) e = launch_k(ps, k_latent_gemm_skinny<STARKV_BF16, 16>, grid, dim3(512), s, a);
-    else e = launch_k(ps, k_latent_gemm_skinny<STARKV_F32, 16>, grid, dim3(512), s, a);
+    if (L.dtype == STARKV_BF16)
+      e = mix ? launch_k(ps, k_latent_gemm_skinny<STARKV_BF16, 16, true>, grid, dim3(512), s, a)
+              : launch_k(ps, k_latent_gemm_skinny<STARKV_BF16, 16, false>, grid, dim3(512), s, a);
+    else
+      e = mix ? launch_k(ps, k_latent_gemm_skinny<STARKV_F32, 16, true>, grid, dim3(512), s, a)
+              : launch_k(ps, k_latent_gemm_skinny<STARKV_F32, 16, false>, grid, dim3(512), s, a);
   } else {
     const dim3 grid((B * n_new + 63) / 64, (a.NS + 63) / 64);
     if (L.dtype == STARKV_BF16) e = launch_k(ps, k_latent_gemm<STARKV_BF16, 0>, grid, dim3(256), s, a);

@@ -129,6 +129,13 @@ int plan_decode(const Layer& L, int B, int n_q, const int32_t* lens, int T_max, 
     seq->split_off[b + 1] = seq->split_off[b] + ceil_div(nc, cps);
     total_splits += ceil_div(nc, cps);
   }
+  seq->uni = 1;
+  for (int b = 1; b < B; ++b)
+    if (lens[b] != lens[0]) seq->uni = 0;
+  seq->u_len = lens[0];
+  seq->u_nch = seq->chunk_off[1];
+  seq->u_nspl = seq->split_off[1];
+  seq->u_nblk = seq->blk_off[1];
 
   // workspace
   const int esz_p = L.latent == STARKV_LATENT_F32 ? 4 : 2;
@@ -388,6 +395,29 @@ __global__ __launch_bounds__(256) void k_qproj(QprojArgs a) {
 // ===========================================================================
 // scores: per (sequence, 64-token chunk): p~ = 2^(s - m_chunk), chunk max and sum
 
+// Sequence bookkeeping of the decode plan: with equal lengths every quantity is a product or a
+// quotient; otherwise it is read from the prefix tables (segment search by the whole wave).
+__device__ __forceinline__ int seq_len(const SeqTable& t, int b) { return t.uni ? t.u_len : t.lens[b]; }
+__device__ __forceinline__ int seq_chunk0(const SeqTable& t, int b) { return t.uni ? b * t.u_nch : t.chunk_off[b]; }
+__device__ __forceinline__ int seq_nch(const SeqTable& t, int b) {
+  return t.uni ? t.u_nch : t.chunk_off[b + 1] - t.chunk_off[b];
+}
+__device__ __forceinline__ int seq_split0(const SeqTable& t, int b) { return t.uni ? b * t.u_nspl : t.split_off[b]; }
+__device__ __forceinline__ int seq_nsplit(const SeqTable& t, int b) {
+  return t.uni ? t.u_nspl : t.split_off[b + 1] - t.split_off[b];
+}
+__device__ __forceinline__ int seq_blk0(const SeqTable& t, int b) { return t.uni ? b * t.u_nblk : t.blk_off[b]; }
+// sequence of a global split / 128-token block / 32-token chunk (call with the whole wave active)
+__device__ __forceinline__ int seq_of_split(const SeqTable& t, int B, int sg) {
+  return t.uni ? sg / t.u_nspl : find_segment_wave(t.split_off, B, sg);
+}
+__device__ __forceinline__ int seq_of_blk(const SeqTable& t, int B, int k) {
+  return t.uni ? k / t.u_nblk : find_segment_wave(t.blk_off, B, k);
+}
+__device__ __forceinline__ int seq_of_chunk(const SeqTable& t, int B, int c) {
+  return t.uni ? c / t.u_nch : find_segment_wave(t.chunk_off, B, c);
+}
+
 struct ScoreArgs {
   const uint8_t* k_rows;
   const uint8_t* qfrag;
@@ -422,9 +452,9 @@ __global__ __launch_bounds__(256) void k_scores(ScoreArgs a) {
   const int n = lane & 15, qq = lane >> 4;
   const int ct = blockIdx.x % g.nct;
   const int gblk = blockIdx.x / g.nct;
-  const int b = find_segment(a.seq.blk_off, g.B, gblk);
-  const int t_blk = (gblk - a.seq.blk_off[b]) * 128;
-  const int len = a.seq.lens[b];
+  const int b = seq_of_blk(a.seq, g.B, gblk);
+  const int t_blk = (gblk - seq_blk0(a.seq, b)) * 128;
+  const int len = seq_len(a.seq, b);
   const uint8_t* kbase = a.k_rows + (size_t)b * g.T_max * g.k_row_bytes;
   const int nkt = a.kts.n[ct];
   const int nkw = nkt > wave ? (nkt - wave + 3) / 4 : 0;  // K-tiles of this wave (uniform)
@@ -584,10 +614,10 @@ __global__ __launch_bounds__(256) void k_scores(ScoreArgs a) {
 
   // wave w finishes chunk w of the block (token tiles 2w, 2w + 1)
   const int t0 = t_blk + 32 * wave;
-  const int nch_b = a.seq.chunk_off[b + 1] - a.seq.chunk_off[b];
+  const int nch_b = seq_nch(a.seq, b);
   const int cidx = t0 / kTC;
   if (cidx >= nch_b) return;
-  const int cg = a.seq.chunk_off[b] + cidx;
+  const int cg = seq_chunk0(a.seq, b) + cidx;
   const int i = ct * 16 + n;
   const bool rowvalid = i < g.M_q;
   const int pos = len - g.n_q + (i % g.n_q);
@@ -663,9 +693,9 @@ __global__ __launch_bounds__(256) void k_scores_chunk(ScoreArgs a) {
     const int ct = u % g.nct;
     const int cg = blockIdx.x * a.nch_wg + u / g.nct;  // global chunk
     if (cg >= a.total_chunks) break;
-    const int b = find_segment(a.seq.chunk_off, g.B, cg);
-    const int t0 = (cg - a.seq.chunk_off[b]) * kTC;
-    const int len = a.seq.lens[b];
+    const int b = seq_of_chunk(a.seq, g.B, cg);
+    const int t0 = (cg - seq_chunk0(a.seq, b)) * kTC;
+    const int len = seq_len(a.seq, b);
     const uint8_t* kbase = a.k_rows + (size_t)b * g.T_max * g.k_row_bytes;
     const int i = ct * 16 + n;  // query row of this lane's result column
     const bool rowvalid = i < g.M_q;
@@ -893,12 +923,12 @@ __global__ __launch_bounds__(256) void k_values(ValueArgs a) {
   const int nb = blockIdx.x * a.bpw + wave;  // value block of this wave (wave-uniform)
   if (nb >= a.NB) return;
   const int sg = blockIdx.y;
-  const int b = find_segment(a.seq.split_off, g.B, sg);
-  const int s = sg - a.seq.split_off[b];
-  const int cbase = a.seq.chunk_off[b];
-  const int nch = a.seq.chunk_off[b + 1] - cbase;
+  const int b = seq_of_split(a.seq, g.B, sg);
+  const int s = sg - seq_split0(a.seq, b);
+  const int cbase = seq_chunk0(a.seq, b);
+  const int nch = seq_nch(a.seq, b);
   const int c_lo = s * a.cps, c_hi = min(c_lo + a.cps, nch);
-  const int len = a.seq.lens[b];
+  const int len = seq_len(a.seq, b);
   const int r = lane & 31, q = lane >> 5;
   const bool is4 = (LAT == STARKV_LATENT_MIX84) && (nb >= a.V8 / 32);
 
@@ -1092,12 +1122,12 @@ __device__ __forceinline__ void values1_run(const ValueArgs& a, int slice, int s
   const DecodeGeom& g = a.g;
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int r = lane & 31, q = lane >> 5;
-  const int b = find_segment(a.seq.split_off, g.B, sg);
-  const int s = sg - a.seq.split_off[b];
-  const int cbase = a.seq.chunk_off[b];
-  const int nch = a.seq.chunk_off[b + 1] - cbase;
+  const int b = seq_of_split(a.seq, g.B, sg);
+  const int s = sg - seq_split0(a.seq, b);
+  const int cbase = seq_chunk0(a.seq, b);
+  const int nch = seq_nch(a.seq, b);
   const int c_lo = s * a.cps, c_hi = min(c_lo + a.cps, nch);
-  const int len = a.seq.lens[b];
+  const int len = seq_len(a.seq, b);
   const bool rok = r < g.M_q;
   const size_t prow = (size_t)(rok ? r : 0);
   const float M = row_max(a.gmax, (size_t)b * g.M_pad + prow);
@@ -1311,7 +1341,7 @@ __global__ __launch_bounds__(256) void k_zmerge(MergeArgs a) {
   const int i = blockIdx.y * 4 + (tid >> 6);
   const int c = blockIdx.x * 256 + (tid & 63) * 4;
   if (i >= g.M_q || c >= g.rv_ld) return;
-  const int s0 = a.seq.split_off[b], ns = a.seq.split_off[b + 1] - s0;
+  const int s0 = seq_split0(a.seq, b), ns = seq_nsplit(a.seq, b);
   const float* zc = a.zp + ((size_t)s0 * g.M_pad + i) * g.rv_ld + c;
   const float* lc = a.sl + (size_t)s0 * g.M_pad + i;
   const size_t zs = (size_t)g.M_pad * g.rv_ld;

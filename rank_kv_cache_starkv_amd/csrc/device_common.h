@@ -92,6 +92,18 @@ __device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f
 // Row of a 32x32 MFMA result held in register v of a lane in half q (= lane / 32).
 __device__ __forceinline__ int d32_row(int v, int q) { return 8 * (v >> 2) + 4 * q + (v & 3); }
 
+// Largest b in [0, n) with off[b] <= x (off ascending, off[0] == 0, n <= 128), found by the whole
+// wave in one round of loads: lane l reads off[l + 1] and off[l + 65], and b counts the segment
+// starts off[1 .. n-1] that are <= x.  Call with every lane of the wave active.
+__device__ __forceinline__ int find_segment_wave(const int* off, int n, int x) {
+  const int lane = threadIdx.x & 63;
+  const int v0 = off[min(lane + 1, n)];
+  const int v1 = off[min(lane + 65, n)];
+  const unsigned long long m0 = __ballot(lane + 1 < n && v0 <= x);
+  const unsigned long long m1 = __ballot(lane + 65 < n && v1 <= x);
+  return __builtin_amdgcn_readfirstlane(__popcll(m0) + __popcll(m1));
+}
+
 // binary search: largest b in [0, n) with off[b] <= x  (off ascending, off[0] == 0)
 __device__ __forceinline__ int find_segment(const int* off, int n, int x) {
   int lo = 0, hi = n - 1;

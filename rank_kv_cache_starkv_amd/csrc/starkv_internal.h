@@ -80,6 +80,8 @@ struct KtList {
 };
 
 struct SeqTable {
+  // every sequence the same length: positions follow by division (no table reads on the device)
+  int uni, u_len, u_nch, u_nspl, u_nblk;
   int lens[kMaxB];
   int chunk_off[kMaxB + 1];  // prefix of 32-token chunks per sequence
   int split_off[kMaxB + 1];  // prefix of value splits per sequence
