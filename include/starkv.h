@@ -249,6 +249,22 @@ int starkv_decode_attention(const starkv_layer* layer, const starkv_cache* cache
                             hipStream_t stream);
 
 /*
+ * One decode step of a layer (Problem Statement: the new tokens' hidden states are
+ * projected into the cache, then attention reads it; Methodology section 2): append
+ * the n_q new tokens X_new[b][0 .. n_q-1] at positions lens_host[b] - n_q ..
+ * lens_host[b] - 1, then decode attention of q over lens_host[b] tokens.  The result
+ * is that of starkv_compress_append (at lengths lens_host - n_q) followed by
+ * starkv_decode_attention (at lengths lens_host), bit for bit; with B * n_q <= 16 new
+ * rows the append and the query projection share one kernel launch.
+ * X_new: device [B][n_q][d] (dtype); q, out: device [B][n_q][H_q][d_h] (dtype).
+ * lens_host: host [B], the lengths after the append.  ws: as for
+ * starkv_decode_attention (same B, n_q, lens).  Errors: those of the two calls.
+ */
+int starkv_decode_step(const starkv_layer* layer, const starkv_cache* cache, const void* X_new, const void* q,
+                       int B, int n_q, const int32_t* lens_host, void* out, void* ws, size_t ws_bytes,
+                       hipStream_t stream);
+
+/*
  * Rebuild dense keys and values of sequence b, tokens [t0, t1) (Problem
  * Statement: reconstruction from the latent): K_out[t][g] = x^_g[t] B_g and
  * V_out[t][g] = x^_v[t] B_v[:, g*d_h:(g+1)*d_h], fp32 accumulation, stored in

@@ -66,7 +66,7 @@ class _Cache(ctypes.Structure):
 EXPORTS = ["starkv_abi_version", "starkv_status_string", "starkv_layer_create", "starkv_layer_destroy",
            "starkv_layer_get_info", "starkv_layer_ranks", "starkv_build_factors", "starkv_bind_factors",
            "starkv_calibrate", "starkv_bind_scales", "starkv_cache_bytes", "starkv_compress_append",
-           "starkv_decode_workspace_bytes", "starkv_decode_attention", "starkv_reconstruct",
+           "starkv_decode_workspace_bytes", "starkv_decode_attention", "starkv_decode_step", "starkv_reconstruct",
            "starkv_profile_enable", "starkv_profile_read"]
 
 _lib = None
@@ -97,6 +97,8 @@ def lib() -> ctypes.CDLL:
     L.starkv_decode_workspace_bytes.argtypes = [vp, ci, ci, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(sz)]
     L.starkv_decode_attention.argtypes = [vp, ctypes.POINTER(_Cache), vp, ci, ci, ctypes.POINTER(ctypes.c_int32),
                                           vp, vp, sz, vp]
+    L.starkv_decode_step.argtypes = [vp, ctypes.POINTER(_Cache), vp, vp, ci, ci, ctypes.POINTER(ctypes.c_int32),
+                                     vp, vp, sz, vp]
     L.starkv_reconstruct.argtypes = [vp, ctypes.POINTER(_Cache), ci, ci, ci, vp, vp, vp]
     L.starkv_profile_enable.argtypes = [ci]
     L.starkv_profile_read.argtypes = [ctypes.POINTER(_KernelTime), ci, ctypes.POINTER(ci), ci]
@@ -289,6 +291,29 @@ class Layer:
                                                  L.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), _ptr(out), _ptr(ws),
                                                  int(ws.numel() * ws.element_size()), _stream(stream)),
                "starkv_decode_attention")
+        return out
+
+    def step(self, cache: Cache, X_new, q, lens: Sequence[int], out=None, ws=None, stream=None):
+        """One decode step: append X_new [B, n_q, d] at lens - n_q, then attention of q
+        [B, n_q, H_q, d_h] over lens (the lengths after the append)."""
+        import torch
+        assert q.dtype == self.torch_dtype and q.is_contiguous() and q.dim() == 4
+        assert X_new.dtype == self.torch_dtype and X_new.is_contiguous() and X_new.dim() == 3
+        B, n_q = int(q.shape[0]), int(q.shape[1])
+        assert tuple(X_new.shape) == (B, n_q, self.d), (tuple(X_new.shape), (B, n_q, self.d))
+        L = _i32(lens)
+        need = self.workspace_bytes(B, n_q, L)
+        if ws is None:
+            if self._ws is None or self._ws.numel() < need:
+                self._ws = torch.empty((max(need, 256),), dtype=torch.uint8, device=q.device)
+            ws = self._ws
+        if out is None:
+            out = torch.empty_like(q)
+        cs = cache.struct()
+        _check(self._lib.starkv_decode_step(self._h, ctypes.byref(cs), _ptr(X_new), _ptr(q), B, n_q,
+                                            L.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), _ptr(out), _ptr(ws),
+                                            int(ws.numel() * ws.element_size()), _stream(stream)),
+               "starkv_decode_step")
         return out
 
     def reconstruct(self, cache: Cache, b: int, t0: int, t1: int, stream=None):

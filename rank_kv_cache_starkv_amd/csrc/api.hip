@@ -269,6 +269,28 @@ int starkv_decode_attention(const starkv_layer* l, const starkv_cache* c, const 
   SKV_GUARD_END
 }
 
+int starkv_decode_step(const starkv_layer* l, const starkv_cache* c, const void* X_new, const void* q, int B,
+                       int n_q, const int32_t* lens_host, void* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  SKV_GUARD_BEGIN
+  if (!l || !q || !out || !ws || !X_new) return STARKV_EINVAL;
+  const Layer& L = l->L;
+  int st = check_decode(L, c, B, n_q, lens_host);
+  if (st != STARKV_OK) return st;
+  st = check_bound(L, true);
+  if (st != STARKV_OK) return st;
+  if (((uintptr_t)ws & 255) != 0) return STARKV_EINVAL;
+  std::vector<int32_t> lens_pre(B);
+  for (int b = 0; b < B; ++b) lens_pre[b] = lens_host[b] - n_q;
+  skv::DecodePlan plan;
+  skv::KtList kts;
+  skv::SeqTable seq;
+  st = skv::plan_decode(L, B, n_q, lens_host, c->T_max, ws, &plan, &kts, &seq);
+  if (st != STARKV_OK) return st;
+  if (ws_bytes < plan.ws_bytes) return STARKV_EWORKSPACE;
+  return hip_status(skv::launch_step(L, *c, plan, kts, seq, X_new, lens_pre.data(), q, out, stream));
+  SKV_GUARD_END
+}
+
 int starkv_reconstruct(const starkv_layer* l, const starkv_cache* c, int b, int t0, int t1, void* K_out,
                        void* V_out, hipStream_t stream) {
   SKV_GUARD_BEGIN

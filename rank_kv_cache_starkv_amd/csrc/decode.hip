@@ -19,6 +19,7 @@
 #include <cstdlib>
 
 #include "device_common.h"
+#include "latent_gemm.h"
 #include "profile.h"
 #include "starkv_internal.h"
 
@@ -78,13 +79,22 @@ int plan_decode(const Layer& L, int B, int n_q, const int32_t* lens, int T_max, 
     } else {
       mark(L.koff[g_lo], L.koff[g_hi + 1]);
     }
-    int n = 0;
-    for (int kt = 0; kt < 256; ++kt)
-      if (used[kt]) {
-        if (n >= kMaxKT) return STARKV_EUNSUPPORTED;
-        kts->kt[ct][n++] = (uint8_t)kt;
+    // the used K-tiles as (at most two) contiguous runs
+    int n = 0, runs = 0;
+    for (int kt = 0; kt < 256; ++kt) {
+      if (!used[kt]) continue;
+      if (kt == 0 || !used[kt - 1]) {
+        if (runs == 0) kts->s0[ct] = kt;
+        else if (runs == 1) kts->s1[ct] = kt;
+        else return STARKV_EUNSUPPORTED;
+        ++runs;
       }
-    kts->n[ct] = (uint8_t)n;
+      if (runs == 1) kts->n0[ct] = n + 1;
+      ++n;
+    }
+    if (n > kMaxKT) return STARKV_EUNSUPPORTED;
+    if (runs == 1) kts->s1[ct] = kts->s0[ct] + kts->n0[ct];
+    kts->n[ct] = n;
     nkt_max = std::max(nkt_max, n);
   }
 
@@ -194,23 +204,33 @@ __device__ __forceinline__ float ldx(const void* p, size_t i) {
 // are complete here, so the per-row quantisation scale is local.  Each row owns the 16-byte
 // fragment chunks of its column in every K-tile of its column tile; the workgroup writes
 // exactly those chunks (zeros outside g's segment), so no two workgroups write the same bytes.
-template <int DT, int LAT>
-__global__ __launch_bounds__(256) void k_qproj(QprojArgs a) {
-  constexpr int RB = 8;     // rows per batch
-  constexpr int RMAX = 256; // max rank (<= d_h <= 256)
+constexpr int kQpRB = 8;      // query-projection rows per batch
+constexpr int kQpRMAX = 256;  // max rank (<= d_h <= 256)
+struct QprojShared {
+  float qh[kQpRB][kQpRMAX];
+  int8_t hi8[kQpRB][kQpRMAX];
+  int8_t lo8[kQpRB][kQpRMAX];
+  float rho_s[kQpRB];
+};
+
+// Body of the query projection for workgroup (KV head gk, sequence b, row group rg of nrg) with
+// NT threads.
+template <int DT, int LAT, int NT>
+__device__ __forceinline__ void qproj_body(const QprojArgs& a, int gk, int b, int rg, int nrg, QprojShared& sh) {
+  constexpr int RB = kQpRB;
+  constexpr int NWV = NT / 64;
   constexpr int CH = DT == STARKV_F32 ? 64 : 128;  // elements of d_h per load round
   constexpr int EPL = DT == STARKV_F32 ? 4 : 8;    // elements per 16-byte load
   constexpr int NX = CH / EPL;                       // 16-byte loads per operand per round
-  __shared__ float qh[RB][RMAX];
-  __shared__ int8_t hi8[RB][RMAX];
-  __shared__ int8_t lo8[RB][RMAX];
-  __shared__ float rho_s[RB];
+  auto& qh = sh.qh;
+  auto& hi8 = sh.hi8;
+  auto& lo8 = sh.lo8;
+  auto& rho_s = sh.rho_s;
   const DecodeGeom& g = a.g;
-  const int gk = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int rph = g.G * g.n_q;
-  const int rpg = (rph + (int)gridDim.z - 1) / (int)gridDim.z;  // rows of this workgroup
-  const int r_lo = blockIdx.z * rpg, r_hi = min(rph, r_lo + rpg);
+  const int rpg = (rph + nrg - 1) / nrg;  // rows of this workgroup
+  const int r_lo = rg * rpg, r_hi = min(rph, r_lo + rpg);
   const int c0 = a.heads.koff[gk];
   const int r = a.heads.koff[gk + 1] - c0;
   const int n8g = (LAT == STARKV_LATENT_MIX84) ? a.heads.n8[gk] : 0;
@@ -218,7 +238,7 @@ __global__ __launch_bounds__(256) void k_qproj(QprojArgs a) {
   const int o4 = (LAT == STARKV_LATENT_MIX84) ? a.heads.off4[gk] : 0;
 
   // the running-maximum slots of these rows start at -inf (the key-score kernel raises them)
-  for (int idx = tid; idx < (r_hi - r_lo) * kMaxSlots; idx += 256)
+  for (int idx = tid; idx < (r_hi - r_lo) * kMaxSlots; idx += NT)
     a.gmax[((size_t)b * g.M_pad + gk * rph + r_lo + idx / kMaxSlots) * kMaxSlots + idx % kMaxSlots] =
         ord_key(-INFINITY);
 
@@ -228,7 +248,7 @@ __global__ __launch_bounds__(256) void k_qproj(QprojArgs a) {
     // q^[n][k] = (q_n . B_k[c0 + k]) * scale * log2(e)/sqrt(d_h): one lane per dot product; the
     // q row and the B_k row are loaded together (CH elements per round, unconditional loads at
     // clamped offsets, masked in the FMAs)
-    for (int p = tid; p < nrows * r; p += 256) {
+    for (int p = tid; p < nrows * r; p += NT) {
       const int n = p / r, k = p % r;
       const int i = gk * rph + rb0 + n;
       const int hh = (i % rph) / g.n_q, j = i % g.n_q;
@@ -272,7 +292,7 @@ __global__ __launch_bounds__(256) void k_qproj(QprojArgs a) {
     __syncthreads();
     // per-row scale (int8 path): rho = max|q^| / 127, one wave per row
     if (LAT == STARKV_LATENT_MIX84) {
-      for (int n = wave; n < nrows; n += 4) {
+      for (int n = wave; n < nrows; n += NWV) {
         float m = 0.f;
         for (int k = lane; k < r; k += 64) m = fmaxf(m, fabsf(qh[n][k]));
 #pragma unroll
@@ -280,7 +300,7 @@ __global__ __launch_bounds__(256) void k_qproj(QprojArgs a) {
         if (lane == 0) rho_s[n] = m > 0.f ? m / 127.f : 1.f;
       }
       __syncthreads();
-      for (int idx = tid; idx < nrows * r; idx += 256) {
+      for (int idx = tid; idx < nrows * r; idx += NT) {
         const int n = idx / r, k = idx % r;
         const float rho = rho_s[n], x = qh[n][k];
         const float hi = fminf(fmaxf(__builtin_rintf(x / rho), -127.f), 127.f);
@@ -291,7 +311,7 @@ __global__ __launch_bounds__(256) void k_qproj(QprojArgs a) {
       __syncthreads();
     }
     // row parameters: rho and the int4 offset-binary bias terms 8 * sum(int4 codes' weights)
-    for (int n = wave; n < nrows; n += 4) {
+    for (int n = wave; n < nrows; n += NWV) {
       int sh = 0, sl = 0;
       if (LAT == STARKV_LATENT_MIX84)
         for (int k = n8g + lane; k < r; k += 64) {
@@ -317,9 +337,9 @@ __global__ __launch_bounds__(256) void k_qproj(QprojArgs a) {
       const int i = gk * rph + rb0 + n;
       const int ct = i >> 4, col = i & 15;
       const int nkt = a.kts.n[ct];
-      for (int item = tid; item < nkt * 4; item += 256) {
+      for (int item = tid; item < nkt * 4; item += NT) {
         const int jt = item >> 2, qq = item & 3;
-        const int kt = a.kts.kt[ct][jt];
+        const int kt = a.kts.at(ct, jt);
         const int ln = col + 16 * qq;  // fragment lane holding this chunk
         uint8_t* frag = a.qfrag + (((size_t)b * g.nct + ct) * a.nkt_max + jt) * 2048;
         if (LAT == STARKV_LATENT_MIX84) {
@@ -373,11 +393,11 @@ __global__ __launch_bounds__(256) void k_qproj(QprojArgs a) {
     }
   }
   // the last head also zeroes the chunks of the padding rows of the last column tile
-  if (gk == g.H_kv - 1 && blockIdx.z == 0) {
+  if (gk == g.H_kv - 1 && rg == 0) {
     for (int i = g.M_q; i < g.nct * 16; ++i) {
       const int ct = i >> 4, col = i & 15;
       const int nkt = a.kts.n[ct];
-      for (int item = tid; item < nkt * 4; item += 256) {
+      for (int item = tid; item < nkt * 4; item += NT) {
         const int jt = item >> 2, qq = item & 3, ln = col + 16 * qq;
         uint8_t* frag = a.qfrag + (((size_t)b * g.nct + ct) * a.nkt_max + jt) * 2048;
         if (LAT == STARKV_LATENT_F32) {
@@ -390,6 +410,12 @@ __global__ __launch_bounds__(256) void k_qproj(QprojArgs a) {
       }
     }
   }
+}
+
+template <int DT, int LAT>
+__global__ __launch_bounds__(256) void k_qproj(QprojArgs a) {
+  __shared__ QprojShared sh;
+  qproj_body<DT, LAT, 256>(a, blockIdx.x, blockIdx.y, blockIdx.z, gridDim.z, sh);
 }
 
 // ===========================================================================
@@ -467,7 +493,7 @@ __global__ __launch_bounds__(256) void k_scores(ScoreArgs a) {
   for (int j = 0; j < KW; ++j) {
     const bool on = j < nkw;
     const int jt = wave + 4 * (on ? j : 0);
-    const int kt = a.kts.kt[ct][jt];
+    const int kt = a.kts.at(ct, jt);
     p0[j] = (LAT == STARKV_LATENT_MIX84 ? kt * 64 + 16 * qq : kt * 32 + 8 * qq);
     const uint8_t* f = fbase + (size_t)jt * 2048;
 #pragma unroll
@@ -727,7 +753,7 @@ __global__ __launch_bounds__(256) void k_scores_chunk(ScoreArgs a) {
 #pragma unroll
         for (int j = 0; j < KU; ++j) {
           const bool on = jt0 + j < nkt;
-          const int kt = on ? a.kts.kt[ct][jt0 + j] : 0;
+          const int kt = on ? a.kts.at(ct, jt0 + j) : 0;
           const int P0 = kt * 64 + 16 * qq;
           fh[j] = on ? __builtin_bit_cast(i32x4, ld16(fbase + (jt0 + j) * 2048 + lane * 16)) : i32x4{0, 0, 0, 0};
           fl[j] = on ? __builtin_bit_cast(i32x4, ld16(fbase + (jt0 + j) * 2048 + 1024 + lane * 16)) : i32x4{0, 0, 0, 0};
@@ -763,7 +789,7 @@ __global__ __launch_bounds__(256) void k_scores_chunk(ScoreArgs a) {
 #pragma unroll
         for (int j = 0; j < KU; ++j) {
           const bool on = jt0 + j < nkt;
-          const int kt = on ? a.kts.kt[ct][jt0 + j] : 0;
+          const int kt = on ? a.kts.at(ct, jt0 + j) : 0;
           const int P0 = kt * 32 + 8 * qq;
           fh[j] = on ? ld16(fbase + (jt0 + j) * 2048 + lane * 16) : u32x4{0, 0, 0, 0};
           fl[j] = on ? ld16(fbase + (jt0 + j) * 2048 + 1024 + lane * 16) : u32x4{0, 0, 0, 0};
@@ -788,7 +814,7 @@ __global__ __launch_bounds__(256) void k_scores_chunk(ScoreArgs a) {
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) acc[tt] = f32x4{0, 0, 0, 0};
       for (int jt = 0; jt < nkt; ++jt) {
-        const int kt = a.kts.kt[ct][jt];
+        const int kt = a.kts.at(ct, jt);
         const u32x4 f0 = ld16(fbase + jt * 2048 + lane * 32);
         const u32x4 f1 = ld16(fbase + jt * 2048 + lane * 32 + 16);
         const int P0 = kt * 32 + 8 * qq;
@@ -1527,34 +1553,112 @@ static hipError_t launch_values1(const ProfScope& ps, int nbw8, int nbw4, dim3 g
   return launch_k(ps, k_values1<LAT, 4, 2>, grid, blk, s, va);
 }
 
-hipError_t launch_decode(const Layer& L, const DecodePlan& plan, const KtList& kts, const SeqTable& seq,
-                         const void* q, void* out, const void* k_rows, const void* v_tiles, hipStream_t s) {
-  const DecodeGeom& g = plan.g;
-  const DecodeWs& w = plan.ws;
-  hipError_t e = hipSuccess;
-  // 1. query fragments (and the running-maximum slots set to -inf)
+static QprojArgs qproj_args(const Layer& L, const DecodePlan& plan, const KtList& kts, const void* q) {
   QprojArgs qa;
   qa.q = q;
   qa.B_k = L.B_k;
   qa.scales = L.scales;
   qa.heads = L.heads();
-  qa.qfrag = (uint8_t*)w.qfrag;
-  qa.rowp = w.rowp;
-  qa.gmax = w.gmax;
-  qa.g = g;
-  qa.nkt_max = w.nkt_max;
+  qa.qfrag = (uint8_t*)plan.ws.qfrag;
+  qa.rowp = plan.ws.rowp;
+  qa.gmax = plan.ws.gmax;
+  qa.g = plan.g;
+  qa.nkt_max = plan.ws.nkt_max;
   qa.kts = kts;
+  return qa;
+}
+
+// query-projection row groups: few KV heads x sequences spread a head's rows over workgroups
+static int qproj_row_groups(const DecodeGeom& g) {
+  return std::min(g.G * g.n_q, std::max(1, ceil_div(256, g.H_kv * g.B)));
+}
+
+// First launch of a fused decode step: the few-token append's workgroups and the query
+// projection's workgroups in one grid.  The two parts touch disjoint memory (the append writes
+// the new cache rows; the projection reads q and B_k and writes the workspace), and the key
+// scores, the first reader of both, run in the next launch.
+struct StepFrontArgs {
+  GemmArgs ga;
+  QprojArgs qa;
+  int n_app;  // append workgroups; the rest are query-projection workgroups
+  int nrg;    // query-projection row groups
+};
+
+template <int DT, int LAT, int SW>
+__global__ __launch_bounds__(512) void k_step_front(StepFrontArgs a) {
+  __shared__ float red[7][4][64];
+  __shared__ QprojShared sh;
+  const int blk = blockIdx.x;
+  if (blk < a.n_app) {
+    skinny_body<DT, SW, LAT == STARKV_LATENT_MIX84>(a.ga, blk, red);
+  } else {
+    const int k = blk - a.n_app;
+    const int H = a.qa.g.H_kv, B = a.qa.g.B;
+    qproj_body<DT, LAT, 512>(a.qa, k % H, (k / H) % B, k / (H * B), a.nrg, sh);
+  }
+}
+
+template <int SW>
+static hipError_t launch_front(const Layer& L, const ProfScope& ps, dim3 grid, hipStream_t s, const StepFrontArgs& fa) {
+  if (L.dtype == STARKV_F32) return launch_k(ps, k_step_front<STARKV_F32, STARKV_LATENT_F32, SW>, grid, dim3(512), s, fa);
+  if (L.latent == STARKV_LATENT_BF16)
+    return launch_k(ps, k_step_front<STARKV_BF16, STARKV_LATENT_BF16, SW>, grid, dim3(512), s, fa);
+  return launch_k(ps, k_step_front<STARKV_BF16, STARKV_LATENT_MIX84, SW>, grid, dim3(512), s, fa);
+}
+
+static hipError_t launch_decode_tail(const Layer& L, const DecodePlan& plan, const KtList& kts, const SeqTable& seq,
+                                     void* out, const void* k_rows, const void* v_tiles, hipStream_t s);
+
+hipError_t launch_decode(const Layer& L, const DecodePlan& plan, const KtList& kts, const SeqTable& seq,
+                         const void* q, void* out, const void* k_rows, const void* v_tiles, hipStream_t s) {
+  const DecodeGeom& g = plan.g;
+  hipError_t e = hipSuccess;
+  // 1. query fragments (and the running-maximum slots set to -inf)
+  const QprojArgs qa = qproj_args(L, plan, kts, q);
   {
     ProfScope ps("decode_qproj");
-    // (KV head, sequence, row group); few heads x sequences: spread a head's rows over workgroups
-    const int rph = g.G * g.n_q;
-    const int nrg = std::min(rph, std::max(1, ceil_div(256, g.H_kv * g.B)));
-    const dim3 gq(g.H_kv, g.B, nrg);
+    const dim3 gq(g.H_kv, g.B, qproj_row_groups(g));
     if (L.dtype == STARKV_F32) e = launch_k(ps, k_qproj<STARKV_F32, STARKV_LATENT_F32>, gq, dim3(256), s, qa);
     else if (L.latent == STARKV_LATENT_BF16) e = launch_k(ps, k_qproj<STARKV_BF16, STARKV_LATENT_BF16>, gq, dim3(256), s, qa);
     else e = launch_k(ps, k_qproj<STARKV_BF16, STARKV_LATENT_MIX84>, gq, dim3(256), s, qa);
     if (e != hipSuccess) return e;
   }
+  return launch_decode_tail(L, plan, kts, seq, out, k_rows, v_tiles, s);
+}
+
+hipError_t launch_step(const Layer& L, const starkv_cache& c, const DecodePlan& plan, const KtList& kts,
+                       const SeqTable& seq, const void* X_new, const int32_t* lens_pre, const void* q, void* out,
+                       hipStream_t s) {
+  const DecodeGeom& g = plan.g;
+  const int M = g.B * g.n_q;
+  const int sw = (M <= 8 && L.d % 64 == 0) ? 8 : ((M <= 16 && L.d % 32 == 0) ? 16 : 0);
+  if (sw == 0) {
+    // many new rows: the tiled append, then the decode
+    const hipError_t e = launch_append(L, c, X_new, g.B, g.n_q, lens_pre, s);
+    if (e != hipSuccess) return e;
+    return launch_decode(L, plan, kts, seq, q, out, c.k_rows, c.v_tiles, s);
+  }
+  StepFrontArgs fa;
+  fa.ga = GemmArgs{};
+  fill_append_args(L, c, fa.ga, X_new, g.B, g.n_q, lens_pre);
+  fa.qa = qproj_args(L, plan, kts, q);
+  fa.n_app = ceil_div(fa.ga.NS, sw);
+  fa.nrg = qproj_row_groups(g);
+  const dim3 grid(fa.n_app + g.H_kv * g.B * fa.nrg);
+  hipError_t e;
+  {
+    ProfScope ps("step_front");
+    e = sw == 8 ? launch_front<8>(L, ps, grid, s, fa) : launch_front<16>(L, ps, grid, s, fa);
+  }
+  if (e != hipSuccess) return e;
+  return launch_decode_tail(L, plan, kts, seq, out, c.k_rows, c.v_tiles, s);
+}
+
+static hipError_t launch_decode_tail(const Layer& L, const DecodePlan& plan, const KtList& kts, const SeqTable& seq,
+                                     void* out, const void* k_rows, const void* v_tiles, hipStream_t s) {
+  const DecodeGeom& g = plan.g;
+  const DecodeWs& w = plan.ws;
+  hipError_t e = hipSuccess;
   // 2. scores
   ScoreArgs sa;
   sa.k_rows = (const uint8_t*)k_rows;

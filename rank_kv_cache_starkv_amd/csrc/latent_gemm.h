@@ -1,0 +1,242 @@
+// Latent projection of appended hidden states (x = X A, fp32 accumulation on MFMA) and the
+// cache store of its result: argument block, epilogue, and the few-token body shared by the
+// append kernel and the fused decode-step front kernel.
+//
+// STAR-KV summary page, Problem Statement: the cache holds the projected hidden states; Methodology
+// section 3: the leading channels of each latent segment are stored as int8, the rest as int4.
+#pragma once
+
+#include "device_common.h"
+#include "starkv_internal.h"
+
+namespace skv {
+
+struct GemmArgs {
+  const void* X;        // [M][d]
+  const void* A_t;      // [n_lat][d]
+  const int* slot_chan; // [NS]
+  int M, d, NS;
+  int key_slots, K8, V8;
+  int n_key, r_v;
+  int latent;
+  // append
+  int n_new, T_max, k_row_bytes, v_rows;
+  uint8_t* k_rows;
+  uint8_t* v_tiles;
+  const uint16_t* scales;
+  int lens[kMaxB];
+  // calibrate
+  uint32_t* absmax;
+};
+
+template <int DT>
+__device__ __forceinline__ void load_frag8(const void* base, size_t elem_off, bool ok, u32x4& lo, u32x4& hi) {
+  // 8 consecutive elements: bf16 -> lo holds all 8; f32 -> lo elements 0..3, hi 4..7
+  if (!ok) {
+    lo = u32x4{0, 0, 0, 0};
+    hi = lo;
+    return;
+  }
+  if (DT == STARKV_BF16) {
+    lo = ld16((const uint16_t*)base + elem_off);
+    hi = u32x4{0, 0, 0, 0};
+  } else {
+    const float* p = (const float*)base + elem_off;
+    lo = ld16(p);
+    hi = ld16(p + 4);
+  }
+}
+
+// Store R latent values of one cache slot (column) for R token rows: quantise/pack (mix84) or
+// round (bf16) or store (f32).  For int4 slots the even-slot lane of each lane pair writes the
+// byte holding both nibbles (the partner slot is in lane ^ 1, same rows); every lane of the wave
+// must call this together.
+// Cache position of token row m of the appended block (0 for rows past M); no branch, the length
+// read at a clamped index.
+__device__ __forceinline__ int row_pos(const GemmArgs& a, int m) {
+  const int mc = min(m, a.M - 1);
+  const int b = mc / a.n_new;
+  const int pos = a.lens[b] + (mc - b * a.n_new);
+  return m < a.M ? pos : 0;
+}
+
+template <int R>
+__device__ __forceinline__ void store_latent(const GemmArgs& a, int slot, int chan, const float* xs, const int* ms,
+                                             const int* ps) {
+  const bool is_key = slot < a.key_slots;
+  if (a.latent == STARKV_LATENT_MIX84) {
+    int qmax;
+    if (is_key) qmax = slot < a.K8 ? 127 : 7;
+    else qmax = (slot - a.key_slots) < a.V8 ? 127 : 7;
+    const float sc = chan >= 0 ? f16_to_f32(a.scales[chan]) : 0.f;
+    const bool nib = qmax == 7;
+#pragma unroll
+    for (int v = 0; v < R; ++v) {
+      const int m = ms[v];
+      int code = 0;
+      if (sc != 0.f) {
+        const float y = xs[v] / sc;  // IEEE fp32 division
+        float rq = __builtin_rintf(y);
+        rq = fminf(fmaxf(rq, -(float)qmax), (float)qmax);
+        code = (int)rq;
+      }
+      const int partner = __shfl_xor(code, 1, 64);
+      if (m >= a.M || slot >= a.NS) continue;
+      const int b = m / a.n_new;
+      const int pos = ps[v];
+      if (is_key) {
+        uint8_t* row = a.k_rows + ((size_t)b * a.T_max + pos) * a.k_row_bytes;
+        if (!nib) row[slot] = (uint8_t)(code & 0xFF);
+        else if ((slot & 1) == 0) row[a.K8 + (slot - a.K8) / 2] = (uint8_t)((code & 0xF) | ((partner & 0xF) << 4));
+      } else {
+        const int u = slot - a.key_slots;
+        uint8_t* tile = a.v_tiles + ((size_t)b * (a.T_max / kTT) + pos / kTT) * a.v_rows * kTT;
+        if (!nib) tile[(size_t)u * kTT + pos % kTT] = (uint8_t)(code & 0xFF);
+        else if ((u & 1) == 0)
+          tile[(size_t)(a.V8 + (u - a.V8) / 2) * kTT + pos % kTT] = (uint8_t)((code & 0xF) | ((partner & 0xF) << 4));
+      }
+    }
+    return;
+  }
+  // unquantised latent: fp32 or bf16 elements
+#pragma unroll
+  for (int v = 0; v < R; ++v) {
+    const int m = ms[v];
+    if (m >= a.M || slot >= a.NS) continue;
+    const int b = m / a.n_new;
+    const int pos = ps[v];
+    const float x = xs[v];
+    if (is_key) {
+      uint8_t* row = a.k_rows + ((size_t)b * a.T_max + pos) * a.k_row_bytes;
+      if (a.latent == STARKV_LATENT_F32) ((float*)row)[slot] = x;
+      else ((uint16_t*)row)[slot] = f32_to_bf16(x);
+    } else {
+      const int u = slot - a.key_slots;
+      uint8_t* tile = a.v_tiles + ((size_t)b * (a.T_max / kTT) + pos / kTT) * a.v_rows * kTT * (a.latent == STARKV_LATENT_F32 ? 4 : 2);
+      if (a.latent == STARKV_LATENT_F32) ((float*)tile)[(size_t)u * kTT + pos % kTT] = x;
+      else ((uint16_t*)tile)[(size_t)u * kTT + pos % kTT] = f32_to_bf16(x);
+    }
+  }
+}
+
+// Natural latent channel of GEMM column `slot`, or -1 for a padding column.  Unquantised
+// latents keep the natural order (key channels, padding to the row size, value channels), so
+// the channel follows from the slot; the int8/int4 layout reorders channels (table lookup).
+__device__ __forceinline__ int slot_channel(const GemmArgs& a, int slot) {
+  if (slot >= a.NS) return -1;
+  if (a.latent == STARKV_LATENT_MIX84) return a.slot_chan[slot];
+  if (slot < a.n_key) return slot;
+  if (slot < a.key_slots) return -1;
+  const int u = slot - a.key_slots;
+  return u < a.r_v ? a.n_key + u : -1;
+}
+// The same without branches (selects only, the table read at a clamped index), so that a
+// kernel's prologue does not wait on argument loads one branch at a time.
+template <bool MIX>
+__device__ __forceinline__ int slot_channel_nb(const GemmArgs& a, int slot) {
+  int ch;
+  if (MIX) {
+    ch = a.slot_chan[min(slot, a.NS - 1)];
+  } else {
+    const int u = slot - a.key_slots;
+    ch = slot < a.n_key ? slot : ((slot >= a.key_slots && u < a.r_v) ? a.n_key + u : -1);
+  }
+  return slot < a.NS ? ch : -1;
+}
+
+// Few-token append (M <= 16 rows): the work is reading A once.  Workgroup = SW cache slots x all
+// rows; the 8 waves split K = d and their 16x16 partial results are summed through LDS.
+//   SW = 16 (M <= 16): MFMA row i = token i, column j = slot j.
+//   SW = 8 (M <= 8): twice as many workgroups, so that every CU streams A.  Row i and column j
+//     of the 16x16 tile take token i % 8 and slot j % 8 over K-half i / 8 (resp. j / 8); the tile
+//     holds the two half-K partials of (token, slot) at (i, j) and (i + 8, j + 8), which are added
+//     with a cross-lane read.
+// A wave issues all its K-steps of loads before its MFMAs; every load is unconditional (rows
+// past M read row 0 and are never stored; padding slots read channel 0 with the A_t operand
+// zeroed).  The cache positions of the output rows are fetched at the start.
+// 16x16x32 bf16 MFMA (16x16x4 f32 for the fp32 path).
+template <int DT, int SW, bool MIX>
+__device__ __forceinline__ void skinny_body(const GemmArgs& a, int blk, float (*red)[4][64]) {
+  constexpr bool HALF = SW == 8;
+  constexpr int KU = DT == STARKV_BF16 ? (HALF ? 8 : 16) : (HALF ? 4 : 8);
+  constexpr int NL = DT == STARKV_BF16 ? 1 : 2;  // 16-byte loads per operand per K-step
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const int n = lane & 15, q = lane >> 4;
+  const int s0 = blk * SW;
+  const int bslot = s0 + (HALF ? (n & 7) : n);
+  const int bchan = slot_channel_nb<MIX>(a, bslot);
+  const bool b_ok = bchan >= 0;
+  const int tok = HALF ? (n & 7) : n;
+  const int khalf = HALF ? (n >> 3) : 0;
+  const int kst_all = HALF ? a.d / 64 : a.d / 32;  // K-steps of this lane's K range
+  const size_t koff = (size_t)khalf * (a.d / 2);
+  const size_t a_base = (size_t)(tok < a.M ? tok : 0) * a.d + koff;
+  const size_t b_base = (size_t)(b_ok ? bchan : 0) * a.d + koff;
+  // output rows of this lane (wave 0 stores them): token 4q + v
+  int ms[4], ps[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    ms[v] = (HALF && (q >= 2 || n >= 8)) ? a.M : 4 * q + v;
+    ps[v] = row_pos(a, ms[v]);
+  }
+  const int per = (kst_all + 7) / 8;
+  const int k_beg = wave * per, k_end = min(kst_all, k_beg + per);
+  f32x4 acc = {0, 0, 0, 0};
+  for (int k0 = k_beg; k0 < k_end; k0 += KU) {
+    u32x4 av[KU][NL], bv[KU][NL];
+#pragma unroll
+    for (int j = 0; j < KU; ++j) {
+      const size_t ko = (size_t)min(k0 + j, k_end - 1) * 32 + 8 * q;
+#pragma unroll
+      for (int h = 0; h < NL; ++h) {
+        if (DT == STARKV_BF16) {
+          av[j][h] = ld16((const uint16_t*)a.X + a_base + ko);
+          bv[j][h] = ld16((const uint16_t*)a.A_t + b_base + ko);
+        } else {
+          av[j][h] = ld16((const float*)a.X + a_base + ko + 4 * h);
+          bv[j][h] = ld16((const float*)a.A_t + b_base + ko + 4 * h);
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep every load of the batch ahead of the MFMAs
+#pragma unroll
+    for (int j = 0; j < KU; ++j) {
+      const bool live = b_ok && k0 + j < k_end;
+#pragma unroll
+      for (int h = 0; h < NL; ++h) bv[j][h] = live ? bv[j][h] : u32x4{0, 0, 0, 0};
+      if (DT == STARKV_BF16) {
+        acc = mfma16_bf16(as_bf16x8(av[j][0]), as_bf16x8(bv[j][0]), acc);
+      } else {
+#pragma unroll
+        for (int h = 0; h < NL; ++h)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc = mfma16_f32(__uint_as_float(av[j][h][e]), __uint_as_float(bv[j][h][e]), acc);
+      }
+    }
+  }
+  if (wave > 0) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) red[wave - 1][v][lane] = acc[v];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  float xs[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    float x = acc[v];
+#pragma unroll
+    for (int w = 0; w < 7; ++w) x += red[w][v][lane];
+    // second K-half of (token 4q + v, slot n): D element (4q + 8 + v, n + 8) in lane + 40
+    if (HALF) x += __shfl(x, (lane + 40) & 63, 64);
+    xs[v] = x;  // D row = token row; D column = n
+  }
+  store_latent<4>(a, bslot, bchan, xs, ms, ps);
+}
+
+// Host side: argument blocks of the latent GEMM for a layer, and for an append into a cache.
+void fill_gemm_args(const Layer& L, GemmArgs& a, const void* X, int M);
+void fill_append_args(const Layer& L, const starkv_cache& c, GemmArgs& a, const void* X_new, int B, int n_new,
+                      const int32_t* lens);
+
+}  // namespace skv

@@ -74,9 +74,15 @@ struct DecodeGeom {
   float qscale;  // log2(e) / sqrt(d_h)
 };
 
+// K-tiles touched by each 16-row column tile of the key-score GEMM: at most two contiguous runs
+// (bf16/fp32: one; int8/int4: one in each region), so K-tile jt of column tile ct is
+// s0 + jt for jt < n0, else s1 + (jt - n0).
 struct KtList {
-  uint8_t n[kMaxCT];
-  uint8_t kt[kMaxCT][kMaxKT];
+  int n[kMaxCT];
+  int s0[kMaxCT], n0[kMaxCT], s1[kMaxCT];
+#ifdef __HIPCC__
+  __host__ __device__ __forceinline__ int at(int ct, int jt) const { return jt < n0[ct] ? s0[ct] + jt : s1[ct] + (jt - n0[ct]); }
+#endif
 };
 
 struct SeqTable {
@@ -118,6 +124,13 @@ int plan_decode(const Layer& L, int B, int n_q, const int32_t* lens, int T_max, 
 
 hipError_t launch_decode(const Layer& L, const DecodePlan& plan, const KtList& kts, const SeqTable& seq,
                          const void* q, void* out, const void* k_rows, const void* v_tiles, hipStream_t s);
+
+// A decode step: append n_q new tokens per sequence at lens_pre, then decode attention over
+// plan's lengths (lens_pre + n_q); few new rows run the append and the query projection in one
+// launch.
+hipError_t launch_step(const Layer& L, const starkv_cache& c, const DecodePlan& plan, const KtList& kts,
+                       const SeqTable& seq, const void* X_new, const int32_t* lens_pre, const void* q, void* out,
+                       hipStream_t s);
 
 hipError_t launch_build_factors(const Layer& L, const float* U_k, const float* V_k, const float* U_v,
                                 const float* V_v, void* A_t, void* B_k, void* B_vt, hipStream_t s);

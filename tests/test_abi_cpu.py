@@ -136,6 +136,12 @@ def test_hot_calls_reject_bad_arguments_without_launching():
     assert L.starkv_decode_attention(h, ctypes.byref(cache), fake, w.B, 1,
                                      big.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), fake, fake, 1 << 30, None) == -3
     assert L.starkv_decode_attention(h, ctypes.byref(cache), fake, w.B, 9, lp, fake, fake, 1 << 30, None) == -4  # 32*9 rows
+    # the fused step: the decode checks, plus a missing X_new
+    assert L.starkv_decode_step(h, ctypes.byref(cache), fake, fake, w.B, 1, lp, fake, fake, 1 << 30, None) == -7
+    assert L.starkv_decode_step(h, ctypes.byref(cache), None, fake, w.B, 1, lp, fake, fake, 1 << 30, None) == -1
+    assert L.starkv_decode_step(h, ctypes.byref(cache), fake, fake, w.B, 0, lp, fake, fake, 1 << 30, None) == -1
+    assert L.starkv_decode_step(h, ctypes.byref(cache), fake, fake, w.B, 1,
+                                big.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), fake, fake, 1 << 30, None) == -3
     assert L.starkv_reconstruct(h, ctypes.byref(cache), w.B, 0, 1, fake, fake, None) == -1
     assert L.starkv_reconstruct(h, ctypes.byref(cache), 0, 5, 4, fake, fake, None) == -1
     assert L.starkv_calibrate(h, fake, 4, fake, None) == -7

@@ -253,3 +253,45 @@ def test_append_few_tokens(cfg, n_new):
     got = H.from_dev(H.decode(run, q))
     for b in range(3):
         H.check_output(w, got[b], H.oracle_decode(run, q, b), f"len {int(run.lens[b])}")
+
+
+# ---------------------------------------------------------------- the fused decode step
+
+@pytest.mark.parametrize("cfg,lens0", [(0, [256]), (1, [300, 129]), (2, [250, 70]), (3, [700]),
+                                       (4, [100, 33, 257]), (4, [100, 33, 257, 64, 90])])
+def test_decode_step_equals_append_then_decode(cfg, lens0):
+    """starkv_decode_step leaves the cache bytes and gives the output of compress_append followed
+    by decode_attention, bit for bit: one fused launch for up to 16 new rows (cfg 0-3, and cfg 4
+    with 3 sequences x 4 queries), the two-launch path beyond (cfg 4 with 5 sequences); the
+    output also meets the oracle's bar for sequence 0."""
+    w = dataclasses.replace(I.WORKLOADS[cfg], B=len(lens0))
+    H.log(f"[step] cfg={cfg} {w.name} lens0={lens0} n_q={w.n_q}")
+    run = H.make_layer(w, exact=True)
+    H.calibrate(run)
+    H.prefill(run, lens0, oracle_seqs=[0])
+    n_q = w.n_q
+    lens_pre = run.lens.copy()
+    k0, v0 = run.cache.k_rows.clone(), run.cache.v_tiles.clone()
+    Xn_np = H.hidden(run, I.x_new(w, n_q, step=3))
+    Xn = H.to_dev(Xn_np, w.dtype)
+    run.lens = lens_pre + n_q
+    q_np = H.queries(run, step=3)
+    q = H.to_dev(q_np, w.dtype)
+    # two calls
+    run.GL.append(run.cache, Xn, lens_pre)
+    out_a = run.GL.decode(run.cache, q, run.lens)
+    torch.cuda.synchronize()
+    ka, va = run.cache.k_rows.clone(), run.cache.v_tiles.clone()
+    # the fused step on the same starting cache
+    run.cache.k_rows.copy_(k0)
+    run.cache.v_tiles.copy_(v0)
+    out_b = run.GL.step(run.cache, Xn, q, run.lens)
+    torch.cuda.synchronize()
+    assert torch.equal(run.cache.k_rows, ka) and torch.equal(run.cache.v_tiles, va), "cache bytes"
+    bits = (lambda t: t.view(torch.int32)) if out_a.dtype == torch.float32 else (lambda t: t.view(torch.int16))
+    assert torch.equal(bits(out_a), bits(out_b)), "output bits"
+    oc = O.compress(Xn_np[0], run.OL, run.scales_o)
+    old = run.ocache[0]
+    run.ocache[0] = O.SequenceCache(np.concatenate([old.key, oc.key]), np.concatenate([old.value, oc.value]))
+    ref = H.oracle_decode(run, q_np, 0, mode="latent")
+    H.check_output(w, H.from_dev(out_b)[0], ref, f"seq 0 len {int(run.lens[0])}")
