@@ -1584,26 +1584,25 @@ struct StepFrontArgs {
   int nrg;    // query-projection row groups
 };
 
+// Grid: the query-projection workgroups first (their chain of dependent steps starts
+// earliest), then the append workgroups; four waves each.
 template <int DT, int LAT, int SW>
-__global__ __launch_bounds__(512) void k_step_front(StepFrontArgs a) {
-  __shared__ float red[7][4][64];
+__global__ __launch_bounds__(256) void k_step_front(StepFrontArgs a) {
+  __shared__ float red[3][4][64];
   __shared__ QprojShared sh;
   const int blk = blockIdx.x;
-  if (blk < a.n_app) {
-    skinny_body<DT, SW, LAT == STARKV_LATENT_MIX84>(a.ga, blk, red);
-  } else {
-    const int k = blk - a.n_app;
-    const int H = a.qa.g.H_kv, B = a.qa.g.B;
-    qproj_body<DT, LAT, 512>(a.qa, k % H, (k / H) % B, k / (H * B), a.nrg, sh);
-  }
+  const int H = a.qa.g.H_kv, B = a.qa.g.B;
+  const int n_qp = H * B * a.nrg;
+  if (blk < n_qp) qproj_body<DT, LAT, 256>(a.qa, blk % H, (blk / H) % B, blk / (H * B), a.nrg, sh);
+  else skinny_body<DT, SW, LAT == STARKV_LATENT_MIX84, 4>(a.ga, blk - n_qp, red);
 }
 
 template <int SW>
 static hipError_t launch_front(const Layer& L, const ProfScope& ps, dim3 grid, hipStream_t s, const StepFrontArgs& fa) {
-  if (L.dtype == STARKV_F32) return launch_k(ps, k_step_front<STARKV_F32, STARKV_LATENT_F32, SW>, grid, dim3(512), s, fa);
+  if (L.dtype == STARKV_F32) return launch_k(ps, k_step_front<STARKV_F32, STARKV_LATENT_F32, SW>, grid, dim3(256), s, fa);
   if (L.latent == STARKV_LATENT_BF16)
-    return launch_k(ps, k_step_front<STARKV_BF16, STARKV_LATENT_BF16, SW>, grid, dim3(512), s, fa);
-  return launch_k(ps, k_step_front<STARKV_BF16, STARKV_LATENT_MIX84, SW>, grid, dim3(512), s, fa);
+    return launch_k(ps, k_step_front<STARKV_BF16, STARKV_LATENT_BF16, SW>, grid, dim3(256), s, fa);
+  return launch_k(ps, k_step_front<STARKV_BF16, STARKV_LATENT_MIX84, SW>, grid, dim3(256), s, fa);
 }
 
 static hipError_t launch_decode_tail(const Layer& L, const DecodePlan& plan, const KtList& kts, const SeqTable& seq,

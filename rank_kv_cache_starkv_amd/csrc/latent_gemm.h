@@ -145,7 +145,7 @@ __device__ __forceinline__ int slot_channel_nb(const GemmArgs& a, int slot) {
 }
 
 // Few-token append (M <= 16 rows): the work is reading A once.  Workgroup = SW cache slots x all
-// rows; the 8 waves split K = d and their 16x16 partial results are summed through LDS.
+// rows; its NWV waves split K = d and their 16x16 partial results are summed through LDS.
 //   SW = 16 (M <= 16): MFMA row i = token i, column j = slot j.
 //   SW = 8 (M <= 8): twice as many workgroups, so that every CU streams A.  Row i and column j
 //     of the 16x16 tile take token i % 8 and slot j % 8 over K-half i / 8 (resp. j / 8); the tile
@@ -155,10 +155,12 @@ __device__ __forceinline__ int slot_channel_nb(const GemmArgs& a, int slot) {
 // past M read row 0 and are never stored; padding slots read channel 0 with the A_t operand
 // zeroed).  The cache positions of the output rows are fetched at the start.
 // 16x16x32 bf16 MFMA (16x16x4 f32 for the fp32 path).
-template <int DT, int SW, bool MIX>
+template <int DT, int SW, bool MIX, int NWV = 8>
 __device__ __forceinline__ void skinny_body(const GemmArgs& a, int blk, float (*red)[4][64]) {
   constexpr bool HALF = SW == 8;
-  constexpr int KU = DT == STARKV_BF16 ? (HALF ? 8 : 16) : (HALF ? 4 : 8);
+  // K-steps per load batch: a wave's whole range with 8 waves; at most 32 16-byte loads per lane
+  constexpr int KU0 = (DT == STARKV_BF16 ? (HALF ? 8 : 16) : (HALF ? 4 : 8)) * (8 / NWV);
+  constexpr int KU = KU0 < (DT == STARKV_BF16 ? 16 : 8) ? KU0 : (DT == STARKV_BF16 ? 16 : 8);
   constexpr int NL = DT == STARKV_BF16 ? 1 : 2;  // 16-byte loads per operand per K-step
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
@@ -180,7 +182,7 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& a, int blk, float (*
     ms[v] = (HALF && (q >= 2 || n >= 8)) ? a.M : 4 * q + v;
     ps[v] = row_pos(a, ms[v]);
   }
-  const int per = (kst_all + 7) / 8;
+  const int per = (kst_all + NWV - 1) / NWV;
   const int k_beg = wave * per, k_end = min(kst_all, k_beg + per);
   f32x4 acc = {0, 0, 0, 0};
   for (int k0 = k_beg; k0 < k_end; k0 += KU) {
@@ -226,7 +228,7 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& a, int blk, float (*
   for (int v = 0; v < 4; ++v) {
     float x = acc[v];
 #pragma unroll
-    for (int w = 0; w < 7; ++w) x += red[w][v][lane];
+    for (int w = 0; w < NWV - 1; ++w) x += red[w][v][lane];
     // second K-half of (token 4q + v, slot n): D element (4q + 8 + v, n + 8) in lane + 40
     if (HALF) x += __shfl(x, (lane + 40) & 63, 64);
     xs[v] = x;  // D row = token row; D column = n
