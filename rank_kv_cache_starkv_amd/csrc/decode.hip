@@ -126,6 +126,8 @@ int plan_decode(const Layer& L, int B, int n_q, const int32_t* lens, int T_max, 
     total_chunks += nc;
     max_chunks = std::max(max_chunks, nc);
   }
+  // running-maximum slots: at most 16 chunks' atomics per slot
+  g.nslots = max_chunks > 256 ? kMaxSlots : 16;
   // splits: aim at ~512 value workgroups (two per CU), at least 8 tiles (two per wave) per split
   const int target_wg = env_int("STARKV_VALUE_WGS", 512);
   int cps = std::max(8, ceil_div(total_chunks, std::max(1, target_wg / n_slices)));
@@ -155,7 +157,7 @@ int plan_decode(const Layer& L, int B, int n_q, const int32_t* lens, int T_max, 
   const size_t o_p = o; o = align256(o + (size_t)total_chunks * g.M_pad * kTC * esz_p);
   const size_t o_cm = o; o = align256(o + (size_t)total_chunks * g.M_pad * 4);
   const size_t o_cl = o; o = align256(o + (size_t)total_chunks * g.M_pad * 4);
-  const size_t o_gmax = o; o = align256(o + (size_t)B * g.M_pad * kMaxSlots * 4);
+  const size_t o_gmax = o; o = align256(o + (size_t)B * g.M_pad * g.nslots * 4);
   const size_t o_zp = o; o = align256(o + (size_t)total_splits * g.M_pad * g.rv_ld * 4);
   const size_t o_sl = o; o = align256(o + (size_t)total_splits * g.M_pad * 4);
   const size_t o_zt = o; o = align256(o + (size_t)B * g.M_pad * g.rv_ld * 4);
@@ -238,8 +240,8 @@ __device__ __forceinline__ void qproj_body(const QprojArgs& a, int gk, int b, in
   const int o4 = (LAT == STARKV_LATENT_MIX84) ? a.heads.off4[gk] : 0;
 
   // the running-maximum slots of these rows start at -inf (the key-score kernel raises them)
-  for (int idx = tid; idx < (r_hi - r_lo) * kMaxSlots; idx += NT)
-    a.gmax[((size_t)b * g.M_pad + gk * rph + r_lo + idx / kMaxSlots) * kMaxSlots + idx % kMaxSlots] =
+  for (int idx = tid; idx < (r_hi - r_lo) * g.nslots; idx += NT)
+    a.gmax[((size_t)b * g.M_pad + gk * rph + r_lo + idx / g.nslots) * g.nslots + idx % g.nslots] =
         ord_key(-INFINITY);
 
   for (int rb0 = r_lo; rb0 < r_hi; rb0 += RB) {
@@ -700,7 +702,7 @@ __global__ __launch_bounds__(256) void k_scores(ScoreArgs a) {
   if (qq == 0) {
     a.cm[(size_t)cg * g.M_pad + i] = m;
     a.cl[(size_t)cg * g.M_pad + i] = l;
-    if (rowvalid) atomicMax(a.gmax + ((size_t)b * g.M_pad + i) * kMaxSlots + cidx % kMaxSlots, ord_key(m));
+    if (rowvalid) atomicMax(a.gmax + ((size_t)b * g.M_pad + i) * g.nslots + cidx % g.nslots, ord_key(m));
   }
 }
 
@@ -879,7 +881,7 @@ __global__ __launch_bounds__(256) void k_scores_chunk(ScoreArgs a) {
       a.cm[(size_t)cg * g.M_pad + i] = m;
       a.cl[(size_t)cg * g.M_pad + i] = l;
       if (rowvalid)
-        atomicMax(a.gmax + ((size_t)b * g.M_pad + i) * kMaxSlots + (t0 / kTC) % kMaxSlots, ord_key(m));
+        atomicMax(a.gmax + ((size_t)b * g.M_pad + i) * g.nslots + (t0 / kTC) % g.nslots, ord_key(m));
     }
   }
 }
@@ -902,15 +904,16 @@ struct ValueArgs {
   int n_sl, n_splits;  // one-M-tile kernel: slices per split, splits in all
 };
 
-// Row maximum of the base-2 logits of query row `row` (index into [B][M_pad]) over its slots.
-__device__ __forceinline__ float row_max(const int* gmax, size_t row) {
-  const int* p = gmax + row * kMaxSlots;
+// Row maximum of the base-2 logits of query row `row` (index into [B][M_pad]) over its nslots
+// (16 or 64) slots: sixteen 16-byte loads issued at once (with 16 slots the last four repeat).
+__device__ __forceinline__ float row_max(const int* gmax, size_t row, int nslots) {
+  const int* p = gmax + row * nslots;
+  u32x4 v[kMaxSlots / 4];
+#pragma unroll
+  for (int k = 0; k < kMaxSlots / 4; ++k) v[k] = ld16(p + 4 * min(k, nslots / 4 - 1));
   int m = ord_key(-INFINITY);
 #pragma unroll
-  for (int k = 0; k < kMaxSlots / 4; ++k) {
-    const u32x4 v = ld16(p + 4 * k);
-    m = max(m, max(max((int)v[0], (int)v[1]), max((int)v[2], (int)v[3])));
-  }
+  for (int k = 0; k < kMaxSlots / 4; ++k) m = max(m, max(max((int)v[k][0], (int)v[k][1]), max((int)v[k][2], (int)v[k][3])));
   return ord_val(m);
 }
 
@@ -963,7 +966,7 @@ __global__ __launch_bounds__(256) void k_values(ValueArgs a) {
 #pragma unroll
   for (int mt = 0; mt < NMT; ++mt) {
     const int row = min(mt * 32 + r, g.M_q - 1);
-    Ms[mt] = row_max(a.gmax, (size_t)b * g.M_pad + row);
+    Ms[mt] = row_max(a.gmax, (size_t)b * g.M_pad + row, g.nslots);
     lsum[mt] = 0.f;
   }
 
@@ -1156,7 +1159,6 @@ __device__ __forceinline__ void values1_run(const ValueArgs& a, int slice, int s
   const int len = seq_len(a.seq, b);
   const bool rok = r < g.M_q;
   const size_t prow = (size_t)(rok ? r : 0);
-  const float M = row_max(a.gmax, (size_t)b * g.M_pad + prow);
   // tiles of this wave: chunks c_lo + wave + 4k, k < ntw (wave-uniform)
   const int ntw = c_lo + wave < c_hi ? (c_hi - c_lo - wave + 3) / 4 : 0;
   const uint8_t* vb = a.v_tiles + (size_t)b * (g.T_max / kTT) * g.v_tile_bytes + 16 * VL::NV * q;
@@ -1170,6 +1172,7 @@ __device__ __forceinline__ void values1_run(const ValueArgs& a, int slice, int s
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[t][v] = 0.f;
   float lsum = 0.f;
+  float M = 0.f;  // the sequence's row maximum (read once the first tiles are in flight)
 
   auto load = [&](VTile<LAT, NBW>& t, int k) {
     const int c = c_lo + wave + 4 * min(k, ntw - 1);
@@ -1267,6 +1270,8 @@ __device__ __forceinline__ void values1_run(const ValueArgs& a, int slice, int s
     VTile<LAT, NBW> ta[U], tb[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) load(ta[u], u);
+    // the sequence's row maximum, read while the first tiles are in flight
+    M = row_max(a.gmax, (size_t)b * g.M_pad + prow, g.nslots);
     for (int k0 = 0; k0 < ntw; k0 += 2 * U) {
 #pragma unroll
       for (int u = 0; u < U; ++u) load(tb[u], k0 + U + u);
@@ -1354,43 +1359,55 @@ struct MergeArgs {
   void* out;
   DecodeGeom g;
   SeqTable seq;
+  int nsp;  // split merge: lanes sharing 4 channels (1, or 4 for many splits)
 };
 
 // Split merge.  Every split of a sequence weighted its tiles against the same row maximum (the
-// whole sequence's), so the merge is a plain sum, taken in split order: z~[c] = (sum_s z_s[c]) *
-// scale_c / (sum_s l_s), and zero in the padding channels [r_v, rv_ld).  Workgroup = 4 rows x
-// 256 channels of one sequence; a thread takes 4 channels with 16-byte loads of every split.
+// whole sequence's), so the merge is a plain sum: z~[c] = (sum_s z_s[c]) * scale_c / (sum_s l_s),
+// and zero in the padding channels [r_v, rv_ld).  Workgroup = 4 rows x (256 / nsp) channels of one
+// sequence; nsp adjacent lanes (1 or 4) share 4 channels and take every nsp-th split each, all
+// their loads issued at once (16 splits per batch), and add their partial sums by lane exchange
+// in a fixed order, so the result is deterministic.
 __global__ __launch_bounds__(256) void k_zmerge(MergeArgs a) {
   const DecodeGeom& g = a.g;
+  const int nsp = a.nsp;
   const int b = blockIdx.z;
   const int tid = threadIdx.x;
+  const int sp = tid & (nsp - 1);
   const int i = blockIdx.y * 4 + (tid >> 6);
-  const int c = blockIdx.x * 256 + (tid & 63) * 4;
-  if (i >= g.M_q || c >= g.rv_ld) return;
+  const int c = blockIdx.x * (256 / nsp) + ((tid & 63) / nsp) * 4;
+  const bool live = i < g.M_q && c < g.rv_ld;
+  const int ic = min(i, g.M_q - 1), cc = min(c, g.rv_ld - 4);
   const int s0 = seq_split0(a.seq, b), ns = seq_nsplit(a.seq, b);
-  const float* zc = a.zp + ((size_t)s0 * g.M_pad + i) * g.rv_ld + c;
-  const float* lc = a.sl + (size_t)s0 * g.M_pad + i;
+  const float* zc = a.zp + ((size_t)s0 * g.M_pad + ic) * g.rv_ld + cc;
+  const float* lc = a.sl + (size_t)s0 * g.M_pad + ic;
   const size_t zs = (size_t)g.M_pad * g.rv_ld;
   float z[4] = {0.f, 0.f, 0.f, 0.f};
   float l = 0.f;
-  for (int s = 0; s < ns; s += 8) {
-    u32x4 v[8];
-    float lv[8];
+  for (int s = sp; s < ns; s += 16 * nsp) {
+    u32x4 v[16];
+    float lv[16];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int ss = min(s + u, ns - 1);
+    for (int u = 0; u < 16; ++u) {
+      const int ss = min(s + u * nsp, ns - 1);
       v[u] = ld16(zc + (size_t)ss * zs);
       lv[u] = lc[(size_t)ss * g.M_pad];
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      if (s + u < ns) {
+    for (int u = 0; u < 16; ++u) {
+      if (s + u * nsp < ns) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) z[e] += __uint_as_float(v[u][e]);
         l += lv[u];
       }
     }
   }
+  for (int m = 1; m < nsp; m <<= 1) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) z[e] += __shfl_xor(z[e], m, 64);
+    l += __shfl_xor(l, m, 64);
+  }
+  if (!live || sp != 0) return;
   const float il = 1.f / l;
   u32x4 o;
 #pragma unroll
@@ -1738,7 +1755,10 @@ static hipError_t launch_decode_tail(const Layer& L, const DecodePlan& plan, con
   ma.seq = seq;
   {
     ProfScope ps("decode_zmerge");
-    const dim3 gz((g.rv_ld + 255) / 256, (g.M_q + 3) / 4, g.B);
+    int max_ns = 1;
+    for (int b = 0; b < g.B; ++b) max_ns = std::max(max_ns, seq.split_off[b + 1] - seq.split_off[b]);
+    ma.nsp = max_ns > 8 ? 4 : 1;
+    const dim3 gz((g.rv_ld + 256 / ma.nsp - 1) / (256 / ma.nsp), (g.M_q + 3) / 4, g.B);
     e = launch_k(ps, k_zmerge, gz, dim3(256), s, ma);
     if (e != hipSuccess) return e;
   }
