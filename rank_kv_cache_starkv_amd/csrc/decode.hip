@@ -115,6 +115,10 @@ int plan_decode(const Layer& L, int B, int n_q, const int32_t* lens, int T_max, 
   w.n_sl8 = ceil_div(nb8, w.nbw8);
   w.n_sl4 = L.mix() ? ceil_div(NB - nb8, w.nbw4) : 0;
   if (g.M_pad == 32) n_slices = w.n_sl8 + w.n_sl4;
+  // many query rows (bf16, int8/int4): groups of four 32-channel N-tiles
+  const int n_nt = L.mix() ? nb8 + 2 * (NB - nb8) : NB;
+  w.n_grp = ceil_div(n_nt, g.M_pad <= 160 ? 8 : 4);  // N-tiles per workgroup: 4 waves x (2, or 1 past 5 row tiles)
+  if (g.M_pad > 32 && L.latent != STARKV_LATENT_F32) n_slices = w.n_grp;
   int total_chunks = 0, max_chunks = 0;
   seq->chunk_off[0] = 0;
   seq->blk_off[0] = 0;
@@ -466,7 +470,8 @@ struct ScoreArgs {
 // workgroup may span sequences); work unit = (column tile ct, chunk).  Per unit the loop runs
 // K-tile outer / 16-token tile inner, so each query fragment is loaded once per unit.
 // Workgroup = (sequence, column tile ct, block of 128 tokens = four 32-token chunks).  The four
-// waves split the K-tiles of ct (wave w takes K-tiles w, w+4, ...) and keep their query
+// waves split the K-tiles of ct (wave w takes K-tiles w, w+4, ...: waves read neighbouring K-tiles
+// of the same key rows at the same time) and keep their query
 // fragments in registers for the whole block; each wave computes partial scores of the 8
 // 16-token tiles over its K-tiles (loads of 4 tiles x 4 K-tiles in flight), the partials are
 // added through LDS, and wave w then finishes chunk w: mask, chunk max and sum, p~ = 2^(s - m).
@@ -1347,6 +1352,209 @@ __global__ __launch_bounds__(256) void k_values1(ValueArgs a) {
   }
 }
 
+// Many query rows per sequence (M_pad = 32 NMT > 32; bf16 or int8/int4 latents): workgroup =
+// (split of one sequence, group of 4 NTW value N-tiles of 32 channels); wave w owns N-tiles
+// NTW w .. NTW w + NTW - 1 of the group -- each a bf16 or int8 block of 32 channels, or the even
+// or odd channels of an int4 block -- for all NMT row tiles.  The probability tile [M_pad][32] of
+// each 32-token chunk is staged in LDS once per workgroup by the first M_pad threads (row t:
+// rescaled by 2^(m_chunk - M_t), rounded to the MFMA input type), double-buffered, and read by
+// every wave as A fragments: the tile is fetched once per 4 NTW N-tiles.  The next chunk's loads
+// are issued before the current chunk's MFMAs.  Grid as k_values1 (one dimension; the groups of a
+// split run on one XCD).
+template <int LAT, int NMT, int NTW>
+__global__ __launch_bounds__(256) void k_values_mt(ValueArgs a) {
+  static_assert(LAT != STARKV_LATENT_F32, "fp32 latents use k_values");
+  constexpr int MP = 32 * NMT;
+  constexpr int RS = 40;                                    // LDS row stride (16-bit elements, 80 B)
+  constexpr int NV = LAT == STARKV_LATENT_BF16 ? 2 : 1;     // 16-byte value loads per lane per chunk
+  constexpr int esz = LAT == STARKV_LATENT_BF16 ? 2 : 1;
+  __shared__ __align__(16) uint16_t pt[2][MP * RS];
+  const DecodeGeom& g = a.g;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int r = lane & 31, q = lane >> 5;
+  const int xcd = blockIdx.x & 7, kk = blockIdx.x >> 3;
+  const int grp = kk % a.n_sl;
+  const int sg = 8 * (kk / a.n_sl) + xcd;
+  if (sg >= a.n_splits) return;
+  const int b = seq_of_split(a.seq, g.B, sg);
+  const int s = sg - seq_split0(a.seq, b);
+  const int cbase = seq_chunk0(a.seq, b);
+  const int nch = seq_nch(a.seq, b);
+  const int c_lo = s * a.cps, c_hi = min(c_lo + a.cps, nch);
+  const int len = seq_len(a.seq, b);
+
+  // this wave's N-tiles
+  const int n_nt8 = LAT == STARKV_LATENT_MIX84 ? a.V8 / 32 : a.NB;
+  const int n_nt = n_nt8 + (LAT == STARKV_LATENT_MIX84 ? 2 * (a.NB - a.V8 / 32) : 0);
+  bool ntok[NTW], is4[NTW];
+  int blk[NTW], par[NTW];
+  const uint8_t* vb[NTW];
+#pragma unroll
+  for (int j = 0; j < NTW; ++j) {
+    const int nt = (grp * 4 + wave) * NTW + j;
+    ntok[j] = nt < n_nt;  // wave-uniform
+    blk[j] = 0;
+    par[j] = 0;
+    is4[j] = false;
+    if (ntok[j]) {
+      if (nt < n_nt8) {
+        blk[j] = nt;
+      } else {
+        blk[j] = a.V8 / 32 + (nt - n_nt8) / 2;
+        par[j] = (nt - n_nt8) & 1;
+        is4[j] = true;
+      }
+    }
+    vb[j] = a.v_tiles + (size_t)b * (g.T_max / kTT) * g.v_tile_bytes + (size_t)(blk[j] * 32 + r) * kTT * esz +
+            16 * NV * q;
+  }
+
+  // staging role: thread t < MP stages row t of every chunk
+  const bool stager = tid < MP;
+  const int srow = min(tid, MP - 1);
+  const bool sval = tid < g.M_q;
+  const size_t srow_g = (size_t)min(srow, g.M_q - 1);
+  const float Ms = row_max(a.gmax, (size_t)b * g.M_pad + srow_g, g.nslots);
+  float lsum = 0.f;
+
+  struct Stage {
+    u32x4 p[4];
+    float cm, cl;
+  };
+  auto sload = [&](Stage& st, int c) {
+    const size_t cr = (size_t)(cbase + c) * g.M_pad + srow;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) st.p[x] = ld16((const uint16_t*)a.p + cr * kTC + 8 * x);
+    st.cm = a.cm[cr];
+    st.cl = a.cl[cr];
+  };
+  auto sstore = [&](const Stage& st, int buf) {
+    const float alpha = (!sval || st.cm == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(st.cm - Ms);
+    lsum += sval ? alpha * st.cl : 0.f;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float x0, x1;
+        if (LAT == STARKV_LATENT_BF16) {
+          x0 = bf16_to_f32((uint16_t)(st.p[x][e] & 0xFFFF)) * alpha;
+          x1 = bf16_to_f32((uint16_t)(st.p[x][e] >> 16)) * alpha;
+          w[e] = (uint32_t)f32_to_bf16(x0) | ((uint32_t)f32_to_bf16(x1) << 16);
+        } else {
+          x0 = f16_to_f32((uint16_t)(st.p[x][e] & 0xFFFF)) * alpha;
+          x1 = f16_to_f32((uint16_t)(st.p[x][e] >> 16)) * alpha;
+          w[e] = (uint32_t)f32_to_f16(x0) | ((uint32_t)f32_to_f16(x1) << 16);
+        }
+      }
+      *reinterpret_cast<u32x4*>(&pt[buf][srow * RS + 8 * x]) = w;
+    }
+  };
+
+  f32x16 acc[NTW][NMT];
+#pragma unroll
+  for (int j = 0; j < NTW; ++j)
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[j][mt][v] = 0.f;
+
+  Stage sn;
+  u32x4 vcur[NTW][NV], vn[NTW][NV];
+  if (stager) {
+    sload(sn, c_lo);
+    sstore(sn, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < NTW; ++j)
+#pragma unroll
+    for (int x = 0; x < NV; ++x) vcur[j][x] = ld16(vb[j] + (size_t)c_lo * g.v_tile_bytes + 16 * x);
+  __syncthreads();
+  for (int c = c_lo; c < c_hi; ++c) {
+    const int cur = (c - c_lo) & 1;
+    const int cn = min(c + 1, c_hi - 1);
+    // next chunk's loads first
+    if (stager) sload(sn, cn);
+#pragma unroll
+    for (int j = 0; j < NTW; ++j)
+#pragma unroll
+      for (int x = 0; x < NV; ++x) vn[j][x] = ld16(vb[j] + (size_t)cn * g.v_tile_bytes + 16 * x);
+    // this chunk
+    if (LAT == STARKV_LATENT_BF16 && c * kTC + kTT > len) {
+      // zero the elements of tokens at or past the length (their bits may be anything)
+#pragma unroll
+      for (int j = 0; j < NTW; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int t = c * kTC + 16 * q + e;
+          if (t >= len) {
+            const uint32_t keep = (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+            vcur[j][e >> 3][(e >> 1) & 3] &= keep;
+          }
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      u32x4 af[NMT];
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt)
+        af[mt] = *reinterpret_cast<const u32x4*>(&pt[cur][(mt * 32 + r) * RS + 16 * q + 8 * h]);
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) {
+        u32x4 bfrag;
+        if (LAT == STARKV_LATENT_BF16) {
+          bfrag = vcur[j][h % NV];
+        } else {
+          f16x8 ev, od;
+          if (is4[j]) {
+            deq_i4x8(vcur[j][0][2 * h], vcur[j][0][2 * h + 1], ev, od);
+            if (par[j]) ev = od;
+          } else {
+            ev = deq_i8x8(vcur[j][0][2 * h], vcur[j][0][2 * h + 1]);
+          }
+          bfrag = __builtin_bit_cast(u32x4, ev);
+        }
+#pragma unroll
+        for (int mt = 0; mt < NMT; ++mt) {
+          if (LAT == STARKV_LATENT_BF16) acc[j][mt] = mfma32_bf16(as_bf16x8(af[mt]), as_bf16x8(bfrag), acc[j][mt]);
+          else acc[j][mt] = mfma32_f16(as_f16x8(af[mt]), as_f16x8(bfrag), acc[j][mt]);
+        }
+      }
+    }
+    if (stager && c + 1 < c_hi) sstore(sn, cur ^ 1);
+#pragma unroll
+    for (int j = 0; j < NTW; ++j)
+#pragma unroll
+      for (int x = 0; x < NV; ++x) vcur[j][x] = vn[j][x];
+    __syncthreads();
+  }
+
+  // z partials: lane holds channel r of each N-tile, rows d32_row(v, q) of each row tile
+#pragma unroll
+  for (int j = 0; j < NTW; ++j) {
+    if (!ntok[j]) continue;
+    int vc;
+    bool cok;
+    if (!is4[j]) {
+      vc = blk[j] * 32 + r;
+      cok = vc < (LAT == STARKV_LATENT_MIX84 ? a.n8v : g.r_v);
+    } else {
+      const int w = 2 * ((blk[j] - a.V8 / 32) * 32 + r) + par[j];
+      cok = w < a.n4v;
+      vc = a.n8v + w;
+    }
+    if (!cok) continue;
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = mt * 32 + d32_row(v, q);
+        if (row < g.M_q) a.zp[((size_t)sg * g.M_pad + row) * g.rv_ld + vc] = acc[j][mt][v];
+      }
+  }
+  if (grp == 0 && sval) a.sl[(size_t)sg * g.M_pad + tid] = lsum;
+}
+
 // ===========================================================================
 // merge + up-projection: out = (sum_s z_s) * scale_v B_v^g / (sum_s l_s)
 
@@ -1418,6 +1626,92 @@ __global__ __launch_bounds__(256) void k_zmerge(MergeArgs a) {
     o[e] = __float_as_uint(ce < g.r_v ? z[e] * sc : 0.f);
   }
   st16(a.zt + ((size_t)b * g.M_pad + i) * g.rv_ld + c, o);
+}
+
+// Up-projection for many rows per KV head (bf16, r_v % 8 == 0): workgroup = (g, 64-row tile of
+// g's rows over all sequences); wave w takes the 32-column slices w, w + 4, ... of d_h over two
+// 32-row tiles (32x32x16 bf16 MFMA, z~ split into hi + lo bf16 parts).  Each workgroup reads its
+// rows of z~ and g's B_v^T slab once from memory (the four waves share them through the caches).
+// Loads are unconditional: rows past the end read the last row (not stored); channels at or past
+// r_v are zero in z~ and masked in B_v (their address clamped into the row).
+__global__ __launch_bounds__(256) void k_upproj_tall(MergeArgs a) {
+  constexpr int KB = 4;  // 16-channel K-steps per load batch
+  const DecodeGeom& g = a.g;
+  const int gk = blockIdx.x;
+  const int rph = g.G * g.n_q;
+  const int Rg = g.B * rph;
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int r = lane & 31, q = lane >> 5;
+  const float* zr[2];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    const int rr = min((int)blockIdx.y * 64 + mt * 32 + r, Rg - 1);
+    zr[mt] = a.zt + ((size_t)(rr / rph) * g.M_pad + gk * rph + rr % rph) * g.rv_ld + 8 * q;
+  }
+  for (int cs = wave; cs < g.d_h / 32; cs += 4) {
+    const uint16_t* bp = (const uint16_t*)a.B_vt + (size_t)(gk * g.d_h + cs * 32 + r) * g.r_v;
+    f32x16 acc[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[mt][v] = 0.f;
+    // K loop double-buffered: the loads of batch i + 1 are issued before the MFMAs of batch i
+    auto loadb = [&](u32x4 (&z)[KB][2][2], u32x4 (&bw)[KB], int k0) {
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
+        const int kc = min(k0 + 16 * u, g.rv_ld - 16);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          z[u][mt][0] = ld16(zr[mt] + kc);
+          z[u][mt][1] = ld16(zr[mt] + kc + 4);
+        }
+        bw[u] = ld16(bp + min(kc + 8 * q, g.r_v - 8));
+      }
+    };
+    auto compb = [&](u32x4 (&z)[KB][2][2], u32x4 (&bw)[KB], int k0) {
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
+        const int kc = k0 + 16 * u;
+        const bool live = kc < g.rv_ld && kc + 8 * q < g.r_v;
+        const u32x4 bb = live ? bw[u] : u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          u32x4 ah, al;
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2) {
+            const float z0 = __uint_as_float(z[u][mt][e2 >> 1][2 * (e2 & 1)]);
+            const float z1 = __uint_as_float(z[u][mt][e2 >> 1][2 * (e2 & 1) + 1]);
+            const uint16_t h0 = f32_to_bf16(z0), h1 = f32_to_bf16(z1);
+            const uint16_t l0 = f32_to_bf16(z0 - bf16_to_f32(h0)), l1 = f32_to_bf16(z1 - bf16_to_f32(h1));
+            ah[e2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+            al[e2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+          }
+          acc[mt] = mfma32_bf16(as_bf16x8(ah), as_bf16x8(bb), acc[mt]);
+          acc[mt] = mfma32_bf16(as_bf16x8(al), as_bf16x8(bb), acc[mt]);
+        }
+      }
+    };
+    u32x4 zA[KB][2][2], bA[KB], zB[KB][2][2], bB[KB];
+    loadb(zA, bA, 0);
+    for (int k0 = 0; k0 < g.rv_ld; k0 += 32 * KB) {
+      loadb(zB, bB, k0 + 16 * KB);
+      compb(zA, bA, k0);
+      if (k0 + 16 * KB >= g.rv_ld) break;
+      loadb(zA, bA, k0 + 32 * KB);
+      compb(zB, bB, k0 + 16 * KB);
+    }
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int orow = blockIdx.y * 64 + mt * 32 + d32_row(v, q);
+        if (orow >= Rg) continue;
+        const int ob = orow / rph, iw = orow % rph;
+        const int hh = iw / g.n_q, j = iw % g.n_q;
+        const int h = gk * g.G + hh;
+        ((uint16_t*)a.out)[(((size_t)ob * g.n_q + j) * g.H_q + h) * g.d_h + cs * 32 + r] = f32_to_bf16(acc[mt][v]);
+      }
+  }
 }
 
 // Up-projection out_i = z~_i B_v^g for the rows of KV head g.  Workgroup = (g, 16-column slice of
@@ -1552,6 +1846,20 @@ static hipError_t launch_values_nmt(const ProfScope& ps, int nmt, dim3 grid, dim
     case 6: return launch_k(ps, k_values<LAT, 6>, grid, block, s, va);
     case 7: return launch_k(ps, k_values<LAT, 7>, grid, block, s, va);
     default: return launch_k(ps, k_values<LAT, 8>, grid, block, s, va);
+  }
+}
+
+template <int LAT>
+static hipError_t launch_values_mt(const ProfScope& ps, int nmt, dim3 grid, hipStream_t s, const ValueArgs& va) {
+  const dim3 blk(256);
+  switch (nmt) {
+    case 2: return launch_k(ps, k_values_mt<LAT, 2, 2>, grid, blk, s, va);
+    case 3: return launch_k(ps, k_values_mt<LAT, 3, 2>, grid, blk, s, va);
+    case 4: return launch_k(ps, k_values_mt<LAT, 4, 2>, grid, blk, s, va);
+    case 5: return launch_k(ps, k_values_mt<LAT, 5, 2>, grid, blk, s, va);
+    case 6: return launch_k(ps, k_values_mt<LAT, 6, 1>, grid, blk, s, va);
+    case 7: return launch_k(ps, k_values_mt<LAT, 7, 1>, grid, blk, s, va);
+    default: return launch_k(ps, k_values_mt<LAT, 8, 1>, grid, blk, s, va);
   }
 }
 
@@ -1734,6 +2042,12 @@ static hipError_t launch_decode_tail(const Layer& L, const DecodePlan& plan, con
       if (L.latent == STARKV_LATENT_MIX84) e = launch_values1<STARKV_LATENT_MIX84>(ps, w.nbw8, w.nbw4, gv, s, va);
       else if (L.latent == STARKV_LATENT_BF16) e = launch_values1<STARKV_LATENT_BF16>(ps, w.nbw8, w.nbw4, gv, s, va);
       else e = launch_values1<STARKV_LATENT_F32>(ps, w.nbw8, w.nbw4, gv, s, va);
+    } else if (L.latent != STARKV_LATENT_F32) {
+      va.n_sl = w.n_grp;
+      va.n_splits = w.total_splits;
+      const dim3 gv(va.n_sl * ((w.total_splits + 7) / 8 * 8));
+      if (L.latent == STARKV_LATENT_MIX84) e = launch_values_mt<STARKV_LATENT_MIX84>(ps, nmt, gv, s, va);
+      else e = launch_values_mt<STARKV_LATENT_BF16>(ps, nmt, gv, s, va);
     } else {
       const dim3 gv((va.NB + va.bpw - 1) / va.bpw, w.total_splits);
       const dim3 bv(64 * va.bpw);
@@ -1767,7 +2081,9 @@ static hipError_t launch_decode_tail(const Layer& L, const DecodePlan& plan, con
     const int Rg = g.B * g.G * g.n_q;
     const dim3 gm(g.H_kv * (g.d_h / 16), (Rg + 15) / 16);
     const bool vec = (g.r_v & 7) == 0;
-    if (L.dtype == STARKV_F32)
+    if (L.dtype == STARKV_BF16 && vec && Rg >= 64)
+      e = launch_k(ps, k_upproj_tall, dim3(g.H_kv, (Rg + 63) / 64), dim3(256), s, ma);
+    else if (L.dtype == STARKV_F32)
       e = vec ? launch_k(ps, k_upproj<STARKV_F32, true>, gm, dim3(256), s, ma)
               : launch_k(ps, k_upproj<STARKV_F32, false>, gm, dim3(256), s, ma);
     else

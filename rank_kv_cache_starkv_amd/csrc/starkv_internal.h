@@ -112,6 +112,7 @@ struct DecodeWs {
   int blocks_per_wg;  // value blocks (waves) per value WG (several query-row tiles)
   int n_sl8, n_sl4;   // one-row-tile value kernel: slices of one-N-tile blocks / of int4 blocks
   int nbw8, nbw4;     // blocks per slice of each kind
+  int n_grp;          // many-row value kernel: groups of four 32-channel N-tiles
 };
 
 struct DecodePlan {

@@ -295,3 +295,36 @@ def test_decode_step_equals_append_then_decode(cfg, lens0):
     run.ocache[0] = O.SequenceCache(np.concatenate([old.key, oc.key]), np.concatenate([old.value, oc.value]))
     ref = H.oracle_decode(run, q_np, 0, mode="latent")
     H.check_output(w, H.from_dev(out_b)[0], ref, f"seq 0 len {int(run.lens[0])}")
+
+
+@pytest.mark.parametrize("cfg,n_q", [(0, 9), (1, 2), (1, 3), (2, 2)])
+def test_many_query_rows(cfg, n_q):
+    """More than 32 query rows per sequence (n_q queries x H_q heads): the staged many-row value
+    kernel (bf16, int8/int4) and the general one (fp32) against the oracle, causal within the
+    chunk of n_q queries."""
+    w, lens0 = mini(cfg)
+    w = dataclasses.replace(w, B=len(lens0), n_q=n_q)
+    H.log(f"[rows] cfg={cfg} n_q={n_q} rows={w.H_q * n_q} lens={lens0}")
+    run = H.make_layer(w, exact=True)
+    H.calibrate(run)
+    H.prefill(run, lens0, oracle_seqs=range(len(lens0)))
+    q = H.queries(run)
+    got = H.from_dev(H.decode(run, q))
+    for b in run.oracle_seqs:
+        ref = H.oracle_decode(run, q, b)
+        H.check_output(w, got[b], ref, f"seq {b} len {int(run.lens[b])}")
+
+
+def test_many_rows_per_kv_head():
+    """64 query rows per KV head (16 sequences x 4 queries, bf16 latent): the tall up-projection
+    and the staged many-row value kernel against the oracle on every sequence."""
+    lens0 = [40, 75, 128, 200, 33, 64, 97, 150, 45, 81, 110, 190, 36, 70, 129, 160]
+    w = dataclasses.replace(I.WORKLOADS[1], B=len(lens0), n_q=4)
+    H.log(f"[tall] rows per KV head {w.B * w.n_q}, lens={lens0}")
+    run = H.make_layer(w, exact=True)
+    H.prefill(run, lens0, oracle_seqs=range(len(lens0)))
+    q = H.queries(run)
+    got = H.from_dev(H.decode(run, q))
+    for b in run.oracle_seqs:
+        ref = H.oracle_decode(run, q, b, mode="latent")
+        H.check_output(w, got[b], ref, f"seq {b} len {int(run.lens[b])}")
