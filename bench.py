@@ -148,8 +148,9 @@ def _step_kernels(rows):
     out = {}
     if first is None:
         return out
-    # the step's append precedes its query projection
-    for r in rows[max(0, first - 1):]:
+    # without the fused front launch the step's append precedes its query projection
+    start = first if "k_step_front" in rows[first]["name"] else max(0, first - 1)
+    for r in rows[start:]:
         for pat, key in KERNEL_KEYS:
             if pat in r["name"]:
                 out.setdefault(key, []).append(r["v"])
