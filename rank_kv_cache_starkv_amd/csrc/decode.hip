@@ -473,7 +473,8 @@ struct ScoreArgs {
 // waves split the K-tiles of ct (wave w takes K-tiles w, w+4, ...: waves read neighbouring K-tiles
 // of the same key rows at the same time) and keep their query
 // fragments in registers for the whole block; each wave computes partial scores of the 8
-// 16-token tiles over its K-tiles (loads of 4 tiles x 4 K-tiles in flight), the partials are
+// 16-token tiles over its K-tiles (loads of 4 tiles x 2 K-tiles in flight: more per wave measured
+// slower on MI355X), the partials are
 // added through LDS, and wave w then finishes chunk w: mask, chunk max and sum, p~ = 2^(s - m).
 template <int LAT>
 __global__ __launch_bounds__(256) void k_scores(ScoreArgs a) {
@@ -531,7 +532,7 @@ __global__ __launch_bounds__(256) void k_scores(ScoreArgs a) {
       tok_ok[t] = tok < len;
       rowp[t] = kbase + (size_t)(tok_ok[t] ? tok : 0) * g.k_row_bytes;
     }
-    for (int j0 = 0; j0 < nkw; j0 += 4) {
+    for (int j0 = 0; j0 < nkw; j0 += 2) {
       if (LAT == STARKV_LATENT_MIX84) {
         i32x4 av[4][4];
 #pragma unroll
@@ -570,9 +571,9 @@ __global__ __launch_bounds__(256) void k_scores(ScoreArgs a) {
           }
         }
       } else if (LAT == STARKV_LATENT_BF16) {
-        u32x4 av[4][4];
+        u32x4 av[2][4];
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
+        for (int jj = 0; jj < 2; ++jj) {
           const int j = j0 + jj;
           const bool on = j < nkw;
           int P0 = 0;
@@ -587,7 +588,7 @@ __global__ __launch_bounds__(256) void k_scores(ScoreArgs a) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) acc[t] = f32x4{sp[t][0], sp[t][1], sp[t][2], sp[t][3]};
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
+        for (int jj = 0; jj < 2; ++jj) {
           u32x4 fh = {0, 0, 0, 0}, fl = {0, 0, 0, 0};
 #pragma unroll
           for (int x = 0; x < KW; ++x)
@@ -1832,6 +1833,123 @@ __global__ __launch_bounds__(256) void k_upproj(MergeArgs a) {
   }
 }
 
+// Split merge folded into the up-projection (sequences of at most 4 splits): workgroup = (g,
+// 16-column slice of d_h, 16-row tile of g's rows over all sequences); its eight waves split K =
+// rv_ld in 32-channel chunks.  A lane sums its row's split partials for its 8 channels (in split
+// order), scales them by scale_c / sum_s l_s -- the merged latent z~ of k_zmerge, bit for bit --
+// and feeds the MFMA as k_upproj does.  Padding channels (>= r_v) are zeroed; loads unconditional.
+template <int DT>
+__global__ __launch_bounds__(512) void k_upproj_merge(MergeArgs a) {
+  constexpr int NSM = 4;  // splits per sequence, at most
+  constexpr int KU = 4;   // 32-channel chunks per wave
+  const DecodeGeom& g = a.g;
+  const int nsl_n = g.d_h / 16;
+  const int gk = blockIdx.x / nsl_n, nsl = blockIdx.x % nsl_n;
+  const int rph = g.G * g.n_q;
+  const int Rg = g.B * rph;
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int n = lane & 15, qq = lane >> 4;
+  __shared__ float red[7][4][64];
+  const int rr = min((int)blockIdx.y * 16 + n, Rg - 1);  // A-fragment row of this lane
+  const int bb = rr / rph;
+  const int ii = gk * rph + rr % rph;
+  const int s0 = seq_split0(a.seq, bb), ns = seq_nsplit(a.seq, bb);
+  const float* zs[NSM];
+  float l = 0.f;
+#pragma unroll
+  for (int sx = 0; sx < NSM; ++sx) {
+    const size_t sp = (size_t)(s0 + min(sx, ns - 1));
+    zs[sx] = a.zp + (sp * g.M_pad + ii) * g.rv_ld + 8 * qq;
+    const float lv = a.sl[sp * g.M_pad + ii];
+    l += sx < ns ? lv : 0.f;
+  }
+  const float il = 1.f / l;
+  const int col = gk * g.d_h + nsl * 16 + n;  // B_v^T row of this lane's output column
+  const int nchk = g.rv_ld / 32;
+  const int k_beg = wave * KU;  // chunks [k_beg, k_beg + KU) of this wave (nchk <= 8 KU)
+  u32x4 z[KU][NSM][2];
+  u32x4 bw[KU][DT == STARKV_F32 ? 2 : 1];
+  u32x4 sc[KU];
+#pragma unroll
+  for (int u = 0; u < KU; ++u) {
+    const int kc = min(k_beg + u, nchk - 1);
+    const int c = 32 * kc + 8 * qq;  // first channel of this lane's 8
+#pragma unroll
+    for (int sx = 0; sx < NSM; ++sx) {
+      z[u][sx][0] = ld16(zs[sx] + 32 * kc);
+      z[u][sx][1] = ld16(zs[sx] + 32 * kc + 4);
+    }
+    const int cc = c < g.r_v ? c : 0;
+    if (DT == STARKV_F32) {
+      const float* bp = (const float*)a.B_vt + (size_t)col * g.r_v;
+      bw[u][0] = ld16(bp + cc);
+      bw[u][DT == STARKV_F32 ? 1 : 0] = ld16(bp + cc + 4);
+    } else {
+      bw[u][0] = ld16((const uint16_t*)a.B_vt + (size_t)col * g.r_v + cc);
+    }
+    sc[u] = a.vscales ? ld16(a.vscales + cc) : u32x4{0, 0, 0, 0};
+  }
+  __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the arithmetic
+  f32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+  for (int u = 0; u < KU; ++u) {
+    const int c = 32 * (k_beg + u) + 8 * qq;
+    const bool live = k_beg + u < nchk;
+    float zz[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float t = 0.f;
+#pragma unroll
+      for (int sx = 0; sx < NSM; ++sx) t += sx < ns ? __uint_as_float(z[u][sx][e >> 2][e & 3]) : 0.f;
+      float scl = il;
+      if (a.vscales) scl *= f16_to_f32((uint16_t)(e & 1 ? sc[u][e >> 1] >> 16 : sc[u][e >> 1] & 0xFFFF));
+      zz[e] = (live && c + e < g.r_v) ? t * scl : 0.f;
+    }
+    if (DT == STARKV_F32) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float bv = (live && c + 4 * h + e < g.r_v) ? __uint_as_float(bw[u][h % 2][e]) : 0.f;
+          acc = mfma16_f32(zz[4 * h + e], bv, acc);
+        }
+    } else {
+      u32x4 ah, al;
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const uint16_t h0 = f32_to_bf16(zz[2 * e2]), h1 = f32_to_bf16(zz[2 * e2 + 1]);
+        const uint16_t l0 = f32_to_bf16(zz[2 * e2] - bf16_to_f32(h0));
+        const uint16_t l1 = f32_to_bf16(zz[2 * e2 + 1] - bf16_to_f32(h1));
+        ah[e2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        al[e2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+      }
+      const u32x4 bv = (live && c < g.r_v) ? bw[u][0] : u32x4{0, 0, 0, 0};
+      acc = mfma16_bf16(as_bf16x8(ah), as_bf16x8(bv), acc);
+      acc = mfma16_bf16(as_bf16x8(al), as_bf16x8(bv), acc);
+    }
+  }
+  if (wave > 0) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) red[wave - 1][v][lane] = acc[v];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    float o = acc[v];
+#pragma unroll
+    for (int w = 0; w < 7; ++w) o += red[w][v][lane];
+    const int orow = blockIdx.y * 16 + 4 * qq + v;  // D row = row within the tile; D column = n
+    if (orow >= Rg) continue;
+    const int ob = orow / rph, iw = orow % rph;
+    const int hh = iw / g.n_q, j = iw % g.n_q;
+    const int h = gk * g.G + hh;
+    const size_t off = (((size_t)ob * g.n_q + j) * g.H_q + h) * g.d_h + nsl * 16 + n;
+    if (DT == STARKV_F32) ((float*)a.out)[off] = o;
+    else ((uint16_t*)a.out)[off] = f32_to_bf16(o);
+  }
+}
+
 // ===========================================================================
 
 template <int LAT>
@@ -2067,10 +2185,22 @@ static hipError_t launch_decode_tail(const Layer& L, const DecodePlan& plan, con
   ma.out = out;
   ma.g = g;
   ma.seq = seq;
+  int max_ns = 1;
+  for (int b = 0; b < g.B; ++b) max_ns = std::max(max_ns, seq.split_off[b + 1] - seq.split_off[b]);
+  const int Rg = g.B * g.G * g.n_q;
+  const bool vec = (g.r_v & 7) == 0;
+  const bool tall = L.dtype == STARKV_BF16 && vec && Rg >= 64;
+  if (max_ns <= 4 && vec && g.rv_ld <= 32 * 32 && !tall) {
+    // one launch: the merge is folded into the up-projection
+    ProfScope ps("decode_upproj");
+    const dim3 gm(g.H_kv * (g.d_h / 16), (Rg + 15) / 16);
+    e = L.dtype == STARKV_F32 ? launch_k(ps, k_upproj_merge<STARKV_F32>, gm, dim3(512), s, ma)
+                              : launch_k(ps, k_upproj_merge<STARKV_BF16>, gm, dim3(512), s, ma);
+    if (e != hipSuccess) return e;
+    return hipGetLastError();
+  }
   {
     ProfScope ps("decode_zmerge");
-    int max_ns = 1;
-    for (int b = 0; b < g.B; ++b) max_ns = std::max(max_ns, seq.split_off[b + 1] - seq.split_off[b]);
     ma.nsp = max_ns > 8 ? 4 : 1;
     const dim3 gz((g.rv_ld + 256 / ma.nsp - 1) / (256 / ma.nsp), (g.M_q + 3) / 4, g.B);
     e = launch_k(ps, k_zmerge, gz, dim3(256), s, ma);
@@ -2078,10 +2208,8 @@ static hipError_t launch_decode_tail(const Layer& L, const DecodePlan& plan, con
   }
   {
     ProfScope ps("decode_upproj");
-    const int Rg = g.B * g.G * g.n_q;
     const dim3 gm(g.H_kv * (g.d_h / 16), (Rg + 15) / 16);
-    const bool vec = (g.r_v & 7) == 0;
-    if (L.dtype == STARKV_BF16 && vec && Rg >= 64)
+    if (tall)
       e = launch_k(ps, k_upproj_tall, dim3(g.H_kv, (Rg + 63) / 64), dim3(256), s, ma);
     else if (L.dtype == STARKV_F32)
       e = vec ? launch_k(ps, k_upproj<STARKV_F32, true>, gm, dim3(256), s, ma)
