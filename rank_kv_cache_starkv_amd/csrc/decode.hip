@@ -107,7 +107,8 @@ int plan_decode(const Layer& L, int B, int n_q, const int32_t* lens, int T_max, 
   DecodeWs& w = P->ws;
   // one-M-tile value kernel: slices of up to nbw8 one-N-tile blocks and nbw4 int4 blocks
   {
-    const int v8 = env_int("STARKV_NBW8", 2), v4 = env_int("STARKV_NBW4", 2);
+    // int8 blocks are half the bytes of bf16 ones: bigger slices (measured on MI355X)
+    const int v8 = env_int("STARKV_NBW8", L.mix() ? 4 : 2), v4 = env_int("STARKV_NBW4", 2);
     w.nbw8 = v8 >= 4 ? 4 : (v8 >= 2 ? 2 : 1);
     w.nbw4 = v4 >= 2 ? 2 : 1;
   }
@@ -136,6 +137,9 @@ int plan_decode(const Layer& L, int B, int n_q, const int32_t* lens, int T_max, 
   const int target_wg = env_int("STARKV_VALUE_WGS", 512);
   int cps = std::max(8, ceil_div(total_chunks, std::max(1, target_wg / n_slices)));
   cps = std::max(cps, ceil_div(max_chunks, kMaxSplitsPerSeq));
+  // at most 4 splits per sequence while that keeps >= 256 value workgroups: longer-lived
+  // workgroups, and the split merge then folds into the up-projection
+  if (B * 4 * n_slices >= 256) cps = std::max(cps, ceil_div(max_chunks, 4));
   const int cps_env = env_int("STARKV_CPS", 0);
   if (cps_env > 0) cps = std::max(cps_env, ceil_div(max_chunks, kMaxSplitsPerSeq));
   int total_splits = 0;
@@ -534,9 +538,9 @@ __global__ __launch_bounds__(256) void k_scores(ScoreArgs a) {
     }
     for (int j0 = 0; j0 < nkw; j0 += 2) {
       if (LAT == STARKV_LATENT_MIX84) {
-        i32x4 av[4][4];
+        i32x4 av[2][4];
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
+        for (int jj = 0; jj < 2; ++jj) {
           const int j = j0 + jj;
           const bool on = j < nkw;
           int P0 = 0;
@@ -554,7 +558,7 @@ __global__ __launch_bounds__(256) void k_scores(ScoreArgs a) {
           }
         }
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
+        for (int jj = 0; jj < 2; ++jj) {
           i32x4 fh = {0, 0, 0, 0}, fl = {0, 0, 0, 0};
 #pragma unroll
           for (int x = 0; x < KW; ++x)
@@ -611,7 +615,7 @@ __global__ __launch_bounds__(256) void k_scores(ScoreArgs a) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) acc[t] = f32x4{sp[t][0], sp[t][1], sp[t][2], sp[t][3]};
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
+        for (int jj = 0; jj < 2; ++jj) {
           const int j = j0 + jj;
           if (j >= nkw) continue;
           int P0 = 0;

@@ -328,3 +328,18 @@ def test_many_rows_per_kv_head():
     for b in run.oracle_seqs:
         ref = H.oracle_decode(run, q, b, mode="latent")
         H.check_output(w, got[b], ref, f"seq {b} len {int(run.lens[b])}")
+
+
+def test_fp32_many_key_tiles():
+    """fp32 latent with key ranks near d_h (396 key channels: 13 K-tiles in the one column tile,
+    so every score wave takes several K-tile groups) against the oracle."""
+    w = dataclasses.replace(I.WORKLOADS[0], d_h=128, d=512, key_ranks=(100, 90, 110, 96), r_v=128, B=2)
+    lens0 = [300, 77]
+    H.log(f"[f32 K-tiles] ranks={w.key_ranks} lens={lens0}")
+    run = H.make_layer(w, exact=True)
+    H.prefill(run, lens0, oracle_seqs=range(len(lens0)))
+    q = H.queries(run)
+    got = H.from_dev(H.decode(run, q))
+    for b in run.oracle_seqs:
+        ref = H.oracle_decode(run, q, b)
+        H.check_output(w, got[b], ref, f"seq {b} len {int(run.lens[b])}")
