@@ -119,16 +119,18 @@ typedef struct starkv_layer_info {
  *          zero-padded.
  *   bf16 / f32: the key latent in channel order (head 0's r_0 channels, head
  *          1's, ...), padded to a multiple of 16 bytes.
- * v_tiles [B][T_max/32][v_tile_rows][32 * elem]  value latent in tiles of 32
- *          tokens, each row holding one channel (or channel pair) for the 32
- *          tokens of the tile.
+ * v_tiles [B][v_tile_rows/32][T_max/32][32][32 * elem]  value latent in tiles
+ *          of 32 tokens, each tile row holding one channel (or channel pair)
+ *          for the 32 tokens of the tile.  Rows are grouped in blocks of 32:
+ *          block rb of tile t of sequence b is the contiguous 32 x 32 x elem
+ *          bytes at [b][rb][t], so one row block's tiles follow each other.
  *   mix84: rows [0, V8): int8 value channels 0, 1, ... (zero-padded rows);
  *          rows [V8, V8 + V4/2): int4 value channels two per row byte (the
  *          even-numbered one of the pair in the low nibble); elem = 1.
  *   bf16 / f32: row c = value channel c (rows padded to a multiple of 32),
  *          elem = 2 or 4.
  * T_max must be a multiple of 32.  Token t of sequence b lives at k_rows row
- * [b][t] and at tile [b][t/32], column t%32.  Bytes of tokens at or beyond a
+ * [b][t] and, for value tile row v, at v_tiles [b][v/32][t/32][v%32][t%32].  Bytes of tokens at or beyond a
  * sequence's length are never read for the result.
  */
 typedef struct starkv_cache {

@@ -988,7 +988,8 @@ __global__ __launch_bounds__(256) void k_values(ValueArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[mt][nt][v] = 0.f;
 
-  const uint8_t* vb = a.v_tiles + (size_t)b * (g.T_max / kTT) * g.v_tile_bytes + (size_t)(nb * 32 + r) * kTT * esz;
+  constexpr int blkb = 32 * kTT * esz;  // bytes of one 32-row block of a tile
+  const uint8_t* vb = a.v_tiles + vblock_off(b, nb, 0, g.v_rows, g.T_max, esz) + (size_t)r * kTT * esz;
   for (int c0 = c_lo; c0 < c_hi; c0 += U) {
     u32x4 vr[U][NV];
     u32x4 pr[U][NMT][2][NP];
@@ -999,7 +1000,7 @@ __global__ __launch_bounds__(256) void k_values(ValueArgs a) {
       const int c = c0 + u;
       const bool on = c < c_hi;  // uniform
       const size_t cgl = (size_t)(cbase + (on ? c : c_lo));
-      const uint8_t* trow = vb + (size_t)(on ? c : c_lo) * g.v_tile_bytes;
+      const uint8_t* trow = vb + (size_t)(on ? c : c_lo) * blkb;
 #pragma unroll
       for (int k = 0; k < NV; ++k) vr[u][k] = on ? ld16(trow + 16 * NV * q + 16 * k) : u32x4{0, 0, 0, 0};
 #pragma unroll
@@ -1133,10 +1134,9 @@ __global__ __launch_bounds__(256) void k_values(ValueArgs a) {
 // each covers every block of the slice, so a probability fragment feeds up to four N-tiles.
 // Slices [0, n_sl8) hold NBW8 blocks of one N-tile each (int8, bf16 or fp32 rows), slices
 // [n_sl8, ...) NBW4 int4 blocks (two N-tiles each: even and odd channels of the byte pairs).
-// Each wave double-buffers its tile loads in registers: the loads of the next U tiles are issued
-// before the MFMAs of the current U, and every load is unconditional (addresses of tiles past
-// the wave's last one are clamped to it; those tiles are loaded but never used).  The waves'
-// accumulators and probability sums are added through LDS at the end.
+// Each wave double-buffers its tile loads in registers (the loads of the next U tiles go out
+// before the MFMAs of the current U).  The waves' accumulators and probability sums are added
+// through LDS at the end.
 template <int LAT>
 struct VLayout {
   static constexpr int esz = LAT == STARKV_LATENT_F32 ? 4 : (LAT == STARKV_LATENT_BF16 ? 2 : 1);
@@ -1169,12 +1169,20 @@ __device__ __forceinline__ void values1_run(const ValueArgs& a, int slice, int s
   const int len = seq_len(a.seq, b);
   const bool rok = r < g.M_q;
   const size_t prow = (size_t)(rok ? r : 0);
-  // tiles of this wave: chunks c_lo + wave + 4k, k < ntw (wave-uniform)
+  // tiles of this wave: chunks c_lo + wave + 4k, k < ntw (wave-uniform), walked from k = rot on
+  // (cyclically): the slices of one split start on different tiles, so they do not all fetch the
+  // same probability tile at the same moment
   const int ntw = c_lo + wave < c_hi ? (c_hi - c_lo - wave + 3) / 4 : 0;
-  const uint8_t* vb = a.v_tiles + (size_t)b * (g.T_max / kTT) * g.v_tile_bytes + 16 * VL::NV * q;
-  int boff[NBW];
+  const int rot = ntw > 0 ? slice % ntw : 0;
+  auto chunk_of = [&](int k) {
+    const int kk = k + rot;
+    return c_lo + wave + 4 * (kk >= ntw ? kk - ntw : kk);
+  };
+  constexpr int blkb = 32 * kTT * VL::esz;  // bytes of one 32-row block of a tile
+  const uint8_t* vb = a.v_tiles + vblock_off(b, 0, 0, g.v_rows, g.T_max, VL::esz) + r * kTT * VL::esz + 16 * VL::NV * q;
+  size_t boff[NBW];
 #pragma unroll
-  for (int j = 0; j < NBW; ++j) boff[j] = ((nb0 + (j < nblk ? j : 0)) * 32 + r) * kTT * VL::esz;
+  for (int j = 0; j < NBW; ++j) boff[j] = vblock_off(0, nb0 + (j < nblk ? j : 0), 0, g.v_rows, g.T_max, VL::esz);
 
   f32x16 acc[NT];
 #pragma unroll
@@ -1185,8 +1193,8 @@ __device__ __forceinline__ void values1_run(const ValueArgs& a, int slice, int s
   float M = 0.f;  // the sequence's row maximum (read once the first tiles are in flight)
 
   auto load = [&](VTile<LAT, NBW>& t, int k) {
-    const int c = c_lo + wave + 4 * min(k, ntw - 1);
-    const uint8_t* tb = vb + (size_t)c * g.v_tile_bytes;
+    const int c = chunk_of(min(k, ntw - 1));
+    const uint8_t* tb = vb + (size_t)c * blkb;
 #pragma unroll
     for (int j = 0; j < NBW; ++j)
 #pragma unroll
@@ -1205,7 +1213,7 @@ __device__ __forceinline__ void values1_run(const ValueArgs& a, int slice, int s
 
   auto compute = [&](VTile<LAT, NBW>& t, int k) {
     if (k >= ntw) return;  // uniform
-    const int tt0 = (c_lo + wave + 4 * k) * kTC;
+    const int tt0 = chunk_of(k) * kTC;
     // rows past M_q read row 0's statistics; their results are never stored
     const float alpha = (t.cm == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(t.cm - M);
     lsum += alpha * t.cl;
@@ -1277,6 +1285,9 @@ __device__ __forceinline__ void values1_run(const ValueArgs& a, int slice, int s
   };
 
   if (ntw > 0) {
+    // two register buffers of U tiles each; a buffer's next loads go out before the other
+    // buffer's MFMAs.  Loads of tiles past the wave's last are clamped to it (L2 hits), except
+    // for the third batch of an iteration, which is skipped (a uniform branch) when no tile is left.
     VTile<LAT, NBW> ta[U], tb[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) load(ta[u], u);
@@ -1288,8 +1299,10 @@ __device__ __forceinline__ void values1_run(const ValueArgs& a, int slice, int s
 #pragma unroll
       for (int u = 0; u < U; ++u) compute(ta[u], k0 + u);
       if (k0 + U >= ntw) break;
+      if (k0 + 2 * U < ntw) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) load(ta[u], k0 + 2 * U + u);
+        for (int u = 0; u < U; ++u) load(ta[u], k0 + 2 * U + u);
+      }
 #pragma unroll
       for (int u = 0; u < U; ++u) compute(tb[u], k0 + U + u);
     }
@@ -1393,6 +1406,7 @@ __global__ __launch_bounds__(256) void k_values_mt(ValueArgs a) {
   const int n_nt = n_nt8 + (LAT == STARKV_LATENT_MIX84 ? 2 * (a.NB - a.V8 / 32) : 0);
   bool ntok[NTW], is4[NTW];
   int blk[NTW], par[NTW];
+  constexpr int blkb = 32 * kTT * esz;  // bytes of one 32-row block of a tile
   const uint8_t* vb[NTW];
 #pragma unroll
   for (int j = 0; j < NTW; ++j) {
@@ -1410,8 +1424,7 @@ __global__ __launch_bounds__(256) void k_values_mt(ValueArgs a) {
         is4[j] = true;
       }
     }
-    vb[j] = a.v_tiles + (size_t)b * (g.T_max / kTT) * g.v_tile_bytes + (size_t)(blk[j] * 32 + r) * kTT * esz +
-            16 * NV * q;
+    vb[j] = a.v_tiles + vblock_off(b, blk[j], 0, g.v_rows, g.T_max, esz) + (size_t)r * kTT * esz + 16 * NV * q;
   }
 
   // staging role: thread t < MP stages row t of every chunk
@@ -1473,7 +1486,7 @@ __global__ __launch_bounds__(256) void k_values_mt(ValueArgs a) {
 #pragma unroll
   for (int j = 0; j < NTW; ++j)
 #pragma unroll
-    for (int x = 0; x < NV; ++x) vcur[j][x] = ld16(vb[j] + (size_t)c_lo * g.v_tile_bytes + 16 * x);
+    for (int x = 0; x < NV; ++x) vcur[j][x] = ld16(vb[j] + (size_t)c_lo * blkb + 16 * x);
   __syncthreads();
   for (int c = c_lo; c < c_hi; ++c) {
     const int cur = (c - c_lo) & 1;
@@ -1483,7 +1496,7 @@ __global__ __launch_bounds__(256) void k_values_mt(ValueArgs a) {
 #pragma unroll
     for (int j = 0; j < NTW; ++j)
 #pragma unroll
-      for (int x = 0; x < NV; ++x) vn[j][x] = ld16(vb[j] + (size_t)cn * g.v_tile_bytes + 16 * x);
+      for (int x = 0; x < NV; ++x) vn[j][x] = ld16(vb[j] + (size_t)cn * blkb + 16 * x);
     // this chunk
     if (LAT == STARKV_LATENT_BF16 && c * kTC + kTT > len) {
       // zero the elements of tokens at or past the length (their bits may be anything)

@@ -90,10 +90,10 @@ __device__ __forceinline__ void store_latent(const GemmArgs& a, int slot, int ch
         else if ((slot & 1) == 0) row[a.K8 + (slot - a.K8) / 2] = (uint8_t)((code & 0xF) | ((partner & 0xF) << 4));
       } else {
         const int u = slot - a.key_slots;
-        uint8_t* tile = a.v_tiles + ((size_t)b * (a.T_max / kTT) + pos / kTT) * a.v_rows * kTT;
-        if (!nib) tile[(size_t)u * kTT + pos % kTT] = (uint8_t)(code & 0xFF);
-        else if ((u & 1) == 0)
-          tile[(size_t)(a.V8 + (u - a.V8) / 2) * kTT + pos % kTT] = (uint8_t)((code & 0xF) | ((partner & 0xF) << 4));
+        const int vr = nib ? a.V8 + (u - a.V8) / 2 : u;  // tile row: channel, or int4 channel pair
+        uint8_t* cell = a.v_tiles + vblock_off(b, vr >> 5, pos / kTT, a.v_rows, a.T_max, 1) + (vr & 31) * kTT + pos % kTT;
+        if (!nib) *cell = (uint8_t)(code & 0xFF);
+        else if ((u & 1) == 0) *cell = (uint8_t)((code & 0xF) | ((partner & 0xF) << 4));
       }
     }
     return;
@@ -112,9 +112,10 @@ __device__ __forceinline__ void store_latent(const GemmArgs& a, int slot, int ch
       else ((uint16_t*)row)[slot] = f32_to_bf16(x);
     } else {
       const int u = slot - a.key_slots;
-      uint8_t* tile = a.v_tiles + ((size_t)b * (a.T_max / kTT) + pos / kTT) * a.v_rows * kTT * (a.latent == STARKV_LATENT_F32 ? 4 : 2);
-      if (a.latent == STARKV_LATENT_F32) ((float*)tile)[(size_t)u * kTT + pos % kTT] = x;
-      else ((uint16_t*)tile)[(size_t)u * kTT + pos % kTT] = f32_to_bf16(x);
+      const int esz = a.latent == STARKV_LATENT_F32 ? 4 : 2;
+      uint8_t* blk = a.v_tiles + vblock_off(b, u >> 5, pos / kTT, a.v_rows, a.T_max, esz);
+      if (a.latent == STARKV_LATENT_F32) ((float*)blk)[(u & 31) * kTT + pos % kTT] = x;
+      else ((uint16_t*)blk)[(u & 31) * kTT + pos % kTT] = f32_to_bf16(x);
     }
   }
 }

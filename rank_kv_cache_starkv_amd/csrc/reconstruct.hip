@@ -33,10 +33,12 @@ __global__ __launch_bounds__(256) void k_reconstruct(ReconArgs a) {
   extern __shared__ float xs[];  // [n_key + r_v]
   const int t = a.t0 + blockIdx.x;
   const uint8_t* row = a.k_rows + ((size_t)a.b * a.T_max + t) * a.k_row_bytes;
-  const int ntile = a.T_max / kTT;
   const int esz = a.latent == STARKV_LATENT_F32 ? 4 : (a.latent == STARKV_LATENT_BF16 ? 2 : 1);
-  const uint8_t* tile = a.v_tiles + ((size_t)a.b * ntile + t / kTT) * (size_t)a.v_rows * kTT * esz;
   const int col = t % kTT;
+  // this token's element of value-tile row vr
+  auto vcell = [&](int vr) {
+    return a.v_tiles + vblock_off(a.b, vr >> 5, t / kTT, a.v_rows, a.T_max, esz) + (size_t)((vr & 31) * kTT + col) * esz;
+  };
   // dequantised latent of this token into LDS
   for (int c = threadIdx.x; c < a.n_key + a.r_v; c += blockDim.x) {
     float x;
@@ -54,18 +56,18 @@ __global__ __launch_bounds__(256) void k_reconstruct(ReconArgs a) {
       } else {
         const int k = c - a.n_key;
         if (k < a.n8v) {
-          code = (int)(int8_t)tile[(size_t)k * kTT + col];
+          code = (int)(int8_t)*vcell(k);
         } else {
           const int w = k - a.n8v;
-          code = snib(tile[(size_t)(a.V8 + w / 2) * kTT + col], w & 1);
+          code = snib(*vcell(a.V8 + w / 2), w & 1);
         }
       }
       x = (float)code * f16_to_f32(a.scales[c]);
     } else if (a.latent == STARKV_LATENT_F32) {
-      x = (c < a.n_key) ? ((const float*)row)[c] : ((const float*)tile)[(size_t)(c - a.n_key) * kTT + col];
+      x = (c < a.n_key) ? ((const float*)row)[c] : *(const float*)vcell(c - a.n_key);
     } else {
       x = (c < a.n_key) ? bf16_to_f32(((const uint16_t*)row)[c])
-                        : bf16_to_f32(((const uint16_t*)tile)[(size_t)(c - a.n_key) * kTT + col]);
+                        : bf16_to_f32(*(const uint16_t*)vcell(c - a.n_key));
     }
     xs[c] = x;
   }

@@ -18,6 +18,14 @@ constexpr int kMaxKT = 32;                     // K-tiles per column tile
 constexpr int kMaxSplitsPerSeq = 64;
 constexpr int kMaxSlots = 64;  // running-maximum slots per (sequence, query row), at most
 
+// Value cache [B][v_rows/32 row blocks][T_max/32 token tiles][32 rows][32 tokens x esz]: byte
+// offset of row block rb of token tile `tile` of sequence b.  A block (32 rows x 32 tokens) is
+// contiguous, and the tiles of one row block follow each other, so a reader that owns a few row
+// blocks of a range of tiles streams contiguous memory.
+__host__ __device__ __forceinline__ size_t vblock_off(int b, int rb, int tile, int v_rows, int T_max, int esz) {
+  return (((size_t)b * (v_rows / 32) + rb) * (size_t)(T_max / kTT) + tile) * (size_t)(32 * kTT * esz);
+}
+
 // Per-KV-head tables on the device (int32 each, H_kv entries unless noted).
 struct HeadTables {
   const int* koff;   // [H_kv + 1] first natural key channel of head g

@@ -163,7 +163,9 @@ def gpu_seq_cache(run: Run, b: int):
     vb = run.cache.v_tiles.numel() // run.cache.B
     k = run.cache.k_rows[b * kb:(b + 1) * kb].view(run.cache.T_max, fmt.k_row_bytes)[:T].cpu().numpy()
     nt = -(-T // O.TT)
-    v = run.cache.v_tiles[b * vb:(b + 1) * vb].view(run.cache.T_max // O.TT, fmt.v_rows, O.TT * fmt.elem)[:nt]
+    # the cache stores [v_rows/32 row blocks][T_max/32 tiles][32 rows][32 tokens]: regroup as tiles
+    v = run.cache.v_tiles[b * vb:(b + 1) * vb].view(fmt.v_rows // 32, run.cache.T_max // O.TT, 32, O.TT * fmt.elem)
+    v = v[:, :nt].permute(1, 0, 2, 3).reshape(nt, fmt.v_rows, O.TT * fmt.elem)
     return k, v.cpu().numpy()
 
 
