@@ -1594,6 +1594,7 @@ struct MergeArgs {
 // sequence; nsp adjacent lanes (1 or 4) share 4 channels and take every nsp-th split each, all
 // their loads issued at once (16 splits per batch), and add their partial sums by lane exchange
 // in a fixed order, so the result is deterministic.
+template <bool MIX>
 __global__ __launch_bounds__(256) void k_zmerge(MergeArgs a) {
   const DecodeGeom& g = a.g;
   const int nsp = a.nsp;
@@ -1608,6 +1609,12 @@ __global__ __launch_bounds__(256) void k_zmerge(MergeArgs a) {
   const float* zc = a.zp + ((size_t)s0 * g.M_pad + ic) * g.rv_ld + cc;
   const float* lc = a.sl + (size_t)s0 * g.M_pad + ic;
   const size_t zs = (size_t)g.M_pad * g.rv_ld;
+  // int8/int4 value scales of this lane's 4 channels, issued with the first partials
+  uint16_t scv[4] = {0, 0, 0, 0};
+  if (MIX) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) scv[e] = a.vscales[min(cc + e, g.r_v - 1)];
+  }
   float z[4] = {0.f, 0.f, 0.f, 0.f};
   float l = 0.f;
   for (int s = sp; s < ns; s += 16 * nsp) {
@@ -1619,6 +1626,7 @@ __global__ __launch_bounds__(256) void k_zmerge(MergeArgs a) {
       v[u] = ld16(zc + (size_t)ss * zs);
       lv[u] = lc[(size_t)ss * g.M_pad];
     }
+    __builtin_amdgcn_sched_barrier(0);  // all 32 loads go out before the first add
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       if (s + u * nsp < ns) {
@@ -1640,7 +1648,7 @@ __global__ __launch_bounds__(256) void k_zmerge(MergeArgs a) {
   for (int e = 0; e < 4; ++e) {
     const int ce = c + e;
     float sc = il;
-    if (a.vscales) sc *= f16_to_f32(a.vscales[min(ce, g.r_v - 1)]);
+    if (MIX) sc *= f16_to_f32(scv[e]);
     o[e] = __float_as_uint(ce < g.r_v ? z[e] * sc : 0.f);
   }
   st16(a.zt + ((size_t)b * g.M_pad + i) * g.rv_ld + c, o);
@@ -1855,13 +1863,18 @@ __global__ __launch_bounds__(256) void k_upproj(MergeArgs a) {
 // rv_ld in 32-channel chunks.  A lane sums its row's split partials for its 8 channels (in split
 // order), scales them by scale_c / sum_s l_s -- the merged latent z~ of k_zmerge, bit for bit --
 // and feeds the MFMA as k_upproj does.  Padding channels (>= r_v) are zeroed; loads unconditional.
-template <int DT>
+template <int DT, bool MIX>
 __global__ __launch_bounds__(512) void k_upproj_merge(MergeArgs a) {
   constexpr int NSM = 4;  // splits per sequence, at most
   constexpr int KU = 4;   // 32-channel chunks per wave
   const DecodeGeom& g = a.g;
   const int nsl_n = g.d_h / 16;
-  const int gk = blockIdx.x / nsl_n, nsl = blockIdx.x % nsl_n;
+  // workgroups go to the eight XCDs in turn (id mod 8): every column slice of KV head gk runs on
+  // XCD gk mod 8, so the head's split partials are fetched into one L2 only
+  const int k = blockIdx.x >> 3;
+  const int nsl = k % nsl_n;
+  const int gk = 8 * (k / nsl_n) + (blockIdx.x & 7);
+  if (gk >= g.H_kv) return;
   const int rph = g.G * g.n_q;
   const int Rg = g.B * rph;
   const int lane = threadIdx.x & 63, wave = wave_id();
@@ -1904,7 +1917,7 @@ __global__ __launch_bounds__(512) void k_upproj_merge(MergeArgs a) {
     } else {
       bw[u][0] = ld16((const uint16_t*)a.B_vt + (size_t)col * g.r_v + cc);
     }
-    sc[u] = a.vscales ? ld16(a.vscales + cc) : u32x4{0, 0, 0, 0};
+    sc[u] = MIX ? ld16(a.vscales + cc) : u32x4{0, 0, 0, 0};
   }
   __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the arithmetic
   f32x4 acc = {0, 0, 0, 0};
@@ -1919,7 +1932,7 @@ __global__ __launch_bounds__(512) void k_upproj_merge(MergeArgs a) {
 #pragma unroll
       for (int sx = 0; sx < NSM; ++sx) t += sx < ns ? __uint_as_float(z[u][sx][e >> 2][e & 3]) : 0.f;
       float scl = il;
-      if (a.vscales) scl *= f16_to_f32((uint16_t)(e & 1 ? sc[u][e >> 1] >> 16 : sc[u][e >> 1] & 0xFFFF));
+      if (MIX) scl *= f16_to_f32((uint16_t)(e & 1 ? sc[u][e >> 1] >> 16 : sc[u][e >> 1] & 0xFFFF));
       zz[e] = (live && c + e < g.r_v) ? t * scl : 0.f;
     }
     if (DT == STARKV_F32) {
@@ -2210,9 +2223,13 @@ static hipError_t launch_decode_tail(const Layer& L, const DecodePlan& plan, con
   if (max_ns <= 4 && vec && g.rv_ld <= 32 * 32 && !tall) {
     // one launch: the merge is folded into the up-projection
     ProfScope ps("decode_upproj");
-    const dim3 gm(g.H_kv * (g.d_h / 16), (Rg + 15) / 16);
-    e = L.dtype == STARKV_F32 ? launch_k(ps, k_upproj_merge<STARKV_F32>, gm, dim3(512), s, ma)
-                              : launch_k(ps, k_upproj_merge<STARKV_BF16>, gm, dim3(512), s, ma);
+    const dim3 gm((g.H_kv + 7) / 8 * 8 * (g.d_h / 16), (Rg + 15) / 16);
+    if (L.dtype == STARKV_F32)
+      e = L.mix() ? launch_k(ps, k_upproj_merge<STARKV_F32, true>, gm, dim3(512), s, ma)
+                  : launch_k(ps, k_upproj_merge<STARKV_F32, false>, gm, dim3(512), s, ma);
+    else
+      e = L.mix() ? launch_k(ps, k_upproj_merge<STARKV_BF16, true>, gm, dim3(512), s, ma)
+                  : launch_k(ps, k_upproj_merge<STARKV_BF16, false>, gm, dim3(512), s, ma);
     if (e != hipSuccess) return e;
     return hipGetLastError();
   }
@@ -2220,7 +2237,7 @@ static hipError_t launch_decode_tail(const Layer& L, const DecodePlan& plan, con
     ProfScope ps("decode_zmerge");
     ma.nsp = max_ns > 8 ? 4 : 1;
     const dim3 gz((g.rv_ld + 256 / ma.nsp - 1) / (256 / ma.nsp), (g.M_q + 3) / 4, g.B);
-    e = launch_k(ps, k_zmerge, gz, dim3(256), s, ma);
+    e = L.mix() ? launch_k(ps, k_zmerge<true>, gz, dim3(256), s, ma) : launch_k(ps, k_zmerge<false>, gz, dim3(256), s, ma);
     if (e != hipSuccess) return e;
   }
   {
