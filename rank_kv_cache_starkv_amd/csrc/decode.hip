@@ -131,8 +131,6 @@ int plan_decode(const Layer& L, int B, int n_q, const int32_t* lens, int T_max, 
     total_chunks += nc;
     max_chunks = std::max(max_chunks, nc);
   }
-  // running-maximum slots: at most 16 chunks' atomics per slot
-  g.nslots = max_chunks > 256 ? kMaxSlots : 16;
   // splits: aim at ~512 value workgroups (two per CU), at least 8 tiles (two per wave) per split
   const int target_wg = env_int("STARKV_VALUE_WGS", 512);
   int cps = std::max(8, ceil_div(total_chunks, std::max(1, target_wg / n_slices)));
@@ -165,9 +163,9 @@ int plan_decode(const Layer& L, int B, int n_q, const int32_t* lens, int T_max, 
   const size_t o_p = o; o = align256(o + (size_t)total_chunks * g.M_pad * kTC * esz_p);
   const size_t o_cm = o; o = align256(o + (size_t)total_chunks * g.M_pad * 4);
   const size_t o_cl = o; o = align256(o + (size_t)total_chunks * g.M_pad * 4);
-  const size_t o_gmax = o; o = align256(o + (size_t)B * g.M_pad * g.nslots * 4);
   const size_t o_zp = o; o = align256(o + (size_t)total_splits * g.M_pad * g.rv_ld * 4);
   const size_t o_sl = o; o = align256(o + (size_t)total_splits * g.M_pad * 4);
+  const size_t o_sm = o; o = align256(o + (size_t)total_splits * g.M_pad * 4);
   const size_t o_zt = o; o = align256(o + (size_t)B * g.M_pad * g.rv_ld * 4);
   P->ws_bytes = o;
   uint8_t* base = (uint8_t*)ws_base;
@@ -176,9 +174,9 @@ int plan_decode(const Layer& L, int B, int n_q, const int32_t* lens, int T_max, 
   w.p = base + o_p;
   w.cm = (float*)(base + o_cm);
   w.cl = (float*)(base + o_cl);
-  w.gmax = (int*)(base + o_gmax);
   w.zp = (float*)(base + o_zp);
   w.sl = (float*)(base + o_sl);
+  w.sm = (float*)(base + o_sm);
   w.zt = (float*)(base + o_zt);
   w.nkt_max = nkt_max;
   w.total_chunks = total_chunks;
@@ -198,7 +196,6 @@ struct QprojArgs {
   HeadTables heads;
   uint8_t* qfrag;
   float* rowp;
-  int* gmax;
   DecodeGeom g;
   int nkt_max;
   KtList kts;
@@ -246,11 +243,6 @@ __device__ __forceinline__ void qproj_body(const QprojArgs& a, int gk, int b, in
   const int n8g = (LAT == STARKV_LATENT_MIX84) ? a.heads.n8[gk] : 0;
   const int o8 = (LAT == STARKV_LATENT_MIX84) ? a.heads.off8[gk] : 0;
   const int o4 = (LAT == STARKV_LATENT_MIX84) ? a.heads.off4[gk] : 0;
-
-  // the running-maximum slots of these rows start at -inf (the key-score kernel raises them)
-  for (int idx = tid; idx < (r_hi - r_lo) * g.nslots; idx += NT)
-    a.gmax[((size_t)b * g.M_pad + gk * rph + r_lo + idx / g.nslots) * g.nslots + idx % g.nslots] =
-        ord_key(-INFINITY);
 
   for (int rb0 = r_lo; rb0 < r_hi; rb0 += RB) {
     const int nrows = min(RB, r_hi - rb0);
@@ -461,7 +453,6 @@ struct ScoreArgs {
   void* p;
   float* cm;
   float* cl;
-  int* gmax;
   DecodeGeom g;
   int nkt_max;
   int nch_wg;        // 64-token chunks per workgroup
@@ -712,7 +703,6 @@ __global__ __launch_bounds__(256) void k_scores(ScoreArgs a) {
   if (qq == 0) {
     a.cm[(size_t)cg * g.M_pad + i] = m;
     a.cl[(size_t)cg * g.M_pad + i] = l;
-    if (rowvalid) atomicMax(a.gmax + ((size_t)b * g.M_pad + i) * g.nslots + cidx % g.nslots, ord_key(m));
   }
 }
 
@@ -890,8 +880,6 @@ __global__ __launch_bounds__(256) void k_scores_chunk(ScoreArgs a) {
     if (qq == 0) {
       a.cm[(size_t)cg * g.M_pad + i] = m;
       a.cl[(size_t)cg * g.M_pad + i] = l;
-      if (rowvalid)
-        atomicMax(a.gmax + ((size_t)b * g.M_pad + i) * g.nslots + (t0 / kTC) % g.nslots, ord_key(m));
     }
   }
 }
@@ -904,9 +892,9 @@ struct ValueArgs {
   const void* p;
   const float* cm;
   const float* cl;
-  const int* gmax;
   float* zp;
   float* sl;
+  float* sm;
   DecodeGeom g;
   SeqTable seq;
   int cps, bpw, NB, V8, n8v, n4v;
@@ -914,17 +902,25 @@ struct ValueArgs {
   int n_sl, n_splits;  // one-M-tile kernel: slices per split, splits in all
 };
 
-// Row maximum of the base-2 logits of query row `row` (index into [B][M_pad]) over its nslots
-// (16 or 64) slots: sixteen 16-byte loads issued at once (with 16 slots the last four repeat).
-__device__ __forceinline__ float row_max(const int* gmax, size_t row, int nslots) {
-  const int* p = gmax + row * nslots;
-  u32x4 v[kMaxSlots / 4];
+// Largest of the chunk maxima cm[c][row] over chunks c = c0, c0 + step, ... (n >= 1 of them),
+// NL loads at a time: the reference against which a value kernel weights its tiles.
+template <int NL = 8>
+__device__ __forceinline__ float chunks_max(const float* cm, int c0, int step, int n, int M_pad, size_t row) {
+  float m = -INFINITY;
+  for (int k0 = 0; k0 < n; k0 += NL) {
+    float v[NL];
 #pragma unroll
-  for (int k = 0; k < kMaxSlots / 4; ++k) v[k] = ld16(p + 4 * min(k, nslots / 4 - 1));
-  int m = ord_key(-INFINITY);
+    for (int u = 0; u < NL; ++u) v[u] = cm[(size_t)(c0 + step * min(k0 + u, n - 1)) * M_pad + row];
 #pragma unroll
-  for (int k = 0; k < kMaxSlots / 4; ++k) m = max(m, max(max((int)v[k][0], (int)v[k][1]), max((int)v[k][2], (int)v[k][3])));
-  return ord_val(m);
+    for (int u = 0; u < NL; ++u) m = fmaxf(m, v[u]);
+  }
+  return m;
+}
+
+// Weight 2^(m - ref) of a partial whose maximum is m, against the reference ref >= m (0 for an
+// empty partial, m = -inf).
+__device__ __forceinline__ float rel_weight(float m, float ref) {
+  return m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - ref);
 }
 
 // 8 tokens of one channel (int8 codes in 8 bytes) -> f16x8
@@ -971,12 +967,13 @@ __global__ __launch_bounds__(256) void k_values(ValueArgs a) {
   const int r = lane & 31, q = lane >> 5;
   const bool is4 = (LAT == STARKV_LATENT_MIX84) && (nb >= a.V8 / 32);
 
-  // row maximum (over the whole sequence) of the rows this lane feeds as A-fragment rows
+  // maximum over the split's chunks of the rows this lane feeds as A-fragment rows: the
+  // reference of this split's weights
   float Ms[NMT], lsum[NMT];
 #pragma unroll
   for (int mt = 0; mt < NMT; ++mt) {
     const int row = min(mt * 32 + r, g.M_q - 1);
-    Ms[mt] = row_max(a.gmax, (size_t)b * g.M_pad + row, g.nslots);
+    Ms[mt] = chunks_max(a.cm, cbase + c_lo, 1, c_hi - c_lo, g.M_pad, row);
     lsum[mt] = 0.f;
   }
 
@@ -1124,7 +1121,10 @@ __global__ __launch_bounds__(256) void k_values(ValueArgs a) {
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) {
       const int row = mt * 32 + r;
-      if (row < g.M_q) a.sl[(size_t)sg * g.M_pad + row] = lsum[mt];
+      if (row < g.M_q) {
+        a.sl[(size_t)sg * g.M_pad + row] = lsum[mt];
+        a.sm[(size_t)sg * g.M_pad + row] = Ms[mt];
+      }
     }
   }
 }
@@ -1153,7 +1153,7 @@ struct VTile {
 
 template <int LAT, int NBW, bool IS4>
 __device__ __forceinline__ void values1_run(const ValueArgs& a, int slice, int sg, int nb0, int nblk,
-                                            float* sred, float (*ssum)[32]) {
+                                            float* sred, float (*ssum)[32], float (*smx)[32]) {
   using VL = VLayout<LAT>;
   constexpr int NT = IS4 ? 2 * NBW : NBW;  // accumulator tiles
   constexpr int TU = NBW * VL::NV + 2 * VL::NP;  // 16-byte loads per lane per tile
@@ -1190,7 +1190,7 @@ __device__ __forceinline__ void values1_run(const ValueArgs& a, int slice, int s
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[t][v] = 0.f;
   float lsum = 0.f;
-  float M = 0.f;  // the sequence's row maximum (read once the first tiles are in flight)
+  float M = -INFINITY;  // this wave's reference: the largest chunk maximum of its tiles (its row)
 
   auto load = [&](VTile<LAT, NBW>& t, int k) {
     const int c = chunk_of(min(k, ntw - 1));
@@ -1285,17 +1285,25 @@ __device__ __forceinline__ void values1_run(const ValueArgs& a, int slice, int s
   };
 
   if (ntw > 0) {
-    // two register buffers of U tiles each; a buffer's next loads go out before the other
-    // buffer's MFMAs.  Loads of tiles past the wave's last are clamped to it (L2 hits), except
-    // for the third batch of an iteration, which is skipped (a uniform branch) when no tile is left.
+    // the chunk maxima of the wave's first 8 tiles go out first, then two register buffers of U
+    // tiles each; a buffer's next loads go out before the other buffer's MFMAs.  Loads of tiles
+    // past the wave's last are clamped to it (L2 hits), except for the refills, which are skipped
+    // (uniform branches) when no tile is left.
+    float cmx[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      cmx[u] = a.cm[(size_t)(cbase + c_lo + wave + 4 * min(u, ntw - 1)) * g.M_pad + prow];
+    __builtin_amdgcn_sched_barrier(0);
     VTile<LAT, NBW> ta[U], tb[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) load(ta[u], u);
-    // the sequence's row maximum, read while the first tiles are in flight
-    M = row_max(a.gmax, (size_t)b * g.M_pad + prow, g.nslots);
-    for (int k0 = 0; k0 < ntw; k0 += 2 * U) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) load(tb[u], k0 + U + u);
+    for (int u = 0; u < U; ++u) load(tb[u], U + u);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) M = fmaxf(M, cmx[u]);
+    if (ntw > 8) M = fmaxf(M, chunks_max(a.cm, cbase + c_lo + wave + 32, 4, ntw - 8, g.M_pad, prow));
+    for (int k0 = 0; k0 < ntw; k0 += 2 * U) {
 #pragma unroll
       for (int u = 0; u < U; ++u) compute(ta[u], k0 + u);
       if (k0 + U >= ntw) break;
@@ -1305,10 +1313,15 @@ __device__ __forceinline__ void values1_run(const ValueArgs& a, int slice, int s
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) compute(tb[u], k0 + U + u);
+      if (k0 + 3 * U < ntw) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) load(tb[u], k0 + 3 * U + u);
+      }
     }
   }
 
-  // add the four waves' accumulators and sums: every wave parks its accumulators in LDS, then
+  // add the four waves' accumulators and sums, each weighted against the split's maximum of the
+  // row (the largest of the waves' references): every wave parks its accumulators in LDS, then
   // wave w adds and stores elements v = 4w .. 4w + 3 of every tile
   const int ntile = IS4 ? 2 * nblk : nblk;
 #pragma unroll
@@ -1317,8 +1330,20 @@ __device__ __forceinline__ void values1_run(const ValueArgs& a, int slice, int s
 #pragma unroll
     for (int v = 0; v < 16; ++v) sred[((wave * NT + t) * 16 + v) * 64 + lane] = acc[t][v];
   }
-  if (q == 0) ssum[wave][r] = lsum;
+  if (q == 0) {
+    ssum[wave][r] = lsum;
+    smx[wave][r] = M;
+  }
   __syncthreads();
+  // weights of the four waves for the rows of elements 4w .. 4w + 3
+  float fw[4][4];
+#pragma unroll
+  for (int vv = 0; vv < 4; ++vv) {
+    const int row = d32_row(4 * wave + vv, q);
+    const float ms = fmaxf(fmaxf(smx[0][row], smx[1][row]), fmaxf(smx[2][row], smx[3][row]));
+#pragma unroll
+    for (int w = 0; w < 4; ++w) fw[vv][w] = rel_weight(smx[w][row], ms);
+  }
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     if (t >= ntile) continue;
@@ -1337,13 +1362,19 @@ __device__ __forceinline__ void values1_run(const ValueArgs& a, int slice, int s
       const int v = 4 * wave + vv;
       float z = 0.f;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) z += sred[((w * NT + t) * 16 + v) * 64 + lane];
+      for (int w = 0; w < 4; ++w) z += fw[vv][w] * sred[((w * NT + t) * 16 + v) * 64 + lane];
       const int row = d32_row(v, q);
       if (cok && row < g.M_q) a.zp[((size_t)sg * g.M_pad + row) * g.rv_ld + vc] = z;
     }
   }
-  if (slice == 0 && wave == 0 && q == 0 && rok)
-    a.sl[(size_t)sg * g.M_pad + r] = ssum[0][r] + ssum[1][r] + ssum[2][r] + ssum[3][r];
+  if (slice == 0 && wave == 0 && q == 0 && rok) {
+    const float ms = fmaxf(fmaxf(smx[0][r], smx[1][r]), fmaxf(smx[2][r], smx[3][r]));
+    float l = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) l += rel_weight(smx[w][r], ms) * ssum[w][r];
+    a.sl[(size_t)sg * g.M_pad + r] = l;
+    a.sm[(size_t)sg * g.M_pad + r] = ms;
+  }
 }
 
 // Grid: one dimension of n_sl x (n_splits rounded up to 8) workgroups.  Workgroups are handed to
@@ -1356,17 +1387,18 @@ __global__ __launch_bounds__(256) void k_values1(ValueArgs a) {
   // most two workgroups share a CU, so the 2-per-CU grids spread evenly over the CUs
   __shared__ float sred[4 * 4 * 16 * 64];
   __shared__ float ssum[4][32];
+  __shared__ float smx[4][32];
   const int xcd = blockIdx.x & 7, k = blockIdx.x >> 3;
   const int slice = k % a.n_sl;
   const int sg = 8 * (k / a.n_sl) + xcd;
   if (sg >= a.n_splits) return;
   if (LAT == STARKV_LATENT_MIX84 && slice >= a.n_sl8) {
     const int nb0 = a.V8 / 32 + (slice - a.n_sl8) * NBW4;
-    values1_run<LAT, NBW4, true>(a, slice, sg, nb0, min(NBW4, a.NB - nb0), sred, ssum);
+    values1_run<LAT, NBW4, true>(a, slice, sg, nb0, min(NBW4, a.NB - nb0), sred, ssum, smx);
   } else {
     const int nb0 = slice * NBW8;
     const int nbe = LAT == STARKV_LATENT_MIX84 ? a.V8 / 32 : a.NB;
-    values1_run<LAT, NBW8, false>(a, slice, sg, nb0, min(NBW8, nbe - nb0), sred, ssum);
+    values1_run<LAT, NBW8, false>(a, slice, sg, nb0, min(NBW8, nbe - nb0), sred, ssum, smx);
   }
 }
 
@@ -1432,7 +1464,7 @@ __global__ __launch_bounds__(256) void k_values_mt(ValueArgs a) {
   const int srow = min(tid, MP - 1);
   const bool sval = tid < g.M_q;
   const size_t srow_g = (size_t)min(srow, g.M_q - 1);
-  const float Ms = row_max(a.gmax, (size_t)b * g.M_pad + srow_g, g.nslots);
+  float Ms = 0.f;  // the stager's reference: the largest chunk maximum of its row over the split
   float lsum = 0.f;
 
   struct Stage {
@@ -1479,14 +1511,16 @@ __global__ __launch_bounds__(256) void k_values_mt(ValueArgs a) {
 
   Stage sn;
   u32x4 vcur[NTW][NV], vn[NTW][NV];
-  if (stager) {
-    sload(sn, c_lo);
-    sstore(sn, 0);
-  }
+  // the first chunk's loads go out before the stager reads its row's chunk maxima
+  if (stager) sload(sn, c_lo);
 #pragma unroll
   for (int j = 0; j < NTW; ++j)
 #pragma unroll
     for (int x = 0; x < NV; ++x) vcur[j][x] = ld16(vb[j] + (size_t)c_lo * blkb + 16 * x);
+  if (stager) {
+    Ms = chunks_max<16>(a.cm, cbase + c_lo, 1, c_hi - c_lo, g.M_pad, srow_g);
+    sstore(sn, 0);
+  }
   __syncthreads();
   for (int c = c_lo; c < c_hi; ++c) {
     const int cur = (c - c_lo) & 1;
@@ -1570,7 +1604,10 @@ __global__ __launch_bounds__(256) void k_values_mt(ValueArgs a) {
         if (row < g.M_q) a.zp[((size_t)sg * g.M_pad + row) * g.rv_ld + vc] = acc[j][mt][v];
       }
   }
-  if (grp == 0 && sval) a.sl[(size_t)sg * g.M_pad + tid] = lsum;
+  if (grp == 0 && sval) {
+    a.sl[(size_t)sg * g.M_pad + tid] = lsum;
+    a.sm[(size_t)sg * g.M_pad + tid] = Ms;
+  }
 }
 
 // ===========================================================================
@@ -1579,6 +1616,7 @@ __global__ __launch_bounds__(256) void k_values_mt(ValueArgs a) {
 struct MergeArgs {
   const float* zp;
   const float* sl;
+  const float* sm;
   float* zt;                // [B][M_pad][rv_ld] merged, scaled, normalised value latent
   const void* B_vt;         // [H_kv * d_h][r_v]
   const uint16_t* vscales;  // [r_v] f16 (mix84) or null
@@ -1588,12 +1626,12 @@ struct MergeArgs {
   int nsp;  // split merge: lanes sharing 4 channels (1, or 4 for many splits)
 };
 
-// Split merge.  Every split of a sequence weighted its tiles against the same row maximum (the
-// whole sequence's), so the merge is a plain sum: z~[c] = (sum_s z_s[c]) * scale_c / (sum_s l_s),
-// and zero in the padding channels [r_v, rv_ld).  Workgroup = 4 rows x (256 / nsp) channels of one
-// sequence; nsp adjacent lanes (1 or 4) share 4 channels and take every nsp-th split each, all
-// their loads issued at once (16 splits per batch), and add their partial sums by lane exchange
-// in a fixed order, so the result is deterministic.
+// Split merge.  Split s weighted its tiles against its own maximum m_s of the row, so with M the
+// largest m_s: z~[c] = (sum_s 2^(m_s - M) z_s[c]) * scale_c / (sum_s 2^(m_s - M) l_s), and zero in
+// the padding channels [r_v, rv_ld).  Workgroup = 4 rows x (256 / nsp) channels of one sequence;
+// nsp adjacent lanes (1 or 4) share 4 channels and take every nsp-th split each, all their loads
+// issued at once (16 splits per batch), keep a running maximum (rescaling their sums when it
+// grows), and combine by lane exchange in a fixed order, so the result is deterministic.
 template <bool MIX>
 __global__ __launch_bounds__(256) void k_zmerge(MergeArgs a) {
   const DecodeGeom& g = a.g;
@@ -1608,6 +1646,7 @@ __global__ __launch_bounds__(256) void k_zmerge(MergeArgs a) {
   const int s0 = seq_split0(a.seq, b), ns = seq_nsplit(a.seq, b);
   const float* zc = a.zp + ((size_t)s0 * g.M_pad + ic) * g.rv_ld + cc;
   const float* lc = a.sl + (size_t)s0 * g.M_pad + ic;
+  const float* mc = a.sm + (size_t)s0 * g.M_pad + ic;
   const size_t zs = (size_t)g.M_pad * g.rv_ld;
   // int8/int4 value scales of this lane's 4 channels, issued with the first partials
   uint16_t scv[4] = {0, 0, 0, 0};
@@ -1617,29 +1656,45 @@ __global__ __launch_bounds__(256) void k_zmerge(MergeArgs a) {
   }
   float z[4] = {0.f, 0.f, 0.f, 0.f};
   float l = 0.f;
+  float M = -INFINITY;  // reference of z and l: the largest split maximum seen so far
   for (int s = sp; s < ns; s += 16 * nsp) {
     u32x4 v[16];
-    float lv[16];
+    float lv[16], mv[16];
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       const int ss = min(s + u * nsp, ns - 1);
       v[u] = ld16(zc + (size_t)ss * zs);
       lv[u] = lc[(size_t)ss * g.M_pad];
+      mv[u] = mc[(size_t)ss * g.M_pad];
     }
-    __builtin_amdgcn_sched_barrier(0);  // all 32 loads go out before the first add
+    __builtin_amdgcn_sched_barrier(0);  // all 48 loads go out before the first add
+    float Mn = M;
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (s + u * nsp < ns) Mn = fmaxf(Mn, mv[u]);
+    const float f0 = rel_weight(M, Mn);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) z[e] *= f0;
+    l *= f0;
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       if (s + u * nsp < ns) {
+        const float w = rel_weight(mv[u], Mn);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) z[e] += __uint_as_float(v[u][e]);
-        l += lv[u];
+        for (int e = 0; e < 4; ++e) z[e] += w * __uint_as_float(v[u][e]);
+        l += w * lv[u];
       }
     }
+    M = Mn;
   }
   for (int m = 1; m < nsp; m <<= 1) {
+    const float Mo = __shfl_xor(M, m, 64);
+    const float Mn = fmaxf(M, Mo);
+    const float fs = rel_weight(M, Mn), fo = rel_weight(Mo, Mn);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) z[e] += __shfl_xor(z[e], m, 64);
-    l += __shfl_xor(l, m, 64);
+    for (int e = 0; e < 4; ++e) z[e] = fs * z[e] + fo * __shfl_xor(z[e], m, 64);
+    l = fs * l + fo * __shfl_xor(l, m, 64);
+    M = Mn;
   }
   if (!live || sp != 0) return;
   const float il = 1.f / l;
@@ -1861,7 +1916,7 @@ __global__ __launch_bounds__(256) void k_upproj(MergeArgs a) {
 // Split merge folded into the up-projection (sequences of at most 4 splits): workgroup = (g,
 // 16-column slice of d_h, 16-row tile of g's rows over all sequences); its eight waves split K =
 // rv_ld in 32-channel chunks.  A lane sums its row's split partials for its 8 channels (in split
-// order), scales them by scale_c / sum_s l_s -- the merged latent z~ of k_zmerge, bit for bit --
+// order, weighted 2^(m_s - M) as in k_zmerge), scales them by scale_c / sum_s 2^(m_s - M) l_s,
 // and feeds the MFMA as k_upproj does.  Padding channels (>= r_v) are zeroed; loads unconditional.
 template <int DT, bool MIX>
 __global__ __launch_bounds__(512) void k_upproj_merge(MergeArgs a) {
@@ -1885,13 +1940,25 @@ __global__ __launch_bounds__(512) void k_upproj_merge(MergeArgs a) {
   const int ii = gk * rph + rr % rph;
   const int s0 = seq_split0(a.seq, bb), ns = seq_nsplit(a.seq, bb);
   const float* zs[NSM];
-  float l = 0.f;
+  float lv[NSM], mv[NSM];
 #pragma unroll
   for (int sx = 0; sx < NSM; ++sx) {
     const size_t sp = (size_t)(s0 + min(sx, ns - 1));
     zs[sx] = a.zp + (sp * g.M_pad + ii) * g.rv_ld + 8 * qq;
-    const float lv = a.sl[sp * g.M_pad + ii];
-    l += sx < ns ? lv : 0.f;
+    lv[sx] = a.sl[sp * g.M_pad + ii];
+    mv[sx] = a.sm[sp * g.M_pad + ii];
+  }
+  // split weights 2^(m_s - M) (zero for the padding splits past ns)
+  float M = -INFINITY;
+#pragma unroll
+  for (int sx = 0; sx < NSM; ++sx)
+    if (sx < ns) M = fmaxf(M, mv[sx]);
+  float wsx[NSM];
+  float l = 0.f;
+#pragma unroll
+  for (int sx = 0; sx < NSM; ++sx) {
+    wsx[sx] = sx < ns ? rel_weight(mv[sx], M) : 0.f;
+    l += wsx[sx] * lv[sx];
   }
   const float il = 1.f / l;
   const int col = gk * g.d_h + nsl * 16 + n;  // B_v^T row of this lane's output column
@@ -1930,7 +1997,7 @@ __global__ __launch_bounds__(512) void k_upproj_merge(MergeArgs a) {
     for (int e = 0; e < 8; ++e) {
       float t = 0.f;
 #pragma unroll
-      for (int sx = 0; sx < NSM; ++sx) t += sx < ns ? __uint_as_float(z[u][sx][e >> 2][e & 3]) : 0.f;
+      for (int sx = 0; sx < NSM; ++sx) t += wsx[sx] * __uint_as_float(z[u][sx][e >> 2][e & 3]);
       float scl = il;
       if (MIX) scl *= f16_to_f32((uint16_t)(e & 1 ? sc[u][e >> 1] >> 16 : sc[u][e >> 1] & 0xFFFF));
       zz[e] = (live && c + e < g.r_v) ? t * scl : 0.f;
@@ -2034,7 +2101,6 @@ static QprojArgs qproj_args(const Layer& L, const DecodePlan& plan, const KtList
   qa.heads = L.heads();
   qa.qfrag = (uint8_t*)plan.ws.qfrag;
   qa.rowp = plan.ws.rowp;
-  qa.gmax = plan.ws.gmax;
   qa.g = plan.g;
   qa.nkt_max = plan.ws.nkt_max;
   qa.kts = kts;
@@ -2139,7 +2205,6 @@ static hipError_t launch_decode_tail(const Layer& L, const DecodePlan& plan, con
   sa.p = w.p;
   sa.cm = w.cm;
   sa.cl = w.cl;
-  sa.gmax = w.gmax;
   sa.g = g;
   sa.nkt_max = w.nkt_max;
   sa.kts = kts;
@@ -2168,7 +2233,7 @@ static hipError_t launch_decode_tail(const Layer& L, const DecodePlan& plan, con
   va.p = w.p;
   va.cm = w.cm;
   va.cl = w.cl;
-  va.gmax = w.gmax;
+  va.sm = w.sm;
   va.zp = w.zp;
   va.sl = w.sl;
   va.g = g;
@@ -2209,6 +2274,7 @@ static hipError_t launch_decode_tail(const Layer& L, const DecodePlan& plan, con
   MergeArgs ma;
   ma.zp = w.zp;
   ma.sl = w.sl;
+  ma.sm = w.sm;
   ma.zt = w.zt;
   ma.B_vt = L.B_vt;
   ma.vscales = L.mix() ? L.scales + L.n_key : nullptr;

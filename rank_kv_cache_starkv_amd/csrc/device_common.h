@@ -30,16 +30,22 @@ __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane
 __device__ __forceinline__ float wave_max_xor(float v, int mask) { return fmaxf(v, __shfl_xor(v, mask, 64)); }
 __device__ __forceinline__ float wave_sum_xor(float v, int mask) { return v + __shfl_xor(v, mask, 64); }
 
-// ---- order-preserving float <-> int map: integer comparison of keys orders the floats, so an
-// integer atomicMax on keys takes a float maximum (-inf included; NaN never occurs here) ----
-__device__ __forceinline__ int ord_key(float x) {
-  const int i = __float_as_int(x);
-  return i >= 0 ? i : (i ^ 0x7FFFFFFF);
-}
-__device__ __forceinline__ float ord_val(int k) { return __int_as_float(k >= 0 ? k : (k ^ 0x7FFFFFFF)); }
-
 // ---- 16-byte loads/stores ----
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// ---- buffer loads ----
+// A buffer resource covering [base, base + bytes) (gfx9 raw layout: no stride, no swizzle).  A
+// load whose byte offset lies at or past `bytes` returns zeros and touches no memory, so a
+// kernel can issue its loads unconditionally and point the ones it does not need past the end,
+// with no branch around them (a branch around a load makes the compiler wait for every load in
+// flight where the paths join).  The base must be wave-uniform; bytes < 2^32.
+constexpr uint32_t kOOB = 0xFFFFFFF0u;  // an offset past the end of every buffer resource
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 __device__ __forceinline__ u32x2 ld8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
 __device__ __forceinline__ void st8(void* p, u32x2 v) { *reinterpret_cast<u32x2*>(p) = v; }

@@ -16,7 +16,6 @@ constexpr int kMaxB = STARKV_MAX_BATCH;
 constexpr int kMaxCT = STARKV_MAX_QROWS / 16;  // 16-row column tiles of the key-score GEMM
 constexpr int kMaxKT = 32;                     // K-tiles per column tile
 constexpr int kMaxSplitsPerSeq = 64;
-constexpr int kMaxSlots = 64;  // running-maximum slots per (sequence, query row), at most
 
 // Value cache [B][v_rows/32 row blocks][T_max/32 token tiles][32 rows][32 tokens x esz]: byte
 // offset of row block rb of token tile `tile` of sequence b.  A block (32 rows x 32 tokens) is
@@ -78,7 +77,6 @@ struct DecodeGeom {
   int B, n_q, M_q, M_pad, nct, G, d_h, H_q, H_kv;
   int n_key, r_v, K8, K4, key_kt, key_kpos, k_row_bytes, v_rows, v_tile_bytes, T_max;
   int rv_ld;  // row stride (elements) of the value-latent workspace rows: r_v rounded up to 32
-  int nslots; // running-maximum slots per row (16 or 64: few chunks share one slot's atomics)
   int latent, dtype;
   float qscale;  // log2(e) / sqrt(d_h)
 };
@@ -110,9 +108,9 @@ struct DecodeWs {
   void* p;          // [total_chunks][M_pad][kTC] probabilities (f16 / bf16 / f32)
   float* cm;        // [total_chunks][M_pad] chunk max (log2 units)
   float* cl;        // [total_chunks][M_pad] chunk sum
-  int* gmax;        // [B][M_pad][nslots] row maximum of the base-2 logits (ord_key), by slot
-  float* zp;        // [total_splits][M_pad][rv_ld] value-latent partials
-  float* sl;        // [total_splits][M_pad] split sum of the probabilities
+  float* zp;        // [total_splits][M_pad][rv_ld] value-latent partials, weighted against sm
+  float* sl;        // [total_splits][M_pad] split sum of the probabilities, weighted against sm
+  float* sm;        // [total_splits][M_pad] split maximum of the base-2 logits (the weights' reference)
   float* zt;        // [B][M_pad][rv_ld] merged value latent (scaled, normalised; zero padding)
   int nkt_max;
   int total_chunks, total_splits;
