@@ -34,6 +34,7 @@ __global__ __launch_bounds__(256) void k_latent_gemm(GemmArgs a) {
   const bool a_ok = arow < a.M;
   const int bslot = s0 + r;
   const int bchan = slot_channel(a, bslot);
+  const uint16_t sc_bits = (MODE == 0 && a.latent == STARKV_LATENT_MIX84) ? scale_bits(a, bchan) : (uint16_t)0;
   const bool b_ok = bchan >= 0;
   const size_t a_base = (size_t)(a_ok ? arow : 0) * a.d;
   const size_t b_base = (size_t)(b_ok ? bchan : 0) * a.d;
@@ -80,7 +81,7 @@ __global__ __launch_bounds__(256) void k_latent_gemm(GemmArgs a) {
   int ps[16];
 #pragma unroll
   for (int v = 0; v < 16; ++v) ps[v] = row_pos(a, ms[v]);
-  store_latent<16>(a, slot, chan, xs, ms, ps);
+  store_latent<16>(a, slot, chan, sc_bits, xs, ms, ps);
 }
 
 __global__ void k_fill_u32(uint32_t* p, int n, uint32_t v) {

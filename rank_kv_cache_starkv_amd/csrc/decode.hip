@@ -238,11 +238,11 @@ __device__ __forceinline__ void qproj_body(const QprojArgs& a, int gk, int b, in
   const int rph = g.G * g.n_q;
   const int rpg = (rph + nrg - 1) / nrg;  // rows of this workgroup
   const int r_lo = rg * rpg, r_hi = min(rph, r_lo + rpg);
-  const int c0 = a.heads.koff[gk];
-  const int r = a.heads.koff[gk + 1] - c0;
-  const int n8g = (LAT == STARKV_LATENT_MIX84) ? a.heads.n8[gk] : 0;
-  const int o8 = (LAT == STARKV_LATENT_MIX84) ? a.heads.off8[gk] : 0;
-  const int o4 = (LAT == STARKV_LATENT_MIX84) ? a.heads.off4[gk] : 0;
+  const int c0 = ld_uniform(a.heads.koff + gk);
+  const int r = ld_uniform(a.heads.koff + gk + 1) - c0;
+  const int n8g = (LAT == STARKV_LATENT_MIX84) ? ld_uniform(a.heads.n8 + gk) : 0;
+  const int o8 = (LAT == STARKV_LATENT_MIX84) ? ld_uniform(a.heads.off8 + gk) : 0;
+  const int o4 = (LAT == STARKV_LATENT_MIX84) ? ld_uniform(a.heads.off4 + gk) : 0;
 
   for (int rb0 = r_lo; rb0 < r_hi; rb0 += RB) {
     const int nrows = min(RB, r_hi - rb0);

@@ -32,6 +32,13 @@ __device__ __forceinline__ float wave_sum_xor(float v, int mask) { return v + __
 
 // ---- 16-byte loads/stores ----
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+// Load of read-only data at a wave-uniform address through the scalar data cache (the constant
+// address space): layer tables that no kernel writes.  Unlike a vector load it needs no VGPRs
+// and returns through the scalar cache.
+template <typename T>
+__device__ __forceinline__ T ld_uniform(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)p;
+}
 
 // ---- buffer loads ----
 // A buffer resource covering [base, base + bytes) (gfx9 raw layout: no stride, no swizzle).  A

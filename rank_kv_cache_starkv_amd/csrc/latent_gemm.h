@@ -14,7 +14,7 @@ namespace skv {
 struct GemmArgs {
   const void* X;        // [M][d]
   const void* A_t;      // [n_lat][d]
-  const int* slot_chan; // [NS]
+  const int* slot_chan; // [NS rounded up to 16]: natural channel of each column, -1 for padding
   int M, d, NS;
   int key_slots, K8, V8;
   int n_key, r_v;
@@ -60,15 +60,19 @@ __device__ __forceinline__ int row_pos(const GemmArgs& a, int m) {
   return m < a.M ? pos : 0;
 }
 
+// Scale of latent channel `chan` for the int8/int4 store (read early by the callers, so that the
+// store does not wait on it); 0 for a padding column.
+__device__ __forceinline__ uint16_t scale_bits(const GemmArgs& a, int chan) { return a.scales[chan >= 0 ? chan : 0]; }
+
 template <int R>
-__device__ __forceinline__ void store_latent(const GemmArgs& a, int slot, int chan, const float* xs, const int* ms,
-                                             const int* ps) {
+__device__ __forceinline__ void store_latent(const GemmArgs& a, int slot, int chan, uint16_t sc_bits, const float* xs,
+                                             const int* ms, const int* ps) {
   const bool is_key = slot < a.key_slots;
   if (a.latent == STARKV_LATENT_MIX84) {
     int qmax;
     if (is_key) qmax = slot < a.K8 ? 127 : 7;
     else qmax = (slot - a.key_slots) < a.V8 ? 127 : 7;
-    const float sc = chan >= 0 ? f16_to_f32(a.scales[chan]) : 0.f;
+    const float sc = chan >= 0 ? f16_to_f32(sc_bits) : 0.f;
     const bool nib = qmax == 7;
 #pragma unroll
     for (int v = 0; v < R; ++v) {
@@ -167,8 +171,22 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& a, int blk, float (*
   const int wave = wave_id();
   const int n = lane & 15, q = lane >> 4;
   const int s0 = blk * SW;
-  const int bslot = s0 + (HALF ? (n & 7) : n);
-  const int bchan = slot_channel_nb<MIX>(a, bslot);
+  const int jn = HALF ? (n & 7) : n;  // this lane's slot within the tile
+  const int bslot = s0 + jn;
+  int bchan;
+  if (MIX) {
+    // the tile's SW table entries (the table is padded to a multiple of 16) with uniform scalar
+    // loads; each lane picks its own
+    int t[SW];
+#pragma unroll
+    for (int i = 0; i < SW; ++i) t[i] = __builtin_amdgcn_readfirstlane(ld_uniform(a.slot_chan + s0 + i));
+    bchan = t[0];
+#pragma unroll
+    for (int i = 1; i < SW; ++i) bchan = jn == i ? t[i] : bchan;
+  } else {
+    bchan = slot_channel_nb<false>(a, bslot);
+  }
+  const uint16_t sc_bits = MIX ? scale_bits(a, bchan) : (uint16_t)0;
   const bool b_ok = bchan >= 0;
   const int tok = HALF ? (n & 7) : n;
   const int khalf = HALF ? (n >> 3) : 0;
@@ -234,7 +252,7 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& a, int blk, float (*
     if (HALF) x += __shfl(x, (lane + 40) & 63, 64);
     xs[v] = x;  // D row = token row; D column = n
   }
-  store_latent<4>(a, bslot, bchan, xs, ms, ps);
+  store_latent<4>(a, bslot, bchan, sc_bits, xs, ms, ps);
 }
 
 // Host side: argument blocks of the latent GEMM for a layer, and for an append into a cache.

@@ -94,7 +94,9 @@ int layer_init(const starkv_layer_desc& d, Layer* L) {
 
 int layer_upload_tables(Layer* L) {
   const int NS = L->key_slots + L->val_slots;
-  std::vector<int> slot_chan(NS, -1);
+  // padded to a multiple of 16 entries (-1): a 16-slot GEMM tile reads its entries unclamped
+  const int NSP = (NS + 15) / 16 * 16;
+  std::vector<int> slot_chan(NSP, -1);
   if (L->mix()) {
     for (int g = 0; g < L->H_kv; ++g) {
       for (int k = 0; k < L->n8[g]; ++k) slot_chan[L->off8[g] + k] = L->koff[g] + k;
@@ -119,12 +121,12 @@ int layer_upload_tables(Layer* L) {
   }
   const int H = L->H_kv;
   // one allocation: slot_chan | koff(H+1) | n8(H) | off8(H+1) | off4(H+1) | sp | src | absmax
-  size_t n_int = (size_t)NS + (H + 1) + H + (H + 1) + (H + 1);
+  size_t n_int = (size_t)NSP + (H + 1) + H + (H + 1) + (H + 1);
   size_t bytes = n_int * 4 + (size_t)L->n_lat * 4 * 3;
   std::vector<uint8_t> host(bytes, 0);
   size_t o = 0;
   auto put = [&](const void* p, size_t nb) { memcpy(host.data() + o, p, nb); o += nb; };
-  put(slot_chan.data(), NS * 4);
+  put(slot_chan.data(), NSP * 4);
   put(L->koff.data(), (H + 1) * 4);
   put(L->n8.data(), H * 4);
   put(L->off8.data(), (H + 1) * 4);
@@ -140,7 +142,7 @@ int layer_upload_tables(Layer* L) {
   L->dev_tables = dev;
   uint8_t* b = (uint8_t*)dev;
   o = 0;
-  L->d_slot_chan = (int*)(b + o); o += NS * 4;
+  L->d_slot_chan = (int*)(b + o); o += NSP * 4;
   L->d_koff = (int*)(b + o); o += (H + 1) * 4;
   L->d_n8 = (int*)(b + o); o += H * 4;
   L->d_off8 = (int*)(b + o); o += (H + 1) * 4;
