@@ -8,6 +8,11 @@
 // GEMM shape: rows = tokens, columns = cache slots (the key-row slots then the value slots,
 // in cache order, so that the two nibbles of an int4 byte are adjacent columns), K = d.
 // Workgroup tile 64 x 64, four waves of 32 x 32 (v_mfma_f32_32x32x16_bf16, or 32x32x2_f32).
+// The K loop keeps two register batches of KU K-steps in flight: a batch's refill is issued right
+// after its MFMAs, so each wave always has the next batch's loads outstanding.  Loads are
+// unconditional and the loop has no branch but its own (rows past M and padding columns read
+// row 0 / channel 0, K-steps past the end re-read the last one; their operands are zeroed after
+// the load).
 #include "device_common.h"
 #include "latent_gemm.h"
 #include "profile.h"
@@ -23,39 +28,116 @@ __global__ __launch_bounds__(512) void k_latent_gemm_skinny(GemmArgs a) {
 
 template <int DT, int MODE>
 __global__ __launch_bounds__(256) void k_latent_gemm(GemmArgs a) {
+  __shared__ float part[4][4][16][64];  // [wave][32 x 32 quadrant][D element][lane]: 64 KiB
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
-  const int wm = wave & 1, wn = wave >> 1;
-  const int m0 = blockIdx.x * 64 + wm * 32;
-  const int s0 = blockIdx.y * 64 + wn * 32;
   const int r = lane & 31, q = lane >> 5;
-
-  const int arow = m0 + r;
-  const bool a_ok = arow < a.M;
-  const int bslot = s0 + r;
-  const int bchan = slot_channel(a, bslot);
-  const uint16_t sc_bits = (MODE == 0 && a.latent == STARKV_LATENT_MIX84) ? scale_bits(a, bchan) : (uint16_t)0;
-  const bool b_ok = bchan >= 0;
-  const size_t a_base = (size_t)(a_ok ? arow : 0) * a.d;
-  const size_t b_base = (size_t)(b_ok ? bchan : 0) * a.d;
-
-  f32x16 acc;
+  const int mb = blockIdx.x * 64, sb = blockIdx.y * 64;
+  // operand rows of the tile's two 32-row halves (i) and two 32-slot halves (j)
+  bool a_ok[2], b_ok[2];
+  size_t a_base[2], b_base[2];
+  uint16_t scb[2];
 #pragma unroll
-  for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+  for (int h = 0; h < 2; ++h) {
+    const int arow = mb + 32 * h + r;
+    a_ok[h] = arow < a.M;
+    a_base[h] = (size_t)(a_ok[h] ? arow : 0) * a.d;
+    const int ch = slot_channel(a, sb + 32 * h + r);
+    b_ok[h] = ch >= 0;
+    b_base[h] = (size_t)(b_ok[h] ? ch : 0) * a.d;
+    scb[h] = (MODE == 0 && a.latent == STARKV_LATENT_MIX84) ? scale_bits(a, ch) : (uint16_t)0;
+  }
+  // this wave's K-steps (16 each): a quarter of K
+  const int nk = a.d / 16;
+  const int per = (nk + 3) / 4;
+  const int kb = wave * per, ke = min(nk, kb + per);
 
-  for (int k0 = 0; k0 < a.d; k0 += 16) {
-    u32x4 alo, ahi, blo, bhi;
-    load_frag8<DT>(a.X, a_base + k0 + 8 * q, a_ok, alo, ahi);
-    load_frag8<DT>(a.A_t, b_base + k0 + 8 * q, b_ok, blo, bhi);
-    if (DT == STARKV_BF16) {
-      acc = mfma32_bf16(as_bf16x8(alo), as_bf16x8(blo), acc);
-    } else {
+  f32x16 acc[2][2];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc = mfma32_f32(__uint_as_float(alo[e]), __uint_as_float(blo[e]), acc);
+  for (int x = 0; x < 2; ++x)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc = mfma32_f32(__uint_as_float(ahi[e]), __uint_as_float(bhi[e]), acc);
+    for (int y = 0; y < 2; ++y)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[x][y][v] = 0.f;
+
+  constexpr int NL = DT == STARKV_BF16 ? 1 : 2;  // 16-byte loads per operand fragment
+  constexpr int KU = DT == STARKV_BF16 ? 4 : 2;  // K-steps per batch
+  struct Batch {
+    u32x4 x[KU][2][NL], w[KU][2][NL];
+  };
+  auto load = [&](Batch& f, int k0) {
+#pragma unroll
+    for (int u = 0; u < KU; ++u) {
+      const size_t ko = (size_t)min(k0 + u, nk - 1) * 16 + 8 * q;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < NL; ++e) {
+          if (DT == STARKV_BF16) {
+            f.x[u][h][e] = ld16((const uint16_t*)a.X + a_base[h] + ko);
+            f.w[u][h][e] = ld16((const uint16_t*)a.A_t + b_base[h] + ko);
+          } else {
+            f.x[u][h][e] = ld16((const float*)a.X + a_base[h] + ko + 4 * e);
+            f.w[u][h][e] = ld16((const float*)a.A_t + b_base[h] + ko + 4 * e);
+          }
+        }
+    }
+  };
+  auto compute = [&](Batch& f, int k0) {
+#pragma unroll
+    for (int u = 0; u < KU; ++u) {
+      const bool kin = k0 + u < ke;  // K-steps past the wave's range (clamped loads) add nothing
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < NL; ++e) {
+          f.x[u][h][e] = a_ok[h] ? f.x[u][h][e] : u32x4{0, 0, 0, 0};
+          f.w[u][h][e] = (b_ok[h] && kin) ? f.w[u][h][e] : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y) {
+          if (DT == STARKV_BF16) {
+            acc[x][y] = mfma32_bf16(as_bf16x8(f.x[u][x][0]), as_bf16x8(f.w[u][y][0]), acc[x][y]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < NL; ++e)
+#pragma unroll
+              for (int c = 0; c < 4; ++c)
+                acc[x][y] = mfma32_f32(__uint_as_float(f.x[u][x][e][c]), __uint_as_float(f.w[u][y][e][c]), acc[x][y]);
+          }
+        }
+    }
+  };
+  if (kb < ke) {  // uniform
+    Batch fa, fb;
+    load(fa, kb);
+    load(fb, kb + KU);
+    for (int k0 = kb; k0 < ke; k0 += 2 * KU) {
+      compute(fa, k0);
+      load(fa, k0 + 2 * KU);
+      compute(fb, k0 + KU);
+      load(fb, k0 + 3 * KU);
     }
   }
+
+  // add the four waves' K-quarters: wave w takes quadrant (rows half w & 1, slots half w >> 1)
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) part[wave][2 * y + x][v][lane] = acc[x][y][v];
+  __syncthreads();
+  const int wm = wave & 1, wn = wave >> 1;
+  f32x16 accq;
+#pragma unroll
+  for (int v = 0; v < 16; ++v)
+    accq[v] = part[0][wave][v][lane] + part[1][wave][v][lane] + part[2][wave][v][lane] + part[3][wave][v][lane];
+  const int m0 = mb + 32 * wm;
+  const int s0 = sb + 32 * wn;
+  const uint16_t sc_bits = wn ? scb[1] : scb[0];
 
   // result: lane holds column n = r (slot s0 + r), rows d32_row(v, q)
   const int slot = s0 + r;
@@ -65,7 +147,7 @@ __global__ __launch_bounds__(256) void k_latent_gemm(GemmArgs a) {
     // calibrate: absmax of this column over the 32 rows (rows >= M hold 0)
     float m = 0.f;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) m = fmaxf(m, fabsf(acc[v]));
+    for (int v = 0; v < 16; ++v) m = fmaxf(m, fabsf(accq[v]));
     m = fmaxf(m, __shfl_xor(m, 32, 64));
     if (q == 0 && chan >= 0) atomicMax(a.absmax + chan, __float_as_uint(m));
     return;
@@ -75,7 +157,7 @@ __global__ __launch_bounds__(256) void k_latent_gemm(GemmArgs a) {
   int ms[16];
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
-    xs[v] = acc[v];
+    xs[v] = accq[v];
     ms[v] = m0 + d32_row(v, q);
   }
   int ps[16];
