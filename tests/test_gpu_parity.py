@@ -330,6 +330,37 @@ def test_many_rows_per_kv_head():
         H.check_output(w, got[b], ref, f"seq {b} len {int(run.lens[b])}")
 
 
+def test_many_rows_per_kv_head_mix84():
+    """64 query rows per KV head with int8/int4 latents (16 sequences x 4 queries): the tall
+    up-projection with the split merge folded in (value scales applied per channel)."""
+    lens0 = [40, 75, 128, 200, 33, 64, 97, 150, 45, 81, 110, 190, 36, 70, 129, 160]
+    w = dataclasses.replace(I.WORKLOADS[2], B=len(lens0), n_q=4)
+    H.log(f"[tall mix84] rows per KV head {w.B * w.n_q}, lens={lens0}")
+    run = H.make_layer(w, exact=True)
+    H.calibrate(run)
+    H.prefill(run, lens0, oracle_seqs=(0, 3, 11, 15))
+    q = H.queries(run)
+    got = H.from_dev(H.decode(run, q))
+    for b in run.oracle_seqs:
+        ref = H.oracle_decode(run, q, b, mode="latent")
+        H.check_output(w, got[b], ref, f"seq {b} len {int(run.lens[b])}")
+
+
+def test_many_rows_many_splits():
+    """64 query rows per KV head (8 sequences x 8 queries, bf16) with a sequence long enough for
+    more than four value splits: the separate split merge, then the tall up-projection."""
+    lens0 = [1400, 60, 130, 300, 45, 90, 220, 75]
+    w = dataclasses.replace(I.WORKLOADS[1], B=len(lens0), n_q=8)
+    H.log(f"[tall, many splits] rows per KV head {w.B * w.n_q}, lens={lens0}")
+    run = H.make_layer(w, exact=True)
+    H.prefill(run, lens0, oracle_seqs=(0, 1, 6))
+    q = H.queries(run)
+    got = H.from_dev(H.decode(run, q))
+    for b in run.oracle_seqs:
+        ref = H.oracle_decode(run, q, b, mode="latent")
+        H.check_output(w, got[b], ref, f"seq {b} len {int(run.lens[b])}")
+
+
 def test_fp32_many_key_tiles():
     """fp32 latent with key ranks near d_h (396 key channels: 13 K-tiles in the one column tile,
     so every score wave takes several K-tile groups) against the oracle."""
