@@ -1402,23 +1402,53 @@ __global__ __launch_bounds__(256) void k_values1(ValueArgs a) {
   }
 }
 
+// ---- asynchronous loads straight into LDS
+// Lane l's 16 bytes at src land at LDS byte address lds + 16 l (lds wave-uniform).  Issued as
+// assembly, so the compiler neither counts nor waits for it (it has no destination register):
+// the kernel waits with vm_wait<n>() (n = loads it may leave in flight) and a barrier before any
+// wave reads the data.  Loads the compiler issues itself can only be over-waited because of it.
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
 // Many query rows per sequence (M_pad = 32 NMT > 32; bf16 or int8/int4 latents): workgroup =
 // (split of one sequence, group of 4 NTW value N-tiles of 32 channels); wave w owns N-tiles
 // NTW w .. NTW w + NTW - 1 of the group -- each a bf16 or int8 block of 32 channels, or the even
-// or odd channels of an int4 block -- for all NMT row tiles.  The probability tile [M_pad][32] of
-// each 32-token chunk is staged in LDS once per workgroup by the first M_pad threads (row t:
-// rescaled by 2^(m_chunk - M_t), rounded to the MFMA input type), double-buffered, and read by
-// every wave as A fragments: the tile is fetched once per 4 NTW N-tiles.  The next chunk's loads
-// are issued before the current chunk's MFMAs.  Grid as k_values1 (one dimension; the groups of a
-// split run on one XCD).
-template <int LAT, int NMT, int NTW>
+// or odd channels of an int4 block -- for all NMT row tiles, so the probability tile of a chunk is
+// fetched once per 4 NTW N-tiles.  Each 32-token chunk's probability tile [M_pad][32] (as the
+// key-score kernel stored it, relative to its chunk maximum), chunk maxima and sums, and the
+// workgroup's value blocks are copied into a ring of D LDS stages by asynchronous LDS loads, D - 1
+// chunks ahead, with no register cost.  Each wave scales its probability A-fragments by
+// 2^(m_chunk - M_row) as it reads them (M_row: the row's largest chunk maximum over the split,
+// read before the loop; fp16 fragments take one packed half multiply per pair), so one barrier
+// per chunk suffices.  The probability rows of a stage are stored with their four 16-byte pieces
+// rotated by (row / 4) mod 4, which makes the A-fragment reads of 16 consecutive rows hit distinct
+// LDS banks.  Grid as k_values1 (one dimension; the groups of a split run on one XCD).
+template <int LAT, int NMT, int NTW, int D>
 __global__ __launch_bounds__(256) void k_values_mt(ValueArgs a) {
   static_assert(LAT != STARKV_LATENT_F32, "fp32 latents use k_values");
   constexpr int MP = 32 * NMT;
-  constexpr int RS = 40;                                    // LDS row stride (16-bit elements, 80 B)
-  constexpr int NV = LAT == STARKV_LATENT_BF16 ? 2 : 1;     // 16-byte value loads per lane per chunk
   constexpr int esz = LAT == STARKV_LATENT_BF16 ? 2 : 1;
-  __shared__ __align__(16) uint16_t pt[2][MP * RS];
+  constexpr int NV = esz;                       // 16-byte B-fragment pieces per lane per chunk
+  constexpr int BLKB = 32 * kTT * esz;          // bytes of one value block (32 rows x 32 tokens)
+  constexpr int NPI = MP / 16;                  // 1 KiB probability loads per stage
+  constexpr int NSI = NPI + 2;                  // + chunk maxima and sums
+  constexpr int SPW = (NSI + 3) / 4;            // of those per wave (uniform count)
+  constexpr int VPW = NTW * (BLKB / 1024);      // 1 KiB value loads per wave per stage
+  constexpr int LPW = SPW + VPW;                // loads per wave per stage
+  constexpr int P_OFF = 0, CM_OFF = MP * 64, CL_OFF = CM_OFF + 1024, V_OFF = CL_OFF + 1024;
+  constexpr int STAGE = V_OFF + 4 * NTW * BLKB;
+  static_assert(LPW * (D - 2) < 64, "vmcnt range");
+  __shared__ __align__(16) uint8_t ring[D * STAGE];
+  __shared__ float msplit[MP];
   const DecodeGeom& g = a.g;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int r = lane & 31, q = lane >> 5;
@@ -1432,14 +1462,13 @@ __global__ __launch_bounds__(256) void k_values_mt(ValueArgs a) {
   const int nch = seq_nch(a.seq, b);
   const int c_lo = s * a.cps, c_hi = min(c_lo + a.cps, nch);
   const int len = seq_len(a.seq, b);
+  const uint32_t ring0 = lds_addr(ring);
 
   // this wave's N-tiles
   const int n_nt8 = LAT == STARKV_LATENT_MIX84 ? a.V8 / 32 : a.NB;
   const int n_nt = n_nt8 + (LAT == STARKV_LATENT_MIX84 ? 2 * (a.NB - a.V8 / 32) : 0);
   bool ntok[NTW], is4[NTW];
   int blk[NTW], par[NTW];
-  constexpr int blkb = 32 * kTT * esz;  // bytes of one 32-row block of a tile
-  const uint8_t* vb[NTW];
 #pragma unroll
   for (int j = 0; j < NTW; ++j) {
     const int nt = (grp * 4 + wave) * NTW + j;
@@ -1456,50 +1485,47 @@ __global__ __launch_bounds__(256) void k_values_mt(ValueArgs a) {
         is4[j] = true;
       }
     }
-    vb[j] = a.v_tiles + vblock_off(b, blk[j], 0, g.v_rows, g.T_max, esz) + (size_t)r * kTT * esz + 16 * NV * q;
   }
 
-  // staging role: thread t < MP stages row t of every chunk
-  const bool stager = tid < MP;
-  const int srow = min(tid, MP - 1);
-  const bool sval = tid < g.M_q;
-  const size_t srow_g = (size_t)min(srow, g.M_q - 1);
-  float Ms = 0.f;  // the stager's reference: the largest chunk maximum of its row over the split
-  float lsum = 0.f;
-
-  struct Stage {
-    u32x4 p[4];
-    float cm, cl;
-  };
-  auto sload = [&](Stage& st, int c) {
-    const size_t cr = (size_t)(cbase + c) * g.M_pad + srow;
+  // asynchronous loads of chunk c (clamped into the split) into stage st
+  auto issue = [&](int c, int st) {
+    c = min(c, c_hi - 1);
+    const uint32_t sb = ring0 + st * STAGE;
+    const size_t cg = (size_t)(cbase + c);
 #pragma unroll
-    for (int x = 0; x < 4; ++x) st.p[x] = ld16((const uint16_t*)a.p + cr * kTC + 8 * x);
-    st.cm = a.cm[cr];
-    st.cl = a.cl[cr];
-  };
-  auto sstore = [&](const Stage& st, int buf) {
-    const float alpha = (!sval || st.cm == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(st.cm - Ms);
-    lsum += sval ? alpha * st.cl : 0.f;
-#pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      u32x4 w;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float x0, x1;
-        if (LAT == STARKV_LATENT_BF16) {
-          x0 = bf16_to_f32((uint16_t)(st.p[x][e] & 0xFFFF)) * alpha;
-          x1 = bf16_to_f32((uint16_t)(st.p[x][e] >> 16)) * alpha;
-          w[e] = (uint32_t)f32_to_bf16(x0) | ((uint32_t)f32_to_bf16(x1) << 16);
-        } else {
-          x0 = f16_to_f32((uint16_t)(st.p[x][e] & 0xFFFF)) * alpha;
-          x1 = f16_to_f32((uint16_t)(st.p[x][e] >> 16)) * alpha;
-          w[e] = (uint32_t)f32_to_f16(x0) | ((uint32_t)f32_to_f16(x1) << 16);
-        }
-      }
-      *reinterpret_cast<u32x4*>(&pt[buf][srow * RS + 8 * x]) = w;
+    for (int u = 0; u < SPW; ++u) {
+      const int i = wave * SPW + u;  // wave-uniform; both addresses formed, one chosen by select
+      // probability rows 16 i .. 16 i + 15: lane l -> row 16 i + l / 4, rotated piece l % 4
+      const int row = 16 * min(i, NPI - 1) + (lane >> 2);
+      const int piece = ((lane & 3) - (row >> 2)) & 3;
+      const void* psrc = (const uint8_t*)a.p + ((cg * g.M_pad + row) * kTC) * 2 + 16 * piece;
+      // chunk maxima (i == NPI) or sums (indexes past NSI repeat the sums)
+      const void* ssrc = (i == NPI ? a.cm : a.cl) + cg * g.M_pad + min(4 * lane, g.M_pad - 4);
+      const uint32_t dst = sb + (i < NPI ? P_OFF + i * 1024 : i == NPI ? CM_OFF : CL_OFF);
+      lds_dma16(i < NPI ? psrc : ssrc, dst);
     }
+#pragma unroll
+    for (int j = 0; j < NTW; ++j)
+#pragma unroll
+      for (int x = 0; x < BLKB / 1024; ++x)
+        lds_dma16(a.v_tiles + vblock_off(b, blk[j], c, g.v_rows, g.T_max, esz) + 1024 * x + 16 * lane,
+                  sb + V_OFF + (wave * NTW + j) * BLKB + 1024 * x);
   };
+
+  // the first D - 1 chunks go out, then each row's largest chunk maximum over the split
+#pragma unroll
+  for (int u = 0; u < D - 1; ++u) issue(c_lo + u, u);
+  if (tid < MP) {
+    const size_t row = (size_t)min(tid, g.M_q - 1);
+    msplit[tid] = chunks_max<16>(a.cm, cbase + c_lo, 1, c_hi - c_lo, g.M_pad, row);
+  }
+  __syncthreads();
+  float Ms[NMT], lsum[NMT];
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt) {
+    Ms[mt] = msplit[mt * 32 + r];
+    lsum[mt] = 0.f;
+  }
 
   f32x16 acc[NTW][NMT];
 #pragma unroll
@@ -1509,29 +1535,37 @@ __global__ __launch_bounds__(256) void k_values_mt(ValueArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[j][mt][v] = 0.f;
 
-  Stage sn;
-  u32x4 vcur[NTW][NV], vn[NTW][NV];
-  // the first chunk's loads go out before the stager reads its row's chunk maxima
-  if (stager) sload(sn, c_lo);
-#pragma unroll
-  for (int j = 0; j < NTW; ++j)
-#pragma unroll
-    for (int x = 0; x < NV; ++x) vcur[j][x] = ld16(vb[j] + (size_t)c_lo * blkb + 16 * x);
-  if (stager) {
-    Ms = chunks_max<16>(a.cm, cbase + c_lo, 1, c_hi - c_lo, g.M_pad, srow_g);
-    sstore(sn, 0);
-  }
-  __syncthreads();
   for (int c = c_lo; c < c_hi; ++c) {
-    const int cur = (c - c_lo) & 1;
-    const int cn = min(c + 1, c_hi - 1);
-    // next chunk's loads first
-    if (stager) sload(sn, cn);
+    const int st = (c - c_lo) % D;
+    vm_wait<LPW * (D - 2)>();  // this wave's loads of chunk c are in
+    __builtin_amdgcn_s_barrier();  // ... and every wave's; chunk c - 1's stage is free
+    asm volatile("" ::: "memory");
+    issue(c + D - 1, (c - c_lo + D - 1) % D);
+    const uint8_t* sp = ring + st * STAGE;
+    // chunk weights of this lane's A-fragment rows (all reads first, no branch between them)
+    float cmv[NMT], clv[NMT], alpha[NMT];
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) {
+      cmv[mt] = ((const float*)(sp + CM_OFF))[mt * 32 + r];
+      clv[mt] = ((const float*)(sp + CL_OFF))[mt * 32 + r];
+    }
+    const float lw = (wave == 0 && q == 0) ? 1.f : 0.f;  // one lane per row keeps the sum
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) {
+      const int row = mt * 32 + r;
+      alpha[mt] = (row >= g.M_q || cmv[mt] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(cmv[mt] - Ms[mt]);
+      lsum[mt] += lw * alpha[mt] * clv[mt];
+    }
+    // B fragments: 8 tokens of one channel (or channel pair) per K-step
+    _Float16 alpha_h[NMT];
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) alpha_h[mt] = (_Float16)alpha[mt];
+    u32x4 vf[NTW][NV];
 #pragma unroll
     for (int j = 0; j < NTW; ++j)
 #pragma unroll
-      for (int x = 0; x < NV; ++x) vn[j][x] = ld16(vb[j] + (size_t)cn * blkb + 16 * x);
-    // this chunk
+      for (int x = 0; x < NV; ++x)
+        vf[j][x] = *(const u32x4*)(sp + V_OFF + (wave * NTW + j) * BLKB + r * kTT * esz + 16 * NV * q + 16 * x);
     if (LAT == STARKV_LATENT_BF16 && c * kTC + kTT > len) {
       // zero the elements of tokens at or past the length (their bits may be anything)
 #pragma unroll
@@ -1541,7 +1575,7 @@ __global__ __launch_bounds__(256) void k_values_mt(ValueArgs a) {
           const int t = c * kTC + 16 * q + e;
           if (t >= len) {
             const uint32_t keep = (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
-            vcur[j][e >> 3][(e >> 1) & 3] &= keep;
+            vf[j][e >> 3][(e >> 1) & 3] &= keep;
           }
         }
     }
@@ -1549,20 +1583,37 @@ __global__ __launch_bounds__(256) void k_values_mt(ValueArgs a) {
     for (int h = 0; h < 2; ++h) {
       u32x4 af[NMT];
 #pragma unroll
-      for (int mt = 0; mt < NMT; ++mt)
-        af[mt] = *reinterpret_cast<const u32x4*>(&pt[cur][(mt * 32 + r) * RS + 16 * q + 8 * h]);
+      for (int mt = 0; mt < NMT; ++mt) {
+        const int row = mt * 32 + r;
+        const int piece = ((2 * q + h) + (row >> 2)) & 3;
+        const u32x4 raw = *(const u32x4*)(sp + P_OFF + row * 64 + 16 * piece);
+        if (LAT == STARKV_LATENT_BF16) {
+          u32x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float x0 = bf16_to_f32((uint16_t)(raw[e] & 0xFFFF)) * alpha[mt];
+            const float x1 = bf16_to_f32((uint16_t)(raw[e] >> 16)) * alpha[mt];
+            w[e] = (uint32_t)f32_to_bf16(x0) | ((uint32_t)f32_to_bf16(x1) << 16);
+          }
+          af[mt] = w;
+        } else {
+          // fp16 probabilities: packed half multiplies by the weight rounded to half
+          const f16x8 pv = as_f16x8(raw) * alpha_h[mt];
+          af[mt] = __builtin_bit_cast(u32x4, pv);
+        }
+      }
 #pragma unroll
       for (int j = 0; j < NTW; ++j) {
         u32x4 bfrag;
         if (LAT == STARKV_LATENT_BF16) {
-          bfrag = vcur[j][h % NV];
+          bfrag = vf[j][h % NV];
         } else {
           f16x8 ev, od;
           if (is4[j]) {
-            deq_i4x8(vcur[j][0][2 * h], vcur[j][0][2 * h + 1], ev, od);
+            deq_i4x8(vf[j][0][2 * h], vf[j][0][2 * h + 1], ev, od);
             if (par[j]) ev = od;
           } else {
-            ev = deq_i8x8(vcur[j][0][2 * h], vcur[j][0][2 * h + 1]);
+            ev = deq_i8x8(vf[j][0][2 * h], vf[j][0][2 * h + 1]);
           }
           bfrag = __builtin_bit_cast(u32x4, ev);
         }
@@ -1573,13 +1624,8 @@ __global__ __launch_bounds__(256) void k_values_mt(ValueArgs a) {
         }
       }
     }
-    if (stager && c + 1 < c_hi) sstore(sn, cur ^ 1);
-#pragma unroll
-    for (int j = 0; j < NTW; ++j)
-#pragma unroll
-      for (int x = 0; x < NV; ++x) vcur[j][x] = vn[j][x];
-    __syncthreads();
   }
+  vm_wait<0>();  // no asynchronous load may still be writing LDS when the workgroup ends
 
   // z partials: lane holds channel r of each N-tile, rows d32_row(v, q) of each row tile
 #pragma unroll
@@ -1604,9 +1650,15 @@ __global__ __launch_bounds__(256) void k_values_mt(ValueArgs a) {
         if (row < g.M_q) a.zp[((size_t)sg * g.M_pad + row) * g.rv_ld + vc] = acc[j][mt][v];
       }
   }
-  if (grp == 0 && sval) {
-    a.sl[(size_t)sg * g.M_pad + tid] = lsum;
-    a.sm[(size_t)sg * g.M_pad + tid] = Ms;
+  if (grp == 0 && wave == 0 && q == 0) {
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) {
+      const int row = mt * 32 + r;
+      if (row < g.M_q) {
+        a.sl[(size_t)sg * g.M_pad + row] = lsum[mt];
+        a.sm[(size_t)sg * g.M_pad + row] = Ms[mt];
+      }
+    }
   }
 }
 
@@ -2068,13 +2120,13 @@ template <int LAT>
 static hipError_t launch_values_mt(const ProfScope& ps, int nmt, dim3 grid, hipStream_t s, const ValueArgs& va) {
   const dim3 blk(256);
   switch (nmt) {
-    case 2: return launch_k(ps, k_values_mt<LAT, 2, 2>, grid, blk, s, va);
-    case 3: return launch_k(ps, k_values_mt<LAT, 3, 2>, grid, blk, s, va);
-    case 4: return launch_k(ps, k_values_mt<LAT, 4, 2>, grid, blk, s, va);
-    case 5: return launch_k(ps, k_values_mt<LAT, 5, 2>, grid, blk, s, va);
-    case 6: return launch_k(ps, k_values_mt<LAT, 6, 1>, grid, blk, s, va);
-    case 7: return launch_k(ps, k_values_mt<LAT, 7, 1>, grid, blk, s, va);
-    default: return launch_k(ps, k_values_mt<LAT, 8, 1>, grid, blk, s, va);
+    case 2: return launch_k(ps, k_values_mt<LAT, 2, 2, 3>, grid, blk, s, va);
+    case 3: return launch_k(ps, k_values_mt<LAT, 3, 2, 3>, grid, blk, s, va);
+    case 4: return launch_k(ps, k_values_mt<LAT, 4, 2, 3>, grid, blk, s, va);
+    case 5: return launch_k(ps, k_values_mt<LAT, 5, 2, 3>, grid, blk, s, va);
+    case 6: return launch_k(ps, k_values_mt<LAT, 6, 1, 3>, grid, blk, s, va);
+    case 7: return launch_k(ps, k_values_mt<LAT, 7, 1, 3>, grid, blk, s, va);
+    default: return launch_k(ps, k_values_mt<LAT, 8, 1, 3>, grid, blk, s, va);
   }
 }
 
