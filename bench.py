@@ -51,13 +51,19 @@ def to_dev_bf16(x: np.ndarray, dev: str):
     return torch.from_numpy(I.to_bf16_bits(x).view(np.int16)).to(dev).view(torch.bfloat16)
 
 
+# quantised latents: the denominator of the high-precision share (int8 region) of a segment
+QUANTIZED = {"mix84": 4, "had43": 5}
+
+
 def algorithmic_bytes(w, ranks, r_v, lens, n_q):
     """Bytes the method must move per step (each latent once, factors once, q, out, X_new, A)."""
     elem = {"f32": 4, "bf16": 2}[w.dtype]
-    if w.latent == "mix84":
-        n8 = [-(-int(r) // 4) for r in ranks]
+    if w.latent in QUANTIZED:
+        # bytes of the int8 region (leading quarter, or the outlier fifth) + the int4 region
+        den = QUANTIZED[w.latent]
+        n8 = [-(-int(r) // den) for r in ranks]
         key_tok = sum(n8) + (sum(int(r) for r in ranks) - sum(n8)) / 2.0
-        n8v = -(-r_v // 4)
+        n8v = -(-r_v // den)
         val_tok = n8v + (r_v - n8v) / 2.0
         scale_k, scale_v = 2 * int(sum(ranks)), 2 * r_v
     else:
@@ -199,7 +205,7 @@ def cpu_baseline(w, lf, lens, n_q, X0, Xcal, q_step, X_step, budget_s: float):
     except Exception:
         cores = os.cpu_count() or 1
     OL = O.build_layer(lf.U_k, lf.s_k, lf.V_k, lf.tau_k, lf.U_v, lf.s_v, lf.V_v, lf.tau_v, w.H_q, w.latent, w.dtype)
-    scales = O.calibrate_scales(Xcal, OL.A_cat, O.channel_qmax(OL)) if w.latent == "mix84" else None
+    scales = O.calibrate_scales(Xcal, OL.A_cat, O.channel_qmax(OL)) if w.latent in QUANTIZED else None
     t_setup = time.perf_counter()
     base = O.compress(X0, OL, scales)
     log(f"[cpu] oracle prefill of sequence 0 ({X0.shape[0]} tokens): {time.perf_counter() - t_setup:.1f} s")
@@ -222,7 +228,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=1, help="workload id (0-4); 1 is the headline")
+    ap.add_argument("--workload", type=int, default=1, help="workload id (0-5); 1 is the headline")
     ap.add_argument("--layers", type=int, default=0, help="layers to rotate (0: enough for 1 GiB)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
@@ -260,7 +266,7 @@ def main() -> int:
     lf = I.layer_factors(w, 0)
     log(f"[setup] workload {w.cfg_id} {w.name}: host factors {time.perf_counter() - t0:.1f} s")
     U = [torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev) for a in (lf.U_k, lf.V_k, lf.U_v, lf.V_v)]
-    Xcal = I.as_dtype(I.x_calibration(w), w.dtype) if w.latent == "mix84" else None
+    Xcal = I.as_dtype(I.x_calibration(w), w.dtype) if w.latent in QUANTIZED else None
     gen = torch.Generator(device=dev)
     gen.manual_seed(2606_08382)
 
@@ -383,7 +389,8 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"f32": "f32", "bf16": "bf16", "mix84": "int8/int4 codes, f16 MFMA, fp32 accumulate"}[w.latent],
+        "dtype": {"f32": "f32", "bf16": "bf16", "mix84": "int8/int4 codes, f16 MFMA, fp32 accumulate",
+                  "had43": "4-bit/3-bit codes in int8/int4 bytes, f16 MFMA, fp32 accumulate"}[w.latent],
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.B, "context": int(lens.max()) if not w.ragged else "ragged",
                    "context_tokens": int(lens.sum()), "queries_per_seq": n_q, "H_q": w.H_q, "H_kv": w.H_kv,

@@ -70,6 +70,18 @@ extern "C" {
 #define STARKV_LATENT_BF16 1  /* bf16 latent (round-to-nearest-even), no quantisation (dtype BF16) */
 #define STARKV_LATENT_MIX84 2 /* int8 codes for the leading ceil(r/4) channels of every segment,
                                  int4 codes for the rest, per-channel fp16 scales (dtype BF16) */
+#define STARKV_LATENT_HAD43 3 /* the block-rotated quantiser of the STAR-KV summary page,
+                                 Methodology section 3: each segment's leading ceil(r/5)
+                                 channels (outlier block) and the rest (inlier block) are
+                                 rotated by independent Hadamard transforms folded into the
+                                 factors (A' = A R, B' = R^T B / n per Sylvester piece of
+                                 order n; blocks whose size is not a power of two are split
+                                 into the power-of-two pieces of their binary decomposition,
+                                 largest first), then quantised to 4-bit (|code| <= 7,
+                                 outliers) and 3-bit (|code| <= 3, inliers) symmetric codes
+                                 with per-channel fp16 scales.  Codes are stored in the
+                                 mix84 byte format: outliers in the int8 region, inliers in
+                                 the int4 region (dtype BF16). */
 
 /* limits of this build */
 #define STARKV_MAX_BATCH 128     /* sequences per call */

@@ -17,6 +17,11 @@ Soft Thresholding for Adaptive Rank Control"):
   (outlier) channels of the latent get more bits than the rest; the abstract adds
   that the quantiser uses data statistics.
   -> :func:`channel_qmax`, :func:`calibrate_scales`, :func:`quantize`.
+  The same section's block-wise Hadamard: the outlier block (20% of the channels)
+  and the inlier block (the rest) each get an independent Hadamard rotation that
+  is folded into the factors, then 4-bit outlier and 3-bit inlier codes
+  (``latent="had43"``).  -> :func:`sylvester`, :func:`pow2_blocks`,
+  :func:`block_hadamard`, :func:`factor_pair`.
 * Problem Statement: the cache holds the projected hidden states (the latent)
   instead of K and V.  -> :func:`latent`, the cache byte format.
 
@@ -31,6 +36,13 @@ with an IEEE fp32 division, and a zero scale gives code 0; the latent is the
 fp32 accumulator value; the softmax scale is ``1/sqrt(d_h)``; query ``j`` of a
 chunk of ``n_q`` sees the tokens at positions ``<= T - n_q + j``; query head
 ``h`` reads KV head ``h // (H_q/H_kv)``; there is no positional rotation.
+For ``had43``: the outlier block is the leading ceil(r/5) channels of each
+segment; a block whose size is not a power of two is rotated by Sylvester
+Hadamards on the power-of-two pieces of its binary decomposition (largest
+first); the +-1 matrix R goes into ``A`` and ``R^T / n`` (n = the piece's
+order) into ``B``, so that ``A B`` is unchanged; codes are clamped to +-7
+(outlier) and +-3 (inlier) and stored in the int8 and int4 regions of the
+mix84 byte format.
 """
 
 from __future__ import annotations
@@ -91,17 +103,63 @@ def kept_spectrum(s, tau, shrink: bool = True) -> np.ndarray:
 # ---------------------------------------------------------------------------
 # O2: factor build (truncated SVD factors; singular values in the down-projection)
 
-def factor_pair(U, s, V, tau, shrink: bool = True, dtype: str = "f32"):
+def factor_pair(U, s, V, tau, shrink: bool = True, dtype: str = "f32", rotate: bool = False):
     """W = U diag(s) V^T  ->  A (d x r) = U[:, :r] diag(s'[:r]),  B (r x n) = V[:, :r]^T.
 
     A is one fp32 multiply per element, then rounded to ``dtype``; B is V^T rounded.
+    rotate=True (Methodology section 3, block-wise Hadamard folded into the factors):
+    A' = A R and B' = D^-1 R^T B with the +-1 block-diagonal R of
+    :func:`block_hadamard` over the outlier and inlier blocks of this segment and D
+    its piece orders; the products are summed in fp64 from the fp32 values, then
+    rounded to fp32 and to ``dtype``.
     """
     r = select_rank(s, tau)
     sp = kept_spectrum(s, tau, shrink)[:r]
     U32 = np.asarray(U, dtype=np.float32)[:, :r]
-    A = round_dtype(U32 * sp[None, :], dtype)
-    B = round_dtype(np.asarray(V, dtype=np.float32)[:, :r].T, dtype)
-    return A, B
+    A32 = U32 * sp[None, :]
+    B32 = np.asarray(V, dtype=np.float32)[:, :r].T
+    if not rotate:
+        return round_dtype(A32, dtype), round_dtype(B32, dtype)
+    R, n = block_hadamard(r, had43_split(r)[0])
+    A = A32.astype(np.float64) @ R
+    B = (R.T @ B32.astype(np.float64)) / n[:, None]
+    return round_dtype(A.astype(np.float32), dtype), round_dtype(B.astype(np.float32), dtype)
+
+
+# ---------------------------------------------------------------------------
+# block-wise Hadamard rotation (Methodology section 3)
+
+def sylvester(n: int) -> np.ndarray:
+    """Sylvester's Hadamard matrix of order n (a power of two): H_1 = [1],
+    H_2m = [[H_m, H_m], [H_m, -H_m]].  Entries +-1 (int64)."""
+    if n < 1 or n & (n - 1):
+        raise ValueError(f"Sylvester order must be a power of two, got {n}")
+    H = np.ones((1, 1), dtype=np.int64)
+    while H.shape[0] < n:
+        H = np.block([[H, H], [H, -H]])
+    return H
+
+
+def pow2_blocks(n: int) -> List[int]:
+    """The powers of two that sum to n, largest first (its binary decomposition)."""
+    return [1 << b for b in range(int(n).bit_length() - 1, -1, -1) if (int(n) >> b) & 1]
+
+
+def block_hadamard(r: int, n_hi: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Rotation of one latent segment of rank r whose leading n_hi channels are the
+    outlier block: R (r x r, entries 0/+-1) is block-diagonal with one Sylvester
+    Hadamard per power-of-two piece of the outlier block, then of the inlier block
+    (pieces in the order of :func:`pow2_blocks`); n (length r) holds, per channel, the
+    order of the piece it belongs to, so that R diag(1/n) R^T = I."""
+    R = np.zeros((r, r), dtype=np.float64)
+    n = np.zeros(r, dtype=np.float64)
+    c = 0
+    for size in pow2_blocks(n_hi) + pow2_blocks(r - n_hi):
+        R[c: c + size, c: c + size] = sylvester(size)
+        n[c: c + size] = size
+        c += size
+    assert c == r
+    return R, n
 
 
 @dataclasses.dataclass
@@ -135,12 +193,13 @@ def build_layer(U_k, s_k, V_k, tau_k, U_v, s_v, V_v, tau_v, H_q: int, latent: st
     """Hybrid decomposition: per-head (HD) key factors, joint (JD) value factors."""
     H_kv, d, d_h = np.shape(U_k)
     As, Bs, ranks = [], [], []
+    rot = latent == "had43"
     for g in range(H_kv):
-        A, B = factor_pair(U_k[g], s_k[g], V_k[g], tau_k[g], shrink, dtype)
+        A, B = factor_pair(U_k[g], s_k[g], V_k[g], tau_k[g], shrink, dtype, rotate=rot)
         As.append(A)
         Bs.append(B)
         ranks.append(A.shape[1])
-    A_v, B_v = factor_pair(U_v, s_v, V_v, tau_v, shrink, dtype)
+    A_v, B_v = factor_pair(U_v, s_v, V_v, tau_v, shrink, dtype, rotate=rot)
     A_cat = np.concatenate(As + [A_v], axis=1)
     B_k = np.concatenate(Bs, axis=0) if Bs else np.zeros((0, d_h), np.float32)
     return Layer(np.asarray(ranks, dtype=np.int64), A_v.shape[1], A_cat, B_k, B_v,
@@ -150,6 +209,13 @@ def build_layer(U_k, s_k, V_k, tau_k, U_v, s_v, V_v, tau_v, H_q: int, latent: st
 # ---------------------------------------------------------------------------
 # mixed precision split (Methodology section 3; leading channels get more bits)
 
+QUANTIZED = ("mix84", "had43")
+
+
+def is_quantized(latent: str) -> bool:
+    return latent in QUANTIZED
+
+
 def mix84_split(r: int) -> Tuple[int, int]:
     """(int8 channels, int4 channels) of a latent segment of rank r: the leading
     ceil(r/4) channels are int8, the rest int4."""
@@ -157,12 +223,31 @@ def mix84_split(r: int) -> Tuple[int, int]:
     return n8, int(r) - n8
 
 
+def had43_split(r: int) -> Tuple[int, int]:
+    """(outlier channels, inlier channels) of a segment of rank r for the rotated
+    quantiser: the leading ceil(r/5) channels (20%) are the outlier block."""
+    n_hi = -(-int(r) // 5)
+    return n_hi, int(r) - n_hi
+
+
+def precision_split(r: int, latent: str) -> Tuple[int, int]:
+    """(channels in the high-precision block, channels in the low one)."""
+    return had43_split(r) if latent == "had43" else mix84_split(r)
+
+
+def code_limits(latent: str) -> Tuple[int, int]:
+    """qmax of the high and the low block: int8/int4 (127, 7) for mix84; 4-bit and
+    3-bit symmetric codes (7, 3) for had43."""
+    return (7, 3) if latent == "had43" else (127, 7)
+
+
 def channel_qmax(layer: Layer) -> np.ndarray:
-    """qmax per latent channel in natural order (127 for int8, 7 for int4)."""
+    """qmax per latent channel in natural order."""
     q = []
+    qhi, qlo = code_limits(layer.latent)
     for r in list(layer.ranks) + [layer.r_v]:
-        n8, n4 = mix84_split(int(r))
-        q += [127] * n8 + [7] * n4
+        nhi, nlo = precision_split(int(r), layer.latent)
+        q += [qhi] * nhi + [qlo] * nlo
     return np.asarray(q, dtype=np.int64)
 
 
@@ -228,6 +313,8 @@ class CacheFormat:
     to a multiple of 32 rows), then V4/2 byte-rows, one per pair of int4 channels
     (low nibble = even channel, padded to a multiple of 64 channels); byte t of a
     row is token t of the tile.
+    had43 uses the same regions, with the outlier block (ceil(r/5) channels) in
+    the int8 region and the inlier block in the int4 region.
     f32/bf16: key row = the key latent in channel order, padded to 16 bytes;
     value tile = r_v (padded to a multiple of 32) element-rows of 32 tokens.
     """
@@ -238,16 +325,24 @@ class CacheFormat:
 
     @property
     def elem(self) -> int:
-        return {"f32": 4, "bf16": 2, "mix84": 1}[self.latent]
+        return {"f32": 4, "bf16": 2, "mix84": 1, "had43": 1}[self.latent]
+
+    @property
+    def quantized(self) -> bool:
+        return is_quantized(self.latent)
+
+    def split(self, r: int) -> Tuple[int, int]:
+        """Channels of a rank-r segment in the int8 region and in the int4 region."""
+        return precision_split(r, self.latent)
 
     # key side
     @property
     def n8(self) -> List[int]:
-        return [mix84_split(r)[0] for r in self.ranks]
+        return [self.split(r)[0] for r in self.ranks]
 
     @property
     def n4(self) -> List[int]:
-        return [mix84_split(r)[1] for r in self.ranks]
+        return [self.split(r)[1] for r in self.ranks]
 
     @property
     def K8(self) -> int:
@@ -259,23 +354,23 @@ class CacheFormat:
 
     @property
     def k_row_bytes(self) -> int:
-        if self.latent == "mix84":
+        if self.quantized:
             return self.K8 + self.K4 // 2
         return _ceil_to(sum(self.ranks) * self.elem, 16)
 
     # value side
     @property
     def V8(self) -> int:
-        return _ceil_to(mix84_split(self.r_v)[0], 32)
+        return _ceil_to(self.split(self.r_v)[0], 32)
 
     @property
     def V4(self) -> int:
-        return _ceil_to(mix84_split(self.r_v)[1], 64)
+        return _ceil_to(self.split(self.r_v)[1], 64)
 
     @property
     def v_rows(self) -> int:
-        """Rows of a value tile (byte-rows for mix84, element-rows otherwise)."""
-        if self.latent == "mix84":
+        """Rows of a value tile (byte-rows when quantised, element-rows otherwise)."""
+        if self.quantized:
             return self.V8 + self.V4 // 2
         return _ceil_to(self.r_v, 32)
 
@@ -285,11 +380,11 @@ class CacheFormat:
 
 
 def pack_key_rows(vals, fmt: CacheFormat) -> np.ndarray:
-    """Key latent rows [T, sum(r)] (codes for mix84, values otherwise) -> bytes [T, k_row_bytes]."""
+    """Key latent rows [T, sum(r)] (codes when quantised, values otherwise) -> bytes [T, k_row_bytes]."""
     vals = np.asarray(vals)
     T = vals.shape[0]
     out = np.zeros((T, fmt.k_row_bytes), dtype=np.uint8)
-    if fmt.latent != "mix84":
+    if not fmt.quantized:
         if fmt.latent == "f32":
             raw = np.ascontiguousarray(vals, dtype=np.float32).view(np.uint8).reshape(T, -1)
         else:
@@ -340,7 +435,7 @@ def pack_value_tiles(vals, fmt: CacheFormat, n_tiles: int) -> np.ndarray:
     vals = np.asarray(vals)
     T = vals.shape[0]
     out = np.zeros((n_tiles, fmt.v_rows, TT * fmt.elem), dtype=np.uint8)
-    if fmt.latent != "mix84":
+    if not fmt.quantized:
         if fmt.latent == "f32":
             ev = np.zeros((n_tiles * TT, fmt.v_rows), dtype=np.float32)
             ev[:T, : fmt.r_v] = vals
@@ -350,7 +445,7 @@ def pack_value_tiles(vals, fmt: CacheFormat, n_tiles: int) -> np.ndarray:
             ev[:T, : fmt.r_v] = (round_bf16(vals).view(np.uint32) >> 16).astype(np.uint16)
             raw = ev.reshape(n_tiles, TT, fmt.v_rows).transpose(0, 2, 1).copy().view(np.uint8)
         return raw.reshape(n_tiles, fmt.v_rows, TT * fmt.elem)
-    n8, n4 = mix84_split(fmt.r_v)
+    n8, n4 = fmt.split(fmt.r_v)
     c = np.zeros((n_tiles * TT, fmt.r_v), dtype=np.int64)
     c[:T] = vals
     byrow = np.zeros((n_tiles * TT, fmt.v_rows), dtype=np.uint8)
@@ -371,7 +466,7 @@ def unpack_value_tiles(tiles, fmt: CacheFormat, T: int) -> np.ndarray:
         v = tiles.copy().view(np.uint16).reshape(n_tiles, fmt.v_rows, TT)
         v = v.transpose(0, 2, 1).reshape(n_tiles * TT, fmt.v_rows)[:T, : fmt.r_v]
         return (v.astype(np.uint32) << 16).view(np.float32)
-    n8, n4 = mix84_split(fmt.r_v)
+    n8, n4 = fmt.split(fmt.r_v)
     by = tiles.transpose(0, 2, 1).reshape(n_tiles * TT, fmt.v_rows)[:T]
     out = np.zeros((T, fmt.r_v), dtype=np.int64)
     out[:, :n8] = by[:, :n8].view(np.int8)
@@ -474,7 +569,7 @@ def lse_merge(parts: Sequence[Tuple[float, float, np.ndarray]]) -> np.ndarray:
 
 @dataclasses.dataclass
 class SequenceCache:
-    """The oracle's cache of one sequence: integer codes (mix84) or stored values."""
+    """The oracle's cache of one sequence: integer codes (mix84, had43) or stored values."""
 
     key: np.ndarray  # [T, sum(r)]
     value: np.ndarray  # [T, r_v]
@@ -484,7 +579,7 @@ def compress(X, layer: Layer, scales=None) -> SequenceCache:
     """Project hidden states X [T, d] into the latent and quantise / round it."""
     x = latent(X, layer.A_cat)
     nk = layer.n_key
-    if layer.latent == "mix84":
+    if is_quantized(layer.latent):
         codes = quantize(x, scales, channel_qmax(layer))
         return SequenceCache(codes[:, :nk], codes[:, nk:])
     v = stored_latent(x, layer.latent)
@@ -493,7 +588,7 @@ def compress(X, layer: Layer, scales=None) -> SequenceCache:
 
 def dequantized(cache: SequenceCache, layer: Layer, scales=None) -> Tuple[np.ndarray, np.ndarray]:
     nk = layer.n_key
-    if layer.latent == "mix84":
+    if is_quantized(layer.latent):
         s = np.asarray(scales, dtype=np.float16)
         return dequantize(cache.key, s[:nk]), dequantize(cache.value, s[nk:])
     return np.asarray(cache.key, np.float64), np.asarray(cache.value, np.float64)

@@ -26,7 +26,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libstarkv.so")
 
 F32, BF16 = 0, 1
-LATENT = {"f32": 0, "bf16": 1, "mix84": 2}
+LATENT = {"f32": 0, "bf16": 1, "mix84": 2, "had43": 3}
 DTYPE = {"f32": F32, "bf16": BF16}
 TILE_TOKENS = 32
 MAX_BATCH = 128
@@ -230,7 +230,7 @@ class Layer:
         _check(self._lib.starkv_bind_factors(self._h, _ptr(A_t), _ptr(B_k), _ptr(B_vt)), "starkv_bind_factors")
 
     def calibrate(self, X_cal, stream=None):
-        """Per-channel fp16 scales from calibration hidden states [n_cal, d] (mix84)."""
+        """Per-channel fp16 scales from calibration hidden states [n_cal, d] (mix84, had43)."""
         import torch
         assert X_cal.dtype == self.torch_dtype and X_cal.is_contiguous()
         self.scales = torch.empty((self.info["n_lat"],), dtype=torch.float16, device=X_cal.device)

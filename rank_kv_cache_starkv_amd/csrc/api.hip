@@ -65,7 +65,8 @@ int starkv_layer_create(const starkv_layer_desc* d, starkv_layer** out) {
   if (d->H_q % d->H_kv != 0) return STARKV_EINVAL;
   if (!d->s_k || !d->tau_k || !d->s_v) return STARKV_EINVAL;
   if (d->dtype != STARKV_F32 && d->dtype != STARKV_BF16) return STARKV_EINVAL;
-  if (d->latent != STARKV_LATENT_F32 && d->latent != STARKV_LATENT_BF16 && d->latent != STARKV_LATENT_MIX84)
+  if (d->latent != STARKV_LATENT_F32 && d->latent != STARKV_LATENT_BF16 && d->latent != STARKV_LATENT_MIX84 &&
+      d->latent != STARKV_LATENT_HAD43)
     return STARKV_EINVAL;
   if (d->shrink != 0 && d->shrink != 1) return STARKV_EINVAL;
   if (bad_float(d->tau_v) || d->tau_v < 0.f) return STARKV_EINVAL;
@@ -107,7 +108,7 @@ int starkv_layer_get_info(const starkv_layer* l, starkv_layer_info* info) {
   info->d_h = L.d_h;
   info->d = L.d;
   info->dtype = L.dtype;
-  info->latent = L.latent;
+  info->latent = L.had ? STARKV_LATENT_HAD43 : L.latent;
   info->n_key = L.n_key;
   info->r_v = L.r_v;
   info->n_lat = L.n_lat;

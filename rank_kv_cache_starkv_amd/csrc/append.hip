@@ -173,13 +173,13 @@ __global__ void k_fill_u32(uint32_t* p, int n, uint32_t v) {
 
 __global__ __launch_bounds__(256) void k_finish_scales(const uint32_t* __restrict__ absmax, const int* __restrict__ src,
                                                        const int* __restrict__ n8, int n8v, int H_kv, int n_lat,
-                                                       uint16_t* __restrict__ scales) {
+                                                       float qmax_hi, float qmax_lo, uint16_t* __restrict__ scales) {
   const int c = blockIdx.x * 256 + threadIdx.x;
   if (c >= n_lat) return;
   const int s = src[c];
   const int g = s >> 16, k = s & 0xFFFF;
   const bool is8 = (g < H_kv) ? (k < n8[g]) : (k < n8v);
-  const float q = is8 ? 127.f : 7.f;
+  const float q = is8 ? qmax_hi : qmax_lo;
   scales[c] = f32_to_f16(__uint_as_float(absmax[c]) / q);
 }
 
@@ -193,6 +193,8 @@ void fill_gemm_args(const Layer& L, GemmArgs& a, const void* X, int M) {
   a.key_slots = L.key_slots;
   a.K8 = L.K8;
   a.V8 = L.V8;
+  a.qmax_hi = L.qmax_hi;
+  a.qmax_lo = L.qmax_lo;
   a.n_key = L.n_key;
   a.r_v = L.r_v;
   a.latent = L.latent;
@@ -220,7 +222,8 @@ hipError_t launch_calibrate(const Layer& L, const void* X_cal, int n_cal, uint16
   if (L.dtype == STARKV_BF16) hipLaunchKernelGGL((k_latent_gemm<STARKV_BF16, 1>), grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL((k_latent_gemm<STARKV_F32, 1>), grid, dim3(256), 0, s, a);
   hipLaunchKernelGGL(k_finish_scales, dim3((L.n_lat + 255) / 256), dim3(256), 0, s, (const uint32_t*)L.d_absmax,
-                     (const int*)L.d_src, (const int*)L.d_n8, L.n8v, L.H_kv, L.n_lat, scales_out);
+                     (const int*)L.d_src, (const int*)L.d_n8, L.n8v, L.H_kv, L.n_lat, (float)L.qmax_hi,
+                     (float)L.qmax_lo, scales_out);
   return hipGetLastError();
 }
 

@@ -3,7 +3,9 @@
 // append kernel and the fused decode-step front kernel.
 //
 // STAR-KV summary page, Problem Statement: the cache holds the projected hidden states; Methodology
-// section 3: the leading channels of each latent segment are stored as int8, the rest as int4.
+// section 3: the leading channels of each latent segment are stored as int8, the rest as int4
+// (with the block-rotated quantiser: 4-bit outlier codes in the int8 region, 3-bit inlier codes
+// in the int4 region).
 #pragma once
 
 #include "device_common.h"
@@ -17,6 +19,7 @@ struct GemmArgs {
   const int* slot_chan; // [NS rounded up to 16]: natural channel of each column, -1 for padding
   int M, d, NS;
   int key_slots, K8, V8;
+  int qmax_hi, qmax_lo;  // code limits of the int8 and int4 regions
   int n_key, r_v;
   int latent;
   // append
@@ -69,11 +72,9 @@ __device__ __forceinline__ void store_latent(const GemmArgs& a, int slot, int ch
                                              const int* ms, const int* ps) {
   const bool is_key = slot < a.key_slots;
   if (a.latent == STARKV_LATENT_MIX84) {
-    int qmax;
-    if (is_key) qmax = slot < a.K8 ? 127 : 7;
-    else qmax = (slot - a.key_slots) < a.V8 ? 127 : 7;
+    const bool nib = is_key ? slot >= a.K8 : (slot - a.key_slots) >= a.V8;
+    const int qmax = nib ? a.qmax_lo : a.qmax_hi;
     const float sc = chan >= 0 ? f16_to_f32(sc_bits) : 0.f;
-    const bool nib = qmax == 7;
 #pragma unroll
     for (int v = 0; v < R; ++v) {
       const int m = ms[v];

@@ -2,7 +2,8 @@
 //
 // STAR-KV summary page, Methodology section 1 (thresholds on the singular values,
 // hard at inference, projections truncated) and section 2 (keys head by head,
-// values jointly); section 3 for the leading-channel split of the latent.
+// values jointly); section 3 for the leading-channel split of the latent and for the
+// block-wise Hadamard rotation that is folded into the factors.
 #include <math.h>
 #include <string.h>
 
@@ -21,7 +22,11 @@ int layer_init(const starkv_layer_desc& d, Layer* L) {
   L->d_h = d.d_h;
   L->d = d.d;
   L->dtype = d.dtype;
-  L->latent = d.latent;
+  // the block-rotated quantiser keeps the mix84 byte format (and kernels)
+  L->had = d.latent == STARKV_LATENT_HAD43;
+  L->latent = L->had ? STARKV_LATENT_MIX84 : d.latent;
+  L->qmax_hi = L->had ? 7 : 127;  // 4-bit outlier codes, or int8
+  L->qmax_lo = L->had ? 3 : 7;    // 3-bit inlier codes, or int4
   L->shrink = d.shrink;
   L->n_v = d.n_v;
   L->G = d.H_q / d.H_kv;
@@ -60,8 +65,10 @@ int layer_init(const starkv_layer_desc& d, Layer* L) {
   L->off8.assign(d.H_kv + 1, 0);
   L->off4.assign(d.H_kv + 1, 0);
   if (L->mix()) {
+    // high-precision block: the leading quarter (int8/int4), or the leading fifth (outliers)
+    const int den = L->had ? 5 : 4;
     for (int g = 0; g < d.H_kv; ++g) {
-      L->n8[g] = (L->rk[g] + 3) / 4;
+      L->n8[g] = (L->rk[g] + den - 1) / den;
       L->n4[g] = L->rk[g] - L->n8[g];
       L->off8[g + 1] = L->off8[g] + L->n8[g];
       L->off4[g + 1] = L->off4[g] + L->n4[g];
@@ -69,7 +76,7 @@ int layer_init(const starkv_layer_desc& d, Layer* L) {
     L->K8 = ceil_to(L->off8[d.H_kv], 16);
     L->K4 = ceil_to(L->off4[d.H_kv], 32);
     L->k_row_bytes = L->K8 + L->K4 / 2;
-    L->n8v = (L->r_v + 3) / 4;
+    L->n8v = (L->r_v + den - 1) / den;
     L->n4v = L->r_v - L->n8v;
     L->V8 = ceil_to(L->n8v, 32);
     L->V4 = ceil_to(L->n4v, 64);
@@ -119,10 +126,35 @@ int layer_upload_tables(Layer* L) {
     sp[L->n_key + k] = L->sp_v[k];
     src[L->n_key + k] = (L->H_kv << 16) | k;
   }
+  // Hadamard pieces of the rotated quantiser: each segment's outlier block, then its inlier
+  // block, cut into the powers of two of their sizes (largest first); without rotation every
+  // channel is a piece of order 1
+  std::vector<int> rot(L->n_lat);
+  auto pieces = [&](int c, int n) {
+    for (int b = 30; b >= 0; --b)
+      if ((n >> b) & 1) {
+        for (int j = 0; j < (1 << b); ++j) rot[c + j] = (c << 5) | b;
+        c += 1 << b;
+      }
+  };
+  for (int g = 0; g < L->H_kv; ++g) {
+    if (L->had) {
+      pieces(L->koff[g], L->n8[g]);
+      pieces(L->koff[g] + L->n8[g], L->n4[g]);
+    } else {
+      for (int k = 0; k < L->rk[g]; ++k) rot[L->koff[g] + k] = (L->koff[g] + k) << 5;
+    }
+  }
+  if (L->had) {
+    pieces(L->n_key, L->n8v);
+    pieces(L->n_key + L->n8v, L->n4v);
+  } else {
+    for (int k = 0; k < L->r_v; ++k) rot[L->n_key + k] = (L->n_key + k) << 5;
+  }
   const int H = L->H_kv;
-  // one allocation: slot_chan | koff(H+1) | n8(H) | off8(H+1) | off4(H+1) | sp | src | absmax
+  // one allocation: slot_chan | koff(H+1) | n8(H) | off8(H+1) | off4(H+1) | sp | src | rot | absmax
   size_t n_int = (size_t)NSP + (H + 1) + H + (H + 1) + (H + 1);
-  size_t bytes = n_int * 4 + (size_t)L->n_lat * 4 * 3;
+  size_t bytes = n_int * 4 + (size_t)L->n_lat * 4 * 4;
   std::vector<uint8_t> host(bytes, 0);
   size_t o = 0;
   auto put = [&](const void* p, size_t nb) { memcpy(host.data() + o, p, nb); o += nb; };
@@ -133,6 +165,7 @@ int layer_upload_tables(Layer* L) {
   put(L->off4.data(), (H + 1) * 4);
   put(sp.data(), L->n_lat * 4);
   put(src.data(), L->n_lat * 4);
+  put(rot.data(), L->n_lat * 4);
   void* dev = nullptr;
   if (hipMalloc(&dev, bytes) != hipSuccess) return STARKV_ENOMEM;
   if (hipMemcpy(dev, host.data(), bytes, hipMemcpyHostToDevice) != hipSuccess) {
@@ -149,6 +182,7 @@ int layer_upload_tables(Layer* L) {
   L->d_off4 = (int*)(b + o); o += (H + 1) * 4;
   L->d_sp = (float*)(b + o); o += L->n_lat * 4;
   L->d_src = (int*)(b + o); o += L->n_lat * 4;
+  L->d_rot = (int*)(b + o); o += L->n_lat * 4;
   L->d_absmax = (uint32_t*)(b + o);
   return STARKV_OK;
 }
@@ -196,6 +230,89 @@ __global__ __launch_bounds__(256) void k_build_bv(const float* __restrict__ V_v,
   store_dt<T>(B_vt, idx, V_v[j * n_v + k]);
 }
 
+// Rotated factors (block-wise Hadamard folded into the factors, Methodology section 3): for
+// the Sylvester piece of order n = 2^m starting at natural channel c0, with H[j][l] =
+// (-1)^popcount(j & l),
+//   A'[:, c0 + l] = sum_j H[j][l] fp32(U[:, c0 + j] s'[c0 + j])       (A' = A H)
+//   B'[c0 + l, :] = (1/n) sum_j H[l][j] B[c0 + j, :]                   (B' = H^T B / n)
+// so that A' B' = A B.  Sums in fp64, in piece order, then rounded to fp32 and to the
+// factor type.
+__device__ __forceinline__ double had_sign(int j, int l, double x) { return (__popc(j & l) & 1) ? -x : x; }
+// fp64 -> fp32 (RNE); the empty register barrier keeps the compiler from merging this rounding
+// and the later fp32 -> bf16 one into a single fp64 -> bf16 rounding, which differs at ties
+__device__ __forceinline__ float to_f32_kept(double x) {
+  float f = (float)x;
+  asm volatile("" : "+v"(f));
+  return f;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_build_a_rot(const float* __restrict__ U_k, const float* __restrict__ U_v,
+                                                     const float* __restrict__ sp, const int* __restrict__ src,
+                                                     const int* __restrict__ rot, T* __restrict__ A_t, int d, int d_h,
+                                                     int n_v, int H_kv) {
+  const int c = blockIdx.y;
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= d) return;
+  const int rt = rot[c];
+  const int c0 = rt >> 5, n = 1 << (rt & 31), l = c - c0;
+  double acc = 0.0;
+  for (int j = 0; j < n; ++j) {
+    const int s = src[c0 + j];
+    const int g = s >> 16, k = s & 0xFFFF;
+    const float u = (g < H_kv) ? U_k[((size_t)g * d + i) * d_h + k] : U_v[(size_t)i * n_v + k];
+    acc += had_sign(j, l, (double)__fmul_rn(u, sp[c0 + j]));
+  }
+  store_dt<T>(A_t, (size_t)c * d + i, to_f32_kept(acc));
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_build_bk_rot(const float* __restrict__ V_k, const int* __restrict__ src,
+                                                      const int* __restrict__ rot, T* __restrict__ B_k, int n_key,
+                                                      int d_h) {
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= n_key * d_h) return;
+  const int c = idx / d_h, e = idx % d_h;
+  const int rt = rot[c];
+  const int c0 = rt >> 5, m = rt & 31, l = c - c0;
+  double acc = 0.0;
+  for (int j = 0; j < (1 << m); ++j) {
+    const int s = src[c0 + j];
+    const int g = s >> 16, k = s & 0xFFFF;
+    acc += had_sign(l, j, (double)V_k[((size_t)g * d_h + e) * d_h + k]);
+  }
+  store_dt<T>(B_k, idx, to_f32_kept(acc / (double)(1 << m)));
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_build_bv_rot(const float* __restrict__ V_v, const int* __restrict__ rot,
+                                                      T* __restrict__ B_vt, int rows, int r_v, int n_v, int n_key) {
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (size_t)rows * r_v) return;
+  const size_t jr = idx / r_v;
+  const int k = (int)(idx % r_v);
+  const int rt = rot[n_key + k];
+  const int k0 = (rt >> 5) - n_key, m = rt & 31, l = k - k0;
+  double acc = 0.0;
+  for (int j = 0; j < (1 << m); ++j) acc += had_sign(l, j, (double)V_v[jr * n_v + k0 + j]);
+  store_dt<T>(B_vt, idx, to_f32_kept(acc / (double)(1 << m)));
+}
+
+template <typename T>
+static hipError_t build_factors_rot(const Layer& L, const float* U_k, const float* V_k, const float* U_v,
+                                    const float* V_v, void* A_t, void* B_k, void* B_vt, hipStream_t s) {
+  dim3 ga((L.d + 255) / 256, L.n_lat);
+  hipLaunchKernelGGL(k_build_a_rot<T>, ga, dim3(256), 0, s, U_k, U_v, L.d_sp, L.d_src, L.d_rot, (T*)A_t, L.d, L.d_h,
+                     L.n_v, L.H_kv);
+  const int nbk = L.n_key * L.d_h;
+  hipLaunchKernelGGL(k_build_bk_rot<T>, dim3((nbk + 255) / 256), dim3(256), 0, s, V_k, L.d_src, L.d_rot, (T*)B_k,
+                     L.n_key, L.d_h);
+  const size_t nbv = (size_t)L.H_kv * L.d_h * L.r_v;
+  hipLaunchKernelGGL(k_build_bv_rot<T>, dim3((unsigned)((nbv + 255) / 256)), dim3(256), 0, s, V_v, L.d_rot,
+                     (T*)B_vt, L.H_kv * L.d_h, L.r_v, L.n_v, L.n_key);
+  return hipGetLastError();
+}
+
 template <typename T>
 static hipError_t build_factors_t(const Layer& L, const float* U_k, const float* V_k, const float* U_v,
                                   const float* V_v, void* A_t, void* B_k, void* B_vt, hipStream_t s) {
@@ -213,6 +330,7 @@ static hipError_t build_factors_t(const Layer& L, const float* U_k, const float*
 
 hipError_t launch_build_factors(const Layer& L, const float* U_k, const float* V_k, const float* U_v,
                                 const float* V_v, void* A_t, void* B_k, void* B_vt, hipStream_t s) {
+  if (L.had) return build_factors_rot<uint16_t>(L, U_k, V_k, U_v, V_v, A_t, B_k, B_vt, s);
   if (L.dtype == STARKV_F32) return build_factors_t<float>(L, U_k, V_k, U_v, V_v, A_t, B_k, B_vt, s);
   return build_factors_t<uint16_t>(L, U_k, V_k, U_v, V_v, A_t, B_k, B_vt, s);
 }

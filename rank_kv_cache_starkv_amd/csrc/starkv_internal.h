@@ -46,6 +46,11 @@ struct Layer {
   std::vector<int> koff, n8, n4, off8, off4;
   int K8 = 0, K4 = 0, V8 = 0, V4 = 0, n8v = 0, n4v = 0;
   int elem = 1;             // bytes per cache element (1 for mix84 codes)
+  // block-rotated 4-bit/3-bit quantiser (STARKV_LATENT_HAD43): kept in the mix84 byte format,
+  // so `latent` is MIX84 and this flag selects the outlier split, the code limits and the
+  // rotated factors
+  int had = 0;
+  int qmax_hi = 127, qmax_lo = 7;  // code limits of the int8 and int4 regions
   int k_row_bytes = 0, v_rows = 0, v_tile_bytes = 0;
   int key_slots = 0, val_slots = 0;  // columns of the append GEMM
   int key_kt = 0;           // K-positions per key-score K-tile (64 for int8 MFMA, 32 otherwise)
@@ -59,6 +64,7 @@ struct Layer {
   int* d_off4 = nullptr;
   float* d_sp = nullptr;       // [n_lat] kept singular value of each natural channel
   int* d_src = nullptr;        // [n_lat] (head << 16) | local index; head = H_kv for values
+  int* d_rot = nullptr;        // [n_lat] rotated factors: (first channel of the Hadamard piece << 5) | log2(order)
   uint32_t* d_absmax = nullptr;  // [n_lat] calibration scratch
   // bound buffers (borrowed)
   const void* A_t = nullptr;

@@ -90,7 +90,7 @@ def make_layer(w: I.Workload, exact: bool = False, layer: int = 0) -> Run:
 
 def calibrate(run: Run) -> None:
     w = run.w
-    if w.latent != "mix84":
+    if not O.is_quantized(w.latent):
         return
     Xc = I.x_calibration(w)
     Xc = I.snap_hidden(Xc) if run.exact else I.as_dtype(Xc, w.dtype)

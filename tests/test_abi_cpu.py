@@ -53,7 +53,7 @@ def _layer(cfg, **kw):
     return w, S.Layer(**args), ranks
 
 
-@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, 5])
 def test_ranks_and_layout_match_oracle(cfg):
     w, layer, ranks = _layer(cfg)
     s_k, tau_k, s_v, tau_v, _ = I.layer_spectra(w)
@@ -66,7 +66,8 @@ def test_ranks_and_layout_match_oracle(cfg):
     assert inf["v_tile_rows"] == fmt.v_rows
     assert inf["v_tile_bytes"] == fmt.v_tile_bytes
     assert inf["n_key"] == sum(exp) and inf["n_lat"] == sum(exp) + w.r_v
-    if w.latent == "mix84":
+    assert inf["latent"] == S.LATENT[w.latent]
+    if O.is_quantized(w.latent):
         assert (inf["K8"], inf["K4"], inf["V8"], inf["V4"]) == (fmt.K8, fmt.K4, fmt.V8, fmt.V4)
     kb, vb = layer.cache_bytes(w.B, 4096)
     assert kb == w.B * 4096 * fmt.k_row_bytes and vb == w.B * 128 * fmt.v_tile_bytes
@@ -106,6 +107,7 @@ def test_create_validation():
     assert status(tau_v=-1.0) == -1
     assert status(dtype="bf16", latent="f32") == -4
     assert status(dtype="f32", latent="mix84") == -4
+    assert status(dtype="f32", latent="had43") == -4
     assert status(d=250) == -4  # d not a multiple of 16
     assert status(d_h=48, s_k=np.ones((4, 48), np.float32)) == -4  # d_h not a multiple of 32
     assert status(tau_v=100.0) == -4  # r_v == 0
@@ -148,7 +150,7 @@ def test_hot_calls_reject_bad_arguments_without_launching():
     layer.close()
 
 
-@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, 5])
 def test_workspace_sizing(cfg):
     w, layer, _ = _layer(cfg)
     lens = I.context_lengths(w) + w.n_append

@@ -24,7 +24,7 @@ else:  # collected on CPU-only machines but never run there (marked gpu)
 
 # ---------------------------------------------------------------- factors and ranks, full shapes
 
-@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, 5])
 def test_ranks_and_factor_bits(cfg):
     w = I.WORKLOADS[cfg]
     H.log(f"[factors] cfg={cfg} {w.name}")
@@ -42,7 +42,7 @@ def test_ranks_and_factor_bits(cfg):
 
 def mini(cfg):
     w = I.WORKLOADS[cfg]
-    lens = {0: [256], 1: [300, 129], 2: [250, 70], 3: [1000], 4: [100, 33, 257]}[cfg]
+    lens = {0: [256], 1: [300, 129], 2: [250, 70], 3: [1000], 4: [100, 33, 257], 5: [250, 70]}[cfg]
     return w, lens
 
 
@@ -52,7 +52,7 @@ def _run_mini(cfg, exact, q_scale=1.0):
     H.log(f"[mini] cfg={cfg} {w.name} exact={exact} lens0={lens0} n_append={w.n_append} q_scale={q_scale}")
     run = H.make_layer(w, exact=exact)
     H.calibrate(run)
-    if exact and w.latent == "mix84":
+    if exact and O.is_quantized(w.latent):
         np.testing.assert_array_equal(H.dev_bits(run.GL.scales), run.scales_o.view(np.uint16))
     H.prefill(run, lens0, oracle_seqs=range(len(lens0)))
     if w.n_append:
@@ -76,7 +76,7 @@ def _compare_cache(run, exact):
             kc = O.unpack_key_rows(gk, run.fmt)
             vc = O.unpack_value_tiles(gv, run.fmt, T)
             okc, ovc = run.ocache[b].key, run.ocache[b].value
-            if w.latent == "mix84":
+            if O.is_quantized(w.latent):
                 dk, dv = np.abs(kc - okc), np.abs(vc - ovc)
                 H.log(f"  seq {b}: natural-run code mismatches key {int((dk > 0).sum())}/{dk.size}, "
                       f"value {int((dv > 0).sum())}/{dv.size}")
@@ -88,7 +88,7 @@ def _compare_cache(run, exact):
                 np.testing.assert_allclose(vc, ovc, rtol=tol, atol=tol * np.abs(ovc).max())
 
 
-@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, 5])
 @pytest.mark.parametrize("exact", [True, False])
 def test_mini_parity(cfg, exact):
     w, run = _run_mini(cfg, exact)
@@ -104,7 +104,7 @@ def test_mini_parity(cfg, exact):
         H.check_output(w, got[b], ref, f"seq {b} len {int(run.lens[b])}")
 
 
-@pytest.mark.parametrize("cfg", [0, 2, 4])
+@pytest.mark.parametrize("cfg", [0, 2, 4, 5])
 @pytest.mark.parametrize("q_scale", [30.0, 300.0])
 def test_mini_softmax_stress(cfg, q_scale):
     w, run = _run_mini(cfg, exact=True)
@@ -114,7 +114,7 @@ def test_mini_softmax_stress(cfg, q_scale):
         H.check_output(w, got[b], H.oracle_decode(run, q, b), f"q x{q_scale} seq {b}")
 
 
-@pytest.mark.parametrize("cfg", [0, 1, 2])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 5])
 def test_reconstruct(cfg):
     w, run = _run_mini(cfg, exact=True)
     b = 0
@@ -181,7 +181,7 @@ def _full(cfg):
     H.log(f"[full] cfg={cfg} {w.name} B={w.B} lens0 in [{lens0.min()}, {lens0.max()}] oracle seqs {sample}")
     run = H.make_layer(w, exact=True)
     H.calibrate(run)
-    if w.latent == "mix84":
+    if O.is_quantized(w.latent):
         np.testing.assert_array_equal(H.dev_bits(run.GL.scales), run.scales_o.view(np.uint16))
     H.prefill(run, lens0, oracle_seqs=sample, fast_fill=True)
     if w.n_append:
@@ -189,7 +189,7 @@ def _full(cfg):
     return w, run
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
 def test_full_size_sampled(cfg):
     w, run = _full(cfg)
     _compare_cache(run, True)
@@ -237,7 +237,7 @@ def test_graph_replay_matches_eager():
         torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("cfg", [0, 1, 2])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 5])
 @pytest.mark.parametrize("n_new", [1, 2])
 def test_append_few_tokens(cfg, n_new):
     """Appends of one or two tokens per sequence (the per-step append) on top of a prefill:
@@ -258,7 +258,7 @@ def test_append_few_tokens(cfg, n_new):
 # ---------------------------------------------------------------- the fused decode step
 
 @pytest.mark.parametrize("cfg,lens0", [(0, [256]), (1, [300, 129]), (2, [250, 70]), (3, [700]),
-                                       (4, [100, 33, 257]), (4, [100, 33, 257, 64, 90])])
+                                       (4, [100, 33, 257]), (4, [100, 33, 257, 64, 90]), (5, [250, 70])])
 def test_decode_step_equals_append_then_decode(cfg, lens0):
     """starkv_decode_step leaves the cache bytes and gives the output of compress_append followed
     by decode_attention, bit for bit: one fused launch for up to 16 new rows (cfg 0-3, and cfg 4

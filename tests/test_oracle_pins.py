@@ -187,17 +187,19 @@ def test_pack_golden():
     np.testing.assert_array_equal(vt, expect_v)
 
 
-@pytest.mark.parametrize("latent", ["mix84", "bf16", "f32"])
+@pytest.mark.parametrize("latent", ["mix84", "had43", "bf16", "f32"])
 def test_pack_round_trip(latent):
     rng = np.random.default_rng(5)
     ranks = (17, 3, 1, 30, 8)
     r_v = 45
     fmt = O.CacheFormat(latent, ranks, r_v)
     T = 70
-    if latent == "mix84":
-        qk = np.concatenate([[127] * O.mix84_split(r)[0] + [7] * O.mix84_split(r)[1] for r in ranks])
+    if O.is_quantized(latent):
+        # the full code range of each region: int8/int4 for mix84, 4-bit/3-bit for had43
+        hi, lo = (127, 7) if latent == "mix84" else (7, 3)
+        qk = np.concatenate([[hi] * fmt.split(r)[0] + [lo] * fmt.split(r)[1] for r in ranks])
         kc = rng.integers(-qk, qk + 1, size=(T, sum(ranks)))
-        qv = np.array([127] * O.mix84_split(r_v)[0] + [7] * O.mix84_split(r_v)[1])
+        qv = np.array([hi] * fmt.split(r_v)[0] + [lo] * fmt.split(r_v)[1])
         vc = rng.integers(-qv, qv + 1, size=(T, r_v))
     else:
         kc = O.stored_latent(rng.standard_normal((T, sum(ranks))).astype(np.float32), latent)
@@ -215,6 +217,112 @@ def test_format_sizes_match_accounting():
     fmt = O.CacheFormat("mix84", tuple([32] * 32), 1024)
     assert fmt.k_row_bytes == 640 and fmt.v_rows == 640
     assert acc.mean_bits(0.25, 8, 4) * 1024 / 8 == 640
+    # had43 in the same byte regions: the outlier fifth in bytes, the rest in nibbles = 4.8
+    # bits of storage per channel for ranks that are multiples of 5 (the codes carry 3.2)
+    fmt = O.CacheFormat("had43", tuple([40] * 32), 1280)
+    assert fmt.n8 == [8] * 32 and fmt.n4 == [32] * 32
+    assert fmt.k_row_bytes == 768 and fmt.v_rows == 256 + 512
+    assert acc.mean_bits(0.2, 8, 4) * 1280 / 8 == pytest.approx(768)
+
+
+# ---------------------------------------------------------------- block-wise Hadamard rotation (had43)
+
+def test_sylvester_is_the_library_hadamard():
+    import scipy.linalg
+    for n in (1, 2, 4, 8, 64, 512):
+        H = O.sylvester(n)
+        np.testing.assert_array_equal(H, scipy.linalg.hadamard(n))
+        np.testing.assert_array_equal(H @ H.T, n * np.eye(n, dtype=np.int64))
+    with pytest.raises(ValueError):
+        O.sylvester(12)
+
+
+def test_pow2_blocks_is_the_binary_decomposition():
+    assert O.pow2_blocks(13) == [8, 4, 1]
+    assert O.pow2_blocks(819) == [512, 256, 32, 16, 2, 1]
+    assert O.pow2_blocks(64) == [64]
+    assert O.pow2_blocks(0) == []
+    for n in range(1, 200):
+        p = O.pow2_blocks(n)
+        assert sum(p) == n and p == sorted(p, reverse=True) and len(set(p)) == len(p)
+
+
+def test_block_hadamard_hand_fixture():
+    # r = 7: the outlier block is ceil(7/5) = 2 channels (one H_2); the inlier block of 5 is
+    # cut into 4 + 1 (H_4, then H_1)
+    R, n = O.block_hadamard(7, O.had43_split(7)[0])
+    expect = np.array([[1, 1, 0, 0, 0, 0, 0],
+                       [1, -1, 0, 0, 0, 0, 0],
+                       [0, 0, 1, 1, 1, 1, 0],
+                       [0, 0, 1, -1, 1, -1, 0],
+                       [0, 0, 1, 1, -1, -1, 0],
+                       [0, 0, 1, -1, -1, 1, 0],
+                       [0, 0, 0, 0, 0, 0, 1]], dtype=np.float64)
+    np.testing.assert_array_equal(R, expect)
+    np.testing.assert_array_equal(n, [2, 2, 4, 4, 4, 4, 1])
+
+
+@pytest.mark.parametrize("r", [1, 5, 13, 16, 37, 64, 1024])
+def test_block_hadamard_inverse_pair_and_blocks(r):
+    n_hi = O.had43_split(r)[0]
+    R, n = O.block_hadamard(r, n_hi)
+    np.testing.assert_array_equal(R @ np.diag(1.0 / n) @ R.T, np.eye(r))
+    # the rotation never mixes the outlier block with the inlier block
+    assert not R[:n_hi, n_hi:].any() and not R[n_hi:, :n_hi].any()
+
+
+def test_had43_split_and_code_limits():
+    assert O.had43_split(16) == (4, 12)
+    assert O.had43_split(64) == (13, 51)
+    assert O.had43_split(5) == (1, 4)
+    assert O.had43_split(1) == (1, 0)
+    assert O.had43_split(1024) == (205, 819)
+    # symmetric b-bit codes reach 2^(b-1) - 1: 4-bit outliers, 3-bit inliers
+    assert O.code_limits("had43") == (2 ** 3 - 1, 2 ** 2 - 1)
+    assert O.code_limits("mix84") == (2 ** 7 - 1, 2 ** 3 - 1)
+    w = I.WORKLOADS[0]
+    lf = I.layer_factors(w, 0)
+    L = O.build_layer(lf.U_k, lf.s_k, lf.V_k, lf.tau_k, lf.U_v, lf.s_v, lf.V_v, lf.tau_v, w.H_q, "had43", "f32")
+    qm = O.channel_qmax(L)
+    c = 0
+    for r in list(L.ranks) + [L.r_v]:
+        n_hi = -(-int(r) // 5)
+        assert list(qm[c: c + n_hi]) == [7] * n_hi and list(qm[c + n_hi: c + int(r)]) == [3] * (int(r) - n_hi)
+        c += int(r)
+    assert c == len(qm)
+    # 3-bit ties and clamps: 2.5 -> 2 (even), 3.5 -> 4 -> 3, -3.5 -> -3, 1.5 -> 2
+    codes = O.quantize(np.array([2.5, 3.5, -3.5, 1.5, -0.5], np.float32), np.ones(5, np.float16), [3] * 5)
+    assert list(codes) == [2, 3, -3, 2, 0]
+
+
+def test_rotation_leaves_unquantised_attention_unchanged():
+    """A' B' = A B: with the latent left unquantised (fp32 factors and latent), the rotated
+    layer's attention equals the plain layer's up to the fp32 rounding of the factors."""
+    w = I.WORKLOADS[0]
+    lf = I.layer_factors(w, 0)
+    args = (lf.U_k, lf.s_k, lf.V_k, lf.tau_k, lf.U_v, lf.s_v, lf.V_v, lf.tau_v, w.H_q)
+    plain = O.build_layer(*args, "f32", "f32")
+    rot = O.build_layer(*args, "had43", "f32")
+    assert list(rot.ranks) == list(plain.ranks) and rot.r_v == plain.r_v
+    assert np.abs(rot.A_cat - plain.A_cat).max() > 0.1 * np.abs(plain.A_cat).max()  # not the identity
+    off = plain.key_offsets
+    for g in range(w.H_kv):
+        P0 = plain.A_cat[:, off[g]: off[g + 1]].astype(np.float64) @ plain.B_k[off[g]: off[g + 1]]
+        P1 = rot.A_cat[:, off[g]: off[g + 1]].astype(np.float64) @ rot.B_k[off[g]: off[g + 1]]
+        assert np.abs(P1 - P0).max() <= 1e-6 * np.abs(P0).max()
+    nk = plain.n_key
+    P0 = plain.A_cat[:, nk:].astype(np.float64) @ plain.B_v
+    P1 = rot.A_cat[:, nk:].astype(np.float64) @ rot.B_v
+    assert np.abs(P1 - P0).max() <= 1e-6 * np.abs(P0).max()
+    rng = np.random.default_rng(21)
+    X = rng.standard_normal((40, w.d)).astype(np.float32)
+    q = rng.standard_normal((1, w.H_q, w.d_h))
+    outs = []
+    for L in (plain, rot):
+        x = O.latent(X, L.A_cat).astype(np.float64)
+        K, V = O.reconstruct(x[:, :nk], x[:, nk:], L)
+        outs.append(O.attention(q, K, V, 1))
+    assert np.abs(outs[1] - outs[0]).max() <= 1e-5 * np.abs(outs[0]).max()
 
 
 # ---------------------------------------------------------------- latent (O4): exact-latent grid
@@ -342,7 +450,7 @@ def _frac_mat(a):
     return [[Fraction(float(v)) for v in row] for row in np.asarray(a, np.float64)]
 
 
-@pytest.mark.parametrize("latent", ["mix84", "f32"])
+@pytest.mark.parametrize("latent", ["mix84", "had43", "f32"])
 def test_brute_force_tiny(latent):
     rng = np.random.default_rng(12)
     w = I.Workload(9, "t", B=1, H_q=4, H_kv=2, d_h=4, d=12, n_q=2, latent=latent, dtype="f32",
@@ -354,7 +462,7 @@ def test_brute_force_tiny(latent):
     q = rng.standard_normal((w.n_q, w.H_q, w.d_h))
     qmax = O.channel_qmax(L)
     A = _frac_mat(L.A_cat)
-    if latent == "mix84":
+    if O.is_quantized(latent):
         sc = O.calibrate_scales(Xc, L.A_cat, qmax)
         bsc = brute.scales(_frac_mat(Xc), A, [int(v) for v in qmax])
         assert [Fraction(float(v)) for v in sc] == bsc
