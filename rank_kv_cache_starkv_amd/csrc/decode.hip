@@ -16,6 +16,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <numeric>
 #include <cstdlib>
 
 #include "device_common.h"
@@ -729,13 +730,16 @@ __global__ __launch_bounds__(256) void k_scores_chunk(ScoreArgs a) {
     const bool rowvalid = i < g.M_q;
     const int pos = len - g.n_q + (i % g.n_q);
     float rho = 1.f, bh = 0.f, bl = 0.f;
-    if (rowvalid) {
-      const float* rp = a.rowp + ((size_t)b * g.M_pad + i) * 4;
-      rho = rp[0];
-      bh = rp[1];
-      bl = rp[2];
+    if (LAT == STARKV_LATENT_MIX84) {
+      // row parameters at a clamped row (no branch around the load; padding rows are masked)
+      const u32x4 rp = ld16(a.rowp + ((size_t)b * g.M_pad + min(i, g.M_q - 1)) * 4);
+      rho = __uint_as_float(rp[0]);
+      bh = __uint_as_float(rp[1]);
+      bl = __uint_as_float(rp[2]);
     }
     const int nkt = a.kts.n[ct];
+    // this column tile's K-tile list (two runs), read once per unit
+    const int ks0 = a.kts.s0[ct], kn0 = a.kts.n0[ct], ks1 = a.kts.s1[ct];
     const uint8_t* fbase = a.qfrag + ((size_t)b * g.nct + ct) * a.nkt_max * 2048;
     const uint8_t* rowp[2];
     bool tok_ok[2];
@@ -747,28 +751,46 @@ __global__ __launch_bounds__(256) void k_scores_chunk(ScoreArgs a) {
     }
     float s2[2][4];
     if (LAT == STARKV_LATENT_MIX84) {
+      // key rows of sequence b as a buffer: each lane issues both an int8 and an int4 load and
+      // points the one it does not need (and every load of a masked token or K-tile) past the
+      // end, so no branch surrounds the loads
+      const __amdgpu_buffer_rsrc_t krs = buf_rsrc(kbase, (uint32_t)g.T_max * (uint32_t)g.k_row_bytes);
+      uint32_t trow[2];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) trow[tt] = (uint32_t)(t0 + tt * 16 + n) * (uint32_t)g.k_row_bytes;
       i32x4 ah[2], al[2];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) ah[tt] = al[tt] = i32x4{0, 0, 0, 0};
       for (int jt0 = 0; jt0 < nkt; jt0 += KU) {
         i32x4 fh[KU], fl[KU], av[KU][2];
+        u32x4 r8[KU][2];
+        u32x2 r4[KU][2];
+        bool is8[KU], is4[KU];
 #pragma unroll
         for (int j = 0; j < KU; ++j) {
           const bool on = jt0 + j < nkt;
-          const int kt = on ? a.kts.at(ct, jt0 + j) : 0;
+          const int jc = on ? jt0 + j : 0;
+          const int kt = jc < kn0 ? ks0 + jc : ks1 + (jc - kn0);
           const int P0 = kt * 64 + 16 * qq;
-          fh[j] = on ? __builtin_bit_cast(i32x4, ld16(fbase + (jt0 + j) * 2048 + lane * 16)) : i32x4{0, 0, 0, 0};
-          fl[j] = on ? __builtin_bit_cast(i32x4, ld16(fbase + (jt0 + j) * 2048 + 1024 + lane * 16)) : i32x4{0, 0, 0, 0};
+          is8[j] = on && P0 < g.K8;
+          is4[j] = on && P0 >= g.K8 && P0 < g.K8 + g.K4;
+          fh[j] = __builtin_bit_cast(i32x4, ld16(fbase + jc * 2048 + lane * 16));
+          fl[j] = __builtin_bit_cast(i32x4, ld16(fbase + jc * 2048 + 1024 + lane * 16));
+          const uint32_t o8 = (uint32_t)P0, o4 = (uint32_t)(g.K8 + (P0 - g.K8) / 2);
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt) {
-            i32x4 v = {0, 0, 0, 0};
-            if (on && tok_ok[tt]) {
-              if (P0 < g.K8) v = __builtin_bit_cast(i32x4, ld16(rowp[tt] + P0));
-              else if (P0 < g.K8 + g.K4) v = unpack_int4_group(ld8(rowp[tt] + g.K8 + (P0 - g.K8) / 2));
-            }
-            av[j][tt] = v;
+            r8[j][tt] = bld16(krs, (is8[j] && tok_ok[tt]) ? trow[tt] + o8 : kOOB);
+            r4[j][tt] = bld8(krs, (is4[j] && tok_ok[tt]) ? trow[tt] + o4 : kOOB);
           }
         }
+        __builtin_amdgcn_sched_barrier(0);  // every load of the batch ahead of its use
+#pragma unroll
+        for (int j = 0; j < KU; ++j)
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt)
+            // (a K-tile past nkt has neither flag: zero operand; masked tokens are masked below)
+            av[j][tt] = is8[j] ? __builtin_bit_cast(i32x4, r8[j][tt])
+                               : (is4[j] ? unpack_int4_group(r4[j][tt]) : i32x4{0, 0, 0, 0});
 #pragma unroll
         for (int j = 0; j < KU; ++j)
 #pragma unroll
@@ -2267,7 +2289,9 @@ static hipError_t launch_decode_tail(const Layer& L, const DecodePlan& plan, con
     if (L.latent == STARKV_LATENT_MIX84) {
       // int8/int4 keys: work unit = (column tile, 32-token chunk), enough chunks per workgroup
       // that each of its four waves has a unit
-      sa.nch_wg = std::max(1, 4 / std::min(g.nct, 4));
+      // chunks per workgroup: the smallest count that gives the four waves equal numbers of
+      // (column tile, chunk) units
+      sa.nch_wg = 4 / std::gcd(g.nct, 4);
       const int n_wg = (w.total_chunks + sa.nch_wg - 1) / sa.nch_wg;
       e = launch_k(ps, k_scores_chunk<STARKV_LATENT_MIX84>, dim3(n_wg), dim3(256), s, sa);
     } else {
