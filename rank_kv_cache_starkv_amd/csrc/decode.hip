@@ -440,6 +440,36 @@ __device__ __forceinline__ int seq_blk0(const SeqTable& t, int b) { return t.uni
 __device__ __forceinline__ int seq_of_split(const SeqTable& t, int B, int sg) {
   return t.uni ? sg / t.u_nspl : find_segment_wave(t.split_off, B, sg);
 }
+// Order in which the value workgroups take the splits: every split that is not the last of its
+// sequence (all of full length) first, then the last split of each sequence (the only ones that
+// may be short), so that with ragged lengths the short workgroups run at the end of the grid
+// instead of full ones.  Every sequence has at least one split.  Returns the split of position
+// idx and sets b to its sequence (call with the whole wave active).
+__device__ __forceinline__ int value_split(const SeqTable& t, int B, int idx, int& b) {
+  if (t.uni) {
+    const int nn = t.u_nspl - 1;  // splits per sequence that are not its last
+    const int n_nl = B * nn;
+    if (idx < n_nl) {
+      b = idx / nn;
+      return b * t.u_nspl + idx % nn;
+    }
+    b = idx - n_nl;
+    return b * t.u_nspl + nn;
+  }
+  const int n_nl = t.split_off[B] - B;
+  if (idx < n_nl) {
+    // non-last splits before sequence b': split_off[b'] - b' (non-decreasing in b'); b is the
+    // largest b' < B with that count <= idx, and the split is idx + b
+    const int lane = threadIdx.x & 63;
+    const int i0 = min(lane + 1, B), i1 = min(lane + 65, B);
+    const unsigned long long m0 = __ballot(lane + 1 < B && t.split_off[i0] - i0 <= idx);
+    const unsigned long long m1 = __ballot(lane + 65 < B && t.split_off[i1] - i1 <= idx);
+    b = __builtin_amdgcn_readfirstlane(__popcll(m0) + __popcll(m1));
+    return idx + b;
+  }
+  b = idx - n_nl;
+  return t.split_off[b + 1] - 1;
+}
 __device__ __forceinline__ int seq_of_blk(const SeqTable& t, int B, int k) {
   return t.uni ? k / t.u_nblk : find_segment_wave(t.blk_off, B, k);
 }
@@ -1476,9 +1506,10 @@ __global__ __launch_bounds__(256) void k_values_mt(ValueArgs a) {
   const int r = lane & 31, q = lane >> 5;
   const int xcd = blockIdx.x & 7, kk = blockIdx.x >> 3;
   const int grp = kk % a.n_sl;
-  const int sg = 8 * (kk / a.n_sl) + xcd;
-  if (sg >= a.n_splits) return;
-  const int b = seq_of_split(a.seq, g.B, sg);
+  const int idx = 8 * (kk / a.n_sl) + xcd;
+  if (idx >= a.n_splits) return;
+  int b;
+  const int sg = value_split(a.seq, g.B, idx, b);
   const int s = sg - seq_split0(a.seq, b);
   const int cbase = seq_chunk0(a.seq, b);
   const int nch = seq_nch(a.seq, b);
