@@ -977,23 +977,31 @@ __device__ __forceinline__ float rel_weight(float m, float ref) {
 
 // 8 tokens of one channel (int8 codes in 8 bytes) -> f16x8
 __device__ __forceinline__ f16x8 deq_i8x8(uint32_t w0, uint32_t w1) {
-  f16x8 r;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    r[e] = (_Float16)sbyte(w0, e);
-    r[4 + e] = (_Float16)sbyte(w1, e);
-  }
-  return r;
+  // exact: a byte b in offset binary (b ^ 0x80) is the low mantissa of the half 0x6400 | u =
+  // 1024 + u, and one packed subtraction of 1024 + 128 gives the code; bytes 2k, 2k + 1 of a word
+  // go to the two halves of one dword by a byte permute (zeros between them)
+  const u32x4 u = {__builtin_amdgcn_perm(0u, w0, 0x0C010C00u) ^ 0x64806480u,
+                   __builtin_amdgcn_perm(0u, w0, 0x0C030C02u) ^ 0x64806480u,
+                   __builtin_amdgcn_perm(0u, w1, 0x0C010C00u) ^ 0x64806480u,
+                   __builtin_amdgcn_perm(0u, w1, 0x0C030C02u) ^ 0x64806480u};
+  return __builtin_bit_cast(f16x8, u) - (_Float16)1152.0f;
+}
+// 8 tokens of one channel of an int4 pair (8 bytes; the even channel in the low nibbles, the odd
+// one in the high nibbles; `odd` picks which), exactly: the nibble in offset binary (n ^ 8) is
+// the low mantissa of the half 0x6400 | u, minus 1024 + 8
+__device__ __forceinline__ f16x8 deq_i4x8_half(uint32_t w0, uint32_t w1, bool odd) {
+  const int sh = odd ? 4 : 0;
+  const uint32_t a = w0 >> sh, b = w1 >> sh;
+  const u32x4 u = {(__builtin_amdgcn_perm(0u, a, 0x0C010C00u) & 0x000F000Fu) ^ 0x64086408u,
+                   (__builtin_amdgcn_perm(0u, a, 0x0C030C02u) & 0x000F000Fu) ^ 0x64086408u,
+                   (__builtin_amdgcn_perm(0u, b, 0x0C010C00u) & 0x000F000Fu) ^ 0x64086408u,
+                   (__builtin_amdgcn_perm(0u, b, 0x0C030C02u) & 0x000F000Fu) ^ 0x64086408u};
+  return __builtin_bit_cast(f16x8, u) - (_Float16)1032.0f;
 }
 // 8 tokens of a channel pair (8 bytes): low nibbles -> even channel, high -> odd channel
 __device__ __forceinline__ void deq_i4x8(uint32_t w0, uint32_t w1, f16x8& ev, f16x8& od) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    ev[e] = (_Float16)snib(w0, 2 * e);
-    od[e] = (_Float16)snib(w0, 2 * e + 1);
-    ev[4 + e] = (_Float16)snib(w1, 2 * e);
-    od[4 + e] = (_Float16)snib(w1, 2 * e + 1);
-  }
+  ev = deq_i4x8_half(w0, w1, false);
+  od = deq_i4x8_half(w0, w1, true);
 }
 
 // Workgroup = (slice of `bpw` value blocks, split of one sequence); wave = one value block
@@ -1661,13 +1669,9 @@ __global__ __launch_bounds__(256) void k_values_mt(ValueArgs a) {
         if (LAT == STARKV_LATENT_BF16) {
           bfrag = vf[j][h % NV];
         } else {
-          f16x8 ev, od;
-          if (is4[j]) {
-            deq_i4x8(vf[j][0][2 * h], vf[j][0][2 * h + 1], ev, od);
-            if (par[j]) ev = od;
-          } else {
-            ev = deq_i8x8(vf[j][0][2 * h], vf[j][0][2 * h + 1]);
-          }
+          f16x8 ev;
+          if (is4[j]) ev = deq_i4x8_half(vf[j][0][2 * h], vf[j][0][2 * h + 1], par[j]);
+          else ev = deq_i8x8(vf[j][0][2 * h], vf[j][0][2 * h + 1]);
           bfrag = __builtin_bit_cast(u32x4, ev);
         }
 #pragma unroll
