@@ -1818,89 +1818,102 @@ __global__ __launch_bounds__(256) void k_zmerge(MergeArgs a) {
   st16(a.zt + ((size_t)b * g.M_pad + i) * g.rv_ld + c, o);
 }
 
-// Up-projection for many rows per KV head (bf16, r_v % 8 == 0): workgroup = (g, 64-row tile of
-// g's rows over all sequences); wave w takes the 32-column slices w, w + 4, ... of d_h over two
-// 32-row tiles (32x32x16 bf16 MFMA, z~ split into hi + lo bf16 parts).  Each workgroup reads its
-// rows of z~ and g's B_v^T slab once from memory (the four waves share them through the caches).
-// Loads are unconditional: rows past the end read the last row (not stored); channels at or past
-// r_v are zero in z~ and masked in B_v (their address clamped into the row).
-__global__ __launch_bounds__(256) void k_upproj_tall(MergeArgs a) {
-  constexpr int KB = 4;  // 16-channel K-steps per load batch
+// Up-projection for many rows per KV head (bf16, r_v % 8 == 0): workgroup = (g, 32-row tile of
+// g's rows over all sequences), all d_h columns, four 32-column slices at a time.  Wave w takes a
+// quarter of K = rv_ld (16-channel steps) for every column, so each element of z~ and of g's
+// B_v^T slab is read and split into hi + lo bf16 parts once per workgroup; the four partial tiles
+// are added through LDS, wave w finishing column slice w (32x32x16 bf16 MFMA).  Loads are
+// unconditional and double-buffered: rows past the end read the last row (not stored); channels at
+// or past r_v are zero in z~ and masked in B_v (their address clamped into the row).
+__global__ __launch_bounds__(256, 2) void k_upproj_tall(MergeArgs a) {
+  constexpr int KB = 1;   // 16-channel K-steps per load batch
+  constexpr int NCS = 4;  // 32-column slices per pass
+  __shared__ float part[4][NCS][16][64];  // [wave][column slice][D element][lane]
   const DecodeGeom& g = a.g;
   const int gk = blockIdx.x;
   const int rph = g.G * g.n_q;
   const int Rg = g.B * rph;
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int r = lane & 31, q = lane >> 5;
-  const float* zr[2];
+  const int rr = min((int)blockIdx.y * 32 + r, Rg - 1);
+  const float* zr = a.zt + ((size_t)(rr / rph) * g.M_pad + gk * rph + rr % rph) * g.rv_ld + 8 * q;
+  const int nks = g.rv_ld / 16;
+  const int kq = (nks + 3) / 4;
+  const int k_beg = min(nks, wave * kq), k_end = min(nks, k_beg + kq);
+  const int ncs = g.d_h / 32;
+  for (int cs0 = 0; cs0 < ncs; cs0 += NCS) {
+    const uint16_t* bp[NCS];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-    const int rr = min((int)blockIdx.y * 64 + mt * 32 + r, Rg - 1);
-    zr[mt] = a.zt + ((size_t)(rr / rph) * g.M_pad + gk * rph + rr % rph) * g.rv_ld + 8 * q;
-  }
-  for (int cs = wave; cs < g.d_h / 32; cs += 4) {
-    const uint16_t* bp = (const uint16_t*)a.B_vt + (size_t)(gk * g.d_h + cs * 32 + r) * g.r_v;
-    f32x16 acc[2];
+    for (int c = 0; c < NCS; ++c)
+      bp[c] = (const uint16_t*)a.B_vt + (size_t)(gk * g.d_h + min(cs0 + c, ncs - 1) * 32 + r) * g.r_v;
+    f32x16 acc[NCS];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int c = 0; c < NCS; ++c)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[mt][v] = 0.f;
-    // K loop double-buffered: the loads of batch i + 1 are issued before the MFMAs of batch i
-    auto loadb = [&](u32x4 (&z)[KB][2][2], u32x4 (&bw)[KB], int k0) {
-#pragma unroll
-      for (int u = 0; u < KB; ++u) {
-        const int kc = min(k0 + 16 * u, g.rv_ld - 16);
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          z[u][mt][0] = ld16(zr[mt] + kc);
-          z[u][mt][1] = ld16(zr[mt] + kc + 4);
-        }
-        bw[u] = ld16(bp + min(kc + 8 * q, g.r_v - 8));
-      }
-    };
-    auto compb = [&](u32x4 (&z)[KB][2][2], u32x4 (&bw)[KB], int k0) {
+      for (int v = 0; v < 16; ++v) acc[c][v] = 0.f;
+    auto loadb = [&](u32x4 (&z)[KB][2], u32x4 (&bw)[KB][NCS], int ks0) {
 #pragma unroll
       for (int u = 0; u < KB; ++u) {
-        const int kc = k0 + 16 * u;
-        const bool live = kc < g.rv_ld && kc + 8 * q < g.r_v;
-        const u32x4 bb = live ? bw[u] : u32x4{0, 0, 0, 0};
+        const int kc = 16 * min(ks0 + u, nks - 1);
+        z[u][0] = ld16(zr + kc);
+        z[u][1] = ld16(zr + kc + 4);
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          u32x4 ah, al;
+        for (int c = 0; c < NCS; ++c) bw[u][c] = ld16(bp[c] + min(kc + 8 * q, g.r_v - 8));
+      }
+    };
+    auto compb = [&](u32x4 (&z)[KB][2], u32x4 (&bw)[KB][NCS], int ks0) {
 #pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2) {
-            const float z0 = __uint_as_float(z[u][mt][e2 >> 1][2 * (e2 & 1)]);
-            const float z1 = __uint_as_float(z[u][mt][e2 >> 1][2 * (e2 & 1) + 1]);
-            const uint16_t h0 = f32_to_bf16(z0), h1 = f32_to_bf16(z1);
-            const uint16_t l0 = f32_to_bf16(z0 - bf16_to_f32(h0)), l1 = f32_to_bf16(z1 - bf16_to_f32(h1));
-            ah[e2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-            al[e2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
-          }
-          acc[mt] = mfma32_bf16(as_bf16x8(ah), as_bf16x8(bb), acc[mt]);
-          acc[mt] = mfma32_bf16(as_bf16x8(al), as_bf16x8(bb), acc[mt]);
+      for (int u = 0; u < KB; ++u) {
+        const int kc = 16 * (ks0 + u);
+        const bool live = ks0 + u < k_end && kc + 8 * q < g.r_v;
+        u32x4 ah, al;
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const float z0 = __uint_as_float(z[u][e2 >> 1][2 * (e2 & 1)]);
+          const float z1 = __uint_as_float(z[u][e2 >> 1][2 * (e2 & 1) + 1]);
+          const uint16_t h0 = f32_to_bf16(z0), h1 = f32_to_bf16(z1);
+          const uint16_t l0 = f32_to_bf16(z0 - bf16_to_f32(h0)), l1 = f32_to_bf16(z1 - bf16_to_f32(h1));
+          ah[e2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+          al[e2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+        }
+#pragma unroll
+        for (int c = 0; c < NCS; ++c) {
+          const u32x4 bb = live ? bw[u][c] : u32x4{0, 0, 0, 0};
+          acc[c] = mfma32_bf16(as_bf16x8(ah), as_bf16x8(bb), acc[c]);
+          acc[c] = mfma32_bf16(as_bf16x8(al), as_bf16x8(bb), acc[c]);
         }
       }
     };
-    u32x4 zA[KB][2][2], bA[KB], zB[KB][2][2], bB[KB];
-    loadb(zA, bA, 0);
-    for (int k0 = 0; k0 < g.rv_ld; k0 += 32 * KB) {
-      loadb(zB, bB, k0 + 16 * KB);
-      compb(zA, bA, k0);
-      if (k0 + 16 * KB >= g.rv_ld) break;
-      loadb(zA, bA, k0 + 32 * KB);
-      compb(zB, bB, k0 + 16 * KB);
+    u32x4 zA[KB][2], bA[KB][NCS], zB[KB][2], bB[KB][NCS];
+    loadb(zA, bA, k_beg);
+    for (int ks = k_beg; ks < k_end; ks += 2 * KB) {
+      loadb(zB, bB, ks + KB);
+      compb(zA, bA, ks);
+      if (ks + KB >= k_end) break;
+      loadb(zA, bA, ks + 2 * KB);
+      compb(zB, bB, ks + KB);
     }
+    // the four K-quarters of every column slice, added by the wave that finishes that slice
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int c = 0; c < NCS; ++c)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) part[wave][c][v][lane] = acc[c][v];
+    __syncthreads();
+    const int cs = cs0 + wave;
+    if (cs < ncs) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int orow = blockIdx.y * 64 + mt * 32 + d32_row(v, q);
+        const float o = part[0][wave][v][lane] + part[1][wave][v][lane] + part[2][wave][v][lane] +
+                        part[3][wave][v][lane];
+        const int orow = blockIdx.y * 32 + d32_row(v, q);
         if (orow >= Rg) continue;
         const int ob = orow / rph, iw = orow % rph;
         const int hh = iw / g.n_q, j = iw % g.n_q;
         const int h = gk * g.G + hh;
-        ((uint16_t*)a.out)[(((size_t)ob * g.n_q + j) * g.H_q + h) * g.d_h + cs * 32 + r] = f32_to_bf16(acc[mt][v]);
+        ((uint16_t*)a.out)[(((size_t)ob * g.n_q + j) * g.H_q + h) * g.d_h + cs * 32 + r] = f32_to_bf16(o);
       }
+    }
+    __syncthreads();  // the partial tiles are reused by the next pass
   }
 }
 
@@ -2421,7 +2434,7 @@ static hipError_t launch_decode_tail(const Layer& L, const DecodePlan& plan, con
     ProfScope ps("decode_upproj");
     const dim3 gm(g.H_kv * (g.d_h / 16), (Rg + 15) / 16);
     if (tall)
-      e = launch_k(ps, k_upproj_tall, dim3(g.H_kv, (Rg + 63) / 64), dim3(256), s, ma);
+      e = launch_k(ps, k_upproj_tall, dim3(g.H_kv, (Rg + 31) / 32), dim3(256), s, ma);
     else if (L.dtype == STARKV_F32)
       e = vec ? launch_k(ps, k_upproj<STARKV_F32, true>, gm, dim3(256), s, ma)
               : launch_k(ps, k_upproj<STARKV_F32, false>, gm, dim3(256), s, ma);
