@@ -1739,9 +1739,9 @@ struct MergeArgs {
 // largest m_s: z~[c] = (sum_s 2^(m_s - M) z_s[c]) * scale_c / (sum_s 2^(m_s - M) l_s), and zero in
 // the padding channels [r_v, rv_ld).  Workgroup = 4 rows x (256 / nsp) channels of one sequence;
 // nsp adjacent lanes (1 or 4) share 4 channels and take every nsp-th split each, all their loads
-// issued at once (16 splits per batch), keep a running maximum (rescaling their sums when it
+// issued at once (NB splits per batch), keep a running maximum (rescaling their sums when it
 // grows), and combine by lane exchange in a fixed order, so the result is deterministic.
-template <bool MIX>
+template <bool MIX, int NB>
 __global__ __launch_bounds__(256) void k_zmerge(MergeArgs a) {
   const DecodeGeom& g = a.g;
   const int nsp = a.nsp;
@@ -1766,27 +1766,27 @@ __global__ __launch_bounds__(256) void k_zmerge(MergeArgs a) {
   float z[4] = {0.f, 0.f, 0.f, 0.f};
   float l = 0.f;
   float M = -INFINITY;  // reference of z and l: the largest split maximum seen so far
-  for (int s = sp; s < ns; s += 16 * nsp) {
-    u32x4 v[16];
-    float lv[16], mv[16];
+  for (int s = sp; s < ns; s += NB * nsp) {
+    u32x4 v[NB];
+    float lv[NB], mv[NB];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
+    for (int u = 0; u < NB; ++u) {
       const int ss = min(s + u * nsp, ns - 1);
       v[u] = ld16(zc + (size_t)ss * zs);
       lv[u] = lc[(size_t)ss * g.M_pad];
       mv[u] = mc[(size_t)ss * g.M_pad];
     }
-    __builtin_amdgcn_sched_barrier(0);  // all 48 loads go out before the first add
+    __builtin_amdgcn_sched_barrier(0);  // all 3 NB loads go out before the first add
     float Mn = M;
 #pragma unroll
-    for (int u = 0; u < 16; ++u)
+    for (int u = 0; u < NB; ++u)
       if (s + u * nsp < ns) Mn = fmaxf(Mn, mv[u]);
     const float f0 = rel_weight(M, Mn);
 #pragma unroll
     for (int e = 0; e < 4; ++e) z[e] *= f0;
     l *= f0;
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
+    for (int u = 0; u < NB; ++u) {
       if (s + u * nsp < ns) {
         const float w = rel_weight(mv[u], Mn);
 #pragma unroll
@@ -2427,7 +2427,13 @@ static hipError_t launch_decode_tail(const Layer& L, const DecodePlan& plan, con
     ProfScope ps("decode_zmerge");
     ma.nsp = max_ns > 8 ? 4 : 1;
     const dim3 gz((g.rv_ld + 256 / ma.nsp - 1) / (256 / ma.nsp), (g.M_q + 3) / 4, g.B);
-    e = L.mix() ? launch_k(ps, k_zmerge<true>, gz, dim3(256), s, ma) : launch_k(ps, k_zmerge<false>, gz, dim3(256), s, ma);
+    // loads per batch: 4 when no sequence has more splits (one batch), else 16
+    if (max_ns <= 4)
+      e = L.mix() ? launch_k(ps, k_zmerge<true, 4>, gz, dim3(256), s, ma)
+                  : launch_k(ps, k_zmerge<false, 4>, gz, dim3(256), s, ma);
+    else
+      e = L.mix() ? launch_k(ps, k_zmerge<true, 16>, gz, dim3(256), s, ma)
+                  : launch_k(ps, k_zmerge<false, 16>, gz, dim3(256), s, ma);
     if (e != hipSuccess) return e;
   }
   {
