@@ -346,6 +346,26 @@ def test_many_rows_per_kv_head_mix84():
         H.check_output(w, got[b], ref, f"seq {b} len {int(run.lens[b])}")
 
 
+@pytest.mark.parametrize("cfg", [1, 4])
+def test_many_sequences(cfg):
+    """32 short sequences of distinct lengths (1024 or more KV-head x sequence pairs, many score
+    workgroups spanning sequence boundaries) against the oracle on the first, a middle and the last
+    sequence."""
+    lens0 = [40 + 7 * i for i in range(32)]
+    w = dataclasses.replace(I.WORKLOADS[cfg], B=len(lens0))
+    H.log(f"[many sequences] cfg={cfg} B={w.B} pairs={w.B * w.H_kv}")
+    run = H.make_layer(w, exact=True)
+    H.calibrate(run)
+    H.prefill(run, lens0, oracle_seqs=(0, 13, 31), fast_fill=True)
+    if w.n_append:
+        H.append_step(run, w.n_append)
+    q = H.queries(run)
+    got = H.from_dev(H.decode(run, q))
+    for b in run.oracle_seqs:
+        ref = H.oracle_decode(run, q, b, mode="latent")
+        H.check_output(w, got[b], ref, f"seq {b} len {int(run.lens[b])}")
+
+
 def test_many_rows_many_splits():
     """64 query rows per KV head (8 sequences x 8 queries, bf16) with a sequence long enough for
     more than four value splits: the separate split merge, then the tall up-projection."""
