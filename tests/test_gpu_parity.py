@@ -297,7 +297,7 @@ def test_decode_step_equals_append_then_decode(cfg, lens0):
     H.check_output(w, H.from_dev(out_b)[0], ref, f"seq 0 len {int(run.lens[0])}")
 
 
-@pytest.mark.parametrize("cfg,n_q", [(0, 9), (1, 2), (1, 3), (2, 2)])
+@pytest.mark.parametrize("cfg,n_q", [(0, 9), (1, 2), (1, 3), (2, 2), (5, 2), (5, 4)])
 def test_many_query_rows(cfg, n_q):
     """More than 32 query rows per sequence (n_q queries x H_q heads): the staged many-row value
     kernel (bf16, int8/int4) and the general one (fp32) against the oracle, causal within the
