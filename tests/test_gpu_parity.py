@@ -297,6 +297,39 @@ def test_decode_step_equals_append_then_decode(cfg, lens0):
     H.check_output(w, H.from_dev(out_b)[0], ref, f"seq 0 len {int(run.lens[0])}")
 
 
+@pytest.mark.parametrize("cfg", [4, 5])
+def test_decode_step_many_rows_natural(cfg):
+    """starkv_decode_step with more than 16 new rows (10 sequences x 4 queries: the tiled append,
+    then the decode) on unsnapped inputs: the new tokens' codes against the oracle's (differences
+    of one code, at most at rounding ties) and the output within the bf16 bar."""
+    lens0 = [60, 33, 100, 75, 41, 90, 128, 64, 50, 81]
+    w = dataclasses.replace(I.WORKLOADS[cfg], B=len(lens0), n_q=4)
+    H.log(f"[step many rows natural] cfg={cfg} B={w.B} rows={w.B * w.n_q}")
+    run = H.make_layer(w, exact=False)
+    H.calibrate(run)
+    H.prefill(run, lens0, oracle_seqs=(0, 6, 9))
+    lens_pre = run.lens.copy()
+    Xn_np = H.hidden(run, I.x_new(w, w.n_q, step=5))
+    run.lens = lens_pre + w.n_q
+    q_np = H.queries(run, step=5)
+    out = run.GL.step(run.cache, H.to_dev(Xn_np, w.dtype), H.to_dev(q_np, w.dtype), run.lens)
+    torch.cuda.synchronize()
+    got = H.from_dev(out)
+    for b in run.oracle_seqs:
+        oc = O.compress(Xn_np[b], run.OL, run.scales_o)
+        old = run.ocache[b]
+        run.ocache[b] = O.SequenceCache(np.concatenate([old.key, oc.key]), np.concatenate([old.value, oc.value]))
+        gk, gv = H.gpu_seq_cache(run, b)
+        T = int(run.lens[b])
+        kc = O.unpack_key_rows(gk, run.fmt)[T - w.n_q: T]
+        vc = O.unpack_value_tiles(gv, run.fmt, T)[T - w.n_q: T]
+        dk, dv = np.abs(kc - oc.key), np.abs(vc - oc.value)
+        H.log(f"  seq {b}: new-token code mismatches key {int((dk > 0).sum())}/{dk.size}, value {int((dv > 0).sum())}/{dv.size}")
+        assert dk.max() <= 1 and dv.max() <= 1
+        assert (dk > 0).mean() < 1e-2 and (dv > 0).mean() < 1e-2
+        H.check_output(w, got[b], H.oracle_decode(run, q_np, b, mode="latent"), f"seq {b} len {T}")
+
+
 @pytest.mark.parametrize("cfg,n_q", [(0, 9), (1, 2), (1, 3), (2, 2), (5, 2), (5, 4)])
 def test_many_query_rows(cfg, n_q):
     """More than 32 query rows per sequence (n_q queries x H_q heads): the staged many-row value
