@@ -241,8 +241,8 @@ def main() -> int:
     if args.copy_probe:
         return copy_probe()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the build targets a single "
-              f"MI355X; multi-GPU sharding is described in DESIGN.md, not built)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the library runs on a single "
+              f"MI355X; sharding across GPUs by sequence, KV head or context is not built)", file=sys.stderr)
         return 2
 
     import torch
