@@ -83,7 +83,7 @@ extern "C" {
                                  mix84 byte format: outliers in the int8 region, inliers in
                                  the int4 region (dtype BF16). */
 
-/* limits of this build */
+/* limits of the library */
 #define STARKV_MAX_BATCH 128     /* sequences per call */
 #define STARKV_MAX_QROWS 256     /* H_q * n_q per sequence */
 #define STARKV_TILE_TOKENS 32    /* tokens per value tile */
