@@ -35,6 +35,78 @@ static int env_int(const char* name, int dflt) {
   return atoi(v);
 }
 
+// Value splits of a ragged batch in XCD order.  The value workgroups go to the eight XCDs in turn
+// by grid position, and each XCD runs its share on its own 32 CUs, so an order that ignores the
+// split lengths can leave one XCD with far more work than another.  Deal the splits (cps chunks
+// each, the last of a sequence shorter) longest first, each to the XCD with the least work so far
+// (the n_sl workgroups of a split stay on one XCD and share its L2), and estimate the time as the
+// latest per-XCD finish when each XCD's workgroups, in that order, are list-scheduled onto its
+// workgroup slots at a cost of (chunks + a fixed overhead).  Returns the estimate in chunk units,
+// or -1 when the order needs more than kMaxVPos grid positions; fills *vo when given.  The
+// estimate stops early (returning a value above `limit`) once it exceeds `limit`.
+constexpr float kWgOvh = 2.f;  // fixed cost of a value workgroup, in chunks
+static double order_splits(const SeqTable& seq, int B, int cps, int n_sl, ValueOrder* vo, float limit = 1e30f) {
+  constexpr int kXcd = 8, kSlots = 64;  // 32 CUs per XCD, two value workgroups on each
+  std::vector<std::pair<int, int>> sp;  // (-chunks, split)
+  for (int b = 0, sg = 0; b < B; ++b) {
+    const int nc = seq.chunk_off[b + 1] - seq.chunk_off[b];
+    for (int c0 = 0; c0 < nc; c0 += cps) sp.emplace_back(-std::min(cps, nc - c0), sg++);
+  }
+  const int n = (int)sp.size();
+  if (ceil_div(n, kXcd) * kXcd > kMaxVPos) return -1;
+  std::sort(sp.begin(), sp.end());  // longest first, then by split
+  float load[kXcd] = {};
+  int cnt[kXcd] = {};
+  std::vector<uint8_t> xcd_of(n);
+  for (int i = 0; i < n; ++i) {
+    int x = 0;
+    for (int y = 1; y < kXcd; ++y)
+      if (load[y] < load[x]) x = y;
+    xcd_of[i] = (uint8_t)x;
+    ++cnt[x];
+    load[x] += (float)(-sp[i].first) + kWgOvh;
+  }
+  const int n_pos = kXcd * *std::max_element(cnt, cnt + kXcd);
+  if (n_pos > kMaxVPos) return -1;
+  // no XCD can finish before its work spread evenly over its slots
+  const float lb = *std::max_element(load, load + kXcd) * n_sl / kSlots;
+  if (!vo && lb > limit) return lb;
+  float span = 0.f;
+  for (int x = 0; x < kXcd; ++x) {
+    float heap[kSlots] = {};  // slot free times, a binary min-heap
+    for (int i = 0; i < n; ++i) {
+      if (xcd_of[i] != x) continue;
+      const float d = (float)(-sp[i].first) + kWgOvh;
+      for (int k = 0; k < n_sl; ++k) {
+        // the earliest free slot takes the workgroup: raise the root by d and sift it down
+        const float v = heap[0] + d;
+        int j = 0;
+        for (;;) {
+          int c = 2 * j + 1;
+          if (c >= kSlots) break;
+          if (c + 1 < kSlots && heap[c + 1] < heap[c]) ++c;
+          if (heap[c] >= v) break;
+          heap[j] = heap[c];
+          j = c;
+        }
+        heap[j] = v;
+        span = std::max(span, v);
+      }
+      if (!vo && span > limit) return span;
+    }
+  }
+  if (vo) {
+    vo->n = n_pos;
+    for (int p = 0; p < n_pos; ++p) vo->sg[p] = 0xFFFF;
+    int j[kXcd] = {};
+    for (int i = 0; i < n; ++i) {
+      const int x = xcd_of[i];
+      vo->sg[kXcd * j[x]++ + x] = (uint16_t)sp[i].second;
+    }
+  }
+  return span;
+}
+
 int plan_decode(const Layer& L, int B, int n_q, const int32_t* lens, int T_max, void* ws_base, DecodePlan* P,
                 KtList* kts, SeqTable* seq) {
   DecodeGeom& g = P->g;
@@ -139,8 +211,35 @@ int plan_decode(const Layer& L, int B, int n_q, const int32_t* lens, int T_max, 
   // at most 4 splits per sequence while that keeps >= 256 value workgroups: longer-lived
   // workgroups, and the split merge then folds into the up-projection
   if (B * 4 * n_slices >= 256) cps = std::max(cps, ceil_div(max_chunks, 4));
+  // ragged lengths (value kernels that take an explicit order): the split length whose
+  // longest-first XCD deal has the least estimated time, from the fewest splits the rules
+  // above allow up to one split per sequence
+  bool uniform = true;
+  for (int b = 1; b < B; ++b)
+    if (lens[b] != lens[0]) uniform = false;
+  const bool ordered = !uniform && !(g.M_pad > 32 && L.latent == STARKV_LATENT_F32) &&
+                       env_int("STARKV_VORDER", 1) != 0;
+  int cps_lo = std::max(8, ceil_div(max_chunks, kMaxSplitsPerSeq));
+  if (B * 4 * n_slices >= 256) cps_lo = std::max(cps_lo, ceil_div(max_chunks, 4));
+  bool have_order = false;
+  if (ordered) {
+    double best_t = 0;
+    for (int c = std::min(cps_lo, max_chunks);; c = std::min(max_chunks, c + std::max(1, c / 8))) {
+      // a longer split takes at least its own length: no later one can win
+      if (have_order && best_t < c + kWgOvh) break;
+      const double t = order_splits(*seq, B, c, n_slices, nullptr, have_order ? (float)best_t : 1e30f);
+      if (t >= 0 && (!have_order || t <= best_t)) {  // ties: the longer split (fewer partials)
+        have_order = true;
+        best_t = t;
+        cps = c;
+      }
+      if (c >= max_chunks) break;
+    }
+  }
   const int cps_env = env_int("STARKV_CPS", 0);
   if (cps_env > 0) cps = std::max(cps_env, ceil_div(max_chunks, kMaxSplitsPerSeq));
+  P->vo.n = 0;
+  if (ordered && order_splits(*seq, B, cps, n_slices, &P->vo) < 0) P->vo.n = 0;
   int total_splits = 0;
   seq->split_off[0] = 0;
   for (int b = 0; b < B; ++b) {
@@ -148,9 +247,7 @@ int plan_decode(const Layer& L, int B, int n_q, const int32_t* lens, int T_max, 
     seq->split_off[b + 1] = seq->split_off[b] + ceil_div(nc, cps);
     total_splits += ceil_div(nc, cps);
   }
-  seq->uni = 1;
-  for (int b = 1; b < B; ++b)
-    if (lens[b] != lens[0]) seq->uni = 0;
+  seq->uni = uniform ? 1 : 0;
   seq->u_len = lens[0];
   seq->u_nch = seq->chunk_off[1];
   seq->u_nspl = seq->split_off[1];
@@ -952,7 +1049,9 @@ struct ValueArgs {
   int cps, bpw, NB, V8, n8v, n4v;
   int n_sl8;  // one-M-tile kernel: slices of one-N-tile blocks (the rest hold int4 blocks)
   int n_sl, n_splits;  // one-M-tile kernel: slices per split, splits in all
+  ValueOrder vo;       // split of each grid position (vo.n = 0: the kernel's own order)
 };
+static_assert(sizeof(ValueArgs) <= 4096, "value kernel arguments");
 
 // Largest of the chunk maxima cm[c][row] over chunks c = c0, c0 + step, ... (n >= 1 of them),
 // NL loads at a time: the reference against which a value kernel weights its tiles.
@@ -1437,10 +1536,11 @@ __device__ __forceinline__ void values1_run(const ValueArgs& a, int slice, int s
   }
 }
 
-// Grid: one dimension of n_sl x (n_splits rounded up to 8) workgroups.  Workgroups are handed to
-// the eight XCDs in turn (id mod 8), so the k-th workgroup of XCD x takes slice k mod n_sl of
-// split 8 (k / n_sl) + x: all slices of a split run on one XCD and share its L2 copy of the
-// split's probabilities.
+// Grid: one dimension of n_sl x P workgroups, P grid positions (n_splits rounded up to 8, or
+// a.vo.n).  Workgroups are handed to the eight XCDs in turn (id mod 8), so the k-th workgroup of
+// XCD x takes slice k mod n_sl of the split at position 8 (k / n_sl) + x (the split itself, or
+// a.vo.sg of it): all slices of a split run on one XCD and share its L2 copy of the split's
+// probabilities.
 template <int LAT, int NBW8, int NBW4>
 __global__ __launch_bounds__(256) void k_values1(ValueArgs a) {
   // room for four accumulator tiles per wave whatever the instance needs: at 64 KiB of LDS at
@@ -1450,8 +1550,10 @@ __global__ __launch_bounds__(256) void k_values1(ValueArgs a) {
   __shared__ float smx[4][32];
   const int xcd = blockIdx.x & 7, k = blockIdx.x >> 3;
   const int slice = k % a.n_sl;
-  const int sg = 8 * (k / a.n_sl) + xcd;
-  if (sg >= a.n_splits) return;
+  const int pos = 8 * (k / a.n_sl) + xcd;
+  if (pos >= (a.vo.n ? a.vo.n : a.n_splits)) return;
+  const int sg = a.vo.n ? a.vo.sg[pos] : pos;
+  if (sg == 0xFFFF) return;
   if (LAT == STARKV_LATENT_MIX84 && slice >= a.n_sl8) {
     const int nb0 = a.V8 / 32 + (slice - a.n_sl8) * NBW4;
     values1_run<LAT, NBW4, true>(a, slice, sg, nb0, min(NBW4, a.NB - nb0), sred, ssum, smx);
@@ -1515,9 +1617,11 @@ __global__ __launch_bounds__(256) void k_values_mt(ValueArgs a) {
   const int xcd = blockIdx.x & 7, kk = blockIdx.x >> 3;
   const int grp = kk % a.n_sl;
   const int idx = 8 * (kk / a.n_sl) + xcd;
-  if (idx >= a.n_splits) return;
+  if (idx >= (a.vo.n ? a.vo.n : a.n_splits)) return;
+  if (a.vo.n && a.vo.sg[idx] == 0xFFFF) return;
   int b;
-  const int sg = value_split(a.seq, g.B, idx, b);
+  const int sg = a.vo.n ? a.vo.sg[idx] : value_split(a.seq, g.B, idx, b);
+  if (a.vo.n) b = seq_of_split(a.seq, g.B, sg);
   const int s = sg - seq_split0(a.seq, b);
   const int cbase = seq_chunk0(a.seq, b);
   const int nch = seq_nch(a.seq, b);
@@ -2369,20 +2473,22 @@ static hipError_t launch_decode_tail(const Layer& L, const DecodePlan& plan, con
   va.n8v = L.n8v;
   va.n4v = L.n4v;
   va.n_sl8 = w.n_sl8;
+  va.vo = plan.vo;
+  const int n_pos = plan.vo.n ? plan.vo.n : (w.total_splits + 7) / 8 * 8;
   const int nmt = g.M_pad / 32;
   {
     ProfScope ps("decode_values");
     if (nmt == 1) {
       va.n_sl = w.n_sl8 + w.n_sl4;
       va.n_splits = w.total_splits;
-      const dim3 gv(va.n_sl * ((w.total_splits + 7) / 8 * 8));
+      const dim3 gv(va.n_sl * n_pos);
       if (L.latent == STARKV_LATENT_MIX84) e = launch_values1<STARKV_LATENT_MIX84>(ps, w.nbw8, w.nbw4, gv, s, va);
       else if (L.latent == STARKV_LATENT_BF16) e = launch_values1<STARKV_LATENT_BF16>(ps, w.nbw8, w.nbw4, gv, s, va);
       else e = launch_values1<STARKV_LATENT_F32>(ps, w.nbw8, w.nbw4, gv, s, va);
     } else if (L.latent != STARKV_LATENT_F32) {
       va.n_sl = w.n_grp;
       va.n_splits = w.total_splits;
-      const dim3 gv(va.n_sl * ((w.total_splits + 7) / 8 * 8));
+      const dim3 gv(va.n_sl * n_pos);
       if (L.latent == STARKV_LATENT_MIX84) e = launch_values_mt<STARKV_LATENT_MIX84>(ps, nmt, gv, s, va);
       else e = launch_values_mt<STARKV_LATENT_BF16>(ps, nmt, gv, s, va);
     } else {

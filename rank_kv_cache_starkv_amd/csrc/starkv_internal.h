@@ -16,6 +16,7 @@ constexpr int kMaxB = STARKV_MAX_BATCH;
 constexpr int kMaxCT = STARKV_MAX_QROWS / 16;  // 16-row column tiles of the key-score GEMM
 constexpr int kMaxKT = 32;                     // K-tiles per column tile
 constexpr int kMaxSplitsPerSeq = 64;
+constexpr int kMaxVPos = 512;  // grid positions of an explicit value-split order
 
 // Value cache [B][v_rows/32 row blocks][T_max/32 token tiles][32 rows][32 tokens x esz]: byte
 // offset of row block rb of token tile `tile` of sequence b.  A block (32 rows x 32 tokens) is
@@ -107,6 +108,14 @@ struct SeqTable {
   int blk_off[kMaxB + 1];    // prefix of 128-token score blocks per sequence
 };
 
+// Explicit order of the value splits over the positions of the value grid (ragged batches): the
+// workgroups of position p (p mod 8 = the XCD that runs them) take split sg[p]; 0xFFFF marks a
+// position with no split.  n = 0: the kernels' own order.
+struct ValueOrder {
+  int n;  // positions, a multiple of 8 (at most kMaxVPos)
+  uint16_t sg[kMaxVPos];
+};
+
 struct DecodeWs {
   // all device pointers into the caller's workspace
   void* qfrag;      // [B][nct][kMaxKT? -> nkt_max][2048 bytes]
@@ -130,6 +139,7 @@ struct DecodeWs {
 struct DecodePlan {
   DecodeGeom g;
   DecodeWs ws;
+  ValueOrder vo;
   size_t ws_bytes;
 };
 
