@@ -432,12 +432,22 @@ __device__ __forceinline__ void qproj_body(const QprojArgs& a, int gk, int b, in
         rp[3] = 0.f;
       }
     }
-    // fragment chunks of these rows: (row, K-tile, 16-position group qq)
-    for (int n = 0; n < nrows; ++n) {
+    // fragment chunks of these rows: (row, K-tile, 16-position group qq), all rows in one pass
+    int pre[RB + 1];  // first item of each row (rows past nrows have none)
+    pre[0] = 0;
+#pragma unroll
+    for (int n = 0; n < RB; ++n) pre[n + 1] = pre[n] + (n < nrows ? 4 * a.kts.n[(gk * rph + rb0 + n) >> 4] : 0);
+    for (int it = tid; it < pre[RB]; it += NT) {
+      int n = 0, item = it;
+#pragma unroll
+      for (int m = 1; m < RB; ++m)
+        if (it >= pre[m]) {
+          n = m;
+          item = it - pre[m];
+        }
       const int i = gk * rph + rb0 + n;
       const int ct = i >> 4, col = i & 15;
-      const int nkt = a.kts.n[ct];
-      for (int item = tid; item < nkt * 4; item += NT) {
+      {
         const int jt = item >> 2, qq = item & 3;
         const int kt = a.kts.at(ct, jt);
         const int ln = col + 16 * qq;  // fragment lane holding this chunk
