@@ -324,9 +324,10 @@ template <int DT, int LAT, int NT>
 __device__ __forceinline__ void qproj_body(const QprojArgs& a, int gk, int b, int rg, int nrg, QprojShared& sh) {
   constexpr int RB = kQpRB;
   constexpr int NWV = NT / 64;
-  constexpr int CH = DT == STARKV_F32 ? 64 : 128;  // elements of d_h per load round
+  constexpr int SUB = 4;                            // lanes per dot product
   constexpr int EPL = DT == STARKV_F32 ? 4 : 8;    // elements per 16-byte load
-  constexpr int NX = CH / EPL;                       // 16-byte loads per operand per round
+  constexpr int NX = 4;                             // 16-byte loads per operand per lane per round
+  constexpr int CH = SUB * NX * EPL;                // elements of d_h per load round
   auto& qh = sh.qh;
   auto& hi8 = sh.hi8;
   auto& lo8 = sh.lo8;
@@ -345,10 +346,13 @@ __device__ __forceinline__ void qproj_body(const QprojArgs& a, int gk, int b, in
   for (int rb0 = r_lo; rb0 < r_hi; rb0 += RB) {
     const int nrows = min(RB, r_hi - rb0);
     __syncthreads();
-    // q^[n][k] = (q_n . B_k[c0 + k]) * scale * log2(e)/sqrt(d_h): one lane per dot product; the
-    // q row and the B_k row are loaded together (CH elements per round, unconditional loads at
-    // clamped offsets, masked in the FMAs)
-    for (int p = tid; p < nrows * r; p += NT) {
+    // q^[n][k] = (q_n . B_k[c0 + k]) * scale * log2(e)/sqrt(d_h): SUB adjacent lanes per dot
+    // product, lane sub taking the 16-byte pieces sub, sub + SUB, ... of the q row and the B_k
+    // row (loaded together, CH elements per round, unconditional loads at clamped offsets, masked
+    // in the FMAs); the SUB lanes of a product are active together (NT and the item count are
+    // multiples of SUB), so they add their parts with shuffles
+    for (int ps = tid; ps < nrows * r * SUB; ps += NT) {
+      const int p = ps / SUB, sub = ps % SUB;
       const int n = p / r, k = p % r;
       const int i = gk * rph + rb0 + n;
       const int hh = (i % rph) / g.n_q, j = i % g.n_q;
@@ -359,7 +363,7 @@ __device__ __forceinline__ void qproj_body(const QprojArgs& a, int gk, int b, in
         u32x4 qv[NX], bv[NX];
 #pragma unroll
         for (int x = 0; x < NX; ++x) {
-          const int ee = min(e0 + x * EPL, g.d_h - EPL);
+          const int ee = min(e0 + (x * SUB + sub) * EPL, g.d_h - EPL);
           if (DT == STARKV_F32) {
             qv[x] = ld16((const float*)a.q + qoff + ee);
             bv[x] = ld16((const float*)a.B_k + boff + ee);
@@ -371,7 +375,7 @@ __device__ __forceinline__ void qproj_body(const QprojArgs& a, int gk, int b, in
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int x = 0; x < NX; ++x) {
-          const bool live = e0 + x * EPL < g.d_h;
+          const bool live = e0 + (x * SUB + sub) * EPL < g.d_h;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             if (DT == STARKV_F32) {
@@ -385,9 +389,11 @@ __device__ __forceinline__ void qproj_body(const QprojArgs& a, int gk, int b, in
           }
         }
       }
+#pragma unroll
+      for (int o = 1; o < SUB; o <<= 1) acc += __shfl_xor(acc, o, 64);
       float sc = 1.f;
       if (LAT == STARKV_LATENT_MIX84) sc = f16_to_f32(a.scales[c0 + k]);
-      qh[n][k] = acc * sc * g.qscale;
+      if (sub == 0) qh[n][k] = acc * sc * g.qscale;
     }
     __syncthreads();
     // per-row scale (int8 path): rho = max|q^| / 127, one wave per row
