@@ -861,11 +861,14 @@ __global__ __launch_bounds__(256) void k_scores_chunk(ScoreArgs a) {
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int n = lane & 15, qq = lane >> 4;
   const int units = g.nct * a.nch_wg;
+  int b = -1;  // sequence of the current chunk: looked up once, then advanced (the chunks of a
+               // wave's units never decrease)
   for (int u = wave; u < units; u += 4) {
     const int ct = u % g.nct;
     const int cg = blockIdx.x * a.nch_wg + u / g.nct;  // global chunk
     if (cg >= a.total_chunks) break;
-    const int b = seq_of_chunk(a.seq, g.B, cg);
+    if (b < 0) b = seq_of_chunk(a.seq, g.B, cg);
+    while (cg >= seq_chunk0(a.seq, b + 1)) ++b;
     const int t0 = (cg - seq_chunk0(a.seq, b)) * kTC;
     const int len = seq_len(a.seq, b);
     const uint8_t* kbase = a.k_rows + (size_t)b * g.T_max * g.k_row_bytes;
@@ -894,9 +897,10 @@ __global__ __launch_bounds__(256) void k_scores_chunk(ScoreArgs a) {
     }
     float s2[2][4];
     if (LAT == STARKV_LATENT_MIX84) {
-      // key rows of sequence b as a buffer: each lane issues both an int8 and an int4 load and
-      // points the one it does not need (and every load of a masked token or K-tile) past the
-      // end, so no branch surrounds the loads
+      // key rows of sequence b as a buffer: one 16-byte load per lane and K-tile, at the lane's
+      // 16 int8 codes or at the aligned 16 bytes that hold its 16 int4 codes (key-row segments
+      // are 16-byte aligned, so these never leave the row); a masked token or K-tile points past
+      // the end, so no branch surrounds the loads
       const __amdgpu_buffer_rsrc_t krs = buf_rsrc(kbase, (uint32_t)g.T_max * (uint32_t)g.k_row_bytes);
       uint32_t trow[2];
 #pragma unroll
@@ -906,9 +910,8 @@ __global__ __launch_bounds__(256) void k_scores_chunk(ScoreArgs a) {
       for (int tt = 0; tt < 2; ++tt) ah[tt] = al[tt] = i32x4{0, 0, 0, 0};
       for (int jt0 = 0; jt0 < nkt; jt0 += KU) {
         i32x4 fh[KU], fl[KU], av[KU][2];
-        u32x4 r8[KU][2];
-        u32x2 r4[KU][2];
-        bool is8[KU], is4[KU];
+        u32x4 rk[KU][2];
+        bool is8[KU], is4[KU], hi4[KU];
 #pragma unroll
         for (int j = 0; j < KU; ++j) {
           const bool on = jt0 + j < nkt;
@@ -919,12 +922,11 @@ __global__ __launch_bounds__(256) void k_scores_chunk(ScoreArgs a) {
           is4[j] = on && P0 >= g.K8 && P0 < g.K8 + g.K4;
           fh[j] = __builtin_bit_cast(i32x4, ld16(fbase + jc * 2048 + lane * 16));
           fl[j] = __builtin_bit_cast(i32x4, ld16(fbase + jc * 2048 + 1024 + lane * 16));
-          const uint32_t o8 = (uint32_t)P0, o4 = (uint32_t)(g.K8 + (P0 - g.K8) / 2);
+          const uint32_t o4 = (uint32_t)(g.K8 + (P0 - g.K8) / 2);
+          hi4[j] = (o4 & 8u) != 0;
+          const uint32_t ok = is8[j] ? (uint32_t)P0 : (o4 & ~15u);
 #pragma unroll
-          for (int tt = 0; tt < 2; ++tt) {
-            r8[j][tt] = bld16(krs, (is8[j] && tok_ok[tt]) ? trow[tt] + o8 : kOOB);
-            r4[j][tt] = bld8(krs, (is4[j] && tok_ok[tt]) ? trow[tt] + o4 : kOOB);
-          }
+          for (int tt = 0; tt < 2; ++tt) rk[j][tt] = bld16(krs, ((is8[j] || is4[j]) && tok_ok[tt]) ? trow[tt] + ok : kOOB);
         }
         __builtin_amdgcn_sched_barrier(0);  // every load of the batch ahead of its use
 #pragma unroll
@@ -932,8 +934,10 @@ __global__ __launch_bounds__(256) void k_scores_chunk(ScoreArgs a) {
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt)
             // (a K-tile past nkt has neither flag: zero operand; masked tokens are masked below)
-            av[j][tt] = is8[j] ? __builtin_bit_cast(i32x4, r8[j][tt])
-                               : (is4[j] ? unpack_int4_group(r4[j][tt]) : i32x4{0, 0, 0, 0});
+            av[j][tt] = is8[j] ? __builtin_bit_cast(i32x4, rk[j][tt])
+                               : (is4[j] ? unpack_int4_group(hi4[j] ? u32x2{rk[j][tt][2], rk[j][tt][3]}
+                                                                    : u32x2{rk[j][tt][0], rk[j][tt][1]})
+                                         : i32x4{0, 0, 0, 0});
 #pragma unroll
         for (int j = 0; j < KU; ++j)
 #pragma unroll
