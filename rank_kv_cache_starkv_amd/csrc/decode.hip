@@ -852,11 +852,12 @@ __global__ __launch_bounds__(256) void k_scores(ScoreArgs a) {
 
 // Workgroup = 4 waves over `nch_wg` consecutive 32-token chunks (global chunk numbering, so a
 // workgroup may span sequences); work unit = (column tile ct, chunk) = 2 MFMA row tiles of 16
-// tokens.  Per unit the K-tiles are walked four at a time: the loads of four K-tiles (query
-// fragments and key rows) are issued before their MFMAs, to keep enough bytes in flight.
-template <int LAT>
+// tokens.  Per unit the K-tiles are walked KU at a time: the loads of KU K-tiles (query
+// fragments and key rows) are issued before their MFMAs.  KU = 4 when no column tile has more
+// than six K-tiles (one or two batches per unit); with more K-tiles, KU = 2 (fewer registers,
+// 6 instead of 4 waves per SIMD) was faster on MI355X.
+template <int LAT, int KU>
 __global__ __launch_bounds__(256) void k_scores_chunk(ScoreArgs a) {
-  constexpr int KU = 4;  // K-tiles in flight
   const DecodeGeom& g = a.g;
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int n = lane & 15, qq = lane >> 4;
@@ -2465,7 +2466,8 @@ static hipError_t launch_decode_tail(const Layer& L, const DecodePlan& plan, con
       // (column tile, chunk) units
       sa.nch_wg = 4 / std::gcd(g.nct, 4);
       const int n_wg = (w.total_chunks + sa.nch_wg - 1) / sa.nch_wg;
-      e = launch_k(ps, k_scores_chunk<STARKV_LATENT_MIX84>, dim3(n_wg), dim3(256), s, sa);
+      if (w.nkt_max <= 6) e = launch_k(ps, k_scores_chunk<STARKV_LATENT_MIX84, 4>, dim3(n_wg), dim3(256), s, sa);
+      else e = launch_k(ps, k_scores_chunk<STARKV_LATENT_MIX84, 2>, dim3(n_wg), dim3(256), s, sa);
     } else {
       // bf16/fp32 keys (many K-tiles per column tile): K split over the waves of a 128-token block
       sa.nch_wg = 4;
