@@ -141,7 +141,8 @@ typedef struct starkv_layer_info {
  *          even-numbered one of the pair in the low nibble); elem = 1.
  *   bf16 / f32: row c = value channel c (rows padded to a multiple of 32),
  *          elem = 2 or 4.
- * T_max must be a multiple of 32.  Token t of sequence b lives at k_rows row
+ * T_max must be a multiple of 32, and one sequence's key rows (T_max x row
+ * bytes) must stay under 4 GiB (EUNSUPPORTED otherwise).  Token t of sequence b lives at k_rows row
  * [b][t] and, for value tile row v, at v_tiles [b][v/32][t/32][v%32][t%32].  Bytes of tokens at or beyond a
  * sequence's length are never read for the result.
  */
@@ -218,7 +219,8 @@ int starkv_calibrate(starkv_layer* layer, const void* X_cal, int n_cal, uint16_t
 /* Bind caller-provided fp16 scales [n_lat] (mix84 layers). */
 int starkv_bind_scales(starkv_layer* layer, const uint16_t* scales);
 
-/* Bytes of k_rows and v_tiles for B sequences of capacity T_max (a multiple of 32). */
+/* Bytes of k_rows and v_tiles for B sequences of capacity T_max (a multiple of 32);
+ * EUNSUPPORTED when one sequence's key rows would reach 4 GiB. */
 int starkv_cache_bytes(const starkv_layer* layer, int B, int T_max, size_t* k_bytes, size_t* v_bytes);
 
 /*

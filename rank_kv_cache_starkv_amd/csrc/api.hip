@@ -180,8 +180,13 @@ int starkv_bind_scales(starkv_layer* l, const uint16_t* scales) {
   return STARKV_OK;
 }
 
+// one sequence's key rows must be addressable by 32-bit buffer offsets below the out-of-range
+// offset the kernels use for masked loads
+constexpr size_t kMaxSeqKeyBytes = 0xFFFFFF00u;
+
 int starkv_cache_bytes(const starkv_layer* l, int B, int T_max, size_t* k_bytes, size_t* v_bytes) {
   if (!l || !k_bytes || !v_bytes || B <= 0 || T_max <= 0 || T_max % STARKV_TILE_TOKENS != 0) return STARKV_EINVAL;
+  if ((size_t)T_max * l->L.k_row_bytes >= kMaxSeqKeyBytes) return STARKV_EUNSUPPORTED;
   *k_bytes = (size_t)B * T_max * l->L.k_row_bytes;
   *v_bytes = (size_t)B * (T_max / STARKV_TILE_TOKENS) * l->L.v_tile_bytes;
   return STARKV_OK;
@@ -191,7 +196,8 @@ static int check_cache(const Layer& L, const starkv_cache* c, int B) {
   if (!c || !c->k_rows || !c->v_tiles) return STARKV_EINVAL;
   if (c->T_max <= 0 || c->T_max % STARKV_TILE_TOKENS != 0 || c->B <= 0) return STARKV_EINVAL;
   if (B > c->B) return STARKV_EINVAL;
-  (void)L;
+  // the kernels address one sequence's key rows with 32-bit buffer offsets
+  if ((size_t)c->T_max * L.k_row_bytes >= kMaxSeqKeyBytes) return STARKV_EUNSUPPORTED;
   return STARKV_OK;
 }
 

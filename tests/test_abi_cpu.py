@@ -71,6 +71,11 @@ def test_ranks_and_layout_match_oracle(cfg):
         assert (inf["K8"], inf["K4"], inf["V8"], inf["V4"]) == (fmt.K8, fmt.K4, fmt.V8, fmt.V4)
     kb, vb = layer.cache_bytes(w.B, 4096)
     assert kb == w.B * 4096 * fmt.k_row_bytes and vb == w.B * 128 * fmt.v_tile_bytes
+    # one sequence's key rows must stay addressable by 32-bit buffer offsets
+    big = -(-(0xFFFFFF00 // fmt.k_row_bytes + 1) // 32) * 32
+    with pytest.raises(S.StarKVError) as ei:
+        layer.cache_bytes(1, big)
+    assert ei.value.status == -4  # EUNSUPPORTED
     layer.close()
 
 
