@@ -32,7 +32,17 @@ __global__ __launch_bounds__(256) void k_latent_gemm(GemmArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   const int r = lane & 31, q = lane >> 5;
-  const int mb = blockIdx.x * 64, sb = blockIdx.y * 64;
+  int rt = blockIdx.x, ctl = blockIdx.y;
+  if (a.xmap_rt > 0) {
+    // 1-D grid, workgroups dealt to the eight XCDs in turn: the k-th workgroup of XCD x takes
+    // row tile k mod xmap_rt of column tile x + 8 (k / xmap_rt), so the row tiles of a column
+    // tile run one after another on one XCD and share its L2 copy of that slab of A
+    const int k = blockIdx.x >> 3;
+    rt = k % a.xmap_rt;
+    ctl = (blockIdx.x & 7) + 8 * (k / a.xmap_rt);
+    if (ctl * 64 >= a.NS) return;  // whole workgroup
+  }
+  const int mb = rt * 64, sb = ctl * 64;
   // operand rows of the tile's two 32-row halves (i) and two 32-slot halves (j)
   bool a_ok[2], b_ok[2];
   size_t a_base[2], b_base[2];
@@ -190,6 +200,7 @@ void fill_gemm_args(const Layer& L, GemmArgs& a, const void* X, int M) {
   a.M = M;
   a.d = L.d;
   a.NS = L.key_slots + L.val_slots;
+  a.xmap_rt = 0;
   a.key_slots = L.key_slots;
   a.K8 = L.K8;
   a.V8 = L.V8;
@@ -251,7 +262,13 @@ hipError_t launch_append(const Layer& L, const starkv_cache& c, const void* X_ne
       e = mix ? launch_k(ps, k_latent_gemm_skinny<STARKV_F32, 16, true>, grid, dim3(512), s, a)
               : launch_k(ps, k_latent_gemm_skinny<STARKV_F32, 16, false>, grid, dim3(512), s, a);
   } else {
-    const dim3 grid((B * n_new + 63) / 64, (a.NS + 63) / 64);
+    const int n_rt = (B * n_new + 63) / 64, n_ct = (a.NS + 63) / 64;
+    dim3 grid(n_rt, n_ct);
+    if (n_rt <= 16) {
+      // a short block of tokens: XCD-aware grid (each slab of A fetched into one L2)
+      a.xmap_rt = n_rt;
+      grid = dim3(8 * n_rt * ((n_ct + 7) / 8));
+    }
     if (L.dtype == STARKV_BF16) e = launch_k(ps, k_latent_gemm<STARKV_BF16, 0>, grid, dim3(256), s, a);
     else e = launch_k(ps, k_latent_gemm<STARKV_F32, 0>, grid, dim3(256), s, a);
   }

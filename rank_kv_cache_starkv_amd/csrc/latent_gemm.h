@@ -18,6 +18,7 @@ struct GemmArgs {
   const void* A_t;      // [n_lat][d]
   const int* slot_chan; // [NS rounded up to 16]: natural channel of each column, -1 for padding
   int M, d, NS;
+  int xmap_rt;          // k_latent_gemm: > 0: row tiles per column tile of an XCD-aware 1-D grid
   int key_slots, K8, V8;
   int qmax_hi, qmax_lo;  // code limits of the int8 and int4 regions
   int n_key, r_v;
