@@ -26,8 +26,10 @@ __global__ __launch_bounds__(512) void k_latent_gemm_skinny(GemmArgs a) {
   skinny_body<DT, SW, MIX>(a, blockIdx.x, red);
 }
 
-template <int DT, int MODE>
-__global__ __launch_bounds__(256) void k_latent_gemm(GemmArgs a) {
+// NW waves (4 or 8) split K; with 8, waves 4-7 hand their partial tiles to waves 0-3 first.
+template <int DT, int MODE, int NW>
+__global__ __launch_bounds__(64 * NW) void k_latent_gemm(GemmArgs a) {
+  static_assert(NW == 4 || NW == 8, "waves per workgroup");
   __shared__ float part[4][4][16][64];  // [wave][32 x 32 quadrant][D element][lane]: 64 KiB
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
@@ -57,9 +59,9 @@ __global__ __launch_bounds__(256) void k_latent_gemm(GemmArgs a) {
     b_base[h] = (size_t)(b_ok[h] ? ch : 0) * a.d;
     scb[h] = (MODE == 0 && a.latent == STARKV_LATENT_MIX84) ? scale_bits(a, ch) : (uint16_t)0;
   }
-  // this wave's K-steps (16 each): a quarter of K
+  // this wave's K-steps (16 each): an NW-th of K
   const int nk = a.d / 16;
-  const int per = (nk + 3) / 4;
+  const int per = (nk + NW - 1) / NW;
   const int kb = wave * per, ke = min(nk, kb + per);
 
   f32x16 acc[2][2];
@@ -132,19 +134,47 @@ __global__ __launch_bounds__(256) void k_latent_gemm(GemmArgs a) {
     }
   }
 
-  // add the four waves' K-quarters: wave w takes quadrant (rows half w & 1, slots half w >> 1)
+  if (NW == 8) {
+    // waves 4-7 hand their partial tiles to waves 0-3
+    if (wave >= 4) {
 #pragma unroll
-  for (int x = 0; x < 2; ++x)
+      for (int x = 0; x < 2; ++x)
 #pragma unroll
-    for (int y = 0; y < 2; ++y)
+        for (int y = 0; y < 2; ++y)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) part[wave][2 * y + x][v][lane] = acc[x][y][v];
+          for (int v = 0; v < 16; ++v) part[wave - 4][2 * y + x][v][lane] = acc[x][y][v];
+    }
+    __syncthreads();
+    if (wave < 4) {
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[x][y][v] += part[wave][2 * y + x][v][lane];
+    }
+    __syncthreads();
+  }
+  // add the four K-parts: with 4 waves wave w takes quadrant w (rows half w & 1, slots half
+  // w >> 1); with 8, wave w takes half w >> 2 of the D elements of quadrant w & 3
+  if (wave < 4) {
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int y = 0; y < 2; ++y)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) part[wave][2 * y + x][v][lane] = acc[x][y][v];
+  }
   __syncthreads();
-  const int wm = wave & 1, wn = wave >> 1;
-  f32x16 accq;
+  constexpr int NVW = NW == 4 ? 16 : 8;  // D elements per lane in this wave's share
+  const int qd = wave & 3;
+  const int v0 = NW == 4 ? 0 : 8 * (wave >> 2);
+  const int wm = qd & 1, wn = qd >> 1;
+  float accq[NVW];
 #pragma unroll
-  for (int v = 0; v < 16; ++v)
-    accq[v] = part[0][wave][v][lane] + part[1][wave][v][lane] + part[2][wave][v][lane] + part[3][wave][v][lane];
+  for (int v = 0; v < NVW; ++v)
+    accq[v] = part[0][qd][v0 + v][lane] + part[1][qd][v0 + v][lane] + part[2][qd][v0 + v][lane] +
+              part[3][qd][v0 + v][lane];
   const int m0 = mb + 32 * wm;
   const int s0 = sb + 32 * wn;
   const uint16_t sc_bits = wn ? scb[1] : scb[0];
@@ -157,23 +187,23 @@ __global__ __launch_bounds__(256) void k_latent_gemm(GemmArgs a) {
     // calibrate: absmax of this column over the 32 rows (rows >= M hold 0)
     float m = 0.f;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) m = fmaxf(m, fabsf(accq[v]));
+    for (int v = 0; v < NVW; ++v) m = fmaxf(m, fabsf(accq[v]));
     m = fmaxf(m, __shfl_xor(m, 32, 64));
     if (q == 0 && chan >= 0) atomicMax(a.absmax + chan, __float_as_uint(m));
     return;
   }
 
-  float xs[16];
-  int ms[16];
+  float xs[NVW];
+  int ms[NVW];
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
+  for (int v = 0; v < NVW; ++v) {
     xs[v] = accq[v];
-    ms[v] = m0 + d32_row(v, q);
+    ms[v] = m0 + d32_row(v0 + v, q);
   }
-  int ps[16];
+  int ps[NVW];
 #pragma unroll
-  for (int v = 0; v < 16; ++v) ps[v] = row_pos(a, ms[v]);
-  store_latent<16>(a, slot, chan, sc_bits, xs, ms, ps);
+  for (int v = 0; v < NVW; ++v) ps[v] = row_pos(a, ms[v]);
+  store_latent<NVW>(a, slot, chan, sc_bits, xs, ms, ps);
 }
 
 __global__ void k_fill_u32(uint32_t* p, int n, uint32_t v) {
@@ -230,8 +260,8 @@ hipError_t launch_calibrate(const Layer& L, const void* X_cal, int n_cal, uint16
   fill_gemm_args(L, a, X_cal, n_cal);
   a.absmax = L.d_absmax;
   dim3 grid((n_cal + 63) / 64, (a.NS + 63) / 64);
-  if (L.dtype == STARKV_BF16) hipLaunchKernelGGL((k_latent_gemm<STARKV_BF16, 1>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((k_latent_gemm<STARKV_F32, 1>), grid, dim3(256), 0, s, a);
+  if (L.dtype == STARKV_BF16) hipLaunchKernelGGL((k_latent_gemm<STARKV_BF16, 1, 4>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((k_latent_gemm<STARKV_F32, 1, 4>), grid, dim3(256), 0, s, a);
   hipLaunchKernelGGL(k_finish_scales, dim3((L.n_lat + 255) / 256), dim3(256), 0, s, (const uint32_t*)L.d_absmax,
                      (const int*)L.d_src, (const int*)L.d_n8, L.n8v, L.H_kv, L.n_lat, (float)L.qmax_hi,
                      (float)L.qmax_lo, scales_out);
@@ -263,14 +293,18 @@ hipError_t launch_append(const Layer& L, const starkv_cache& c, const void* X_ne
               : launch_k(ps, k_latent_gemm_skinny<STARKV_F32, 16, false>, grid, dim3(512), s, a);
   } else {
     const int n_rt = (B * n_new + 63) / 64, n_ct = (a.NS + 63) / 64;
-    dim3 grid(n_rt, n_ct);
     if (n_rt <= 16) {
-      // a short block of tokens: XCD-aware grid (each slab of A fetched into one L2)
+      // a short block of tokens: XCD-aware grid (each slab of A fetched into one L2) and eight
+      // waves per workgroup (few workgroups: K split eight ways)
       a.xmap_rt = n_rt;
-      grid = dim3(8 * n_rt * ((n_ct + 7) / 8));
+      const dim3 grid(8 * n_rt * ((n_ct + 7) / 8));
+      if (L.dtype == STARKV_BF16) e = launch_k(ps, k_latent_gemm<STARKV_BF16, 0, 8>, grid, dim3(512), s, a);
+      else e = launch_k(ps, k_latent_gemm<STARKV_F32, 0, 8>, grid, dim3(512), s, a);
+    } else {
+      const dim3 grid(n_rt, n_ct);
+      if (L.dtype == STARKV_BF16) e = launch_k(ps, k_latent_gemm<STARKV_BF16, 0, 4>, grid, dim3(256), s, a);
+      else e = launch_k(ps, k_latent_gemm<STARKV_F32, 0, 4>, grid, dim3(256), s, a);
     }
-    if (L.dtype == STARKV_BF16) e = launch_k(ps, k_latent_gemm<STARKV_BF16, 0>, grid, dim3(256), s, a);
-    else e = launch_k(ps, k_latent_gemm<STARKV_F32, 0>, grid, dim3(256), s, a);
   }
   if (e != hipSuccess) return e;
   return hipGetLastError();
