@@ -265,6 +265,31 @@ int starkv_decode_attention(const starkv_layer* layer, const starkv_cache* cache
                             hipStream_t stream);
 
 /*
+ * Weight absorption of the key factors into the query projection (Methodology
+ * section 2: the reconstruction matrices are fused into the projections).  W_q:
+ * device [d][H_q*d_h] (dtype), the layer's query projection (q = x W_q, head h in
+ * columns [h*d_h, (h+1)*d_h)).  Builds, in device memory the layer owns (allocated
+ * by the first call, freed by starkv_layer_destroy), for every query head h of KV
+ * head g = h / G:  Wqk_h = W_q[:, h] B_g^T  (d x r_g, fp64 sums kept in fp32), so
+ * that the query in the key latent space is x Wqk_h directly.  W_q is read during
+ * the call only.  Binding or building new factors drops the absorbed factors.
+ * Errors: EINVAL (null), ESTATE (no bound factors), ENOMEM, EHIP.
+ */
+int starkv_absorb_query(starkv_layer* layer, const void* W_q, hipStream_t stream);
+
+/*
+ * starkv_decode_attention with the query taken from hidden states: identical
+ * except that q[b][j][h] = x[b][j] W_q[:, h] is formed as x[b][j] Wqk_h inside the
+ * query projection (the absorbed factors of starkv_absorb_query).
+ * x: device [B][n_q][d] (dtype); out: device [B][n_q][H_q][d_h] (dtype).  Same
+ * workspace as starkv_decode_attention.  Errors: as starkv_decode_attention, plus
+ * ESTATE when no absorbed factors are present.
+ */
+int starkv_decode_attention_hidden(const starkv_layer* layer, const starkv_cache* cache, const void* x, int B,
+                                   int n_q, const int32_t* lens_host, void* out, void* ws, size_t ws_bytes,
+                                   hipStream_t stream);
+
+/*
  * One decode step of a layer (Problem Statement: the new tokens' hidden states are
  * projected into the cache, then attention reads it; Methodology section 2): append
  * the n_q new tokens X_new[b][0 .. n_q-1] at positions lens_host[b] - n_q ..

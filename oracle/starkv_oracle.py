@@ -594,6 +594,15 @@ def dequantized(cache: SequenceCache, layer: Layer, scales=None) -> Tuple[np.nda
     return np.asarray(cache.key, np.float64), np.asarray(cache.value, np.float64)
 
 
+def query_from_hidden(x, W_q, H_q: int, d_h: int) -> np.ndarray:
+    """Queries of hidden states x [n_q, d] through the query projection W_q [d, H_q d_h]:
+    q[j, h] = x[j] W_q[:, h d_h:(h + 1) d_h], in fp64 (the product the absorbed factors
+    W_q^h B_g^T fold into the key latent; Methodology section 2)."""
+    x = np.asarray(x, np.float64)
+    W = np.asarray(W_q, np.float64)
+    return (x @ W).reshape(x.shape[0], H_q, d_h)
+
+
 def decode(q, cache: SequenceCache, layer: Layer, n_q: int, scales=None, mode: str = "reconstruct") -> np.ndarray:
     """Decode attention of one sequence; ``mode`` = "reconstruct" (O7 + O8) or "latent" (O9)."""
     xk, xv = dequantized(cache, layer, scales)

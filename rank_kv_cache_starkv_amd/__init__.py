@@ -67,7 +67,7 @@ EXPORTS = ["starkv_abi_version", "starkv_status_string", "starkv_layer_create", 
            "starkv_layer_get_info", "starkv_layer_ranks", "starkv_build_factors", "starkv_bind_factors",
            "starkv_calibrate", "starkv_bind_scales", "starkv_cache_bytes", "starkv_compress_append",
            "starkv_decode_workspace_bytes", "starkv_decode_attention", "starkv_decode_step", "starkv_reconstruct",
-           "starkv_profile_enable", "starkv_profile_read"]
+           "starkv_absorb_query", "starkv_decode_attention_hidden", "starkv_profile_enable", "starkv_profile_read"]
 
 _lib = None
 
@@ -99,6 +99,9 @@ def lib() -> ctypes.CDLL:
                                           vp, vp, sz, vp]
     L.starkv_decode_step.argtypes = [vp, ctypes.POINTER(_Cache), vp, vp, ci, ci, ctypes.POINTER(ctypes.c_int32),
                                      vp, vp, sz, vp]
+    L.starkv_absorb_query.argtypes = [vp, vp, vp]
+    L.starkv_decode_attention_hidden.argtypes = [vp, ctypes.POINTER(_Cache), vp, ci, ci,
+                                                 ctypes.POINTER(ctypes.c_int32), vp, vp, sz, vp]
     L.starkv_reconstruct.argtypes = [vp, ctypes.POINTER(_Cache), ci, ci, ci, vp, vp, vp]
     L.starkv_profile_enable.argtypes = [ci]
     L.starkv_profile_read.argtypes = [ctypes.POINTER(_KernelTime), ci, ctypes.POINTER(ci), ci]
@@ -291,6 +294,33 @@ class Layer:
                                                  L.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), _ptr(out), _ptr(ws),
                                                  int(ws.numel() * ws.element_size()), _stream(stream)),
                "starkv_decode_attention")
+        return out
+
+    def absorb_query(self, W_q, stream=None) -> None:
+        """Absorb the key factors into the query projection W_q [d, H_q * d_h] (device, layer dtype)."""
+        assert W_q.dtype == self.torch_dtype and W_q.is_contiguous() and tuple(W_q.shape) == (self.d, self.H_q * self.d_h)
+        _check(self._lib.starkv_absorb_query(self._h, _ptr(W_q), _stream(stream)), "starkv_absorb_query")
+
+    def decode_hidden(self, cache: Cache, x, lens: Sequence[int], out=None, ws=None, stream=None):
+        """Attention with the query taken from hidden states x [B, n_q, d] through the absorbed
+        query factors; returns out [B, n_q, H_q, d_h]."""
+        import torch
+        assert x.dtype == self.torch_dtype and x.is_contiguous() and x.dim() == 3 and int(x.shape[2]) == self.d
+        B, n_q = int(x.shape[0]), int(x.shape[1])
+        L = _i32(lens)
+        need = self.workspace_bytes(B, n_q, L)
+        if ws is None:
+            if self._ws is None or self._ws.numel() < need:
+                self._ws = torch.empty((max(need, 256),), dtype=torch.uint8, device=x.device)
+            ws = self._ws
+        if out is None:
+            out = torch.empty((B, n_q, self.H_q, self.d_h), dtype=x.dtype, device=x.device)
+        cs = cache.struct()
+        _check(self._lib.starkv_decode_attention_hidden(self._h, ctypes.byref(cs), _ptr(x), B, n_q,
+                                                        L.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), _ptr(out),
+                                                        _ptr(ws), int(ws.numel() * ws.element_size()),
+                                                        _stream(stream)),
+               "starkv_decode_attention_hidden")
         return out
 
     def step(self, cache: Cache, X_new, q, lens: Sequence[int], out=None, ws=None, stream=None):

@@ -96,6 +96,7 @@ int starkv_layer_create(const starkv_layer_desc* d, starkv_layer** out) {
 int starkv_layer_destroy(starkv_layer* l) {
   if (!l) return STARKV_EINVAL;
   if (l->L.dev_tables) (void)hipFree(l->L.dev_tables);
+  if (l->L.d_wqk) (void)hipFree(l->L.d_wqk);
   delete l;
   return STARKV_OK;
 }
@@ -134,6 +135,12 @@ int starkv_layer_ranks(const starkv_layer* l, int32_t* ranks_out) {
   return STARKV_OK;
 }
 
+// absorbed query factors depend on the bound B_k: binding new factors drops them
+static void drop_absorbed(Layer* L) {
+  if (L->d_wqk) (void)hipFree(L->d_wqk);
+  L->d_wqk = nullptr;
+}
+
 int starkv_build_factors(starkv_layer* l, const float* U_k, const float* V_k, const float* U_v, const float* V_v,
                          void* A_t, void* B_k, void* B_vt, hipStream_t stream) {
   SKV_GUARD_BEGIN
@@ -145,6 +152,7 @@ int starkv_build_factors(starkv_layer* l, const float* U_k, const float* V_k, co
     l->L.A_t = A_t;
     l->L.B_k = B_k;
     l->L.B_vt = B_vt;
+    drop_absorbed(&l->L);
   }
   return st;
   SKV_GUARD_END
@@ -158,7 +166,26 @@ int starkv_bind_factors(starkv_layer* l, const void* A_t, const void* B_k, const
   l->L.A_t = A_t;
   l->L.B_k = B_k;
   l->L.B_vt = B_vt;
+  drop_absorbed(&l->L);
   return STARKV_OK;
+  SKV_GUARD_END
+}
+
+int starkv_absorb_query(starkv_layer* l, const void* W_q, hipStream_t stream) {
+  SKV_GUARD_BEGIN
+  if (!l || !W_q) return STARKV_EINVAL;
+  Layer& L = l->L;
+  if (!L.dev_tables || !L.B_k) return STARKV_ESTATE;
+  if (!L.d_wqk) {
+    const size_t bytes = (size_t)L.G * L.n_key * L.d * sizeof(float);
+    if (hipMalloc((void**)&L.d_wqk, bytes) != hipSuccess) {
+      L.d_wqk = nullptr;
+      return STARKV_ENOMEM;
+    }
+  }
+  const int st = hip_status(skv::launch_absorb_query(L, W_q, L.d_wqk, stream));
+  if (st != STARKV_OK) drop_absorbed(&L);
+  return st;
   SKV_GUARD_END
 }
 
@@ -273,6 +300,28 @@ int starkv_decode_attention(const starkv_layer* l, const starkv_cache* c, const 
   if (st != STARKV_OK) return st;
   if (ws_bytes < plan.ws_bytes) return STARKV_EWORKSPACE;
   return hip_status(skv::launch_decode(L, plan, kts, seq, q, out, c->k_rows, c->v_tiles, stream));
+  SKV_GUARD_END
+}
+
+int starkv_decode_attention_hidden(const starkv_layer* l, const starkv_cache* c, const void* x, int B, int n_q,
+                                   const int32_t* lens_host, void* out, void* ws, size_t ws_bytes,
+                                   hipStream_t stream) {
+  SKV_GUARD_BEGIN
+  if (!l || !x || !out || !ws) return STARKV_EINVAL;
+  const Layer& L = l->L;
+  int st = check_decode(L, c, B, n_q, lens_host);
+  if (st != STARKV_OK) return st;
+  st = check_bound(L, true);
+  if (st != STARKV_OK) return st;
+  if (!L.d_wqk) return STARKV_ESTATE;
+  if (((uintptr_t)ws & 255) != 0) return STARKV_EINVAL;
+  skv::DecodePlan plan;
+  skv::KtList kts;
+  skv::SeqTable seq;
+  st = skv::plan_decode(L, B, n_q, lens_host, c->T_max, ws, &plan, &kts, &seq);
+  if (st != STARKV_OK) return st;
+  if (ws_bytes < plan.ws_bytes) return STARKV_EWORKSPACE;
+  return hip_status(skv::launch_decode(L, plan, kts, seq, x, out, c->k_rows, c->v_tiles, stream, L.d_wqk));
   SKV_GUARD_END
 }
 

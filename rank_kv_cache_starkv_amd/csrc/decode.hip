@@ -117,6 +117,7 @@ int plan_decode(const Layer& L, int B, int n_q, const int32_t* lens, int T_max, 
   g.nct = ceil_div(g.M_q, 16);
   g.G = L.G;
   g.d_h = L.d_h;
+  g.d = L.d;
   g.H_q = L.H_q;
   g.H_kv = L.H_kv;
   g.n_key = L.n_key;
@@ -288,8 +289,9 @@ int plan_decode(const Layer& L, int B, int n_q, const int32_t* lens, int T_max, 
 // qproj: query fragments of the key-score GEMM
 
 struct QprojArgs {
-  const void* q;
+  const void* q;        // queries [B][n_q][H_q][d_h], or hidden states [B][n_q][d] when wqk is set
   const void* B_k;
+  const float* wqk;     // absorbed query factors [G n_key][d] (fp32), or null
   const uint16_t* scales;
   HeadTables heads;
   uint8_t* qfrag;
@@ -320,7 +322,7 @@ struct QprojShared {
 
 // Body of the query projection for workgroup (KV head gk, sequence b, row group rg of nrg) with
 // NT threads.
-template <int DT, int LAT, int NT>
+template <int DT, int LAT, int NT, bool HID = false>
 __device__ __forceinline__ void qproj_body(const QprojArgs& a, int gk, int b, int rg, int nrg, QprojShared& sh) {
   constexpr int RB = kQpRB;
   constexpr int NWV = NT / 64;
@@ -354,6 +356,49 @@ __device__ __forceinline__ void qproj_body(const QprojArgs& a, int gk, int b, in
     for (int ps = tid; ps < nrows * r * SUB; ps += NT) {
       const int p = ps / SUB, sub = ps % SUB;
       const int n = p / r, k = p % r;
+      if (HID) {
+        // hidden state x_(b, j) against the absorbed factor row of (query head, k): length d,
+        // 8 elements per lane piece (x: one 16-byte bf16 load or two fp32; wqk: two fp32)
+        const int i = gk * rph + rb0 + n;
+        const int hh = (i % rph) / g.n_q, j = i % g.n_q;
+        const size_t xoff = ((size_t)b * g.n_q + j) * g.d;
+        const float* wr = a.wqk + ((size_t)g.G * c0 + (size_t)hh * r + k) * g.d;
+        float acc = 0.f;
+        for (int e0 = 0; e0 < g.d; e0 += SUB * NX * 8) {
+          u32x4 xv[NX][2], wv[NX][2];
+#pragma unroll
+          for (int x = 0; x < NX; ++x) {
+            const int ee = min(e0 + (x * SUB + sub) * 8, g.d - 8);
+            if (DT == STARKV_F32) {
+              xv[x][0] = ld16((const float*)a.q + xoff + ee);
+              xv[x][1] = ld16((const float*)a.q + xoff + ee + 4);
+            } else {
+              xv[x][0] = ld16((const uint16_t*)a.q + xoff + ee);
+              xv[x][1] = xv[x][0];
+            }
+            wv[x][0] = ld16(wr + ee);
+            wv[x][1] = ld16(wr + ee + 4);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int x = 0; x < NX; ++x) {
+            const bool live = e0 + (x * SUB + sub) * 8 < g.d;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              float xe;
+              if (DT == STARKV_F32) xe = __uint_as_float(xv[x][e >> 2][e & 3]);
+              else xe = bf16_to_f32((uint16_t)((xv[x][0][e >> 1] >> (16 * (e & 1))) & 0xFFFF));
+              acc = fmaf(live ? xe : 0.f, __uint_as_float(wv[x][e >> 2][e & 3]), acc);
+            }
+          }
+        }
+#pragma unroll
+        for (int o = 1; o < SUB; o <<= 1) acc += __shfl_xor(acc, o, 64);
+        float sc = 1.f;
+        if (LAT == STARKV_LATENT_MIX84) sc = f16_to_f32(a.scales[c0 + k]);
+        if (sub == 0) qh[n][k] = acc * sc * g.qscale;
+        continue;
+      }
       const int i = gk * rph + rb0 + n;
       const int hh = (i % rph) / g.n_q, j = i % g.n_q;
       const size_t qoff = (((size_t)b * g.n_q + j) * g.H_q + gk * g.G + hh) * g.d_h;
@@ -528,10 +573,11 @@ __device__ __forceinline__ void qproj_body(const QprojArgs& a, int gk, int b, in
   }
 }
 
-template <int DT, int LAT>
+// HID: the query comes from hidden states through the absorbed factors (a.wqk)
+template <int DT, int LAT, bool HID>
 __global__ __launch_bounds__(256) void k_qproj(QprojArgs a) {
   __shared__ QprojShared sh;
-  qproj_body<DT, LAT, 256>(a, blockIdx.x, blockIdx.y, blockIdx.z, gridDim.z, sh);
+  qproj_body<DT, LAT, 256, HID>(a, blockIdx.x, blockIdx.y, blockIdx.z, gridDim.z, sh);
 }
 
 // ===========================================================================
@@ -2344,6 +2390,7 @@ static QprojArgs qproj_args(const Layer& L, const DecodePlan& plan, const KtList
   QprojArgs qa;
   qa.q = q;
   qa.B_k = L.B_k;
+  qa.wqk = nullptr;
   qa.scales = L.scales;
   qa.heads = L.heads();
   qa.qfrag = (uint8_t*)plan.ws.qfrag;
@@ -2395,17 +2442,25 @@ static hipError_t launch_decode_tail(const Layer& L, const DecodePlan& plan, con
                                      void* out, const void* k_rows, const void* v_tiles, hipStream_t s);
 
 hipError_t launch_decode(const Layer& L, const DecodePlan& plan, const KtList& kts, const SeqTable& seq,
-                         const void* q, void* out, const void* k_rows, const void* v_tiles, hipStream_t s) {
+                         const void* q, void* out, const void* k_rows, const void* v_tiles, hipStream_t s,
+                         const float* wqk) {
   const DecodeGeom& g = plan.g;
   hipError_t e = hipSuccess;
-  // 1. query fragments (and the running-maximum slots set to -inf)
-  const QprojArgs qa = qproj_args(L, plan, kts, q);
+  // 1. query fragments
+  QprojArgs qa = qproj_args(L, plan, kts, q);
+  qa.wqk = wqk;
   {
     ProfScope ps("decode_qproj");
     const dim3 gq(g.H_kv, g.B, qproj_row_groups(g));
-    if (L.dtype == STARKV_F32) e = launch_k(ps, k_qproj<STARKV_F32, STARKV_LATENT_F32>, gq, dim3(256), s, qa);
-    else if (L.latent == STARKV_LATENT_BF16) e = launch_k(ps, k_qproj<STARKV_BF16, STARKV_LATENT_BF16>, gq, dim3(256), s, qa);
-    else e = launch_k(ps, k_qproj<STARKV_BF16, STARKV_LATENT_MIX84>, gq, dim3(256), s, qa);
+    if (wqk) {
+      if (L.dtype == STARKV_F32) e = launch_k(ps, k_qproj<STARKV_F32, STARKV_LATENT_F32, true>, gq, dim3(256), s, qa);
+      else if (L.latent == STARKV_LATENT_BF16) e = launch_k(ps, k_qproj<STARKV_BF16, STARKV_LATENT_BF16, true>, gq, dim3(256), s, qa);
+      else e = launch_k(ps, k_qproj<STARKV_BF16, STARKV_LATENT_MIX84, true>, gq, dim3(256), s, qa);
+    } else {
+      if (L.dtype == STARKV_F32) e = launch_k(ps, k_qproj<STARKV_F32, STARKV_LATENT_F32, false>, gq, dim3(256), s, qa);
+      else if (L.latent == STARKV_LATENT_BF16) e = launch_k(ps, k_qproj<STARKV_BF16, STARKV_LATENT_BF16, false>, gq, dim3(256), s, qa);
+      else e = launch_k(ps, k_qproj<STARKV_BF16, STARKV_LATENT_MIX84, false>, gq, dim3(256), s, qa);
+    }
     if (e != hipSuccess) return e;
   }
   return launch_decode_tail(L, plan, kts, seq, out, k_rows, v_tiles, s);

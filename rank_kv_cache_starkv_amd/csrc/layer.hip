@@ -335,4 +335,43 @@ hipError_t launch_build_factors(const Layer& L, const float* U_k, const float* V
   return build_factors_t<uint16_t>(L, U_k, V_k, U_v, V_v, A_t, B_k, B_vt, s);
 }
 
+// Weight absorption of the key factors into the query projection (Methodology section 2: the
+// reconstruction matrices move past the attention product, here into W_q): for query head h of
+// KV head g = h / G (rank r_g, first key channel c0) and k < r_g,
+//   wqk[G c0 + (h mod G) r_g + k][e] = sum_c W_q[e][h d_h + c] * B_k[c0 + k][c]
+// summed in fp64 and kept in fp32 (no rounding to the layer dtype).  Grid (ceil(d / 256), H_q,
+// largest rank); threads past d or the head's rank exit.
+template <int DT>
+__global__ __launch_bounds__(256) void k_absorb_query(const void* __restrict__ W_q, const void* __restrict__ B_k,
+                                                      const int* __restrict__ koff, int G, int H_q, int d_h, int d,
+                                                      float* __restrict__ wqk) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  const int h = blockIdx.y, k = blockIdx.z;
+  const int g = h / G, hh = h % G;
+  const int c0 = koff[g], r = koff[g + 1] - c0;
+  if (e >= d || k >= r) return;
+  const size_t wrow = (size_t)e * H_q * d_h + (size_t)h * d_h;
+  const size_t brow = (size_t)(c0 + k) * d_h;
+  double acc = 0.0;
+  for (int c = 0; c < d_h; ++c) {
+    const float w = DT == STARKV_F32 ? ((const float*)W_q)[wrow + c] : bf16_to_f32(((const uint16_t*)W_q)[wrow + c]);
+    const float bb = DT == STARKV_F32 ? ((const float*)B_k)[brow + c] : bf16_to_f32(((const uint16_t*)B_k)[brow + c]);
+    acc += (double)w * (double)bb;
+  }
+  wqk[((size_t)G * c0 + (size_t)hh * r + k) * d + e] = (float)acc;
+}
+
+hipError_t launch_absorb_query(const Layer& L, const void* W_q, float* wqk, hipStream_t s) {
+  int rmax = 1;
+  for (int g = 0; g < L.H_kv; ++g) rmax = std::max(rmax, L.rk[g]);
+  const dim3 grid((L.d + 255) / 256, L.H_q, rmax);
+  if (L.dtype == STARKV_F32)
+    hipLaunchKernelGGL(k_absorb_query<STARKV_F32>, grid, dim3(256), 0, s, W_q, L.B_k, (const int*)L.d_koff, L.G,
+                       L.H_q, L.d_h, L.d, wqk);
+  else
+    hipLaunchKernelGGL(k_absorb_query<STARKV_BF16>, grid, dim3(256), 0, s, W_q, L.B_k, (const int*)L.d_koff, L.G,
+                       L.H_q, L.d_h, L.d, wqk);
+  return hipGetLastError();
+}
+
 }  // namespace skv

@@ -67,6 +67,7 @@ struct Layer {
   int* d_src = nullptr;        // [n_lat] (head << 16) | local index; head = H_kv for values
   int* d_rot = nullptr;        // [n_lat] rotated factors: (first channel of the Hadamard piece << 5) | log2(order)
   uint32_t* d_absmax = nullptr;  // [n_lat] calibration scratch
+  float* d_wqk = nullptr;        // [G * n_key][d] absorbed query factors W_q^h B_g^T (owned; null: none)
   // bound buffers (borrowed)
   const void* A_t = nullptr;
   const void* B_k = nullptr;
@@ -81,7 +82,7 @@ struct Layer {
 // decode plan (host-built per call, passed by value to the kernels)
 
 struct DecodeGeom {
-  int B, n_q, M_q, M_pad, nct, G, d_h, H_q, H_kv;
+  int B, n_q, M_q, M_pad, nct, G, d_h, H_q, H_kv, d;
   int n_key, r_v, K8, K4, key_kt, key_kpos, k_row_bytes, v_rows, v_tile_bytes, T_max;
   int rv_ld;  // row stride (elements) of the value-latent workspace rows: r_v rounded up to 32
   int latent, dtype;
@@ -146,8 +147,14 @@ struct DecodePlan {
 int plan_decode(const Layer& L, int B, int n_q, const int32_t* lens, int T_max, void* ws_base, DecodePlan* plan,
                 KtList* kts, SeqTable* seq);
 
+// q: [B][n_q][H_q][d_h] queries, or with wqk set [B][n_q][d] hidden states whose query
+// projection is absorbed into wqk
 hipError_t launch_decode(const Layer& L, const DecodePlan& plan, const KtList& kts, const SeqTable& seq,
-                         const void* q, void* out, const void* k_rows, const void* v_tiles, hipStream_t s);
+                         const void* q, void* out, const void* k_rows, const void* v_tiles, hipStream_t s,
+                         const float* wqk = nullptr);
+
+// Absorbed query factors: wqk[G r_g-row block of head h][e] = sum_c W_q[e][h d_h + c] B_k[row][c].
+hipError_t launch_absorb_query(const Layer& L, const void* W_q, float* wqk, hipStream_t s);
 
 // A decode step: append n_q new tokens per sequence at lens_pre, then decode attention over
 // plan's lengths (lens_pre + n_q); few new rows run the append and the query projection in one

@@ -44,6 +44,8 @@ _PURPOSE = {
     "q": 7,
     "lens": 8,
     "misc": 9,
+    "W_q": 10,
+    "x_q": 11,
 }
 
 
@@ -276,6 +278,17 @@ def x_calibration(w: Workload, layer: int = 0) -> np.ndarray:
 def x_new(w: Workload, n_new: int, layer: int = 0, step: int = 0) -> np.ndarray:
     """Hidden states of the tokens appended in one step: [B, n_new, d]."""
     return gaussian(rng_for(w.cfg_id, layer, "x_new", step), (w.B, n_new, w.d))
+
+
+def query_weights(w: Workload, layer: int = 0) -> np.ndarray:
+    """Synthetic query projection W_q [d, H_q * d_h] (q = x W_q), Gaussian / sqrt(d)."""
+    g = gaussian(rng_for(w.cfg_id, layer, "W_q"), (w.d, w.H_q * w.d_h))
+    return (g / np.float32(math.sqrt(w.d))).astype(np.float32)
+
+
+def query_hidden(w: Workload, layer: int = 0, step: int = 0) -> np.ndarray:
+    """Hidden states of the decode queries [B, n_q, d]."""
+    return gaussian(rng_for(w.cfg_id, layer, "x_q", step), (w.B, w.n_q, w.d))
 
 
 def queries(w: Workload, layer: int = 0, step: int = 0, scale: float = 1.0) -> np.ndarray:

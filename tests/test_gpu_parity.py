@@ -104,6 +104,36 @@ def test_mini_parity(cfg, exact):
         H.check_output(w, got[b], ref, f"seq {b} len {int(run.lens[b])}")
 
 
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 5])
+def test_absorbed_query_from_hidden(cfg):
+    """Decode with the query taken from hidden states through the absorbed factors W_q^h B_g^T,
+    against the oracle's q = x W_q followed by the same attention."""
+    from rank_kv_cache_starkv_amd import StarKVError
+    w, run = _run_mini(cfg, exact=True)
+    B = len(run.lens)
+    x = I.as_dtype(I.query_hidden(dataclasses.replace(w, B=B)), w.dtype)
+    W = I.as_dtype(I.query_weights(w), w.dtype)
+    xd, Wd = H.to_dev(x, w.dtype), H.to_dev(W, w.dtype)
+    with pytest.raises(StarKVError) as ei:
+        run.GL.decode_hidden(run.cache, xd, run.lens)
+    assert ei.value.status == -7  # ESTATE: nothing absorbed yet
+    run.GL.absorb_query(Wd)
+    out = run.GL.decode_hidden(run.cache, xd, run.lens)
+    out2 = run.GL.decode_hidden(run.cache, xd, run.lens)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2), "determinism"
+    got = H.from_dev(out)
+    for b in run.oracle_seqs:
+        q = O.query_from_hidden(x[b], W, w.H_q, w.d_h)
+        ref = O.decode(q, run.ocache[b], run.OL, w.n_q, run.scales_o)
+        H.check_output(w, got[b], ref, f"hidden-state query seq {b} len {int(run.lens[b])}")
+    # binding factors again drops the absorbed ones
+    run.GL.bind_factors(run.GL.A_t, run.GL.B_k, run.GL.B_vt)
+    with pytest.raises(StarKVError) as ei:
+        run.GL.decode_hidden(run.cache, xd, run.lens)
+    assert ei.value.status == -7
+
+
 @pytest.mark.parametrize("cfg", [0, 2, 4, 5])
 @pytest.mark.parametrize("q_scale", [30.0, 300.0])
 def test_mini_softmax_stress(cfg, q_scale):

@@ -495,3 +495,21 @@ def test_accounting_closed_forms():
     # Methodology section 2: joint decomposition costs h times the reconstruction of head-wise
     for H in (8, 32, 40):
         assert acc.reconstruction_flops_per_token(1024, H, 128, True) == H * acc.reconstruction_flops_per_token(1024, H, 128, False)
+
+
+def test_query_from_hidden_special_cases():
+    """The query projection of hidden states: with an identity projection the query is the
+    hidden state itself, head by head; on a tiny projection it matches the sum written out."""
+    rng = np.random.default_rng(11)
+    H_q, d_h = 3, 4
+    x = rng.standard_normal((2, H_q * d_h))
+    np.testing.assert_array_equal(O.query_from_hidden(x, np.eye(H_q * d_h), H_q, d_h), x.reshape(2, H_q, d_h))
+    d = 5
+    x = rng.standard_normal((2, d))
+    W = rng.standard_normal((d, H_q * d_h))
+    q = O.query_from_hidden(x, W, H_q, d_h)
+    for j in range(2):
+        for h in range(H_q):
+            for c in range(d_h):
+                ref = sum(x[j, e] * W[e, h * d_h + c] for e in range(d))
+                assert abs(q[j, h, c] - ref) <= 1e-12 * max(1.0, abs(ref))
