@@ -55,8 +55,10 @@ def to_dev_bf16(x: np.ndarray, dev: str):
 QUANTIZED = {"mix84": 4, "had43": 5}
 
 
-def algorithmic_bytes(w, ranks, r_v, lens, n_q):
-    """Bytes the method must move per step (each latent once, factors once, q, out, X_new, A)."""
+def algorithmic_bytes(w, ranks, r_v, lens, n_q, hidden=False):
+    """Bytes the method must move per step (each latent once, factors once, q, out, X_new, A).
+    hidden: the query projection reads hidden states [B, n_q, d] and the absorbed fp32 factors
+    W_q^h B_g^T (G n_key x d) instead of q and B_k."""
     elem = {"f32": 4, "bf16": 2}[w.dtype]
     if w.latent in QUANTIZED:
         # bytes of the int8 region (leading quarter, or the outlier fifth) + the int4 region
@@ -73,8 +75,11 @@ def algorithmic_bytes(w, ranks, r_v, lens, n_q):
     n_key = int(sum(ranks))
     tokens = float(np.sum(lens))
     qo = w.B * n_q * w.H_q * w.d_h * elem
+    qproj = qo + n_key * w.d_h * elem + scale_k
+    if hidden:
+        qproj = w.B * n_q * w.d * elem + (w.H_q // w.H_kv) * n_key * w.d * 4 + scale_k
     b = {
-        "decode_qproj": qo + n_key * w.d_h * elem + scale_k,
+        "decode_qproj": qproj,
         "decode_scores": tokens * key_tok,
         "decode_values": tokens * val_tok,
         "decode_zmerge": scale_v,
@@ -232,6 +237,9 @@ def main() -> int:
     ap.add_argument("--layers", type=int, default=0, help="layers to rotate (0: enough for 1 GiB)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--hidden-query", action="store_true",
+                    help="queries from hidden states through the absorbed factors W_q B_g^T (step = append, "
+                         "then starkv_decode_attention_hidden); no CPU baseline")
     ap.add_argument("--copy-probe", action="store_true", help=f"copy {COPY_PROBE_MIB} MiB device to device")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"))
     args = ap.parse_args()
@@ -319,6 +327,22 @@ def main() -> int:
         li = i % n_layers
         layers[li].step(caches[li], X_step, q, lens, out=outs[li], ws=ws)
 
+    if args.hidden_query:
+        # each layer absorbs its own synthetic W_q [d, H_q d_h]; the step appends, then attends
+        # with the queries formed from hidden states inside the query projection
+        for L in layers:
+            Wq = (torch.randn((w.d, w.H_q * w.d_h), generator=gen, device=dev, dtype=torch.float32)
+                  / math.sqrt(w.d)).to(tdt)
+            L.absorb_query(Wq)
+            del Wq
+        xq_np = I.as_dtype(I.query_hidden(w), w.dtype)
+        x_q = to_dev_bf16(xq_np, dev) if w.dtype == "bf16" else torch.from_numpy(xq_np).to(dev)
+
+        def step(i):  # noqa: F811
+            li = i % n_layers
+            layers[li].append(caches[li], X_step, lens_pre)
+            layers[li].decode_hidden(caches[li], x_q, lens, out=outs[li], ws=ws)
+
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -372,10 +396,10 @@ def main() -> int:
     for k, us in sorted(kern_us.items()):
         log(f"[kernel] {k:14s} {us:9.2f} us/launch ({prof[k][0]} launches)")
 
-    ab = algorithmic_bytes(w, probe.ranks, probe.r_v, lens, n_q)
+    ab = algorithmic_bytes(w, probe.ranks, probe.r_v, lens, n_q, hidden=args.hidden_query)
     dom = max((k for k in kern_us if k.startswith("decode_")), key=lambda k: kern_us[k])
     achieved = ab[dom] / (kern_us[dom] * 1e-6) / 1e9
-    traffic = traffic_for(dom, w.name)
+    traffic = None if args.hidden_query else traffic_for(dom, w.name)  # counters cover the q path only
     qps = w.B * n_q / (ms_step * 1e-3)
     dec_us = sum(us for k, us in kern_us.items() if k.startswith("decode_"))
     result = {
@@ -395,7 +419,8 @@ def main() -> int:
         "config": {"workload": w.name, "batch": w.B, "context": int(lens.max()) if not w.ragged else "ragged",
                    "context_tokens": int(lens.sum()), "queries_per_seq": n_q, "H_q": w.H_q, "H_kv": w.H_kv,
                    "d_h": w.d_h, "hidden": w.d, "key_rank_sum": int(np.sum(probe.ranks)), "value_rank": probe.r_v,
-                   "latent": w.latent, "layers_rotated": n_layers},
+                   "latent": w.latent, "layers_rotated": n_layers,
+                   "query": "hidden states, absorbed W_q B_g^T" if args.hidden_query else "q"},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                      "alg_bytes_per_launch": ab[dom], "us_per_launch": kern_us[dom]},
@@ -409,7 +434,7 @@ def main() -> int:
         "kernel_us": kern_us,
         "alg_bytes": ab,
     }
-    if not args.no_cpu:
+    if not args.no_cpu and not args.hidden_query:
         t0 = time.perf_counter()
         result["cpu_baseline"] = cpu_baseline(w, lf, lens, n_q, X0, Xcal, q_np, X_np, args.cpu_budget)
         log(f"[cpu] {time.perf_counter() - t0:.1f} s")

@@ -292,6 +292,7 @@ struct QprojArgs {
   const void* q;        // queries [B][n_q][H_q][d_h], or hidden states [B][n_q][d] when wqk is set
   const void* B_k;
   const float* wqk;     // absorbed query factors [G n_key][d] (fp32), or null
+  int nrg;              // row groups per (KV head, sequence) of the hidden-state projection grid
   const uint16_t* scales;
   HeadTables heads;
   uint8_t* qfrag;
@@ -573,11 +574,23 @@ __device__ __forceinline__ void qproj_body(const QprojArgs& a, int gk, int b, in
   }
 }
 
-// HID: the query comes from hidden states through the absorbed factors (a.wqk)
+// HID: the query comes from hidden states through the absorbed factors (a.wqk).  Its grid is
+// one dimension, workgroups dealt to the eight XCDs in turn: the k-th workgroup of XCD x takes
+// KV head x + 8 (k / (B nrg)) and, within it, sequence and row group k mod (B nrg), so the
+// workgroups of one head run one after another on one XCD and share its L2 copy of the head's
+// absorbed rows.
 template <int DT, int LAT, bool HID>
 __global__ __launch_bounds__(256) void k_qproj(QprojArgs a) {
   __shared__ QprojShared sh;
-  qproj_body<DT, LAT, 256, HID>(a, blockIdx.x, blockIdx.y, blockIdx.z, gridDim.z, sh);
+  if (!HID) {
+    qproj_body<DT, LAT, 256, false>(a, blockIdx.x, blockIdx.y, blockIdx.z, gridDim.z, sh);
+    return;
+  }
+  const int nrg = a.nrg;
+  const int k = blockIdx.x >> 3, per = a.g.B * nrg;
+  const int gk = (blockIdx.x & 7) + 8 * (k / per), rem = k % per;
+  if (gk >= a.g.H_kv) return;  // whole workgroup
+  qproj_body<DT, LAT, 256, true>(a, gk, rem / nrg, rem % nrg, nrg, sh);
 }
 
 // ===========================================================================
@@ -2391,6 +2404,7 @@ static QprojArgs qproj_args(const Layer& L, const DecodePlan& plan, const KtList
   qa.q = q;
   qa.B_k = L.B_k;
   qa.wqk = nullptr;
+  qa.nrg = 1;
   qa.scales = L.scales;
   qa.heads = L.heads();
   qa.qfrag = (uint8_t*)plan.ws.qfrag;
@@ -2451,12 +2465,15 @@ hipError_t launch_decode(const Layer& L, const DecodePlan& plan, const KtList& k
   qa.wqk = wqk;
   {
     ProfScope ps("decode_qproj");
-    const dim3 gq(g.H_kv, g.B, qproj_row_groups(g));
+    const int nrg = qproj_row_groups(g);
+    qa.nrg = nrg;
     if (wqk) {
+      const dim3 gq(8 * ((g.H_kv + 7) / 8) * g.B * nrg);
       if (L.dtype == STARKV_F32) e = launch_k(ps, k_qproj<STARKV_F32, STARKV_LATENT_F32, true>, gq, dim3(256), s, qa);
       else if (L.latent == STARKV_LATENT_BF16) e = launch_k(ps, k_qproj<STARKV_BF16, STARKV_LATENT_BF16, true>, gq, dim3(256), s, qa);
       else e = launch_k(ps, k_qproj<STARKV_BF16, STARKV_LATENT_MIX84, true>, gq, dim3(256), s, qa);
     } else {
+      const dim3 gq(g.H_kv, g.B, nrg);
       if (L.dtype == STARKV_F32) e = launch_k(ps, k_qproj<STARKV_F32, STARKV_LATENT_F32, false>, gq, dim3(256), s, qa);
       else if (L.latent == STARKV_LATENT_BF16) e = launch_k(ps, k_qproj<STARKV_BF16, STARKV_LATENT_BF16, false>, gq, dim3(256), s, qa);
       else e = launch_k(ps, k_qproj<STARKV_BF16, STARKV_LATENT_MIX84, false>, gq, dim3(256), s, qa);
