@@ -57,8 +57,9 @@ QUANTIZED = {"mix84": 4, "had43": 5}
 
 def algorithmic_bytes(w, ranks, r_v, lens, n_q, hidden=False):
     """Bytes the method must move per step (each latent once, factors once, q, out, X_new, A).
-    hidden: the query projection reads hidden states [B, n_q, d] and the absorbed fp32 factors
-    W_q^h B_g^T (G n_key x d) instead of q and B_k."""
+    hidden: the hidden states [B, n_q, d] meet the absorbed factors W_q^h B_g^T (G n_key x d,
+    4 bytes per element) in a GEMM that writes the raw projection (fp32), which the query
+    projection then reads instead of q and B_k."""
     elem = {"f32": 4, "bf16": 2}[w.dtype]
     if w.latent in QUANTIZED:
         # bytes of the int8 region (leading quarter, or the outlier fifth) + the int4 region
@@ -76,8 +77,9 @@ def algorithmic_bytes(w, ranks, r_v, lens, n_q, hidden=False):
     tokens = float(np.sum(lens))
     qo = w.B * n_q * w.H_q * w.d_h * elem
     qproj = qo + n_key * w.d_h * elem + scale_k
+    raw = w.B * n_q * (w.H_q // w.H_kv) * n_key * 4
     if hidden:
-        qproj = w.B * n_q * w.d * elem + (w.H_q // w.H_kv) * n_key * w.d * 4 + scale_k
+        qproj = raw + scale_k
     b = {
         "decode_qproj": qproj,
         "decode_scores": tokens * key_tok,
@@ -87,6 +89,8 @@ def algorithmic_bytes(w, ranks, r_v, lens, n_q, hidden=False):
         "append": w.B * n_q * w.d * elem + (n_key + r_v) * w.d * elem + w.B * n_q * (key_tok + val_tok)
         + scale_k + scale_v,
     }
+    if hidden:
+        b["decode_hidden_q"] = w.B * n_q * w.d * elem + (w.H_q // w.H_kv) * n_key * w.d * 4 + raw
     b["decode"] = sum(v for k, v in b.items() if k.startswith("decode_"))
     b["step"] = b["decode"] + b["append"]
     b["step_front"] = b["append"] + b["decode_qproj"]  # fused launch: append + query projection

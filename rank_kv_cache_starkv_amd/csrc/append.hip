@@ -20,10 +20,10 @@
 
 namespace skv {
 
-template <int DT, int SW, bool MIX>
+template <int DT, int SW, bool MIX, int MODE = 0>
 __global__ __launch_bounds__(512) void k_latent_gemm_skinny(GemmArgs a) {
   __shared__ float red[7][4][64];
-  skinny_body<DT, SW, MIX>(a, blockIdx.x, red);
+  skinny_body<DT, SW, MIX, 8, MODE>(a, blockIdx.x, red);
 }
 
 // NW waves (4 or 8) split K; with 8, waves 4-7 hand their partial tiles to waves 0-3 first.
@@ -200,6 +200,10 @@ __global__ __launch_bounds__(64 * NW) void k_latent_gemm(GemmArgs a) {
     xs[v] = accq[v];
     ms[v] = m0 + d32_row(v0 + v, q);
   }
+  if (MODE >= 2) {
+    store_raw<MODE, NVW>(a, slot, xs, ms);
+    return;
+  }
   int ps[NVW];
 #pragma unroll
   for (int v = 0; v < NVW; ++v) ps[v] = row_pos(a, ms[v]);
@@ -308,6 +312,66 @@ hipError_t launch_append(const Layer& L, const starkv_cache& c, const void* X_ne
   }
   if (e != hipSuccess) return e;
   return hipGetLastError();
+}
+
+// Hidden-state query projection through the absorbed factors: out[m][c] = sum_e x[m][e] wqk[c][e]
+// for the M = B n_q rows and the NS = G n_key absorbed columns, on the append GEMMs with a raw
+// fp32 epilogue.  bf16 layers keep the factors as bf16 high and low parts (wqk_hi, wqk_lo), so
+// the product takes two passes (store, then add); fp32 layers take one.
+// One launch, with the timing events attached when given.
+template <typename A>
+static hipError_t launch_ev(void (*kernel)(A), dim3 grid, dim3 block, hipStream_t s, A arg, hipEvent_t start,
+                            hipEvent_t stop) {
+  void* argv[] = {(void*)&arg};
+  if (start || stop) return hipExtLaunchKernel((const void*)kernel, grid, block, argv, 0, s, start, stop, 0);
+  return hipLaunchKernel((const void*)kernel, grid, block, argv, 0, s);
+}
+
+hipError_t launch_hidden_query(const Layer& L, const void* x, int M, const void* wqk_hi, const void* wqk_lo,
+                               float* out, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
+  GemmArgs a = {};
+  a.X = x;
+  a.M = M;
+  a.d = L.d;
+  a.NS = L.G * L.n_key;
+  a.n_key = a.NS;  // every column is a live channel (slot = channel)
+  a.key_slots = a.NS;
+  a.r_v = 0;
+  a.latent = STARKV_LATENT_F32;  // not the int8/int4 table layout
+  a.n_new = 1;
+  a.xmap_rt = 0;
+  a.out_f32 = out;
+  const bool bf = L.dtype == STARKV_BF16;
+  const int n_pass = bf ? 2 : 1;
+  hipError_t e = hipSuccess;
+  for (int pass = 0; pass < n_pass && e == hipSuccess; ++pass) {
+    a.A_t = pass == 0 ? wqk_hi : wqk_lo;
+    const hipEvent_t e0 = pass == 0 ? start : nullptr, e1 = pass == n_pass - 1 ? stop : nullptr;
+    void (*kern)(GemmArgs);
+    dim3 grid, block;
+    if (M <= 16 && L.d % 32 == 0) {
+      grid = dim3((a.NS + 15) / 16);
+      block = dim3(512);
+      kern = !bf ? k_latent_gemm_skinny<STARKV_F32, 16, false, 2>
+                 : (pass == 0 ? k_latent_gemm_skinny<STARKV_BF16, 16, false, 2> : k_latent_gemm_skinny<STARKV_BF16, 16, false, 3>);
+    } else {
+      const int n_rt = (M + 63) / 64, n_ct = (a.NS + 63) / 64;
+      a.xmap_rt = n_rt <= 16 ? n_rt : 0;
+      if (a.xmap_rt > 0) {
+        grid = dim3(8 * n_rt * ((n_ct + 7) / 8));
+        block = dim3(512);
+        kern = !bf ? k_latent_gemm<STARKV_F32, 2, 8>
+                   : (pass == 0 ? k_latent_gemm<STARKV_BF16, 2, 8> : k_latent_gemm<STARKV_BF16, 3, 8>);
+      } else {
+        grid = dim3(n_rt, n_ct);
+        block = dim3(256);
+        kern = !bf ? k_latent_gemm<STARKV_F32, 2, 4>
+                   : (pass == 0 ? k_latent_gemm<STARKV_BF16, 2, 4> : k_latent_gemm<STARKV_BF16, 3, 4>);
+      }
+    }
+    e = launch_ev(kern, grid, block, s, a, e0, e1);
+  }
+  return e;
 }
 
 }  // namespace skv

@@ -266,6 +266,7 @@ int plan_decode(const Layer& L, int B, int n_q, const int32_t* lens, int T_max, 
   const size_t o_sl = o; o = align256(o + (size_t)total_splits * g.M_pad * 4);
   const size_t o_sm = o; o = align256(o + (size_t)total_splits * g.M_pad * 4);
   const size_t o_zt = o; o = align256(o + (size_t)B * g.M_pad * g.rv_ld * 4);
+  const size_t o_qraw = o; o = align256(o + (size_t)B * n_q * L.G * L.n_key * 4);
   P->ws_bytes = o;
   uint8_t* base = (uint8_t*)ws_base;
   w.qfrag = base + o_qfrag;
@@ -277,6 +278,7 @@ int plan_decode(const Layer& L, int B, int n_q, const int32_t* lens, int T_max, 
   w.sl = (float*)(base + o_sl);
   w.sm = (float*)(base + o_sm);
   w.zt = (float*)(base + o_zt);
+  w.qraw = (float*)(base + o_qraw);
   w.nkt_max = nkt_max;
   w.total_chunks = total_chunks;
   w.total_splits = total_splits;
@@ -291,7 +293,8 @@ int plan_decode(const Layer& L, int B, int n_q, const int32_t* lens, int T_max, 
 struct QprojArgs {
   const void* q;        // queries [B][n_q][H_q][d_h], or hidden states [B][n_q][d] when wqk is set
   const void* B_k;
-  const float* wqk;     // absorbed query factors [G n_key][d] (fp32), or null
+  const float* wqk;     // absorbed path: non-null (the projection x wqk^T is in qraw)
+  const float* qraw;    // [B n_q][G n_key] hidden-state query projection
   int nrg;              // row groups per (KV head, sequence) of the hidden-state projection grid
   const uint16_t* scales;
   HeadTables heads;
@@ -358,46 +361,13 @@ __device__ __forceinline__ void qproj_body(const QprojArgs& a, int gk, int b, in
       const int p = ps / SUB, sub = ps % SUB;
       const int n = p / r, k = p % r;
       if (HID) {
-        // hidden state x_(b, j) against the absorbed factor row of (query head, k): length d,
-        // 8 elements per lane piece (x: one 16-byte bf16 load or two fp32; wqk: two fp32)
+        // hidden-state query: the projection x_(b, j) . wqk[row of (query head, k)] is in qraw
         const int i = gk * rph + rb0 + n;
         const int hh = (i % rph) / g.n_q, j = i % g.n_q;
-        const size_t xoff = ((size_t)b * g.n_q + j) * g.d;
-        const float* wr = a.wqk + ((size_t)g.G * c0 + (size_t)hh * r + k) * g.d;
-        float acc = 0.f;
-        for (int e0 = 0; e0 < g.d; e0 += SUB * NX * 8) {
-          u32x4 xv[NX][2], wv[NX][2];
-#pragma unroll
-          for (int x = 0; x < NX; ++x) {
-            const int ee = min(e0 + (x * SUB + sub) * 8, g.d - 8);
-            if (DT == STARKV_F32) {
-              xv[x][0] = ld16((const float*)a.q + xoff + ee);
-              xv[x][1] = ld16((const float*)a.q + xoff + ee + 4);
-            } else {
-              xv[x][0] = ld16((const uint16_t*)a.q + xoff + ee);
-              xv[x][1] = xv[x][0];
-            }
-            wv[x][0] = ld16(wr + ee);
-            wv[x][1] = ld16(wr + ee + 4);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int x = 0; x < NX; ++x) {
-            const bool live = e0 + (x * SUB + sub) * 8 < g.d;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              float xe;
-              if (DT == STARKV_F32) xe = __uint_as_float(xv[x][e >> 2][e & 3]);
-              else xe = bf16_to_f32((uint16_t)((xv[x][0][e >> 1] >> (16 * (e & 1))) & 0xFFFF));
-              acc = fmaf(live ? xe : 0.f, __uint_as_float(wv[x][e >> 2][e & 3]), acc);
-            }
-          }
-        }
-#pragma unroll
-        for (int o = 1; o < SUB; o <<= 1) acc += __shfl_xor(acc, o, 64);
         float sc = 1.f;
         if (LAT == STARKV_LATENT_MIX84) sc = f16_to_f32(a.scales[c0 + k]);
-        if (sub == 0) qh[n][k] = acc * sc * g.qscale;
+        const float v = a.qraw[((size_t)b * g.n_q + j) * ((size_t)g.G * g.n_key) + (size_t)g.G * c0 + hh * r + k];
+        if (sub == 0) qh[n][k] = v * sc * g.qscale;
         continue;
       }
       const int i = gk * rph + rb0 + n;
@@ -2404,6 +2374,7 @@ static QprojArgs qproj_args(const Layer& L, const DecodePlan& plan, const KtList
   qa.q = q;
   qa.B_k = L.B_k;
   qa.wqk = nullptr;
+  qa.qraw = plan.ws.qraw;
   qa.nrg = 1;
   qa.scales = L.scales;
   qa.heads = L.heads();
@@ -2463,6 +2434,14 @@ hipError_t launch_decode(const Layer& L, const DecodePlan& plan, const KtList& k
   // 1. query fragments
   QprojArgs qa = qproj_args(L, plan, kts, q);
   qa.wqk = wqk;
+  if (wqk) {
+    // hidden-state queries: x wqk^T for all heads (the absorbed factors) into qraw
+    ProfScope ps("decode_hidden_q");
+    const size_t half = (size_t)L.G * L.n_key * L.d;  // bf16 high part, then low part
+    e = launch_hidden_query(L, q, g.B * g.n_q, wqk, (const uint16_t*)wqk + half, plan.ws.qraw, s, ps.start(),
+                            ps.stop());
+    if (e != hipSuccess) return e;
+  }
   {
     ProfScope ps("decode_qproj");
     const int nrg = qproj_row_groups(g);

@@ -31,7 +31,20 @@ struct GemmArgs {
   int lens[kMaxB];
   // calibrate
   uint32_t* absmax;
+  // raw fp32 output [M][NS] (the hidden-state query projection): MODE 2 stores, MODE 3 adds
+  float* out_f32;
 };
+
+// MODE 2 / 3 epilogue: out_f32[m][slot] = x (MODE 2) or += x (MODE 3), rows < M and slots < NS.
+template <int MODE, int R>
+__device__ __forceinline__ void store_raw(const GemmArgs& a, int slot, const float* xs, const int* ms) {
+#pragma unroll
+  for (int v = 0; v < R; ++v) {
+    if (ms[v] >= a.M || slot >= a.NS) continue;
+    float* o = a.out_f32 + (size_t)ms[v] * a.NS + slot;
+    *o = MODE == 3 ? *o + xs[v] : xs[v];
+  }
+}
 
 template <int DT>
 __device__ __forceinline__ void load_frag8(const void* base, size_t elem_off, bool ok, u32x4& lo, u32x4& hi) {
@@ -162,7 +175,7 @@ __device__ __forceinline__ int slot_channel_nb(const GemmArgs& a, int slot) {
 // past M read row 0 and are never stored; padding slots read channel 0 with the A_t operand
 // zeroed).  The cache positions of the output rows are fetched at the start.
 // 16x16x32 bf16 MFMA (16x16x4 f32 for the fp32 path).
-template <int DT, int SW, bool MIX, int NWV = 8>
+template <int DT, int SW, bool MIX, int NWV = 8, int MODE = 0>
 __device__ __forceinline__ void skinny_body(const GemmArgs& a, int blk, float (*red)[4][64]) {
   constexpr bool HALF = SW == 8;
   // K-steps per load batch: a wave's whole range with 8 waves; at most 32 16-byte loads per lane
@@ -254,7 +267,8 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& a, int blk, float (*
     if (HALF) x += __shfl(x, (lane + 40) & 63, 64);
     xs[v] = x;  // D row = token row; D column = n
   }
-  store_latent<4>(a, bslot, bchan, sc_bits, xs, ms, ps);
+  if (MODE >= 2) store_raw<MODE, 4>(a, bslot, xs, ms);
+  else store_latent<4>(a, bslot, bchan, sc_bits, xs, ms, ps);
 }
 
 // Host side: argument blocks of the latent GEMM for a layer, and for an append into a cache.

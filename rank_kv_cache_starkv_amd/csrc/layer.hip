@@ -339,12 +339,14 @@ hipError_t launch_build_factors(const Layer& L, const float* U_k, const float* V
 // reconstruction matrices move past the attention product, here into W_q): for query head h of
 // KV head g = h / G (rank r_g, first key channel c0) and k < r_g,
 //   wqk[G c0 + (h mod G) r_g + k][e] = sum_c W_q[e][h d_h + c] * B_k[c0 + k][c]
-// summed in fp64 and kept in fp32 (no rounding to the layer dtype).  Grid (ceil(d / 256), H_q,
-// largest rank); threads past d or the head's rank exit.
+// summed in fp64 and kept in fp32 (no rounding to the layer dtype): as fp32 for fp32 layers, and
+// for bf16 layers as a bf16 high part [rows][d] followed by a bf16 low part [rows][d] (the value
+// minus the high part, rounded), the operands of the two bf16 MFMA passes of the projection.
+// Grid (ceil(d / 256), H_q, largest rank); threads past d or the head's rank exit.
 template <int DT>
 __global__ __launch_bounds__(256) void k_absorb_query(const void* __restrict__ W_q, const void* __restrict__ B_k,
                                                       const int* __restrict__ koff, int G, int H_q, int d_h, int d,
-                                                      float* __restrict__ wqk) {
+                                                      int rows, float* __restrict__ wqk) {
   const int e = blockIdx.x * 256 + threadIdx.x;
   const int h = blockIdx.y, k = blockIdx.z;
   const int g = h / G, hh = h % G;
@@ -358,7 +360,16 @@ __global__ __launch_bounds__(256) void k_absorb_query(const void* __restrict__ W
     const float bb = DT == STARKV_F32 ? ((const float*)B_k)[brow + c] : bf16_to_f32(((const uint16_t*)B_k)[brow + c]);
     acc += (double)w * (double)bb;
   }
-  wqk[((size_t)G * c0 + (size_t)hh * r + k) * d + e] = (float)acc;
+  const size_t o = ((size_t)G * c0 + (size_t)hh * r + k) * d + e;
+  const float v = (float)acc;
+  if (DT == STARKV_F32) {
+    wqk[o] = v;
+  } else {
+    const uint16_t hi = f32_to_bf16(v);
+    uint16_t* w16 = (uint16_t*)wqk;
+    w16[o] = hi;
+    w16[(size_t)rows * d + o] = f32_to_bf16(v - bf16_to_f32(hi));
+  }
 }
 
 hipError_t launch_absorb_query(const Layer& L, const void* W_q, float* wqk, hipStream_t s) {
@@ -367,10 +378,10 @@ hipError_t launch_absorb_query(const Layer& L, const void* W_q, float* wqk, hipS
   const dim3 grid((L.d + 255) / 256, L.H_q, rmax);
   if (L.dtype == STARKV_F32)
     hipLaunchKernelGGL(k_absorb_query<STARKV_F32>, grid, dim3(256), 0, s, W_q, L.B_k, (const int*)L.d_koff, L.G,
-                       L.H_q, L.d_h, L.d, wqk);
+                       L.H_q, L.d_h, L.d, L.G * L.n_key, wqk);
   else
     hipLaunchKernelGGL(k_absorb_query<STARKV_BF16>, grid, dim3(256), 0, s, W_q, L.B_k, (const int*)L.d_koff, L.G,
-                       L.H_q, L.d_h, L.d, wqk);
+                       L.H_q, L.d_h, L.d, L.G * L.n_key, wqk);
   return hipGetLastError();
 }
 

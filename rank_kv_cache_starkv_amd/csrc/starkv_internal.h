@@ -67,7 +67,8 @@ struct Layer {
   int* d_src = nullptr;        // [n_lat] (head << 16) | local index; head = H_kv for values
   int* d_rot = nullptr;        // [n_lat] rotated factors: (first channel of the Hadamard piece << 5) | log2(order)
   uint32_t* d_absmax = nullptr;  // [n_lat] calibration scratch
-  float* d_wqk = nullptr;        // [G * n_key][d] absorbed query factors W_q^h B_g^T (owned; null: none)
+  float* d_wqk = nullptr;        // [G * n_key][d] absorbed query factors W_q^h B_g^T, fp32 or bf16 hi + lo
+                                 // (owned; null: none)
   // bound buffers (borrowed)
   const void* A_t = nullptr;
   const void* B_k = nullptr;
@@ -128,6 +129,7 @@ struct DecodeWs {
   float* sl;        // [total_splits][M_pad] split sum of the probabilities, weighted against sm
   float* sm;        // [total_splits][M_pad] split maximum of the base-2 logits (the weights' reference)
   float* zt;        // [B][M_pad][rv_ld] merged value latent (scaled, normalised; zero padding)
+  float* qraw;      // [B n_q][G n_key] hidden-state query projection (absorbed path)
   int nkt_max;
   int total_chunks, total_splits;
   int cps;          // score chunks per value split
@@ -153,8 +155,14 @@ hipError_t launch_decode(const Layer& L, const DecodePlan& plan, const KtList& k
                          const void* q, void* out, const void* k_rows, const void* v_tiles, hipStream_t s,
                          const float* wqk = nullptr);
 
-// Absorbed query factors: wqk[G r_g-row block of head h][e] = sum_c W_q[e][h d_h + c] B_k[row][c].
+// Absorbed query factors: wqk[G r_g-row block of head h][e] = sum_c W_q[e][h d_h + c] B_k[row][c]
+// (fp32; bf16 layers: bf16 high part then bf16 low part, the same bytes).
 hipError_t launch_absorb_query(const Layer& L, const void* W_q, float* wqk, hipStream_t s);
+
+// out[m][c] = x[m] . wqk[c] for M hidden rows and the G n_key absorbed columns (fp32 out); the
+// timing events start, stop (either may be null) bracket all of its launches.
+hipError_t launch_hidden_query(const Layer& L, const void* x, int M, const void* wqk_hi, const void* wqk_lo,
+                               float* out, hipStream_t s, hipEvent_t start, hipEvent_t stop);
 
 // A decode step: append n_q new tokens per sequence at lens_pre, then decode attention over
 // plan's lengths (lens_pre + n_q); few new rows run the append and the query projection in one
