@@ -429,6 +429,27 @@ def test_many_sequences(cfg):
         H.check_output(w, got[b], ref, f"seq {b} len {int(run.lens[b])}")
 
 
+@pytest.mark.parametrize("cfg", [2, 4])
+def test_max_batch_skewed_lengths(cfg):
+    """The largest batch (128 sequences) with a skewed length mix, every 16th sequence long and
+    the rest short: the longest-first XCD order of the value splits over many splits (one query
+    row tile for the 7B layer, many for the 13B-class one), against the oracle on long and short
+    sequences."""
+    lens0 = [1900 + 13 * i if i % 16 == 0 else 33 + 5 * i for i in range(128)]
+    w = dataclasses.replace(I.WORKLOADS[cfg], B=len(lens0))
+    H.log(f"[max batch, skewed] cfg={cfg} B={w.B} lens {min(lens0)}..{max(lens0)}")
+    run = H.make_layer(w, exact=True)
+    H.calibrate(run)
+    H.prefill(run, lens0, oracle_seqs=(0, 1, 64, 127), fast_fill=True)
+    if w.n_append:
+        H.append_step(run, w.n_append)
+    q = H.queries(run)
+    got = H.from_dev(H.decode(run, q))
+    for b in run.oracle_seqs:
+        ref = H.oracle_decode(run, q, b, mode="latent")
+        H.check_output(w, got[b], ref, f"seq {b} len {int(run.lens[b])}")
+
+
 def test_many_rows_many_splits():
     """64 query rows per KV head (8 sequences x 8 queries, bf16) with a sequence long enough for
     more than four value splits: the separate split merge, then the tall up-projection."""
