@@ -349,7 +349,13 @@ hipError_t launch_hidden_query(const Layer& L, const void* x, int M, const void*
     const hipEvent_t e0 = pass == 0 ? start : nullptr, e1 = pass == n_pass - 1 ? stop : nullptr;
     void (*kern)(GemmArgs);
     dim3 grid, block;
-    if (M <= 16 && L.d % 32 == 0) {
+    if (M <= 8 && L.d % 64 == 0) {
+      // twice the workgroups of the 16-row form, as in the append of at most 8 rows
+      grid = dim3((a.NS + 7) / 8);
+      block = dim3(512);
+      kern = !bf ? k_latent_gemm_skinny<STARKV_F32, 8, false, 2>
+                 : (pass == 0 ? k_latent_gemm_skinny<STARKV_BF16, 8, false, 2> : k_latent_gemm_skinny<STARKV_BF16, 8, false, 3>);
+    } else if (M <= 16 && L.d % 32 == 0) {
       grid = dim3((a.NS + 15) / 16);
       block = dim3(512);
       kern = !bf ? k_latent_gemm_skinny<STARKV_F32, 16, false, 2>
