@@ -295,7 +295,6 @@ struct QprojArgs {
   const void* B_k;
   const float* wqk;     // absorbed path: non-null (the projection x wqk^T is in qraw)
   const float* qraw;    // [B n_q][G n_key] hidden-state query projection
-  int nrg;              // row groups per (KV head, sequence) of the hidden-state projection grid
   const uint16_t* scales;
   HeadTables heads;
   uint8_t* qfrag;
@@ -544,23 +543,12 @@ __device__ __forceinline__ void qproj_body(const QprojArgs& a, int gk, int b, in
   }
 }
 
-// HID: the query comes from hidden states through the absorbed factors (a.wqk).  Its grid is
-// one dimension, workgroups dealt to the eight XCDs in turn: the k-th workgroup of XCD x takes
-// KV head x + 8 (k / (B nrg)) and, within it, sequence and row group k mod (B nrg), so the
-// workgroups of one head run one after another on one XCD and share its L2 copy of the head's
-// absorbed rows.
+// HID: the query comes from hidden states; their projection through the absorbed factors is
+// already in a.qraw.
 template <int DT, int LAT, bool HID>
 __global__ __launch_bounds__(256) void k_qproj(QprojArgs a) {
   __shared__ QprojShared sh;
-  if (!HID) {
-    qproj_body<DT, LAT, 256, false>(a, blockIdx.x, blockIdx.y, blockIdx.z, gridDim.z, sh);
-    return;
-  }
-  const int nrg = a.nrg;
-  const int k = blockIdx.x >> 3, per = a.g.B * nrg;
-  const int gk = (blockIdx.x & 7) + 8 * (k / per), rem = k % per;
-  if (gk >= a.g.H_kv) return;  // whole workgroup
-  qproj_body<DT, LAT, 256, true>(a, gk, rem / nrg, rem % nrg, nrg, sh);
+  qproj_body<DT, LAT, 256, HID>(a, blockIdx.x, blockIdx.y, blockIdx.z, gridDim.z, sh);
 }
 
 // ===========================================================================
@@ -2375,7 +2363,6 @@ static QprojArgs qproj_args(const Layer& L, const DecodePlan& plan, const KtList
   qa.B_k = L.B_k;
   qa.wqk = nullptr;
   qa.qraw = plan.ws.qraw;
-  qa.nrg = 1;
   qa.scales = L.scales;
   qa.heads = L.heads();
   qa.qfrag = (uint8_t*)plan.ws.qfrag;
@@ -2444,15 +2431,12 @@ hipError_t launch_decode(const Layer& L, const DecodePlan& plan, const KtList& k
   }
   {
     ProfScope ps("decode_qproj");
-    const int nrg = qproj_row_groups(g);
-    qa.nrg = nrg;
+    const dim3 gq(g.H_kv, g.B, qproj_row_groups(g));
     if (wqk) {
-      const dim3 gq(8 * ((g.H_kv + 7) / 8) * g.B * nrg);
       if (L.dtype == STARKV_F32) e = launch_k(ps, k_qproj<STARKV_F32, STARKV_LATENT_F32, true>, gq, dim3(256), s, qa);
       else if (L.latent == STARKV_LATENT_BF16) e = launch_k(ps, k_qproj<STARKV_BF16, STARKV_LATENT_BF16, true>, gq, dim3(256), s, qa);
       else e = launch_k(ps, k_qproj<STARKV_BF16, STARKV_LATENT_MIX84, true>, gq, dim3(256), s, qa);
     } else {
-      const dim3 gq(g.H_kv, g.B, nrg);
       if (L.dtype == STARKV_F32) e = launch_k(ps, k_qproj<STARKV_F32, STARKV_LATENT_F32, false>, gq, dim3(256), s, qa);
       else if (L.latent == STARKV_LATENT_BF16) e = launch_k(ps, k_qproj<STARKV_BF16, STARKV_LATENT_BF16, false>, gq, dim3(256), s, qa);
       else e = launch_k(ps, k_qproj<STARKV_BF16, STARKV_LATENT_MIX84, false>, gq, dim3(256), s, qa);
