@@ -316,8 +316,9 @@ hipError_t launch_append(const Layer& L, const starkv_cache& c, const void* X_ne
 
 // Hidden-state query projection through the absorbed factors: out[m][c] = sum_e x[m][e] wqk[c][e]
 // for the M = B n_q rows and the NS = G n_key absorbed columns, on the append GEMMs with a raw
-// fp32 epilogue.  bf16 layers keep the factors as bf16 high and low parts (wqk_hi, wqk_lo), so
-// the product takes two passes (store, then add); fp32 layers take one.
+// fp32 epilogue.  bf16 layers keep the factors as bf16 high and low parts (wqk_hi, wqk_lo): the
+// skinny form loads both in one pass, the tiled form takes two (store, then add); fp32 layers
+// take one.
 // One launch, with the timing events attached when given.
 template <typename A>
 static hipError_t launch_ev(void (*kernel)(A), dim3 grid, dim3 block, hipStream_t s, A arg, hipEvent_t start,
@@ -342,38 +343,37 @@ hipError_t launch_hidden_query(const Layer& L, const void* x, int M, const void*
   a.xmap_rt = 0;
   a.out_f32 = out;
   const bool bf = L.dtype == STARKV_BF16;
+  if (M <= 16 && L.d % 32 == 0) {
+    // skinny form, one launch: bf16 loads the high and low parts together (MODE 4); twice the
+    // workgroups (8 slots each) for at most 8 rows, as in the append
+    a.A_t = wqk_hi;
+    a.A_t2 = wqk_lo;
+    if (M <= 8 && L.d % 64 == 0)
+      return launch_ev(bf ? k_latent_gemm_skinny<STARKV_BF16, 8, false, 4> : k_latent_gemm_skinny<STARKV_F32, 8, false, 2>,
+                       dim3((a.NS + 7) / 8), dim3(512), s, a, start, stop);
+    return launch_ev(bf ? k_latent_gemm_skinny<STARKV_BF16, 16, false, 4> : k_latent_gemm_skinny<STARKV_F32, 16, false, 2>,
+                     dim3((a.NS + 15) / 16), dim3(512), s, a, start, stop);
+  }
+  // tiled form: bf16 takes two passes (store the high part's product, add the low part's)
   const int n_pass = bf ? 2 : 1;
   hipError_t e = hipSuccess;
+  const int n_rt = (M + 63) / 64, n_ct = (a.NS + 63) / 64;
+  a.xmap_rt = n_rt <= 16 ? n_rt : 0;
   for (int pass = 0; pass < n_pass && e == hipSuccess; ++pass) {
     a.A_t = pass == 0 ? wqk_hi : wqk_lo;
     const hipEvent_t e0 = pass == 0 ? start : nullptr, e1 = pass == n_pass - 1 ? stop : nullptr;
     void (*kern)(GemmArgs);
     dim3 grid, block;
-    if (M <= 8 && L.d % 64 == 0) {
-      // twice the workgroups of the 16-row form, as in the append of at most 8 rows
-      grid = dim3((a.NS + 7) / 8);
+    if (a.xmap_rt > 0) {
+      grid = dim3(8 * n_rt * ((n_ct + 7) / 8));
       block = dim3(512);
-      kern = !bf ? k_latent_gemm_skinny<STARKV_F32, 8, false, 2>
-                 : (pass == 0 ? k_latent_gemm_skinny<STARKV_BF16, 8, false, 2> : k_latent_gemm_skinny<STARKV_BF16, 8, false, 3>);
-    } else if (M <= 16 && L.d % 32 == 0) {
-      grid = dim3((a.NS + 15) / 16);
-      block = dim3(512);
-      kern = !bf ? k_latent_gemm_skinny<STARKV_F32, 16, false, 2>
-                 : (pass == 0 ? k_latent_gemm_skinny<STARKV_BF16, 16, false, 2> : k_latent_gemm_skinny<STARKV_BF16, 16, false, 3>);
+      kern = !bf ? k_latent_gemm<STARKV_F32, 2, 8>
+                 : (pass == 0 ? k_latent_gemm<STARKV_BF16, 2, 8> : k_latent_gemm<STARKV_BF16, 3, 8>);
     } else {
-      const int n_rt = (M + 63) / 64, n_ct = (a.NS + 63) / 64;
-      a.xmap_rt = n_rt <= 16 ? n_rt : 0;
-      if (a.xmap_rt > 0) {
-        grid = dim3(8 * n_rt * ((n_ct + 7) / 8));
-        block = dim3(512);
-        kern = !bf ? k_latent_gemm<STARKV_F32, 2, 8>
-                   : (pass == 0 ? k_latent_gemm<STARKV_BF16, 2, 8> : k_latent_gemm<STARKV_BF16, 3, 8>);
-      } else {
-        grid = dim3(n_rt, n_ct);
-        block = dim3(256);
-        kern = !bf ? k_latent_gemm<STARKV_F32, 2, 4>
-                   : (pass == 0 ? k_latent_gemm<STARKV_BF16, 2, 4> : k_latent_gemm<STARKV_BF16, 3, 4>);
-      }
+      grid = dim3(n_rt, n_ct);
+      block = dim3(256);
+      kern = !bf ? k_latent_gemm<STARKV_F32, 2, 4>
+                 : (pass == 0 ? k_latent_gemm<STARKV_BF16, 2, 4> : k_latent_gemm<STARKV_BF16, 3, 4>);
     }
     e = launch_ev(kern, grid, block, s, a, e0, e1);
   }

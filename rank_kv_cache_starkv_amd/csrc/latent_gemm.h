@@ -31,8 +31,10 @@ struct GemmArgs {
   int lens[kMaxB];
   // calibrate
   uint32_t* absmax;
-  // raw fp32 output [M][NS] (the hidden-state query projection): MODE 2 stores, MODE 3 adds
+  // raw fp32 output [M][NS] (the hidden-state query projection): MODE 2 stores, MODE 3 adds,
+  // MODE 4 (skinny form) stores X (A_t + A_t2)^T, the two parts loaded together
   float* out_f32;
+  const void* A_t2;
 };
 
 // MODE 2 / 3 epilogue: out_f32[m][slot] = x (MODE 2) or += x (MODE 3), rows < M and slots < NS.
@@ -220,7 +222,7 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& a, int blk, float (*
   const int k_beg = wave * per, k_end = min(kst_all, k_beg + per);
   f32x4 acc = {0, 0, 0, 0};
   for (int k0 = k_beg; k0 < k_end; k0 += KU) {
-    u32x4 av[KU][NL], bv[KU][NL];
+    u32x4 av[KU][NL], bv[KU][NL], bv2[KU][MODE == 4 ? NL : 1];
 #pragma unroll
     for (int j = 0; j < KU; ++j) {
       const size_t ko = (size_t)min(k0 + j, k_end - 1) * 32 + 8 * q;
@@ -229,6 +231,7 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& a, int blk, float (*
         if (DT == STARKV_BF16) {
           av[j][h] = ld16((const uint16_t*)a.X + a_base + ko);
           bv[j][h] = ld16((const uint16_t*)a.A_t + b_base + ko);
+          if (MODE == 4) bv2[j][0] = ld16((const uint16_t*)a.A_t2 + b_base + ko);
         } else {
           av[j][h] = ld16((const float*)a.X + a_base + ko + 4 * h);
           bv[j][h] = ld16((const float*)a.A_t + b_base + ko + 4 * h);
@@ -243,6 +246,10 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& a, int blk, float (*
       for (int h = 0; h < NL; ++h) bv[j][h] = live ? bv[j][h] : u32x4{0, 0, 0, 0};
       if (DT == STARKV_BF16) {
         acc = mfma16_bf16(as_bf16x8(av[j][0]), as_bf16x8(bv[j][0]), acc);
+        if (MODE == 4) {
+          const u32x4 b2 = live ? bv2[j][0] : u32x4{0, 0, 0, 0};
+          acc = mfma16_bf16(as_bf16x8(av[j][0]), as_bf16x8(b2), acc);
+        }
       } else {
 #pragma unroll
         for (int h = 0; h < NL; ++h)
