@@ -73,9 +73,10 @@ __global__ __launch_bounds__(64 * NW) void k_latent_gemm(GemmArgs a) {
       for (int v = 0; v < 16; ++v) acc[x][y][v] = 0.f;
 
   constexpr int NL = DT == STARKV_BF16 ? 1 : 2;  // 16-byte loads per operand fragment
-  constexpr int KU = DT == STARKV_BF16 ? 4 : 2;  // K-steps per batch
+  constexpr int KU = DT == STARKV_BF16 ? (MODE == 4 ? 2 : 4) : 2;  // K-steps per batch
+  constexpr int NW2 = MODE == 4 ? 2 : 1;  // MODE 4 (bf16): second operand part (low) too
   struct Batch {
-    u32x4 x[KU][2][NL], w[KU][2][NL];
+    u32x4 x[KU][2][NL], w[KU][2][NL], w2[KU][NW2][NL];
   };
   auto load = [&](Batch& f, int k0) {
 #pragma unroll
@@ -88,6 +89,7 @@ __global__ __launch_bounds__(64 * NW) void k_latent_gemm(GemmArgs a) {
           if (DT == STARKV_BF16) {
             f.x[u][h][e] = ld16((const uint16_t*)a.X + a_base[h] + ko);
             f.w[u][h][e] = ld16((const uint16_t*)a.A_t + b_base[h] + ko);
+            if (MODE == 4) f.w2[u][h % NW2][e] = ld16((const uint16_t*)a.A_t2 + b_base[h] + ko);
           } else {
             f.x[u][h][e] = ld16((const float*)a.X + a_base[h] + ko + 4 * e);
             f.w[u][h][e] = ld16((const float*)a.A_t + b_base[h] + ko + 4 * e);
@@ -105,6 +107,7 @@ __global__ __launch_bounds__(64 * NW) void k_latent_gemm(GemmArgs a) {
         for (int e = 0; e < NL; ++e) {
           f.x[u][h][e] = a_ok[h] ? f.x[u][h][e] : u32x4{0, 0, 0, 0};
           f.w[u][h][e] = (b_ok[h] && kin) ? f.w[u][h][e] : u32x4{0, 0, 0, 0};
+          if (MODE == 4) f.w2[u][h % NW2][e] = (b_ok[h] && kin) ? f.w2[u][h % NW2][e] : u32x4{0, 0, 0, 0};
         }
 #pragma unroll
       for (int x = 0; x < 2; ++x)
@@ -112,6 +115,7 @@ __global__ __launch_bounds__(64 * NW) void k_latent_gemm(GemmArgs a) {
         for (int y = 0; y < 2; ++y) {
           if (DT == STARKV_BF16) {
             acc[x][y] = mfma32_bf16(as_bf16x8(f.x[u][x][0]), as_bf16x8(f.w[u][y][0]), acc[x][y]);
+            if (MODE == 4) acc[x][y] = mfma32_bf16(as_bf16x8(f.x[u][x][0]), as_bf16x8(f.w2[u][y % NW2][0]), acc[x][y]);
           } else {
 #pragma unroll
             for (int e = 0; e < NL; ++e)
@@ -316,9 +320,8 @@ hipError_t launch_append(const Layer& L, const starkv_cache& c, const void* X_ne
 
 // Hidden-state query projection through the absorbed factors: out[m][c] = sum_e x[m][e] wqk[c][e]
 // for the M = B n_q rows and the NS = G n_key absorbed columns, on the append GEMMs with a raw
-// fp32 epilogue.  bf16 layers keep the factors as bf16 high and low parts (wqk_hi, wqk_lo): the
-// skinny form loads both in one pass, the tiled form takes two (store, then add); fp32 layers
-// take one.
+// fp32 epilogue.  bf16 layers keep the factors as bf16 high and low parts (wqk_hi, wqk_lo), which
+// both forms load together in one pass (MODE 4: one MFMA per part into the same accumulators).
 // One launch, with the timing events attached when given.
 template <typename A>
 static hipError_t launch_ev(void (*kernel)(A), dim3 grid, dim3 block, hipStream_t s, A arg, hipEvent_t start,
@@ -354,29 +357,16 @@ hipError_t launch_hidden_query(const Layer& L, const void* x, int M, const void*
     return launch_ev(bf ? k_latent_gemm_skinny<STARKV_BF16, 16, false, 4> : k_latent_gemm_skinny<STARKV_F32, 16, false, 2>,
                      dim3((a.NS + 15) / 16), dim3(512), s, a, start, stop);
   }
-  // tiled form: bf16 takes two passes (store the high part's product, add the low part's)
-  const int n_pass = bf ? 2 : 1;
-  hipError_t e = hipSuccess;
+  // tiled form, one launch: bf16 loads the high and low parts together (MODE 4)
   const int n_rt = (M + 63) / 64, n_ct = (a.NS + 63) / 64;
+  a.A_t = wqk_hi;
+  a.A_t2 = wqk_lo;
   a.xmap_rt = n_rt <= 16 ? n_rt : 0;
-  for (int pass = 0; pass < n_pass && e == hipSuccess; ++pass) {
-    a.A_t = pass == 0 ? wqk_hi : wqk_lo;
-    const hipEvent_t e0 = pass == 0 ? start : nullptr, e1 = pass == n_pass - 1 ? stop : nullptr;
-    void (*kern)(GemmArgs);
-    dim3 grid, block;
-    if (a.xmap_rt > 0) {
-      grid = dim3(8 * n_rt * ((n_ct + 7) / 8));
-      block = dim3(512);
-      kern = !bf ? k_latent_gemm<STARKV_F32, 2, 8>
-                 : (pass == 0 ? k_latent_gemm<STARKV_BF16, 2, 8> : k_latent_gemm<STARKV_BF16, 3, 8>);
-    } else {
-      grid = dim3(n_rt, n_ct);
-      block = dim3(256);
-      kern = !bf ? k_latent_gemm<STARKV_F32, 2, 4>
-                 : (pass == 0 ? k_latent_gemm<STARKV_BF16, 2, 4> : k_latent_gemm<STARKV_BF16, 3, 4>);
-    }
-    e = launch_ev(kern, grid, block, s, a, e0, e1);
-  }
+  if (a.xmap_rt > 0)
+    return launch_ev(bf ? k_latent_gemm<STARKV_BF16, 4, 8> : k_latent_gemm<STARKV_F32, 2, 8>,
+                     dim3(8 * n_rt * ((n_ct + 7) / 8)), dim3(512), s, a, start, stop);
+  hipError_t e = launch_ev(bf ? k_latent_gemm<STARKV_BF16, 4, 4> : k_latent_gemm<STARKV_F32, 2, 4>, dim3(n_rt, n_ct),
+                           dim3(256), s, a, start, stop);
   return e;
 }
 

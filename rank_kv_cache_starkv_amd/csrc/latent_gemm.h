@@ -31,20 +31,20 @@ struct GemmArgs {
   int lens[kMaxB];
   // calibrate
   uint32_t* absmax;
-  // raw fp32 output [M][NS] (the hidden-state query projection): MODE 2 stores, MODE 3 adds,
-  // MODE 4 (skinny form) stores X (A_t + A_t2)^T, the two parts loaded together
+  // raw fp32 output [M][NS] (the hidden-state query projection): MODE 2 stores X A_t^T, MODE 4
+  // stores X (A_t + A_t2)^T with the two parts loaded together
   float* out_f32;
   const void* A_t2;
 };
 
-// MODE 2 / 3 epilogue: out_f32[m][slot] = x (MODE 2) or += x (MODE 3), rows < M and slots < NS.
-template <int MODE, int R>
+// MODE 2 / 4 epilogue: out_f32[m][slot] = x for rows < M and slots < NS.
+template <int MODE, int R>  // MODE only documents the caller
 __device__ __forceinline__ void store_raw(const GemmArgs& a, int slot, const float* xs, const int* ms) {
 #pragma unroll
   for (int v = 0; v < R; ++v) {
     if (ms[v] >= a.M || slot >= a.NS) continue;
     float* o = a.out_f32 + (size_t)ms[v] * a.NS + slot;
-    *o = MODE == 3 ? *o + xs[v] : xs[v];
+    *o = xs[v];
   }
 }
 
