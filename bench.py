@@ -8,8 +8,10 @@ append and the query projection share the first launch.  Inputs are resident in 
 timing starts.  Steps rotate over distinct layers (own factors, own cache) totalling more
 than 1 GiB, so every step reads cold HBM rather than the 256 MB Infinity Cache.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1] [--no-cpu]
-Prints one JSON line on stdout; progress goes to stderr.
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4] [--no-cpu] [--no-sub]
+Prints one JSON line on stdout; progress goes to stderr.  The headline is workload 4, the
+13B-class high-batch step (64 ragged sequences, 4 queries each); the 7B-class bf16 and int8/int4
+layers and the long-context GQA layer are measured in the same run as sub-results.
 
 Two helper modes serve the HBM-traffic figures:
   --copy-probe       copies 1 GiB between two device buffers a few times (a plain copy
@@ -204,67 +206,82 @@ def pmc_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, workload: 
     return 0
 
 
-def cpu_baseline(w, lf, lens, n_q, X0, Xcal, q_step, X_step, budget_s: float):
-    """The CPU oracle (NumPy fp64) on one sequence: one decode step = append n_q tokens +
-    attention, repeated until ``budget_s`` of CPU time is used."""
-    from oracle import starkv_oracle as O
+def host_info() -> dict:
+    """The host the CPU baseline ran on: core counts, CPU model, BLAS library and its threads."""
+    info = {"os_cpu_count": os.cpu_count()}
+    try:
+        info["affinity"] = len(os.sched_getaffinity(0))
+    except Exception:
+        info["affinity"] = None
+    try:
+        model = [ln.split(":", 1)[1].strip() for ln in open("/proc/cpuinfo") if ln.startswith("model name")]
+        info["cpu_model"] = model[0] if model else None
+    except Exception:
+        info["cpu_model"] = None
     try:
         from threadpoolctl import threadpool_info
-        cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+        blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        info["blas"] = [f"{p.get('internal_api')} {p.get('version')} ({p.get('num_threads')} threads)" for p in blas]
+        info["blas_threads"] = max((p.get("num_threads", 1) for p in blas), default=1)
     except Exception:
-        cores = os.cpu_count() or 1
+        info["blas"], info["blas_threads"] = None, None
+    return info
+
+
+def cpu_baseline(w, lf, lens, n_q, X0, Xcal, q_step, X_step, budget_s: float):
+    """The CPU oracle (NumPy fp64) on one sequence: one decode step = append n_q tokens +
+    attention, repeated until ``budget_s`` of CPU time is used; then the same with one BLAS
+    thread for a fifth of the budget, and the append alone."""
+    from oracle import starkv_oracle as O
+    host = host_info()
     OL = O.build_layer(lf.U_k, lf.s_k, lf.V_k, lf.tau_k, lf.U_v, lf.s_v, lf.V_v, lf.tau_v, w.H_q, w.latent, w.dtype)
     scales = O.calibrate_scales(Xcal, OL.A_cat, O.channel_qmax(OL)) if w.latent in QUANTIZED else None
     t_setup = time.perf_counter()
     base = O.compress(X0, OL, scales)
     log(f"[cpu] oracle prefill of sequence 0 ({X0.shape[0]} tokens): {time.perf_counter() - t_setup:.1f} s")
-    reps, spent = 0, 0.0
-    while spent < budget_s:
-        t0 = time.perf_counter()
-        new = O.compress(X_step[0], OL, scales)
-        cache = O.SequenceCache(np.concatenate([base.key, new.key]), np.concatenate([base.value, new.value]))
-        O.decode(q_step[0].astype(np.float64), cache, OL, n_q, scales)
-        spent += time.perf_counter() - t0
-        reps += 1
+
+    def run(budget):
+        reps, spent = 0, 0.0
+        while spent < budget or reps == 0:
+            t0 = time.perf_counter()
+            new = O.compress(X_step[0], OL, scales)
+            cache = O.SequenceCache(np.concatenate([base.key, new.key]), np.concatenate([base.value, new.value]))
+            O.decode(q_step[0].astype(np.float64), cache, OL, n_q, scales)
+            spent += time.perf_counter() - t0
+            reps += 1
+        return reps, spent
+
+    reps, spent = run(budget_s)
     qps = reps * n_q / spent
-    return {"value": qps, "unit": "queries/s", "cores": int(cores), "kind": "oracle",
+    # the append alone (projection + quantisation of the step's tokens), all BLAS threads
+    t0, na = time.perf_counter(), 0
+    while time.perf_counter() - t0 < 1.0 or na == 0:
+        O.compress(X_step.reshape(-1, X_step.shape[-1]), OL, scales)
+        na += 1
+    append_tps = na * X_step.shape[0] * X_step.shape[1] / (time.perf_counter() - t0)
+    single = None
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            r1, s1 = run(budget_s / 5)
+        single = r1 * n_q / s1
+    except Exception:
+        pass
+    return {"value": qps, "unit": "queries/s", "cores": int(host.get("blas_threads") or host["os_cpu_count"] or 1),
+            "kind": "oracle",
             "sample": f"sequence 0 of {w.B} (context {int(lens[0])}), {reps} decode steps "
-                      f"(append {n_q} token(s) + attention), {spent:.1f} s; GPU value is all {w.B} sequences"}
+                      f"(append {n_q} token(s) + attention), {spent:.1f} s; GPU value is all {w.B} sequences",
+            "single_thread_value": single, "append_tokens_per_s": append_tps, "host": host}
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=1, help="workload id (0-5); 1 is the headline")
-    ap.add_argument("--layers", type=int, default=0, help="layers to rotate (0: enough for 1 GiB)")
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-budget", type=float, default=15.0)
-    ap.add_argument("--hidden-query", action="store_true",
-                    help="queries from hidden states through the absorbed factors W_q B_g^T (step = append, "
-                         "then starkv_decode_attention_hidden); no CPU baseline")
-    ap.add_argument("--copy-probe", action="store_true", help=f"copy {COPY_PROBE_MIB} MiB device to device")
-    ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"))
-    args = ap.parse_args()
-    if args.pmc_summary:
-        from rank_kv_cache_starkv_amd import inputs as I
-        return pmc_summary(*args.pmc_summary, I.WORKLOADS[args.workload].name)
-    if args.copy_probe:
-        return copy_probe()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the library runs on a single "
-              f"MI355X; sharding across GPUs by sequence, KV head or context is not built)", file=sys.stderr)
-        return 2
-
+def measure(w, args, dev, with_cpu: bool, steps: int, warmup: int) -> dict:
+    """Set up one workload (rotated layers, prefilled caches), time `steps` decode steps (graph
+    replay: exactly `steps` steps in one captured graph; eager alongside), time each kernel, and
+    return the result fields of the JSON line."""
     import torch
     import rank_kv_cache_starkv_amd as S
     from rank_kv_cache_starkv_amd import inputs as I
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    dev = "cuda:0"
-    torch.cuda.set_device(0)
-    w = I.WORKLOADS[args.workload]
     n_q = w.n_q
     lens = I.context_lengths(w) + w.n_append  # lengths at decode (include the n_q step tokens)
     if not w.ragged:
@@ -316,8 +333,7 @@ def main() -> int:
         layers.append(L)
         caches.append(c)
     torch.cuda.synchronize()
-    t_prefill = time.perf_counter() - t0
-    log(f"[setup] prefill {n_layers} layers ({n_layers * int(lens_pre.sum())} tokens): {t_prefill:.1f} s")
+    log(f"[setup] prefill {n_layers} layers ({n_layers * int(lens_pre.sum())} tokens): {time.perf_counter() - t0:.1f} s")
 
     q_np = I.as_dtype(I.queries(w), w.dtype)
     X_np = I.as_dtype(I.x_new(w, n_q), w.dtype)
@@ -347,22 +363,23 @@ def main() -> int:
             layers[li].append(caches[li], X_step, lens_pre)
             layers[li].decode_hidden(caches[li], x_q, lens, out=outs[li], ws=ws)
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    # eager: one host call per append / decode
+    # eager: one host call per step (append + attention)
     t_host = time.perf_counter()
     ev0.record()
-    for i in range(args.steps):
-        step(args.warmup + i)
+    for i in range(steps):
+        step(warmup + i)
     ev1.record()
     t_host = time.perf_counter() - t_host
     torch.cuda.synchronize()
-    ms_step_eager = ev0.elapsed_time(ev1) / args.steps
-    log(f"[time] eager: {ms_step_eager * 1000:.2f} us/step (host issue {t_host / args.steps * 1e6:.1f} us/step)")
+    ms_step_eager = ev0.elapsed_time(ev1) / steps
+    host_us = t_host / steps * 1e6
+    log(f"[time] eager: {ms_step_eager * 1000:.2f} us/step (host issue {host_us:.1f} us/step)")
 
-    # graph: one rotation over the layers captured once and replayed (no host work per step)
+    # graph: exactly `steps` steps (rotating over the layers) captured once and replayed once
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     graph = torch.cuda.CUDAGraph()
@@ -371,28 +388,25 @@ def main() -> int:
             step(li)
         side.synchronize()
         with torch.cuda.graph(graph, stream=side):
-            for li in range(n_layers):
-                step(li)
+            for i in range(steps):
+                step(i)
     torch.cuda.synchronize()
-    reps = max(1, -(-args.steps // n_layers))
-    for _ in range(2):
-        graph.replay()
+    graph.replay()  # untimed: the first replay uploads the graph
     torch.cuda.synchronize()
     ev0.record()
-    for _ in range(reps):
-        graph.replay()
+    graph.replay()
     ev1.record()
     torch.cuda.synchronize()
-    n_steps = reps * n_layers
     ms_total = ev0.elapsed_time(ev1)
-    ms_step = ms_total / n_steps
-    log(f"[time] graph: {n_steps} steps: {ms_total:.3f} ms, {ms_step * 1000:.2f} us/step")
+    ms_step = ms_total / steps
+    log(f"[time] graph: {steps} steps: {ms_total:.3f} ms, {ms_step * 1000:.2f} us/step")
+    del graph
 
     # second pass with per-kernel events (same steps, same stream)
     S.profile_enable(True)
     S.profile_read(reset=True)
-    for i in range(args.steps):
-        step(args.warmup + args.steps + i)
+    for i in range(steps):
+        step(warmup + steps + i)
     torch.cuda.synchronize()
     prof = S.profile_read(reset=True)
     S.profile_enable(False)
@@ -404,32 +418,22 @@ def main() -> int:
     dom = max((k for k in kern_us if k.startswith("decode_")), key=lambda k: kern_us[k])
     achieved = ab[dom] / (kern_us[dom] * 1e-6) / 1e9
     traffic = None if args.hidden_query else traffic_for(dom, w.name)  # counters cover the q path only
-    qps = w.B * n_q / (ms_step * 1e-3)
     dec_us = sum(us for k, us in kern_us.items() if k.startswith("decode_"))
-    result = {
-        "metric": METRIC,
-        "value": qps,
-        "unit": "queries/s",
-        "n_gpus": 1,
-        "steps": n_steps,
-        "warmup": args.warmup,
+    res = {
+        "value": w.B * n_q / (ms_step * 1e-3),
         "ms_per_step": ms_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": {"f32": "f32", "bf16": "bf16", "mix84": "int8/int4 codes, f16 MFMA, fp32 accumulate",
-                  "had43": "4-bit/3-bit codes in int8/int4 bytes, f16 MFMA, fp32 accumulate"}[w.latent],
-        "data": "synthetic",
         "config": {"workload": w.name, "batch": w.B, "context": int(lens.max()) if not w.ragged else "ragged",
                    "context_tokens": int(lens.sum()), "queries_per_seq": n_q, "H_q": w.H_q, "H_kv": w.H_kv,
                    "d_h": w.d_h, "hidden": w.d, "key_rank_sum": int(np.sum(probe.ranks)), "value_rank": probe.r_v,
                    "latent": w.latent, "layers_rotated": n_layers,
                    "query": "hidden states, absorbed W_q B_g^T" if args.hidden_query else "q"},
+        "dtype": {"f32": "f32", "bf16": "bf16", "mix84": "int8/int4 codes, f16 MFMA, fp32 accumulate",
+                  "had43": "4-bit/3-bit codes in int8/int4 bytes, f16 MFMA, fp32 accumulate"}[w.latent],
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                      "alg_bytes_per_launch": ab[dom], "us_per_launch": kern_us[dom]},
-        "timing": "HIP graph of one rotation over the layers, replayed; events on the replay stream",
         "ms_per_step_eager": ms_step_eager,
+        "host_issue_us_per_step": host_us,
         "step_hbm_gbps": ab["step"] / (ms_step * 1e-3) / 1e9,
         "step_frac": ab["step"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "decode_kernels_us": dec_us,
@@ -438,12 +442,89 @@ def main() -> int:
         "kernel_us": kern_us,
         "alg_bytes": ab,
     }
-    if not args.no_cpu and not args.hidden_query:
+    if with_cpu and not args.hidden_query:
         t0 = time.perf_counter()
-        result["cpu_baseline"] = cpu_baseline(w, lf, lens, n_q, X0, Xcal, q_np, X_np, args.cpu_budget)
+        res["cpu_baseline"] = cpu_baseline(w, lf, lens, n_q, X0, Xcal, q_np, X_np, args.cpu_budget)
         log(f"[cpu] {time.perf_counter() - t0:.1f} s")
     else:
-        result["cpu_baseline"] = None
+        res["cpu_baseline"] = None
+    del layers, caches, outs, ws, U, probe
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=4,
+                    help="workload id (0-5); 4 (the 13B-class ragged high-batch step) is the headline")
+    ap.add_argument("--layers", type=int, default=0, help="layers to rotate (0: enough for 1 GiB)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-sub", action="store_true", help="skip the other workloads' sub-results")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--hidden-query", action="store_true",
+                    help="queries from hidden states through the absorbed factors W_q B_g^T (step = append, "
+                         "then starkv_decode_attention_hidden); no CPU baseline")
+    ap.add_argument("--copy-probe", action="store_true", help=f"copy {COPY_PROBE_MIB} MiB device to device")
+    ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"))
+    args = ap.parse_args()
+    if args.pmc_summary:
+        from rank_kv_cache_starkv_amd import inputs as I
+        return pmc_summary(*args.pmc_summary, I.WORKLOADS[args.workload].name)
+    if args.copy_probe:
+        return copy_probe()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the library runs on a single "
+              f"MI355X; sharding across GPUs by sequence, KV head or context is not built)", file=sys.stderr)
+        return 2
+
+    import torch
+    from rank_kv_cache_starkv_amd import inputs as I
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    w = I.WORKLOADS[args.workload]
+    r = measure(w, args, dev, with_cpu=not args.no_cpu, steps=args.steps, warmup=args.warmup)
+    result = {
+        "metric": METRIC,
+        "value": r["value"],
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": r["dtype"],
+        "data": "synthetic",
+        "config": r["config"],
+        "roofline": r["roofline"],
+        "cpu_baseline": r["cpu_baseline"],
+        "timing": "HIP graph of exactly `steps` steps (rotating over the layers), replayed once; events on the "
+                  "replay stream",
+    }
+    result.update({k: r[k] for k in ("ms_per_step_eager", "host_issue_us_per_step", "step_hbm_gbps", "step_frac",
+                                     "decode_kernels_us", "decode_hbm_gbps", "kv_tokens_per_s", "kernel_us",
+                                     "alg_bytes")})
+    if not args.no_sub and args.workload == 4 and not args.hidden_query:
+        # the other workloads of the same metric, measured in the same run (no CPU baseline)
+        subs = {}
+        for wid in (1, 2, 3):
+            ws = I.WORKLOADS[wid]
+            sr = measure(ws, args, dev, with_cpu=False, steps=min(args.steps, 100), warmup=min(args.warmup, 10))
+            subs[ws.name] = {"queries_per_s": sr["value"], "ms_per_step": sr["ms_per_step"],
+                             "ms_per_step_eager": sr["ms_per_step_eager"],
+                             "host_issue_us_per_step": sr["host_issue_us_per_step"],
+                             "kv_tokens_per_s": sr["kv_tokens_per_s"], "step_frac": sr["step_frac"],
+                             "roofline": {k: sr["roofline"][k] for k in ("kernel", "achieved", "frac", "traffic",
+                                                                          "us_per_launch")},
+                             "kernel_us": sr["kernel_us"], "config": sr["config"]}
+        result["sub_results"] = subs
     print(json.dumps(result))
     return 0
 

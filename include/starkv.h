@@ -117,14 +117,15 @@ typedef struct starkv_layer_info {
   size_t a_bytes;    /* bytes of A^T  [n_lat][d] (dtype) */
   size_t bk_bytes;   /* bytes of B_k  [n_key][d_h] (dtype) */
   size_t bv_bytes;   /* bytes of B_v^T [H_kv*d_h][r_v] (dtype) */
-  size_t scale_bytes;/* bytes of the fp16 scales [n_lat] (mix84; 0 otherwise) */
+  size_t scale_bytes;/* bytes of the fp16 scales [n_lat] (mix84, had43; 0 otherwise) */
 } starkv_layer_info;
 
 /*
  * The cache of one layer, caller-owned device memory:
  *
  * k_rows  [B][T_max][k_row_bytes]  one key row per token.
- *   mix84: bytes [0, K8): the leading ceil(r_g/4) channels of head 0, then of
+ *   mix84 (had43 alike, with the leading ceil(r_g/5) channels in the first region):
+ *          bytes [0, K8): the leading ceil(r_g/4) channels of head 0, then of
  *          head 1, ... as int8 (two's complement), zero-padded; bytes
  *          [K8, K8 + K4/2): the remaining channels of head 0, head 1, ... as
  *          int4 two per byte (channel 2k in the low nibble, two's complement),
@@ -168,7 +169,8 @@ const char* starkv_status_string(int status);
  * scratch) are allocated on the current device by the first
  * starkv_build_factors / starkv_bind_factors call.
  * Errors: EINVAL (null, non-positive sizes, H_q % H_kv != 0, n_v < 1 or above
- * min(d, H_kv*d_h), NaN or negative thresholds), EUNSUPPORTED (dtype/latent
+ * min(d, H_kv*d_h), NaN or negative thresholds, non-finite or ascending singular
+ * values: each spectrum must be non-increasing), EUNSUPPORTED (dtype/latent
  * combination, d not a multiple of 16, d_h not a multiple of 32 or above 256,
  * every key rank 0, r_v == 0, n_lat above 8192), ENOMEM.
  */
@@ -207,16 +209,18 @@ int starkv_bind_factors(starkv_layer* layer, const void* A_t, const void* B_k, c
 /*
  * Per-channel fp16 scales from calibration statistics (Methodology section 3;
  * the abstract: the quantiser uses data statistics).  For every latent channel
- * c: scale_c = fp16_rne( fp32( max_t |(X_cal A)_{t,c}| ) / qmax_c ), qmax 127 for
- * the int8 channels and 7 for the int4 ones.  X_cal: device [n_cal][d] (dtype).
- * scales_out: device fp16 [n_lat], bound to the layer.  mix84 layers only
- * (EUNSUPPORTED otherwise); needs bound factors (ESTATE).  Uses the layer's own
- * device scratch: calls on the same layer must not overlap.
+ * c: scale_c = fp16_rne( fp32( max_t |(X_cal A)_{t,c}| ) / qmax_c ), with qmax_c
+ * the channel's code limit: mix84 127 (int8 channels) and 7 (int4 channels); had43
+ * 7 (4-bit outlier channels) and 3 (3-bit inlier channels), A being the rotated
+ * down-projection.  X_cal: device [n_cal][d] (dtype).  scales_out: device fp16
+ * [n_lat], bound to the layer.  Quantised layers only (mix84, had43; EUNSUPPORTED
+ * otherwise); needs bound factors (ESTATE).  Uses the layer's own device scratch:
+ * calls on the same layer must not overlap.
  */
 int starkv_calibrate(starkv_layer* layer, const void* X_cal, int n_cal, uint16_t* scales_out,
                      hipStream_t stream);
 
-/* Bind caller-provided fp16 scales [n_lat] (mix84 layers). */
+/* Bind caller-provided fp16 scales [n_lat] (quantised layers: mix84, had43). */
 int starkv_bind_scales(starkv_layer* layer, const uint16_t* scales);
 
 /* Bytes of k_rows and v_tiles for B sequences of capacity T_max (a multiple of 32);
@@ -229,8 +233,10 @@ int starkv_cache_bytes(const starkv_layer* layer, int B, int T_max, size_t* k_by
  * precision).  For sequence b and new token i, x = X_new[b][i] A (fp32
  * accumulation) is stored at position lens_host[b] + i:
  *   f32 latent: x;  bf16 latent: bf16_rne(x);
- *   mix84: code_c = clamp(rne(x_c / scale_c), -qmax_c, qmax_c) with an IEEE fp32
- *   division (code 0 where scale_c == 0), packed as starkv_cache documents.
+ *   mix84 and had43: code_c = clamp(rne(x_c / scale_c), -qmax_c, qmax_c) with an
+ *   IEEE fp32 division (code 0 where scale_c == 0) and the code limits of
+ *   starkv_calibrate (mix84 127 / 7, had43 7 / 3; x from the rotated factors for
+ *   had43), packed as starkv_cache documents (had43 codes in the same byte regions).
  * X_new: device [B][n_new][d] (dtype).  lens_host: host [B], the lengths before
  * the append (the caller updates its lengths itself).  n_new == 0 is a no-op.
  * Errors: EINVAL, ECAPACITY (lens_host[b] + n_new > T_max), ESTATE, EHIP.

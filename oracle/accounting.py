@@ -13,8 +13,6 @@ Sources (STAR-KV summary page):
 
 from __future__ import annotations
 
-from typing import Sequence
-
 
 def mean_bits(frac_hi: float, bits_hi: float, bits_lo: float) -> float:
     """Average bits per latent channel of a two-block mixed-precision quantiser."""
@@ -36,7 +34,3 @@ def reconstruction_flops_per_token(total_rank: int, heads: int, d_h: int, joint:
         return 2 * total_rank * heads * d_h
     return 2 * total_rank * d_h
 
-
-def bits_per_token(ranks: Sequence[int], bits_of) -> int:
-    """Total latent bits per token for segments of the given ranks; ``bits_of(r)`` -> bits."""
-    return int(sum(bits_of(int(r)) for r in ranks))

@@ -142,6 +142,23 @@ def _ptr(t) -> int:
     return int(t.data_ptr())
 
 
+def _need(cond: bool, what: str) -> None:
+    """Argument check of the binding (shapes, dtypes, devices): a mismatch would make the
+    kernels read or write past the caller's buffers, so it is refused before the call."""
+    if not cond:
+        raise ValueError(what)
+
+
+def _lens(lens, B: int) -> np.ndarray:
+    L = _i32(lens).reshape(-1)
+    _need(L.shape[0] == B, f"lens has {L.shape[0]} entries for a batch of {B}")
+    return L
+
+
+def _on_device(t, like) -> bool:
+    return t.is_cuda and t.device == like.device
+
+
 def _stream(stream=None) -> int:
     import torch
     s = stream if stream is not None else torch.cuda.current_stream()
@@ -195,6 +212,8 @@ class Layer:
         self.H_q, self.H_kv, self.d_h, self.d = H_q, H_kv, d_h, d
         self.A_t = self.B_k = self.B_vt = self.scales = None
         self._ws = None
+        self._ws_memo = None  # (B, n_q, lens bytes) -> workspace bytes of the last query
+        self._cb_memo = {}  # (B, T_max) -> cache bytes
 
     # -- lifecycle
     def close(self) -> None:
@@ -222,26 +241,37 @@ class Layer:
         self.A_t = torch.empty((n_lat, self.d), dtype=self.torch_dtype, device=dev)
         self.B_k = torch.empty((n_key, self.d_h), dtype=self.torch_dtype, device=dev)
         self.B_vt = torch.empty((self.H_kv * self.d_h, self.r_v), dtype=self.torch_dtype, device=dev)
-        for t in (U_k, V_k, U_v, V_v):
-            assert t.dtype == torch.float32 and t.is_contiguous() and t.is_cuda
+        n_v = len(self._s_v)
+        for t, shape in ((U_k, (self.H_kv, self.d, self.d_h)), (V_k, (self.H_kv, self.d_h, self.d_h)),
+                         (U_v, (self.d, n_v)), (V_v, (self.H_kv * self.d_h, n_v))):
+            _need(t.dtype == torch.float32 and t.is_contiguous() and _on_device(t, U_k) and tuple(t.shape) == shape,
+                  f"SVD factor: contiguous float32 device tensor {shape} expected, got {tuple(t.shape)}")
         _check(self._lib.starkv_build_factors(self._h, _ptr(U_k), _ptr(V_k), _ptr(U_v), _ptr(V_v), _ptr(self.A_t),
                                               _ptr(self.B_k), _ptr(self.B_vt), _stream(stream)), "starkv_build_factors")
         return self.A_t, self.B_k, self.B_vt
 
     def bind_factors(self, A_t, B_k, B_vt) -> None:
+        for t, shape in ((A_t, (self.info["n_lat"], self.d)), (B_k, (self.info["n_key"], self.d_h)),
+                         (B_vt, (self.H_kv * self.d_h, self.r_v))):
+            _need(t.dtype == self.torch_dtype and t.is_contiguous() and t.is_cuda and tuple(t.shape) == shape,
+                  f"factor: contiguous {self.torch_dtype} device tensor {shape} expected, got {tuple(t.shape)}")
         self.A_t, self.B_k, self.B_vt = A_t, B_k, B_vt
         _check(self._lib.starkv_bind_factors(self._h, _ptr(A_t), _ptr(B_k), _ptr(B_vt)), "starkv_bind_factors")
 
     def calibrate(self, X_cal, stream=None):
         """Per-channel fp16 scales from calibration hidden states [n_cal, d] (mix84, had43)."""
         import torch
-        assert X_cal.dtype == self.torch_dtype and X_cal.is_contiguous()
+        _need(X_cal.dtype == self.torch_dtype and X_cal.is_contiguous() and X_cal.is_cuda and X_cal.dim() == 2 and
+              int(X_cal.shape[1]) == self.d, f"X_cal: contiguous {self.torch_dtype} device tensor [n_cal, {self.d}] expected")
         self.scales = torch.empty((self.info["n_lat"],), dtype=torch.float16, device=X_cal.device)
         _check(self._lib.starkv_calibrate(self._h, _ptr(X_cal), int(X_cal.shape[0]), _ptr(self.scales),
                                           _stream(stream)), "starkv_calibrate")
         return self.scales
 
     def bind_scales(self, scales) -> None:
+        import torch
+        _need(scales.dtype == torch.float16 and scales.is_contiguous() and scales.is_cuda and
+              scales.numel() == self.info["n_lat"], f"scales: contiguous float16 device tensor [{self.info['n_lat']}] expected")
         self.scales = scales
         _check(self._lib.starkv_bind_scales(self._h, _ptr(scales)), "starkv_bind_scales")
 
@@ -258,11 +288,49 @@ class Layer:
         mk = torch.zeros if zero else torch.empty
         return Cache(mk((kb,), dtype=torch.uint8, device=device), mk((vb,), dtype=torch.uint8, device=device), B, T_max)
 
+    def _check_cache(self, cache: Cache, like) -> None:
+        key = (cache.B, cache.T_max)
+        if key not in self._cb_memo:
+            self._cb_memo[key] = self.cache_bytes(cache.B, cache.T_max)
+        kb, vb = self._cb_memo[key]
+        _need(cache.k_rows.numel() * cache.k_rows.element_size() >= kb and
+              cache.v_tiles.numel() * cache.v_tiles.element_size() >= vb, "cache buffers smaller than its layout")
+        _need(_on_device(cache.k_rows, like) and _on_device(cache.v_tiles, like), "cache on another device")
+
+    def _check_q(self, q, what: str = "q"):
+        _need(q.dtype == self.torch_dtype and q.is_contiguous() and q.dim() == 4,
+              f"{what}: contiguous {self.torch_dtype} tensor [B, n_q, H_q, d_h] expected")
+        _need(tuple(q.shape[2:]) == (self.H_q, self.d_h), f"{what} shape {tuple(q.shape)}: heads and head dim "
+              f"must be ({self.H_q}, {self.d_h})")
+        _need(q.is_cuda, f"{what} must be a device tensor")
+        return int(q.shape[0]), int(q.shape[1])
+
+    def _out(self, out, shape, like):
+        import torch
+        if out is None:
+            return torch.empty(shape, dtype=self.torch_dtype, device=like.device)
+        _need(out.dtype == self.torch_dtype and out.is_contiguous() and tuple(out.shape) == tuple(shape) and
+              _on_device(out, like), f"out: contiguous {self.torch_dtype} tensor {tuple(shape)} on {like.device} expected")
+        return out
+
+    def _workspace(self, ws, need: int, like):
+        import torch
+        if ws is None:
+            if self._ws is None or self._ws.numel() < need or self._ws.device != like.device:
+                self._ws = torch.empty((max(need, 256),), dtype=torch.uint8, device=like.device)
+            return self._ws
+        _need(ws.is_contiguous() and _on_device(ws, like), "ws: contiguous tensor on the device of the inputs")
+        return ws
+
     def append(self, cache: Cache, X_new, lens: Sequence[int], stream=None) -> None:
         """Project X_new [B, n_new, d] into the latent and store it after position lens[b]."""
-        assert X_new.dtype == self.torch_dtype and X_new.is_contiguous() and X_new.dim() == 3
+        _need(X_new.dtype == self.torch_dtype and X_new.is_contiguous() and X_new.dim() == 3,
+              f"X_new: contiguous {self.torch_dtype} tensor [B, n_new, d] expected")
+        _need(int(X_new.shape[2]) == self.d, f"X_new shape {tuple(X_new.shape)}: hidden size must be {self.d}")
         B, n_new = int(X_new.shape[0]), int(X_new.shape[1])
-        L = _i32(lens)
+        L = _lens(lens, B)
+        _need(X_new.is_cuda, "X_new must be a device tensor")
+        self._check_cache(cache, X_new)
         cs = cache.struct()
         _check(self._lib.starkv_compress_append(self._h, ctypes.byref(cs), _ptr(X_new), B, n_new,
                                                 L.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), _stream(stream)),
@@ -270,25 +338,25 @@ class Layer:
 
     # -- decode
     def workspace_bytes(self, B: int, n_q: int, lens: Sequence[int]) -> int:
-        L = _i32(lens)
+        L = _lens(lens, B)
+        key = (B, n_q, L.tobytes())
+        if self._ws_memo is not None and self._ws_memo[0] == key:
+            return self._ws_memo[1]
         n = ctypes.c_size_t()
         _check(self._lib.starkv_decode_workspace_bytes(self._h, B, n_q, L.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
                                                        ctypes.byref(n)), "starkv_decode_workspace_bytes")
+        self._ws_memo = (key, n.value)
         return n.value
 
     def decode(self, cache: Cache, q, lens: Sequence[int], out=None, ws=None, stream=None):
         """Attention of q [B, n_q, H_q, d_h] over the cache (lens include the n_q query tokens)."""
-        import torch
-        assert q.dtype == self.torch_dtype and q.is_contiguous() and q.dim() == 4
-        B, n_q = int(q.shape[0]), int(q.shape[1])
-        L = _i32(lens)
+        _need(q.dim() == 4, "q: tensor [B, n_q, H_q, d_h] expected")
+        L = _lens(lens, int(q.shape[0]))
+        B, n_q = self._check_q(q)
+        self._check_cache(cache, q)
         need = self.workspace_bytes(B, n_q, L)
-        if ws is None:
-            if self._ws is None or self._ws.numel() < need:
-                self._ws = torch.empty((max(need, 256),), dtype=torch.uint8, device=q.device)
-            ws = self._ws
-        if out is None:
-            out = torch.empty_like(q)
+        ws = self._workspace(ws, need, q)
+        out = self._out(out, q.shape, q)
         cs = cache.struct()
         _check(self._lib.starkv_decode_attention(self._h, ctypes.byref(cs), _ptr(q), B, n_q,
                                                  L.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), _ptr(out), _ptr(ws),
@@ -298,23 +366,24 @@ class Layer:
 
     def absorb_query(self, W_q, stream=None) -> None:
         """Absorb the key factors into the query projection W_q [d, H_q * d_h] (device, layer dtype)."""
-        assert W_q.dtype == self.torch_dtype and W_q.is_contiguous() and tuple(W_q.shape) == (self.d, self.H_q * self.d_h)
+        _need(W_q.dtype == self.torch_dtype and W_q.is_contiguous() and W_q.is_cuda and
+              tuple(W_q.shape) == (self.d, self.H_q * self.d_h),
+              f"W_q: contiguous {self.torch_dtype} device tensor {(self.d, self.H_q * self.d_h)} expected")
         _check(self._lib.starkv_absorb_query(self._h, _ptr(W_q), _stream(stream)), "starkv_absorb_query")
 
     def decode_hidden(self, cache: Cache, x, lens: Sequence[int], out=None, ws=None, stream=None):
         """Attention with the query taken from hidden states x [B, n_q, d] through the absorbed
         query factors; returns out [B, n_q, H_q, d_h]."""
-        import torch
-        assert x.dtype == self.torch_dtype and x.is_contiguous() and x.dim() == 3 and int(x.shape[2]) == self.d
+        _need(x.dtype == self.torch_dtype and x.is_contiguous() and x.dim() == 3,
+              f"x: contiguous {self.torch_dtype} tensor [B, n_q, d] expected")
+        _need(int(x.shape[2]) == self.d, f"x shape {tuple(x.shape)}: hidden size must be {self.d}")
         B, n_q = int(x.shape[0]), int(x.shape[1])
-        L = _i32(lens)
+        L = _lens(lens, B)
+        _need(x.is_cuda, "x must be a device tensor")
+        self._check_cache(cache, x)
         need = self.workspace_bytes(B, n_q, L)
-        if ws is None:
-            if self._ws is None or self._ws.numel() < need:
-                self._ws = torch.empty((max(need, 256),), dtype=torch.uint8, device=x.device)
-            ws = self._ws
-        if out is None:
-            out = torch.empty((B, n_q, self.H_q, self.d_h), dtype=x.dtype, device=x.device)
+        ws = self._workspace(ws, need, x)
+        out = self._out(out, (B, n_q, self.H_q, self.d_h), x)
         cs = cache.struct()
         _check(self._lib.starkv_decode_attention_hidden(self._h, ctypes.byref(cs), _ptr(x), B, n_q,
                                                         L.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), _ptr(out),
@@ -326,19 +395,18 @@ class Layer:
     def step(self, cache: Cache, X_new, q, lens: Sequence[int], out=None, ws=None, stream=None):
         """One decode step: append X_new [B, n_q, d] at lens - n_q, then attention of q
         [B, n_q, H_q, d_h] over lens (the lengths after the append)."""
-        import torch
-        assert q.dtype == self.torch_dtype and q.is_contiguous() and q.dim() == 4
-        assert X_new.dtype == self.torch_dtype and X_new.is_contiguous() and X_new.dim() == 3
+        _need(q.dim() == 4, "q: tensor [B, n_q, H_q, d_h] expected")
         B, n_q = int(q.shape[0]), int(q.shape[1])
-        assert tuple(X_new.shape) == (B, n_q, self.d), (tuple(X_new.shape), (B, n_q, self.d))
-        L = _i32(lens)
+        _need(X_new.dtype == self.torch_dtype and X_new.is_contiguous(),
+              f"X_new: contiguous {self.torch_dtype} tensor expected")
+        _need(tuple(X_new.shape) == (B, n_q, self.d), f"X_new shape {tuple(X_new.shape)}, expected {(B, n_q, self.d)}")
+        L = _lens(lens, B)
+        self._check_q(q)
+        _need(_on_device(X_new, q), f"X_new must be on {q.device}")
+        self._check_cache(cache, q)
         need = self.workspace_bytes(B, n_q, L)
-        if ws is None:
-            if self._ws is None or self._ws.numel() < need:
-                self._ws = torch.empty((max(need, 256),), dtype=torch.uint8, device=q.device)
-            ws = self._ws
-        if out is None:
-            out = torch.empty_like(q)
+        ws = self._workspace(ws, need, q)
+        out = self._out(out, q.shape, q)
         cs = cache.struct()
         _check(self._lib.starkv_decode_step(self._h, ctypes.byref(cs), _ptr(X_new), _ptr(q), B, n_q,
                                             L.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), _ptr(out), _ptr(ws),
@@ -349,6 +417,7 @@ class Layer:
     def reconstruct(self, cache: Cache, b: int, t0: int, t1: int, stream=None):
         """Dense K, V [t1 - t0, H_kv, d_h] rebuilt from the latent of sequence b."""
         import torch
+        self._check_cache(cache, cache.k_rows)
         K = torch.empty((t1 - t0, self.H_kv, self.d_h), dtype=self.torch_dtype, device=cache.k_rows.device)
         V = torch.empty_like(K)
         cs = cache.struct()

@@ -2,7 +2,11 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <string.h>
+
+#include <mutex>
 #include <new>
+#include <vector>
 
 #include "device_common.h"
 #include "profile.h"
@@ -13,9 +17,67 @@ int layer_init(const starkv_layer_desc& d, Layer* L);
 int layer_upload_tables(Layer* L);
 }  // namespace skv
 
+// The last decode plan of a layer, reused while the batch, query count and lengths repeat (a
+// decode loop calls workspace_bytes and then the decode with the same lengths; a serving loop
+// repeats them while the lengths do not change).  The plan depends on the cache capacity and the
+// workspace address only through the capacity field and the workspace pointers, which a hit
+// rebases.
+struct PlanMemo {
+  std::mutex mu;
+  bool valid = false;
+  int B = 0, n_q = 0;
+  std::vector<int32_t> lens;
+  uintptr_t ws_base = 0;
+  skv::DecodePlan plan;
+  skv::KtList kts;
+  skv::SeqTable seq;
+};
+
 struct starkv_layer {
   skv::Layer L;
+  PlanMemo memo;
 };
+
+static void rebase_plan(skv::DecodePlan* P, uintptr_t from, uintptr_t to, int T_max) {
+  auto rb = [&](auto*& p) { p = reinterpret_cast<std::remove_reference_t<decltype(p)>>((uintptr_t)p - from + to); };
+  skv::DecodeWs& w = P->ws;
+  rb(w.qfrag);
+  rb(w.rowp);
+  rb(w.p);
+  rb(w.cm);
+  rb(w.cl);
+  rb(w.zp);
+  rb(w.sl);
+  rb(w.sm);
+  rb(w.zt);
+  rb(w.qraw);
+  P->g.T_max = T_max;
+}
+
+// plan_decode through the layer's memo (thread-safe: the memo has its own lock)
+static int get_plan(const starkv_layer* l, int B, int n_q, const int32_t* lens, int T_max, void* ws,
+                    skv::DecodePlan* plan, skv::KtList* kts, skv::SeqTable* seq) {
+  PlanMemo& m = const_cast<PlanMemo&>(l->memo);
+  std::lock_guard<std::mutex> lk(m.mu);
+  if (m.valid && m.B == B && m.n_q == n_q && memcmp(m.lens.data(), lens, sizeof(int32_t) * B) == 0) {
+    *plan = m.plan;
+    *kts = m.kts;
+    *seq = m.seq;
+    rebase_plan(plan, m.ws_base, (uintptr_t)ws, T_max);
+    return STARKV_OK;
+  }
+  const int st = skv::plan_decode(l->L, B, n_q, lens, T_max, ws, plan, kts, seq);
+  if (st != STARKV_OK) return st;
+  m.valid = true;
+  m.B = B;
+  m.n_q = n_q;
+  m.lens.assign(lens, lens + B);
+  m.ws_base = (uintptr_t)ws;
+  m.plan = *plan;
+  m.kts = *kts;
+  m.seq = *seq;
+  return STARKV_OK;
+}
 
 using skv::Layer;
 
@@ -76,6 +138,13 @@ int starkv_layer_create(const starkv_layer_desc* d, starkv_layer** out) {
     if (bad_float(d->s_k[i])) return STARKV_EINVAL;
   for (int i = 0; i < d->n_v; ++i)
     if (bad_float(d->s_v[i])) return STARKV_EINVAL;
+  // the rank is the count of values above the threshold, taken as a prefix: the spectra must be
+  // descending (ties allowed), as singular values are
+  for (int g = 0; g < d->H_kv; ++g)
+    for (int i = 1; i < d->d_h; ++i)
+      if (d->s_k[(long)g * d->d_h + i] > d->s_k[(long)g * d->d_h + i - 1]) return STARKV_EINVAL;
+  for (int i = 1; i < d->n_v; ++i)
+    if (d->s_v[i] > d->s_v[i - 1]) return STARKV_EINVAL;
   // supported combinations and sizes
   if (d->latent == STARKV_LATENT_F32 && d->dtype != STARKV_F32) return STARKV_EUNSUPPORTED;
   if (d->latent != STARKV_LATENT_F32 && d->dtype != STARKV_BF16) return STARKV_EUNSUPPORTED;
@@ -276,7 +345,7 @@ int starkv_decode_workspace_bytes(const starkv_layer* l, int B, int n_q, const i
   skv::DecodePlan plan;
   skv::KtList kts;
   skv::SeqTable seq;
-  int st = skv::plan_decode(l->L, B, n_q, lens_host, 1 << 30, nullptr, &plan, &kts, &seq);
+  int st = get_plan(l, B, n_q, lens_host, 1 << 30, nullptr, &plan, &kts, &seq);
   if (st != STARKV_OK) return st;
   *bytes = plan.ws_bytes;
   return STARKV_OK;
@@ -296,7 +365,7 @@ int starkv_decode_attention(const starkv_layer* l, const starkv_cache* c, const 
   skv::DecodePlan plan;
   skv::KtList kts;
   skv::SeqTable seq;
-  st = skv::plan_decode(L, B, n_q, lens_host, c->T_max, ws, &plan, &kts, &seq);
+  st = get_plan(l, B, n_q, lens_host, c->T_max, ws, &plan, &kts, &seq);
   if (st != STARKV_OK) return st;
   if (ws_bytes < plan.ws_bytes) return STARKV_EWORKSPACE;
   return hip_status(skv::launch_decode(L, plan, kts, seq, q, out, c->k_rows, c->v_tiles, stream));
@@ -318,7 +387,7 @@ int starkv_decode_attention_hidden(const starkv_layer* l, const starkv_cache* c,
   skv::DecodePlan plan;
   skv::KtList kts;
   skv::SeqTable seq;
-  st = skv::plan_decode(L, B, n_q, lens_host, c->T_max, ws, &plan, &kts, &seq);
+  st = get_plan(l, B, n_q, lens_host, c->T_max, ws, &plan, &kts, &seq);
   if (st != STARKV_OK) return st;
   if (ws_bytes < plan.ws_bytes) return STARKV_EWORKSPACE;
   return hip_status(skv::launch_decode(L, plan, kts, seq, x, out, c->k_rows, c->v_tiles, stream, L.d_wqk));
@@ -340,7 +409,7 @@ int starkv_decode_step(const starkv_layer* l, const starkv_cache* c, const void*
   skv::DecodePlan plan;
   skv::KtList kts;
   skv::SeqTable seq;
-  st = skv::plan_decode(L, B, n_q, lens_host, c->T_max, ws, &plan, &kts, &seq);
+  st = get_plan(l, B, n_q, lens_host, c->T_max, ws, &plan, &kts, &seq);
   if (st != STARKV_OK) return st;
   if (ws_bytes < plan.ws_bytes) return STARKV_EWORKSPACE;
   return hip_status(skv::launch_step(L, *c, plan, kts, seq, X_new, lens_pre.data(), q, out, stream));

@@ -1603,12 +1603,11 @@ __global__ __launch_bounds__(256) void k_values1(ValueArgs a) {
 }
 
 // ---- asynchronous loads straight into LDS
-// Lane l's 16 bytes at src land at LDS byte address lds + 16 l (lds wave-uniform).  Issued as
-// assembly, so the compiler neither counts nor waits for it (it has no destination register):
-// the kernel waits with vm_wait<n>() (n = loads it may leave in flight) and a barrier before any
-// wave reads the data.  Loads the compiler issues itself can only be over-waited because of it.
+// Lane l's 16 bytes at src land at LDS byte address lds + 16 l (lds wave-uniform; the builtin
+// puts it in M0).  The kernel waits with vm_wait<n>() (n = loads it may leave in flight) and a
+// barrier before any wave reads the data.
 __device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(uintptr_t)lds, 16, 0, 0);
 }
 template <int N>
 __device__ __forceinline__ void vm_wait() {

@@ -166,3 +166,52 @@ def test_workspace_sizing(cfg):
     assert n >= chunks * M_pad * 64 * esz  # the probability buffer alone
     assert n % 256 == 0
     layer.close()
+
+
+def test_create_rejects_ascending_spectra():
+    """The rank is the count of singular values above the threshold, kept as a prefix: a spectrum
+    that is not non-increasing is refused with EINVAL before anything is built."""
+    w = I.WORKLOADS[0]
+    s_k, tau_k, s_v, tau_v, _ = I.layer_spectra(w)
+    base = dict(H_q=w.H_q, H_kv=w.H_kv, d_h=w.d_h, d=w.d, dtype=w.dtype, latent=w.latent, tau_k=tau_k, tau_v=tau_v)
+    bad_k = s_k.copy()
+    bad_k[2, 5], bad_k[2, 6] = bad_k[2, 6], bad_k[2, 5] * 1.5  # one ascending step in head 2
+    with pytest.raises(S.StarKVError) as ei:
+        S.Layer(s_k=bad_k, s_v=s_v, **base)
+    assert ei.value.status == -1
+    bad_v = s_v.copy()
+    bad_v[-1] = bad_v[-2] * 2
+    with pytest.raises(S.StarKVError) as ei:
+        S.Layer(s_k=s_k, s_v=bad_v, **base)
+    assert ei.value.status == -1
+    tie = s_k.copy()
+    tie[1, 3] = tie[1, 2]  # equal neighbours are a valid spectrum
+    S.Layer(s_k=tie, s_v=s_v, **base).close()
+
+
+def test_binding_refuses_mismatched_arguments():
+    """The binding checks shapes, batch size and devices before calling the library, so a
+    mis-shaped query, hidden state or length list never reaches a kernel."""
+    import torch
+    w, layer, _ = _layer(2)
+    bf = torch.bfloat16
+    cache = S.Cache(torch.empty(16, dtype=torch.uint8), torch.empty(16, dtype=torch.uint8), 2, 64)
+    with pytest.raises(ValueError, match="lens has 1 entries"):
+        layer.workspace_bytes(2, 1, [64])
+    with pytest.raises(ValueError, match="heads and head dim"):
+        layer.decode(cache, torch.zeros((2, 1, w.H_q, w.d_h + 1), dtype=bf), [64, 64])
+    with pytest.raises(ValueError, match="lens has 3 entries"):
+        layer.decode(cache, torch.zeros((2, 1, w.H_q, w.d_h), dtype=bf), [64, 64, 64])
+    with pytest.raises(ValueError, match="bfloat16"):
+        layer.decode(cache, torch.zeros((2, 1, w.H_q, w.d_h), dtype=torch.float32), [64, 64])
+    with pytest.raises(ValueError, match="device tensor"):
+        layer.decode(cache, torch.zeros((2, 1, w.H_q, w.d_h), dtype=bf), [64, 64])
+    with pytest.raises(ValueError, match="hidden size"):
+        layer.append(cache, torch.zeros((2, 3, w.d - 16), dtype=bf), [0, 0])
+    with pytest.raises(ValueError, match="lens has 1 entries"):
+        layer.append(cache, torch.zeros((2, 3, w.d), dtype=bf), [0])
+    with pytest.raises(ValueError, match="hidden size"):
+        layer.decode_hidden(cache, torch.zeros((2, 1, w.d + 16), dtype=bf), [64, 64])
+    with pytest.raises(ValueError, match="X_new shape"):
+        layer.step(cache, torch.zeros((2, 2, w.d), dtype=bf), torch.zeros((2, 1, w.H_q, w.d_h), dtype=bf), [64, 64])
+    layer.close()

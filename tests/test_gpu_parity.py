@@ -51,9 +51,7 @@ def _run_mini(cfg, exact, q_scale=1.0):
     w = dataclasses.replace(w, B=len(lens0))
     H.log(f"[mini] cfg={cfg} {w.name} exact={exact} lens0={lens0} n_append={w.n_append} q_scale={q_scale}")
     run = H.make_layer(w, exact=exact)
-    H.calibrate(run)
-    if exact and O.is_quantized(w.latent):
-        np.testing.assert_array_equal(H.dev_bits(run.GL.scales), run.scales_o.view(np.uint16))
+    H.calibrate(run)  # scales: bit-exact (exact-latent), or within the accumulation bound (natural)
     H.prefill(run, lens0, oracle_seqs=range(len(lens0)))
     if w.n_append:
         H.append_step(run, w.n_append)
@@ -77,11 +75,8 @@ def _compare_cache(run, exact):
             vc = O.unpack_value_tiles(gv, run.fmt, T)
             okc, ovc = run.ocache[b].key, run.ocache[b].value
             if O.is_quantized(w.latent):
-                dk, dv = np.abs(kc - okc), np.abs(vc - ovc)
-                H.log(f"  seq {b}: natural-run code mismatches key {int((dk > 0).sum())}/{dk.size}, "
-                      f"value {int((dv > 0).sum())}/{dv.size}")
-                assert dk.max() <= 1 and dv.max() <= 1
-                assert (dk > 0).mean() < 1e-3 and (dv > 0).mean() < 1e-3
+                nd = H.check_natural_codes(run, b, kc, vc)
+                H.log(f"  seq {b}: natural-run codes differing by one at rounding boundaries: {nd}/{kc.size + vc.size}")
             else:
                 tol = 1e-5 if w.latent == "f32" else 2 ** -7
                 np.testing.assert_allclose(kc, okc, rtol=tol, atol=tol * np.abs(okc).max())
@@ -104,10 +99,11 @@ def test_mini_parity(cfg, exact):
         H.check_output(w, got[b], ref, f"seq {b} len {int(run.lens[b])}")
 
 
-@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 5])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, 5])
 def test_absorbed_query_from_hidden(cfg):
     """Decode with the query taken from hidden states through the absorbed factors W_q^h B_g^T,
-    against the oracle's q = x W_q followed by the same attention."""
+    against the oracle's q = x W_q followed by the same attention (at most 16 hidden rows: the
+    8-row skinny projection GEMM, and the 16-row one for the 13B-class mini's 12 rows)."""
     from rank_kv_cache_starkv_amd import StarKVError
     w, run = _run_mini(cfg, exact=True)
     B = len(run.lens)
@@ -132,6 +128,50 @@ def test_absorbed_query_from_hidden(cfg):
     with pytest.raises(StarKVError) as ei:
         run.GL.decode_hidden(run.cache, xd, run.lens)
     assert ei.value.status == -7
+
+
+def _small_head_mix84():
+    return dataclasses.replace(I.WORKLOADS[2], H_q=4, H_kv=4, d=512, key_ranks=(20, 33, 48, 27), r_v=96)
+
+
+HIDDEN_FORMS = {
+    # name: (workload, batch, n_q, oracle sequences); rows = batch x n_q hidden rows
+    "13b-64x4-tiled8": (I.WORKLOADS[4], 64, 4, (0, 31, 63)),  # 256 rows, XCD-mapped 8-wave tiles, bf16 hi+lo
+    "gqa-8x4-tiled8": (I.WORKLOADS[3], 8, 4, (0, 7)),  # 32 rows, GQA (G = 4 absorbed copies per KV head)
+    "f32-8x4-tiled8": (I.WORKLOADS[0], 8, 4, (0, 5, 7)),  # 32 rows, fp32 factors
+    "f32-128x9-tiled4": (I.WORKLOADS[0], 128, 9, (0, 77, 127)),  # 1152 rows: the 4-wave grid
+    "bf16-128x9-tiled4": (None, 128, 9, (0, 64, 127)),  # 1152 rows, small-head int8/int4 layer, bf16 hi+lo
+}
+
+
+@pytest.mark.parametrize("form", list(HIDDEN_FORMS))
+def test_absorbed_query_gemm_forms(form):
+    """Hidden-state queries with more than 16 rows, one case per tiled form of the projection GEMM
+    (8-wave XCD-mapped tiles up to 1024 rows, 4-wave tiles beyond; fp32 factors and bf16 high +
+    low parts), against the oracle's q = x W_q followed by the same attention."""
+    w0, B, n_q, sample = HIDDEN_FORMS[form]
+    w0 = w0 if w0 is not None else _small_head_mix84()
+    w = dataclasses.replace(w0, B=B, n_q=n_q)
+    lens0 = [17 + (37 * b) % 150 for b in range(B)]
+    H.log(f"[hidden-query form] {form}: {w.name} B={B} n_q={n_q} rows={B * n_q} lens0 {min(lens0)}..{max(lens0)}")
+    run = H.make_layer(w, exact=True)
+    H.calibrate(run)
+    H.prefill(run, lens0, oracle_seqs=sample, fast_fill=True)
+    H.append_step(run, max(w.n_append, n_q))
+    x = I.as_dtype(I.query_hidden(w), w.dtype)
+    W = I.as_dtype(I.query_weights(w), w.dtype)
+    run.GL.absorb_query(H.to_dev(W, w.dtype))
+    xd = H.to_dev(x, w.dtype)
+    out = run.GL.decode_hidden(run.cache, xd, run.lens)
+    out2 = run.GL.decode_hidden(run.cache, xd, run.lens)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2), "determinism"
+    got = H.from_dev(out)
+    assert np.all(np.isfinite(got))
+    for b in sample:
+        q = O.query_from_hidden(x[b], W, w.H_q, w.d_h)
+        ref = O.decode(q, run.ocache[b], run.OL, n_q, run.scales_o, mode="latent")
+        H.check_output(w, got[b], ref, f"{form} seq {b} len {int(run.lens[b])}")
 
 
 @pytest.mark.parametrize("cfg", [0, 2, 4, 5])
@@ -205,7 +245,7 @@ def _full(cfg):
     lens0 = I.context_lengths(w)
     if cfg == 4:
         order = np.argsort(lens0)
-        sample = [int(order[0]), int(order[len(order) // 2])]
+        sample = [int(order[0]), int(order[len(order) // 2]), int(order[-1])]  # shortest, median, longest
     else:
         sample = [0] if w.B == 1 else [0, w.B - 1]
     H.log(f"[full] cfg={cfg} {w.name} B={w.B} lens0 in [{lens0.min()}, {lens0.max()}] oracle seqs {sample}")
@@ -346,17 +386,13 @@ def test_decode_step_many_rows_natural(cfg):
     torch.cuda.synchronize()
     got = H.from_dev(out)
     for b in run.oracle_seqs:
-        oc = O.compress(Xn_np[b], run.OL, run.scales_o)
-        old = run.ocache[b]
-        run.ocache[b] = O.SequenceCache(np.concatenate([old.key, oc.key]), np.concatenate([old.value, oc.value]))
+        H.extend_oracle(run, b, Xn_np[b])
         gk, gv = H.gpu_seq_cache(run, b)
         T = int(run.lens[b])
         kc = O.unpack_key_rows(gk, run.fmt)[T - w.n_q: T]
         vc = O.unpack_value_tiles(gv, run.fmt, T)[T - w.n_q: T]
-        dk, dv = np.abs(kc - oc.key), np.abs(vc - oc.value)
-        H.log(f"  seq {b}: new-token code mismatches key {int((dk > 0).sum())}/{dk.size}, value {int((dv > 0).sum())}/{dv.size}")
-        assert dk.max() <= 1 and dv.max() <= 1
-        assert (dk > 0).mean() < 1e-2 and (dv > 0).mean() < 1e-2
+        nd = H.check_natural_codes(run, b, kc, vc, t0=T - w.n_q)
+        H.log(f"  seq {b}: new-token codes differing by one at rounding boundaries: {nd}/{kc.size + vc.size}")
         H.check_output(w, got[b], H.oracle_decode(run, q_np, b, mode="latent"), f"seq {b} len {T}")
 
 

@@ -492,9 +492,44 @@ def test_accounting_closed_forms():
     assert acc.reduction(0.75, 16) == pytest.approx(4.0)
     # leading 25% int8 + 75% int4 = 5 bits -> 12.8x at 75% low-rank compression
     assert acc.reduction(0.75, acc.mean_bits(0.25, 8, 4)) == pytest.approx(12.8)
-    # Methodology section 2: joint decomposition costs h times the reconstruction of head-wise
-    for H in (8, 32, 40):
-        assert acc.reconstruction_flops_per_token(1024, H, 128, True) == H * acc.reconstruction_flops_per_token(1024, H, 128, False)
+
+
+def _counted_reconstruct(x, B_blocks, rows, cols):
+    """Rebuild one token's keys by explicit loops over (latent channel, output) pairs of the
+    given factor blocks, counting every multiply and every add; returns (keys, flops)."""
+    flops = 0
+    out = []
+    for (r0, r1), (c0, c1), Bm in zip(rows, cols, B_blocks):
+        for c in range(c1 - c0):
+            acc_v = 0.0
+            for i in range(r1 - r0):
+                acc_v += x[r0 + i] * Bm[i][c]
+                flops += 2
+            out.append(acc_v)
+    return np.array(out), flops
+
+
+@pytest.mark.parametrize("H,R,d_h", [(2, 4, 3), (3, 6, 2), (4, 8, 5)])
+def test_reconstruction_flops_counted(H, R, d_h):
+    """Methodology section 2: the joint factorisation rebuilds every head from the whole latent
+    (rank R), the head-wise one each head from its own R/H channels.  The helper's flop counts
+    equal the multiplies and adds of an explicit-loop reconstruction on a tiny layer, whose
+    result also matches the matrix product; their ratio is the number of heads."""
+    rng = np.random.default_rng(H * 100 + R)
+    x = rng.standard_normal(R)
+    # joint: one block, all R channels to all H d_h outputs
+    Bj = rng.standard_normal((R, H * d_h))
+    kj, fj = _counted_reconstruct(x, [Bj], [(0, R)], [(0, H * d_h)])
+    np.testing.assert_allclose(kj, x @ Bj, rtol=1e-12, atol=1e-12)
+    # head-wise: head h's R/H channels to its own d_h outputs
+    rh = R // H
+    Bh = [rng.standard_normal((rh, d_h)) for _ in range(H)]
+    kh, fh = _counted_reconstruct(x, Bh, [(h * rh, (h + 1) * rh) for h in range(H)], [(0, d_h)] * H)
+    np.testing.assert_allclose(kh, np.concatenate([x[h * rh:(h + 1) * rh] @ Bh[h] for h in range(H)]),
+                               rtol=1e-12, atol=1e-12)
+    assert acc.reconstruction_flops_per_token(R, H, d_h, joint=True) == fj
+    assert acc.reconstruction_flops_per_token(R, H, d_h, joint=False) == fh
+    assert fj == H * fh
 
 
 def test_query_from_hidden_special_cases():
