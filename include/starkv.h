@@ -312,6 +312,24 @@ int starkv_decode_step(const starkv_layer* layer, const starkv_cache* cache, con
                        hipStream_t stream);
 
 /*
+ * starkv_decode_step without a workspace argument and without any device allocation, for callers
+ * that cannot allocate device memory or pass a workspace: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  Identical results to starkv_decode_step (the
+ * same kernels, bit for bit).  The workspace is a static device array of
+ * STARKV_NOALLOC_SCRATCH_BYTES in the library, one copy per GPU, held until the process ends;
+ * the call uses the copy of the current device (hipGetDevice), which must be the device of the
+ * stream and buffers.  Its contents need no initialisation and persist between calls.  All calls
+ * on one GPU share that array: calls that overlap in time on one GPU (concurrent streams, or
+ * several host threads) race and corrupt each other's results; serialise them.  Errors: those of
+ * starkv_decode_step, and EWORKSPACE when the step needs more workspace than the array holds
+ * (starkv_decode_workspace_bytes > STARKV_NOALLOC_SCRATCH_BYTES).
+ */
+#define STARKV_NOALLOC_SCRATCH_BYTES (64u << 20)
+int starkv_decode_step_noalloc(const starkv_layer* layer, const starkv_cache* cache, const void* X_new,
+                               const void* q, int B, int n_q, const int32_t* lens_host, void* out,
+                               hipStream_t stream);
+
+/*
  * Rebuild dense keys and values of sequence b, tokens [t0, t1) (Problem
  * Statement: reconstruction from the latent): K_out[t][g] = x^_g[t] B_g and
  * V_out[t][g] = x^_v[t] B_v[:, g*d_h:(g+1)*d_h], fp32 accumulation, stored in

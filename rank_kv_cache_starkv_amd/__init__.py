@@ -30,6 +30,7 @@ LATENT = {"f32": 0, "bf16": 1, "mix84": 2, "had43": 3}
 DTYPE = {"f32": F32, "bf16": BF16}
 TILE_TOKENS = 32
 MAX_BATCH = 128
+NOALLOC_SCRATCH_BYTES = 64 << 20  # STARKV_NOALLOC_SCRATCH_BYTES
 
 STATUS = {0: "ok", -1: "EINVAL", -2: "ENOMEM", -3: "ECAPACITY", -4: "EUNSUPPORTED", -5: "EWORKSPACE",
           -6: "EHIP", -7: "ESTATE"}
@@ -67,7 +68,8 @@ EXPORTS = ["starkv_abi_version", "starkv_status_string", "starkv_layer_create", 
            "starkv_layer_get_info", "starkv_layer_ranks", "starkv_build_factors", "starkv_bind_factors",
            "starkv_calibrate", "starkv_bind_scales", "starkv_cache_bytes", "starkv_compress_append",
            "starkv_decode_workspace_bytes", "starkv_decode_attention", "starkv_decode_step", "starkv_reconstruct",
-           "starkv_absorb_query", "starkv_decode_attention_hidden", "starkv_profile_enable", "starkv_profile_read"]
+           "starkv_absorb_query", "starkv_decode_attention_hidden", "starkv_profile_enable", "starkv_profile_read",
+           "starkv_decode_step_noalloc"]
 
 _lib = None
 
@@ -99,6 +101,8 @@ def lib() -> ctypes.CDLL:
                                           vp, vp, sz, vp]
     L.starkv_decode_step.argtypes = [vp, ctypes.POINTER(_Cache), vp, vp, ci, ci, ctypes.POINTER(ctypes.c_int32),
                                      vp, vp, sz, vp]
+    L.starkv_decode_step_noalloc.argtypes = [vp, ctypes.POINTER(_Cache), vp, vp, ci, ci,
+                                             ctypes.POINTER(ctypes.c_int32), vp, vp]
     L.starkv_absorb_query.argtypes = [vp, vp, vp]
     L.starkv_decode_attention_hidden.argtypes = [vp, ctypes.POINTER(_Cache), vp, ci, ci,
                                                  ctypes.POINTER(ctypes.c_int32), vp, vp, sz, vp]
@@ -412,6 +416,28 @@ class Layer:
                                             L.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), _ptr(out), _ptr(ws),
                                             int(ws.numel() * ws.element_size()), _stream(stream)),
                "starkv_decode_step")
+        return out
+
+    def step_noalloc(self, cache: Cache, X_new, q, lens: Sequence[int], out, stream=None):
+        """starkv_decode_step with the library's static device scratch instead of a workspace: the
+        call allocates no device memory (``out`` [B, n_q, H_q, d_h] is the caller's).  Calls that
+        overlap on one GPU share the scratch and must be serialised."""
+        _need(q.dim() == 4, "q: tensor [B, n_q, H_q, d_h] expected")
+        B, n_q = int(q.shape[0]), int(q.shape[1])
+        _need(X_new.dtype == self.torch_dtype and X_new.is_contiguous(),
+              f"X_new: contiguous {self.torch_dtype} tensor expected")
+        _need(tuple(X_new.shape) == (B, n_q, self.d), f"X_new shape {tuple(X_new.shape)}, expected {(B, n_q, self.d)}")
+        L = _lens(lens, B)
+        self._check_q(q)
+        _need(_on_device(X_new, q), f"X_new must be on {q.device}")
+        self._check_cache(cache, q)
+        _need(out is not None, "out must be given (the call allocates nothing)")
+        out = self._out(out, q.shape, q)
+        cs = cache.struct()
+        _check(self._lib.starkv_decode_step_noalloc(self._h, ctypes.byref(cs), _ptr(X_new), _ptr(q), B, n_q,
+                                                    L.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), _ptr(out),
+                                                    _stream(stream)),
+               "starkv_decode_step_noalloc")
         return out
 
     def reconstruct(self, cache: Cache, b: int, t0: int, t1: int, stream=None):

@@ -38,6 +38,31 @@ struct starkv_layer {
   PlanMemo memo;
 };
 
+// Device scratch of starkv_decode_step_noalloc: one array per GPU, in the library's code object,
+// held until the process ends.  Host code never uses the array's name as an address (on the host
+// it only names the symbol): the device address of each GPU's copy is looked up once per device
+// with hipGetSymbolAddress, and that pointer is what the kernels receive.
+constexpr size_t kScratchBytes = (size_t)STARKV_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of the scratch array (looked up on the first call on that device).
+static int scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return STARKV_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return STARKV_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return STARKV_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return STARKV_OK;
+}
+
 static void rebase_plan(skv::DecodePlan* P, uintptr_t from, uintptr_t to, int T_max) {
   auto rb = [&](auto*& p) { p = reinterpret_cast<std::remove_reference_t<decltype(p)>>((uintptr_t)p - from + to); };
   skv::DecodeWs& w = P->ws;
@@ -413,6 +438,30 @@ int starkv_decode_step(const starkv_layer* l, const starkv_cache* c, const void*
   if (st != STARKV_OK) return st;
   if (ws_bytes < plan.ws_bytes) return STARKV_EWORKSPACE;
   return hip_status(skv::launch_step(L, *c, plan, kts, seq, X_new, lens_pre.data(), q, out, stream));
+  SKV_GUARD_END
+}
+
+int starkv_decode_step_noalloc(const starkv_layer* l, const starkv_cache* c, const void* X_new, const void* q,
+                               int B, int n_q, const int32_t* lens_host, void* out, hipStream_t stream) {
+  SKV_GUARD_BEGIN
+  if (!l || !q || !out || !X_new) return STARKV_EINVAL;
+  const Layer& L = l->L;
+  int st = check_decode(L, c, B, n_q, lens_host);
+  if (st != STARKV_OK) return st;
+  st = check_bound(L, true);
+  if (st != STARKV_OK) return st;
+  void* ws = nullptr;
+  st = scratch_of_current_device(&ws);
+  if (st != STARKV_OK) return st;
+  int32_t lens_pre[STARKV_MAX_BATCH];
+  for (int b = 0; b < B; ++b) lens_pre[b] = lens_host[b] - n_q;
+  skv::DecodePlan plan;
+  skv::KtList kts;
+  skv::SeqTable seq;
+  st = get_plan(l, B, n_q, lens_host, c->T_max, ws, &plan, &kts, &seq);
+  if (st != STARKV_OK) return st;
+  if (plan.ws_bytes > kScratchBytes) return STARKV_EWORKSPACE;
+  return hip_status(skv::launch_step(L, *c, plan, kts, seq, X_new, lens_pre, q, out, stream));
   SKV_GUARD_END
 }
 

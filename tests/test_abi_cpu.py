@@ -215,3 +215,9 @@ def test_binding_refuses_mismatched_arguments():
     with pytest.raises(ValueError, match="X_new shape"):
         layer.step(cache, torch.zeros((2, 2, w.d), dtype=bf), torch.zeros((2, 1, w.H_q, w.d_h), dtype=bf), [64, 64])
     layer.close()
+
+
+def test_noalloc_scratch_size_matches_header():
+    src = open(HEADER).read()
+    m = re.search(r"#define STARKV_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == S.NOALLOC_SCRATCH_BYTES
