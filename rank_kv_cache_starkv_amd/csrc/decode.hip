@@ -1071,6 +1071,160 @@ __global__ __launch_bounds__(256) void k_scores_chunk(ScoreArgs a) {
   }
 }
 
+// Key scores of int8/int4 latents, walking chunks with the column tile's state in registers.
+// Workgroup = (block of CPB = nch_wg consecutive 32-token chunks in the global numbering, possibly
+// spanning sequences; pair of 16-row column tiles), four waves: wave w takes column tile
+// 2 p + (w & 1) and chunks w >> 1, w >> 1 + 2, ... of the block.  The pairs of one block run on one
+// XCD (grid position mod 8), so the key rows they share are fetched into one L2.  A wave keeps
+// its column tile's query fragments, the per-lane key-row offsets of its K-tiles and its row's
+// parameters in registers while it walks its chunks (the fragments and parameters are reloaded
+// only when a chunk starts another sequence) and issues the key loads of its next chunk before the
+// MFMAs of the current one.  Used when there are at least four column tiles to share the key rows
+// (with two, the per-unit kernel above was faster on MI355X).  The two int8 query parts are combined in integers
+// (254 hi + lo, minus the int4 offset bias) before one conversion.  Output as k_scores_chunk.
+template <int KTM>
+__global__ __launch_bounds__(256) void k_scores_mix(ScoreArgs a) {
+  const int CPB = a.nch_wg;  // chunks per block
+  const DecodeGeom& g = a.g;
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int n = lane & 15, qq = lane >> 4;
+  const int n_pairs = (g.nct + 1) / 2;
+  const int xcd = blockIdx.x & 7, kk = blockIdx.x >> 3;
+  const int pr = kk % n_pairs, blk = 8 * (kk / n_pairs) + xcd;
+  const int ct = 2 * pr + (wave & 1);
+  const int c_first = blk * CPB + (wave >> 1);
+  const int c_end = min(blk * CPB + CPB, a.total_chunks);
+  if (ct >= g.nct || c_first >= c_end) return;  // wave-uniform; the kernel has no barrier
+
+  // K-tiles of the column tile: per-lane byte offset of the lane's 16 bytes in a key row (kOOB
+  // when unused), int8 or int4, and which half of an int4 group's 16 bytes holds the lane's codes
+  const int nkt = a.kts.n[ct];
+  const int ks0 = a.kts.s0[ct], kn0 = a.kts.n0[ct], ks1 = a.kts.s1[ct];
+  uint32_t kofs[KTM];
+  bool k8[KTM], khi[KTM];
+#pragma unroll
+  for (int jt = 0; jt < KTM; ++jt) {
+    const int kt = jt < kn0 ? ks0 + jt : ks1 + (jt - kn0);
+    const int P0 = kt * 64 + 16 * qq;
+    const bool on = jt < nkt;
+    k8[jt] = on && P0 < g.K8;
+    const bool i4 = on && P0 >= g.K8 && P0 < g.K8 + g.K4;
+    const uint32_t o4 = (uint32_t)(g.K8 + (P0 - g.K8) / 2);
+    khi[jt] = (o4 & 8u) != 0;
+    kofs[jt] = k8[jt] ? (uint32_t)P0 : (i4 ? (o4 & ~15u) : kOOB);
+  }
+  const int i = ct * 16 + n;
+  const bool rowvalid = i < g.M_q;
+  const int jq = i % g.n_q;
+  const uint32_t rb = (uint32_t)g.k_row_bytes;
+
+  // key loads of chunk c (sequence bb) into kr
+  auto issue = [&](u32x4 kr[KTM][2], int bb, int c) {
+    const __amdgpu_buffer_rsrc_t krs =
+        buf_rsrc(a.k_rows + (size_t)bb * g.T_max * g.k_row_bytes, (uint32_t)g.T_max * rb);
+    const int t0 = (c - seq_chunk0(a.seq, bb)) * kTC;
+    const int ln = seq_len(a.seq, bb);
+#pragma unroll
+    for (int jt = 0; jt < KTM; ++jt)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const int tok = t0 + tt * 16 + n;
+        kr[jt][tt] = bld16(krs, (kofs[jt] != kOOB && tok < ln) ? (uint32_t)tok * rb + kofs[jt] : kOOB);
+      }
+  };
+  // query fragments and row parameters of sequence bb
+  i32x4 fh[KTM], fl[KTM];
+  float rs = 0.f;
+  int ibias = 0;
+  auto load_seq = [&](int bb) {
+    const uint8_t* fbase = a.qfrag + ((size_t)bb * g.nct + ct) * a.nkt_max * 2048;
+#pragma unroll
+    for (int jt = 0; jt < KTM; ++jt) {
+      const int jc = jt < nkt ? jt : 0;
+      fh[jt] = __builtin_bit_cast(i32x4, ld16(fbase + jc * 2048 + lane * 16));
+      fl[jt] = __builtin_bit_cast(i32x4, ld16(fbase + jc * 2048 + 1024 + lane * 16));
+    }
+    const u32x4 rp = ld16(a.rowp + ((size_t)bb * g.M_pad + min(i, g.M_q - 1)) * 4);
+    rs = __uint_as_float(rp[0]) * (1.f / 254.f);
+    ibias = 254 * (int)__uint_as_float(rp[1]) + (int)__uint_as_float(rp[2]);
+  };
+  int b = seq_of_chunk(a.seq, g.B, c_first);
+  load_seq(b);
+  u32x4 kr[KTM][2];
+  issue(kr, b, c_first);
+
+  for (int c = c_first; c < c_end; c += 2) {
+    const int cn = c + 2;
+    int bn = b;
+    if (cn < c_end)
+      while (cn >= seq_chunk0(a.seq, bn + 1)) ++bn;
+    u32x4 kn[KTM][2];
+    if (cn < c_end) issue(kn, bn, cn);  // the next chunk's keys go out before these MFMAs
+    // scores of chunk c (sequence b): lane holds tokens 16 tt + 4 qq + v of row i
+    i32x4 ah[2], al[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) ah[tt] = al[tt] = i32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int jt = 0; jt < KTM; ++jt) {
+      if (jt < nkt) {  // wave-uniform
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const i32x4 av = k8[jt] ? __builtin_bit_cast(i32x4, kr[jt][tt])
+                                  : unpack_int4_group(khi[jt] ? u32x2{kr[jt][tt][2], kr[jt][tt][3]}
+                                                              : u32x2{kr[jt][tt][0], kr[jt][tt][1]});
+          ah[tt] = mfma16_i8(av, fh[jt], ah[tt]);
+          al[tt] = mfma16_i8(av, fl[jt], al[tt]);
+        }
+      }
+    }
+    const int t0 = (c - seq_chunk0(a.seq, b)) * kTC;
+    const int len = seq_len(a.seq, b);
+    const int lim = rowvalid ? len - g.n_q + jq : -1;  // last token this row sees
+    float s2[2][4];
+    float m = -INFINITY;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int t = t0 + tt * 16 + 4 * qq + v;
+        s2[tt][v] = t <= lim ? rs * (float)(254 * ah[tt][v] + al[tt][v] - ibias) : -INFINITY;
+        m = fmaxf(m, s2[tt][v]);
+      }
+    m = wave_max_xor(m, 16);
+    m = wave_max_xor(m, 32);
+    float l = 0.f;
+    const size_t prow = ((size_t)c * g.M_pad + i) * kTC;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      float e4[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        e4[v] = (s2[tt][v] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s2[tt][v] - m);
+        l += e4[v];
+      }
+      const uint32_t w0 = (uint32_t)f32_to_f16(e4[0]) | ((uint32_t)f32_to_f16(e4[1]) << 16);
+      const uint32_t w1 = (uint32_t)f32_to_f16(e4[2]) | ((uint32_t)f32_to_f16(e4[3]) << 16);
+      st8((uint16_t*)a.p + prow + tt * 16 + 4 * qq, u32x2{w0, w1});
+    }
+    l = wave_sum_xor(l, 16);
+    l = wave_sum_xor(l, 32);
+    if (qq == 0) {
+      a.cm[(size_t)c * g.M_pad + i] = m;
+      a.cl[(size_t)c * g.M_pad + i] = l;
+    }
+    if (cn < c_end) {
+      if (bn != b) {
+        b = bn;
+        load_seq(b);
+      }
+#pragma unroll
+      for (int jt = 0; jt < KTM; ++jt)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) kr[jt][tt] = kn[jt][tt];
+    }
+  }
+}
+
 // ===========================================================================
 // values: z partial of one (sequence, split) for a slice of value blocks
 
@@ -2498,10 +2652,21 @@ static hipError_t launch_decode_tail(const Layer& L, const DecodePlan& plan, con
       // that each of its four waves has a unit
       // chunks per workgroup: the smallest count that gives the four waves equal numbers of
       // (column tile, chunk) units
-      sa.nch_wg = 4 / std::gcd(g.nct, 4);
-      const int n_wg = (w.total_chunks + sa.nch_wg - 1) / sa.nch_wg;
-      if (w.nkt_max <= 6) e = launch_k(ps, k_scores_chunk<STARKV_LATENT_MIX84, 4>, dim3(n_wg), dim3(256), s, sa);
-      else e = launch_k(ps, k_scores_chunk<STARKV_LATENT_MIX84, 2>, dim3(n_wg), dim3(256), s, sa);
+      if (g.nct >= 4 && w.nkt_max <= 8) {
+        // many column tiles: column-tile state in registers while walking blocks of chunks
+        sa.nch_wg = 32;  // chunks per block (16 waves' worth of column tiles x 16 chunks each)
+        const int n_pairs = (g.nct + 1) / 2;
+        const int n_blk = ceil_div(w.total_chunks, sa.nch_wg);
+        const dim3 grid(8 * n_pairs * ceil_div(n_blk, 8));
+        if (w.nkt_max <= 4) e = launch_k(ps, k_scores_mix<4>, grid, dim3(256), s, sa);
+        else if (w.nkt_max <= 6) e = launch_k(ps, k_scores_mix<6>, grid, dim3(256), s, sa);
+        else e = launch_k(ps, k_scores_mix<8>, grid, dim3(256), s, sa);
+      } else {
+        sa.nch_wg = 4 / std::gcd(g.nct, 4);
+        const int n_wg = (w.total_chunks + sa.nch_wg - 1) / sa.nch_wg;
+        if (w.nkt_max <= 6) e = launch_k(ps, k_scores_chunk<STARKV_LATENT_MIX84, 4>, dim3(n_wg), dim3(256), s, sa);
+        else e = launch_k(ps, k_scores_chunk<STARKV_LATENT_MIX84, 2>, dim3(n_wg), dim3(256), s, sa);
+      }
     } else {
       // bf16/fp32 keys (many K-tiles per column tile): K split over the waves of a 128-token block
       sa.nch_wg = 4;
