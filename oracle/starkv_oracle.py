@@ -517,6 +517,30 @@ def attention(q, K, V, n_q: int) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
+# Rotary position embedding of the reconstructed keys and of the queries.  The pages evaluate
+# Llama-family models, whose attention rotates keys and queries by their positions after the
+# key projection; a latent cache then holds the keys before the rotation, which the attention
+# applies to each reconstructed key (Problem Statement: the reconstruction cost; Methodology
+# section 2: head-wise key factors keep it per head).
+
+def rope(x, positions, theta: float, rotary_dim: int) -> np.ndarray:
+    """x [T, ..., d] at integer positions [T] (fp64): for i < rotary_dim / 2 the pair
+    (x[..., i], x[..., i + rotary_dim / 2]) is rotated by the angle
+    positions[t] * theta^(-2 i / rotary_dim); dimensions from rotary_dim on are unchanged."""
+    x = np.asarray(x, np.float64)
+    half = rotary_dim // 2
+    inv = float(theta) ** (-2.0 * np.arange(half) / rotary_dim)
+    ang = np.asarray(positions, np.float64)[:, None] * inv[None, :]  # [T, half]
+    shape = (x.shape[0],) + (1,) * (x.ndim - 2) + (half,)
+    c, sn = np.cos(ang).reshape(shape), np.sin(ang).reshape(shape)
+    out = x.copy()
+    a, b = x[..., :half], x[..., half:rotary_dim]
+    out[..., :half] = a * c - b * sn
+    out[..., half:rotary_dim] = a * sn + b * c
+    return out
+
+
+# ---------------------------------------------------------------------------
 # O9: the same attention computed in the latent space (operations reordered)
 
 def attention_latent(q, xk_hat, xv_hat, layer: Layer, n_q: int) -> np.ndarray:
@@ -603,9 +627,21 @@ def query_from_hidden(x, W_q, H_q: int, d_h: int) -> np.ndarray:
     return (x @ W).reshape(x.shape[0], H_q, d_h)
 
 
-def decode(q, cache: SequenceCache, layer: Layer, n_q: int, scales=None, mode: str = "reconstruct") -> np.ndarray:
-    """Decode attention of one sequence; ``mode`` = "reconstruct" (O7 + O8) or "latent" (O9)."""
+def decode(q, cache: SequenceCache, layer: Layer, n_q: int, scales=None, mode: str = "reconstruct",
+           rope_theta: float = 0.0, rotary_dim: int = 0) -> np.ndarray:
+    """Decode attention of one sequence; ``mode`` = "reconstruct" (O7 + O8) or "latent" (O9).
+    With ``rope_theta`` > 0 the reconstructed keys (position t) and the queries (position
+    T - n_q + j) are rotated first; the latent order does not apply then (the rotation depends
+    on the position, so B_g cannot move past it)."""
     xk, xv = dequantized(cache, layer, scales)
+    if rope_theta > 0:
+        if mode != "reconstruct":
+            raise ValueError("rotary keys need the reconstruct order")
+        K, V = reconstruct(xk, xv, layer)
+        T = K.shape[0]
+        K = rope(K, np.arange(T), rope_theta, rotary_dim)
+        q = rope(np.asarray(q, np.float64), np.arange(T - n_q, T), rope_theta, rotary_dim)
+        return attention(q, K, V, n_q)
     if mode == "latent":
         return attention_latent(q, xk, xv, layer, n_q)
     K, V = reconstruct(xk, xv, layer)

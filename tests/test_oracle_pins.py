@@ -548,3 +548,95 @@ def test_query_from_hidden_special_cases():
             for c in range(d_h):
                 ref = sum(x[j, e] * W[e, h * d_h + c] for e in range(d))
                 assert abs(q[j, h, c] - ref) <= 1e-12 * max(1.0, abs(ref))
+
+
+# ---------------------------------------------------------------------------- rotary keys and queries
+
+def _rope_complex(x, positions, theta, rotary_dim):
+    """The rotation written as complex multiplication: z = x[:h] + i x[h:2h] times e^(i p w)."""
+    h = rotary_dim // 2
+    w = np.array([theta ** (-(2.0 * k) / rotary_dim) for k in range(h)])
+    z = (x[..., :h] + 1j * x[..., h:2 * h]) * np.exp(1j * np.multiply.outer(positions, w)).reshape(
+        (len(positions),) + (1,) * (x.ndim - 2) + (h,))
+    out = np.array(x, dtype=np.float64, copy=True)
+    out[..., :h], out[..., h:2 * h] = z.real, z.imag
+    return out
+
+
+@pytest.mark.parametrize("rd,d", [(8, 8), (64, 128), (128, 128)])
+def test_rope_matches_complex_rotation_and_keeps_norms(rd, d):
+    rng = np.random.default_rng(rd + d)
+    x = rng.standard_normal((7, 3, d))
+    pos = np.array([0, 1, 5, 100, 4095, 32767, 7])
+    got = O.rope(x, pos, 10000.0, rd)
+    # angles reach 3.3e4 rad, whose fp64 argument reduction differs between the two forms by
+    # about 3.3e4 * 2^-53 ~ 4e-12
+    np.testing.assert_allclose(got, _rope_complex(x, pos, 10000.0, rd), rtol=1e-10, atol=1e-10)
+    # position 0 is the identity; dimensions past the rotary ones are untouched
+    np.testing.assert_array_equal(got[0], x[0])
+    np.testing.assert_array_equal(got[..., rd:], x[..., rd:])
+    # each rotated pair keeps its length
+    h = rd // 2
+    np.testing.assert_allclose(got[..., :h] ** 2 + got[..., h:rd] ** 2, x[..., :h] ** 2 + x[..., h:rd] ** 2,
+                               rtol=1e-12, atol=1e-12)
+
+
+def test_rope_scores_depend_on_relative_position_only():
+    """q rotated at m against k rotated at n depends only on m - n (shifting both changes nothing)."""
+    rng = np.random.default_rng(5)
+    q, k = rng.standard_normal((1, 64)), rng.standard_normal((1, 64))
+    for m, n, sh in ((3, 1, 10), (100, 37, 2000), (5, 5, 123)):
+        a = O.rope(q, [m], 500000.0, 64)[0] @ O.rope(k, [n], 500000.0, 64)[0]
+        b = O.rope(q, [m + sh], 500000.0, 64)[0] @ O.rope(k, [n + sh], 500000.0, 64)[0]
+        assert abs(a - b) <= 1e-9 * max(1.0, abs(a))
+
+
+def test_rotary_decode_equals_rotated_dense_attention_and_needs_reconstruct_order():
+    """With identity factors the rotary decode is textbook attention of rotated q and K, written
+    here as a loop over heads against torch's SDPA on CPU (fp64)."""
+    H, d_h, T, n_q = 2, 64, 40, 3
+    d = H * d_h
+    eye_k = np.stack([np.eye(d)[:, g * d_h:(g + 1) * d_h] for g in range(H)])  # U_g
+    L = O.build_layer(eye_k, np.ones((H, d_h), np.float32), np.stack([np.eye(d_h)] * H), np.zeros(H, np.float32),
+                      np.eye(d), np.ones(d, np.float32), np.eye(d), np.float32(0.0), H, "f32", "f32")
+    rng = np.random.default_rng(9)
+    X = rng.standard_normal((T, d)).astype(np.float32)
+    q = rng.standard_normal((n_q, H, d_h))
+    cache = O.compress(X, L)
+    got = O.decode(q, cache, L, n_q, rope_theta=10000.0, rotary_dim=d_h)
+    K = O.rope(X.astype(np.float64).reshape(T, H, d_h), np.arange(T), 10000.0, d_h)
+    qr = O.rope(q, np.arange(T - n_q, T), 10000.0, d_h)
+    V = X.astype(np.float64).reshape(T, H, d_h)
+    for h in range(H):
+        mask = torch.tensor(np.arange(T)[None, :] <= np.arange(T - n_q, T)[:, None])
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.tensor(qr[:, h][None]), torch.tensor(K[:, h][None]), torch.tensor(V[:, h][None]), attn_mask=mask)
+        np.testing.assert_allclose(got[:, h], ref[0].numpy(), rtol=1e-10, atol=1e-12)
+    with pytest.raises(ValueError):
+        O.decode(q, cache, L, n_q, mode="latent", rope_theta=10000.0, rotary_dim=d_h)
+
+
+def test_prefill_chunk_is_causal_attention():
+    """A long query chunk (prefill: every position of the sequence) is causal attention: against
+    torch's SDPA with is_causal on CPU (fp64), on a full-rank orthogonal layer."""
+    H, d_h, T = 2, 16, 24
+    d = H * d_h
+    rng = np.random.default_rng(3)
+    Uk = np.stack([I.orthonormal_columns(rng, d, d_h) for _ in range(H)])
+    Vk = np.stack([I.orthonormal_columns(rng, d_h, d_h) for _ in range(H)])
+    Uv, Vv = I.orthonormal_columns(rng, d, d), I.orthonormal_columns(rng, d, d)
+    L = O.build_layer(Uk, np.ones((H, d_h), np.float32), Vk, np.zeros(H, np.float32), Uv, np.ones(d, np.float32), Vv,
+                      np.float32(0.0), H, "f32", "f32")
+    X = rng.standard_normal((T, d)).astype(np.float32)
+    q = rng.standard_normal((T, H, d_h))
+    got = O.decode(q, O.compress(X, L), L, T)
+    K = (X.astype(np.float64) @ np.concatenate([Uk[g] @ Vk[g].T for g in range(H)], axis=1)).reshape(T, H, d_h)
+    V = (X.astype(np.float64) @ (Uv @ Vv.T)).reshape(T, H, d_h)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.tensor(q.transpose(1, 0, 2)), torch.tensor(K.transpose(1, 0, 2)), torch.tensor(V.transpose(1, 0, 2)),
+        is_causal=True)
+    # the oracle's layer rounds the factors and the stored latent to fp32 (2^-24 relative each)
+    np.testing.assert_allclose(got, ref.numpy().transpose(1, 0, 2), rtol=1e-5, atol=1e-6)
+    # planted mistake: an off-by-one causal limit is far outside that bound
+    shifted = O.decode(q[:-1], O.compress(X, L), L, T - 1)  # query j placed at position j + 1
+    assert np.max(np.abs(shifted - got[:-1])) > 1e-3
