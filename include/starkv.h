@@ -312,6 +312,47 @@ int starkv_decode_step(const starkv_layer* layer, const starkv_cache* cache, con
                        hipStream_t stream);
 
 /*
+ * Rotary position embedding of the keys and queries (the Llama-family layers the STAR-KV summary
+ * page evaluates rotate both by position after the key projection; the latent cache holds the
+ * keys before the rotation).  theta: the rotation base (10000 for Llama-2, 500000 for Llama-3);
+ * rotary_dim: the rotated dimensions, which must equal d_h (0 turns the rotation off).  For
+ * i < d_h / 2 the pair (x_i, x_{i + d_h/2}) of a key at cache position t, or of query j of a
+ * chunk of n_q (position T - n_q + j), is rotated by the angle position * theta^(-2 i / d_h).
+ * A position-dependent rotation does not commute with the key up-projection (Problem Statement:
+ * the reconstruction cost; Methodology section 2: head-wise key factors keep it per head), so a
+ * rotary layer attends over reconstructed keys: starkv_decode_attention, starkv_decode_step and
+ * starkv_decode_step_noalloc take the path of starkv_prefill_attention (their workspace query
+ * returns its size), and starkv_decode_attention_hidden returns EUNSUPPORTED.
+ * Errors: EINVAL (null, rotary_dim < 0 or > d_h, theta not finite and positive), EUNSUPPORTED
+ * (rotary_dim != d_h, d_h not a multiple of 64, fp32 layers).  Setup call: not concurrent with
+ * other calls on the layer.
+ */
+int starkv_layer_set_rope(starkv_layer* layer, float theta, int rotary_dim);
+
+/* Workspace bytes of starkv_prefill_attention for these lengths (host math). */
+int starkv_prefill_workspace_bytes(const starkv_layer* layer, int B, int n_q, const int32_t* lens_host,
+                                   size_t* bytes);
+
+/*
+ * Attention of a chunk of n_q queries per sequence (prefill or chunked prefill; any n_q up to
+ * the length) over keys and values reconstructed from the latent cache (Problem Statement:
+ * reconstruction from the latent; Methodology section 2: K_g = L_g B_g head by head, V = C_v B_v
+ * jointly).  Same result as starkv_decode_attention with that n_q (query j at position
+ * lens_host[b] - n_q + j sees positions up to its own), with the rotation of
+ * starkv_layer_set_rope when set.  For a long chunk rebuilding K and V once (2 T r_v d_h H_kv
+ * flops) and attending densely is cheaper than the latent-space order (2 n_q T r_v per head).
+ * Steps, all on the stream: the dequantised latent of every cached token (fp32), K^ and V^ per KV
+ * head on MFMA (f16, rotated keys), then causal attention with an online softmax over 32-token
+ * tiles.  q: device [B][n_q][H_q][d_h] (bf16); out: same shape.  ws: device workspace of
+ * starkv_prefill_workspace_bytes (256-byte aligned, no initialisation): the latent and K^, V^ of
+ * all sequences (each padded to a multiple of 32 tokens).  bf16 layers only (EUNSUPPORTED for
+ * fp32).  Reconstructed keys and values are held in f16: their magnitudes must stay within its
+ * range.  Errors: EINVAL, ECAPACITY, EWORKSPACE, ESTATE, EUNSUPPORTED, EHIP.
+ */
+int starkv_prefill_attention(const starkv_layer* layer, const starkv_cache* cache, const void* q, int B, int n_q,
+                             const int32_t* lens_host, void* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * starkv_decode_step without a workspace argument and without any device allocation, for callers
  * that cannot allocate device memory or pass a workspace: code under HIP graph capture, tight
  * serving loops, harnesses that forbid hipMalloc.  Identical results to starkv_decode_step (the

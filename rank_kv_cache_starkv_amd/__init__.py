@@ -69,7 +69,8 @@ EXPORTS = ["starkv_abi_version", "starkv_status_string", "starkv_layer_create", 
            "starkv_calibrate", "starkv_bind_scales", "starkv_cache_bytes", "starkv_compress_append",
            "starkv_decode_workspace_bytes", "starkv_decode_attention", "starkv_decode_step", "starkv_reconstruct",
            "starkv_absorb_query", "starkv_decode_attention_hidden", "starkv_profile_enable", "starkv_profile_read",
-           "starkv_decode_step_noalloc"]
+           "starkv_decode_step_noalloc", "starkv_layer_set_rope", "starkv_prefill_workspace_bytes",
+           "starkv_prefill_attention"]
 
 _lib = None
 
@@ -103,6 +104,10 @@ def lib() -> ctypes.CDLL:
                                      vp, vp, sz, vp]
     L.starkv_decode_step_noalloc.argtypes = [vp, ctypes.POINTER(_Cache), vp, vp, ci, ci,
                                              ctypes.POINTER(ctypes.c_int32), vp, vp]
+    L.starkv_layer_set_rope.argtypes = [vp, ctypes.c_float, ci]
+    L.starkv_prefill_workspace_bytes.argtypes = [vp, ci, ci, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(sz)]
+    L.starkv_prefill_attention.argtypes = [vp, ctypes.POINTER(_Cache), vp, ci, ci, ctypes.POINTER(ctypes.c_int32),
+                                           vp, vp, sz, vp]
     L.starkv_absorb_query.argtypes = [vp, vp, vp]
     L.starkv_decode_attention_hidden.argtypes = [vp, ctypes.POINTER(_Cache), vp, ci, ci,
                                                  ctypes.POINTER(ctypes.c_int32), vp, vp, sz, vp]
@@ -438,6 +443,41 @@ class Layer:
                                                     L.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), _ptr(out),
                                                     _stream(stream)),
                "starkv_decode_step_noalloc")
+        return out
+
+    def set_rope(self, theta: float, rotary_dim: Optional[int] = None) -> None:
+        """Rotate keys and queries by position (theta: the base; rotary_dim: d_h, or 0 to turn the
+        rotation off).  Decode of a rotary layer attends over reconstructed keys."""
+        rd = self.d_h if rotary_dim is None else int(rotary_dim)
+        _check(self._lib.starkv_layer_set_rope(self._h, float(theta), rd), "starkv_layer_set_rope")
+        self._ws_memo = None
+
+    def prefill_workspace_bytes(self, B: int, n_q: int, lens: Sequence[int]) -> int:
+        L = _lens(lens, B)
+        n = ctypes.c_size_t()
+        _check(self._lib.starkv_prefill_workspace_bytes(self._h, B, n_q, L.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                                        ctypes.byref(n)), "starkv_prefill_workspace_bytes")
+        return n.value
+
+    def prefill(self, cache: Cache, q, lens: Sequence[int], out=None, ws=None, stream=None):
+        """Attention of a query chunk q [B, n_q, H_q, d_h] (positions lens[b] - n_q ..) over keys
+        and values reconstructed from the cache; any n_q up to the lengths."""
+        _need(q.dim() == 4, "q: tensor [B, n_q, H_q, d_h] expected")
+        L = _lens(lens, int(q.shape[0]))
+        B, n_q = self._check_q(q)
+        self._check_cache(cache, q)
+        need = self.prefill_workspace_bytes(B, n_q, L)
+        if ws is None:
+            import torch
+            ws = torch.empty((max(need, 256),), dtype=torch.uint8, device=q.device)
+        else:
+            _need(ws.is_contiguous() and _on_device(ws, q), "ws: contiguous tensor on the device of the inputs")
+        out = self._out(out, q.shape, q)
+        cs = cache.struct()
+        _check(self._lib.starkv_prefill_attention(self._h, ctypes.byref(cs), _ptr(q), B, n_q,
+                                                  L.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), _ptr(out),
+                                                  _ptr(ws), int(ws.numel() * ws.element_size()), _stream(stream)),
+               "starkv_prefill_attention")
         return out
 
     def reconstruct(self, cache: Cache, b: int, t0: int, t1: int, stream=None):

@@ -13,7 +13,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libstarkv.so")
 INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 
-SOURCES = ["api.hip", "layer.hip", "append.hip", "decode.hip", "reconstruct.hip", "profile.hip"]
+SOURCES = ["api.hip", "layer.hip", "append.hip", "decode.hip", "prefill.hip", "reconstruct.hip", "profile.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

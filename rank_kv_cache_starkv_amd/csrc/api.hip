@@ -367,6 +367,11 @@ int starkv_decode_workspace_bytes(const starkv_layer* l, int B, int n_q, const i
   if (B > STARKV_MAX_BATCH || l->L.H_q * n_q > STARKV_MAX_QROWS) return STARKV_EUNSUPPORTED;
   for (int b = 0; b < B; ++b)
     if (lens_host[b] < n_q) return STARKV_EINVAL;
+  if (l->L.rope_theta > 0.f) {
+    // rotary layers attend over reconstructed keys and values
+    *bytes = skv::prefill_workspace_bytes(l->L, B, lens_host);
+    return STARKV_OK;
+  }
   skv::DecodePlan plan;
   skv::KtList kts;
   skv::SeqTable seq;
@@ -387,6 +392,10 @@ int starkv_decode_attention(const starkv_layer* l, const starkv_cache* c, const 
   st = check_bound(L, true);
   if (st != STARKV_OK) return st;
   if (((uintptr_t)ws & 255) != 0) return STARKV_EINVAL;
+  if (L.rope_theta > 0.f) {
+    if (ws_bytes < skv::prefill_workspace_bytes(L, B, lens_host)) return STARKV_EWORKSPACE;
+    return hip_status(skv::launch_prefill(L, *c, q, B, n_q, lens_host, out, ws, stream));
+  }
   skv::DecodePlan plan;
   skv::KtList kts;
   skv::SeqTable seq;
@@ -407,6 +416,7 @@ int starkv_decode_attention_hidden(const starkv_layer* l, const starkv_cache* c,
   if (st != STARKV_OK) return st;
   st = check_bound(L, true);
   if (st != STARKV_OK) return st;
+  if (L.rope_theta > 0.f) return STARKV_EUNSUPPORTED;  // rotated keys: B_g cannot be absorbed into W_q
   if (!L.d_wqk) return STARKV_ESTATE;
   if (((uintptr_t)ws & 255) != 0) return STARKV_EINVAL;
   skv::DecodePlan plan;
@@ -429,15 +439,79 @@ int starkv_decode_step(const starkv_layer* l, const starkv_cache* c, const void*
   st = check_bound(L, true);
   if (st != STARKV_OK) return st;
   if (((uintptr_t)ws & 255) != 0) return STARKV_EINVAL;
-  std::vector<int32_t> lens_pre(B);
+  int32_t lens_pre[STARKV_MAX_BATCH];
   for (int b = 0; b < B; ++b) lens_pre[b] = lens_host[b] - n_q;
+  if (L.rope_theta > 0.f) {
+    if (ws_bytes < skv::prefill_workspace_bytes(L, B, lens_host)) return STARKV_EWORKSPACE;
+    const hipError_t e = skv::launch_append(L, *c, X_new, B, n_q, lens_pre, stream);
+    if (e != hipSuccess) return STARKV_EHIP;
+    return hip_status(skv::launch_prefill(L, *c, q, B, n_q, lens_host, out, ws, stream));
+  }
   skv::DecodePlan plan;
   skv::KtList kts;
   skv::SeqTable seq;
   st = get_plan(l, B, n_q, lens_host, c->T_max, ws, &plan, &kts, &seq);
   if (st != STARKV_OK) return st;
   if (ws_bytes < plan.ws_bytes) return STARKV_EWORKSPACE;
-  return hip_status(skv::launch_step(L, *c, plan, kts, seq, X_new, lens_pre.data(), q, out, stream));
+  return hip_status(skv::launch_step(L, *c, plan, kts, seq, X_new, lens_pre, q, out, stream));
+  SKV_GUARD_END
+}
+
+int starkv_layer_set_rope(starkv_layer* l, float theta, int rotary_dim) {
+  if (!l) return STARKV_EINVAL;
+  Layer& L = l->L;
+  if (rotary_dim == 0) {
+    L.rope_theta = 0.f;
+    L.rotary_dim = 0;
+    return STARKV_OK;
+  }
+  if (rotary_dim < 0 || rotary_dim > L.d_h || bad_float(theta) || !(theta > 0.f)) return STARKV_EINVAL;
+  if (rotary_dim != L.d_h || L.d_h % 64 != 0 || L.dtype != STARKV_BF16) return STARKV_EUNSUPPORTED;
+  L.rope_theta = theta;
+  L.rotary_dim = rotary_dim;
+  return STARKV_OK;
+}
+
+static int check_prefill(const Layer& L, const starkv_cache* c, int B, int n_q, const int32_t* lens) {
+  if (!lens || B <= 0 || n_q <= 0) return STARKV_EINVAL;
+  if (B > STARKV_MAX_BATCH) return STARKV_EUNSUPPORTED;
+  if (L.dtype != STARKV_BF16) return STARKV_EUNSUPPORTED;
+  if (c) {
+    const int st = check_cache(L, c, B);
+    if (st != STARKV_OK) return st;
+  }
+  long total = 0;
+  for (int b = 0; b < B; ++b) {
+    if (lens[b] < n_q) return STARKV_EINVAL;
+    if (c && lens[b] > c->T_max) return STARKV_ECAPACITY;
+    total += (lens[b] + STARKV_TILE_TOKENS - 1) / STARKV_TILE_TOKENS * STARKV_TILE_TOKENS;
+  }
+  if (total > (1L << 30) / (L.n_lat > L.H_kv * L.d_h ? L.n_lat : L.H_kv * L.d_h)) return STARKV_EUNSUPPORTED;
+  return STARKV_OK;
+}
+
+int starkv_prefill_workspace_bytes(const starkv_layer* l, int B, int n_q, const int32_t* lens_host, size_t* bytes) {
+  SKV_GUARD_BEGIN
+  if (!l || !bytes) return STARKV_EINVAL;
+  const int st = check_prefill(l->L, nullptr, B, n_q, lens_host);
+  if (st != STARKV_OK) return st;
+  *bytes = skv::prefill_workspace_bytes(l->L, B, lens_host);
+  return STARKV_OK;
+  SKV_GUARD_END
+}
+
+int starkv_prefill_attention(const starkv_layer* l, const starkv_cache* c, const void* q, int B, int n_q,
+                             const int32_t* lens_host, void* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  SKV_GUARD_BEGIN
+  if (!l || !q || !out || !ws) return STARKV_EINVAL;
+  const Layer& L = l->L;
+  int st = check_prefill(L, c, B, n_q, lens_host);
+  if (st != STARKV_OK) return st;
+  st = check_bound(L, true);
+  if (st != STARKV_OK) return st;
+  if (((uintptr_t)ws & 255) != 0) return STARKV_EINVAL;
+  if (ws_bytes < skv::prefill_workspace_bytes(L, B, lens_host)) return STARKV_EWORKSPACE;
+  return hip_status(skv::launch_prefill(L, *c, q, B, n_q, lens_host, out, ws, stream));
   SKV_GUARD_END
 }
 
@@ -455,6 +529,12 @@ int starkv_decode_step_noalloc(const starkv_layer* l, const starkv_cache* c, con
   if (st != STARKV_OK) return st;
   int32_t lens_pre[STARKV_MAX_BATCH];
   for (int b = 0; b < B; ++b) lens_pre[b] = lens_host[b] - n_q;
+  if (L.rope_theta > 0.f) {
+    if (skv::prefill_workspace_bytes(L, B, lens_host) > kScratchBytes) return STARKV_EWORKSPACE;
+    const hipError_t e = skv::launch_append(L, *c, X_new, B, n_q, lens_pre, stream);
+    if (e != hipSuccess) return STARKV_EHIP;
+    return hip_status(skv::launch_prefill(L, *c, q, B, n_q, lens_host, out, ws, stream));
+  }
   skv::DecodePlan plan;
   skv::KtList kts;
   skv::SeqTable seq;

@@ -1,0 +1,555 @@
+// Attention over keys and values reconstructed from the latent cache, for query chunks of any
+// length (prefill, chunked prefill) and for layers whose keys carry a rotary position embedding.
+//
+// STAR-KV summary page, Problem Statement: the cache holds the projected hidden states, and
+// rebuilding K and V from them costs compute; Methodology section 2: keys are factored head by
+// head (K_g = L_g B_g), values jointly (V = C_v B_v).  The latent-space order used by decode moves
+// B_g and B_v past the attention weights, which pays when a few queries meet many tokens; a chunk
+// of n_q queries does 2 n_q T r_v value work in the latent space against 2 T r_v d_h H_kv to
+// rebuild V once plus 2 n_q T d_h per head to attend, so long chunks rebuild K and V first.  A
+// position-dependent rotation of the keys does not commute with B_g at all: a rotary layer always
+// takes this path.
+//
+//   1. k_deq_latent  the dequantised latent of every cached token, token-major fp32:
+//                    xhat[t][c] = code * scale_c (or the stored bf16 / fp32 latent)
+//   2. k_recon       K^_g = xhat_g B_g and V^_g = xhat_v B_v[:, g d_h:(g + 1) d_h] per KV head on
+//                    MFMA (fp32 latent split into bf16 high and low parts), the rotation of the
+//                    keys at their positions in the epilogue; stored as f16, K^ token-major and V^
+//                    transposed (dims x tokens)
+//   3. k_flash       causal attention of the query chunk over K^, V^: 32-token key tiles with an
+//                    online softmax (base 2), S^T = K^ Q^T and O^T = V^T P^T on f16 MFMA so that a
+//                    row's softmax state lives in one lane
+//
+// Tokens of every sequence are laid out back to back, each sequence padded to a multiple of 32.
+#include <math.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "device_common.h"
+#include "profile.h"
+#include "starkv_internal.h"
+
+namespace skv {
+
+namespace {
+
+constexpr int kRT = 32;  // token tile of every prefill kernel
+
+int ceil_div(int a, int b) { return (a + b - 1) / b; }
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// sequence whose padded token range holds token t (bases ascending, base[0] = 0)
+__device__ __forceinline__ int seq_of_token(const int* base, int B, int t) {
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (base[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// sin and cos of a rotation angle given in fp64 (positions reach 2^15 and more, where an fp32
+// angle would already be off by ~2^-9 rad): reduced to [-pi, pi] in fp64, then sincosf
+__device__ __forceinline__ void rot_sincos(double ang, float* sn, float* cs) {
+  constexpr double kTwoPi = 6.283185307179586476925287;
+  const double red = ang - kTwoPi * rint(ang / kTwoPi);
+  sincosf((float)red, sn, cs);
+}
+
+struct SeqBases {
+  int B;
+  int lens[kMaxB];
+  int base[kMaxB + 1];  // first padded token of each sequence; base[B] = total
+};
+
+// ---------------------------------------------------------------------------------------------
+// 1. dequantised latent, token-major
+
+struct DeqArgs {
+  const uint8_t* k_rows;
+  const uint8_t* v_tiles;
+  const uint16_t* scales;
+  const int* src;  // [n_lat] (head << 16) | index within the head; head = H_kv for value channels
+  HeadTables heads;
+  float* xhat;     // [total][n_lat]
+  int n_lat, n_key, H_kv, K8, V8, n8v, k_row_bytes, v_rows, T_max;
+  SeqBases sb;
+};
+
+// Workgroup = one 32-token tile of one sequence; thread items walk (token, channel) with the
+// channel fastest, so the fp32 stores are contiguous.  Tokens past the length get 0.
+template <int LAT>
+__global__ __launch_bounds__(256) void k_deq_latent(DeqArgs a) {
+  const int tok0 = blockIdx.x * kRT;
+  const int b = seq_of_token(a.sb.base, a.sb.B, tok0);
+  const int t0 = tok0 - a.sb.base[b], len = a.sb.lens[b];
+  for (int idx = threadIdx.x; idx < kRT * a.n_lat; idx += 256) {
+    const int tl = idx / a.n_lat, c = idx % a.n_lat;
+    const int t = t0 + tl;
+    float x = 0.f;
+    if (t < len) {
+      if (c < a.n_key) {
+        const uint8_t* row = a.k_rows + ((size_t)b * a.T_max + t) * a.k_row_bytes;
+        if (LAT == STARKV_LATENT_MIX84) {
+          const int s = a.src[c];
+          const int g = s >> 16, k = s & 0xFFFF;
+          const int n8 = a.heads.n8[g];
+          int code;
+          if (k < n8) {
+            code = (int)(int8_t)row[a.heads.off8[g] + k];
+          } else {
+            const int u = a.heads.off4[g] + (k - n8);
+            const int byte = row[a.K8 + (u >> 1)];
+            code = ((int)(((u & 1) ? byte >> 4 : byte) & 0xF) ^ 8) - 8;  // signed nibble
+          }
+          x = (float)code * f16_to_f32(a.scales[c]);
+        } else if (LAT == STARKV_LATENT_BF16) {
+          x = bf16_to_f32(((const uint16_t*)row)[c]);
+        } else {
+          x = ((const float*)row)[c];
+        }
+      } else {
+        const int cv = c - a.n_key;
+        if (LAT == STARKV_LATENT_MIX84) {
+          const bool i4 = cv >= a.n8v;
+          const int w = cv - a.n8v;
+          const int vr = i4 ? a.V8 + (w >> 1) : cv;
+          const int byte = a.v_tiles[vblock_off(b, vr >> 5, t / kTT, a.v_rows, a.T_max, 1) + (vr & 31) * kTT + t % kTT];
+          const int code = i4 ? ((int)(((w & 1) ? byte >> 4 : byte) & 0xF) ^ 8) - 8 : (int)(int8_t)byte;
+          x = (float)code * f16_to_f32(a.scales[c]);
+        } else if (LAT == STARKV_LATENT_BF16) {
+          const uint16_t* blk = (const uint16_t*)(a.v_tiles + vblock_off(b, cv >> 5, t / kTT, a.v_rows, a.T_max, 2));
+          x = bf16_to_f32(blk[(cv & 31) * kTT + t % kTT]);
+        } else {
+          const float* blk = (const float*)(a.v_tiles + vblock_off(b, cv >> 5, t / kTT, a.v_rows, a.T_max, 4));
+          x = blk[(cv & 31) * kTT + t % kTT];
+        }
+      }
+    }
+    a.xhat[(size_t)(tok0 + tl) * a.n_lat + c] = x;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// 2. reconstruction of K^ and V^ per KV head (bf16 factors)
+
+struct ReconArgs {
+  const float* xhat;
+  const uint16_t* B_k;   // [n_key][d_h]
+  const uint16_t* B_vt;  // [H_kv d_h][r_v]
+  const int* koff;       // [H_kv + 1]
+  _Float16* kh;          // [total][H_kv][d_h]
+  _Float16* vt;          // [H_kv d_h][total], tokens of each 16-group in swapped-middle order
+  int n_lat, n_key, r_v, H_kv, d_h, total, rpad;
+  float rope_theta;
+  int rotary_dim;
+  SeqBases sb;
+};
+
+// position of token t in the transposed value store: within each group of 16, tokens 4..7 and
+// 8..11 trade places, so that lane half q of the attention's value operand reads 8 consecutive
+// entries holding exactly the tokens its probability operand holds
+__device__ __forceinline__ int vt_slot(int t) {
+  const int u = t & 15;
+  return (t & ~15) | (u & 3) | ((u & 4) << 1) | ((u & 8) >> 1);
+}
+
+// Workgroup = (128 tokens, KV head g, keys or values), four waves of 32 tokens x all d_h columns
+// (NT = d_h / 32 column tiles of 32x32x16 bf16 MFMA).  The latent row of a token is split into
+// bf16 high and low parts (two MFMAs), so the product is as accurate as fp32 x bf16.  Keys read
+// B_g transposed from LDS (staged by the workgroup); values read B_v^T rows directly.  Rotary keys
+// (over the whole head dimension): the pair (e, e + d_h / 2) is rotated by
+// position * theta^(-2 e / d_h), the angle formed and reduced in fp64.
+template <int NT, bool VEC>
+__global__ __launch_bounds__(256) void k_recon(ReconArgs a) {
+  extern __shared__ uint16_t bkt[];  // keys: B_g^T [d_h][rpad]
+  const int g = blockIdx.y, kind = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int r = lane & 31, q = lane >> 5;
+  const int c_lo = kind == 0 ? a.koff[g] : a.n_key;
+  const int rk = kind == 0 ? a.koff[g + 1] - c_lo : a.r_v;
+  if (kind == 0) {
+    for (int i = threadIdx.x; i < a.d_h * a.rpad; i += 256) {
+      const int e = i / a.rpad, k = i % a.rpad;
+      bkt[i] = k < rk ? a.B_k[(size_t)(c_lo + k) * a.d_h + e] : (uint16_t)0;
+    }
+    __syncthreads();
+  }
+  const int tw = blockIdx.x * 128 + wave * 32;  // first token of this wave
+  if (tw >= a.total) return;  // wave-uniform, after the only barrier
+  const int tok = tw + r;     // this lane's A-operand token
+  f32x16 acc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[nt][v] = 0.f;
+  const float* xr = a.xhat + (size_t)tok * a.n_lat + c_lo;
+  for (int k0 = 0; k0 < rk; k0 += 16) {
+    const int kb = k0 + 8 * q;
+    float xv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) xv[i] = kb + i < rk ? xr[kb + i] : 0.f;
+    uint32_t hw[4], lw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint16_t h0 = f32_to_bf16(xv[2 * i]), h1 = f32_to_bf16(xv[2 * i + 1]);
+      const uint16_t l0 = f32_to_bf16(xv[2 * i] - bf16_to_f32(h0)), l1 = f32_to_bf16(xv[2 * i + 1] - bf16_to_f32(h1));
+      hw[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+      lw[i] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+    }
+    const bf16x8 ah = as_bf16x8(u32x4{hw[0], hw[1], hw[2], hw[3]});
+    const bf16x8 al = as_bf16x8(u32x4{lw[0], lw[1], lw[2], lw[3]});
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int e = nt * 32 + r;
+      u32x4 bw;
+      if (kind == 0) {
+        bw = *(const u32x4*)(bkt + e * a.rpad + kb);
+      } else if (VEC) {
+        bw = kb < rk ? ld16(a.B_vt + (size_t)(g * a.d_h + e) * a.r_v + kb) : u32x4{0, 0, 0, 0};
+      } else {
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int k = kb + 2 * i;
+          const uint32_t lo = k < rk ? a.B_vt[(size_t)(g * a.d_h + e) * a.r_v + k] : 0u;
+          const uint32_t hi = k + 1 < rk ? a.B_vt[(size_t)(g * a.d_h + e) * a.r_v + k + 1] : 0u;
+          w[i] = lo | (hi << 16);
+        }
+        bw = u32x4{w[0], w[1], w[2], w[3]};
+      }
+      acc[nt] = mfma32_bf16(ah, as_bf16x8(bw), acc[nt]);
+      acc[nt] = mfma32_bf16(al, as_bf16x8(bw), acc[nt]);
+    }
+  }
+  // epilogue: lane holds column e = 32 nt + r of tokens tw + d32_row(v, q)
+  const int b = seq_of_token(a.sb.base, a.sb.B, tw);
+  const int base = a.sb.base[b], len = a.sb.lens[b];
+  if (kind == 0 && a.rope_theta > 0.f) {
+    // rotary keys over the whole head dimension: pairs (e, e + d_h / 2) in column tiles nt and
+    // nt + NT / 2 of the same lane
+    const double lt = log2((double)a.rope_theta);
+#pragma unroll
+    for (int nt = 0; nt < NT / 2; ++nt) {
+      const int e = nt * 32 + r;
+      const double inv = exp2(-2.0 * (double)e / (double)a.d_h * lt);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int t = tw + d32_row(v, q) - base;  // position in the sequence
+        float sn, cs;
+        rot_sincos((double)t * inv, &sn, &cs);
+        const float x0 = acc[nt][v], x1 = acc[nt + NT / 2][v];
+        acc[nt][v] = x0 * cs - x1 * sn;
+        acc[nt + NT / 2][v] = x0 * sn + x1 * cs;
+      }
+    }
+  }
+  // every token of the padded range is stored: padding tokens (past the length) hold zeros, so
+  // the attention's masked products never meet uninitialised memory
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int e = nt * 32 + r;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int tf = tw + d32_row(v, q);
+      const _Float16 x = tf - base < len ? (_Float16)acc[nt][v] : (_Float16)0.f;
+      if (kind == 0) a.kh[((size_t)tf * a.H_kv + g) * a.d_h + e] = x;
+      else a.vt[(size_t)(g * a.d_h + e) * a.total + vt_slot(tf)] = x;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// 3. causal attention over the reconstructed keys and values
+
+struct FlashArgs {
+  const void* q;  // [B][n_q][H_q][d_h] (dtype)
+  void* out;      // same shape and dtype
+  const _Float16* kh;
+  const _Float16* vt;
+  int n_q, H_q, H_kv, G, d_h, total;
+  float qscale;  // log2(e) / sqrt(d_h)
+  float rope_theta;
+  int rotary_dim;
+  SeqBases sb;
+};
+
+// Workgroup = (128 queries of one head, sequence), four waves of 32 queries; no barrier.  Query j
+// (position len - n_q + j) sees tokens <= its position.  Per 32-token key tile: S^T = K^ Q^T
+// (lane = query row, 16 tokens), masked and scaled to base 2, an online softmax whose row
+// maximum and sum stay in the lane (the two lane halves hold different tokens of the same rows and
+// agree on the maximum through one exchange), then O^T += V^T P^T with the probabilities as the
+// B operand straight from the S^T registers (the value store's token order matches them).
+template <int NT, int DT>
+__global__ __launch_bounds__(256) void k_flash(FlashArgs a) {
+  constexpr int KS = NT * 2;  // 16-dim K-steps of the scores
+  const int h = blockIdx.y, b = blockIdx.z, g = h / a.G;
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int r = lane & 31, q = lane >> 5;
+  const int jw = blockIdx.x * 128 + wave * 32;  // first query of this wave
+  if (jw >= a.n_q) return;                      // wave-uniform
+  const int len = a.sb.lens[b], base = a.sb.base[b];
+  const int j = min(jw + r, a.n_q - 1);         // this lane's query (rows past n_q repeat the last, not stored)
+  const int pos = len - a.n_q + j;
+  const int pos_max = len - a.n_q + min(jw + 31, a.n_q - 1);
+  // query fragments: K-step ks holds dims 16 ks + 8 q .. + 7; the rotation pairs dims e and
+  // e + d_h / 2, which sit in K-steps ks and ks + KS / 2 of the same lane
+  f16x8 qh[KS];
+  const size_t qoff = (((size_t)b * a.n_q + j) * a.H_q + h) * a.d_h;
+  auto ldq = [&](int ks, float x[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const size_t e = (size_t)ks * 16 + 8 * q + i;
+      x[i] = DT == STARKV_F32 ? ((const float*)a.q)[qoff + e] : bf16_to_f32(((const uint16_t*)a.q)[qoff + e]);
+    }
+  };
+#pragma unroll
+  for (int ks = 0; ks < KS / 2; ++ks) {
+    float x0[8], x1[8];
+    ldq(ks, x0);
+    ldq(ks + KS / 2, x1);
+    if (a.rope_theta > 0.f) {
+      const double lt = log2((double)a.rope_theta);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int e = ks * 16 + 8 * q + i;
+        float sn, cs;
+        rot_sincos((double)pos * exp2(-2.0 * (double)e / (double)a.d_h * lt), &sn, &cs);
+        const float y0 = x0[i] * cs - x1[i] * sn;
+        const float y1 = x0[i] * sn + x1[i] * cs;
+        x0[i] = y0;
+        x1[i] = y1;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      qh[ks][i] = (_Float16)x0[i];
+      qh[ks + KS / 2][i] = (_Float16)x1[i];
+    }
+  }
+
+  f32x16 acc[NT];
+#pragma unroll
+  for (int mt = 0; mt < NT; ++mt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[mt][v] = 0.f;
+  float m_run = -INFINITY, l = 0.f;
+  const _Float16* krow = a.kh + ((size_t)(base + r) * a.H_kv + g) * a.d_h + 8 * q;
+  const size_t kstep = (size_t)kRT * a.H_kv * a.d_h;  // key-tile stride
+  const int n_kt = pos_max / kRT + 1;
+  for (int kt = 0; kt < n_kt; ++kt) {
+    // S^T: rows = tokens kt 32 + d32_row(v, q), columns = queries
+    f32x16 s;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) s[v] = 0.f;
+    const _Float16* kp = krow + (size_t)kt * kstep;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) s = mfma32_f16(as_f16x8(ld16(kp + ks * 16)), qh[ks], s);
+    float mt = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int t = kt * kRT + d32_row(v, q);
+      s[v] = t <= pos ? s[v] * a.qscale : -INFINITY;
+      mt = fmaxf(mt, s[v]);
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    const float m_new = fmaxf(m_run, mt);  // finite: token 0 is visible to every query
+    const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    float ps = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      s[v] = s[v] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s[v] - m_new);  // probability
+      ps += s[v];
+    }
+    l = l * alpha + ps;
+    m_run = m_new;
+#pragma unroll
+    for (int mt2 = 0; mt2 < NT; ++mt2)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[mt2][v] *= alpha;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      f16x8 pb;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pb[i] = (_Float16)s[8 * kk + i];
+#pragma unroll
+      for (int mt2 = 0; mt2 < NT; ++mt2) {
+        const _Float16* vp = a.vt + (size_t)(g * a.d_h + mt2 * 32 + r) * a.total + base + kt * kRT + 16 * kk + 8 * q;
+        acc[mt2] = mfma32_f16(as_f16x8(ld16(vp)), pb, acc[mt2]);
+      }
+    }
+  }
+  l += __shfl_xor(l, 32, 64);
+  if (jw + r >= a.n_q) return;
+  const float il = 1.f / l;
+  const size_t ooff = (((size_t)b * a.n_q + j) * a.H_q + h) * a.d_h;
+  // O^T: lane holds query j, dims 32 mt + d32_row(v, q) (runs of 4)
+#pragma unroll
+  for (int mt2 = 0; mt2 < NT; ++mt2)
+#pragma unroll
+    for (int v4 = 0; v4 < 4; ++v4) {
+      const int e = mt2 * 32 + 8 * v4 + 4 * q;
+      float o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = acc[mt2][4 * v4 + i] * il;
+      if (DT == STARKV_F32) {
+        st16((float*)a.out + ooff + e, u32x4{__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]),
+                                             __float_as_uint(o[3])});
+      } else {
+        st8((uint16_t*)a.out + ooff + e,
+            u32x2{(uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16),
+                  (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16)});
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// host side
+
+void seq_bases(int B, const int32_t* lens, SeqBases* sb) {
+  sb->B = B;
+  sb->base[0] = 0;
+  for (int b = 0; b < B; ++b) {
+    sb->lens[b] = lens[b];
+    sb->base[b + 1] = sb->base[b] + ceil_div(lens[b], kRT) * kRT;
+  }
+}
+
+struct PrefillWs {
+  size_t o_xhat, o_kh, o_vt, bytes;
+};
+
+PrefillWs prefill_layout(const Layer& L, int total) {
+  PrefillWs w;
+  size_t o = 0;
+  w.o_xhat = o;
+  o = align256(o + (size_t)total * L.n_lat * 4);
+  w.o_kh = o;
+  o = align256(o + (size_t)total * L.H_kv * L.d_h * 2);
+  w.o_vt = o;
+  o = align256(o + (size_t)total * L.H_kv * L.d_h * 2);
+  w.bytes = o;
+  return w;
+}
+
+// launch with dynamic LDS, timed like launch_k
+template <typename A>
+hipError_t launch_lds(const ProfScope& ps, void (*kernel)(A), dim3 grid, dim3 block, size_t lds, hipStream_t s, A arg) {
+  void* argv[] = {(void*)&arg};
+  if (ps.start() && ps.stop())
+    return hipExtLaunchKernel((const void*)kernel, grid, block, argv, lds, s, ps.start(), ps.stop(), 0);
+  return hipLaunchKernel((const void*)kernel, grid, block, argv, lds, s);
+}
+
+template <int NT>
+hipError_t launch_recon_flash(const Layer& L, const ReconArgs& ra, const FlashArgs& fa, int B, int n_q, hipStream_t s) {
+  const int total = ra.total;
+  const size_t lds = (size_t)L.d_h * ra.rpad * 2;
+  {
+    ProfScope ps("prefill_recon");
+    const dim3 grid(ceil_div(total, 128), L.H_kv, 2);
+    const hipError_t e = (L.r_v & 7) == 0 ? launch_lds(ps, k_recon<NT, true>, grid, dim3(256), lds, s, ra)
+                                          : launch_lds(ps, k_recon<NT, false>, grid, dim3(256), lds, s, ra);
+    if (e != hipSuccess) return e;
+  }
+  ProfScope ps("prefill_attend");
+  const dim3 grid(ceil_div(n_q, 128), L.H_q, B);
+  return launch_k(ps, k_flash<NT, STARKV_BF16>, grid, dim3(256), s, fa);
+}
+
+}  // namespace
+
+size_t prefill_workspace_bytes(const Layer& L, int B, const int32_t* lens) {
+  size_t total = 0;
+  for (int b = 0; b < B; ++b) total += (size_t)ceil_div(lens[b], kRT) * kRT;
+  return prefill_layout(L, (int)total).bytes;
+}
+
+hipError_t launch_prefill(const Layer& L, const starkv_cache& c, const void* q, int B, int n_q, const int32_t* lens,
+                          void* out, void* ws, hipStream_t s) {
+  SeqBases sb;
+  seq_bases(B, lens, &sb);
+  const int total = sb.base[B];
+  const PrefillWs w = prefill_layout(L, total);
+  uint8_t* base = (uint8_t*)ws;
+  float* xhat = (float*)(base + w.o_xhat);
+  _Float16* kh = (_Float16*)(base + w.o_kh);
+  _Float16* vt = (_Float16*)(base + w.o_vt);
+  // 1. dequantised latent
+  DeqArgs da;
+  da.k_rows = (const uint8_t*)c.k_rows;
+  da.v_tiles = (const uint8_t*)c.v_tiles;
+  da.scales = L.scales;
+  da.src = L.d_src;
+  da.heads = L.heads();
+  da.xhat = xhat;
+  da.n_lat = L.n_lat;
+  da.n_key = L.n_key;
+  da.H_kv = L.H_kv;
+  da.K8 = L.K8;
+  da.V8 = L.V8;
+  da.n8v = L.n8v;
+  da.k_row_bytes = L.k_row_bytes;
+  da.v_rows = L.v_rows;
+  da.T_max = c.T_max;
+  da.sb = sb;
+  hipError_t e;
+  {
+    ProfScope ps("prefill_dequant");
+    const dim3 grid(total / kRT);
+    if (L.latent == STARKV_LATENT_MIX84) e = launch_k(ps, k_deq_latent<STARKV_LATENT_MIX84>, grid, dim3(256), s, da);
+    else if (L.latent == STARKV_LATENT_BF16) e = launch_k(ps, k_deq_latent<STARKV_LATENT_BF16>, grid, dim3(256), s, da);
+    else e = launch_k(ps, k_deq_latent<STARKV_LATENT_F32>, grid, dim3(256), s, da);
+    if (e != hipSuccess) return e;
+  }
+  // 2 + 3. reconstruction, attention
+  int rmax = 1;
+  for (int g = 0; g < L.H_kv; ++g) rmax = std::max(rmax, L.rk[g]);
+  ReconArgs ra;
+  ra.xhat = xhat;
+  ra.B_k = (const uint16_t*)L.B_k;
+  ra.B_vt = (const uint16_t*)L.B_vt;
+  ra.koff = L.d_koff;
+  ra.kh = kh;
+  ra.vt = vt;
+  ra.n_lat = L.n_lat;
+  ra.n_key = L.n_key;
+  ra.r_v = L.r_v;
+  ra.H_kv = L.H_kv;
+  ra.d_h = L.d_h;
+  ra.total = total;
+  ra.rpad = ceil_div(rmax, 16) * 16;
+  ra.rope_theta = L.rope_theta;
+  ra.rotary_dim = L.rotary_dim;
+  ra.sb = sb;
+  FlashArgs fa;
+  fa.q = q;
+  fa.out = out;
+  fa.kh = kh;
+  fa.vt = vt;
+  fa.n_q = n_q;
+  fa.H_q = L.H_q;
+  fa.H_kv = L.H_kv;
+  fa.G = L.G;
+  fa.d_h = L.d_h;
+  fa.total = total;
+  fa.qscale = (float)(1.4426950408889634 / sqrt((double)L.d_h));
+  fa.rope_theta = L.rope_theta;
+  fa.rotary_dim = L.rotary_dim;
+  fa.sb = sb;
+  switch (L.d_h / 32) {
+    case 1: e = launch_recon_flash<1>(L, ra, fa, B, n_q, s); break;
+    case 2: e = launch_recon_flash<2>(L, ra, fa, B, n_q, s); break;
+    case 3: e = launch_recon_flash<3>(L, ra, fa, B, n_q, s); break;
+    case 4: e = launch_recon_flash<4>(L, ra, fa, B, n_q, s); break;
+    case 5: e = launch_recon_flash<5>(L, ra, fa, B, n_q, s); break;
+    case 6: e = launch_recon_flash<6>(L, ra, fa, B, n_q, s); break;
+    case 7: e = launch_recon_flash<7>(L, ra, fa, B, n_q, s); break;
+    default: e = launch_recon_flash<8>(L, ra, fa, B, n_q, s); break;
+  }
+  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+}  // namespace skv

@@ -52,6 +52,9 @@ struct Layer {
   // rotated factors
   int had = 0;
   int qmax_hi = 127, qmax_lo = 7;  // code limits of the int8 and int4 regions
+  // rotary position embedding of the reconstructed keys and of the queries (0: none)
+  float rope_theta = 0.f;
+  int rotary_dim = 0;
   int k_row_bytes = 0, v_rows = 0, v_tile_bytes = 0;
   int key_slots = 0, val_slots = 0;  // columns of the append GEMM
   int key_kt = 0;           // K-positions per key-score K-tile (64 for int8 MFMA, 32 otherwise)
@@ -181,5 +184,11 @@ hipError_t launch_append(const Layer& L, const starkv_cache& c, const void* X_ne
 
 hipError_t launch_reconstruct(const Layer& L, const starkv_cache& c, int b, int t0, int t1, void* K_out,
                               void* V_out, hipStream_t s);
+
+// Attention over reconstructed keys and values (query chunks of any length; rotary layers):
+// workspace bytes for these lengths, and the launch (q, out: [B][n_q][H_q][d_h], bf16 layers).
+size_t prefill_workspace_bytes(const Layer& L, int B, const int32_t* lens);
+hipError_t launch_prefill(const Layer& L, const starkv_cache& c, const void* q, int B, int n_q, const int32_t* lens,
+                          void* out, void* ws, hipStream_t s);
 
 }  // namespace skv

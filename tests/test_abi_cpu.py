@@ -221,3 +221,41 @@ def test_noalloc_scratch_size_matches_header():
     src = open(HEADER).read()
     m = re.search(r"#define STARKV_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", src)
     assert m and int(m.group(1)) << int(m.group(2)) == S.NOALLOC_SCRATCH_BYTES
+
+
+def test_rope_setup_and_prefill_workspace():
+    """Rotary setup checks, and the prefill workspace: the dequantised latent (fp32) plus K^ and
+    V^ (f16) of every sequence padded to 32 tokens; a rotary layer's decode workspace is that."""
+    w, layer, _ = _layer(2)
+    with pytest.raises(S.StarKVError) as ei:
+        layer.set_rope(10000.0, w.d_h + 2)
+    assert ei.value.status == -1
+    with pytest.raises(S.StarKVError) as ei:
+        layer.set_rope(-1.0)
+    assert ei.value.status == -1
+    with pytest.raises(S.StarKVError) as ei:
+        layer.set_rope(10000.0, 64)  # partial rotation
+    assert ei.value.status == -4
+    lens = [100, 33]
+    tot = 128 + 64
+    n_lat, H_kv, d_h = layer.info["n_lat"], w.H_kv, w.d_h
+    al = lambda x: -(-x // 256) * 256  # noqa: E731
+    exp = al(tot * n_lat * 4) + 2 * al(tot * H_kv * d_h * 2)
+    assert layer.prefill_workspace_bytes(2, 7, lens) == exp
+    dec = layer.workspace_bytes(2, 1, lens)
+    layer.set_rope(10000.0)
+    assert layer.workspace_bytes(2, 1, lens) == exp != dec
+    layer.set_rope(10000.0, 0)
+    assert layer.workspace_bytes(2, 1, lens) == dec
+    with pytest.raises(S.StarKVError) as ei:
+        layer.prefill_workspace_bytes(2, 101, lens)  # a chunk longer than a sequence
+    assert ei.value.status == -1
+    layer.close()
+    w0, l0, _ = _layer(0)
+    with pytest.raises(S.StarKVError) as ei:
+        l0.set_rope(10000.0)
+    assert ei.value.status == -4  # fp32 layers keep the latent-space path only
+    with pytest.raises(S.StarKVError) as ei:
+        l0.prefill_workspace_bytes(1, 1, [10])
+    assert ei.value.status == -4
+    l0.close()
