@@ -25,6 +25,7 @@ from __future__ import annotations
 
 import argparse
 import csv
+import dataclasses
 import glob
 import hashlib
 import json
@@ -304,6 +305,8 @@ def measure(w, args, dev, with_cpu: bool, steps: int, warmup: int) -> dict:
         L.build_factors(*U)
         if Xcal is not None:
             L.calibrate(to_dev_bf16(Xcal, dev) if w.dtype == "bf16" else torch.from_numpy(Xcal).to(dev))
+        if args.rope:
+            L.set_rope(args.rope)
         return L
 
     probe = new_layer()
@@ -415,9 +418,17 @@ def measure(w, args, dev, with_cpu: bool, steps: int, warmup: int) -> dict:
         log(f"[kernel] {k:14s} {us:9.2f} us/launch ({prof[k][0]} launches)")
 
     ab = algorithmic_bytes(w, probe.ranks, probe.r_v, lens, n_q, hidden=args.hidden_query)
-    dom = max((k for k in kern_us if k.startswith("decode_")), key=lambda k: kern_us[k])
-    achieved = ab[dom] / (kern_us[dom] * 1e-6) / 1e9
-    traffic = None if args.hidden_query else traffic_for(dom, w.name)  # counters cover the q path only
+    if args.rope:
+        # rotary layers: reconstructed keys and values; the dominant kernel against the MFMA peak
+        fl = prefill_flops(w, probe.ranks, probe.r_v, lens, n_q)
+        dom = max((k for k in kern_us if k in fl), key=lambda k: kern_us[k])
+        ab.update(fl)
+        achieved = fl[dom] / (kern_us[dom] * 1e-6) / 1e12
+        traffic = None
+    else:
+        dom = max((k for k in kern_us if k.startswith("decode_")), key=lambda k: kern_us[k])
+        achieved = ab[dom] / (kern_us[dom] * 1e-6) / 1e9
+        traffic = None if args.hidden_query else traffic_for(dom, w.name)  # counters cover the q path only
     dec_us = sum(us for k, us in kern_us.items() if k.startswith("decode_"))
     res = {
         "value": w.B * n_q / (ms_step * 1e-3),
@@ -426,18 +437,22 @@ def measure(w, args, dev, with_cpu: bool, steps: int, warmup: int) -> dict:
                    "context_tokens": int(lens.sum()), "queries_per_seq": n_q, "H_q": w.H_q, "H_kv": w.H_kv,
                    "d_h": w.d_h, "hidden": w.d, "key_rank_sum": int(np.sum(probe.ranks)), "value_rank": probe.r_v,
                    "latent": w.latent, "layers_rotated": n_layers,
-                   "query": "hidden states, absorbed W_q B_g^T" if args.hidden_query else "q"},
+                   "query": "hidden states, absorbed W_q B_g^T" if args.hidden_query else "q",
+                   "rope_theta": args.rope or None},
         "dtype": {"f32": "f32", "bf16": "bf16", "mix84": "int8/int4 codes, f16 MFMA, fp32 accumulate",
                   "had43": "4-bit/3-bit codes in int8/int4 bytes, f16 MFMA, fp32 accumulate"}[w.latent],
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-                     "alg_bytes_per_launch": ab[dom], "us_per_launch": kern_us[dom]},
+        "roofline": ({"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": 2500.0, "unit": "TFLOP/s",
+                      "frac": achieved / 2500.0, "traffic": None, "alg_flops_per_launch": ab[dom],
+                      "us_per_launch": kern_us[dom]} if args.rope else
+                     {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                      "alg_bytes_per_launch": ab[dom], "us_per_launch": kern_us[dom]}),
         "ms_per_step_eager": ms_step_eager,
         "host_issue_us_per_step": host_us,
         "step_hbm_gbps": ab["step"] / (ms_step * 1e-3) / 1e9,
         "step_frac": ab["step"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "decode_kernels_us": dec_us,
-        "decode_hbm_gbps": ab["decode"] / (dec_us * 1e-6) / 1e9,
+        "decode_hbm_gbps": ab["decode"] / (dec_us * 1e-6) / 1e9 if dec_us > 0 else None,
         "kv_tokens_per_s": float(lens.sum()) / (ms_step * 1e-3),
         "kernel_us": kern_us,
         "alg_bytes": ab,
@@ -454,6 +469,103 @@ def measure(w, args, dev, with_cpu: bool, steps: int, warmup: int) -> dict:
     return res
 
 
+def prefill_flops(w, ranks, r_v, lens, n_q):
+    """Algorithmic flops of attention over reconstructed keys and values: rebuilding K^ (each
+    head's r_g channels) and V^ (r_v channels per KV head) for every cached token, then causal
+    attention of the chunk (query j of n_q sees lens - n_q + j + 1 tokens; QK^T and PV)."""
+    recon = sum(2.0 * int(T) * w.d_h * (float(np.sum(ranks)) + w.H_kv * r_v) for T in lens)
+    attend = 0.0
+    for T in lens:
+        seen = float(n_q * (int(T) - n_q) + n_q * (n_q + 1) / 2)
+        attend += 4.0 * w.H_q * w.d_h * seen
+    return {"prefill_recon": recon, "prefill_attend": attend}
+
+
+def measure_prefill(w, args, dev, n_q: int, steps: int, warmup: int) -> dict:
+    """A query chunk of n_q per sequence (the workload's batch and context) attending over keys and
+    values reconstructed from its latent cache: starkv_prefill_attention, timed like the decode
+    step (graph of `steps` calls), with the MFMA roofline of the dominant kernel."""
+    import torch
+    import rank_kv_cache_starkv_amd as S
+    from rank_kv_cache_starkv_amd import inputs as I
+
+    lens = I.context_lengths(w) + w.n_append
+    if not w.ragged:
+        lens = np.full(w.B, w.T, np.int32)
+    lens = lens.astype(np.int32)
+    T_max = int(-(-int(lens.max()) // 32) * 32)
+    tdt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    lf = I.layer_factors(w, 0)
+    U = [torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev) for a in (lf.U_k, lf.V_k, lf.U_v, lf.V_v)]
+    L = S.Layer(w.H_q, w.H_kv, w.d_h, w.d, w.dtype, w.latent, lf.s_k, lf.tau_k, lf.s_v, lf.tau_v)
+    L.build_factors(*U)
+    if w.latent in QUANTIZED:
+        L.calibrate(to_dev_bf16(I.as_dtype(I.x_calibration(w), w.dtype), dev))
+    if args.rope:
+        L.set_rope(args.rope)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(2606_08382)
+    c = L.new_cache(w.B, T_max)
+    for b in range(w.B):
+        for s0 in range(0, int(lens[b]), 4096):
+            s1 = min(int(lens[b]), s0 + 4096)
+            X = torch.randn((s1 - s0, w.d), generator=gen, device=dev, dtype=torch.float32).to(tdt)
+            L.append(c.seq(b), X[None].contiguous(), [s0])
+    wq = dataclasses.replace(w, n_q=n_q)
+    q = to_dev_bf16(I.as_dtype(I.queries(wq), w.dtype), dev)
+    ws = torch.empty((L.prefill_workspace_bytes(w.B, n_q, lens),), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    log(f"[prefill] {w.name}: B={w.B} n_q={n_q} lens {int(lens.min())}..{int(lens.max())}, "
+        f"workspace {ws.numel() / 2**20:.0f} MiB")
+    for _ in range(warmup):
+        L.prefill(c, q, lens, out=out, ws=ws)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        L.prefill(c, q, lens, out=out, ws=ws)
+        side.synchronize()
+        with torch.cuda.graph(graph, stream=side):
+            for _ in range(steps):
+                L.prefill(c, q, lens, out=out, ws=ws)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    graph.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    log(f"[time] graph: {steps} calls, {ms * 1000:.1f} us/call")
+    S.profile_enable(True)
+    S.profile_read(reset=True)
+    for _ in range(steps):
+        L.prefill(c, q, lens, out=out, ws=ws)
+    torch.cuda.synchronize()
+    prof = S.profile_read(reset=True)
+    S.profile_enable(False)
+    kern_us = {k: 1000.0 * t / n for k, (n, t) in prof.items()}
+    for k, us in sorted(kern_us.items()):
+        log(f"[kernel] {k:14s} {us:9.2f} us/launch ({prof[k][0]} launches)")
+    fl = prefill_flops(w, L.ranks, L.r_v, lens, n_q)
+    dom = max((k for k in kern_us if k in fl), key=lambda k: kern_us[k])
+    tflops = fl[dom] / (kern_us[dom] * 1e-6) / 1e12
+    return {
+        "metric": "attention over reconstructed keys and values: queries/s (query chunk per sequence)",
+        "value": w.B * n_q / (ms * 1e-3), "unit": "queries/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16 MFMA (reconstructed K, V, P), bf16 reconstruction, fp32 accumulate", "data": "synthetic",
+        "config": {"workload": f"{w.name}-chunk{n_q}" + (f"-rope{args.rope:g}" if args.rope else ""), "batch": w.B,
+                   "context_tokens": int(lens.sum()), "queries_per_seq": n_q, "latent": w.latent},
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": tflops, "peak": 2500.0, "unit": "TFLOP/s",
+                     "frac": tflops / 2500.0, "traffic": None, "alg_flops_per_launch": fl[dom],
+                     "us_per_launch": kern_us[dom]},
+        "kernel_us": kern_us, "tokens_per_s_reconstructed": float(lens.sum()) / (ms * 1e-3),
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -468,6 +580,11 @@ def main() -> int:
     ap.add_argument("--hidden-query", action="store_true",
                     help="queries from hidden states through the absorbed factors W_q B_g^T (step = append, "
                          "then starkv_decode_attention_hidden); no CPU baseline")
+    ap.add_argument("--prefill", type=int, default=0, metavar="N",
+                    help="time a chunk of N queries per sequence attending over reconstructed keys and values "
+                         "(starkv_prefill_attention) instead of the decode step")
+    ap.add_argument("--rope", type=float, default=0.0, metavar="THETA",
+                    help="rotary layers (base THETA): decode and prefill attend over reconstructed keys")
     ap.add_argument("--copy-probe", action="store_true", help=f"copy {COPY_PROBE_MIB} MiB device to device")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"))
     args = ap.parse_args()
@@ -488,7 +605,10 @@ def main() -> int:
     dev = "cuda:0"
     torch.cuda.set_device(0)
     w = I.WORKLOADS[args.workload]
-    r = measure(w, args, dev, with_cpu=not args.no_cpu, steps=args.steps, warmup=args.warmup)
+    if args.prefill:
+        print(json.dumps(measure_prefill(w, args, dev, args.prefill, args.steps, args.warmup)))
+        return 0
+    r = measure(w, args, dev, with_cpu=not args.no_cpu and not args.rope, steps=args.steps, warmup=args.warmup)
     result = {
         "metric": METRIC,
         "value": r["value"],
@@ -511,7 +631,7 @@ def main() -> int:
     result.update({k: r[k] for k in ("ms_per_step_eager", "host_issue_us_per_step", "step_hbm_gbps", "step_frac",
                                      "decode_kernels_us", "decode_hbm_gbps", "kv_tokens_per_s", "kernel_us",
                                      "alg_bytes")})
-    if not args.no_sub and args.workload == 4 and not args.hidden_query:
+    if not args.no_sub and args.workload == 4 and not args.hidden_query and not args.rope:
         # the other workloads of the same metric, measured in the same run (no CPU baseline)
         subs = {}
         for wid in (1, 2, 3):
