@@ -418,8 +418,11 @@ def measure(w, args, dev, with_cpu: bool, steps: int, warmup: int) -> dict:
         log(f"[kernel] {k:14s} {us:9.2f} us/launch ({prof[k][0]} launches)")
 
     ab = algorithmic_bytes(w, probe.ranks, probe.r_v, lens, n_q, hidden=args.hidden_query)
-    if args.rope:
-        # rotary layers: reconstructed keys and values; the dominant kernel against the MFMA peak
+    recon = bool(args.rope) and not any(k.startswith("decode_") for k in kern_us)
+    if recon:
+        # rotary layers past 32 query rows per KV head: reconstructed keys and values; the
+        # dominant kernel against the MFMA peak (up to 32 rows, the latent-space decode rebuilds
+        # key tiles in its score kernel, which reads the same latent as the plain one: HBM roofline)
         fl = prefill_flops(w, probe.ranks, probe.r_v, lens, n_q)
         dom = max((k for k in kern_us if k in fl), key=lambda k: kern_us[k])
         ab.update(fl)
@@ -428,7 +431,8 @@ def measure(w, args, dev, with_cpu: bool, steps: int, warmup: int) -> dict:
     else:
         dom = max((k for k in kern_us if k.startswith("decode_")), key=lambda k: kern_us[k])
         achieved = ab[dom] / (kern_us[dom] * 1e-6) / 1e9
-        traffic = None if args.hidden_query else traffic_for(dom, w.name)  # counters cover the q path only
+        # counters cover the q path of unrotated layers only
+        traffic = None if args.hidden_query or args.rope else traffic_for(dom, w.name)
     dec_us = sum(us for k, us in kern_us.items() if k.startswith("decode_"))
     res = {
         "value": w.B * n_q / (ms_step * 1e-3),
@@ -443,7 +447,7 @@ def measure(w, args, dev, with_cpu: bool, steps: int, warmup: int) -> dict:
                   "had43": "4-bit/3-bit codes in int8/int4 bytes, f16 MFMA, fp32 accumulate"}[w.latent],
         "roofline": ({"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": 2500.0, "unit": "TFLOP/s",
                       "frac": achieved / 2500.0, "traffic": None, "alg_flops_per_launch": ab[dom],
-                      "us_per_launch": kern_us[dom]} if args.rope else
+                      "us_per_launch": kern_us[dom]} if recon else
                      {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                       "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                       "alg_bytes_per_launch": ab[dom], "us_per_launch": kern_us[dom]}),

@@ -367,8 +367,8 @@ int starkv_decode_workspace_bytes(const starkv_layer* l, int B, int n_q, const i
   if (B > STARKV_MAX_BATCH || l->L.H_q * n_q > STARKV_MAX_QROWS) return STARKV_EUNSUPPORTED;
   for (int b = 0; b < B; ++b)
     if (lens_host[b] < n_q) return STARKV_EINVAL;
-  if (l->L.rope_theta > 0.f) {
-    // rotary layers attend over reconstructed keys and values
+  if (l->L.rope_theta > 0.f && !skv::rope_latent_scores(l->L, n_q)) {
+    // rotary layers with more than 32 query rows per KV head attend over reconstructed K and V
     *bytes = skv::prefill_workspace_bytes(l->L, B, lens_host);
     return STARKV_OK;
   }
@@ -392,7 +392,7 @@ int starkv_decode_attention(const starkv_layer* l, const starkv_cache* c, const 
   st = check_bound(L, true);
   if (st != STARKV_OK) return st;
   if (((uintptr_t)ws & 255) != 0) return STARKV_EINVAL;
-  if (L.rope_theta > 0.f) {
+  if (L.rope_theta > 0.f && !skv::rope_latent_scores(L, n_q)) {
     if (ws_bytes < skv::prefill_workspace_bytes(L, B, lens_host)) return STARKV_EWORKSPACE;
     return hip_status(skv::launch_prefill(L, *c, q, B, n_q, lens_host, out, ws, stream));
   }
@@ -441,7 +441,7 @@ int starkv_decode_step(const starkv_layer* l, const starkv_cache* c, const void*
   if (((uintptr_t)ws & 255) != 0) return STARKV_EINVAL;
   int32_t lens_pre[STARKV_MAX_BATCH];
   for (int b = 0; b < B; ++b) lens_pre[b] = lens_host[b] - n_q;
-  if (L.rope_theta > 0.f) {
+  if (L.rope_theta > 0.f && !skv::rope_latent_scores(L, n_q)) {
     if (ws_bytes < skv::prefill_workspace_bytes(L, B, lens_host)) return STARKV_EWORKSPACE;
     const hipError_t e = skv::launch_append(L, *c, X_new, B, n_q, lens_pre, stream);
     if (e != hipSuccess) return STARKV_EHIP;
@@ -529,7 +529,7 @@ int starkv_decode_step_noalloc(const starkv_layer* l, const starkv_cache* c, con
   if (st != STARKV_OK) return st;
   int32_t lens_pre[STARKV_MAX_BATCH];
   for (int b = 0; b < B; ++b) lens_pre[b] = lens_host[b] - n_q;
-  if (L.rope_theta > 0.f) {
+  if (L.rope_theta > 0.f && !skv::rope_latent_scores(L, n_q)) {
     if (skv::prefill_workspace_bytes(L, B, lens_host) > kScratchBytes) return STARKV_EWORKSPACE;
     const hipError_t e = skv::launch_append(L, *c, X_new, B, n_q, lens_pre, stream);
     if (e != hipSuccess) return STARKV_EHIP;

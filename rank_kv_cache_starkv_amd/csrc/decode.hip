@@ -1225,6 +1225,411 @@ __global__ __launch_bounds__(256) void k_scores_mix(ScoreArgs a) {
   }
 }
 
+// ---- asynchronous loads straight into LDS
+// Lane l's 16 bytes at src land at LDS byte address lds + 16 l (lds wave-uniform; the builtin
+// puts it in M0).  The kernel waits with vm_wait<n>() (n = loads it may leave in flight) and a
+// barrier before any wave reads the data.
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(uintptr_t)lds, 16, 0, 0);
+}
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Key scores of a rotary layer (keys rotated by position after the key projection): the rotation
+// does not commute with B_g, so each key tile is rebuilt from the latent before the dot product
+// (STAR-KV summary page, Problem Statement: the reconstruction cost; Methodology section 2: the
+// head-wise key factors keep it per head, 2 r_g d_h flops per token and head).  Workgroup =
+// (sequence b, KV head g, block of 4 cpw 32-token chunks), four waves of cpw chunks each.
+// Staged in LDS once per workgroup: the MFMA A operand of the reconstruction (B_g^T in bf16 for
+// bf16 latents; B_g^T with the channel scales folded in, in f16, for int8/int4 latents, whose
+// codes are then exact f16), the head's query rows rotated to their positions (high and low f16
+// parts, in the register order of the score MFMA's B operand) and the cos/sin of r w_e, r < 32.
+// Each wave streams the head's latent bytes of its chunks into its own two LDS stages (4-byte
+// LDS DMA, the next chunk in flight while the current one computes) and builds the cos/sin of
+// 32 c w_e for each chunk; the rotation of token 32 c + r composes the two (angle sum).  Per chunk:
+//   K^T tile  = A x^_g^T              (32x32x16 MFMA; lane = token, 16 of the d_h dims per tile)
+//   rotation  of the pairs (e, e + d_h / 2), which sit in the same lane (tiles mt and mt + NT/2)
+//   S^T       = K^ Q_rot^T            (32x32x16 f16 MFMA; the K^T registers are the A operand as
+//                                      they are; lane = query row, 16 tokens)
+// then the chunk statistics and p~ = 2^(s - m) in the format of the other score kernels, for the
+// value, merge and up-projection kernels of the latent-space path.  At most 32 query rows per KV
+// head (G n_q); d_h = 64 or 128.
+struct RopeScoreArgs {
+  const uint8_t* k_rows;
+  const void* q;           // [B][n_q][H_q][d_h] bf16
+  const uint16_t* B_k;     // [n_key][d_h] bf16
+  const uint16_t* scales;  // int8/int4: [n_lat] f16
+  HeadTables heads;
+  void* p;
+  float* cm;
+  float* cl;
+  DecodeGeom g;
+  float rope_theta;
+  int rpad;                // staged B_g^T: rows of rpad + 8 halves (rpad = largest key rank rounded to 16)
+  int cpw;                 // chunks per wave
+  int npair_max;           // dword pairs of a latent stage (both segments), largest over the heads
+  SeqTable seq;
+};
+
+// sin and cos of a rotation angle formed in fp64 (positions reach 2^15 and more): reduced to
+// [-pi, pi] in fp64, then sincosf
+__device__ __forceinline__ void rope_sincos(double ang, float* sn, float* cs) {
+  constexpr double kTwoPi = 6.283185307179586476925287;
+  const double red = ang - kTwoPi * rint(ang / kTwoPi);
+  sincosf((float)red, sn, cs);
+}
+
+// The byte segments of KV head g in a key row that a latent stage holds, as dwords: bf16, the
+// head's channels; int8/int4, its int8 codes (nd8 dwords) then its int4 codes (nd4).  A stage
+// keeps each segment dword-pair-major: pair p is 256 bytes, lane l of its DMA holding dword
+// 2 p + l / 32 of token l % 32 -- a load of one dword of 32 tokens touches 32 banks.
+struct RopeSeg {
+  int a8, nd8, a4, nd4;  // byte offsets of the segments' first dwords in the row; dword counts
+  int np8, np4;          // dword pairs of each segment
+  __host__ __device__ RopeSeg(bool mix, int c0, int rg, int o8, int n8, int o4, int K8) {
+    if (mix) {
+      a8 = o8 & ~3;
+      nd8 = (o8 + n8 - a8 + 3) >> 2;
+      const int b4lo = K8 + (o4 >> 1), b4hi = K8 + ((o4 + (rg - n8) + 1) >> 1);
+      a4 = b4lo & ~3;
+      nd4 = (b4hi - a4 + 3) >> 2;
+    } else {
+      a8 = (2 * c0) & ~3;
+      nd8 = (2 * (c0 + rg) - a8 + 3) >> 2;
+      a4 = 0;
+      nd4 = 0;
+    }
+    np8 = (nd8 + 1) >> 1;
+    np4 = (nd4 + 1) >> 1;
+  }
+};
+
+// LDS layout of k_scores_rope (bytes), shared by the kernel and its launch
+struct RopeLds {
+  int tab_r, q_hi, q_lo, bkt, wave0, wstride, stage, total;
+  int qst;  // bytes per staged query row (one part)
+  __host__ __device__ RopeLds(int d_h, int rpad, int rows, int npair_max) {
+    const int np = d_h / 2, ks = d_h / 16;
+    qst = ks * 32 + 16;
+    tab_r = 0;                                   // [32][np + 1] float2
+    q_hi = tab_r + 32 * (np + 1) * 8;            // [rows][qst]
+    q_lo = q_hi + rows * qst;
+    bkt = q_lo + rows * qst;                     // [d_h][rpad + 8] halves
+    wave0 = bkt + d_h * (rpad + 8) * 2;          // per wave: tab_c [np] float2, two stages
+    stage = (npair_max + 1) * 256;  // one pair of slack: windows that run past the segments
+    wstride = np * 8 + 2 * stage;
+    total = wave0 + 4 * wstride;
+  }
+};
+
+template <int LAT, int NT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_scores_rope(RopeScoreArgs a) {
+  constexpr int DH = 32 * NT, NP = DH / 2, KS = 2 * NT;
+  constexpr bool MIX = LAT == STARKV_LATENT_MIX84;
+  extern __shared__ __align__(16) uint8_t lds[];
+  const DecodeGeom& g = a.g;
+  const int b = blockIdx.z, gk = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int r = lane & 31, q = lane >> 5;
+  const int nch = seq_nch(a.seq, b), len = seq_len(a.seq, b);
+  const int cbase = blockIdx.x * 4 * a.cpw;
+  if (cbase >= nch) return;  // whole workgroup, before any barrier
+  const int rows = g.G * g.n_q;  // query rows of this KV head (at most 32)
+  const RopeLds L(DH, a.rpad, rows, a.npair_max);
+  const int rst = a.rpad + 8;
+  const int c0 = ld_uniform(a.heads.koff + gk);
+  const int rg = ld_uniform(a.heads.koff + gk + 1) - c0;
+  int n8 = 0, o8 = 0, o4 = 0;
+  if (MIX) {
+    n8 = ld_uniform(a.heads.n8 + gk);
+    o8 = ld_uniform(a.heads.off8 + gk);
+    o4 = ld_uniform(a.heads.off4 + gk);
+  }
+  const RopeSeg sg(MIX, c0, rg, o8, n8, o4, g.K8);
+  const int c_first = cbase + wave * a.cpw;
+  const int c_last = min(c_first + a.cpw, nch);  // this wave's chunks [c_first, c_last)
+  const uint32_t wbase = lds_addr(lds) + L.wave0 + wave * L.wstride;
+  float2* tab_c = (float2*)(lds + L.wave0 + wave * L.wstride);
+
+  // latent bytes of chunk c into stage st: buffer loads straight into LDS through a resource that
+  // ends at the sequence's last token, so tokens past it read as zero
+  const __amdgpu_buffer_rsrc_t krs =
+      buf_rsrc(a.k_rows + (size_t)b * g.T_max * g.k_row_bytes, (uint32_t)len * (uint32_t)g.k_row_bytes);
+  auto issue = [&](int c, int st) {
+    const uint32_t dst = wbase + NP * 8 + st * L.stage;
+    const uint32_t vo = (uint32_t)(c * kTC + (lane & 31)) * (uint32_t)g.k_row_bytes + 4 * (lane >> 5);
+    for (int pp = 0; pp < sg.np8; ++pp)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)(uintptr_t)(dst + 256 * pp),
+                                               4, (int)(vo + sg.a8 + 8 * pp), 0, 0, 0);
+    for (int pp = 0; pp < sg.np4; ++pp)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs,
+                                               (__attribute__((address_space(3))) void*)(uintptr_t)(dst + 256 * (sg.np8 + pp)),
+                                               4, (int)(vo + sg.a4 + 8 * pp), 0, 0, 0);
+  };
+  if (c_first < c_last) issue(c_first, 0);  // in flight during the set-up
+
+  const double lt = log2((double)a.rope_theta);
+  // inverse frequency of pair j: theta^(-2 j / d_h)
+  auto omega = [&](int j) { return exp2(-2.0 * (double)j / (double)DH * lt); };
+
+  // 1. the reconstruction's A operand: A[e][k] = B_g[k][e] (bf16), or B_g[k][e] s_k (f16); zero
+  //    past the rank.  16-byte loads of B_g rows, all issued before the first LDS write.
+  {
+    constexpr int EV = DH / 8;              // 16-byte vectors per B_g row
+    constexpr int MAXIT = 128 * EV / 256;   // rpad <= 128
+    const int nv = a.rpad * EV;
+    // buffer loads (zero past the head's rows): no branch, all in flight together
+    const __amdgpu_buffer_rsrc_t brs = buf_rsrc(a.B_k + (size_t)c0 * DH, (uint32_t)(rg * DH * 2));
+    u32x4 v[MAXIT];
+    float sc[MAXIT];
+#pragma unroll
+    for (int it = 0; it < MAXIT; ++it) {
+      const int i = tid + 256 * it;
+      const int k = i % a.rpad, e0 = (i / a.rpad) * 8;
+      const bool on = i < nv && k < rg;
+      v[it] = bld16(brs, on ? (uint32_t)((k * DH + e0) * 2) : kOOB);
+      if (MIX) sc[it] = f16_to_f32(a.scales[c0 + max(min(k, rg - 1), 0)]);
+    }
+    uint16_t* bkt = (uint16_t*)(lds + L.bkt);
+#pragma unroll
+    for (int it = 0; it < MAXIT; ++it) {
+      const int i = tid + 256 * it;
+      if (i < nv) {
+        const int k = i % a.rpad, e0 = (i / a.rpad) * 8;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const uint16_t hb = (uint16_t)(v[it][u >> 1] >> (16 * (u & 1)));
+          uint16_t o = hb;
+          if (MIX) o = f32_to_f16(bf16_to_f32(hb) * sc[it]);
+          bkt[(e0 + u) * rst + k] = o;
+        }
+      }
+    }
+  }
+  // 2. cos/sin of r w_j
+  {
+    const double w = omega(tid % NP);
+#pragma unroll
+    for (int it = 0; it < 32 * NP / 256; ++it) {
+      const int i = tid + 256 * it;
+      const int rr = i / NP, j = i % NP;
+      float sn, cs;
+      rope_sincos((double)rr * w, &sn, &cs);
+      ((float2*)(lds + L.tab_r))[rr * (NP + 1) + j] = float2{cs, sn};
+    }
+  }
+  // 3. query rows rotated to their positions: dim e of row n goes to K-step 2 (e / 32) + (v / 8),
+  //    half hq, element v % 8, where e % 32 = d32_row(v, hq) -- the order in which the K^T
+  //    registers feed the score MFMA
+  {
+    constexpr int MAXIT = 32 * NP / 256;
+    const int j = tid % NP;
+    const double w = omega(j);
+    float x0[MAXIT], x1[MAXIT];
+#pragma unroll
+    for (int it = 0; it < MAXIT; ++it) {
+      const int n = min((tid + 256 * it) / NP, rows - 1);  // rows past the head's repeat its last
+      const int hq = gk * g.G + n / g.n_q, jq = n % g.n_q;
+      const uint16_t* qr = (const uint16_t*)a.q + (((size_t)b * g.n_q + jq) * g.H_q + hq) * DH;
+      x0[it] = bf16_to_f32(qr[j]);
+      x1[it] = bf16_to_f32(qr[j + NP]);
+    }
+#pragma unroll
+    for (int it = 0; it < MAXIT; ++it) {
+      const int n = (tid + 256 * it) / NP;
+      if (n < rows) {
+        const int pos = len - g.n_q + n % g.n_q;
+        float sn, cs;
+        rope_sincos((double)pos * w, &sn, &cs);
+        const float y0 = x0[it] * cs - x1[it] * sn, y1 = x0[it] * sn + x1[it] * cs;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int e = j + h * NP;
+          const float y = h ? y1 : y0;
+          const int e32 = e & 31;
+          const int vv = 4 * (e32 >> 3) + (e32 & 3), half = (e32 >> 2) & 1;
+          const int ks = 2 * (e >> 5) + (vv >> 3);
+          const int off = n * L.qst + (ks * 2 + half) * 16 + (vv & 7) * 2;
+          const _Float16 yh = (_Float16)y;
+          *(_Float16*)(lds + L.q_hi + off) = yh;
+          *(_Float16*)(lds + L.q_lo + off) = (_Float16)(y - (float)yh);
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // cos/sin of the chunk base angle 32 c w_j for pair j = lane % NP, advanced chunk by chunk by
+  // the angle sum with 32 w_j (a few roundings of 2^-24 over at most eight steps)
+  float ccs, csn, c32, s32;
+  {
+    const double wl = omega(lane % NP);
+    rope_sincos((double)(c_first * kTC) * wl, &csn, &ccs);
+    rope_sincos((double)kTC * wl, &s32, &c32);
+  }
+  const int lim = r < rows ? len - g.n_q + r % g.n_q : -1;  // last token row r sees
+  const int ig = gk * rows + r;                             // the row among the sequence's rows
+  const int qrow = min(r, rows - 1) * L.qst;
+  const uint16_t* bkt = (const uint16_t*)(lds + L.bkt);
+  for (int c = c_first; c < c_last; ++c) {
+    const int st = (c - c_first) & 1;
+    vm_wait<0>();  // this wave's latent bytes of chunk c are in its stage
+    asm volatile("" ::: "memory");
+    if (lane < NP) tab_c[lane] = float2{ccs, csn};
+    {
+      const float nc = ccs * c32 - csn * s32, ns = csn * c32 + ccs * s32;
+      ccs = nc;
+      csn = ns;
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (c + 1 < c_last) issue(c + 1, st ^ 1);
+    // 1. K^T tile: lane (token 32 c + r) holds dims 32 mt + d32_row(v, q)
+    const uint8_t* seg8 = lds + L.wave0 + wave * L.wstride + NP * 8 + st * L.stage + 4 * r;
+    const uint8_t* seg4 = seg8 + 256 * sg.np8;
+    // dword dw of this lane's token in a segment (dw >= -1; -1 lands in the pair before)
+    auto ldw = [&](const uint8_t* sb, int dw) { return *(const uint32_t*)(sb + 256 * (dw >> 1) + 128 * (dw & 1)); };
+    const int dlim8 = 2 * sg.np8 - 1, dlim4 = 2 * sg.np4 - 1;  // last loaded dword of each segment
+    f32x16 kt[NT];
+#pragma unroll
+    for (int mt = 0; mt < NT; ++mt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) kt[mt][v] = 0.f;
+    for (int k0 = 0; k0 < rg; k0 += 16) {
+      const int kb = k0 + 8 * q;
+      const bool last = k0 + 16 > rg;  // the partial K-step: channels past the rank are masked
+      uint32_t w[4];
+      if (!MIX) {
+        // channels kb .. kb + 7: dwords kb / 2 .. kb / 2 + 4 of the segment (one more when c0 is odd)
+        const int d0 = kb / 2;
+        uint32_t d[5];
+#pragma unroll
+        for (int i = 0; i < 5; ++i) d[i] = ldw(seg8, last ? min(d0 + i, dlim8) : d0 + i);
+        const uint32_t sh = (uint32_t)(c0 & 1) * 16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = __builtin_amdgcn_alignbit(d[i + 1], d[i], sh);
+        if (last) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t mlo = kb + 2 * i < rg ? 0xFFFFu : 0u;
+            const uint32_t mhi = kb + 2 * i + 1 < rg ? 0xFFFF0000u : 0u;
+            w[i] &= mlo | mhi;
+          }
+        }
+      } else {
+        // int8 codes of channels kb .. kb + 7 (bytes o8 - a8 + kb ..), and int4 codes of the
+        // same channels (nibbles o4 + kb - n8 .. of the int4 segment); each channel takes one
+        int code[8];
+        {
+          // past the int8 codes the window is clamped (same alignment; its bytes go unused)
+          const int d0 = min(kb, n8 & ~7) / 4;
+          const uint32_t sh = (uint32_t)(o8 - sg.a8) * 8;
+          const uint32_t e0 = ldw(seg8, d0), e1 = ldw(seg8, min(d0 + 1, dlim8)), e2 = ldw(seg8, min(d0 + 2, dlim8));
+          const uint32_t lo = __builtin_amdgcn_alignbit(e1, e0, sh), hi = __builtin_amdgcn_alignbit(e2, e1, sh);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) code[i] = __builtin_amdgcn_sbfe((int)(i < 4 ? lo : hi), 8 * (i & 3), 8);
+        }
+        {
+          // nibble offset from the int4 segment's first byte (>= -7: the window may start in the
+          // dword before the segment when it begins with int8 channels)
+          int nb = (o4 + kb - n8) - 2 * (sg.a4 - g.K8);
+          if (nb < -7) nb &= 7;  // all eight channels are int8 ones: any window of the same phase
+          const int f = (4 * nb) >> 5;  // dword of the first nibble (arithmetic shift: -1 for nb < 0)
+          const uint32_t f0 = ldw(seg4, min(f, dlim4)), f1 = ldw(seg4, min(f + 1, dlim4));
+          const uint32_t w4 = __builtin_amdgcn_alignbit(f1, f0, (uint32_t)((4 * nb) & 31));
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            if (kb + i >= n8) code[i] = __builtin_amdgcn_sbfe((int)w4, 4 * i, 4);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int c_lo = (!last || kb + 2 * i < rg) ? code[2 * i] : 0;
+          const int c_hi = (!last || kb + 2 * i + 1 < rg) ? code[2 * i + 1] : 0;
+          const _Float16 h0 = (_Float16)(short)c_lo, h1 = (_Float16)(short)c_hi;
+          w[i] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+        }
+      }
+#pragma unroll
+      for (int mt = 0; mt < NT; ++mt) {
+        const u32x4 at = *(const u32x4*)(bkt + (mt * 32 + r) * rst + kb);
+        if (MIX)
+          kt[mt] = mfma32_f16(__builtin_bit_cast(f16x8, at), __builtin_bit_cast(f16x8, u32x4{w[0], w[1], w[2], w[3]}),
+                              kt[mt]);
+        else
+          kt[mt] = mfma32_bf16(as_bf16x8(at), as_bf16x8(u32x4{w[0], w[1], w[2], w[3]}), kt[mt]);
+      }
+    }
+    // 2. rotation of the key at position t = 32 c + r by the angle sum of the two tables
+    const float2* tr = (const float2*)(lds + L.tab_r) + r * (NP + 1);
+#pragma unroll
+    for (int mt = 0; mt < NT / 2; ++mt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int j = mt * 32 + d32_row(v, q);
+        const float2 tc = tab_c[j], tt = tr[j];
+        const float cs = tc.x * tt.x - tc.y * tt.y, sn = tc.y * tt.x + tc.x * tt.y;
+        const float x0 = kt[mt][v], x1 = kt[mt + NT / 2][v];
+        kt[mt][v] = x0 * cs - x1 * sn;
+        kt[mt + NT / 2][v] = x0 * sn + x1 * cs;
+      }
+    // 3. S^T: lane (query row n = r, half q) holds tokens 32 c + d32_row(v, q)
+    f32x16 s;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) s[v] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      f16x8 ak;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ak[i] = (_Float16)kt[ks >> 1][8 * (ks & 1) + i];
+      const int off = qrow + (ks * 2 + q) * 16;
+      s = mfma32_f16(ak, *(const f16x8*)(lds + L.q_hi + off), s);
+      s = mfma32_f16(ak, *(const f16x8*)(lds + L.q_lo + off), s);
+    }
+    // 4. mask, chunk statistics, p~
+    float m = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int tt = c * kTC + d32_row(v, q);
+      s[v] = tt <= lim ? s[v] * g.qscale : -INFINITY;
+      m = fmaxf(m, s[v]);
+    }
+    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    float l = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      s[v] = s[v] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s[v] - m);
+      l += s[v];
+    }
+    l += __shfl_xor(l, 32, 64);
+    if (r < rows) {
+      const size_t cgl = (size_t)seq_chunk0(a.seq, b) + c;
+      const size_t prow = (cgl * g.M_pad + ig) * kTC;
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4) {
+        const int tt = 8 * v4 + 4 * q;  // tokens tt .. tt + 3 of the chunk
+        uint32_t w0, w1;
+        if (MIX) {
+          w0 = (uint32_t)f32_to_f16(s[4 * v4]) | ((uint32_t)f32_to_f16(s[4 * v4 + 1]) << 16);
+          w1 = (uint32_t)f32_to_f16(s[4 * v4 + 2]) | ((uint32_t)f32_to_f16(s[4 * v4 + 3]) << 16);
+        } else {
+          w0 = (uint32_t)f32_to_bf16(s[4 * v4]) | ((uint32_t)f32_to_bf16(s[4 * v4 + 1]) << 16);
+          w1 = (uint32_t)f32_to_bf16(s[4 * v4 + 2]) | ((uint32_t)f32_to_bf16(s[4 * v4 + 3]) << 16);
+        }
+        st8((uint16_t*)a.p + prow + tt, u32x2{w0, w1});
+      }
+      if (q == 0) {
+        a.cm[cgl * g.M_pad + ig] = m;
+        a.cl[cgl * g.M_pad + ig] = l;
+      }
+    }
+  }
+}
+
 // ===========================================================================
 // values: z partial of one (sequence, split) for a slice of value blocks
 
@@ -1756,21 +2161,6 @@ __global__ __launch_bounds__(256) void k_values1(ValueArgs a) {
   }
 }
 
-// ---- asynchronous loads straight into LDS
-// Lane l's 16 bytes at src land at LDS byte address lds + 16 l (lds wave-uniform; the builtin
-// puts it in M0).  The kernel waits with vm_wait<n>() (n = loads it may leave in flight) and a
-// barrier before any wave reads the data.
-__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(uintptr_t)lds, 16, 0, 0);
-}
-template <int N>
-__device__ __forceinline__ void vm_wait() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
 
 // Many query rows per sequence (M_pad = 32 NMT > 32; bf16 or int8/int4 latents): workgroup =
 // (split of one sequence, group of 4 NTW value N-tiles of 32 channels); wave w owns N-tiles
@@ -2564,13 +2954,74 @@ static hipError_t launch_front(const Layer& L, const ProfScope& ps, dim3 grid, h
 }
 
 static hipError_t launch_decode_tail(const Layer& L, const DecodePlan& plan, const KtList& kts, const SeqTable& seq,
-                                     void* out, const void* k_rows, const void* v_tiles, hipStream_t s);
+                                     void* out, const void* k_rows, const void* v_tiles, hipStream_t s,
+                                     bool scores = true);
+
+template <int NT>
+static hipError_t launch_scores_rope(const Layer& L, const ProfScope& ps, dim3 grid, size_t lds, hipStream_t s,
+                                     const RopeScoreArgs& ra) {
+  void* argv[] = {(void*)&ra};
+  const void* k = L.latent == STARKV_LATENT_MIX84 ? (const void*)k_scores_rope<STARKV_LATENT_MIX84, NT>
+                                                  : (const void*)k_scores_rope<STARKV_LATENT_BF16, NT>;
+  if (ps.start() && ps.stop()) return hipExtLaunchKernel(k, grid, dim3(256), argv, lds, s, ps.start(), ps.stop(), 0);
+  return hipLaunchKernel(k, grid, dim3(256), argv, lds, s);
+}
+
+bool rope_latent_scores(const Layer& L, int n_q) {
+  return L.G * n_q <= 32 && (L.d_h == 64 || L.d_h == 128);
+}
+
+// Decode of a rotary layer: scores over rebuilt, rotated key tiles, then the latent-space value
+// path (values are not rotated).
+static hipError_t launch_decode_rope(const Layer& L, const DecodePlan& plan, const KtList& kts, const SeqTable& seq,
+                                     const void* q, void* out, const void* k_rows, const void* v_tiles,
+                                     hipStream_t s) {
+  const DecodeGeom& g = plan.g;
+  RopeScoreArgs ra;
+  ra.k_rows = (const uint8_t*)k_rows;
+  ra.q = q;
+  ra.B_k = (const uint16_t*)L.B_k;
+  ra.scales = L.scales;
+  ra.heads = L.heads();
+  ra.p = plan.ws.p;
+  ra.cm = plan.ws.cm;
+  ra.cl = plan.ws.cl;
+  ra.g = g;
+  ra.rope_theta = L.rope_theta;
+  int rmax = 1, npair_max = 1;
+  for (int gk = 0; gk < L.H_kv; ++gk) {
+    rmax = std::max(rmax, L.rk[gk]);
+    const RopeSeg sg(L.mix(), L.koff[gk], L.rk[gk], L.mix() ? L.off8[gk] : 0, L.mix() ? L.n8[gk] : 0,
+                     L.mix() ? L.off4[gk] : 0, L.K8);
+    npair_max = std::max(npair_max, sg.np8 + sg.np4);
+  }
+  ra.rpad = ceil_div(rmax, 16) * 16;
+  ra.npair_max = npair_max;
+  int max_nch = 1;
+  for (int b = 0; b < g.B; ++b) max_nch = std::max(max_nch, seq.chunk_off[b + 1] - seq.chunk_off[b]);
+  // chunks per wave: 8, fewer while that leaves under 1024 workgroups
+  int cpw = 8;
+  while (cpw > 1 && (long)g.B * g.H_kv * ceil_div(max_nch, 4 * cpw) < 1024) cpw /= 2;
+  ra.cpw = cpw;
+  ra.seq = seq;
+  const dim3 grid(ceil_div(max_nch, 4 * cpw), g.H_kv, g.B);
+  const size_t lds = RopeLds(g.d_h, ra.rpad, g.G * g.n_q, npair_max).total;
+  if (lds > 160 * 1024) return hipErrorInvalidValue;
+  hipError_t e;
+  {
+    ProfScope ps("decode_scores");
+    e = g.d_h == 64 ? launch_scores_rope<2>(L, ps, grid, lds, s, ra) : launch_scores_rope<4>(L, ps, grid, lds, s, ra);
+    if (e != hipSuccess) return e;
+  }
+  return launch_decode_tail(L, plan, kts, seq, out, k_rows, v_tiles, s, false);
+}
 
 hipError_t launch_decode(const Layer& L, const DecodePlan& plan, const KtList& kts, const SeqTable& seq,
                          const void* q, void* out, const void* k_rows, const void* v_tiles, hipStream_t s,
                          const float* wqk) {
   const DecodeGeom& g = plan.g;
   hipError_t e = hipSuccess;
+  if (L.rope_theta > 0.f) return launch_decode_rope(L, plan, kts, seq, q, out, k_rows, v_tiles, s);
   // 1. query fragments
   QprojArgs qa = qproj_args(L, plan, kts, q);
   qa.wqk = wqk;
@@ -2605,7 +3056,7 @@ hipError_t launch_step(const Layer& L, const starkv_cache& c, const DecodePlan& 
   const DecodeGeom& g = plan.g;
   const int M = g.B * g.n_q;
   const int sw = (M <= 8 && L.d % 64 == 0) ? 8 : ((M <= 16 && L.d % 32 == 0) ? 16 : 0);
-  if (sw == 0) {
+  if (sw == 0 || L.rope_theta > 0.f) {
     // many new rows: the tiled append, then the decode
     const hipError_t e = launch_append(L, c, X_new, g.B, g.n_q, lens_pre, s);
     if (e != hipSuccess) return e;
@@ -2628,11 +3079,12 @@ hipError_t launch_step(const Layer& L, const starkv_cache& c, const DecodePlan& 
 }
 
 static hipError_t launch_decode_tail(const Layer& L, const DecodePlan& plan, const KtList& kts, const SeqTable& seq,
-                                     void* out, const void* k_rows, const void* v_tiles, hipStream_t s) {
+                                     void* out, const void* k_rows, const void* v_tiles, hipStream_t s, bool scores) {
   const DecodeGeom& g = plan.g;
   const DecodeWs& w = plan.ws;
   hipError_t e = hipSuccess;
   // 2. scores
+  if (scores) {
   ScoreArgs sa;
   sa.k_rows = (const uint8_t*)k_rows;
   sa.qfrag = (const uint8_t*)w.qfrag;
@@ -2675,6 +3127,7 @@ static hipError_t launch_decode_tail(const Layer& L, const DecodePlan& plan, con
       else e = launch_k(ps, k_scores<STARKV_LATENT_F32>, dim3(n_wg), dim3(256), s, sa);
     }
     if (e != hipSuccess) return e;
+  }
   }
   // 3. values
   ValueArgs va;

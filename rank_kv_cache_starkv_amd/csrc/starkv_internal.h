@@ -154,6 +154,9 @@ int plan_decode(const Layer& L, int B, int n_q, const int32_t* lens, int T_max, 
 
 // q: [B][n_q][H_q][d_h] queries, or with wqk set [B][n_q][d] hidden states whose query
 // projection is absorbed into wqk
+// rotary layers: whether decode scores rebuilt key tiles in the latent-space path (else it attends
+// over fully reconstructed keys and values)
+bool rope_latent_scores(const Layer& L, int n_q);
 hipError_t launch_decode(const Layer& L, const DecodePlan& plan, const KtList& kts, const SeqTable& seq,
                          const void* q, void* out, const void* k_rows, const void* v_tiles, hipStream_t s,
                          const float* wqk = nullptr);

@@ -225,7 +225,8 @@ def test_noalloc_scratch_size_matches_header():
 
 def test_rope_setup_and_prefill_workspace():
     """Rotary setup checks, and the prefill workspace: the dequantised latent (fp32) plus K^ and
-    V^ (f16) of every sequence padded to 32 tokens; a rotary layer's decode workspace is that."""
+    V^ (f16) of every sequence padded to 32 tokens; a rotary layer's decode workspace is that past
+    32 query rows per KV head."""
     w, layer, _ = _layer(2)
     with pytest.raises(S.StarKVError) as ei:
         layer.set_rope(10000.0, w.d_h + 2)
@@ -244,13 +245,28 @@ def test_rope_setup_and_prefill_workspace():
     assert layer.prefill_workspace_bytes(2, 7, lens) == exp
     dec = layer.workspace_bytes(2, 1, lens)
     layer.set_rope(10000.0)
-    assert layer.workspace_bytes(2, 1, lens) == exp != dec
+    # up to 32 query rows per KV head: the latent-space decode (rebuilt key tiles), whose
+    # workspace does not change; past that, attention over reconstructed K and V
+    assert layer.workspace_bytes(2, 1, lens) == dec != exp
     layer.set_rope(10000.0, 0)
     assert layer.workspace_bytes(2, 1, lens) == dec
     with pytest.raises(S.StarKVError) as ei:
         layer.prefill_workspace_bytes(2, 101, lens)  # a chunk longer than a sequence
     assert ei.value.status == -1
     layer.close()
+    # eight query heads per KV head: 5 new tokens make 40 rows per KV head, past the 32 that the
+    # latent-space rotary decode takes, so that decode attends over reconstructed K and V
+    rng = np.random.default_rng(3)
+    H_q, H_kv, d_h = 16, 2, 64
+    s_k = -np.sort(-rng.uniform(0.1, 1.0, (H_kv, d_h)), axis=1)
+    s_v = -np.sort(-rng.uniform(0.1, 1.0, H_kv * d_h))
+    gl = S.Layer(H_q=H_q, H_kv=H_kv, d_h=d_h, d=H_q * d_h, dtype="bf16", latent="bf16", s_k=s_k,
+                 tau_k=np.full(H_kv, 0.5), s_v=s_v, tau_v=0.5)
+    dec4 = gl.workspace_bytes(2, 4, lens)  # 32 rows per KV head
+    gl.set_rope(10000.0)
+    assert gl.workspace_bytes(2, 4, lens) == dec4
+    assert gl.workspace_bytes(2, 5, lens) == gl.prefill_workspace_bytes(2, 5, lens)
+    gl.close()
     w0, l0, _ = _layer(0)
     with pytest.raises(S.StarKVError) as ei:
         l0.set_rope(10000.0)

@@ -59,8 +59,8 @@ def test_prefill_chunk_parity(cfg, chunk):
 
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
 def test_rotary_decode_parity(cfg):
-    """A rotary layer's decode (routed to the reconstructed path) and its fused step against the
-    oracle's rotated reconstruct-then-attend."""
+    """A rotary layer's decode (scores over key tiles rebuilt from the latent and rotated, values in
+    the latent space) and its fused step against the oracle's rotated reconstruct-then-attend."""
     w, run = _setup(cfg, MINI[cfg])
     theta = 10000.0 if cfg != 3 else 500000.0
     run.GL.set_rope(theta)
@@ -105,6 +105,19 @@ def test_rotary_prefill_far_positions():
     ref = O.decode(q[0].astype(np.float64), run.ocache[0], run.OL, 64, run.scales_o, rope_theta=500000.0,
                    rotary_dim=w.d_h)
     H.check_output(wq, got[0], ref, f"rotary prefill len {int(run.lens[0])}")
+
+
+def test_rotary_decode_far_positions():
+    """Rotary decode of a GQA layer 20011 tokens in: many 512-token key blocks, a ragged last chunk,
+    rotation angles of positions past 2^14."""
+    w, run = _setup(3, [20011])
+    run.GL.set_rope(500000.0)
+    H.log(f"[rotary decode far] cfg=3 len={int(run.lens[0])}")
+    q = H.queries(run)
+    got = H.from_dev(H.decode(run, q))
+    ref = O.decode(q[0].astype(np.float64), run.ocache[0], run.OL, w.n_q, run.scales_o, rope_theta=500000.0,
+                   rotary_dim=w.d_h)
+    H.check_output(w, got[0], ref, f"rotary decode len {int(run.lens[0])}")
 
 
 def test_rotary_layer_refuses_absorbed_queries():
