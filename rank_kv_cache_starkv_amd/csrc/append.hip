@@ -13,6 +13,8 @@
 // unconditional and the loop has no branch but its own (rows past M and padding columns read
 // row 0 / channel 0, K-steps past the end re-read the last one; their operands are zeroed after
 // the load).
+#include <algorithm>
+
 #include "device_common.h"
 #include "latent_gemm.h"
 #include "profile.h"
@@ -214,6 +216,117 @@ __global__ __launch_bounds__(64 * NW) void k_latent_gemm(GemmArgs a) {
   store_latent<NVW>(a, slot, chan, sc_bits, xs, ms, ps);
 }
 
+// Epilogue of one wave's 32 x 32 quadrant of a 64 x 64 tile (rows mb + 32 wm .., slots
+// sb + 32 wn ..): lane holds column n = r (slot), rows d32_row(v, q).  MODE 0 stores the cache
+// rows (padding columns store zero), MODE 1 takes the per-channel absmax over the rows < M.
+template <int MODE>
+__device__ __forceinline__ void gemm_tile_epilogue(const GemmArgs& a, int mb, int sb, int wm, int wn, const f32x16& acc) {
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 31, q = lane >> 5;
+  const int m0 = mb + 32 * wm;
+  const int slot = sb + 32 * wn + r;
+  const int chan = slot_channel(a, slot);
+  if (MODE == 1) {
+    float m = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) m = fmaxf(m, m0 + d32_row(v, q) < a.M ? fabsf(acc[v]) : 0.f);
+    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    if (q == 0 && chan >= 0) atomicMax(a.absmax + chan, __float_as_uint(m));
+    return;
+  }
+  const uint16_t sc_bits = a.latent == STARKV_LATENT_MIX84 ? scale_bits(a, chan) : (uint16_t)0;
+  float xs[16];
+  int ms[16], ps[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    xs[v] = chan >= 0 ? acc[v] : 0.f;
+    ms[v] = m0 + d32_row(v, q);
+    ps[v] = row_pos(a, ms[v]);
+  }
+  store_latent<16>(a, slot, chan, sc_bits, xs, ms, ps);
+}
+
+// bf16 operands, d a multiple of 64: the X and A_t tiles stream through LDS.  Workgroup tile
+// 64 token rows x 64 cache slots, four waves in 2 x 2 quadrants of 32 x 32, each over the whole
+// K (no partial sums to add).  K advances in blocks of 64: a block's two 8 KiB operand tiles
+// arrive by 16-byte LDS DMA (each wave issues two loads per tile) into a ring of NST stages, NST - 1
+// blocks ahead of the MFMAs, so the loads of a CU run deep without holding registers.  In a tile,
+// row R's eight 16-byte K-chunks sit at chunk c ^ ((R >> 1) & 7): the 16 lanes of a fragment read
+// (rows R .. R + 15, one chunk) then hit 16 different 4-bank groups.  Rows past M and padding
+// columns load row 0 / channel 0 (valid addresses); such rows are never stored and padding
+// columns store zero.  Grid and epilogue as k_latent_gemm (MODE 0: store, MODE 1: absmax).
+// NST stages of 16 KiB each in dynamic LDS (4: two workgroups per CU).  On MI355X the kernel is
+// bound by the operand bytes each CU pulls (about 40 GB/s per CU from L2): eight stages, or K
+// split over more workgroups with a reduce pass, measured no faster on the 256 x 2560 x 5120 step.
+template <int MODE, int NST>
+__global__ __launch_bounds__(256) void k_latent_gemm_dma(GemmArgs a) {
+  constexpr int TB = 64 * 64 * 2;  // bytes of one operand tile of a K block
+  extern __shared__ __align__(16) uint8_t ring_raw[];
+  uint8_t (*ring)[2][TB] = (uint8_t (*)[2][TB])ring_raw;
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const int r = lane & 31, q = lane >> 5;
+  int rt = blockIdx.x, ctl = blockIdx.y;
+  if (a.xmap_rt > 0) {
+    const int k = blockIdx.x >> 3;
+    rt = k % a.xmap_rt;
+    ctl = (blockIdx.x & 7) + 8 * (k / a.xmap_rt);
+    if (ctl * 64 >= a.NS) return;  // whole workgroup
+  }
+  const int mb = rt * 64, sb = ctl * 64;
+  // this lane's DMA sources: load jj of the wave fills tile slot i = 64 (2 wave + jj) + lane,
+  // i.e. row i / 8 and stored chunk i % 8, which holds K-chunk (i % 8) ^ ((row >> 1) & 7)
+  const uint16_t* xsrc[2];
+  const uint16_t* wsrc[2];
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj) {
+    const int i = 64 * (2 * wave + jj) + lane;
+    const int row = i >> 3;
+    const int kc = (i & 7) ^ ((row >> 1) & 7);
+    const int xr = mb + row < a.M ? mb + row : 0;
+    const int ch = slot_channel(a, sb + row);
+    xsrc[jj] = (const uint16_t*)a.X + (size_t)xr * a.d + 8 * kc;
+    wsrc[jj] = (const uint16_t*)a.A_t + (size_t)(ch >= 0 ? ch : 0) * a.d + 8 * kc;
+  }
+  const int nkb = a.d / 64;
+  const uint32_t ring0 = lds_addr(ring);
+  auto issue = [&](int kb, int st) {
+    kb = min(kb, nkb - 1);  // past the end: reload the last block (never read)
+    const uint32_t xb = ring0 + st * 2 * TB, wb = xb + TB;
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      lds_dma16(xsrc[jj] + 64 * kb, xb + 1024 * (2 * wave + jj));
+      lds_dma16(wsrc[jj] + 64 * kb, wb + 1024 * (2 * wave + jj));
+    }
+  };
+  const int wm = wave & 1, wn = wave >> 1;
+  const int xrow = 32 * wm + r, wrow = 32 * wn + r;
+  const int xo = xrow * 128, wo = wrow * 128;
+  const int xsw = (xrow >> 1) & 7, wsw = (wrow >> 1) & 7;
+  f32x16 acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+#pragma unroll
+  for (int u = 0; u < NST - 1; ++u) issue(u, u);
+  for (int kb = 0; kb < nkb; ++kb) {
+    vm_wait<4 * (NST - 2)>();      // this wave's loads of block kb are in
+    __builtin_amdgcn_s_barrier();  // ... and every wave's; block kb - 1's stage is free
+    asm volatile("" ::: "memory");
+    issue(kb + NST - 1, (kb + NST - 1) % NST);
+    const uint8_t* xt = ring[kb % NST][0];
+    const uint8_t* wt = ring[kb % NST][1];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int c = 2 * ks + q;
+      const u32x4 xf = *(const u32x4*)(xt + xo + 16 * (c ^ xsw));
+      const u32x4 wf = *(const u32x4*)(wt + wo + 16 * (c ^ wsw));
+      acc = mfma32_bf16(as_bf16x8(xf), as_bf16x8(wf), acc);
+    }
+  }
+  vm_wait<0>();  // the trailing reloads land before the workgroup ends
+  gemm_tile_epilogue<MODE>(a, mb, sb, wm, wn, acc);
+}
+
 __global__ void k_fill_u32(uint32_t* p, int n, uint32_t v) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i < n) p[i] = v;
@@ -268,12 +381,24 @@ hipError_t launch_calibrate(const Layer& L, const void* X_cal, int n_cal, uint16
   fill_gemm_args(L, a, X_cal, n_cal);
   a.absmax = L.d_absmax;
   dim3 grid((n_cal + 63) / 64, (a.NS + 63) / 64);
-  if (L.dtype == STARKV_BF16) hipLaunchKernelGGL((k_latent_gemm<STARKV_BF16, 1, 4>), grid, dim3(256), 0, s, a);
+  if (L.dtype == STARKV_BF16 && L.d % 64 == 0)
+    hipLaunchKernelGGL((k_latent_gemm_dma<1, 4>), grid, dim3(256), 4 * 2 * 8192, s, a);
+  else if (L.dtype == STARKV_BF16) hipLaunchKernelGGL((k_latent_gemm<STARKV_BF16, 1, 4>), grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL((k_latent_gemm<STARKV_F32, 1, 4>), grid, dim3(256), 0, s, a);
   hipLaunchKernelGGL(k_finish_scales, dim3((L.n_lat + 255) / 256), dim3(256), 0, s, (const uint32_t*)L.d_absmax,
                      (const int*)L.d_src, (const int*)L.d_n8, L.n8v, L.H_kv, L.n_lat, (float)L.qmax_hi,
                      (float)L.qmax_lo, scales_out);
   return hipGetLastError();
+}
+
+// One launch with dynamic LDS, with the timing events attached when given.
+template <typename A>
+static hipError_t launch_lds(const ProfScope& ps, void (*kernel)(A), dim3 grid, dim3 block, size_t lds, hipStream_t s,
+                             A arg) {
+  void* argv[] = {(void*)&arg};
+  if (ps.start() && ps.stop())
+    return hipExtLaunchKernel((const void*)kernel, grid, block, argv, lds, s, ps.start(), ps.stop(), 0);
+  return hipLaunchKernel((const void*)kernel, grid, block, argv, lds, s);
 }
 
 hipError_t launch_append(const Layer& L, const starkv_cache& c, const void* X_new, int B, int n_new,
@@ -299,6 +424,16 @@ hipError_t launch_append(const Layer& L, const starkv_cache& c, const void* X_ne
     else
       e = mix ? launch_k(ps, k_latent_gemm_skinny<STARKV_F32, 16, true>, grid, dim3(512), s, a)
               : launch_k(ps, k_latent_gemm_skinny<STARKV_F32, 16, false>, grid, dim3(512), s, a);
+  } else if (L.dtype == STARKV_BF16 && L.d % 64 == 0) {
+    // bf16: operands staged through LDS; a short block of tokens takes the XCD-aware grid (the
+    // row tiles of a column tile on one XCD, sharing its L2 copy of that slab of A)
+    const int n_rt = (B * n_new + 63) / 64, n_ct = (a.NS + 63) / 64;
+    if (n_rt <= 16) {
+      a.xmap_rt = n_rt;
+      e = launch_lds(ps, k_latent_gemm_dma<0, 4>, dim3(8 * n_rt * ((n_ct + 7) / 8)), dim3(256), 4 * 2 * 8192, s, a);
+    } else {
+      e = launch_lds(ps, k_latent_gemm_dma<0, 4>, dim3(n_rt, n_ct), dim3(256), 4 * 2 * 8192, s, a);
+    }
   } else {
     const int n_rt = (B * n_new + 63) / 64, n_ct = (a.NS + 63) / 64;
     if (n_rt <= 16) {

@@ -1225,22 +1225,6 @@ __global__ __launch_bounds__(256) void k_scores_mix(ScoreArgs a) {
   }
 }
 
-// ---- asynchronous loads straight into LDS
-// Lane l's 16 bytes at src land at LDS byte address lds + 16 l (lds wave-uniform; the builtin
-// puts it in M0).  The kernel waits with vm_wait<n>() (n = loads it may leave in flight) and a
-// barrier before any wave reads the data.
-__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(uintptr_t)lds, 16, 0, 0);
-}
-template <int N>
-__device__ __forceinline__ void vm_wait() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
 // Key scores of a rotary layer (keys rotated by position after the key projection): the rotation
 // does not commute with B_g, so each key tile is rebuilt from the latent before the dot product
 // (STAR-KV summary page, Problem Statement: the reconstruction cost; Methodology section 2: the

@@ -131,4 +131,20 @@ __device__ __forceinline__ int find_segment(const int* off, int n, int x) {
   return lo;
 }
 
+// ---- asynchronous loads straight into LDS
+// Lane l's 16 bytes at src land at LDS byte address lds + 16 l (lds wave-uniform; the builtin
+// puts it in M0).  The kernel waits with vm_wait<n>() (n = loads it may leave in flight) and a
+// barrier before any wave reads the data.
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(uintptr_t)lds, 16, 0, 0);
+}
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
 }  // namespace skv
