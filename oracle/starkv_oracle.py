@@ -42,7 +42,10 @@ Hadamards on the power-of-two pieces of its binary decomposition (largest
 first); the +-1 matrix R goes into ``A`` and ``R^T / n`` (n = the piece's
 order) into ``B``, so that ``A B`` is unchanged; codes are clamped to +-7
 (outlier) and +-3 (inlier) and stored in the int8 and int4 regions of the
-mix84 byte format.
+mix84 byte format.  ``had43p`` holds the same codes packed to their own widths:
+the outlier block as 4-bit nibbles and the inlier block as 3-bit fields in bit
+planes (the layout is :class:`CacheFormat`'s), which is how the codes reach the
+3.2 bits per channel of the summary page's Key Results.
 """
 
 from __future__ import annotations
@@ -193,7 +196,7 @@ def build_layer(U_k, s_k, V_k, tau_k, U_v, s_v, V_v, tau_v, H_q: int, latent: st
     """Hybrid decomposition: per-head (HD) key factors, joint (JD) value factors."""
     H_kv, d, d_h = np.shape(U_k)
     As, Bs, ranks = [], [], []
-    rot = latent == "had43"
+    rot = latent in ROTATED
     for g in range(H_kv):
         A, B = factor_pair(U_k[g], s_k[g], V_k[g], tau_k[g], shrink, dtype, rotate=rot)
         As.append(A)
@@ -209,7 +212,8 @@ def build_layer(U_k, s_k, V_k, tau_k, U_v, s_v, V_v, tau_v, H_q: int, latent: st
 # ---------------------------------------------------------------------------
 # mixed precision split (Methodology section 3; leading channels get more bits)
 
-QUANTIZED = ("mix84", "had43")
+QUANTIZED = ("mix84", "had43", "had43p")
+ROTATED = ("had43", "had43p")  # the block-rotated 4-bit/3-bit quantiser (byte regions / packed)
 
 
 def is_quantized(latent: str) -> bool:
@@ -232,13 +236,13 @@ def had43_split(r: int) -> Tuple[int, int]:
 
 def precision_split(r: int, latent: str) -> Tuple[int, int]:
     """(channels in the high-precision block, channels in the low one)."""
-    return had43_split(r) if latent == "had43" else mix84_split(r)
+    return had43_split(r) if latent in ROTATED else mix84_split(r)
 
 
 def code_limits(latent: str) -> Tuple[int, int]:
     """qmax of the high and the low block: int8/int4 (127, 7) for mix84; 4-bit and
-    3-bit symmetric codes (7, 3) for had43."""
-    return (7, 3) if latent == "had43" else (127, 7)
+    3-bit symmetric codes (7, 3) for had43 / had43p."""
+    return (7, 3) if latent in ROTATED else (127, 7)
 
 
 def channel_qmax(layer: Layer) -> np.ndarray:
@@ -315,6 +319,20 @@ class CacheFormat:
     row is token t of the tile.
     had43 uses the same regions, with the outlier block (ceil(r/5) channels) in
     the int8 region and the inlier block in the int4 region.
+    had43p key row: a nibble region of K4/2 bytes holding, head after head, each
+    head's outlier channels as two's complement nibbles (low nibble first),
+    zero-padded to a multiple of 64 nibbles; then a 3-bit region holding, head
+    after head, the inlier channels in groups of 32: a group is three little-endian
+    32-bit words P0, P1, P2, where bit j of Pb is bit b of (code + 4) of the
+    group's channel j (a field of 1..7; padding channels are 0); the region is
+    padded to a multiple of 64 channels and the row to a multiple of 16 bytes.
+    had43p value tile: one byte-row per outlier channel pair (low nibble = even
+    channel, padded to a multiple of 64 channels), then the inlier channels as a
+    byte stream laid over 32-byte rows (stream byte k in row V4/2 + k // 32,
+    column k % 32): 12 bytes per channel, three little-endian words P0, P1, P2
+    over the tile's 32 tokens, token t at bit 8 (t >> 3) + 4 (t & 1) + ((t >> 1) & 3)
+    of each word holding bit b of (code + 4); the stream is padded to a multiple
+    of 64 channels and the rows to a multiple of 32.
     f32/bf16: key row = the key latent in channel order, padded to 16 bytes;
     value tile = r_v (padded to a multiple of 32) element-rows of 32 tokens.
     """
@@ -325,11 +343,16 @@ class CacheFormat:
 
     @property
     def elem(self) -> int:
-        return {"f32": 4, "bf16": 2, "mix84": 1, "had43": 1}[self.latent]
+        return {"f32": 4, "bf16": 2, "mix84": 1, "had43": 1, "had43p": 1}[self.latent]
 
     @property
     def quantized(self) -> bool:
         return is_quantized(self.latent)
+
+    @property
+    def packed(self) -> bool:
+        """Codes at their own widths (had43p): 4-bit nibbles and 3-bit planes."""
+        return self.latent == "had43p"
 
     def split(self, r: int) -> Tuple[int, int]:
         """Channels of a rank-r segment in the int8 region and in the int4 region."""
@@ -346,14 +369,25 @@ class CacheFormat:
 
     @property
     def K8(self) -> int:
-        return _ceil_to(sum(self.n8), 16)
+        """Byte positions of the int8 region (none when packed)."""
+        return 0 if self.packed else _ceil_to(sum(self.n8), 16)
 
     @property
     def K4(self) -> int:
+        """Nibble positions of the 4-bit region: the int4 block, or the packed outlier block."""
+        if self.packed:
+            return _ceil_to(sum(self.n8), 64)
         return _ceil_to(sum(self.n4), 32)
 
     @property
+    def K3(self) -> int:
+        """Channel positions of the packed 3-bit region (0 unless packed)."""
+        return _ceil_to(sum(self.n4), 64) if self.packed else 0
+
+    @property
     def k_row_bytes(self) -> int:
+        if self.packed:
+            return _ceil_to(self.K4 // 2 + 3 * self.K3 // 8, 16)
         if self.quantized:
             return self.K8 + self.K4 // 2
         return _ceil_to(sum(self.ranks) * self.elem, 16)
@@ -361,15 +395,23 @@ class CacheFormat:
     # value side
     @property
     def V8(self) -> int:
-        return _ceil_to(self.split(self.r_v)[0], 32)
+        return 0 if self.packed else _ceil_to(self.split(self.r_v)[0], 32)
 
     @property
     def V4(self) -> int:
-        return _ceil_to(self.split(self.r_v)[1], 64)
+        """Channels of the nibble-pair rows: the int4 block, or the packed outlier block."""
+        return _ceil_to(self.split(self.r_v)[0 if self.packed else 1], 64)
+
+    @property
+    def V3(self) -> int:
+        """Channels of the packed 3-bit stream (0 unless packed)."""
+        return _ceil_to(self.split(self.r_v)[1], 64) if self.packed else 0
 
     @property
     def v_rows(self) -> int:
         """Rows of a value tile (byte-rows when quantised, element-rows otherwise)."""
+        if self.packed:
+            return _ceil_to(self.V4 // 2 + 3 * self.V3 // 8, 32)
         if self.quantized:
             return self.V8 + self.V4 // 2
         return _ceil_to(self.r_v, 32)
@@ -379,10 +421,120 @@ class CacheFormat:
         return self.v_rows * TT * self.elem
 
 
+def token_bit3(t: int) -> int:
+    """Bit of token t (0..31) in a packed value plane word: 8 (t >> 3) + 4 (t & 1) + ((t >> 1) & 3)."""
+    return 8 * (t >> 3) + 4 * (t & 1) + ((t >> 1) & 3)
+
+
+def _planes(fields) -> np.ndarray:
+    """Bit planes of 3-bit fields [..., 32] -> little-endian words [..., 3] (bit j of word b is
+    bit b of field j)."""
+    f = np.asarray(fields, dtype=np.uint64)
+    w = np.zeros(f.shape[:-1] + (3,), dtype=np.uint64)
+    for b in range(3):
+        for j in range(32):
+            w[..., b] |= ((f[..., j] >> np.uint64(b)) & np.uint64(1)) << np.uint64(j)
+    return w.astype(np.uint32)
+
+
+def _unplanes(words) -> np.ndarray:
+    """Inverse of :func:`_planes`: words [..., 3] -> fields [..., 32]."""
+    w = np.asarray(words, dtype=np.uint64)
+    f = np.zeros(w.shape[:-1] + (32,), dtype=np.int64)
+    for b in range(3):
+        for j in range(32):
+            f[..., j] |= (((w[..., b] >> np.uint64(j)) & np.uint64(1)) << np.uint64(b)).astype(np.int64)
+    return f
+
+
+def _pack_key_rows_packed(vals, fmt: CacheFormat) -> np.ndarray:
+    T = vals.shape[0]
+    out = np.zeros((T, fmt.k_row_bytes), dtype=np.uint8)
+    koff = np.concatenate([[0], np.cumsum(fmt.ranks)])
+    nh = [fmt.split(r)[0] for r in fmt.ranks]
+    nl = [fmt.split(r)[1] for r in fmt.ranks]
+    oh = np.concatenate([[0], np.cumsum(nh)])
+    ol = np.concatenate([[0], np.cumsum(nl)])
+    fields = np.zeros((T, fmt.K3), dtype=np.int64)  # padding channels: 0
+    for g, r in enumerate(fmt.ranks):
+        seg = vals[:, koff[g]: koff[g] + r].astype(np.int64)
+        for k in range(nh[g]):
+            u = oh[g] + k
+            out[:, u // 2] |= ((seg[:, k] & 0xF) << (4 * (u % 2))).astype(np.uint8)
+        fields[:, ol[g]: ol[g] + nl[g]] = seg[:, nh[g]:] + 4
+    words = _planes(fields.reshape(T, fmt.K3 // 32, 32))  # [T, groups, 3]
+    b3 = fmt.K4 // 2
+    out[:, b3: b3 + 3 * fmt.K3 // 8] = np.ascontiguousarray(words.astype("<u4")).view(np.uint8).reshape(T, -1)
+    return out
+
+
+def _unpack_key_rows_packed(rows, fmt: CacheFormat) -> np.ndarray:
+    T = rows.shape[0]
+    out = np.zeros((T, sum(fmt.ranks)), dtype=np.int64)
+    koff = np.concatenate([[0], np.cumsum(fmt.ranks)])
+    nh = [fmt.split(r)[0] for r in fmt.ranks]
+    nl = [fmt.split(r)[1] for r in fmt.ranks]
+    oh = np.concatenate([[0], np.cumsum(nh)])
+    ol = np.concatenate([[0], np.cumsum(nl)])
+    b3 = fmt.K4 // 2
+    words = np.ascontiguousarray(rows[:, b3: b3 + 3 * fmt.K3 // 8]).view("<u4").reshape(T, fmt.K3 // 32, 3)
+    fields = _unplanes(words).reshape(T, fmt.K3)
+    for g in range(len(fmt.ranks)):
+        for k in range(nh[g]):
+            u = oh[g] + k
+            nib = (rows[:, u // 2].astype(np.int64) >> (4 * (u % 2))) & 0xF
+            out[:, koff[g] + k] = np.where(nib >= 8, nib - 16, nib)
+        out[:, koff[g] + nh[g]: koff[g] + nh[g] + nl[g]] = fields[:, ol[g]: ol[g] + nl[g]] - 4
+    return out
+
+
+def _pack_value_tiles_packed(vals, fmt: CacheFormat, n_tiles: int) -> np.ndarray:
+    T = vals.shape[0]
+    nh, nl = fmt.split(fmt.r_v)
+    c = np.zeros((n_tiles * TT, fmt.r_v), dtype=np.int64)
+    c[:T] = vals
+    out = np.zeros((n_tiles, fmt.v_rows, TT), dtype=np.uint8)
+    for k in range(nh):
+        nib = (c[:, k] & 0xF).astype(np.uint8).reshape(n_tiles, TT)
+        out[:, k // 2, :] |= nib if k % 2 == 0 else (nib << 4)
+    # fields [tile, channel, bit position]: token t of the tile at position token_bit3(t);
+    # tokens past T and padding channels hold 0
+    fields = np.zeros((n_tiles, fmt.V3, 32), dtype=np.int64)
+    valid = (np.arange(n_tiles * TT) < T).reshape(n_tiles, TT)
+    perm = [token_bit3(t) for t in range(TT)]
+    for k in range(nl):
+        f = (c[:, nh + k] + 4).reshape(n_tiles, TT)
+        fields[:, k, perm] = np.where(valid, f, 0)
+    stream = np.ascontiguousarray(_planes(fields).astype("<u4")).view(np.uint8).reshape(n_tiles, -1)
+    r3 = fmt.V4 // 2
+    flat = out.reshape(n_tiles, -1)
+    flat[:, r3 * TT: r3 * TT + stream.shape[1]] = stream
+    return out
+
+
+def _unpack_value_tiles_packed(tiles, fmt: CacheFormat, T: int) -> np.ndarray:
+    n_tiles = tiles.shape[0]
+    nh, nl = fmt.split(fmt.r_v)
+    out = np.zeros((n_tiles * TT, fmt.r_v), dtype=np.int64)
+    for k in range(nh):
+        nib = (tiles[:, k // 2, :].astype(np.int64) >> (4 * (k % 2))) & 0xF
+        out[:, k] = np.where(nib >= 8, nib - 16, nib).reshape(-1)
+    r3 = fmt.V4 // 2
+    flat = tiles.reshape(n_tiles, -1)
+    stream = np.ascontiguousarray(flat[:, r3 * TT: r3 * TT + 12 * fmt.V3])
+    fields = _unplanes(stream.view("<u4").reshape(n_tiles, fmt.V3, 3))  # [tile, channel, position]
+    perm = [token_bit3(t) for t in range(TT)]
+    for k in range(nl):
+        out[:, nh + k] = (fields[:, k, perm] - 4).reshape(-1)
+    return out[:T]
+
+
 def pack_key_rows(vals, fmt: CacheFormat) -> np.ndarray:
     """Key latent rows [T, sum(r)] (codes when quantised, values otherwise) -> bytes [T, k_row_bytes]."""
     vals = np.asarray(vals)
     T = vals.shape[0]
+    if fmt.packed:
+        return _pack_key_rows_packed(vals, fmt)
     out = np.zeros((T, fmt.k_row_bytes), dtype=np.uint8)
     if not fmt.quantized:
         if fmt.latent == "f32":
@@ -409,6 +561,8 @@ def pack_key_rows(vals, fmt: CacheFormat) -> np.ndarray:
 def unpack_key_rows(rows, fmt: CacheFormat) -> np.ndarray:
     rows = np.asarray(rows, dtype=np.uint8)
     T = rows.shape[0]
+    if fmt.packed:
+        return _unpack_key_rows_packed(rows, fmt)
     nk = sum(fmt.ranks)
     if fmt.latent == "f32":
         return rows[:, : nk * 4].copy().view(np.float32).reshape(T, nk)
@@ -434,6 +588,8 @@ def pack_value_tiles(vals, fmt: CacheFormat, n_tiles: int) -> np.ndarray:
     """Value latent [T, r_v] -> tiles [n_tiles, v_rows, 32 * elem] (tokens >= T are zero)."""
     vals = np.asarray(vals)
     T = vals.shape[0]
+    if fmt.packed:
+        return _pack_value_tiles_packed(vals, fmt, n_tiles)
     out = np.zeros((n_tiles, fmt.v_rows, TT * fmt.elem), dtype=np.uint8)
     if not fmt.quantized:
         if fmt.latent == "f32":
@@ -459,6 +615,8 @@ def pack_value_tiles(vals, fmt: CacheFormat, n_tiles: int) -> np.ndarray:
 def unpack_value_tiles(tiles, fmt: CacheFormat, T: int) -> np.ndarray:
     tiles = np.asarray(tiles, dtype=np.uint8)
     n_tiles = tiles.shape[0]
+    if fmt.packed:
+        return _unpack_value_tiles_packed(tiles, fmt, T)
     if fmt.latent == "f32":
         v = tiles.copy().view(np.float32).reshape(n_tiles, fmt.v_rows, TT)
         return v.transpose(0, 2, 1).reshape(n_tiles * TT, fmt.v_rows)[:T, : fmt.r_v].copy()
@@ -593,7 +751,7 @@ def lse_merge(parts: Sequence[Tuple[float, float, np.ndarray]]) -> np.ndarray:
 
 @dataclasses.dataclass
 class SequenceCache:
-    """The oracle's cache of one sequence: integer codes (mix84, had43) or stored values."""
+    """The oracle's cache of one sequence: integer codes (mix84, had43, had43p) or stored values."""
 
     key: np.ndarray  # [T, sum(r)]
     value: np.ndarray  # [T, r_v]

@@ -187,7 +187,35 @@ def test_pack_golden():
     np.testing.assert_array_equal(vt, expect_v)
 
 
-@pytest.mark.parametrize("latent", ["mix84", "had43", "bf16", "f32"])
+def test_pack_golden_packed():
+    """The packed 4-bit/3-bit layout (had43p) against bytes derived by hand in the fixture."""
+    gd = json.load(open(os.path.join(GOLDEN, "pack_tiny_had43p.json")))
+    fmt = O.CacheFormat("had43p", tuple(gd["key_ranks"]), gd["r_v"])
+    assert fmt.k_row_bytes == gd["key_row_bytes"] and fmt.v_rows == gd["value_rows"]
+    kr = O.pack_key_rows(np.array(gd["key_codes"]), fmt)
+    expect = np.zeros_like(kr)
+    for t, cells in gd["key_rows_nonzero"].items():
+        for col, val in cells:
+            expect[int(t), col] = val
+    np.testing.assert_array_equal(kr, expect)
+    vt = O.pack_value_tiles(np.array(gd["value_codes"]), fmt, 1)
+    expect_v = np.zeros_like(vt)
+    for row, col, val in gd["value_tile_nonzero"]:
+        expect_v[0, row, col] = val
+    np.testing.assert_array_equal(vt, expect_v)
+    # and back
+    np.testing.assert_array_equal(O.unpack_key_rows(kr, fmt), gd["key_codes"])
+    np.testing.assert_array_equal(O.unpack_value_tiles(vt, fmt, 2), gd["value_codes"])
+
+
+def test_token_bit3_is_a_permutation():
+    # the packed value planes place 8 tokens per byte: token t in byte t >> 3
+    bits = [O.token_bit3(t) for t in range(32)]
+    assert sorted(bits) == list(range(32))
+    assert all(b // 8 == t // 8 for t, b in enumerate(bits))
+
+
+@pytest.mark.parametrize("latent", ["mix84", "had43", "had43p", "bf16", "f32"])
 def test_pack_round_trip(latent):
     rng = np.random.default_rng(5)
     ranks = (17, 3, 1, 30, 8)
@@ -195,7 +223,7 @@ def test_pack_round_trip(latent):
     fmt = O.CacheFormat(latent, ranks, r_v)
     T = 70
     if O.is_quantized(latent):
-        # the full code range of each region: int8/int4 for mix84, 4-bit/3-bit for had43
+        # the full code range of each region: int8/int4 for mix84, 4-bit/3-bit for had43(p)
         hi, lo = (127, 7) if latent == "mix84" else (7, 3)
         qk = np.concatenate([[hi] * fmt.split(r)[0] + [lo] * fmt.split(r)[1] for r in ranks])
         kc = rng.integers(-qk, qk + 1, size=(T, sum(ranks)))
@@ -223,6 +251,14 @@ def test_format_sizes_match_accounting():
     assert fmt.n8 == [8] * 32 and fmt.n4 == [32] * 32
     assert fmt.k_row_bytes == 768 and fmt.v_rows == 256 + 512
     assert acc.mean_bits(0.2, 8, 4) * 1280 / 8 == pytest.approx(768)
+    # had43p packs the same codes to their widths: 4-bit outliers + 3-bit inliers = the summary
+    # page's 3.2 bits per channel (Key Results), 512 bytes per token for 1280 channels
+    fmt = O.CacheFormat("had43p", tuple([40] * 32), 1280)
+    assert fmt.K4 == 256 and fmt.K3 == 1024 and fmt.V4 == 256 and fmt.V3 == 1024
+    assert fmt.k_row_bytes == 512 and fmt.v_rows == 512
+    assert acc.mean_bits(0.2, 4, 3) * 1280 / 8 == pytest.approx(512)
+    # with 75% low-rank compression that is the pages' 20x reduction of a 16-bit cache
+    assert acc.reduction(0.75, fmt.k_row_bytes * 8 / 1280) == pytest.approx(20.0)
 
 
 # ---------------------------------------------------------------- block-wise Hadamard rotation (had43)
@@ -450,7 +486,7 @@ def _frac_mat(a):
     return [[Fraction(float(v)) for v in row] for row in np.asarray(a, np.float64)]
 
 
-@pytest.mark.parametrize("latent", ["mix84", "had43", "f32"])
+@pytest.mark.parametrize("latent", ["mix84", "had43", "had43p", "f32"])
 def test_brute_force_tiny(latent):
     rng = np.random.default_rng(12)
     w = I.Workload(9, "t", B=1, H_q=4, H_kv=2, d_h=4, d=12, n_q=2, latent=latent, dtype="f32",
