@@ -82,6 +82,22 @@ extern "C" {
                                  with per-channel fp16 scales.  Codes are stored in the
                                  mix84 byte format: outliers in the int8 region, inliers in
                                  the int4 region (dtype BF16). */
+#define STARKV_LATENT_HAD43P 4 /* the same quantiser and codes as STARKV_LATENT_HAD43, stored at
+                                 their own widths (the summary page's 3.2 bits per channel,
+                                 Key Results): outlier codes as nibbles, inlier codes as 3-bit
+                                 fields in bit planes.  Key row: K4/2 bytes of outlier nibbles
+                                 (head after head, two's complement, low nibble first, K4 a
+                                 multiple of 64), then the inlier channels of all heads in
+                                 groups of 32: three little-endian 32-bit words P0, P1, P2, bit j
+                                 of Pb = bit b of (code + 4) of the group's channel j (padding:
+                                 0), K3 channels (a multiple of 64); row padded to 16 bytes.
+                                 Value tile: V4/2 byte-rows of outlier channel pairs (nibbles,
+                                 low = even channel), then the inlier channels as a byte stream
+                                 over the following 32-byte rows: 12 bytes per channel, words
+                                 P0, P1, P2 over the tile's 32 tokens with token t at bit
+                                 8 (t >> 3) + 4 (t & 1) + ((t >> 1) & 3).  Decode with at most 32
+                                 query rows per sequence (H_q * n_q <= 32); rotary layers
+                                 attend over reconstructed K and V.  dtype BF16, d % 64 == 0. */
 
 /* limits of the library */
 #define STARKV_MAX_BATCH 128     /* sequences per call */
@@ -112,12 +128,16 @@ typedef struct starkv_layer_info {
   int k_row_bytes;   /* bytes of one token's key row */
   int v_tile_rows;   /* rows of a value tile */
   int v_tile_bytes;  /* bytes of one value tile (STARKV_TILE_TOKENS tokens) */
-  int K8, K4;        /* mix84 key row: int8 region channels (padded to 16), int4 region channels (padded to 32) */
-  int V8, V4;        /* mix84 value tile: int8 rows (padded to 32), int4 channels (padded to 64) */
+  int K8, K4;        /* mix84 key row: int8 region channels (padded to 16), int4 region channels (padded to 32);
+                        had43p: K8 = 0, K4 = outlier nibbles (padded to 64) */
+  int V8, V4;        /* mix84 value tile: int8 rows (padded to 32), int4 channels (padded to 64);
+                        had43p: V8 = 0, V4 = outlier channels (padded to 64) */
+  int K3, V3;        /* had43p: inlier channels of the key row's and of the value tile's 3-bit
+                        regions (each padded to 64); 0 otherwise */
   size_t a_bytes;    /* bytes of A^T  [n_lat][d] (dtype) */
   size_t bk_bytes;   /* bytes of B_k  [n_key][d_h] (dtype) */
   size_t bv_bytes;   /* bytes of B_v^T [H_kv*d_h][r_v] (dtype) */
-  size_t scale_bytes;/* bytes of the fp16 scales [n_lat] (mix84, had43; 0 otherwise) */
+  size_t scale_bytes;/* bytes of the fp16 scales [n_lat] (mix84, had43, had43p; 0 otherwise) */
 } starkv_layer_info;
 
 /*

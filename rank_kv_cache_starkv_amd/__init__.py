@@ -26,7 +26,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libstarkv.so")
 
 F32, BF16 = 0, 1
-LATENT = {"f32": 0, "bf16": 1, "mix84": 2, "had43": 3}
+LATENT = {"f32": 0, "bf16": 1, "mix84": 2, "had43": 3, "had43p": 4}
 DTYPE = {"f32": F32, "bf16": BF16}
 TILE_TOKENS = 32
 MAX_BATCH = 128
@@ -51,7 +51,8 @@ class _Desc(ctypes.Structure):
 
 class _Info(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in ("H_q", "H_kv", "d_h", "d", "dtype", "latent", "n_key", "r_v", "n_lat",
-                                            "k_row_bytes", "v_tile_rows", "v_tile_bytes", "K8", "K4", "V8", "V4")] + \
+                                            "k_row_bytes", "v_tile_rows", "v_tile_bytes", "K8", "K4", "V8", "V4", "K3",
+                                            "V3")] + \
                [(n, ctypes.c_size_t) for n in ("a_bytes", "bk_bytes", "bv_bytes", "scale_bytes")]
 
 
@@ -268,7 +269,7 @@ class Layer:
         _check(self._lib.starkv_bind_factors(self._h, _ptr(A_t), _ptr(B_k), _ptr(B_vt)), "starkv_bind_factors")
 
     def calibrate(self, X_cal, stream=None):
-        """Per-channel fp16 scales from calibration hidden states [n_cal, d] (mix84, had43)."""
+        """Per-channel fp16 scales from calibration hidden states [n_cal, d] (mix84, had43, had43p)."""
         import torch
         _need(X_cal.dtype == self.torch_dtype and X_cal.is_contiguous() and X_cal.is_cuda and X_cal.dim() == 2 and
               int(X_cal.shape[1]) == self.d, f"X_cal: contiguous {self.torch_dtype} device tensor [n_cal, {self.d}] expected")

@@ -153,7 +153,7 @@ int starkv_layer_create(const starkv_layer_desc* d, starkv_layer** out) {
   if (!d->s_k || !d->tau_k || !d->s_v) return STARKV_EINVAL;
   if (d->dtype != STARKV_F32 && d->dtype != STARKV_BF16) return STARKV_EINVAL;
   if (d->latent != STARKV_LATENT_F32 && d->latent != STARKV_LATENT_BF16 && d->latent != STARKV_LATENT_MIX84 &&
-      d->latent != STARKV_LATENT_HAD43)
+      d->latent != STARKV_LATENT_HAD43 && d->latent != STARKV_LATENT_HAD43P)
     return STARKV_EINVAL;
   if (d->shrink != 0 && d->shrink != 1) return STARKV_EINVAL;
   if (bad_float(d->tau_v) || d->tau_v < 0.f) return STARKV_EINVAL;
@@ -174,6 +174,7 @@ int starkv_layer_create(const starkv_layer_desc* d, starkv_layer** out) {
   if (d->latent == STARKV_LATENT_F32 && d->dtype != STARKV_F32) return STARKV_EUNSUPPORTED;
   if (d->latent != STARKV_LATENT_F32 && d->dtype != STARKV_BF16) return STARKV_EUNSUPPORTED;
   if (d->d % 16 != 0 || d->d_h % 32 != 0 || d->d_h > 256) return STARKV_EUNSUPPORTED;
+  if (d->latent == STARKV_LATENT_HAD43P && d->d % 64 != 0) return STARKV_EUNSUPPORTED;
   if (d->n_v > d->d || d->n_v > d->H_kv * d->d_h) return STARKV_EINVAL;
   starkv_layer* l = new starkv_layer();
   int st = skv::layer_init(*d, &l->L);
@@ -203,7 +204,7 @@ int starkv_layer_get_info(const starkv_layer* l, starkv_layer_info* info) {
   info->d_h = L.d_h;
   info->d = L.d;
   info->dtype = L.dtype;
-  info->latent = L.had ? STARKV_LATENT_HAD43 : L.latent;
+  info->latent = L.pack3 ? STARKV_LATENT_HAD43P : (L.had ? STARKV_LATENT_HAD43 : L.latent);
   info->n_key = L.n_key;
   info->r_v = L.r_v;
   info->n_lat = L.n_lat;
@@ -214,6 +215,8 @@ int starkv_layer_get_info(const starkv_layer* l, starkv_layer_info* info) {
   info->K4 = L.K4;
   info->V8 = L.V8;
   info->V4 = L.V4;
+  info->K3 = L.K3;
+  info->V3 = L.V3;
   const size_t es = L.dtype == STARKV_F32 ? 4 : 2;
   info->a_bytes = (size_t)L.n_lat * L.d * es;
   info->bk_bytes = (size_t)L.n_key * L.d_h * es;

@@ -355,6 +355,9 @@ void fill_gemm_args(const Layer& L, GemmArgs& a, const void* X, int M) {
   a.key_slots = L.key_slots;
   a.K8 = L.K8;
   a.V8 = L.V8;
+  a.pack3 = L.pack3;
+  a.K4 = L.K4;
+  a.V4 = L.V4;
   a.qmax_hi = L.qmax_hi;
   a.qmax_lo = L.qmax_lo;
   a.n_key = L.n_key;
@@ -408,7 +411,16 @@ hipError_t launch_append(const Layer& L, const starkv_cache& c, const void* X_ne
   ProfScope ps("append");
   hipError_t e;
   const bool mix = L.mix();
-  if (B * n_new <= 8 && L.d % 64 == 0) {
+  if (L.pack3) {
+    // packed 3-bit planes: stored from the 64 x 64 tiles' lane layout only
+    const int n_rt = (B * n_new + 63) / 64, n_ct = (a.NS + 63) / 64;
+    if (n_rt <= 16) {
+      a.xmap_rt = n_rt;
+      e = launch_lds(ps, k_latent_gemm_dma<0, 4>, dim3(8 * n_rt * ((n_ct + 7) / 8)), dim3(256), 4 * 2 * 8192, s, a);
+    } else {
+      e = launch_lds(ps, k_latent_gemm_dma<0, 4>, dim3(n_rt, n_ct), dim3(256), 4 * 2 * 8192, s, a);
+    }
+  } else if (B * n_new <= 8 && L.d % 64 == 0) {
     const dim3 grid((a.NS + 7) / 8);
     if (L.dtype == STARKV_BF16)
       e = mix ? launch_k(ps, k_latent_gemm_skinny<STARKV_BF16, 8, true>, grid, dim3(512), s, a)

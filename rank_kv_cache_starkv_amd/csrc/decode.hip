@@ -124,6 +124,10 @@ int plan_decode(const Layer& L, int B, int n_q, const int32_t* lens, int T_max, 
   g.r_v = L.r_v;
   g.K8 = L.K8;
   g.K4 = L.K4;
+  g.K3 = L.K3;
+  g.pack3 = L.pack3;
+  // the packed layout's value kernel takes one tile of at most 32 query rows per sequence
+  if (L.pack3 && g.M_pad > 32) return STARKV_EUNSUPPORTED;
   g.key_kt = L.key_kt;
   g.key_kpos = L.key_kpos;
   g.k_row_bytes = L.k_row_bytes;
@@ -148,8 +152,10 @@ int plan_decode(const Layer& L, int B, int n_q, const int32_t* lens, int T_max, 
       for (int kt = lo / L.key_kt; kt <= (hi - 1) / L.key_kt; ++kt) used[kt] = true;
     };
     if (L.mix()) {
+      // int8 (or packed: outlier nibble) positions, then int4 (or packed: 3-bit) positions
+      const int base_lo = L.pack3 ? L.K4 : L.K8;
       mark(L.off8[g_lo], L.off8[g_hi + 1]);
-      mark(L.K8 + L.off4[g_lo], L.K8 + L.off4[g_hi + 1]);
+      mark(base_lo + L.off4[g_lo], base_lo + L.off4[g_hi + 1]);
     } else {
       mark(L.koff[g_lo], L.koff[g_hi + 1]);
     }
@@ -188,8 +194,11 @@ int plan_decode(const Layer& L, int B, int n_q, const int32_t* lens, int T_max, 
   }
   const int nb8 = L.mix() ? L.V8 / 32 : NB;
   w.n_sl8 = ceil_div(nb8, w.nbw8);
-  w.n_sl4 = L.mix() ? ceil_div(NB - nb8, w.nbw4) : 0;
-  if (g.M_pad == 32) n_slices = w.n_sl8 + w.n_sl4;
+  // int4 blocks: the rest, or with the packed layout the outlier blocks (V4 / 64) before the
+  // 3-bit N-tiles (V3 / 32, two per slice)
+  w.n_sl4 = L.mix() ? ceil_div((L.pack3 ? L.V4 / 64 : NB) - nb8, w.nbw4) : 0;
+  w.n_sl3 = L.pack3 ? ceil_div(L.V3 / 32, 2) : 0;
+  if (g.M_pad == 32) n_slices = w.n_sl8 + w.n_sl4 + w.n_sl3;
   // many query rows (bf16, int8/int4): groups of four 32-channel N-tiles
   const int n_nt = L.mix() ? nb8 + 2 * (NB - nb8) : NB;
   w.n_grp = ceil_div(n_nt, g.M_pad <= 160 ? 8 : 4);  // N-tiles per workgroup: 4 waves x (2, or 1 past 5 row tiles)
@@ -433,11 +442,14 @@ __device__ __forceinline__ void qproj_body(const QprojArgs& a, int gk, int b, in
     }
     // row parameters: rho and the int4 offset-binary bias terms 8 * sum(int4 codes' weights)
     for (int n = wave; n < nrows; n += NWV) {
+      // offset-binary codes: int4 nibbles read as code + 8; packed layout: outlier nibbles
+      // code + 8, 3-bit inlier fields code + 4
       int sh = 0, sl = 0;
       if (LAT == STARKV_LATENT_MIX84)
-        for (int k = n8g + lane; k < r; k += 64) {
-          sh += hi8[n][k];
-          sl += lo8[n][k];
+        for (int k = (g.pack3 ? 0 : n8g) + lane; k < r; k += 64) {
+          const int wgt = (g.pack3 && k >= n8g) ? 4 : 8;
+          sh += wgt * hi8[n][k];
+          sl += wgt * lo8[n][k];
         }
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) {
@@ -448,8 +460,8 @@ __device__ __forceinline__ void qproj_body(const QprojArgs& a, int gk, int b, in
         const int i = gk * rph + rb0 + n;
         float* rp = a.rowp + ((size_t)b * g.M_pad + i) * 4;
         rp[0] = LAT == STARKV_LATENT_MIX84 ? rho_s[n] : 1.f;
-        rp[1] = (float)(8 * sh);
-        rp[2] = (float)(8 * sl);
+        rp[1] = (float)sh;
+        rp[2] = (float)sl;
         rp[3] = 0.f;
       }
     }
@@ -479,7 +491,17 @@ __device__ __forceinline__ void qproj_body(const QprojArgs& a, int gk, int b, in
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
             int k = -1;
-            if (P0 < g.K8) {
+            if (g.pack3) {
+              if (P0 < g.K4) {  // outlier nibbles, unpacked as int4 groups
+                const int u = P0 + int4_perm16(e);
+                if (u >= o8 && u < o8 + n8g) k = u - o8;
+              } else if (P0 < g.K4 + g.K3) {  // 3-bit planes: element e holds channel
+                // 8 (e & 3) + (e >> 2) + 4 h of its 32-channel group (unpack_int3_group)
+                const int rel = P0 - g.K4;
+                const int u = (rel & ~31) + 8 * (e & 3) + (e >> 2) + 4 * ((rel >> 4) & 1);
+                if (u >= o4 && u < o4 + (r - n8g)) k = n8g + (u - o4);
+              }
+            } else if (P0 < g.K8) {
               const int slot = P0 + e;
               if (slot >= o8 && slot < o8 + n8g) k = slot - o8;
             } else if (P0 < g.K8 + g.K4) {
@@ -873,7 +895,9 @@ __global__ __launch_bounds__(256) void k_scores(ScoreArgs a) {
 // fragments and key rows) are issued before their MFMAs.  KU = 4 when no column tile has more
 // than six K-tiles (one or two batches per unit); with more K-tiles, KU = 2 (fewer registers,
 // 6 instead of 4 waves per SIMD) was faster on MI355X.
-template <int LAT, int KU>
+// P3: the packed layout (outlier nibbles from position 0, 3-bit planes from K4); a 3-bit lane
+// loads its 32-channel group's three plane words (12 bytes) and unpacks its half.
+template <int LAT, int KU, bool P3 = false>
 __global__ __launch_bounds__(256) void k_scores_chunk(ScoreArgs a) {
   const DecodeGeom& g = a.g;
   const int lane = threadIdx.x & 63, wave = wave_id();
@@ -929,7 +953,8 @@ __global__ __launch_bounds__(256) void k_scores_chunk(ScoreArgs a) {
       for (int jt0 = 0; jt0 < nkt; jt0 += KU) {
         i32x4 fh[KU], fl[KU], av[KU][2];
         u32x4 rk[KU][2];
-        bool is8[KU], is4[KU], hi4[KU];
+        u32x3 r3[P3 ? KU : 1][2];
+        bool is8[KU], is4[KU], hi4[KU], is3[KU], h3[KU];
 #pragma unroll
         for (int j = 0; j < KU; ++j) {
           const bool on = jt0 + j < nkt;
@@ -945,6 +970,13 @@ __global__ __launch_bounds__(256) void k_scores_chunk(ScoreArgs a) {
           const uint32_t ok = is8[j] ? (uint32_t)P0 : (o4 & ~15u);
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt) rk[j][tt] = bld16(krs, ((is8[j] || is4[j]) && tok_ok[tt]) ? trow[tt] + ok : kOOB);
+          is3[j] = P3 && on && P0 >= g.K4 && P0 < g.K4 + g.K3;
+          h3[j] = ((P0 - g.K4) >> 4) & 1;
+          if (P3) {
+            const uint32_t o3 = (uint32_t)(g.K4 / 2 + 12 * ((P0 - g.K4) >> 5));
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) r3[j % (P3 ? KU : 1)][tt] = bld12(krs, (is3[j] && tok_ok[tt]) ? trow[tt] + o3 : kOOB);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);  // every load of the batch ahead of its use
 #pragma unroll
@@ -955,7 +987,8 @@ __global__ __launch_bounds__(256) void k_scores_chunk(ScoreArgs a) {
             av[j][tt] = is8[j] ? __builtin_bit_cast(i32x4, rk[j][tt])
                                : (is4[j] ? unpack_int4_group(hi4[j] ? u32x2{rk[j][tt][2], rk[j][tt][3]}
                                                                     : u32x2{rk[j][tt][0], rk[j][tt][1]})
-                                         : i32x4{0, 0, 0, 0});
+                                         : ((P3 && is3[j]) ? unpack_int3_group(r3[j % (P3 ? KU : 1)][tt], h3[j])
+                                                           : i32x4{0, 0, 0, 0}));
 #pragma unroll
         for (int j = 0; j < KU; ++j)
 #pragma unroll
@@ -1629,6 +1662,10 @@ struct ValueArgs {
   SeqTable seq;
   int cps, bpw, NB, V8, n8v, n4v;
   int n_sl8;  // one-M-tile kernel: slices of one-N-tile blocks (the rest hold int4 blocks)
+  int n_sl4;  // one-M-tile kernel: slices of int4 blocks (packed layout: then 3-bit N-tiles)
+  int NB4;    // end of the int4 blocks (packed layout: the outlier blocks, V4 / 64)
+  int n3t;    // packed layout: 3-bit N-tiles (V3 / 32)
+  int V4;     // packed layout: outlier channels (the 3-bit stream starts at row V4 / 2)
   int n_sl, n_splits;  // one-M-tile kernel: slices per split, splits in all
   ValueOrder vo;       // split of each grid position (vo.n = 0: the kernel's own order)
 };
@@ -1678,10 +1715,26 @@ __device__ __forceinline__ f16x8 deq_i4x8_half(uint32_t w0, uint32_t w1, bool od
                    (__builtin_amdgcn_perm(0u, b, 0x0C030C02u) & 0x000F000Fu) ^ 0x64086408u};
   return __builtin_bit_cast(f16x8, u) - (_Float16)1032.0f;
 }
-// 8 tokens of a channel pair (8 bytes): low nibbles -> even channel, high -> odd channel
+// 8 tokens of one channel of an int4 pair (8 bytes): low nibbles -> even channel, high -> odd channel
 __device__ __forceinline__ void deq_i4x8(uint32_t w0, uint32_t w1, f16x8& ev, f16x8& od) {
   ev = deq_i4x8_half(w0, w1, false);
   od = deq_i4x8_half(w0, w1, true);
+}
+// 8 tokens (byte `by` of the three token-plane words) of one packed 3-bit channel, exactly.
+// The three plane bytes side by side (bits 0-7, 8-15, 16-23) hold tokens 2w and 2w + 1 of the
+// byte at bits w and 4 + w; shifted by w and masked, the six bits multiplied by 0x4081
+// (= 2^14 + 2^7 + 1) land without overlap at 14-16 (field of token 2w) and 18-20 (token
+// 2w + 1).  Each field f = code + 4 becomes the half 0x6400 | f = 1024 + f, minus 1028.
+__device__ __forceinline__ f16x8 deq_i3x8(uint32_t p0, uint32_t p1, uint32_t p2, int by) {
+  const uint32_t sh = 8u * (uint32_t)by;
+  const uint32_t B = ((p0 >> sh) & 0xFFu) | (((p1 >> sh) & 0xFFu) << 8) | (((p2 >> sh) & 0xFFu) << 16);
+  u32x4 u;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t y = __umul24((B >> w) & 0x111111u, 0x4081u);
+    u[w] = 0x64006400u | ((y >> 14) & 7u) | (((y >> 18) & 7u) << 16);
+  }
+  return __builtin_bit_cast(f16x8, u) - (_Float16)1028.0f;
 }
 
 // Workgroup = (slice of `bpw` value blocks, split of one sequence); wave = one value block
@@ -1891,10 +1944,13 @@ struct VTile {
   float cm, cl;
 };
 
-template <int LAT, int NBW, bool IS4>
+// KIND 0: one-N-tile blocks (int8, bf16, fp32 rows); 1: int4 blocks (two N-tiles: even and odd
+// channels); 2: packed 3-bit N-tiles (32 channels of the 3-bit stream; nb0 counts N-tiles).
+template <int LAT, int NBW, int KIND>
 __device__ __forceinline__ void values1_run(const ValueArgs& a, int slice, int sg, int nb0, int nblk,
                                             float* sred, float (*ssum)[32], float (*smx)[32]) {
   using VL = VLayout<LAT>;
+  constexpr bool IS4 = KIND == 1;
   constexpr int NT = IS4 ? 2 * NBW : NBW;  // accumulator tiles
   constexpr int TU = NBW * VL::NV + 2 * VL::NP;  // 16-byte loads per lane per tile
   constexpr int U = TU <= 6 ? 2 : 1;       // tiles per pipeline stage
@@ -1923,6 +1979,20 @@ __device__ __forceinline__ void values1_run(const ValueArgs& a, int slice, int s
   size_t boff[NBW];
 #pragma unroll
   for (int j = 0; j < NBW; ++j) boff[j] = vblock_off(0, nb0 + (j < nblk ? j : 0), 0, g.v_rows, g.T_max, VL::esz);
+  // packed 3-bit N-tiles: the lane's channel k = 32 (nb0 + j) + r has its three words at stream
+  // bytes 12 k + 4 pb, stream byte x in row V4 / 2 + x / 32, column x % 32
+  const uint8_t* vb3 = a.v_tiles + vblock_off(b, 0, 0, g.v_rows, g.T_max, 1);
+  size_t off3[KIND == 2 ? NBW : 1][3];
+  if (KIND == 2) {
+#pragma unroll
+    for (int j = 0; j < (KIND == 2 ? NBW : 1); ++j)
+#pragma unroll
+      for (int pb = 0; pb < 3; ++pb) {
+        const int x = 12 * (32 * (nb0 + (j < nblk ? j : 0)) + r) + 4 * pb;
+        const int row = a.V4 / 2 + (x >> 5);
+        off3[j][pb] = vblock_off(0, row >> 5, 0, g.v_rows, g.T_max, 1) + (size_t)(row & 31) * kTT + (x & 31);
+      }
+  }
 
   f32x16 acc[NT];
 #pragma unroll
@@ -1935,10 +2005,19 @@ __device__ __forceinline__ void values1_run(const ValueArgs& a, int slice, int s
   auto load = [&](VTile<LAT, NBW>& t, int k) {
     const int c = chunk_of(min(k, ntw - 1));
     const uint8_t* tb = vb + (size_t)c * blkb;
+    if (KIND == 2) {
+      const uint8_t* tb3 = vb3 + (size_t)c * blkb;
 #pragma unroll
-    for (int j = 0; j < NBW; ++j)
+      for (int j = 0; j < NBW; ++j)
+        t.v[j][0] = u32x4{*(const uint32_t*)(tb3 + off3[j % (KIND == 2 ? NBW : 1)][0]),
+                          *(const uint32_t*)(tb3 + off3[j % (KIND == 2 ? NBW : 1)][1]),
+                          *(const uint32_t*)(tb3 + off3[j % (KIND == 2 ? NBW : 1)][2]), 0u};
+    } else {
 #pragma unroll
-      for (int x = 0; x < VL::NV; ++x) t.v[j][x] = ld16(tb + boff[j] + 16 * x);
+      for (int j = 0; j < NBW; ++j)
+#pragma unroll
+        for (int x = 0; x < VL::NV; ++x) t.v[j][x] = ld16(tb + boff[j] + 16 * x);
+    }
     const size_t cr = (size_t)(cbase + c) * g.M_pad + prow;
 #pragma unroll
     for (int h = 0; h < 2; ++h)
@@ -2011,7 +2090,9 @@ __device__ __forceinline__ void values1_run(const ValueArgs& a, int slice, int s
 #pragma unroll
         for (int j = 0; j < NBW; ++j) {
           if (j >= nblk) continue;
-          if (!IS4) {
+          if (KIND == 2) {
+            acc[j] = mfma32_f16(ps, deq_i3x8(t.v[j][0][0], t.v[j][0][1], t.v[j][0][2], 2 * q + h), acc[j]);
+          } else if (!IS4) {
             acc[j] = mfma32_f16(ps, deq_i8x8(t.v[j][0][2 * h], t.v[j][0][2 * h + 1]), acc[j]);
           } else {
             f16x8 ev, od;
@@ -2089,13 +2170,18 @@ __device__ __forceinline__ void values1_run(const ValueArgs& a, int slice, int s
     if (t >= ntile) continue;
     int vc;
     bool cok;
-    if (!IS4) {
+    if (KIND == 2) {
+      const int w = (nb0 + t) * 32 + r;  // inlier channel
+      cok = w < a.n4v;
+      vc = a.n8v + w;
+    } else if (!IS4) {
       vc = (nb0 + t) * 32 + r;
       cok = vc < (LAT == STARKV_LATENT_MIX84 ? a.n8v : g.r_v);
     } else {
       const int w = 2 * ((nb0 + t / 2 - a.V8 / 32) * 32 + r) + (t & 1);
-      cok = w < a.n4v;
-      vc = a.n8v + w;
+      // the nibble pairs hold the int4 block, or with the packed layout the outliers
+      cok = w < (g.pack3 ? a.n8v : a.n4v);
+      vc = g.pack3 ? w : a.n8v + w;
     }
 #pragma unroll
     for (int vv = 0; vv < 4; ++vv) {
@@ -2135,13 +2221,17 @@ __global__ __launch_bounds__(256) void k_values1(ValueArgs a) {
   if (pos >= (a.vo.n ? a.vo.n : a.n_splits)) return;
   const int sg = a.vo.n ? a.vo.sg[pos] : pos;
   if (sg == 0xFFFF) return;
-  if (LAT == STARKV_LATENT_MIX84 && slice >= a.n_sl8) {
+  if (LAT == STARKV_LATENT_MIX84 && slice >= a.n_sl8 + a.n_sl4) {
+    // packed layout: two 3-bit N-tiles per slice
+    const int nt0 = (slice - a.n_sl8 - a.n_sl4) * 2;
+    values1_run<LAT, 2, 2>(a, slice, sg, nt0, min(2, a.n3t - nt0), sred, ssum, smx);
+  } else if (LAT == STARKV_LATENT_MIX84 && slice >= a.n_sl8) {
     const int nb0 = a.V8 / 32 + (slice - a.n_sl8) * NBW4;
-    values1_run<LAT, NBW4, true>(a, slice, sg, nb0, min(NBW4, a.NB - nb0), sred, ssum, smx);
+    values1_run<LAT, NBW4, 1>(a, slice, sg, nb0, min(NBW4, a.NB4 - nb0), sred, ssum, smx);
   } else {
     const int nb0 = slice * NBW8;
     const int nbe = LAT == STARKV_LATENT_MIX84 ? a.V8 / 32 : a.NB;
-    values1_run<LAT, NBW8, false>(a, slice, sg, nb0, min(NBW8, nbe - nb0), sred, ssum, smx);
+    values1_run<LAT, NBW8, 0>(a, slice, sg, nb0, min(NBW8, nbe - nb0), sred, ssum, smx);
   }
 }
 
@@ -2952,7 +3042,7 @@ static hipError_t launch_scores_rope(const Layer& L, const ProfScope& ps, dim3 g
 }
 
 bool rope_latent_scores(const Layer& L, int n_q) {
-  return L.G * n_q <= 32 && (L.d_h == 64 || L.d_h == 128);
+  return L.G * n_q <= 32 && (L.d_h == 64 || L.d_h == 128) && !L.pack3;
 }
 
 // Decode of a rotary layer: scores over rebuilt, rotated key tiles, then the latent-space value
@@ -3040,7 +3130,7 @@ hipError_t launch_step(const Layer& L, const starkv_cache& c, const DecodePlan& 
   const DecodeGeom& g = plan.g;
   const int M = g.B * g.n_q;
   const int sw = (M <= 8 && L.d % 64 == 0) ? 8 : ((M <= 16 && L.d % 32 == 0) ? 16 : 0);
-  if (sw == 0 || L.rope_theta > 0.f) {
+  if (sw == 0 || L.rope_theta > 0.f || L.pack3) {
     // many new rows: the tiled append, then the decode
     const hipError_t e = launch_append(L, c, X_new, g.B, g.n_q, lens_pre, s);
     if (e != hipSuccess) return e;
@@ -3088,7 +3178,12 @@ static hipError_t launch_decode_tail(const Layer& L, const DecodePlan& plan, con
       // that each of its four waves has a unit
       // chunks per workgroup: the smallest count that gives the four waves equal numbers of
       // (column tile, chunk) units
-      if (g.nct >= 4 && w.nkt_max <= 8) {
+      if (L.pack3) {
+        sa.nch_wg = 4 / std::gcd(g.nct, 4);
+        const int n_wg = ceil_div(w.total_chunks, sa.nch_wg);
+        if (w.nkt_max <= 6) e = launch_k(ps, k_scores_chunk<STARKV_LATENT_MIX84, 4, true>, dim3(n_wg), dim3(256), s, sa);
+        else e = launch_k(ps, k_scores_chunk<STARKV_LATENT_MIX84, 2, true>, dim3(n_wg), dim3(256), s, sa);
+      } else if (g.nct >= 4 && w.nkt_max <= 8) {
         // many column tiles: column-tile state in registers while walking blocks of chunks
         sa.nch_wg = 32;  // chunks per block (16 waves' worth of column tiles x 16 chunks each)
         const int n_pairs = (g.nct + 1) / 2;
@@ -3131,13 +3226,17 @@ static hipError_t launch_decode_tail(const Layer& L, const DecodePlan& plan, con
   va.n8v = L.n8v;
   va.n4v = L.n4v;
   va.n_sl8 = w.n_sl8;
+  va.n_sl4 = w.n_sl4;
+  va.NB4 = L.pack3 ? L.V4 / 64 : va.NB;
+  va.n3t = L.pack3 ? L.V3 / 32 : 0;
+  va.V4 = L.V4;
   va.vo = plan.vo;
   const int n_pos = plan.vo.n ? plan.vo.n : (w.total_splits + 7) / 8 * 8;
   const int nmt = g.M_pad / 32;
   {
     ProfScope ps("decode_values");
     if (nmt == 1) {
-      va.n_sl = w.n_sl8 + w.n_sl4;
+      va.n_sl = w.n_sl8 + w.n_sl4 + w.n_sl3;
       va.n_splits = w.total_splits;
       const dim3 gv(va.n_sl * n_pos);
       if (L.latent == STARKV_LATENT_MIX84) e = launch_values1<STARKV_LATENT_MIX84>(ps, w.nbw8, w.nbw4, gv, s, va);

@@ -12,6 +12,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 
 #define SKV_LOG2E 1.4426950408889634f
 
@@ -54,6 +55,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uin
 __device__ __forceinline__ u32x4 bld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
+// 12 bytes at a 4-byte aligned offset (zeros past the end, like bld16)
+__device__ __forceinline__ u32x3 bld12(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x3, __builtin_amdgcn_raw_buffer_load_b96(r, (int)off, 0, 0));
+}
 __device__ __forceinline__ u32x2 bld8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
 }
@@ -74,6 +79,19 @@ __device__ __forceinline__ i32x4 unpack_int4_group(u32x2 w) {
   r[1] = (int)(b & 0x0F0F0F0Fu);
   r[2] = (int)((a >> 4) & 0x0F0F0F0Fu);
   r[3] = (int)((b >> 4) & 0x0F0F0F0Fu);
+  return r;
+}
+
+// 16 packed 3-bit fields (offset binary, code + 4) of half h of a 32-channel group given as its
+// three bit-plane words: word k, byte j = the field of channel 8 j + k + 4 h (bit b from plane b)
+__device__ __forceinline__ i32x4 unpack_int3_group(u32x3 p, bool h) {
+  const uint32_t s0 = h ? 4u : 0u;
+  i32x4 r;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t s = s0 + (uint32_t)k;
+    r[k] = (int)(((p.x >> s) & 0x01010101u) | (((p.y >> s) & 0x01010101u) << 1) | (((p.z >> s) & 0x01010101u) << 2));
+  }
   return r;
 }
 

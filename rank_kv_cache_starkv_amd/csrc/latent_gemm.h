@@ -20,6 +20,7 @@ struct GemmArgs {
   int M, d, NS;
   int xmap_rt;          // k_latent_gemm: > 0: row tiles per column tile of an XCD-aware 1-D grid
   int key_slots, K8, V8;
+  int pack3, K4, V4;     // had43p: 3-bit inlier planes from key slot K4 and value slot V4 on
   int qmax_hi, qmax_lo;  // code limits of the int8 and int4 regions
   int n_key, r_v;
   int latent;
@@ -83,13 +84,99 @@ __device__ __forceinline__ int row_pos(const GemmArgs& a, int m) {
 // store does not wait on it); 0 for a padding column.
 __device__ __forceinline__ uint16_t scale_bits(const GemmArgs& a, int chan) { return a.scales[chan >= 0 ? chan : 0]; }
 
+// Packed 3-bit inlier slots (had43p), from the 64 x 64 GEMM tiles' lane layout: lane = slot
+// (the 32 lanes of a half hold 32 consecutive slots of one 32-channel group), rows d32_row(v, q).
+// Fields are code + 4 (padding channels 0).  A key row's group is three words, one bit per
+// channel: three ballots per row, stored by the first lane of each half.  A value channel's
+// tile holds three words over the tile's 32 tokens: the lane merges its consecutive rows of one
+// tile into a mask and sets those bits with atomic AND / OR (other tokens of the word may belong
+// to earlier appends or to other lanes).
+template <int R>
+__device__ __forceinline__ void store_planes3(const GemmArgs& a, int slot, int chan, uint16_t sc_bits, const float* xs,
+                                              const int* ms, const int* ps) {
+  const int lane = threadIdx.x & 63;
+  const bool is_key = slot < a.key_slots;
+  const float sc = chan >= 0 ? f16_to_f32(sc_bits) : 0.f;
+  int fld[R];
+#pragma unroll
+  for (int v = 0; v < R; ++v) {
+    int code = 0;
+    if (sc != 0.f) {
+      const float rq = fminf(fmaxf(__builtin_rintf(xs[v] / sc), -(float)a.qmax_lo), (float)a.qmax_lo);
+      code = (int)rq;
+    }
+    fld[v] = chan >= 0 ? code + 4 : 0;
+  }
+  if (is_key) {
+    const int G = (slot - a.K4) >> 5;  // the wave's group (uniform)
+#pragma unroll
+    for (int v = 0; v < R; ++v) {
+      uint32_t w[3];
+#pragma unroll
+      for (int b = 0; b < 3; ++b) {
+        const uint64_t bal = __builtin_amdgcn_ballot_w64(((fld[v] >> b) & 1) != 0);
+        w[b] = (uint32_t)(bal >> (lane & 32));
+      }
+      const int m = ms[v];
+      if ((lane & 31) != 0 || m >= a.M) continue;
+      const int b = m / a.n_new;
+      uint32_t* row = (uint32_t*)(a.k_rows + ((size_t)b * a.T_max + ps[v]) * a.k_row_bytes + a.K4 / 2 + 12 * G);
+      row[0] = w[0];
+      row[1] = w[1];
+      row[2] = w[2];
+    }
+    return;
+  }
+  if (slot >= a.NS) return;
+  const int k = slot - a.key_slots - a.V4;  // channel of the 3-bit stream
+  const int r3 = a.V4 / 2;                  // first row of the stream
+  int cur_b = -1, cur_tile = -1;
+  uint32_t mask = 0, bits[3] = {0, 0, 0};
+  auto flush = [&]() {
+    if (cur_b < 0) return;
+#pragma unroll
+    for (int pb = 0; pb < 3; ++pb) {
+      const int sb = 12 * k + 4 * pb;  // stream byte of the word
+      const int row = r3 + (sb >> 5);
+      uint32_t* wp = (uint32_t*)(a.v_tiles + vblock_off(cur_b, row >> 5, cur_tile, a.v_rows, a.T_max, 1) + (row & 31) * kTT +
+                                 (sb & 31));
+      atomicAnd(wp, ~mask);
+      atomicOr(wp, bits[pb]);
+    }
+  };
+#pragma unroll
+  for (int v = 0; v < R; ++v) {
+    const int m = ms[v];
+    if (m >= a.M) continue;
+    const int b = m / a.n_new;
+    const int tile = ps[v] / kTT;
+    if (b != cur_b || tile != cur_tile) {
+      flush();
+      cur_b = b;
+      cur_tile = tile;
+      mask = 0;
+      bits[0] = bits[1] = bits[2] = 0;
+    }
+    const uint32_t bit = 1u << token_bit3(ps[v] % kTT);
+    mask |= bit;
+#pragma unroll
+    for (int pb = 0; pb < 3; ++pb) bits[pb] |= ((fld[v] >> pb) & 1) ? bit : 0u;
+  }
+  flush();
+}
+
 template <int R>
 __device__ __forceinline__ void store_latent(const GemmArgs& a, int slot, int chan, uint16_t sc_bits, const float* xs,
                                              const int* ms, const int* ps) {
   const bool is_key = slot < a.key_slots;
+  if (a.pack3 && (is_key ? slot >= a.K4 : slot - a.key_slots >= a.V4)) {
+    store_planes3<R>(a, slot, chan, sc_bits, xs, ms, ps);
+    return;
+  }
   if (a.latent == STARKV_LATENT_MIX84) {
     const bool nib = is_key ? slot >= a.K8 : (slot - a.key_slots) >= a.V8;
-    const int qmax = nib ? a.qmax_lo : a.qmax_hi;
+    // the nibbles hold the low block, or with the packed layout the outlier (high) block
+    const int qmax = (nib && !a.pack3) ? a.qmax_lo : a.qmax_hi;
     const float sc = chan >= 0 ? f16_to_f32(sc_bits) : 0.f;
 #pragma unroll
     for (int v = 0; v < R; ++v) {

@@ -23,7 +23,8 @@ int layer_init(const starkv_layer_desc& d, Layer* L) {
   L->d = d.d;
   L->dtype = d.dtype;
   // the block-rotated quantiser keeps the mix84 byte format (and kernels)
-  L->had = d.latent == STARKV_LATENT_HAD43;
+  L->had = d.latent == STARKV_LATENT_HAD43 || d.latent == STARKV_LATENT_HAD43P;
+  L->pack3 = d.latent == STARKV_LATENT_HAD43P;
   L->latent = L->had ? STARKV_LATENT_MIX84 : d.latent;
   L->qmax_hi = L->had ? 7 : 127;  // 4-bit outlier codes, or int8
   L->qmax_lo = L->had ? 3 : 7;    // 3-bit inlier codes, or int4
@@ -73,19 +74,34 @@ int layer_init(const starkv_layer_desc& d, Layer* L) {
       L->off8[g + 1] = L->off8[g] + L->n8[g];
       L->off4[g + 1] = L->off4[g] + L->n4[g];
     }
-    L->K8 = ceil_to(L->off8[d.H_kv], 16);
-    L->K4 = ceil_to(L->off4[d.H_kv], 32);
-    L->k_row_bytes = L->K8 + L->K4 / 2;
     L->n8v = (L->r_v + den - 1) / den;
     L->n4v = L->r_v - L->n8v;
-    L->V8 = ceil_to(L->n8v, 32);
-    L->V4 = ceil_to(L->n4v, 64);
-    L->v_rows = L->V8 + L->V4 / 2;
+    if (L->pack3) {
+      // outlier nibbles, then inlier bit planes (groups of 32 channels, 12 bytes each)
+      L->K8 = 0;
+      L->K4 = ceil_to(L->off8[d.H_kv], 64);
+      L->K3 = ceil_to(L->off4[d.H_kv], 64);
+      L->k_row_bytes = ceil_to(L->K4 / 2 + 3 * L->K3 / 8, 16);
+      L->V8 = 0;
+      L->V4 = ceil_to(L->n8v, 64);
+      L->V3 = ceil_to(L->n4v, 64);
+      L->v_rows = ceil_to(L->V4 / 2 + 3 * L->V3 / 8, 32);
+      L->key_slots = L->K4 + L->K3;
+      L->val_slots = L->V4 + L->V3;
+      L->key_kpos = L->K4 + L->K3;
+    } else {
+      L->K8 = ceil_to(L->off8[d.H_kv], 16);
+      L->K4 = ceil_to(L->off4[d.H_kv], 32);
+      L->k_row_bytes = L->K8 + L->K4 / 2;
+      L->V8 = ceil_to(L->n8v, 32);
+      L->V4 = ceil_to(L->n4v, 64);
+      L->v_rows = L->V8 + L->V4 / 2;
+      L->key_slots = L->K8 + L->K4;
+      L->val_slots = L->V8 + L->V4;
+      L->key_kpos = L->K8 + L->K4;
+    }
     L->elem = 1;
-    L->key_slots = L->K8 + L->K4;
-    L->val_slots = L->V8 + L->V4;
     L->key_kt = 64;
-    L->key_kpos = L->K8 + L->K4;
   } else {
     L->elem = (L->latent == STARKV_LATENT_F32) ? 4 : 2;
     L->k_row_bytes = ceil_to(L->n_key * L->elem, 16);
@@ -104,7 +120,15 @@ int layer_upload_tables(Layer* L) {
   // padded to a multiple of 16 entries (-1): a 16-slot GEMM tile reads its entries unclamped
   const int NSP = (NS + 15) / 16 * 16;
   std::vector<int> slot_chan(NSP, -1);
-  if (L->mix()) {
+  if (L->pack3) {
+    // key slots: outlier nibbles [0, K4), inlier planes [K4, K4 + K3); value slots likewise
+    for (int g = 0; g < L->H_kv; ++g) {
+      for (int k = 0; k < L->n8[g]; ++k) slot_chan[L->off8[g] + k] = L->koff[g] + k;
+      for (int k = 0; k < L->n4[g]; ++k) slot_chan[L->K4 + L->off4[g] + k] = L->koff[g] + L->n8[g] + k;
+    }
+    for (int k = 0; k < L->n8v; ++k) slot_chan[L->key_slots + k] = L->n_key + k;
+    for (int k = 0; k < L->n4v; ++k) slot_chan[L->key_slots + L->V4 + k] = L->n_key + L->n8v + k;
+  } else if (L->mix()) {
     for (int g = 0; g < L->H_kv; ++g) {
       for (int k = 0; k < L->n8[g]; ++k) slot_chan[L->off8[g] + k] = L->koff[g] + k;
       for (int k = 0; k < L->n4[g]; ++k) slot_chan[L->K8 + L->off4[g] + k] = L->koff[g] + L->n8[g] + k;

@@ -74,6 +74,7 @@ struct DeqArgs {
   HeadTables heads;
   float* xhat;     // [total][n_lat]
   int n_lat, n_key, H_kv, K8, V8, n8v, k_row_bytes, v_rows, T_max;
+  int pack3, K4, V4;  // packed layout: outlier nibbles, then 3-bit planes from K4 / V4
   SeqBases sb;
 };
 
@@ -96,7 +97,14 @@ __global__ __launch_bounds__(256) void k_deq_latent(DeqArgs a) {
           const int g = s >> 16, k = s & 0xFFFF;
           const int n8 = a.heads.n8[g];
           int code;
-          if (k < n8) {
+          if (a.pack3) {
+            if (k < n8) {
+              const int u = a.heads.off8[g] + k;
+              code = snib(row[u >> 1], u & 1);
+            } else {
+              code = key_code3(row, a.K4, a.heads.off4[g] + (k - n8));
+            }
+          } else if (k < n8) {
             code = (int)(int8_t)row[a.heads.off8[g] + k];
           } else {
             const int u = a.heads.off4[g] + (k - n8);
@@ -111,7 +119,17 @@ __global__ __launch_bounds__(256) void k_deq_latent(DeqArgs a) {
         }
       } else {
         const int cv = c - a.n_key;
-        if (LAT == STARKV_LATENT_MIX84) {
+        if (LAT == STARKV_LATENT_MIX84 && a.pack3) {
+          int code;
+          if (cv < a.n8v) {
+            const int byte = a.v_tiles[vblock_off(b, (cv >> 1) >> 5, t / kTT, a.v_rows, a.T_max, 1) +
+                                       ((cv >> 1) & 31) * kTT + t % kTT];
+            code = snib(byte, cv & 1);
+          } else {
+            code = val_code3(a.v_tiles, b, t, cv - a.n8v, a.V4, a.v_rows, a.T_max);
+          }
+          x = (float)code * f16_to_f32(a.scales[c]);
+        } else if (LAT == STARKV_LATENT_MIX84) {
           const bool i4 = cv >= a.n8v;
           const int w = cv - a.n8v;
           const int vr = i4 ? a.V8 + (w >> 1) : cv;
@@ -488,6 +506,9 @@ hipError_t launch_prefill(const Layer& L, const starkv_cache& c, const void* q, 
   da.n_key = L.n_key;
   da.H_kv = L.H_kv;
   da.K8 = L.K8;
+  da.pack3 = L.pack3;
+  da.K4 = L.K4;
+  da.V4 = L.V4;
   da.V8 = L.V8;
   da.n8v = L.n8v;
   da.k_row_bytes = L.k_row_bytes;

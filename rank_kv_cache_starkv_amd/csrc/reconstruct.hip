@@ -20,6 +20,7 @@ struct ReconArgs {
   void* V_out;
   int b, t0, t1, T_max;
   int H_kv, d_h, n_key, r_v, n8v, K8, V8, k_row_bytes, v_rows, latent, dtype;
+  int pack3, K4, V4;  // packed layout: outlier nibbles, then 3-bit planes from K4 / V4
 };
 
 template <int DT>
@@ -47,7 +48,14 @@ __global__ __launch_bounds__(256) void k_reconstruct(ReconArgs a) {
       if (c < a.n_key) {
         const int g = find_segment(a.koff, a.H_kv, c);
         const int k = c - a.koff[g];
-        if (k < a.n8[g]) {
+        if (a.pack3) {
+          if (k < a.n8[g]) {
+            const int u = a.off8[g] + k;
+            code = snib(row[u / 2], u & 1);
+          } else {
+            code = key_code3(row, a.K4, a.off4[g] + (k - a.n8[g]));
+          }
+        } else if (k < a.n8[g]) {
           code = (int)(int8_t)row[a.off8[g] + k];
         } else {
           const int u = a.off4[g] + (k - a.n8[g]);
@@ -55,7 +63,9 @@ __global__ __launch_bounds__(256) void k_reconstruct(ReconArgs a) {
         }
       } else {
         const int k = c - a.n_key;
-        if (k < a.n8v) {
+        if (a.pack3) {
+          code = k < a.n8v ? snib(*vcell(k / 2), k & 1) : val_code3(a.v_tiles, a.b, t, k - a.n8v, a.V4, a.v_rows, a.T_max);
+        } else if (k < a.n8v) {
           code = (int)(int8_t)*vcell(k);
         } else {
           const int w = k - a.n8v;
@@ -115,6 +125,9 @@ hipError_t launch_reconstruct(const Layer& L, const starkv_cache& c, int b, int 
   a.r_v = L.r_v;
   a.n8v = L.n8v;
   a.K8 = L.K8;
+  a.pack3 = L.pack3;
+  a.K4 = L.K4;
+  a.V4 = L.V4;
   a.V8 = L.V8;
   a.k_row_bytes = L.k_row_bytes;
   a.v_rows = L.v_rows;

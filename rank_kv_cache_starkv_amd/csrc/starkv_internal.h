@@ -26,6 +26,33 @@ __host__ __device__ __forceinline__ size_t vblock_off(int b, int rb, int tile, i
   return (((size_t)b * (v_rows / 32) + rb) * (size_t)(T_max / kTT) + tile) * (size_t)(32 * kTT * esz);
 }
 
+#ifdef __HIPCC__
+// Packed 3-bit layout (had43p): bit of token t (0..31) in a value plane word
+__host__ __device__ __forceinline__ int token_bit3(int t) { return 8 * (t >> 3) + 4 * (t & 1) + ((t >> 1) & 3); }
+// code of inlier channel u (head-major) of a key row: group u / 32 after the K4 / 2 nibble bytes,
+// bit u % 32 of its three plane words
+__device__ __forceinline__ int key_code3(const uint8_t* row, int K4, int u) {
+  const uint32_t* w = (const uint32_t*)(row + K4 / 2 + 12 * (u >> 5));
+  const int j = u & 31;
+  return (int)(((w[0] >> j) & 1u) | (((w[1] >> j) & 1u) << 1) | (((w[2] >> j) & 1u) << 2)) - 4;
+}
+// code of inlier value channel w of token t of sequence b: plane words at stream bytes
+// 12 w + 4 pb of the token's tile, stream byte x in row V4 / 2 + x / 32, column x % 32
+__device__ __forceinline__ int val_code3(const uint8_t* v_tiles, int b, int t, int w, int V4, int v_rows, int T_max) {
+  int f = 0;
+  const int bit = token_bit3(t % kTT);
+#pragma unroll
+  for (int pb = 0; pb < 3; ++pb) {
+    const int x = 12 * w + 4 * pb;
+    const int row = V4 / 2 + (x >> 5);
+    const uint32_t word =
+        *(const uint32_t*)(v_tiles + vblock_off(b, row >> 5, t / kTT, v_rows, T_max, 1) + (row & 31) * kTT + (x & 31));
+    f |= (int)((word >> bit) & 1u) << pb;
+  }
+  return f - 4;
+}
+#endif
+
 // Per-KV-head tables on the device (int32 each, H_kv entries unless noted).
 struct HeadTables {
   const int* koff;   // [H_kv + 1] first natural key channel of head g
@@ -51,6 +78,12 @@ struct Layer {
   // so `latent` is MIX84 and this flag selects the outlier split, the code limits and the
   // rotated factors
   int had = 0;
+  // had43p: the same codes packed to their widths -- outliers in the K4 / V4 nibble regions (no
+  // int8 region: K8 = V8 = 0), inliers as 3-bit bit planes in K3 / V3 channels; n8 / n8v count
+  // the outliers and n4 / n4v the inliers, off8 is a head's first outlier nibble and off4 its
+  // first inlier channel
+  int pack3 = 0;
+  int K3 = 0, V3 = 0;
   int qmax_hi = 127, qmax_lo = 7;  // code limits of the int8 and int4 regions
   // rotary position embedding of the reconstructed keys and of the queries (0: none)
   float rope_theta = 0.f;
@@ -88,6 +121,7 @@ struct Layer {
 struct DecodeGeom {
   int B, n_q, M_q, M_pad, nct, G, d_h, H_q, H_kv, d;
   int n_key, r_v, K8, K4, key_kt, key_kpos, k_row_bytes, v_rows, v_tile_bytes, T_max;
+  int K3, pack3;  // packed 3-bit key region (channels) and the packed-layout flag
   int rv_ld;  // row stride (elements) of the value-latent workspace rows: r_v rounded up to 32
   int latent, dtype;
   float qscale;  // log2(e) / sqrt(d_h)
@@ -138,6 +172,7 @@ struct DecodeWs {
   int cps;          // score chunks per value split
   int blocks_per_wg;  // value blocks (waves) per value WG (several query-row tiles)
   int n_sl8, n_sl4;   // one-row-tile value kernel: slices of one-N-tile blocks / of int4 blocks
+  int n_sl3;          // ... and (packed layout) slices of two 3-bit N-tiles
   int nbw8, nbw4;     // blocks per slice of each kind
   int n_grp;          // many-row value kernel: groups of four 32-channel N-tiles
 };

@@ -68,7 +68,8 @@ class Workload:
     d_h: int
     d: int
     n_q: int
-    latent: str  # "f32", "bf16", "mix84" (int8 lead / int4 rest) or "had43" (rotated 4-bit / 3-bit)
+    latent: str  # "f32", "bf16", "mix84" (int8 lead / int4 rest), "had43" (rotated 4-bit / 3-bit) or
+    #              "had43p" (the same codes packed to 4 / 3 bits)
     dtype: str  # "f32" or "bf16": X, q, factors, out
     p: float  # spectrum exponent: sigma_i = i^-p
     r_v: int  # value latent rank (joint decomposition)
@@ -95,7 +96,8 @@ class Workload:
 # a 4K context (the LongBench/RULER length), a GQA layer at long context, and a
 # high-batch 13B-class serving step with a speculative-style chunk of 4 queries.
 # Workload 5 is the 7B-class quantised layer with the block-rotated 4-bit/3-bit
-# quantiser instead of the int8/int4 split.
+# quantiser instead of the int8/int4 split; workload 6 is the same layer with those
+# codes packed to their own widths (3.2 bits per channel).
 WORKLOADS: Dict[int, Workload] = {
     0: Workload(0, "tiny-f32", B=1, H_q=4, H_kv=4, d_h=64, d=256, n_q=1, latent="f32", dtype="f32",
                 p=0.7, r_v=64, key_ranks=(16, 24, 32, 16), T=256),
@@ -113,6 +115,9 @@ WORKLOADS: Dict[int, Workload] = {
                 T_lo=1024, T_hi=8192, n_cal=512, n_append=4),
     5: Workload(5, "llama2-7b-had43", B=8, H_q=32, H_kv=32, d_h=128, d=4096, n_q=1,
                 latent="had43", dtype="bf16", p=0.5, r_v=1024, rank_lo=16, rank_hi=64, rank_sum=1024,
+                T=4096, n_cal=512, n_append=128),
+    6: Workload(6, "llama2-7b-had43p", B=8, H_q=32, H_kv=32, d_h=128, d=4096, n_q=1,
+                latent="had43p", dtype="bf16", p=0.5, r_v=1024, rank_lo=16, rank_hi=64, rank_sum=1024,
                 T=4096, n_cal=512, n_append=128),
 }
 

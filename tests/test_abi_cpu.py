@@ -53,7 +53,7 @@ def _layer(cfg, **kw):
     return w, S.Layer(**args), ranks
 
 
-@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, 5])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, 5, 6])
 def test_ranks_and_layout_match_oracle(cfg):
     w, layer, ranks = _layer(cfg)
     s_k, tau_k, s_v, tau_v, _ = I.layer_spectra(w)
@@ -69,6 +69,7 @@ def test_ranks_and_layout_match_oracle(cfg):
     assert inf["latent"] == S.LATENT[w.latent]
     if O.is_quantized(w.latent):
         assert (inf["K8"], inf["K4"], inf["V8"], inf["V4"]) == (fmt.K8, fmt.K4, fmt.V8, fmt.V4)
+        assert (inf["K3"], inf["V3"]) == (fmt.K3, fmt.V3)
     kb, vb = layer.cache_bytes(w.B, 4096)
     assert kb == w.B * 4096 * fmt.k_row_bytes and vb == w.B * 128 * fmt.v_tile_bytes
     # one sequence's key rows must stay addressable by 32-bit buffer offsets
@@ -155,7 +156,7 @@ def test_hot_calls_reject_bad_arguments_without_launching():
     layer.close()
 
 
-@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, 5])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, 5, 6])
 def test_workspace_sizing(cfg):
     w, layer, _ = _layer(cfg)
     lens = I.context_lengths(w) + w.n_append
@@ -166,6 +167,24 @@ def test_workspace_sizing(cfg):
     assert n >= chunks * M_pad * 64 * esz  # the probability buffer alone
     assert n % 256 == 0
     layer.close()
+
+
+def test_packed_layout_limits():
+    """The packed 4-bit/3-bit layout (had43p) decodes with one value tile of at most 32 query rows
+    per sequence: more rows are refused with EUNSUPPORTED before anything runs; d must be a
+    multiple of 64."""
+    w, layer, _ = _layer(6)
+    lens = [100, 33]
+    assert layer.workspace_bytes(2, 1, lens) > 0  # 32 query rows
+    with pytest.raises(S.StarKVError) as ei:
+        layer.workspace_bytes(2, 2, lens)  # 64 query rows
+    assert ei.value.status == -4
+    layer.close()
+    s_k, tau_k, s_v, tau_v, _ = I.layer_spectra(w)
+    with pytest.raises(S.StarKVError) as ei:
+        S.Layer(H_q=w.H_q, H_kv=w.H_kv, d_h=w.d_h, d=w.d - 32, dtype="bf16", latent="had43p", s_k=s_k, tau_k=tau_k,
+                s_v=s_v[: w.d - 32], tau_v=tau_v)
+    assert ei.value.status == -4
 
 
 def test_create_rejects_ascending_spectra():

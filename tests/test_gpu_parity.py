@@ -24,7 +24,7 @@ else:  # collected on CPU-only machines but never run there (marked gpu)
 
 # ---------------------------------------------------------------- factors and ranks, full shapes
 
-@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, 5])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, 5, 6])
 def test_ranks_and_factor_bits(cfg):
     w = I.WORKLOADS[cfg]
     H.log(f"[factors] cfg={cfg} {w.name}")
@@ -42,7 +42,7 @@ def test_ranks_and_factor_bits(cfg):
 
 def mini(cfg):
     w = I.WORKLOADS[cfg]
-    lens = {0: [256], 1: [300, 129], 2: [250, 70], 3: [1000], 4: [100, 33, 257], 5: [250, 70]}[cfg]
+    lens = {0: [256], 1: [300, 129], 2: [250, 70], 3: [1000], 4: [100, 33, 257], 5: [250, 70], 6: [250, 70]}[cfg]
     return w, lens
 
 
@@ -64,7 +64,22 @@ def _compare_cache(run, exact):
         gk, gv = H.gpu_seq_cache(run, b)
         ok, ov = H.oracle_seq_bytes(run, b)
         T = int(run.lens[b])
-        if exact:
+        if exact and run.fmt.packed:
+            # packed layout: the row bytes the format defines (not the row padding), the outlier
+            # nibble rows at the columns of tokens < T, and the 3-bit stream's plane words at the
+            # bits of tokens < T (a word also holds the tile's later tokens)
+            fmt = run.fmt
+            used = fmt.K4 // 2 + 3 * fmt.K3 // 8
+            np.testing.assert_array_equal(gk[:, :used], ok[:, :used])
+            r3 = fmt.V4 // 2
+            for t in range(0, T, O.TT):
+                n = min(O.TT, T - t)
+                np.testing.assert_array_equal(gv[t // O.TT, :r3, :n], ov[t // O.TT, :r3, :n])
+                words = [np.ascontiguousarray(x[t // O.TT].reshape(-1)[r3 * O.TT: r3 * O.TT + 12 * fmt.V3]).view("<u4")
+                         for x in (gv, ov)]
+                mask = np.uint32(sum(1 << O.token_bit3(j) for j in range(n)))
+                np.testing.assert_array_equal(words[0] & mask, words[1] & mask)
+        elif exact:
             np.testing.assert_array_equal(gk, ok)
             # value tiles: compare the columns of tokens < T only
             for t in range(0, T, O.TT):
@@ -83,7 +98,7 @@ def _compare_cache(run, exact):
                 np.testing.assert_allclose(vc, ovc, rtol=tol, atol=tol * np.abs(ovc).max())
 
 
-@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, 5])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, 5, 6])
 @pytest.mark.parametrize("exact", [True, False])
 def test_mini_parity(cfg, exact):
     w, run = _run_mini(cfg, exact)
@@ -99,7 +114,7 @@ def test_mini_parity(cfg, exact):
         H.check_output(w, got[b], ref, f"seq {b} len {int(run.lens[b])}")
 
 
-@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, 5])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, 5, 6])
 def test_absorbed_query_from_hidden(cfg):
     """Decode with the query taken from hidden states through the absorbed factors W_q^h B_g^T,
     against the oracle's q = x W_q followed by the same attention (at most 16 hidden rows: the
@@ -174,7 +189,7 @@ def test_absorbed_query_gemm_forms(form):
         H.check_output(w, got[b], ref, f"{form} seq {b} len {int(run.lens[b])}")
 
 
-@pytest.mark.parametrize("cfg", [0, 2, 4, 5])
+@pytest.mark.parametrize("cfg", [0, 2, 4, 5, 6])
 @pytest.mark.parametrize("q_scale", [30.0, 300.0])
 def test_mini_softmax_stress(cfg, q_scale):
     w, run = _run_mini(cfg, exact=True)
@@ -184,7 +199,7 @@ def test_mini_softmax_stress(cfg, q_scale):
         H.check_output(w, got[b], H.oracle_decode(run, q, b), f"q x{q_scale} seq {b}")
 
 
-@pytest.mark.parametrize("cfg", [0, 1, 2, 5])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 5, 6])
 def test_reconstruct(cfg):
     w, run = _run_mini(cfg, exact=True)
     b = 0
@@ -259,7 +274,7 @@ def _full(cfg):
     return w, run
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5, 6])
 def test_full_size_sampled(cfg):
     w, run = _full(cfg)
     _compare_cache(run, True)
@@ -307,7 +322,7 @@ def test_graph_replay_matches_eager():
         torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("cfg", [0, 1, 2, 5])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 5, 6])
 @pytest.mark.parametrize("n_new", [1, 2])
 def test_append_few_tokens(cfg, n_new):
     """Appends of one or two tokens per sequence (the per-step append) on top of a prefill:
@@ -328,7 +343,8 @@ def test_append_few_tokens(cfg, n_new):
 # ---------------------------------------------------------------- the fused decode step
 
 @pytest.mark.parametrize("cfg,lens0", [(0, [256]), (1, [300, 129]), (2, [250, 70]), (3, [700]),
-                                       (4, [100, 33, 257]), (4, [100, 33, 257, 64, 90]), (5, [250, 70])])
+                                       (4, [100, 33, 257]), (4, [100, 33, 257, 64, 90]), (5, [250, 70]),
+                                       (6, [250, 70])])
 def test_decode_step_equals_append_then_decode(cfg, lens0):
     """starkv_decode_step leaves the cache bytes and gives the output of compress_append followed
     by decode_attention, bit for bit: one fused launch for up to 16 new rows (cfg 0-3, and cfg 4

@@ -21,7 +21,7 @@ if torch.cuda.is_available():
 else:  # collected on CPU-only machines but never run there (marked gpu)
     H = None
 
-MINI = {1: [300, 129], 2: [250, 70], 3: [1000], 4: [100, 33, 257], 5: [250, 70]}
+MINI = {1: [300, 129], 2: [250, 70], 3: [1000], 4: [100, 33, 257], 5: [250, 70], 6: [250, 70]}
 
 
 def _setup(cfg, lens0, n_q=None, exact=True):
@@ -36,7 +36,7 @@ def _setup(cfg, lens0, n_q=None, exact=True):
     return w, run
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 5])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 5, 6])
 @pytest.mark.parametrize("chunk", ["whole", "ragged"])
 def test_prefill_chunk_parity(cfg, chunk):
     """A chunk of queries at the end of every sequence: the whole shortest sequence (every one
@@ -57,7 +57,7 @@ def test_prefill_chunk_parity(cfg, chunk):
         H.check_output(wq, got[b], ref, f"prefill seq {b} len {int(run.lens[b])} n_q {n_q}")
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5, 6])
 def test_rotary_decode_parity(cfg):
     """A rotary layer's decode (scores over key tiles rebuilt from the latent and rotated, values in
     the latent space) and its fused step against the oracle's rotated reconstruct-then-attend."""
