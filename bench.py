@@ -55,7 +55,7 @@ def to_dev_bf16(x: np.ndarray, dev: str):
 
 
 # quantised latents: the denominator of the high-precision share (int8 region) of a segment
-QUANTIZED = {"mix84": 4, "had43": 5}
+QUANTIZED = {"mix84": 4, "had43": 5, "had43p": 5}
 
 
 def algorithmic_bytes(w, ranks, r_v, lens, n_q, hidden=False):
@@ -65,12 +65,14 @@ def algorithmic_bytes(w, ranks, r_v, lens, n_q, hidden=False):
     projection then reads instead of q and B_k."""
     elem = {"f32": 4, "bf16": 2}[w.dtype]
     if w.latent in QUANTIZED:
-        # bytes of the int8 region (leading quarter, or the outlier fifth) + the int4 region
+        # bytes of the int8 region (leading quarter, or the outlier fifth) + the int4 region;
+        # packed (had43p): 4-bit outliers + 3-bit inliers
         den = QUANTIZED[w.latent]
         n8 = [-(-int(r) // den) for r in ranks]
-        key_tok = sum(n8) + (sum(int(r) for r in ranks) - sum(n8)) / 2.0
         n8v = -(-r_v // den)
-        val_tok = n8v + (r_v - n8v) / 2.0
+        hi_b, lo_b = (0.5, 3.0 / 8.0) if w.latent == "had43p" else (1.0, 0.5)
+        key_tok = hi_b * sum(n8) + lo_b * (sum(int(r) for r in ranks) - sum(n8))
+        val_tok = hi_b * n8v + lo_b * (r_v - n8v)
         scale_k, scale_v = 2 * int(sum(ranks)), 2 * r_v
     else:
         le = 4 if w.latent == "f32" else 2
@@ -444,7 +446,8 @@ def measure(w, args, dev, with_cpu: bool, steps: int, warmup: int) -> dict:
                    "query": "hidden states, absorbed W_q B_g^T" if args.hidden_query else "q",
                    "rope_theta": args.rope or None},
         "dtype": {"f32": "f32", "bf16": "bf16", "mix84": "int8/int4 codes, f16 MFMA, fp32 accumulate",
-                  "had43": "4-bit/3-bit codes in int8/int4 bytes, f16 MFMA, fp32 accumulate"}[w.latent],
+                  "had43": "4-bit/3-bit codes in int8/int4 bytes, f16 MFMA, fp32 accumulate",
+                  "had43p": "4-bit/3-bit codes packed (3.2 bits), f16 MFMA, fp32 accumulate"}[w.latent],
         "roofline": ({"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": 2500.0, "unit": "TFLOP/s",
                       "frac": achieved / 2500.0, "traffic": None, "alg_flops_per_launch": ab[dom],
                       "us_per_launch": kern_us[dom]} if recon else
@@ -576,7 +579,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=4,
-                    help="workload id (0-5); 4 (the 13B-class ragged high-batch step) is the headline")
+                    help="workload id (0-6); 4 (the 13B-class ragged high-batch step) is the headline")
     ap.add_argument("--layers", type=int, default=0, help="layers to rotate (0: enough for 1 GiB)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-sub", action="store_true", help="skip the other workloads' sub-results")
