@@ -1111,12 +1111,11 @@ __global__ __launch_bounds__(256) void k_scores_chunk(ScoreArgs a) {
 // XCD (grid position mod 8), so the key rows they share are fetched into one L2.  A wave keeps
 // its column tile's query fragments, the per-lane key-row offsets of its K-tiles and its row's
 // parameters in registers while it walks its chunks (the fragments and parameters are reloaded
-// only when a chunk starts another sequence) and issues the key loads of its next chunk before the
-// MFMAs of the current one.  Used when there are at least four column tiles to share the key rows
+// only when a chunk starts another sequence), with the key loads of its next NS chunks in flight.  Used when there are at least four column tiles to share the key rows
 // (with two, the per-unit kernel above was faster on MI355X).  The two int8 query parts are combined in integers
 // (254 hi + lo, minus the int4 offset bias) before one conversion.  Output as k_scores_chunk.
-template <int KTM>
-__global__ __launch_bounds__(256) void k_scores_mix(ScoreArgs a) {
+template <int KTM, int NS = (KTM <= 6 ? 3 : 2)>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_scores_mix(ScoreArgs a) {
   const int CPB = a.nch_wg;  // chunks per block
   const DecodeGeom& g = a.g;
   const int lane = threadIdx.x & 63, wave = wave_id();
@@ -1151,12 +1150,24 @@ __global__ __launch_bounds__(256) void k_scores_mix(ScoreArgs a) {
   const int jq = i % g.n_q;
   const uint32_t rb = (uint32_t)g.k_row_bytes;
 
-  // key loads of chunk c (sequence bb) into kr
-  auto issue = [&](u32x4 kr[KTM][2], int bb, int c) {
+  // Loads of the wave's chunks go out NS steps ahead of their use, into NS register sets that
+  // take turns (no copies between them, so each wait covers only the set about to be used).
+  // The issue side keeps its own chunk and sequence; past the wave's last chunk it issues loads
+  // at kOOB that return zeros without touching memory.
+  int ci = c_first;
+  int bi = seq_of_chunk(a.seq, g.B, c_first);
+  int bi_end = seq_chunk0(a.seq, bi + 1);
+  auto issue = [&](u32x4 kr[KTM][2]) {
+    const bool live = ci < c_end;  // wave-uniform
+    if (live)
+      while (ci >= bi_end) {
+        ++bi;
+        bi_end = seq_chunk0(a.seq, bi + 1);
+      }
     const __amdgpu_buffer_rsrc_t krs =
-        buf_rsrc(a.k_rows + (size_t)bb * g.T_max * g.k_row_bytes, (uint32_t)g.T_max * rb);
-    const int t0 = (c - seq_chunk0(a.seq, bb)) * kTC;
-    const int ln = seq_len(a.seq, bb);
+        buf_rsrc(a.k_rows + (size_t)bi * g.T_max * g.k_row_bytes, (uint32_t)g.T_max * rb);
+    const int t0 = (ci - seq_chunk0(a.seq, bi)) * kTC;
+    const int ln = live ? seq_len(a.seq, bi) : 0;
 #pragma unroll
     for (int jt = 0; jt < KTM; ++jt)
 #pragma unroll
@@ -1164,6 +1175,7 @@ __global__ __launch_bounds__(256) void k_scores_mix(ScoreArgs a) {
         const int tok = t0 + tt * 16 + n;
         kr[jt][tt] = bld16(krs, (kofs[jt] != kOOB && tok < ln) ? (uint32_t)tok * rb + kofs[jt] : kOOB);
       }
+    ci += 2;
   };
   // query fragments and row parameters of sequence bb
   i32x4 fh[KTM], fl[KTM];
@@ -1181,19 +1193,23 @@ __global__ __launch_bounds__(256) void k_scores_mix(ScoreArgs a) {
     rs = __uint_as_float(rp[0]) * (1.f / 254.f);
     ibias = 254 * (int)__uint_as_float(rp[1]) + (int)__uint_as_float(rp[2]);
   };
-  int b = seq_of_chunk(a.seq, g.B, c_first);
-  load_seq(b);
-  u32x4 kr[KTM][2];
-  issue(kr, b, c_first);
-
-  for (int c = c_first; c < c_end; c += 2) {
-    const int cn = c + 2;
-    int bn = b;
-    if (cn < c_end)
-      while (cn >= seq_chunk0(a.seq, bn + 1)) ++bn;
-    u32x4 kn[KTM][2];
-    if (cn < c_end) issue(kn, bn, cn);  // the next chunk's keys go out before these MFMAs
-    // scores of chunk c (sequence b): lane holds tokens 16 tt + 4 qq + v of row i
+  // compute side: chunk cc of sequence bc (fragments of sequence bf loaded)
+  int cc = c_first;
+  int bc = bi, bf = -1;
+  int bc0 = seq_chunk0(a.seq, bc), bc_end = bi_end, bc_len = seq_len(a.seq, bc);
+  auto step = [&](const u32x4 kr[KTM][2]) {
+    while (cc >= bc_end) {
+      ++bc;
+      bc0 = bc_end;
+      bc_end = seq_chunk0(a.seq, bc + 1);
+      bc_len = seq_len(a.seq, bc);
+    }
+    if (bc != bf) {  // the block reaches another sequence (rare): its fragments first
+      bf = bc;
+      load_seq(bc);
+      vm_wait<0>();  // so that no later wait counts the fragments as still in flight
+    }
+    // scores of chunk cc: lane holds tokens 16 tt + 4 qq + v of row i
     i32x4 ah[2], al[2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) ah[tt] = al[tt] = i32x4{0, 0, 0, 0};
@@ -1210,9 +1226,8 @@ __global__ __launch_bounds__(256) void k_scores_mix(ScoreArgs a) {
         }
       }
     }
-    const int t0 = (c - seq_chunk0(a.seq, b)) * kTC;
-    const int len = seq_len(a.seq, b);
-    const int lim = rowvalid ? len - g.n_q + jq : -1;  // last token this row sees
+    const int t0 = (cc - bc0) * kTC;
+    const int lim = rowvalid ? bc_len - g.n_q + jq : -1;  // last token this row sees
     float s2[2][4];
     float m = -INFINITY;
 #pragma unroll
@@ -1225,14 +1240,16 @@ __global__ __launch_bounds__(256) void k_scores_mix(ScoreArgs a) {
       }
     m = wave_max_xor(m, 16);
     m = wave_max_xor(m, 32);
+    // exp2(-inf - m) is 0; a row with no visible token keeps m = -inf and takes 0 for reference
+    const float mref = m == -INFINITY ? 0.f : m;
     float l = 0.f;
-    const size_t prow = ((size_t)c * g.M_pad + i) * kTC;
+    const size_t prow = ((size_t)cc * g.M_pad + i) * kTC;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       float e4[4];
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        e4[v] = (s2[tt][v] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s2[tt][v] - m);
+        e4[v] = __builtin_amdgcn_exp2f(s2[tt][v] - mref);
         l += e4[v];
       }
       const uint32_t w0 = (uint32_t)f32_to_f16(e4[0]) | ((uint32_t)f32_to_f16(e4[1]) << 16);
@@ -1241,21 +1258,43 @@ __global__ __launch_bounds__(256) void k_scores_mix(ScoreArgs a) {
     }
     l = wave_sum_xor(l, 16);
     l = wave_sum_xor(l, 32);
-    if (qq == 0) {
-      a.cm[(size_t)c * g.M_pad + i] = m;
-      a.cl[(size_t)c * g.M_pad + i] = l;
+    // the four lanes of a row hold the same m and l: all store them (one store per wave, no branch)
+    a.cm[(size_t)cc * g.M_pad + i] = m;
+    a.cl[(size_t)cc * g.M_pad + i] = l;
+    cc += 2;
+  };
+
+  const int n_mine = (c_end - c_first + 1) / 2;  // chunks c_first, c_first + 2, ... below c_end
+  if (NS == 3) {
+    u32x4 k0[KTM][2], k1[KTM][2], k2[KTM][2];
+    issue(k0);
+    issue(k1);
+    issue(k2);
+    int k = 0;
+    for (; k + 3 <= n_mine; k += 3) {
+      step(k0);
+      issue(k0);
+      step(k1);
+      issue(k1);
+      step(k2);
+      issue(k2);
     }
-    if (cn < c_end) {
-      if (bn != b) {
-        b = bn;
-        load_seq(b);
-      }
-#pragma unroll
-      for (int jt = 0; jt < KTM; ++jt)
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) kr[jt][tt] = kn[jt][tt];
+    if (k < n_mine) step(k0);
+    if (k + 1 < n_mine) step(k1);
+  } else {
+    u32x4 k0[KTM][2], k1[KTM][2];
+    issue(k0);
+    issue(k1);
+    int k = 0;
+    for (; k + 2 <= n_mine; k += 2) {
+      step(k0);
+      issue(k0);
+      step(k1);
+      issue(k1);
     }
+    if (k < n_mine) step(k0);
   }
+  vm_wait<0>();  // the trailing loads (at kOOB) have returned before the wave ends
 }
 
 // Key scores of a rotary layer (keys rotated by position after the key projection): the rotation
