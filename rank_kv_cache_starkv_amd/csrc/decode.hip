@@ -1128,12 +1128,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   const int c_end = min(blk * CPB + CPB, a.total_chunks);
   if (ct >= g.nct || c_first >= c_end) return;  // wave-uniform; the kernel has no barrier
 
-  // K-tiles of the column tile: per-lane byte offset of the lane's 16 bytes in a key row (kOOB
-  // when unused), int8 or int4, and which half of an int4 group's 16 bytes holds the lane's codes
+  // K-tiles of the column tile: per-lane byte offset in a key row of the lane's 16 int8 codes,
+  // or of the 8 bytes that hold its 16 int4 codes (a 16-byte load from there: the lane uses the
+  // first half), or 2^31 when the lane has no codes in the K-tile: past the end of the buffer
+  // (zeros, no memory traffic) whenever a sequence's key rows span less than 2 GiB, and in any
+  // case harmless (an unused K-tile is skipped; a padding lane meets a zero query fragment).
   const int nkt = a.kts.n[ct];
   const int ks0 = a.kts.s0[ct], kn0 = a.kts.n0[ct], ks1 = a.kts.s1[ct];
   uint32_t kofs[KTM];
-  bool k8[KTM], khi[KTM];
+  bool k8[KTM];
 #pragma unroll
   for (int jt = 0; jt < KTM; ++jt) {
     const int kt = jt < kn0 ? ks0 + jt : ks1 + (jt - kn0);
@@ -1142,18 +1145,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     k8[jt] = on && P0 < g.K8;
     const bool i4 = on && P0 >= g.K8 && P0 < g.K8 + g.K4;
     const uint32_t o4 = (uint32_t)(g.K8 + (P0 - g.K8) / 2);
-    khi[jt] = (o4 & 8u) != 0;
-    kofs[jt] = k8[jt] ? (uint32_t)P0 : (i4 ? (o4 & ~15u) : kOOB);
+    kofs[jt] = k8[jt] ? (uint32_t)P0 : (i4 ? o4 : 0x80000000u);
   }
   const int i = ct * 16 + n;
   const bool rowvalid = i < g.M_q;
+  // every row of the column tile is a query row: tokens need masking only near the end
+  const bool tile_full = (ct + 1) * 16 <= g.M_q;
   const int jq = i % g.n_q;
   const uint32_t rb = (uint32_t)g.k_row_bytes;
 
   // Loads of the wave's chunks go out NS steps ahead of their use, into NS register sets that
   // take turns (no copies between them, so each wait covers only the set about to be used).
-  // The issue side keeps its own chunk and sequence; past the wave's last chunk it issues loads
-  // at kOOB that return zeros without touching memory.
+  // The issue side keeps its own chunk and sequence; past the wave's last chunk its buffer is
+  // empty, so those loads return zeros without touching memory.  Tokens past the length (in the
+  // last chunk of a sequence) load whatever the row holds and are masked in the scores.
   int ci = c_first;
   int bi = seq_of_chunk(a.seq, g.B, c_first);
   int bi_end = seq_chunk0(a.seq, bi + 1);
@@ -1165,16 +1170,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         bi_end = seq_chunk0(a.seq, bi + 1);
       }
     const __amdgpu_buffer_rsrc_t krs =
-        buf_rsrc(a.k_rows + (size_t)bi * g.T_max * g.k_row_bytes, (uint32_t)g.T_max * rb);
-    const int t0 = (ci - seq_chunk0(a.seq, bi)) * kTC;
-    const int ln = live ? seq_len(a.seq, bi) : 0;
+        buf_rsrc(a.k_rows + (size_t)bi * g.T_max * g.k_row_bytes, live ? (uint32_t)g.T_max * rb : 0u);
+    const uint32_t t0 = (uint32_t)(ci - seq_chunk0(a.seq, bi)) * kTC;
+    const uint32_t to0 = (t0 + n) * rb, to1 = to0 + 16 * rb;
 #pragma unroll
-    for (int jt = 0; jt < KTM; ++jt)
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const int tok = t0 + tt * 16 + n;
-        kr[jt][tt] = bld16(krs, (kofs[jt] != kOOB && tok < ln) ? (uint32_t)tok * rb + kofs[jt] : kOOB);
-      }
+    for (int jt = 0; jt < KTM; ++jt) {
+      kr[jt][0] = bld16(krs, to0 + kofs[jt]);
+      kr[jt][1] = bld16(krs, to1 + kofs[jt]);
+    }
     ci += 2;
   };
   // query fragments and row parameters of sequence bb
@@ -1209,35 +1212,48 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       load_seq(bc);
       vm_wait<0>();  // so that no later wait counts the fragments as still in flight
     }
-    // scores of chunk cc: lane holds tokens 16 tt + 4 qq + v of row i
+    // scores of chunk cc: lane holds tokens 16 tt + 4 qq + v of row i; the low part's
+    // accumulator starts at minus the row's offset-binary bias
     i32x4 ah[2], al[2];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) ah[tt] = al[tt] = i32x4{0, 0, 0, 0};
+    for (int tt = 0; tt < 2; ++tt) {
+      ah[tt] = i32x4{0, 0, 0, 0};
+      al[tt] = i32x4{-ibias, -ibias, -ibias, -ibias};
+    }
 #pragma unroll
     for (int jt = 0; jt < KTM; ++jt) {
       if (jt < nkt) {  // wave-uniform
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
           const i32x4 av = k8[jt] ? __builtin_bit_cast(i32x4, kr[jt][tt])
-                                  : unpack_int4_group(khi[jt] ? u32x2{kr[jt][tt][2], kr[jt][tt][3]}
-                                                              : u32x2{kr[jt][tt][0], kr[jt][tt][1]});
+                                  : unpack_int4_group(u32x2{kr[jt][tt][0], kr[jt][tt][1]});
           ah[tt] = mfma16_i8(av, fh[jt], ah[tt]);
           al[tt] = mfma16_i8(av, fl[jt], al[tt]);
         }
       }
     }
     const int t0 = (cc - bc0) * kTC;
-    const int lim = rowvalid ? bc_len - g.n_q + jq : -1;  // last token this row sees
     float s2[2][4];
     float m = -INFINITY;
+    if (tile_full && t0 + kTC - 1 <= bc_len - g.n_q) {  // wave-uniform: every row sees every token
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+      for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int t = t0 + tt * 16 + 4 * qq + v;
-        s2[tt][v] = t <= lim ? rs * (float)(254 * ah[tt][v] + al[tt][v] - ibias) : -INFINITY;
-        m = fmaxf(m, s2[tt][v]);
-      }
+        for (int v = 0; v < 4; ++v) {
+          s2[tt][v] = rs * (float)(254 * ah[tt][v] + al[tt][v]);
+          m = fmaxf(m, s2[tt][v]);
+        }
+    } else {
+      const int lim = rowvalid ? bc_len - g.n_q + jq : -1;  // last token this row sees
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int t = t0 + tt * 16 + 4 * qq + v;
+          s2[tt][v] = t <= lim ? rs * (float)(254 * ah[tt][v] + al[tt][v]) : -INFINITY;
+          m = fmaxf(m, s2[tt][v]);
+        }
+    }
     m = wave_max_xor(m, 16);
     m = wave_max_xor(m, 32);
     // exp2(-inf - m) is 0; a row with no visible token keeps m = -inf and takes 0 for reference
