@@ -2362,29 +2362,44 @@ __global__ __launch_bounds__(256) void k_values_mt(ValueArgs a) {
     }
   }
 
+  // Sources of this wave's asynchronous loads at the split's first chunk (a wave-uniform base and
+  // a per-lane offset) and their strides per chunk.  Probability rows 16 i .. 16 i + 15: lane l
+  // takes row 16 i + l / 4, rotated piece l % 4; i == NPI: the chunk maxima; past that, the sums
+  // (indexes past NSI repeat them).  Value blocks: consecutive tiles of a row block are BLKB apart.
+  const uint8_t* ubase[SPW];
+  uint32_t uoff[SPW], ustr[SPW], udst[SPW];
+  const size_t cg0 = (size_t)(cbase + c_lo);
+#pragma unroll
+  for (int u = 0; u < SPW; ++u) {
+    const int i = wave * SPW + u;  // wave-uniform
+    if (i < NPI) {
+      const int row = 16 * i + (lane >> 2);
+      const int piece = ((lane & 3) - (row >> 2)) & 3;
+      ubase[u] = (const uint8_t*)a.p + cg0 * g.M_pad * (kTC * 2);
+      uoff[u] = (uint32_t)(row * (kTC * 2) + 16 * piece);
+      ustr[u] = (uint32_t)g.M_pad * (kTC * 2);
+      udst[u] = P_OFF + i * 1024;
+    } else {
+      ubase[u] = (const uint8_t*)(i == NPI ? a.cm : a.cl) + cg0 * g.M_pad * 4;
+      uoff[u] = (uint32_t)min(4 * lane, g.M_pad - 4) * 4;
+      ustr[u] = (uint32_t)g.M_pad * 4;
+      udst[u] = i == NPI ? CM_OFF : CL_OFF;
+    }
+  }
+  const uint8_t* vbase[NTW];
+#pragma unroll
+  for (int j = 0; j < NTW; ++j) vbase[j] = a.v_tiles + vblock_off(b, blk[j], c_lo, g.v_rows, g.T_max, esz);
   // asynchronous loads of chunk c (clamped into the split) into stage st
   auto issue = [&](int c, int st) {
-    c = min(c, c_hi - 1);
+    const uint32_t dc = (uint32_t)(min(c, c_hi - 1) - c_lo);
     const uint32_t sb = ring0 + st * STAGE;
-    const size_t cg = (size_t)(cbase + c);
 #pragma unroll
-    for (int u = 0; u < SPW; ++u) {
-      const int i = wave * SPW + u;  // wave-uniform; both addresses formed, one chosen by select
-      // probability rows 16 i .. 16 i + 15: lane l -> row 16 i + l / 4, rotated piece l % 4
-      const int row = 16 * min(i, NPI - 1) + (lane >> 2);
-      const int piece = ((lane & 3) - (row >> 2)) & 3;
-      const void* psrc = (const uint8_t*)a.p + ((cg * g.M_pad + row) * kTC) * 2 + 16 * piece;
-      // chunk maxima (i == NPI) or sums (indexes past NSI repeat the sums)
-      const void* ssrc = (i == NPI ? a.cm : a.cl) + cg * g.M_pad + min(4 * lane, g.M_pad - 4);
-      const uint32_t dst = sb + (i < NPI ? P_OFF + i * 1024 : i == NPI ? CM_OFF : CL_OFF);
-      lds_dma16(i < NPI ? psrc : ssrc, dst);
-    }
+    for (int u = 0; u < SPW; ++u) lds_dma16(ubase[u] + dc * ustr[u] + uoff[u], sb + udst[u]);
 #pragma unroll
     for (int j = 0; j < NTW; ++j)
 #pragma unroll
       for (int x = 0; x < BLKB / 1024; ++x)
-        lds_dma16(a.v_tiles + vblock_off(b, blk[j], c, g.v_rows, g.T_max, esz) + 1024 * x + 16 * lane,
-                  sb + V_OFF + (wave * NTW + j) * BLKB + 1024 * x);
+        lds_dma16(vbase[j] + dc * BLKB + 1024 * x + 16 * lane, sb + V_OFF + (wave * NTW + j) * BLKB + 1024 * x);
   };
 
   // the first D - 1 chunks go out, then each row's largest chunk maximum over the split
@@ -2410,13 +2425,15 @@ __global__ __launch_bounds__(256) void k_values_mt(ValueArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[j][mt][v] = 0.f;
 
+  int st = 0, st_next = D - 1;  // stages of chunk c and of chunk c + D - 1
   for (int c = c_lo; c < c_hi; ++c) {
-    const int st = (c - c_lo) % D;
     vm_wait<LPW * (D - 2)>();  // this wave's loads of chunk c are in
     __builtin_amdgcn_s_barrier();  // ... and every wave's; chunk c - 1's stage is free
     asm volatile("" ::: "memory");
-    issue(c + D - 1, (c - c_lo + D - 1) % D);
+    issue(c + D - 1, st_next);
+    st_next = st;
     const uint8_t* sp = ring + st * STAGE;
+    st = st + 1 == D ? 0 : st + 1;
     // chunk weights of this lane's A-fragment rows (all reads first, no branch between them)
     float cmv[NMT], clv[NMT], alpha[NMT];
 #pragma unroll
