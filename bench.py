@@ -425,7 +425,7 @@ def measure(w, args, dev, with_cpu: bool, steps: int, warmup: int) -> dict:
         # rotary layers past 32 query rows per KV head: reconstructed keys and values; the
         # dominant kernel against the MFMA peak (up to 32 rows, the latent-space decode rebuilds
         # key tiles in its score kernel, which reads the same latent as the plain one: HBM roofline)
-        fl = prefill_flops(w, probe.ranks, probe.r_v, lens, n_q)
+        fl = prefill_flops(w, probe.ranks, probe.r_v, lens, n_q, "prefill_recon_v" in kern_us)
         dom = max((k for k in kern_us if k in fl), key=lambda k: kern_us[k])
         ab.update(fl)
         achieved = fl[dom] / (kern_us[dom] * 1e-6) / 1e12
@@ -476,16 +476,20 @@ def measure(w, args, dev, with_cpu: bool, steps: int, warmup: int) -> dict:
     return res
 
 
-def prefill_flops(w, ranks, r_v, lens, n_q):
+def prefill_flops(w, ranks, r_v, lens, n_q, split_values: bool):
     """Algorithmic flops of attention over reconstructed keys and values: rebuilding K^ (each
     head's r_g channels) and V^ (r_v channels per KV head) for every cached token, then causal
-    attention of the chunk (query j of n_q sees lens - n_q + j + 1 tokens; QK^T and PV)."""
-    recon = sum(2.0 * int(T) * w.d_h * (float(np.sum(ranks)) + w.H_kv * r_v) for T in lens)
+    attention of the chunk (query j of n_q sees lens - n_q + j + 1 tokens; QK^T and PV).  With
+    split_values the values' rebuild is its own kernel (prefill_recon_v)."""
+    rk = sum(2.0 * int(T) * w.d_h * float(np.sum(ranks)) for T in lens)
+    rv = sum(2.0 * int(T) * w.d_h * w.H_kv * r_v for T in lens)
     attend = 0.0
     for T in lens:
         seen = float(n_q * (int(T) - n_q) + n_q * (n_q + 1) / 2)
         attend += 4.0 * w.H_q * w.d_h * seen
-    return {"prefill_recon": recon, "prefill_attend": attend}
+    if split_values:
+        return {"prefill_recon": rk, "prefill_recon_v": rv, "prefill_attend": attend}
+    return {"prefill_recon": rk + rv, "prefill_attend": attend}
 
 
 def measure_prefill(w, args, dev, n_q: int, steps: int, warmup: int) -> dict:
@@ -556,7 +560,7 @@ def measure_prefill(w, args, dev, n_q: int, steps: int, warmup: int) -> dict:
     kern_us = {k: 1000.0 * t / n for k, (n, t) in prof.items()}
     for k, us in sorted(kern_us.items()):
         log(f"[kernel] {k:14s} {us:9.2f} us/launch ({prof[k][0]} launches)")
-    fl = prefill_flops(w, L.ranks, L.r_v, lens, n_q)
+    fl = prefill_flops(w, L.ranks, L.r_v, lens, n_q, "prefill_recon_v" in kern_us)
     dom = max((k for k in kern_us if k in fl), key=lambda k: kern_us[k])
     tflops = fl[dom] / (kern_us[dom] * 1e-6) / 1e12
     return {

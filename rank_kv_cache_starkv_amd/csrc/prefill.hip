@@ -10,12 +10,15 @@
 // position-dependent rotation of the keys does not commute with B_g at all: a rotary layer always
 // takes this path.
 //
-//   1. k_deq_latent  the dequantised latent of every cached token, token-major fp32:
-//                    xhat[t][c] = code * scale_c (or the stored bf16 / fp32 latent)
-//   2. k_recon       K^_g = xhat_g B_g and V^_g = xhat_v B_v[:, g d_h:(g + 1) d_h] per KV head on
-//                    MFMA (fp32 latent split into bf16 high and low parts), the rotation of the
-//                    keys at their positions in the epilogue; stored as f16, K^ token-major and V^
-//                    transposed (dims x tokens)
+//   1. k_deq_latent  the dequantised latent of every cached token, token-major: key channels
+//                    in fp32, xk[t][c] = code * scale_c (or the stored bf16 / fp32 latent); value
+//                    channels as bf16 high and low parts of the same fp32 value, xv_hi[t][c] and
+//                    xv_lo[t][c], rows padded with zeros to a multiple of 64 channels
+//   2. k_recon       K^_g = xk_g B_g per KV head on MFMA (fp32 latent split into bf16 high and low
+//                    parts), the rotation of the keys at their positions in the epilogue;
+//      k_recon_v     V^ = (xv_hi + xv_lo) B_v for all heads at once, a GEMM whose operand tiles
+//                    stream through LDS; stored as f16, K^ token-major and V^ transposed (dims x
+//                    tokens)
 //   3. k_flash       causal attention of the query chunk over K^, V^: 32-token key tiles with an
 //                    online softmax (base 2), S^T = K^ Q^T and O^T = V^T P^T on f16 MFMA so that a
 //                    row's softmax state lives in one lane
@@ -72,80 +75,98 @@ struct DeqArgs {
   const uint16_t* scales;
   const int* src;  // [n_lat] (head << 16) | index within the head; head = H_kv for value channels
   HeadTables heads;
-  float* xhat;     // [total][n_lat]
-  int n_lat, n_key, H_kv, K8, V8, n8v, k_row_bytes, v_rows, T_max;
+  float* xk;       // [total][n_key]
+  uint16_t* xv_hi;  // [total][rvp]
+  uint16_t* xv_lo;  // [total][rvp]
+  int n_lat, n_key, r_v, rvp, H_kv, K8, V8, n8v, k_row_bytes, v_rows, T_max;
   int pack3, K4, V4;  // packed layout: outlier nibbles, then 3-bit planes from K4 / V4
   SeqBases sb;
 };
 
 // Workgroup = one 32-token tile of one sequence; thread items walk (token, channel) with the
-// channel fastest, so the fp32 stores are contiguous.  Tokens past the length get 0.
+// channel fastest, so the stores are contiguous.  Tokens past the length get 0.
+template <int LAT>
+__device__ __forceinline__ float deq_key(const DeqArgs& a, int b, int t, int c) {
+  const uint8_t* row = a.k_rows + ((size_t)b * a.T_max + t) * a.k_row_bytes;
+  if (LAT == STARKV_LATENT_MIX84) {
+    const int s = a.src[c];
+    const int g = s >> 16, k = s & 0xFFFF;
+    const int n8 = a.heads.n8[g];
+    int code;
+    if (a.pack3) {
+      if (k < n8) {
+        const int u = a.heads.off8[g] + k;
+        code = snib(row[u >> 1], u & 1);
+      } else {
+        code = key_code3(row, a.K4, a.heads.off4[g] + (k - n8));
+      }
+    } else if (k < n8) {
+      code = (int)(int8_t)row[a.heads.off8[g] + k];
+    } else {
+      const int u = a.heads.off4[g] + (k - n8);
+      const int byte = row[a.K8 + (u >> 1)];
+      code = ((int)(((u & 1) ? byte >> 4 : byte) & 0xF) ^ 8) - 8;  // signed nibble
+    }
+    return (float)code * f16_to_f32(a.scales[c]);
+  } else if (LAT == STARKV_LATENT_BF16) {
+    return bf16_to_f32(((const uint16_t*)row)[c]);
+  } else {
+    return ((const float*)row)[c];
+  }
+}
+template <int LAT>
+__device__ __forceinline__ float deq_value(const DeqArgs& a, int b, int t, int cv) {
+  const int c = a.n_key + cv;
+  if (LAT == STARKV_LATENT_MIX84 && a.pack3) {
+    int code;
+    if (cv < a.n8v) {
+      const int byte = a.v_tiles[vblock_off(b, (cv >> 1) >> 5, t / kTT, a.v_rows, a.T_max, 1) +
+                                 ((cv >> 1) & 31) * kTT + t % kTT];
+      code = snib(byte, cv & 1);
+    } else {
+      code = val_code3(a.v_tiles, b, t, cv - a.n8v, a.V4, a.v_rows, a.T_max);
+    }
+    return (float)code * f16_to_f32(a.scales[c]);
+  } else if (LAT == STARKV_LATENT_MIX84) {
+    const bool i4 = cv >= a.n8v;
+    const int w = cv - a.n8v;
+    const int vr = i4 ? a.V8 + (w >> 1) : cv;
+    const int byte = a.v_tiles[vblock_off(b, vr >> 5, t / kTT, a.v_rows, a.T_max, 1) + (vr & 31) * kTT + t % kTT];
+    const int code = i4 ? ((int)(((w & 1) ? byte >> 4 : byte) & 0xF) ^ 8) - 8 : (int)(int8_t)byte;
+    return (float)code * f16_to_f32(a.scales[c]);
+  } else if (LAT == STARKV_LATENT_BF16) {
+    const uint16_t* blk = (const uint16_t*)(a.v_tiles + vblock_off(b, cv >> 5, t / kTT, a.v_rows, a.T_max, 2));
+    return bf16_to_f32(blk[(cv & 31) * kTT + t % kTT]);
+  } else {
+    const float* blk = (const float*)(a.v_tiles + vblock_off(b, cv >> 5, t / kTT, a.v_rows, a.T_max, 4));
+    return blk[(cv & 31) * kTT + t % kTT];
+  }
+}
 template <int LAT>
 __global__ __launch_bounds__(256) void k_deq_latent(DeqArgs a) {
   const int tok0 = blockIdx.x * kRT;
   const int b = seq_of_token(a.sb.base, a.sb.B, tok0);
   const int t0 = tok0 - a.sb.base[b], len = a.sb.lens[b];
-  for (int idx = threadIdx.x; idx < kRT * a.n_lat; idx += 256) {
-    const int tl = idx / a.n_lat, c = idx % a.n_lat;
+  for (int idx = threadIdx.x; idx < kRT * a.n_key; idx += 256) {
+    const int tl = idx / a.n_key, c = idx % a.n_key;
     const int t = t0 + tl;
-    float x = 0.f;
+    a.xk[(size_t)(tok0 + tl) * a.n_key + c] = t < len ? deq_key<LAT>(a, b, t, c) : 0.f;
+  }
+  // value channels in pairs: one 32-bit store of each part per pair
+  const int np = a.rvp / 2;
+  for (int idx = threadIdx.x; idx < kRT * np; idx += 256) {
+    const int tl = idx / np, cv = 2 * (idx % np);
+    const int t = t0 + tl;
+    float x0 = 0.f, x1 = 0.f;
     if (t < len) {
-      if (c < a.n_key) {
-        const uint8_t* row = a.k_rows + ((size_t)b * a.T_max + t) * a.k_row_bytes;
-        if (LAT == STARKV_LATENT_MIX84) {
-          const int s = a.src[c];
-          const int g = s >> 16, k = s & 0xFFFF;
-          const int n8 = a.heads.n8[g];
-          int code;
-          if (a.pack3) {
-            if (k < n8) {
-              const int u = a.heads.off8[g] + k;
-              code = snib(row[u >> 1], u & 1);
-            } else {
-              code = key_code3(row, a.K4, a.heads.off4[g] + (k - n8));
-            }
-          } else if (k < n8) {
-            code = (int)(int8_t)row[a.heads.off8[g] + k];
-          } else {
-            const int u = a.heads.off4[g] + (k - n8);
-            const int byte = row[a.K8 + (u >> 1)];
-            code = ((int)(((u & 1) ? byte >> 4 : byte) & 0xF) ^ 8) - 8;  // signed nibble
-          }
-          x = (float)code * f16_to_f32(a.scales[c]);
-        } else if (LAT == STARKV_LATENT_BF16) {
-          x = bf16_to_f32(((const uint16_t*)row)[c]);
-        } else {
-          x = ((const float*)row)[c];
-        }
-      } else {
-        const int cv = c - a.n_key;
-        if (LAT == STARKV_LATENT_MIX84 && a.pack3) {
-          int code;
-          if (cv < a.n8v) {
-            const int byte = a.v_tiles[vblock_off(b, (cv >> 1) >> 5, t / kTT, a.v_rows, a.T_max, 1) +
-                                       ((cv >> 1) & 31) * kTT + t % kTT];
-            code = snib(byte, cv & 1);
-          } else {
-            code = val_code3(a.v_tiles, b, t, cv - a.n8v, a.V4, a.v_rows, a.T_max);
-          }
-          x = (float)code * f16_to_f32(a.scales[c]);
-        } else if (LAT == STARKV_LATENT_MIX84) {
-          const bool i4 = cv >= a.n8v;
-          const int w = cv - a.n8v;
-          const int vr = i4 ? a.V8 + (w >> 1) : cv;
-          const int byte = a.v_tiles[vblock_off(b, vr >> 5, t / kTT, a.v_rows, a.T_max, 1) + (vr & 31) * kTT + t % kTT];
-          const int code = i4 ? ((int)(((w & 1) ? byte >> 4 : byte) & 0xF) ^ 8) - 8 : (int)(int8_t)byte;
-          x = (float)code * f16_to_f32(a.scales[c]);
-        } else if (LAT == STARKV_LATENT_BF16) {
-          const uint16_t* blk = (const uint16_t*)(a.v_tiles + vblock_off(b, cv >> 5, t / kTT, a.v_rows, a.T_max, 2));
-          x = bf16_to_f32(blk[(cv & 31) * kTT + t % kTT]);
-        } else {
-          const float* blk = (const float*)(a.v_tiles + vblock_off(b, cv >> 5, t / kTT, a.v_rows, a.T_max, 4));
-          x = blk[(cv & 31) * kTT + t % kTT];
-        }
-      }
+      if (cv < a.r_v) x0 = deq_value<LAT>(a, b, t, cv);
+      if (cv + 1 < a.r_v) x1 = deq_value<LAT>(a, b, t, cv + 1);
     }
-    a.xhat[(size_t)(tok0 + tl) * a.n_lat + c] = x;
+    const uint16_t h0 = f32_to_bf16(x0), h1 = f32_to_bf16(x1);
+    const uint16_t l0 = f32_to_bf16(x0 - bf16_to_f32(h0)), l1 = f32_to_bf16(x1 - bf16_to_f32(h1));
+    const size_t o = (size_t)(tok0 + tl) * a.rvp + cv;
+    *(uint32_t*)(a.xv_hi + o) = (uint32_t)h0 | ((uint32_t)h1 << 16);
+    *(uint32_t*)(a.xv_lo + o) = (uint32_t)l0 | ((uint32_t)l1 << 16);
   }
 }
 
@@ -153,13 +174,16 @@ __global__ __launch_bounds__(256) void k_deq_latent(DeqArgs a) {
 // 2. reconstruction of K^ and V^ per KV head (bf16 factors)
 
 struct ReconArgs {
-  const float* xhat;
+  const float* xk;       // [total][n_key]
+  const uint16_t* xv_hi;  // [total][rvp]
+  const uint16_t* xv_lo;
   const uint16_t* B_k;   // [n_key][d_h]
   const uint16_t* B_vt;  // [H_kv d_h][r_v]
   const int* koff;       // [H_kv + 1]
   _Float16* kh;          // [total][H_kv][d_h]
   _Float16* vt;          // [H_kv d_h][total], tokens of each 16-group in swapped-middle order
-  int n_lat, n_key, r_v, H_kv, d_h, total, rpad;
+  int n_lat, n_key, r_v, rvp, H_kv, d_h, total, rpad;
+  int kind0;  // kind of grid z = 0 (0 keys, 1 values)
   float rope_theta;
   int rotary_dim;
   SeqBases sb;
@@ -176,13 +200,14 @@ __device__ __forceinline__ int vt_slot(int t) {
 // Workgroup = (128 tokens, KV head g, keys or values), four waves of 32 tokens x all d_h columns
 // (NT = d_h / 32 column tiles of 32x32x16 bf16 MFMA).  The latent row of a token is split into
 // bf16 high and low parts (two MFMAs), so the product is as accurate as fp32 x bf16.  Keys read
-// B_g transposed from LDS (staged by the workgroup); values read B_v^T rows directly.  Rotary keys
+// B_g transposed from LDS (staged by the workgroup); values (only when r_v is not a multiple of 8:
+// otherwise k_recon_v) read B_v^T rows directly and the latent's parts as stored.  Rotary keys
 // (over the whole head dimension): the pair (e, e + d_h / 2) is rotated by
 // position * theta^(-2 e / d_h), the angle formed and reduced in fp64.
 template <int NT, bool VEC>
 __global__ __launch_bounds__(256) void k_recon(ReconArgs a) {
   extern __shared__ uint16_t bkt[];  // keys: B_g^T [d_h][rpad]
-  const int g = blockIdx.y, kind = blockIdx.z;
+  const int g = blockIdx.y, kind = blockIdx.z + a.kind0;
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int r = lane & 31, q = lane >> 5;
   const int c_lo = kind == 0 ? a.koff[g] : a.n_key;
@@ -202,22 +227,29 @@ __global__ __launch_bounds__(256) void k_recon(ReconArgs a) {
   for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[nt][v] = 0.f;
-  const float* xr = a.xhat + (size_t)tok * a.n_lat + c_lo;
+  const float* xr = a.xk + (size_t)tok * a.n_key + c_lo;
   for (int k0 = 0; k0 < rk; k0 += 16) {
     const int kb = k0 + 8 * q;
-    float xv[8];
+    bf16x8 ah, al;
+    if (kind == 0) {
+      float xv[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) xv[i] = kb + i < rk ? xr[kb + i] : 0.f;
-    uint32_t hw[4], lw[4];
+      for (int i = 0; i < 8; ++i) xv[i] = kb + i < rk ? xr[kb + i] : 0.f;
+      uint32_t hw[4], lw[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint16_t h0 = f32_to_bf16(xv[2 * i]), h1 = f32_to_bf16(xv[2 * i + 1]);
-      const uint16_t l0 = f32_to_bf16(xv[2 * i] - bf16_to_f32(h0)), l1 = f32_to_bf16(xv[2 * i + 1] - bf16_to_f32(h1));
-      hw[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-      lw[i] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+      for (int i = 0; i < 4; ++i) {
+        const uint16_t h0 = f32_to_bf16(xv[2 * i]), h1 = f32_to_bf16(xv[2 * i + 1]);
+        const uint16_t l0 = f32_to_bf16(xv[2 * i] - bf16_to_f32(h0)), l1 = f32_to_bf16(xv[2 * i + 1] - bf16_to_f32(h1));
+        hw[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        lw[i] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+      }
+      ah = as_bf16x8(u32x4{hw[0], hw[1], hw[2], hw[3]});
+      al = as_bf16x8(u32x4{lw[0], lw[1], lw[2], lw[3]});
+    } else {
+      // the stored parts (channels past r_v are zero up to rvp, a multiple of 64)
+      ah = as_bf16x8(ld16(a.xv_hi + (size_t)tok * a.rvp + kb));
+      al = as_bf16x8(ld16(a.xv_lo + (size_t)tok * a.rvp + kb));
     }
-    const bf16x8 ah = as_bf16x8(u32x4{hw[0], hw[1], hw[2], hw[3]});
-    const bf16x8 al = as_bf16x8(u32x4{lw[0], lw[1], lw[2], lw[3]});
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const int e = nt * 32 + r;
@@ -275,6 +307,110 @@ __global__ __launch_bounds__(256) void k_recon(ReconArgs a) {
       if (kind == 0) a.kh[((size_t)tf * a.H_kv + g) * a.d_h + e] = x;
       else a.vt[(size_t)(g * a.d_h + e) * a.total + vt_slot(tf)] = x;
     }
+  }
+}
+
+// V^ for all KV heads as one GEMM, C[m][n] = sum_k (xv_hi + xv_lo)[m][k] B_vt[n][k] (m = token of
+// the padded token range, n = g d_h + e, k < r_v; r_v a multiple of 8), stored transposed in f16.
+// Workgroup tile 64 tokens x 64 columns, four waves in 2 x 2 quadrants of 32 x 32 over the whole
+// K.  K advances in blocks of 64: the block's three 8 KiB operand tiles (latent high part, low
+// part, B_vt rows) arrive by 16-byte LDS DMA into a ring of NST stages, NST - 1 blocks ahead of
+// the MFMAs; in a tile, row R's eight 16-byte K-chunks sit at chunk c ^ ((R >> 1) & 7), so the 16
+// lanes of a fragment read hit 16 different 4-bank groups.  B_vt is read through a buffer
+// resource: its K-chunks past r_v read the next row (or zeros past the end), which meet zero
+// latent parts (rows padded to rvp).  Tokens past total repeat the last token and are not stored.
+struct ReconVArgs {
+  const uint16_t* xv_hi;  // [total][rvp]
+  const uint16_t* xv_lo;
+  const uint16_t* B_vt;   // [N][r_v]
+  _Float16* vt;           // [N][total]
+  int rvp, r_v, N, total;
+  SeqBases sb;
+};
+
+template <int NST>
+__global__ __launch_bounds__(256) void k_recon_v(ReconVArgs a) {
+  constexpr int TB = 64 * 64 * 2;  // bytes of one operand tile of a K block
+  extern __shared__ __align__(16) uint8_t ring_raw[];
+  uint8_t (*ring)[3][TB] = (uint8_t (*)[3][TB])ring_raw;
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const int r = lane & 31, q = lane >> 5;
+  const int mb = blockIdx.x * 64, nb = blockIdx.y * 64;
+  const __amdgpu_buffer_rsrc_t wrs = buf_rsrc(a.B_vt, (uint32_t)a.N * (uint32_t)a.r_v * 2u);
+  // this lane's DMA sources: load jj of the wave fills tile slot i = 64 (2 wave + jj) + lane,
+  // i.e. row i / 8 and stored chunk i % 8, which holds K-chunk (i % 8) ^ ((row >> 1) & 7)
+  size_t xoff[2];
+  uint32_t woff[2];
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj) {
+    const int i = 64 * (2 * wave + jj) + lane;
+    const int row = i >> 3;
+    const int kc = (i & 7) ^ ((row >> 1) & 7);
+    xoff[jj] = (size_t)min(mb + row, a.total - 1) * a.rvp + 8 * kc;
+    woff[jj] = (uint32_t)(nb + row) * (uint32_t)a.r_v * 2u + 16u * (uint32_t)kc;
+  }
+  const int nkb = a.rvp / 64;
+  const uint32_t ring0 = lds_addr(ring);
+  auto issue = [&](int kb, int st) {
+    kb = min(kb, nkb - 1);  // past the end: reload the last block (never read)
+    const uint32_t hb = ring0 + st * 3 * TB, lb = hb + TB, wb = lb + TB;
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const uint32_t slot = 1024 * (2 * wave + jj);
+      lds_dma16(a.xv_hi + xoff[jj] + 64 * kb, hb + slot);
+      lds_dma16(a.xv_lo + xoff[jj] + 64 * kb, lb + slot);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, (__attribute__((address_space(3))) void*)(uintptr_t)(wb + slot),
+                                               16, (int)(woff[jj] + 128u * (uint32_t)kb), 0, 0, 0);
+    }
+  };
+  const int wm = wave & 1, wn = wave >> 1;
+  const int xrow = 32 * wm + r, wrow = 32 * wn + r;
+  const int xo = xrow * 128, wo = wrow * 128;
+  const int xsw = (xrow >> 1) & 7, wsw = (wrow >> 1) & 7;
+  f32x16 acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+#pragma unroll
+  for (int u = 0; u < NST - 1; ++u) issue(u, u);
+  for (int kb = 0; kb < nkb; ++kb) {
+    vm_wait<6 * (NST - 2)>();      // this wave's loads of block kb are in
+    __builtin_amdgcn_s_barrier();  // ... and every wave's; block kb - 1's stage is free
+    asm volatile("" ::: "memory");
+    issue(kb + NST - 1, (kb + NST - 1) % NST);
+    const uint8_t* ht = ring[kb % NST][0];
+    const uint8_t* lt = ring[kb % NST][1];
+    const uint8_t* wt = ring[kb % NST][2];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int c = 2 * ks + q;
+      const u32x4 xh = *(const u32x4*)(ht + xo + 16 * (c ^ xsw));
+      const u32x4 xl = *(const u32x4*)(lt + xo + 16 * (c ^ xsw));
+      const u32x4 wf = *(const u32x4*)(wt + wo + 16 * (c ^ wsw));
+      acc = mfma32_bf16(as_bf16x8(xh), as_bf16x8(wf), acc);
+      acc = mfma32_bf16(as_bf16x8(xl), as_bf16x8(wf), acc);
+    }
+  }
+  vm_wait<0>();  // the trailing reloads land before the workgroup ends
+  // lane holds column n of tokens m0 + d32_row(v, q); run j (v = 8 j .. 8 j + 7) covers tokens
+  // 16 j + 4 q + {0..3} and 16 j + 8 + 4 q + {0..3}, which the transposed store keeps at the
+  // 8 consecutive slots 16 j + 8 q .. + 7 (see vt_slot)
+  const int n = nb + 32 * wn + r;
+  const int m0 = mb + 32 * wm;
+  if (n >= a.N || m0 >= a.total) return;
+  const int b = seq_of_token(a.sb.base, a.sb.B, m0);  // a 32-token tile lies in one sequence
+  const int tl = m0 - a.sb.base[b], len = a.sb.lens[b];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const int t0 = tl + d32_row(8 * j + e, q), t1 = tl + d32_row(8 * j + e + 1, q);
+      const _Float16 x0 = t0 < len ? (_Float16)acc[8 * j + e] : (_Float16)0.f;
+      const _Float16 x1 = t1 < len ? (_Float16)acc[8 * j + e + 1] : (_Float16)0.f;
+      w[e / 2] = (uint32_t)__builtin_bit_cast(uint16_t, x0) | ((uint32_t)__builtin_bit_cast(uint16_t, x1) << 16);
+    }
+    st16(a.vt + (size_t)n * a.total + m0 + 16 * j + 8 * q, u32x4{w[0], w[1], w[2], w[3]});
   }
 }
 
@@ -435,14 +571,20 @@ void seq_bases(int B, const int32_t* lens, SeqBases* sb) {
 }
 
 struct PrefillWs {
-  size_t o_xhat, o_kh, o_vt, bytes;
+  size_t o_xk, o_xvh, o_xvl, o_kh, o_vt, bytes;
 };
+
+int value_rows_padded(const Layer& L) { return ceil_div(L.r_v, 64) * 64; }
 
 PrefillWs prefill_layout(const Layer& L, int total) {
   PrefillWs w;
   size_t o = 0;
-  w.o_xhat = o;
-  o = align256(o + (size_t)total * L.n_lat * 4);
+  w.o_xk = o;
+  o = align256(o + (size_t)total * L.n_key * 4);
+  w.o_xvh = o;
+  o = align256(o + (size_t)total * value_rows_padded(L) * 2);
+  w.o_xvl = o;
+  o = align256(o + (size_t)total * value_rows_padded(L) * 2);
   w.o_kh = o;
   o = align256(o + (size_t)total * L.H_kv * L.d_h * 2);
   w.o_vt = o;
@@ -460,15 +602,27 @@ hipError_t launch_lds(const ProfScope& ps, void (*kernel)(A), dim3 grid, dim3 bl
   return hipLaunchKernel((const void*)kernel, grid, block, argv, lds, s);
 }
 
+constexpr int kReconVStages = 3;
+
 template <int NT>
-hipError_t launch_recon_flash(const Layer& L, const ReconArgs& ra, const FlashArgs& fa, int B, int n_q, hipStream_t s) {
+hipError_t launch_recon_flash(const Layer& L, const ReconArgs& ra, const ReconVArgs& va, const FlashArgs& fa, int B,
+                              int n_q, hipStream_t s) {
   const int total = ra.total;
   const size_t lds = (size_t)L.d_h * ra.rpad * 2;
-  {
+  if ((L.r_v & 7) == 0) {
+    {
+      ProfScope ps("prefill_recon");
+      const hipError_t e = launch_lds(ps, k_recon<NT, true>, dim3(ceil_div(total, 128), L.H_kv, 1), dim3(256), lds, s, ra);
+      if (e != hipSuccess) return e;
+    }
+    ProfScope ps("prefill_recon_v");
+    const dim3 grid(total / 64 + (total % 64 ? 1 : 0), ceil_div(va.N, 64));
+    const hipError_t e = launch_lds(ps, k_recon_v<kReconVStages>, grid, dim3(256),
+                                    (size_t)kReconVStages * 3 * 64 * 64 * 2, s, va);
+    if (e != hipSuccess) return e;
+  } else {
     ProfScope ps("prefill_recon");
-    const dim3 grid(ceil_div(total, 128), L.H_kv, 2);
-    const hipError_t e = (L.r_v & 7) == 0 ? launch_lds(ps, k_recon<NT, true>, grid, dim3(256), lds, s, ra)
-                                          : launch_lds(ps, k_recon<NT, false>, grid, dim3(256), lds, s, ra);
+    const hipError_t e = launch_lds(ps, k_recon<NT, false>, dim3(ceil_div(total, 128), L.H_kv, 2), dim3(256), lds, s, ra);
     if (e != hipSuccess) return e;
   }
   ProfScope ps("prefill_attend");
@@ -491,7 +645,10 @@ hipError_t launch_prefill(const Layer& L, const starkv_cache& c, const void* q, 
   const int total = sb.base[B];
   const PrefillWs w = prefill_layout(L, total);
   uint8_t* base = (uint8_t*)ws;
-  float* xhat = (float*)(base + w.o_xhat);
+  float* xk = (float*)(base + w.o_xk);
+  uint16_t* xvh = (uint16_t*)(base + w.o_xvh);
+  uint16_t* xvl = (uint16_t*)(base + w.o_xvl);
+  const int rvp = value_rows_padded(L);
   _Float16* kh = (_Float16*)(base + w.o_kh);
   _Float16* vt = (_Float16*)(base + w.o_vt);
   // 1. dequantised latent
@@ -501,9 +658,13 @@ hipError_t launch_prefill(const Layer& L, const starkv_cache& c, const void* q, 
   da.scales = L.scales;
   da.src = L.d_src;
   da.heads = L.heads();
-  da.xhat = xhat;
+  da.xk = xk;
+  da.xv_hi = xvh;
+  da.xv_lo = xvl;
   da.n_lat = L.n_lat;
   da.n_key = L.n_key;
+  da.r_v = L.r_v;
+  da.rvp = rvp;
   da.H_kv = L.H_kv;
   da.K8 = L.K8;
   da.pack3 = L.pack3;
@@ -528,7 +689,9 @@ hipError_t launch_prefill(const Layer& L, const starkv_cache& c, const void* q, 
   int rmax = 1;
   for (int g = 0; g < L.H_kv; ++g) rmax = std::max(rmax, L.rk[g]);
   ReconArgs ra;
-  ra.xhat = xhat;
+  ra.xk = xk;
+  ra.xv_hi = xvh;
+  ra.xv_lo = xvl;
   ra.B_k = (const uint16_t*)L.B_k;
   ra.B_vt = (const uint16_t*)L.B_vt;
   ra.koff = L.d_koff;
@@ -537,6 +700,8 @@ hipError_t launch_prefill(const Layer& L, const starkv_cache& c, const void* q, 
   ra.n_lat = L.n_lat;
   ra.n_key = L.n_key;
   ra.r_v = L.r_v;
+  ra.rvp = rvp;
+  ra.kind0 = 0;
   ra.H_kv = L.H_kv;
   ra.d_h = L.d_h;
   ra.total = total;
@@ -544,6 +709,16 @@ hipError_t launch_prefill(const Layer& L, const starkv_cache& c, const void* q, 
   ra.rope_theta = L.rope_theta;
   ra.rotary_dim = L.rotary_dim;
   ra.sb = sb;
+  ReconVArgs va;
+  va.xv_hi = xvh;
+  va.xv_lo = xvl;
+  va.B_vt = (const uint16_t*)L.B_vt;
+  va.vt = vt;
+  va.rvp = rvp;
+  va.r_v = L.r_v;
+  va.N = L.H_kv * L.d_h;
+  va.total = total;
+  va.sb = sb;
   FlashArgs fa;
   fa.q = q;
   fa.out = out;
@@ -560,14 +735,14 @@ hipError_t launch_prefill(const Layer& L, const starkv_cache& c, const void* q, 
   fa.rotary_dim = L.rotary_dim;
   fa.sb = sb;
   switch (L.d_h / 32) {
-    case 1: e = launch_recon_flash<1>(L, ra, fa, B, n_q, s); break;
-    case 2: e = launch_recon_flash<2>(L, ra, fa, B, n_q, s); break;
-    case 3: e = launch_recon_flash<3>(L, ra, fa, B, n_q, s); break;
-    case 4: e = launch_recon_flash<4>(L, ra, fa, B, n_q, s); break;
-    case 5: e = launch_recon_flash<5>(L, ra, fa, B, n_q, s); break;
-    case 6: e = launch_recon_flash<6>(L, ra, fa, B, n_q, s); break;
-    case 7: e = launch_recon_flash<7>(L, ra, fa, B, n_q, s); break;
-    default: e = launch_recon_flash<8>(L, ra, fa, B, n_q, s); break;
+    case 1: e = launch_recon_flash<1>(L, ra, va, fa, B, n_q, s); break;
+    case 2: e = launch_recon_flash<2>(L, ra, va, fa, B, n_q, s); break;
+    case 3: e = launch_recon_flash<3>(L, ra, va, fa, B, n_q, s); break;
+    case 4: e = launch_recon_flash<4>(L, ra, va, fa, B, n_q, s); break;
+    case 5: e = launch_recon_flash<5>(L, ra, va, fa, B, n_q, s); break;
+    case 6: e = launch_recon_flash<6>(L, ra, va, fa, B, n_q, s); break;
+    case 7: e = launch_recon_flash<7>(L, ra, va, fa, B, n_q, s); break;
+    default: e = launch_recon_flash<8>(L, ra, va, fa, B, n_q, s); break;
   }
   if (e != hipSuccess) return e;
   return hipGetLastError();
