@@ -147,21 +147,25 @@ __global__ __launch_bounds__(256) void k_deq_latent(DeqArgs a) {
   const int tok0 = blockIdx.x * kRT;
   const int b = seq_of_token(a.sb.base, a.sb.B, tok0);
   const int t0 = tok0 - a.sb.base[b], len = a.sb.lens[b];
+  // no branch around the loads (tokens of the tile past the length are still cache rows below
+  // T_max; their values are replaced by 0 after the load), so unrolled iterations overlap
+#pragma unroll 4
   for (int idx = threadIdx.x; idx < kRT * a.n_key; idx += 256) {
     const int tl = idx / a.n_key, c = idx % a.n_key;
     const int t = t0 + tl;
-    a.xk[(size_t)(tok0 + tl) * a.n_key + c] = t < len ? deq_key<LAT>(a, b, t, c) : 0.f;
+    const float x = deq_key<LAT>(a, b, t, c);
+    a.xk[(size_t)(tok0 + tl) * a.n_key + c] = t < len ? x : 0.f;
   }
   // value channels in pairs: one 32-bit store of each part per pair
   const int np = a.rvp / 2;
+#pragma unroll 4
   for (int idx = threadIdx.x; idx < kRT * np; idx += 256) {
     const int tl = idx / np, cv = 2 * (idx % np);
     const int t = t0 + tl;
-    float x0 = 0.f, x1 = 0.f;
-    if (t < len) {
-      if (cv < a.r_v) x0 = deq_value<LAT>(a, b, t, cv);
-      if (cv + 1 < a.r_v) x1 = deq_value<LAT>(a, b, t, cv + 1);
-    }
+    float x0 = deq_value<LAT>(a, b, t, min(cv, a.r_v - 1));
+    float x1 = deq_value<LAT>(a, b, t, min(cv + 1, a.r_v - 1));
+    x0 = t < len && cv < a.r_v ? x0 : 0.f;
+    x1 = t < len && cv + 1 < a.r_v ? x1 : 0.f;
     const uint16_t h0 = f32_to_bf16(x0), h1 = f32_to_bf16(x1);
     const uint16_t l0 = f32_to_bf16(x0 - bf16_to_f32(h0)), l1 = f32_to_bf16(x1 - bf16_to_f32(h1));
     const size_t o = (size_t)(tok0 + tl) * a.rvp + cv;
@@ -207,16 +211,38 @@ __device__ __forceinline__ int vt_slot(int t) {
 template <int NT, bool VEC>
 __global__ __launch_bounds__(256) void k_recon(ReconArgs a) {
   extern __shared__ uint16_t bkt[];  // keys: B_g^T [d_h][rpad]
+  __shared__ double inv_freq[128];    // rotary keys: theta^(-2 e / d_h), e < d_h / 2
   const int g = blockIdx.y, kind = blockIdx.z + a.kind0;
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int r = lane & 31, q = lane >> 5;
   const int c_lo = kind == 0 ? a.koff[g] : a.n_key;
   const int rk = kind == 0 ? a.koff[g + 1] - c_lo : a.r_v;
   if (kind == 0) {
-    for (int i = threadIdx.x; i < a.d_h * a.rpad; i += 256) {
-      const int e = i / a.rpad, k = i % a.rpad;
-      bkt[i] = k < rk ? a.B_k[(size_t)(c_lo + k) * a.d_h + e] : (uint16_t)0;
+    // 16-byte pieces of B_g's rows (8 dims of channel k), four per thread in flight at once,
+    // stored transposed; channels past the head's rank are zero
+    constexpr int DH = 32 * NT;
+    const int n16 = a.rpad * (DH / 8);
+    for (int i0 = threadIdx.x; i0 < n16; i0 += 1024) {
+      u32x4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + 256 * u;
+        const int k = i % a.rpad, e8 = i / a.rpad;
+        v[u] = ld16(a.B_k + (size_t)min(c_lo + k, a.n_key - 1) * DH + 8 * min(e8, DH / 8 - 1));
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + 256 * u;
+        const int k = i % a.rpad, e8 = i / a.rpad;
+        if (i < n16) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            bkt[(8 * e8 + j) * a.rpad + k] = k < rk ? (uint16_t)(v[u][j >> 1] >> (16 * (j & 1))) : (uint16_t)0;
+        }
+      }
     }
+    if (a.rope_theta > 0.f && (int)threadIdx.x < a.d_h / 2)
+      inv_freq[threadIdx.x] = exp2(-2.0 * (double)threadIdx.x / (double)a.d_h * log2((double)a.rope_theta));
     __syncthreads();
   }
   const int tw = blockIdx.x * 128 + wave * 32;  // first token of this wave
@@ -269,43 +295,63 @@ __global__ __launch_bounds__(256) void k_recon(ReconArgs a) {
         }
         bw = u32x4{w[0], w[1], w[2], w[3]};
       }
-      acc[nt] = mfma32_bf16(ah, as_bf16x8(bw), acc[nt]);
-      acc[nt] = mfma32_bf16(al, as_bf16x8(bw), acc[nt]);
-    }
-  }
-  // epilogue: lane holds column e = 32 nt + r of tokens tw + d32_row(v, q)
-  const int b = seq_of_token(a.sb.base, a.sb.B, tw);
-  const int base = a.sb.base[b], len = a.sb.lens[b];
-  if (kind == 0 && a.rope_theta > 0.f) {
-    // rotary keys over the whole head dimension: pairs (e, e + d_h / 2) in column tiles nt and
-    // nt + NT / 2 of the same lane
-    const double lt = log2((double)a.rope_theta);
-#pragma unroll
-    for (int nt = 0; nt < NT / 2; ++nt) {
-      const int e = nt * 32 + r;
-      const double inv = exp2(-2.0 * (double)e / (double)a.d_h * lt);
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int t = tw + d32_row(v, q) - base;  // position in the sequence
-        float sn, cs;
-        rot_sincos((double)t * inv, &sn, &cs);
-        const float x0 = acc[nt][v], x1 = acc[nt + NT / 2][v];
-        acc[nt][v] = x0 * cs - x1 * sn;
-        acc[nt + NT / 2][v] = x0 * sn + x1 * cs;
+      if (kind == 0) {
+        // keys: K^T tiles (rows = head dims, columns = tokens), so that a lane holds runs of 4
+        // consecutive dims of one token for the token-major store
+        acc[nt] = mfma32_bf16(as_bf16x8(bw), ah, acc[nt]);
+        acc[nt] = mfma32_bf16(as_bf16x8(bw), al, acc[nt]);
+      } else {
+        acc[nt] = mfma32_bf16(ah, as_bf16x8(bw), acc[nt]);
+        acc[nt] = mfma32_bf16(al, as_bf16x8(bw), acc[nt]);
       }
     }
   }
+  const int b = seq_of_token(a.sb.base, a.sb.B, tw);
+  const int base = a.sb.base[b], len = a.sb.lens[b];
   // every token of the padded range is stored: padding tokens (past the length) hold zeros, so
   // the attention's masked products never meet uninitialised memory
+  if (kind == 0) {
+    // lane holds token tok, dims 32 nt + d32_row(v, q)
+    const int t = tok - base;  // position in the sequence
+    if (a.rope_theta > 0.f) {
+      // rotary keys over the whole head dimension: pairs (e, e + d_h / 2) in tiles nt and
+      // nt + NT / 2 of the same lane
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int e = nt * 32 + r;
+      for (int nt = 0; nt < NT / 2; ++nt)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int tf = tw + d32_row(v, q);
-      const _Float16 x = tf - base < len ? (_Float16)acc[nt][v] : (_Float16)0.f;
-      if (kind == 0) a.kh[((size_t)tf * a.H_kv + g) * a.d_h + e] = x;
-      else a.vt[(size_t)(g * a.d_h + e) * a.total + vt_slot(tf)] = x;
+        for (int v = 0; v < 16; ++v) {
+          float sn, cs;
+          rot_sincos((double)t * inv_freq[nt * 32 + d32_row(v, q)], &sn, &cs);
+          const float x0 = acc[nt][v], x1 = acc[nt + NT / 2][v];
+          acc[nt][v] = x0 * cs - x1 * sn;
+          acc[nt + NT / 2][v] = x0 * sn + x1 * cs;
+        }
+    }
+    _Float16* kr = a.kh + ((size_t)tok * a.H_kv + g) * a.d_h;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4) {
+        uint32_t w[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const _Float16 x0 = t < len ? (_Float16)acc[nt][4 * v4 + 2 * i] : (_Float16)0.f;
+          const _Float16 x1 = t < len ? (_Float16)acc[nt][4 * v4 + 2 * i + 1] : (_Float16)0.f;
+          w[i] = (uint32_t)__builtin_bit_cast(uint16_t, x0) | ((uint32_t)__builtin_bit_cast(uint16_t, x1) << 16);
+        }
+        st8(kr + nt * 32 + 8 * v4 + 4 * q, u32x2{w[0], w[1]});
+      }
+  } else {
+    // lane holds column e = 32 nt + r of tokens tw + d32_row(v, q)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int e = nt * 32 + r;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int tf = tw + d32_row(v, q);
+        const _Float16 x = tf - base < len ? (_Float16)acc[nt][v] : (_Float16)0.f;
+        a.vt[(size_t)(g * a.d_h + e) * a.total + vt_slot(tf)] = x;
+      }
     }
   }
 }
