@@ -187,7 +187,6 @@ struct ReconArgs {
   _Float16* kh;          // [total][H_kv][d_h]
   _Float16* vt;          // [H_kv d_h][total], tokens of each 16-group in swapped-middle order
   int n_lat, n_key, r_v, rvp, H_kv, d_h, total, rpad;
-  int kind0;  // kind of grid z = 0 (0 keys, 1 values)
   float rope_theta;
   int rotary_dim;
   SeqBases sb;
@@ -208,11 +207,12 @@ __device__ __forceinline__ int vt_slot(int t) {
 // otherwise k_recon_v) read B_v^T rows directly and the latent's parts as stored.  Rotary keys
 // (over the whole head dimension): the pair (e, e + d_h / 2) is rotated by
 // position * theta^(-2 e / d_h), the angle formed and reduced in fp64.
-template <int NT, bool VEC>
+template <int NT, bool VEC, int KIND, bool ROPE>
 __global__ __launch_bounds__(256) void k_recon(ReconArgs a) {
   extern __shared__ uint16_t bkt[];  // keys: B_g^T [d_h][rpad]
   __shared__ double inv_freq[128];    // rotary keys: theta^(-2 e / d_h), e < d_h / 2
-  const int g = blockIdx.y, kind = blockIdx.z + a.kind0;
+  constexpr int kind = KIND;
+  const int g = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int r = lane & 31, q = lane >> 5;
   const int c_lo = kind == 0 ? a.koff[g] : a.n_key;
@@ -241,7 +241,7 @@ __global__ __launch_bounds__(256) void k_recon(ReconArgs a) {
         }
       }
     }
-    if (a.rope_theta > 0.f && (int)threadIdx.x < a.d_h / 2)
+    if (ROPE && (int)threadIdx.x < a.d_h / 2)
       inv_freq[threadIdx.x] = exp2(-2.0 * (double)threadIdx.x / (double)a.d_h * log2((double)a.rope_theta));
     __syncthreads();
   }
@@ -313,7 +313,7 @@ __global__ __launch_bounds__(256) void k_recon(ReconArgs a) {
   if (kind == 0) {
     // lane holds token tok, dims 32 nt + d32_row(v, q)
     const int t = tok - base;  // position in the sequence
-    if (a.rope_theta > 0.f) {
+    if (ROPE) {
       // rotary keys over the whole head dimension: pairs (e, e + d_h / 2) in tiles nt and
       // nt + NT / 2 of the same lane
 #pragma unroll
@@ -358,13 +358,16 @@ __global__ __launch_bounds__(256) void k_recon(ReconArgs a) {
 
 // V^ for all KV heads as one GEMM, C[m][n] = sum_k (xv_hi + xv_lo)[m][k] B_vt[n][k] (m = token of
 // the padded token range, n = g d_h + e, k < r_v; r_v a multiple of 8), stored transposed in f16.
-// Workgroup tile 64 tokens x 64 columns, four waves in 2 x 2 quadrants of 32 x 32 over the whole
-// K.  K advances in blocks of 64: the block's three 8 KiB operand tiles (latent high part, low
-// part, B_vt rows) arrive by 16-byte LDS DMA into a ring of NST stages, NST - 1 blocks ahead of
-// the MFMAs; in a tile, row R's eight 16-byte K-chunks sit at chunk c ^ ((R >> 1) & 7), so the 16
-// lanes of a fragment read hit 16 different 4-bank groups.  B_vt is read through a buffer
-// resource: its K-chunks past r_v read the next row (or zeros past the end), which meet zero
-// latent parts (rows padded to rvp).  Tokens past total repeat the last token and are not stored.
+// Workgroup tile TM tokens x TN columns, four waves in 2 x 2 quadrants of (TM / 2) x (TN / 2) over
+// the whole K, each quadrant in 32 x 32 MFMA tiles.  K advances in blocks of 64: the block's
+// three operand tiles (latent high part, low part, B_vt rows; 128 bytes per row) arrive by
+// 16-byte LDS DMA into a ring of NST stages, NST - 1 blocks ahead of the MFMAs; in a tile, row
+// R's eight 16-byte K-chunks sit at chunk c ^ ((R >> 1) & 7), so the 16 lanes of a fragment read
+// hit 16 different 4-bank groups.  A 128 x 128 tile reads each operand byte half as often as a
+// 64 x 64 one: the kernel is bound by the bytes each CU pulls from L2.  B_vt is read through a
+// buffer resource: its K-chunks past r_v read the next row (or zeros past the end), which meet
+// zero latent parts (rows padded to rvp).  Tokens past total repeat the last token and are not
+// stored.
 struct ReconVArgs {
   const uint16_t* xv_hi;  // [total][rvp]
   const uint16_t* xv_lo;
@@ -374,89 +377,131 @@ struct ReconVArgs {
   SeqBases sb;
 };
 
-template <int NST>
+template <int TM, int TN, int NST>
 __global__ __launch_bounds__(256) void k_recon_v(ReconVArgs a) {
-  constexpr int TB = 64 * 64 * 2;  // bytes of one operand tile of a K block
+  constexpr int XB = TM * 128, WB = TN * 128;  // bytes of the operand tiles of a K block
+  constexpr int SB = 2 * XB + WB;              // bytes of a stage
+  constexpr int LX = TM / 32, LW = TN / 32;    // 16-byte loads per wave per X / W tile
+  constexpr int MT = TM / 64, NTT = TN / 64;   // 32 x 32 tiles per wave, rows and columns
   extern __shared__ __align__(16) uint8_t ring_raw[];
-  uint8_t (*ring)[3][TB] = (uint8_t (*)[3][TB])ring_raw;
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   const int r = lane & 31, q = lane >> 5;
-  const int mb = blockIdx.x * 64, nb = blockIdx.y * 64;
+  const int mb = blockIdx.x * TM, nb = blockIdx.y * TN;
   const __amdgpu_buffer_rsrc_t wrs = buf_rsrc(a.B_vt, (uint32_t)a.N * (uint32_t)a.r_v * 2u);
-  // this lane's DMA sources: load jj of the wave fills tile slot i = 64 (2 wave + jj) + lane,
+  // this lane's DMA sources: load jj of the wave fills tile slot i = 64 (L wave + jj) + lane,
   // i.e. row i / 8 and stored chunk i % 8, which holds K-chunk (i % 8) ^ ((row >> 1) & 7)
-  size_t xoff[2];
-  uint32_t woff[2];
+  size_t xoff[LX];
+  uint32_t woff[LW];
 #pragma unroll
-  for (int jj = 0; jj < 2; ++jj) {
-    const int i = 64 * (2 * wave + jj) + lane;
+  for (int jj = 0; jj < LX; ++jj) {
+    const int i = 64 * (LX * wave + jj) + lane;
     const int row = i >> 3;
     const int kc = (i & 7) ^ ((row >> 1) & 7);
     xoff[jj] = (size_t)min(mb + row, a.total - 1) * a.rvp + 8 * kc;
+  }
+#pragma unroll
+  for (int jj = 0; jj < LW; ++jj) {
+    const int i = 64 * (LW * wave + jj) + lane;
+    const int row = i >> 3;
+    const int kc = (i & 7) ^ ((row >> 1) & 7);
     woff[jj] = (uint32_t)(nb + row) * (uint32_t)a.r_v * 2u + 16u * (uint32_t)kc;
   }
   const int nkb = a.rvp / 64;
-  const uint32_t ring0 = lds_addr(ring);
+  const uint32_t ring0 = lds_addr(ring_raw);
   auto issue = [&](int kb, int st) {
     kb = min(kb, nkb - 1);  // past the end: reload the last block (never read)
-    const uint32_t hb = ring0 + st * 3 * TB, lb = hb + TB, wb = lb + TB;
+    const uint32_t hb = ring0 + st * SB, lb = hb + XB, wb = lb + XB;
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      const uint32_t slot = 1024 * (2 * wave + jj);
+    for (int jj = 0; jj < LX; ++jj) {
+      const uint32_t slot = 1024 * (LX * wave + jj);
       lds_dma16(a.xv_hi + xoff[jj] + 64 * kb, hb + slot);
       lds_dma16(a.xv_lo + xoff[jj] + 64 * kb, lb + slot);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, (__attribute__((address_space(3))) void*)(uintptr_t)(wb + slot),
-                                               16, (int)(woff[jj] + 128u * (uint32_t)kb), 0, 0, 0);
     }
+#pragma unroll
+    for (int jj = 0; jj < LW; ++jj)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          wrs, (__attribute__((address_space(3))) void*)(uintptr_t)(wb + 1024 * (LW * wave + jj)), 16,
+          (int)(woff[jj] + 128u * (uint32_t)kb), 0, 0, 0);
   };
   const int wm = wave & 1, wn = wave >> 1;
-  const int xrow = 32 * wm + r, wrow = 32 * wn + r;
-  const int xo = xrow * 128, wo = wrow * 128;
-  const int xsw = (xrow >> 1) & 7, wsw = (wrow >> 1) & 7;
-  f32x16 acc;
+  int xo[MT], xsw[MT], wo[NTT], wsw[NTT];
 #pragma unroll
-  for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+  for (int i = 0; i < MT; ++i) {
+    const int row = (TM / 2) * wm + 32 * i + r;
+    xo[i] = row * 128;
+    xsw[i] = (row >> 1) & 7;
+  }
+#pragma unroll
+  for (int j = 0; j < NTT; ++j) {
+    const int row = (TN / 2) * wn + 32 * j + r;
+    wo[j] = row * 128;
+    wsw[j] = (row >> 1) & 7;
+  }
+  f32x16 acc[MT][NTT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NTT; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 #pragma unroll
   for (int u = 0; u < NST - 1; ++u) issue(u, u);
   for (int kb = 0; kb < nkb; ++kb) {
-    vm_wait<6 * (NST - 2)>();      // this wave's loads of block kb are in
-    __builtin_amdgcn_s_barrier();  // ... and every wave's; block kb - 1's stage is free
+    vm_wait<(2 * LX + LW) * (NST - 2)>();  // this wave's loads of block kb are in
+    __builtin_amdgcn_s_barrier();            // ... and every wave's; block kb - 1's stage is free
     asm volatile("" ::: "memory");
     issue(kb + NST - 1, (kb + NST - 1) % NST);
-    const uint8_t* ht = ring[kb % NST][0];
-    const uint8_t* lt = ring[kb % NST][1];
-    const uint8_t* wt = ring[kb % NST][2];
+    const uint8_t* ht = ring_raw + (kb % NST) * SB;
+    const uint8_t* lt = ht + XB;
+    const uint8_t* wt = lt + XB;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int c = 2 * ks + q;
-      const u32x4 xh = *(const u32x4*)(ht + xo + 16 * (c ^ xsw));
-      const u32x4 xl = *(const u32x4*)(lt + xo + 16 * (c ^ xsw));
-      const u32x4 wf = *(const u32x4*)(wt + wo + 16 * (c ^ wsw));
-      acc = mfma32_bf16(as_bf16x8(xh), as_bf16x8(wf), acc);
-      acc = mfma32_bf16(as_bf16x8(xl), as_bf16x8(wf), acc);
+      u32x4 xh[MT], xl[MT], wf[NTT];
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        xh[i] = *(const u32x4*)(ht + xo[i] + 16 * (c ^ xsw[i]));
+        xl[i] = *(const u32x4*)(lt + xo[i] + 16 * (c ^ xsw[i]));
+      }
+#pragma unroll
+      for (int j = 0; j < NTT; ++j) wf[j] = *(const u32x4*)(wt + wo[j] + 16 * (c ^ wsw[j]));
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NTT; ++j) {
+          acc[i][j] = mfma32_bf16(as_bf16x8(xh[i]), as_bf16x8(wf[j]), acc[i][j]);
+          acc[i][j] = mfma32_bf16(as_bf16x8(xl[i]), as_bf16x8(wf[j]), acc[i][j]);
+        }
     }
   }
   vm_wait<0>();  // the trailing reloads land before the workgroup ends
-  // lane holds column n of tokens m0 + d32_row(v, q); run j (v = 8 j .. 8 j + 7) covers tokens
-  // 16 j + 4 q + {0..3} and 16 j + 8 + 4 q + {0..3}, which the transposed store keeps at the
-  // 8 consecutive slots 16 j + 8 q .. + 7 (see vt_slot)
-  const int n = nb + 32 * wn + r;
-  const int m0 = mb + 32 * wm;
-  if (n >= a.N || m0 >= a.total) return;
-  const int b = seq_of_token(a.sb.base, a.sb.B, m0);  // a 32-token tile lies in one sequence
-  const int tl = m0 - a.sb.base[b], len = a.sb.lens[b];
+  // lane holds column n of tokens m0 + d32_row(v, q); run h (v = 8 h .. 8 h + 7) covers tokens
+  // 16 h + 4 q + {0..3} and 16 h + 8 + 4 q + {0..3}, which the transposed store keeps at the
+  // 8 consecutive slots 16 h + 8 q .. + 7 (see vt_slot)
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    uint32_t w[4];
+  for (int i = 0; i < MT; ++i) {
+    const int m0 = mb + (TM / 2) * wm + 32 * i;
+    if (m0 >= a.total) continue;
+    const int b = seq_of_token(a.sb.base, a.sb.B, m0);  // a 32-token tile lies in one sequence
+    const int tl = m0 - a.sb.base[b], len = a.sb.lens[b];
 #pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      const int t0 = tl + d32_row(8 * j + e, q), t1 = tl + d32_row(8 * j + e + 1, q);
-      const _Float16 x0 = t0 < len ? (_Float16)acc[8 * j + e] : (_Float16)0.f;
-      const _Float16 x1 = t1 < len ? (_Float16)acc[8 * j + e + 1] : (_Float16)0.f;
-      w[e / 2] = (uint32_t)__builtin_bit_cast(uint16_t, x0) | ((uint32_t)__builtin_bit_cast(uint16_t, x1) << 16);
+    for (int j = 0; j < NTT; ++j) {
+      const int n = nb + (TN / 2) * wn + 32 * j + r;
+      if (n >= a.N) continue;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const int t0 = tl + d32_row(8 * h + e, q), t1 = tl + d32_row(8 * h + e + 1, q);
+          const _Float16 x0 = t0 < len ? (_Float16)acc[i][j][8 * h + e] : (_Float16)0.f;
+          const _Float16 x1 = t1 < len ? (_Float16)acc[i][j][8 * h + e + 1] : (_Float16)0.f;
+          w[e / 2] = (uint32_t)__builtin_bit_cast(uint16_t, x0) | ((uint32_t)__builtin_bit_cast(uint16_t, x1) << 16);
+        }
+        st16(a.vt + (size_t)n * a.total + m0 + 16 * h + 8 * q, u32x4{w[0], w[1], w[2], w[3]});
+      }
     }
-    st16(a.vt + (size_t)n * a.total + m0 + 16 * j + 8 * q, u32x4{w[0], w[1], w[2], w[3]});
   }
 }
 
@@ -648,27 +693,30 @@ hipError_t launch_lds(const ProfScope& ps, void (*kernel)(A), dim3 grid, dim3 bl
   return hipLaunchKernel((const void*)kernel, grid, block, argv, lds, s);
 }
 
-constexpr int kReconVStages = 3;
+constexpr int kReconVTile = 128, kReconVStages = 3;
 
 template <int NT>
 hipError_t launch_recon_flash(const Layer& L, const ReconArgs& ra, const ReconVArgs& va, const FlashArgs& fa, int B,
                               int n_q, hipStream_t s) {
   const int total = ra.total;
   const size_t lds = (size_t)L.d_h * ra.rpad * 2;
+  const dim3 grid_r(ceil_div(total, 128), L.H_kv);
+  {
+    ProfScope ps("prefill_recon");
+    const hipError_t e = ra.rope_theta > 0.f ? launch_lds(ps, k_recon<NT, true, 0, true>, grid_r, dim3(256), lds, s, ra)
+                                             : launch_lds(ps, k_recon<NT, true, 0, false>, grid_r, dim3(256), lds, s, ra);
+    if (e != hipSuccess) return e;
+  }
   if ((L.r_v & 7) == 0) {
-    {
-      ProfScope ps("prefill_recon");
-      const hipError_t e = launch_lds(ps, k_recon<NT, true>, dim3(ceil_div(total, 128), L.H_kv, 1), dim3(256), lds, s, ra);
-      if (e != hipSuccess) return e;
-    }
     ProfScope ps("prefill_recon_v");
-    const dim3 grid(total / 64 + (total % 64 ? 1 : 0), ceil_div(va.N, 64));
-    const hipError_t e = launch_lds(ps, k_recon_v<kReconVStages>, grid, dim3(256),
-                                    (size_t)kReconVStages * 3 * 64 * 64 * 2, s, va);
+    constexpr int T = kReconVTile;
+    const dim3 grid(ceil_div(total, T), ceil_div(va.N, T));
+    const hipError_t e = launch_lds(ps, k_recon_v<T, T, kReconVStages>, grid, dim3(256),
+                                    (size_t)kReconVStages * 3 * T * 128, s, va);
     if (e != hipSuccess) return e;
   } else {
-    ProfScope ps("prefill_recon");
-    const hipError_t e = launch_lds(ps, k_recon<NT, false>, dim3(ceil_div(total, 128), L.H_kv, 2), dim3(256), lds, s, ra);
+    ProfScope ps("prefill_recon_v");
+    const hipError_t e = launch_lds(ps, k_recon<NT, false, 1, false>, grid_r, dim3(256), 0, s, ra);
     if (e != hipSuccess) return e;
   }
   ProfScope ps("prefill_attend");
@@ -747,7 +795,6 @@ hipError_t launch_prefill(const Layer& L, const starkv_cache& c, const void* q, 
   ra.n_key = L.n_key;
   ra.r_v = L.r_v;
   ra.rvp = rvp;
-  ra.kind0 = 0;
   ra.H_kv = L.H_kv;
   ra.d_h = L.d_h;
   ra.total = total;
