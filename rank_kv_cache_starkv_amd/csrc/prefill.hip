@@ -520,20 +520,35 @@ struct FlashArgs {
   SeqBases sb;
 };
 
-// Workgroup = (128 queries of one head, sequence), four waves of 32 queries; no barrier.  Query j
-// (position len - n_q + j) sees tokens <= its position.  Per 32-token key tile: S^T = K^ Q^T
-// (lane = query row, 16 tokens), masked and scaled to base 2, an online softmax whose row
-// maximum and sum stay in the lane (the two lane halves hold different tokens of the same rows and
-// agree on the maximum through one exchange), then O^T += V^T P^T with the probabilities as the
-// B operand straight from the S^T registers (the value store's token order matches them).
-template <int NT, int DT>
+// Workgroup = (128 queries of one head, sequence), four waves of 32 queries.  Query j (position
+// len - n_q + j) sees tokens <= its position.  Per 32-token key tile: S^T = K^ Q^T (lane = query
+// row, 16 tokens), masked and scaled to base 2, an online softmax whose row maximum and sum stay
+// in the lane (the two lane halves hold different tokens of the same rows and agree on the
+// maximum through one exchange), then O^T += V^T P^T with the probabilities as the B operand
+// straight from the S^T registers (the value store's token order matches them).
+// STAGE (d_h = 64, 128, 256): the four waves share each key tile's K^ rows and V^T rows, which
+// arrive by 16-byte LDS DMA in a ring of kFlashStages stages, two tiles ahead; every wave walks
+// the workgroup's key tiles (tiles past a wave's own queries are fully masked).  In a stage, K^
+// row t keeps its 16-byte dim chunk c at c ^ fk(t) and V^T row e its token chunk c at
+// c ^ ((e >> 2) & 3), so the 16 lanes of a fragment read hit 16 different 4-bank groups.
+// Otherwise each wave reads its tiles from memory itself, with no barrier.
+constexpr int kFlashStages = 3;
+
+template <int NT, int DT, bool STAGE>
 __global__ __launch_bounds__(256) void k_flash(FlashArgs a) {
   constexpr int KS = NT * 2;  // 16-dim K-steps of the scores
+  constexpr int DH = 32 * NT;
+  constexpr int CPR = DH / 8;                                 // 16-byte chunks of a K^ row
+  constexpr int FSH = CPR >= 16 ? 0 : (CPR == 8 ? 1 : 2);     // K^ chunk swizzle: row >> FSH ...
+  constexpr int FMK = (CPR >= 16 ? 16 : CPR) - 1;             // ... masked
+  constexpr int TBY = kRT * DH * 2;                           // bytes of a K^ tile and of a V^T tile
+  constexpr int LPH = STAGE ? NT / 2 : 1;                     // DMA loads per wave per tile half
+  extern __shared__ __align__(16) uint8_t fring[];
   const int h = blockIdx.y, b = blockIdx.z, g = h / a.G;
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int r = lane & 31, q = lane >> 5;
   const int jw = blockIdx.x * 128 + wave * 32;  // first query of this wave
-  if (jw >= a.n_q) return;                      // wave-uniform
+  if (!STAGE && jw >= a.n_q) return;            // wave-uniform (the staged kernel has barriers)
   const int len = a.sb.lens[b], base = a.sb.base[b];
   const int j = min(jw + r, a.n_q - 1);         // this lane's query (rows past n_q repeat the last, not stored)
   const int pos = len - a.n_q + j;
@@ -582,15 +597,55 @@ __global__ __launch_bounds__(256) void k_flash(FlashArgs a) {
   float m_run = -INFINITY, l = 0.f;
   const _Float16* krow = a.kh + ((size_t)(base + r) * a.H_kv + g) * a.d_h + 8 * q;
   const size_t kstep = (size_t)kRT * a.H_kv * a.d_h;  // key-tile stride
-  const int n_kt = pos_max / kRT + 1;
+  // key tiles: this wave's own (unstaged), or the workgroup's (staged: its last query's)
+  const int n_kt = STAGE ? (len - a.n_q + min((int)blockIdx.x * 128 + 127, a.n_q - 1)) / kRT + 1 : pos_max / kRT + 1;
+  // staged: DMA sources of this lane (piece u of the wave: slot 64 (LPH wave + u) + lane)
+  const _Float16* ksrc[LPH];
+  const _Float16* vsrc[LPH];
+  if (STAGE) {
+#pragma unroll
+    for (int u = 0; u < LPH; ++u) {
+      const int sl = 64 * (LPH * wave + u) + lane;
+      const int kr = sl / CPR, kc = (sl % CPR) ^ ((kr >> FSH) & FMK);
+      ksrc[u] = a.kh + ((size_t)(base + kr) * a.H_kv + g) * DH + 8 * kc;
+      const int vr = sl >> 2, vc = (sl & 3) ^ ((vr >> 2) & 3);
+      vsrc[u] = a.vt + (size_t)(g * DH + vr) * a.total + base + 8 * vc;
+    }
+  }
+  const uint32_t ring0 = lds_addr(fring);
+  auto issue = [&](int kt, int st) {
+    kt = min(kt, n_kt - 1);  // past the end: reload the last tile (never read)
+    const uint32_t kb = ring0 + st * 2 * TBY, vb = kb + TBY;
+#pragma unroll
+    for (int u = 0; u < LPH; ++u) {
+      lds_dma16(ksrc[u] + (size_t)kt * kstep, kb + 1024 * (LPH * wave + u));
+      lds_dma16(vsrc[u] + kt * kRT, vb + 1024 * (LPH * wave + u));
+    }
+  };
+  if (STAGE) {
+#pragma unroll
+    for (int u = 0; u < kFlashStages - 1; ++u) issue(u, u);
+  }
   for (int kt = 0; kt < n_kt; ++kt) {
+    const uint8_t* kst = fring + (kt % kFlashStages) * 2 * TBY;
+    const uint8_t* vst = kst + TBY;
+    if (STAGE) {
+      vm_wait<2 * LPH * (kFlashStages - 2)>();  // this wave's loads of tile kt are in
+      __builtin_amdgcn_s_barrier();             // ... and every wave's; tile kt - 1's stage is free
+      asm volatile("" ::: "memory");
+      issue(kt + kFlashStages - 1, (kt + kFlashStages - 1) % kFlashStages);
+    }
     // S^T: rows = tokens kt 32 + d32_row(v, q), columns = queries
     f32x16 s;
 #pragma unroll
     for (int v = 0; v < 16; ++v) s[v] = 0.f;
     const _Float16* kp = krow + (size_t)kt * kstep;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) s = mfma32_f16(as_f16x8(ld16(kp + ks * 16)), qh[ks], s);
+    for (int ks = 0; ks < KS; ++ks) {
+      const u32x4 kf = STAGE ? *(const u32x4*)(kst + 16 * (CPR * r + ((2 * ks + q) ^ ((r >> FSH) & FMK))))
+                             : ld16(kp + ks * 16);
+      s = mfma32_f16(as_f16x8(kf), qh[ks], s);
+    }
     float mt = -INFINITY;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
@@ -620,11 +675,18 @@ __global__ __launch_bounds__(256) void k_flash(FlashArgs a) {
       for (int i = 0; i < 8; ++i) pb[i] = (_Float16)s[8 * kk + i];
 #pragma unroll
       for (int mt2 = 0; mt2 < NT; ++mt2) {
-        const _Float16* vp = a.vt + (size_t)(g * a.d_h + mt2 * 32 + r) * a.total + base + kt * kRT + 16 * kk + 8 * q;
-        acc[mt2] = mfma32_f16(as_f16x8(ld16(vp)), pb, acc[mt2]);
+        u32x4 vf;
+        if (STAGE) {
+          const int vr = mt2 * 32 + r;
+          vf = *(const u32x4*)(vst + 16 * (4 * vr + ((2 * kk + q) ^ ((vr >> 2) & 3))));
+        } else {
+          vf = ld16(a.vt + (size_t)(g * a.d_h + mt2 * 32 + r) * a.total + base + kt * kRT + 16 * kk + 8 * q);
+        }
+        acc[mt2] = mfma32_f16(as_f16x8(vf), pb, acc[mt2]);
       }
     }
   }
+  if (STAGE) vm_wait<0>();  // the trailing reloads land before the workgroup ends
   l += __shfl_xor(l, 32, 64);
   if (jw + r >= a.n_q) return;
   const float il = 1.f / l;
@@ -721,7 +783,9 @@ hipError_t launch_recon_flash(const Layer& L, const ReconArgs& ra, const ReconVA
   }
   ProfScope ps("prefill_attend");
   const dim3 grid(ceil_div(n_q, 128), L.H_q, B);
-  return launch_k(ps, k_flash<NT, STARKV_BF16>, grid, dim3(256), s, fa);
+  constexpr bool stage = NT == 2 || NT == 4 || NT == 8;
+  return launch_lds(ps, k_flash<NT, STARKV_BF16, stage>, grid, dim3(256),
+                    stage ? (size_t)kFlashStages * 2 * kRT * 32 * NT * 2 : 0, s, fa);
 }
 
 }  // namespace
