@@ -411,8 +411,12 @@ hipError_t launch_append(const Layer& L, const starkv_cache& c, const void* X_ne
   ProfScope ps("append");
   hipError_t e;
   const bool mix = L.mix();
-  if (L.pack3) {
-    // packed 3-bit planes: stored from the 64 x 64 tiles' lane layout only
+  if (L.pack3 && B * n_new <= 16) {  // (packed layers: bf16, d a multiple of 64)
+    // packed 3-bit planes from the 16-slot skinny tiles (the 8-slot form is not used: its key
+    // plane words would take four writers)
+    e = launch_k(ps, k_latent_gemm_skinny<STARKV_BF16, 16, true>, dim3((a.NS + 15) / 16), dim3(512), s, a);
+  } else if (L.pack3) {
+    // packed 3-bit planes from the 64 x 64 tiles
     const int n_rt = (B * n_new + 63) / 64, n_ct = (a.NS + 63) / 64;
     if (n_rt <= 16) {
       a.xmap_rt = n_rt;

@@ -3201,8 +3201,9 @@ hipError_t launch_step(const Layer& L, const starkv_cache& c, const DecodePlan& 
                        hipStream_t s) {
   const DecodeGeom& g = plan.g;
   const int M = g.B * g.n_q;
-  const int sw = (M <= 8 && L.d % 64 == 0) ? 8 : ((M <= 16 && L.d % 32 == 0) ? 16 : 0);
-  if (sw == 0 || L.rope_theta > 0.f || L.pack3) {
+  // packed 3-bit layers take the 16-slot front (see store_planes3)
+  const int sw = (M <= 8 && L.d % 64 == 0 && !L.pack3) ? 8 : ((M <= 16 && L.d % 32 == 0) ? 16 : 0);
+  if (sw == 0 || L.rope_theta > 0.f) {
     // many new rows: the tiled append, then the decode
     const hipError_t e = launch_append(L, c, X_new, g.B, g.n_q, lens_pre, s);
     if (e != hipSuccess) return e;

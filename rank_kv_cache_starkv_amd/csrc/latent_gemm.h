@@ -84,14 +84,18 @@ __device__ __forceinline__ int row_pos(const GemmArgs& a, int m) {
 // store does not wait on it); 0 for a padding column.
 __device__ __forceinline__ uint16_t scale_bits(const GemmArgs& a, int chan) { return a.scales[chan >= 0 ? chan : 0]; }
 
-// Packed 3-bit inlier slots (had43p), from the 64 x 64 GEMM tiles' lane layout: lane = slot
-// (the 32 lanes of a half hold 32 consecutive slots of one 32-channel group), rows d32_row(v, q).
-// Fields are code + 4 (padding channels 0).  A key row's group is three words, one bit per
-// channel: three ballots per row, stored by the first lane of each half.  A value channel's
-// tile holds three words over the tile's 32 tokens: the lane merges its consecutive rows of one
-// tile into a mask and sets those bits with atomic AND / OR (other tokens of the word may belong
-// to earlier appends or to other lanes).
-template <int R>
+// Packed 3-bit inlier slots (had43p).  Fields are code + 4 (padding channels 0).  A key row's
+// group is three words, one bit per channel, built with three ballots per row:
+//   64 x 64 GEMM tiles (SK false): lane = slot, the 32 lanes of a half holding 32 consecutive
+//     slots of one 32-channel group, rows d32_row(v, q); the first lane of each half stores the
+//     three words.
+//   skinny tiles (SK true): 16 consecutive slots (lane & 15) of half a group, rows 4 (lane >> 4)
+//     + v; the first lane of each row group sets its 16 bits of the three words with atomic AND /
+//     OR (the other half of each word belongs to another workgroup).
+// A value channel's tile holds three words over the tile's 32 tokens: the lane merges its
+// consecutive rows of one tile into a mask and sets those bits with atomic AND / OR (other tokens
+// of the word may belong to earlier appends or to other lanes).
+template <int R, bool SK = false>
 __device__ __forceinline__ void store_planes3(const GemmArgs& a, int slot, int chan, uint16_t sc_bits, const float* xs,
                                               const int* ms, const int* ps) {
   const int lane = threadIdx.x & 63;
@@ -106,6 +110,30 @@ __device__ __forceinline__ void store_planes3(const GemmArgs& a, int slot, int c
       code = (int)rq;
     }
     fld[v] = chan >= 0 ? code + 4 : 0;
+  }
+  if (is_key && SK) {
+    const int G = (slot - a.K4) >> 5;   // the tile's group (uniform)
+    const int sh = (slot - a.K4) & 16;  // its half of the group's words
+    const int n = lane & 15, rg = lane >> 4;
+#pragma unroll
+    for (int v = 0; v < R; ++v) {
+      uint32_t w[3];
+#pragma unroll
+      for (int b = 0; b < 3; ++b) {
+        const uint64_t bal = __builtin_amdgcn_ballot_w64(((fld[v] >> b) & 1) != 0);
+        w[b] = (uint32_t)(bal >> (16 * rg)) & 0xFFFFu;
+      }
+      const int m = ms[v];
+      if (n != 0 || m >= a.M) continue;
+      const int b = m / a.n_new;
+      uint32_t* row = (uint32_t*)(a.k_rows + ((size_t)b * a.T_max + ps[v]) * a.k_row_bytes + a.K4 / 2 + 12 * G);
+#pragma unroll
+      for (int pb = 0; pb < 3; ++pb) {
+        atomicAnd(row + pb, ~(0xFFFFu << sh));
+        atomicOr(row + pb, w[pb] << sh);
+      }
+    }
+    return;
   }
   if (is_key) {
     const int G = (slot - a.K4) >> 5;  // the wave's group (uniform)
@@ -165,12 +193,12 @@ __device__ __forceinline__ void store_planes3(const GemmArgs& a, int slot, int c
   flush();
 }
 
-template <int R>
+template <int R, bool SK = false>
 __device__ __forceinline__ void store_latent(const GemmArgs& a, int slot, int chan, uint16_t sc_bits, const float* xs,
                                              const int* ms, const int* ps) {
   const bool is_key = slot < a.key_slots;
   if (a.pack3 && (is_key ? slot >= a.K4 : slot - a.key_slots >= a.V4)) {
-    store_planes3<R>(a, slot, chan, sc_bits, xs, ms, ps);
+    store_planes3<R, SK>(a, slot, chan, sc_bits, xs, ms, ps);
     return;
   }
   if (a.latent == STARKV_LATENT_MIX84) {
@@ -362,7 +390,7 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& a, int blk, float (*
     xs[v] = x;  // D row = token row; D column = n
   }
   if (MODE >= 2) store_raw<MODE, 4>(a, bslot, xs, ms);
-  else store_latent<4>(a, bslot, bchan, sc_bits, xs, ms, ps);
+  else store_latent<4, !HALF>(a, bslot, bchan, sc_bits, xs, ms, ps);  // (packed 3-bit keys: SW 16 only)
 }
 
 // Host side: argument blocks of the latent GEMM for a layer, and for an append into a cache.
