@@ -4,6 +4,7 @@
 
 #include <string.h>
 
+#include <cmath>
 #include <mutex>
 #include <new>
 #include <vector>
@@ -15,6 +16,7 @@
 namespace skv {
 int layer_init(const starkv_layer_desc& d, Layer* L);
 int layer_upload_tables(Layer* L);
+int layer_write_rope(Layer* L);
 }  // namespace skv
 
 // The last decode plan of a layer, reused while the batch, query count and lengths repeat (a
@@ -472,7 +474,7 @@ int starkv_layer_set_rope(starkv_layer* l, float theta, int rotary_dim) {
   if (rotary_dim != L.d_h || L.d_h % 64 != 0 || L.dtype != STARKV_BF16) return STARKV_EUNSUPPORTED;
   L.rope_theta = theta;
   L.rotary_dim = rotary_dim;
-  return STARKV_OK;
+  return skv::layer_write_rope(&L);  // (no-op until the layer's device tables exist)
 }
 
 static int check_prefill(const Layer& L, const starkv_cache* c, int B, int n_q, const int32_t* lens) {

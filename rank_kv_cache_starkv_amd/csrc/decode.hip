@@ -1343,6 +1343,8 @@ struct RopeScoreArgs {
   float* cl;
   DecodeGeom g;
   float rope_theta;
+  const double* rope_w;    // [d_h / 2] theta^(-2 j / d_h)
+  const float2* rope_tab;  // [32][d_h / 2] (cos, sin) of r theta^(-2 j / d_h)
   int rpad;                // staged B_g^T: rows of rpad + 8 halves (rpad = largest key rank rounded to 16)
   int cpw;                 // chunks per wave
   int npair_max;           // dword pairs of a latent stage (both segments), largest over the heads
@@ -1383,26 +1385,32 @@ struct RopeSeg {
 };
 
 // LDS layout of k_scores_rope (bytes), shared by the kernel and its launch
+// qc (query-side chunk rotation): the shared query area holds the rows rotated to their
+// positions in fp32, natural dim order ([rows][d_h]); each wave rotates them back by its chunk's
+// base angle into its own fragment area (high then low parts) before the chunk's scores.
 struct RopeLds {
   int tab_r, q_hi, q_lo, bkt, wave0, wstride, stage, total;
-  int qst;  // bytes per staged query row (one part)
-  __host__ __device__ RopeLds(int d_h, int rpad, int rows, int npair_max) {
+  int qst;   // bytes per staged query row (one part)
+  int wst0;  // offset of a wave's stages in its region (its tab_c first, then with qc its fragments)
+  __host__ __device__ RopeLds(int d_h, int rpad, int rows, int npair_max, bool qc) {
     const int np = d_h / 2, ks = d_h / 16;
     qst = ks * 32 + 16;
-    tab_r = 0;                                   // [32][np + 1] float2
-    q_hi = tab_r + 32 * (np + 1) * 8;            // [rows][qst]
-    q_lo = q_hi + rows * qst;
-    bkt = q_lo + rows * qst;                     // [d_h][rpad + 8] halves
-    wave0 = bkt + d_h * (rpad + 8) * 2;          // per wave: tab_c [np] float2, two stages
+    tab_r = 0;                                    // [32][np + 1] float2
+    q_hi = tab_r + 32 * (np + 1) * 8;             // [rows][qst], or with qc [rows][d_h] fp32
+    q_lo = q_hi + (qc ? rows * d_h * 4 : rows * qst);
+    bkt = q_lo + (qc ? 0 : rows * qst);           // [d_h][rpad + 8] halves
+    wave0 = bkt + d_h * (rpad + 8) * 2;           // per wave: tab_c [np] float2, (fragments), two stages
     stage = (npair_max + 1) * 256;  // one pair of slack: windows that run past the segments
-    wstride = np * 8 + 2 * stage;
+    wst0 = np * 8 + (qc ? 2 * rows * qst : 0);
+    wstride = wst0 + 2 * stage;
     total = wave0 + 4 * wstride;
   }
 };
 
-template <int LAT, int NT>
+template <int LAT, int NT, bool QC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_scores_rope(RopeScoreArgs a) {
   constexpr int DH = 32 * NT, NP = DH / 2, KS = 2 * NT;
+  constexpr int LPP = 64 / NP;  // qc: lanes per rotation pair (lane l takes pair l % NP)
   constexpr bool MIX = LAT == STARKV_LATENT_MIX84;
   extern __shared__ __align__(16) uint8_t lds[];
   const DecodeGeom& g = a.g;
@@ -1413,7 +1421,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   const int cbase = blockIdx.x * 4 * a.cpw;
   if (cbase >= nch) return;  // whole workgroup, before any barrier
   const int rows = g.G * g.n_q;  // query rows of this KV head (at most 32)
-  const RopeLds L(DH, a.rpad, rows, a.npair_max);
+  const RopeLds L(DH, a.rpad, rows, a.npair_max, QC);
   const int rst = a.rpad + 8;
   const int c0 = ld_uniform(a.heads.koff + gk);
   const int rg = ld_uniform(a.heads.koff + gk + 1) - c0;
@@ -1434,7 +1442,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   const __amdgpu_buffer_rsrc_t krs =
       buf_rsrc(a.k_rows + (size_t)b * g.T_max * g.k_row_bytes, (uint32_t)len * (uint32_t)g.k_row_bytes);
   auto issue = [&](int c, int st) {
-    const uint32_t dst = wbase + NP * 8 + st * L.stage;
+    const uint32_t dst = wbase + L.wst0 + st * L.stage;
     const uint32_t vo = (uint32_t)(c * kTC + (lane & 31)) * (uint32_t)g.k_row_bytes + 4 * (lane >> 5);
     for (int pp = 0; pp < sg.np8; ++pp)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)(uintptr_t)(dst + 256 * pp),
@@ -1446,9 +1454,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   };
   if (c_first < c_last) issue(c_first, 0);  // in flight during the set-up
 
-  const double lt = log2((double)a.rope_theta);
-  // inverse frequency of pair j: theta^(-2 j / d_h)
-  auto omega = [&](int j) { return exp2(-2.0 * (double)j / (double)DH * lt); };
+  // inverse frequency of pair j: theta^(-2 j / d_h), from the layer's table
+  auto omega = [&](int j) { return a.rope_w[j]; };
 
   // 1. the reconstruction's A operand: A[e][k] = B_g[k][e] (bf16), or B_g[k][e] s_k (f16); zero
   //    past the rank.  16-byte loads of B_g rows, all issued before the first LDS write.
@@ -1484,16 +1491,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       }
     }
   }
-  // 2. cos/sin of r w_j
+  // 2. cos/sin of r w_j, from the layer's table (rows padded by one pair in LDS)
   {
-    const double w = omega(tid % NP);
+    float2 t[32 * NP / 256];
+#pragma unroll
+    for (int it = 0; it < 32 * NP / 256; ++it) t[it] = a.rope_tab[tid + 256 * it];
 #pragma unroll
     for (int it = 0; it < 32 * NP / 256; ++it) {
       const int i = tid + 256 * it;
-      const int rr = i / NP, j = i % NP;
-      float sn, cs;
-      rope_sincos((double)rr * w, &sn, &cs);
-      ((float2*)(lds + L.tab_r))[rr * (NP + 1) + j] = float2{cs, sn};
+      ((float2*)(lds + L.tab_r))[(i / NP) * (NP + 1) + i % NP] = t[it];
     }
   }
   // 3. query rows rotated to their positions: dim e of row n goes to K-step 2 (e / 32) + (v / 8),
@@ -1520,6 +1526,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         float sn, cs;
         rope_sincos((double)pos * w, &sn, &cs);
         const float y0 = x0[it] * cs - x1[it] * sn, y1 = x0[it] * sn + x1[it] * cs;
+        if (QC) {
+          ((float*)(lds + L.q_hi))[n * DH + j] = y0;
+          ((float*)(lds + L.q_hi))[n * DH + j + NP] = y1;
+          continue;
+        }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int e = j + h * NP;
@@ -1553,7 +1564,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     const int st = (c - c_first) & 1;
     vm_wait<0>();  // this wave's latent bytes of chunk c are in its stage
     asm volatile("" ::: "memory");
-    if (lane < NP) tab_c[lane] = float2{ccs, csn};
+    uint8_t* wq = lds + L.wave0 + wave * L.wstride + NP * 8;  // qc: this wave's query fragments
+    if (QC) {
+      // the query rows rotated back by the chunk's base angle 32 c w_j (the keys then turn by
+      // their offset in the chunk only): lane l takes pair j = l % NP of rows l / NP + LPP i
+      const int j = lane % NP;
+      const float* qf = (const float*)(lds + L.q_hi);
+      for (int n = lane / NP; n < rows; n += LPP) {
+        const float x0 = qf[n * DH + j], x1 = qf[n * DH + j + NP];
+        const float y0 = x0 * ccs + x1 * csn, y1 = x1 * ccs - x0 * csn;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int e = j + h * NP;
+          const float y = h ? y1 : y0;
+          const int e32 = e & 31;
+          const int vv = 4 * (e32 >> 3) + (e32 & 3), half = (e32 >> 2) & 1;
+          const int ks = 2 * (e >> 5) + (vv >> 3);
+          const int off = n * L.qst + (ks * 2 + half) * 16 + (vv & 7) * 2;
+          const _Float16 yh = (_Float16)y;
+          *(_Float16*)(wq + off) = yh;
+          *(_Float16*)(wq + rows * L.qst + off) = (_Float16)(y - (float)yh);
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // lgkmcnt(0): the fragments are written
+    } else if (lane < NP) {
+      tab_c[lane] = float2{ccs, csn};
+    }
     {
       const float nc = ccs * c32 - csn * s32, ns = csn * c32 + ccs * s32;
       ccs = nc;
@@ -1562,7 +1598,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     __builtin_amdgcn_wave_barrier();
     if (c + 1 < c_last) issue(c + 1, st ^ 1);
     // 1. K^T tile: lane (token 32 c + r) holds dims 32 mt + d32_row(v, q)
-    const uint8_t* seg8 = lds + L.wave0 + wave * L.wstride + NP * 8 + st * L.stage + 4 * r;
+    const uint8_t* seg8 = lds + L.wave0 + wave * L.wstride + L.wst0 + st * L.stage + 4 * r;
     const uint8_t* seg4 = seg8 + 256 * sg.np8;
     // dword dw of this lane's token in a segment (dw >= -1; -1 lands in the pair before)
     auto ldw = [&](const uint8_t* sb, int dw) { return *(const uint32_t*)(sb + 256 * (dw >> 1) + 128 * (dw & 1)); };
@@ -1643,8 +1679,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int j = mt * 32 + d32_row(v, q);
-        const float2 tc = tab_c[j], tt = tr[j];
-        const float cs = tc.x * tt.x - tc.y * tt.y, sn = tc.y * tt.x + tc.x * tt.y;
+        const float2 tt = tr[j];
+        float cs = tt.x, sn = tt.y;
+        if (!QC) {
+          const float2 tc = tab_c[j];
+          cs = tc.x * tt.x - tc.y * tt.y;
+          sn = tc.y * tt.x + tc.x * tt.y;
+        }
         const float x0 = kt[mt][v], x1 = kt[mt + NT / 2][v];
         kt[mt][v] = x0 * cs - x1 * sn;
         kt[mt + NT / 2][v] = x0 * sn + x1 * cs;
@@ -1659,22 +1700,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
       for (int i = 0; i < 8; ++i) ak[i] = (_Float16)kt[ks >> 1][8 * (ks & 1) + i];
       const int off = qrow + (ks * 2 + q) * 16;
-      s = mfma32_f16(ak, *(const f16x8*)(lds + L.q_hi + off), s);
-      s = mfma32_f16(ak, *(const f16x8*)(lds + L.q_lo + off), s);
+      const uint8_t* qh = QC ? wq : lds + L.q_hi;
+      const uint8_t* ql = QC ? wq + rows * L.qst : lds + L.q_lo;
+      s = mfma32_f16(ak, *(const f16x8*)(qh + off), s);
+      s = mfma32_f16(ak, *(const f16x8*)(ql + off), s);
     }
-    // 4. mask, chunk statistics, p~
+    // 4. mask (only where a token of the chunk lies past some row's last; lanes past the head's
+    //    rows hold finite values that are never stored), chunk statistics, p~
     float m = -INFINITY;
+    if (c * kTC + kTC - 1 <= len - g.n_q) {  // wave-uniform: every row sees every token
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int tt = c * kTC + d32_row(v, q);
-      s[v] = tt <= lim ? s[v] * g.qscale : -INFINITY;
-      m = fmaxf(m, s[v]);
+      for (int v = 0; v < 16; ++v) {
+        s[v] *= g.qscale;
+        m = fmaxf(m, s[v]);
+      }
+    } else {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int tt = c * kTC + d32_row(v, q);
+        s[v] = tt <= lim ? s[v] * g.qscale : -INFINITY;
+        m = fmaxf(m, s[v]);
+      }
     }
     m = fmaxf(m, __shfl_xor(m, 32, 64));
+    // exp2(-inf - m) is 0; a row with no visible token keeps m = -inf and takes 0 for reference
+    const float mref = m == -INFINITY ? 0.f : m;
     float l = 0.f;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      s[v] = s[v] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s[v] - m);
+      s[v] = __builtin_amdgcn_exp2f(s[v] - mref);
       l += s[v];
     }
     l += __shfl_xor(l, 32, 64);
@@ -3105,10 +3159,13 @@ static hipError_t launch_decode_tail(const Layer& L, const DecodePlan& plan, con
 
 template <int NT>
 static hipError_t launch_scores_rope(const Layer& L, const ProfScope& ps, dim3 grid, size_t lds, hipStream_t s,
-                                     const RopeScoreArgs& ra) {
+                                     const RopeScoreArgs& ra, bool qc) {
   void* argv[] = {(void*)&ra};
-  const void* k = L.latent == STARKV_LATENT_MIX84 ? (const void*)k_scores_rope<STARKV_LATENT_MIX84, NT>
-                                                  : (const void*)k_scores_rope<STARKV_LATENT_BF16, NT>;
+  const void* k = L.latent == STARKV_LATENT_MIX84
+                      ? (qc ? (const void*)k_scores_rope<STARKV_LATENT_MIX84, NT, true>
+                            : (const void*)k_scores_rope<STARKV_LATENT_MIX84, NT, false>)
+                      : (qc ? (const void*)k_scores_rope<STARKV_LATENT_BF16, NT, true>
+                            : (const void*)k_scores_rope<STARKV_LATENT_BF16, NT, false>);
   if (ps.start() && ps.stop()) return hipExtLaunchKernel(k, grid, dim3(256), argv, lds, s, ps.start(), ps.stop(), 0);
   return hipLaunchKernel(k, grid, dim3(256), argv, lds, s);
 }
@@ -3134,6 +3191,8 @@ static hipError_t launch_decode_rope(const Layer& L, const DecodePlan& plan, con
   ra.cl = plan.ws.cl;
   ra.g = g;
   ra.rope_theta = L.rope_theta;
+  ra.rope_w = L.d_rope_w;
+  ra.rope_tab = (const float2*)L.d_rope_tab;
   int rmax = 1, npair_max = 1;
   for (int gk = 0; gk < L.H_kv; ++gk) {
     rmax = std::max(rmax, L.rk[gk]);
@@ -3151,12 +3210,18 @@ static hipError_t launch_decode_rope(const Layer& L, const DecodePlan& plan, con
   ra.cpw = cpw;
   ra.seq = seq;
   const dim3 grid(ceil_div(max_nch, 4 * cpw), g.H_kv, g.B);
-  const size_t lds = RopeLds(g.d_h, ra.rpad, g.G * g.n_q, npair_max).total;
+  // a few query rows per KV head: each wave turns them by its chunk's base angle (cheaper than
+  // composing the two angles for every key element), while two workgroups still fit on a CU
+  const int rows = g.G * g.n_q;
+  const size_t lds_plain = RopeLds(g.d_h, ra.rpad, rows, npair_max, false).total;
+  const size_t lds_qc = RopeLds(g.d_h, ra.rpad, rows, npair_max, true).total;
+  const bool qc = rows <= 8 && lds_qc <= std::max(lds_plain, (size_t)80 * 1024);
+  const size_t lds = qc ? lds_qc : lds_plain;
   if (lds > 160 * 1024) return hipErrorInvalidValue;
   hipError_t e;
   {
     ProfScope ps("decode_scores");
-    e = g.d_h == 64 ? launch_scores_rope<2>(L, ps, grid, lds, s, ra) : launch_scores_rope<4>(L, ps, grid, lds, s, ra);
+    e = g.d_h == 64 ? launch_scores_rope<2>(L, ps, grid, lds, s, ra, qc) : launch_scores_rope<4>(L, ps, grid, lds, s, ra, qc);
     if (e != hipSuccess) return e;
   }
   return launch_decode_tail(L, plan, kts, seq, out, k_rows, v_tiles, s, false);

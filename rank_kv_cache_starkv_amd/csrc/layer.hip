@@ -8,6 +8,8 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
+#include <vector>
 
 #include "device_common.h"
 #include "starkv_internal.h"
@@ -115,6 +117,8 @@ int layer_init(const starkv_layer_desc& d, Layer* L) {
   return STARKV_OK;
 }
 
+int layer_write_rope(Layer* L);
+
 int layer_upload_tables(Layer* L) {
   const int NS = L->key_slots + L->val_slots;
   // padded to a multiple of 16 entries (-1): a 16-slot GEMM tile reads its entries unclamped
@@ -177,8 +181,11 @@ int layer_upload_tables(Layer* L) {
   }
   const int H = L->H_kv;
   // one allocation: slot_chan | koff(H+1) | n8(H) | off8(H+1) | off4(H+1) | sp | src | rot | absmax
+  // | (16-byte aligned) rotary frequencies [d_h / 2] (double) | rotary table [32][d_h / 2] (float2),
+  // the last two written by starkv_layer_set_rope
   size_t n_int = (size_t)NSP + (H + 1) + H + (H + 1) + (H + 1);
-  size_t bytes = n_int * 4 + (size_t)L->n_lat * 4 * 4;
+  const size_t o_rope = (n_int * 4 + (size_t)L->n_lat * 4 * 4 + 15) & ~(size_t)15;
+  size_t bytes = o_rope + (size_t)(L->d_h / 2) * 8 + 32 * (size_t)(L->d_h / 2) * 8;
   std::vector<uint8_t> host(bytes, 0);
   size_t o = 0;
   auto put = [&](const void* p, size_t nb) { memcpy(host.data() + o, p, nb); o += nb; };
@@ -208,6 +215,30 @@ int layer_upload_tables(Layer* L) {
   L->d_src = (int*)(b + o); o += L->n_lat * 4;
   L->d_rot = (int*)(b + o); o += L->n_lat * 4;
   L->d_absmax = (uint32_t*)(b + o);
+  L->d_rope_w = (double*)(b + o_rope);
+  L->d_rope_tab = (float*)(b + o_rope + (size_t)(L->d_h / 2) * 8);
+  return layer_write_rope(L);
+}
+
+// The rotation's frequencies theta^(-2 j / d_h) and the (cos, sin) of r times them for the 32
+// token offsets of a tile, in fp64 (the table rounded to fp32), into the layer's device tables;
+// nothing when the layer has no rotation or no device tables yet.
+int layer_write_rope(Layer* L) {
+  if (!L->dev_tables || !(L->rope_theta > 0.f)) return STARKV_OK;
+  const int np = L->d_h / 2;
+  std::vector<double> w(np);
+  std::vector<float> tab(32 * (size_t)np * 2);
+  const double lt = std::log2((double)L->rope_theta);
+  for (int j = 0; j < np; ++j) w[j] = std::exp2(-2.0 * (double)j / (double)L->d_h * lt);
+  for (int r = 0; r < 32; ++r)
+    for (int j = 0; j < np; ++j) {
+      const double ang = (double)r * w[j];
+      tab[2 * ((size_t)r * np + j)] = (float)std::cos(ang);
+      tab[2 * ((size_t)r * np + j) + 1] = (float)std::sin(ang);
+    }
+  if (hipMemcpy(L->d_rope_w, w.data(), np * sizeof(double), hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemcpy(L->d_rope_tab, tab.data(), tab.size() * sizeof(float), hipMemcpyHostToDevice) != hipSuccess)
+    return STARKV_EHIP;
   return STARKV_OK;
 }
 

@@ -95,6 +95,8 @@ struct Layer {
   // device tables (owned)
   void* dev_tables = nullptr;
   int* d_slot_chan = nullptr;  // [key_slots + val_slots] natural channel of each GEMM column or -1
+  double* d_rope_w = nullptr;  // rotary layers: [d_h / 2] theta^(-2 j / d_h)
+  float* d_rope_tab = nullptr;  // rotary layers: [32][d_h / 2] (cos, sin) of r theta^(-2 j / d_h)
   int* d_koff = nullptr;
   int* d_n8 = nullptr;
   int* d_off8 = nullptr;
