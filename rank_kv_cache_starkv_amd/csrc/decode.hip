@@ -2710,7 +2710,8 @@ __global__ __launch_bounds__(256) void k_zmerge(MergeArgs a) {
 // are added through LDS, wave w finishing column slice w (32x32x16 bf16 MFMA).  Loads are
 // unconditional and double-buffered: rows past the end read the last row (not stored); channels at
 // or past r_v are zero in z~ and masked in B_v (their address clamped into the row).
-__global__ __launch_bounds__(256, 2) void k_upproj_tall(MergeArgs a) {
+template <int RT>
+__global__ __launch_bounds__(256, 3 - RT) void k_upproj_tall(MergeArgs a) {
   constexpr int KB = 1;   // 16-channel K-steps per load batch
   constexpr int NCS = 4;  // 32-column slices per pass
   __shared__ float part[4][NCS][16][64];  // [wave][column slice][D element][lane]
@@ -2720,8 +2721,13 @@ __global__ __launch_bounds__(256, 2) void k_upproj_tall(MergeArgs a) {
   const int Rg = g.B * rph;
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int r = lane & 31, q = lane >> 5;
-  const int rr = min((int)blockIdx.y * 32 + r, Rg - 1);
-  const float* zr = a.zt + ((size_t)(rr / rph) * g.M_pad + gk * rph + rr % rph) * g.rv_ld + 8 * q;
+  const int row0 = blockIdx.y * 32 * RT;  // first row of this workgroup's RT row tiles
+  const float* zr[RT];
+#pragma unroll
+  for (int i = 0; i < RT; ++i) {
+    const int rr = min(row0 + 32 * i + r, Rg - 1);
+    zr[i] = a.zt + ((size_t)(rr / rph) * g.M_pad + gk * rph + rr % rph) * g.rv_ld + 8 * q;
+  }
   const int nks = g.rv_ld / 16;
   const int kq = (nks + 3) / 4;
   const int k_beg = min(nks, wave * kq), k_end = min(nks, k_beg + kq);
@@ -2731,45 +2737,53 @@ __global__ __launch_bounds__(256, 2) void k_upproj_tall(MergeArgs a) {
 #pragma unroll
     for (int c = 0; c < NCS; ++c)
       bp[c] = (const uint16_t*)a.B_vt + (size_t)(gk * g.d_h + min(cs0 + c, ncs - 1) * 32 + r) * g.r_v;
-    f32x16 acc[NCS];
+    f32x16 acc[RT][NCS];
 #pragma unroll
-    for (int c = 0; c < NCS; ++c)
+    for (int i = 0; i < RT; ++i)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[c][v] = 0.f;
-    auto loadb = [&](u32x4 (&z)[KB][2], u32x4 (&bw)[KB][NCS], int ks0) {
+      for (int c = 0; c < NCS; ++c)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][c][v] = 0.f;
+    auto loadb = [&](u32x4 (&z)[KB][RT][2], u32x4 (&bw)[KB][NCS], int ks0) {
 #pragma unroll
       for (int u = 0; u < KB; ++u) {
         const int kc = 16 * min(ks0 + u, nks - 1);
-        z[u][0] = ld16(zr + kc);
-        z[u][1] = ld16(zr + kc + 4);
+#pragma unroll
+        for (int i = 0; i < RT; ++i) {
+          z[u][i][0] = ld16(zr[i] + kc);
+          z[u][i][1] = ld16(zr[i] + kc + 4);
+        }
 #pragma unroll
         for (int c = 0; c < NCS; ++c) bw[u][c] = ld16(bp[c] + min(kc + 8 * q, g.r_v - 8));
       }
     };
-    auto compb = [&](u32x4 (&z)[KB][2], u32x4 (&bw)[KB][NCS], int ks0) {
+    auto compb = [&](u32x4 (&z)[KB][RT][2], u32x4 (&bw)[KB][NCS], int ks0) {
 #pragma unroll
       for (int u = 0; u < KB; ++u) {
         const int kc = 16 * (ks0 + u);
         const bool live = ks0 + u < k_end && kc + 8 * q < g.r_v;
-        u32x4 ah, al;
 #pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-          const float z0 = __uint_as_float(z[u][e2 >> 1][2 * (e2 & 1)]);
-          const float z1 = __uint_as_float(z[u][e2 >> 1][2 * (e2 & 1) + 1]);
-          const uint16_t h0 = f32_to_bf16(z0), h1 = f32_to_bf16(z1);
-          const uint16_t l0 = f32_to_bf16(z0 - bf16_to_f32(h0)), l1 = f32_to_bf16(z1 - bf16_to_f32(h1));
-          ah[e2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-          al[e2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
-        }
+        for (int i = 0; i < RT; ++i) {
+          u32x4 ah, al;
 #pragma unroll
-        for (int c = 0; c < NCS; ++c) {
-          const u32x4 bb = live ? bw[u][c] : u32x4{0, 0, 0, 0};
-          acc[c] = mfma32_bf16(as_bf16x8(ah), as_bf16x8(bb), acc[c]);
-          acc[c] = mfma32_bf16(as_bf16x8(al), as_bf16x8(bb), acc[c]);
+          for (int e2 = 0; e2 < 4; ++e2) {
+            const float z0 = __uint_as_float(z[u][i][e2 >> 1][2 * (e2 & 1)]);
+            const float z1 = __uint_as_float(z[u][i][e2 >> 1][2 * (e2 & 1) + 1]);
+            const uint16_t h0 = f32_to_bf16(z0), h1 = f32_to_bf16(z1);
+            const uint16_t l0 = f32_to_bf16(z0 - bf16_to_f32(h0)), l1 = f32_to_bf16(z1 - bf16_to_f32(h1));
+            ah[e2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+            al[e2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+          }
+#pragma unroll
+          for (int c = 0; c < NCS; ++c) {
+            const u32x4 bb = live ? bw[u][c] : u32x4{0, 0, 0, 0};
+            acc[i][c] = mfma32_bf16(as_bf16x8(ah), as_bf16x8(bb), acc[i][c]);
+            acc[i][c] = mfma32_bf16(as_bf16x8(al), as_bf16x8(bb), acc[i][c]);
+          }
         }
       }
     };
-    u32x4 zA[KB][2], bA[KB][NCS], zB[KB][2], bB[KB][NCS];
+    u32x4 zA[KB][RT][2], bA[KB][NCS], zB[KB][RT][2], bB[KB][NCS];
     loadb(zA, bA, k_beg);
     for (int ks = k_beg; ks < k_end; ks += 2 * KB) {
       loadb(zB, bB, ks + KB);
@@ -2778,27 +2792,31 @@ __global__ __launch_bounds__(256, 2) void k_upproj_tall(MergeArgs a) {
       loadb(zA, bA, ks + 2 * KB);
       compb(zB, bB, ks + KB);
     }
-    // the four K-quarters of every column slice, added by the wave that finishes that slice
+    // the four K-quarters of every column slice, added by the wave that finishes that slice;
+    // one row tile at a time through the shared partial tiles
 #pragma unroll
-    for (int c = 0; c < NCS; ++c)
+    for (int i = 0; i < RT; ++i) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) part[wave][c][v][lane] = acc[c][v];
-    __syncthreads();
-    const int cs = cs0 + wave;
-    if (cs < ncs) {
+      for (int c = 0; c < NCS; ++c)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float o = part[0][wave][v][lane] + part[1][wave][v][lane] + part[2][wave][v][lane] +
-                        part[3][wave][v][lane];
-        const int orow = blockIdx.y * 32 + d32_row(v, q);
-        if (orow >= Rg) continue;
-        const int ob = orow / rph, iw = orow % rph;
-        const int hh = iw / g.n_q, j = iw % g.n_q;
-        const int h = gk * g.G + hh;
-        ((uint16_t*)a.out)[(((size_t)ob * g.n_q + j) * g.H_q + h) * g.d_h + cs * 32 + r] = f32_to_bf16(o);
+        for (int v = 0; v < 16; ++v) part[wave][c][v][lane] = acc[i][c][v];
+      __syncthreads();
+      const int cs = cs0 + wave;
+      if (cs < ncs) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float o = part[0][wave][v][lane] + part[1][wave][v][lane] + part[2][wave][v][lane] +
+                          part[3][wave][v][lane];
+          const int orow = row0 + 32 * i + d32_row(v, q);
+          if (orow >= Rg) continue;
+          const int ob = orow / rph, iw = orow % rph;
+          const int hh = iw / g.n_q, j = iw % g.n_q;
+          const int h = gk * g.G + hh;
+          ((uint16_t*)a.out)[(((size_t)ob * g.n_q + j) * g.H_q + h) * g.d_h + cs * 32 + r] = f32_to_bf16(o);
+        }
       }
+      __syncthreads();  // the partial tiles are reused by the next row tile or pass
     }
-    __syncthreads();  // the partial tiles are reused by the next pass
   }
 }
 
@@ -3441,7 +3459,12 @@ static hipError_t launch_decode_tail(const Layer& L, const DecodePlan& plan, con
     ProfScope ps("decode_upproj");
     const dim3 gm(g.H_kv * (g.d_h / 16), (Rg + 15) / 16);
     if (tall)
-      e = launch_k(ps, k_upproj_tall, dim3(g.H_kv, (Rg + 31) / 32), dim3(256), s, ma);
+      // two row tiles per workgroup while that leaves at least 128 workgroups: B_v^g is fetched
+      // by half as many workgroups (the kernel is bound by the bytes each CU pulls from L2)
+      if ((long)g.H_kv * ((Rg + 63) / 64) >= 128)
+        e = launch_k(ps, k_upproj_tall<2>, dim3(g.H_kv, (Rg + 63) / 64), dim3(256), s, ma);
+      else
+        e = launch_k(ps, k_upproj_tall<1>, dim3(g.H_kv, (Rg + 31) / 32), dim3(256), s, ma);
     else if (L.dtype == STARKV_F32)
       e = vec ? launch_k(ps, k_upproj<STARKV_F32, true>, gm, dim3(256), s, ma)
               : launch_k(ps, k_upproj<STARKV_F32, false>, gm, dim3(256), s, ma);
