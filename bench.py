@@ -577,6 +577,102 @@ def measure_prefill(w, args, dev, n_q: int, steps: int, warmup: int) -> dict:
     }
 
 
+def measure_append(w, args, dev, n_new: int, steps: int, warmup: int) -> dict:
+    """starkv_compress_append of n_new tokens per sequence (B x n_new rows of hidden states
+    projected, quantised and packed into the cache), over enough rotated layers that the factors
+    come from HBM; graph of `steps` calls, with the append kernel's MFMA and HBM rates."""
+    import torch
+    import rank_kv_cache_starkv_amd as S
+    from rank_kv_cache_starkv_amd import inputs as I
+
+    tdt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    lf = I.layer_factors(w, 0)
+    U = [torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev) for a in (lf.U_k, lf.V_k, lf.U_v, lf.V_v)]
+    Xcal = I.as_dtype(I.x_calibration(w), w.dtype) if w.latent in QUANTIZED else None
+    T_max = -(-n_new // 32) * 32
+    lens_pre = np.zeros(w.B, np.int32)  # every call writes positions [0, n_new) again
+
+    def new_layer():
+        L = S.Layer(w.H_q, w.H_kv, w.d_h, w.d, w.dtype, w.latent, lf.s_k, lf.tau_k, lf.s_v, lf.tau_v)
+        L.build_factors(*U)
+        if Xcal is not None:
+            L.calibrate(to_dev_bf16(Xcal, dev) if w.dtype == "bf16" else torch.from_numpy(Xcal).to(dev))
+        return L
+
+    probe = new_layer()
+    kb, vb = probe.cache_bytes(w.B, T_max)
+    inf = probe.info
+    per_layer = kb + vb + inf["a_bytes"]
+    n_layers = args.layers or max(2, math.ceil(MIN_ROTATION_BYTES / per_layer))
+    layers = [probe] + [new_layer() for _ in range(n_layers - 1)]
+    caches = [L.new_cache(w.B, T_max) for L in layers]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(2606_08382)
+    X = torch.randn((w.B, n_new, w.d), generator=gen, device=dev, dtype=torch.float32).to(tdt)
+    log(f"[append] {w.name}: B={w.B} n_new={n_new} ({w.B * n_new} rows), {n_layers} layers x "
+        f"{per_layer / 2**20:.0f} MiB")
+    for i in range(warmup):
+        layers[i % n_layers].append(caches[i % n_layers], X, lens_pre)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        layers[0].append(caches[0], X, lens_pre)
+        side.synchronize()
+        with torch.cuda.graph(graph, stream=side):
+            for i in range(steps):
+                layers[i % n_layers].append(caches[i % n_layers], X, lens_pre)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    graph.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    log(f"[time] graph: {steps} calls, {ms * 1000:.2f} us/call")
+    S.profile_enable(True)
+    S.profile_read(reset=True)
+    for i in range(steps):
+        layers[i % n_layers].append(caches[i % n_layers], X, lens_pre)
+    torch.cuda.synchronize()
+    prof = S.profile_read(reset=True)
+    S.profile_enable(False)
+    kern_us = {k: 1000.0 * t / n for k, (n, t) in prof.items()}
+    for k, us in sorted(kern_us.items()):
+        log(f"[kernel] {k:14s} {us:9.2f} us/launch ({prof[k][0]} launches)")
+    M = w.B * n_new
+    n_lat = int(np.sum(probe.ranks)) + int(probe.r_v)
+    flops = 2.0 * M * w.d * n_lat
+    elem = 4 if w.dtype == "f32" else 2
+    byts = float(inf["a_bytes"]) + M * w.d * elem + M * (inf["k_row_bytes"] + inf["v_tile_rows"] * elem_of(w.latent))
+    us = kern_us["append"]
+    tf = flops / (us * 1e-6) / 1e12
+    gbps = byts / (us * 1e-6) / 1e9
+    log(f"[append] {flops / 1e9:.2f} GFLOP, {byts / 1e6:.1f} MB per call: {tf:.1f} TFLOP/s "
+        f"({tf / 2500.0:.3f} of MFMA peak), {gbps:.0f} GB/s ({gbps / 8000.0:.3f} of HBM peak)")
+    return {
+        "metric": "compress_append: tokens/s projected, quantised and packed into the latent cache",
+        "value": M / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": f"{w.dtype} MFMA, fp32 accumulate, {w.latent} store", "data": "synthetic",
+        "config": {"workload": f"{w.name}-append{n_new}", "batch": w.B, "new_tokens_per_seq": n_new,
+                   "rows": M, "hidden": w.d, "latent_channels": n_lat, "latent": w.latent},
+        "roofline": {"bound": "mfma", "kernel": "append", "achieved": tf, "peak": 2500.0, "unit": "TFLOP/s",
+                     "frac": tf / 2500.0, "traffic": None, "alg_flops_per_launch": flops, "us_per_launch": us},
+        "hbm": {"achieved": gbps, "peak": 8000.0, "unit": "GB/s", "frac": gbps / 8000.0, "alg_bytes_per_launch": byts},
+        "kernel_us": kern_us,
+    }
+
+
+def elem_of(latent: str) -> float:
+    """Bytes per value-tile row element of one token (value tile rows hold one byte, or one
+    bf16/fp32 element, per token)."""
+    return {"f32": 4, "bf16": 2}.get(latent, 1)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -594,6 +690,9 @@ def main() -> int:
     ap.add_argument("--prefill", type=int, default=0, metavar="N",
                     help="time a chunk of N queries per sequence attending over reconstructed keys and values "
                          "(starkv_prefill_attention) instead of the decode step")
+    ap.add_argument("--append", type=int, default=0, metavar="N",
+                    help="time starkv_compress_append of N tokens per sequence (the append GEMM's MFMA and "
+                         "HBM rates) instead of the decode step")
     ap.add_argument("--rope", type=float, default=0.0, metavar="THETA",
                     help="rotary layers (base THETA): decode and prefill attend over reconstructed keys")
     ap.add_argument("--copy-probe", action="store_true", help=f"copy {COPY_PROBE_MIB} MiB device to device")
@@ -618,6 +717,9 @@ def main() -> int:
     w = I.WORKLOADS[args.workload]
     if args.prefill:
         print(json.dumps(measure_prefill(w, args, dev, args.prefill, args.steps, args.warmup)))
+        return 0
+    if args.append:
+        print(json.dumps(measure_append(w, args, dev, args.append, args.steps, args.warmup)))
         return 0
     r = measure(w, args, dev, with_cpu=not args.no_cpu and not args.rope, steps=args.steps, warmup=args.warmup)
     result = {

@@ -247,22 +247,24 @@ __device__ __forceinline__ void gemm_tile_epilogue(const GemmArgs& a, int mb, in
 }
 
 // bf16 operands, d a multiple of 64: the X and A_t tiles stream through LDS.  Workgroup tile
-// 64 token rows x 64 cache slots, four waves in 2 x 2 quadrants of 32 x 32, each over the whole
-// K (no partial sums to add).  K advances in blocks of 64: a block's two 8 KiB operand tiles
-// arrive by 16-byte LDS DMA (each wave issues two loads per tile) into a ring of NST stages, NST - 1
-// blocks ahead of the MFMAs, so the loads of a CU run deep without holding registers.  In a tile,
-// row R's eight 16-byte K-chunks sit at chunk c ^ ((R >> 1) & 7): the 16 lanes of a fragment read
-// (rows R .. R + 15, one chunk) then hit 16 different 4-bank groups.  Rows past M and padding
-// columns load row 0 / channel 0 (valid addresses); such rows are never stored and padding
-// columns store zero.  Grid and epilogue as k_latent_gemm (MODE 0: store, MODE 1: absmax).
-// NST stages of 16 KiB each in dynamic LDS (4: two workgroups per CU).  On MI355X the kernel is
-// bound by the operand bytes each CU pulls (about 40 GB/s per CU from L2): eight stages, or K
-// split over more workgroups with a reduce pass, measured no faster on the 256 x 2560 x 5120 step.
-template <int MODE, int NST>
+// T token rows x T cache slots (T = 64 or 128), four waves in 2 x 2 quadrants of T/2 x T/2, each
+// in 32 x 32 MFMA tiles over the whole K (no partial sums to add).  K advances in blocks of 64:
+// a block's two operand tiles (T rows of 128 bytes each) arrive by 16-byte LDS DMA into a ring of
+// NST stages, NST - 1 blocks ahead of the MFMAs, so the loads of a CU run deep without holding
+// registers.  In a tile, row R's eight 16-byte K-chunks sit at chunk c ^ ((R >> 1) & 7): the 16
+// lanes of a fragment read (rows R .. R + 15, one chunk) then hit 16 different 4-bank groups.
+// Rows past M and padding columns load row 0 / channel 0 (valid addresses); such rows are never
+// stored and padding columns store zero.  Grid as k_latent_gemm (MODE 0: store, MODE 1: absmax).
+// On MI355X the kernel is bound by the operand bytes each CU pulls from L2 (about 40 GB/s per
+// workgroup): a 128 x 128 tile pulls half the bytes per flop of a 64 x 64 one and serves the
+// appends of many rows; short blocks of rows keep 64 x 64 tiles for their workgroup count.
+template <int MODE, int NST, int T = 64>
 __global__ __launch_bounds__(256) void k_latent_gemm_dma(GemmArgs a) {
-  constexpr int TB = 64 * 64 * 2;  // bytes of one operand tile of a K block
+  constexpr int TB = T * 128;      // bytes of one operand tile of a K block
+  constexpr int LP = T / 32;       // 16-byte DMA loads per wave per tile
+  constexpr int MQ = T / 64;       // 32 x 32 MFMA tiles per wave quadrant, each way (1 or 2)
+  static_assert(T == 64 || T == 128, "tile");
   extern __shared__ __align__(16) uint8_t ring_raw[];
-  uint8_t (*ring)[2][TB] = (uint8_t (*)[2][TB])ring_raw;
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   const int r = lane & 31, q = lane >> 5;
@@ -271,16 +273,16 @@ __global__ __launch_bounds__(256) void k_latent_gemm_dma(GemmArgs a) {
     const int k = blockIdx.x >> 3;
     rt = k % a.xmap_rt;
     ctl = (blockIdx.x & 7) + 8 * (k / a.xmap_rt);
-    if (ctl * 64 >= a.NS) return;  // whole workgroup
+    if (ctl * T >= a.NS) return;  // whole workgroup
   }
-  const int mb = rt * 64, sb = ctl * 64;
-  // this lane's DMA sources: load jj of the wave fills tile slot i = 64 (2 wave + jj) + lane,
+  const int mb = rt * T, sb = ctl * T;
+  // this lane's DMA sources: load jj of the wave fills tile slot i = 64 (LP wave + jj) + lane,
   // i.e. row i / 8 and stored chunk i % 8, which holds K-chunk (i % 8) ^ ((row >> 1) & 7)
-  const uint16_t* xsrc[2];
-  const uint16_t* wsrc[2];
+  const uint16_t* xsrc[LP];
+  const uint16_t* wsrc[LP];
 #pragma unroll
-  for (int jj = 0; jj < 2; ++jj) {
-    const int i = 64 * (2 * wave + jj) + lane;
+  for (int jj = 0; jj < LP; ++jj) {
+    const int i = 64 * (LP * wave + jj) + lane;
     const int row = i >> 3;
     const int kc = (i & 7) ^ ((row >> 1) & 7);
     const int xr = mb + row < a.M ? mb + row : 0;
@@ -289,42 +291,67 @@ __global__ __launch_bounds__(256) void k_latent_gemm_dma(GemmArgs a) {
     wsrc[jj] = (const uint16_t*)a.A_t + (size_t)(ch >= 0 ? ch : 0) * a.d + 8 * kc;
   }
   const int nkb = a.d / 64;
-  const uint32_t ring0 = lds_addr(ring);
+  const uint32_t ring0 = lds_addr(ring_raw);
   auto issue = [&](int kb, int st) {
     kb = min(kb, nkb - 1);  // past the end: reload the last block (never read)
     const uint32_t xb = ring0 + st * 2 * TB, wb = xb + TB;
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      lds_dma16(xsrc[jj] + 64 * kb, xb + 1024 * (2 * wave + jj));
-      lds_dma16(wsrc[jj] + 64 * kb, wb + 1024 * (2 * wave + jj));
+    for (int jj = 0; jj < LP; ++jj) {
+      lds_dma16(xsrc[jj] + 64 * kb, xb + 1024 * (LP * wave + jj));
+      lds_dma16(wsrc[jj] + 64 * kb, wb + 1024 * (LP * wave + jj));
     }
   };
   const int wm = wave & 1, wn = wave >> 1;
-  const int xrow = 32 * wm + r, wrow = 32 * wn + r;
-  const int xo = xrow * 128, wo = wrow * 128;
-  const int xsw = (xrow >> 1) & 7, wsw = (wrow >> 1) & 7;
-  f32x16 acc;
+  int xo[MQ], xsw[MQ], wo[MQ], wsw[MQ];
 #pragma unroll
-  for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+  for (int i = 0; i < MQ; ++i) {
+    const int xrow = (T / 2) * wm + 32 * i + r, wrow = (T / 2) * wn + 32 * i + r;
+    xo[i] = xrow * 128;
+    wo[i] = wrow * 128;
+    xsw[i] = (xrow >> 1) & 7;
+    wsw[i] = (wrow >> 1) & 7;
+  }
+  f32x16 acc[MQ][MQ];
+#pragma unroll
+  for (int i = 0; i < MQ; ++i)
+#pragma unroll
+    for (int j = 0; j < MQ; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 #pragma unroll
   for (int u = 0; u < NST - 1; ++u) issue(u, u);
   for (int kb = 0; kb < nkb; ++kb) {
-    vm_wait<4 * (NST - 2)>();      // this wave's loads of block kb are in
-    __builtin_amdgcn_s_barrier();  // ... and every wave's; block kb - 1's stage is free
+    vm_wait<2 * LP * (NST - 2)>();  // this wave's loads of block kb are in
+    __builtin_amdgcn_s_barrier();   // ... and every wave's; block kb - 1's stage is free
     asm volatile("" ::: "memory");
     issue(kb + NST - 1, (kb + NST - 1) % NST);
-    const uint8_t* xt = ring[kb % NST][0];
-    const uint8_t* wt = ring[kb % NST][1];
+    const uint8_t* xt = ring_raw + (kb % NST) * 2 * TB;
+    const uint8_t* wt = xt + TB;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int c = 2 * ks + q;
-      const u32x4 xf = *(const u32x4*)(xt + xo + 16 * (c ^ xsw));
-      const u32x4 wf = *(const u32x4*)(wt + wo + 16 * (c ^ wsw));
-      acc = mfma32_bf16(as_bf16x8(xf), as_bf16x8(wf), acc);
+      u32x4 xf[MQ], wf[MQ];
+#pragma unroll
+      for (int i = 0; i < MQ; ++i) {
+        xf[i] = *(const u32x4*)(xt + xo[i] + 16 * (c ^ xsw[i]));
+        wf[i] = *(const u32x4*)(wt + wo[i] + 16 * (c ^ wsw[i]));
+      }
+#pragma unroll
+      for (int i = 0; i < MQ; ++i)
+#pragma unroll
+        for (int j = 0; j < MQ; ++j) acc[i][j] = mfma32_bf16(as_bf16x8(xf[i]), as_bf16x8(wf[j]), acc[i][j]);
     }
   }
   vm_wait<0>();  // the trailing reloads land before the workgroup ends
-  gemm_tile_epilogue<MODE>(a, mb, sb, wm, wn, acc);
+  // (sub-tiles named with constant indexes: a loop the compiler leaves rolled would index the
+  // accumulators dynamically, through scratch)
+  const int m0 = mb + (T / 2) * wm, s0 = sb + (T / 2) * wn;
+  gemm_tile_epilogue<MODE>(a, m0, s0, 0, 0, acc[0][0]);
+  if (MQ > 1) {
+    gemm_tile_epilogue<MODE>(a, m0, s0 + 32, 0, 0, acc[0][MQ - 1]);
+    gemm_tile_epilogue<MODE>(a, m0 + 32, s0, 0, 0, acc[MQ - 1][0]);
+    gemm_tile_epilogue<MODE>(a, m0 + 32, s0 + 32, 0, 0, acc[MQ - 1][MQ - 1]);
+  }
 }
 
 __global__ void k_fill_u32(uint32_t* p, int n, uint32_t v) {
@@ -404,6 +431,21 @@ static hipError_t launch_lds(const ProfScope& ps, void (*kernel)(A), dim3 grid, 
   return hipLaunchKernel((const void*)kernel, grid, block, argv, lds, s);
 }
 
+// The DMA append GEMM (bf16, d a multiple of 64): 128 x 128 tiles when they still give every CU
+// at least two workgroups; otherwise 64 x 64 tiles, with the XCD-aware grid for a short block of
+// rows (the row tiles of a column tile run on one XCD and share its L2 copy of that slab of A).
+static hipError_t launch_dma_append(const ProfScope& ps, GemmArgs& a, int M, hipStream_t s) {
+  const int r128 = (M + 127) / 128, c128 = (a.NS + 127) / 128;
+  if ((long)r128 * c128 >= 512)
+    return launch_lds(ps, k_latent_gemm_dma<0, 3, 128>, dim3(r128, c128), dim3(256), 3 * 2 * 128 * 128, s, a);
+  const int n_rt = (M + 63) / 64, n_ct = (a.NS + 63) / 64;
+  if (n_rt <= 16) {
+    a.xmap_rt = n_rt;
+    return launch_lds(ps, k_latent_gemm_dma<0, 4>, dim3(8 * n_rt * ((n_ct + 7) / 8)), dim3(256), 4 * 2 * 8192, s, a);
+  }
+  return launch_lds(ps, k_latent_gemm_dma<0, 4>, dim3(n_rt, n_ct), dim3(256), 4 * 2 * 8192, s, a);
+}
+
 hipError_t launch_append(const Layer& L, const starkv_cache& c, const void* X_new, int B, int n_new,
                          const int32_t* lens, hipStream_t s) {
   GemmArgs a = {};
@@ -416,14 +458,8 @@ hipError_t launch_append(const Layer& L, const starkv_cache& c, const void* X_ne
     // plane words would take four writers)
     e = launch_k(ps, k_latent_gemm_skinny<STARKV_BF16, 16, true>, dim3((a.NS + 15) / 16), dim3(512), s, a);
   } else if (L.pack3) {
-    // packed 3-bit planes from the 64 x 64 tiles
-    const int n_rt = (B * n_new + 63) / 64, n_ct = (a.NS + 63) / 64;
-    if (n_rt <= 16) {
-      a.xmap_rt = n_rt;
-      e = launch_lds(ps, k_latent_gemm_dma<0, 4>, dim3(8 * n_rt * ((n_ct + 7) / 8)), dim3(256), 4 * 2 * 8192, s, a);
-    } else {
-      e = launch_lds(ps, k_latent_gemm_dma<0, 4>, dim3(n_rt, n_ct), dim3(256), 4 * 2 * 8192, s, a);
-    }
+    // packed 3-bit planes from the GEMM tiles (32-slot groups in the lanes of a half-wave)
+    e = launch_dma_append(ps, a, B * n_new, s);
   } else if (B * n_new <= 8 && L.d % 64 == 0) {
     const dim3 grid((a.NS + 7) / 8);
     if (L.dtype == STARKV_BF16)
@@ -441,15 +477,8 @@ hipError_t launch_append(const Layer& L, const starkv_cache& c, const void* X_ne
       e = mix ? launch_k(ps, k_latent_gemm_skinny<STARKV_F32, 16, true>, grid, dim3(512), s, a)
               : launch_k(ps, k_latent_gemm_skinny<STARKV_F32, 16, false>, grid, dim3(512), s, a);
   } else if (L.dtype == STARKV_BF16 && L.d % 64 == 0) {
-    // bf16: operands staged through LDS; a short block of tokens takes the XCD-aware grid (the
-    // row tiles of a column tile on one XCD, sharing its L2 copy of that slab of A)
-    const int n_rt = (B * n_new + 63) / 64, n_ct = (a.NS + 63) / 64;
-    if (n_rt <= 16) {
-      a.xmap_rt = n_rt;
-      e = launch_lds(ps, k_latent_gemm_dma<0, 4>, dim3(8 * n_rt * ((n_ct + 7) / 8)), dim3(256), 4 * 2 * 8192, s, a);
-    } else {
-      e = launch_lds(ps, k_latent_gemm_dma<0, 4>, dim3(n_rt, n_ct), dim3(256), 4 * 2 * 8192, s, a);
-    }
+    // bf16: operands staged through LDS
+    e = launch_dma_append(ps, a, B * n_new, s);
   } else {
     const int n_rt = (B * n_new + 63) / 64, n_ct = (a.NS + 63) / 64;
     if (n_rt <= 16) {
