@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define STARKV_ABI_VERSION 1
+#define STARKV_ABI_VERSION 2
 
 /* status codes */
 #define STARKV_OK 0
@@ -258,11 +258,29 @@ int starkv_cache_bytes(const starkv_layer* layer, int B, int T_max, size_t* k_by
  *   starkv_calibrate (mix84 127 / 7, had43 7 / 3; x from the rotated factors for
  *   had43), packed as starkv_cache documents (had43 codes in the same byte regions).
  * X_new: device [B][n_new][d] (dtype).  lens_host: host [B], the lengths before
- * the append (the caller updates its lengths itself).  n_new == 0 is a no-op.
+ * the append (the caller updates its lengths itself).  lens_dev: null, or device
+ * int32 [B] (4-byte aligned) read by the kernels when they run: the tokens then go
+ * after position min(max(lens_dev[b], 0), lens_host[b]), lens_host being an upper
+ * bound (see "Device lengths" below).  n_new == 0 is a no-op.
  * Errors: EINVAL, ECAPACITY (lens_host[b] + n_new > T_max), ESTATE, EHIP.
  */
 int starkv_compress_append(const starkv_layer* layer, const starkv_cache* cache, const void* X_new, int B,
-                           int n_new, const int32_t* lens_host, hipStream_t stream);
+                           int n_new, const int32_t* lens_host, const int32_t* lens_dev, hipStream_t stream);
+
+/*
+ * Device lengths.  The decode calls below and starkv_compress_append take the
+ * sequence lengths twice: lens_host (host memory, read during the call) and lens_dev
+ * (null, or device int32 [B], read by the kernels when they run).  Without lens_dev
+ * the lengths are lens_host.  With it, lens_host is an upper bound that sizes the
+ * plan (the split table over 32-token chunks, the XCD placement, the workspace), and
+ * sequence b has length T_b = min(max(lens_dev[b], n_q), lens_host[b]) (decode) at the
+ * time the kernels run; chunks past T_b count as empty.  A launch sequence captured in
+ * a HIP graph with lens_host at a capacity can so be replayed while the caller
+ * advances lens_dev (the library never writes it).  The work of the kernels follows
+ * lens_host: chunks past T_b are still visited (and masked).  Rotary layers that attend
+ * over reconstructed keys (more than 32 query rows per KV head) return EUNSUPPORTED
+ * with lens_dev.
+ */
 
 /* Workspace bytes that starkv_decode_attention needs for these lengths and n_q. */
 int starkv_decode_workspace_bytes(const starkv_layer* layer, int B, int n_q, const int32_t* lens_host,
@@ -280,15 +298,16 @@ int starkv_decode_workspace_bytes(const starkv_layer* layer, int B, int n_q, con
  *   out[b][j][h] = z B_v[:, g*d_h:(g+1)*d_h]
  * which equals dense attention over K_g = x^_g B_g and V = x^_v B_v.
  * q: device [B][n_q][H_q][d_h] (dtype); out: device, same shape and dtype.
+ * lens_dev: null, or the device lengths (see "Device lengths").
  * ws: device workspace of at least starkv_decode_workspace_bytes() bytes (no
  * alignment beyond 256 bytes needed; contents need no initialisation).
  * Errors: EINVAL (n_q < 1, T < n_q, H_q*n_q > STARKV_MAX_QROWS, ...), ECAPACITY
- * (T > T_max), EWORKSPACE, ESTATE, EHIP.  Deterministic: the same inputs give
- * bit-identical outputs.
+ * (T > T_max), EWORKSPACE, ESTATE, EUNSUPPORTED, EHIP.  Deterministic: the same
+ * inputs give bit-identical outputs.
  */
 int starkv_decode_attention(const starkv_layer* layer, const starkv_cache* cache, const void* q, int B,
-                            int n_q, const int32_t* lens_host, void* out, void* ws, size_t ws_bytes,
-                            hipStream_t stream);
+                            int n_q, const int32_t* lens_host, const int32_t* lens_dev, void* out, void* ws,
+                            size_t ws_bytes, hipStream_t stream);
 
 /*
  * Weight absorption of the key factors into the query projection (Methodology
@@ -312,8 +331,8 @@ int starkv_absorb_query(starkv_layer* layer, const void* W_q, hipStream_t stream
  * ESTATE when no absorbed factors are present.
  */
 int starkv_decode_attention_hidden(const starkv_layer* layer, const starkv_cache* cache, const void* x, int B,
-                                   int n_q, const int32_t* lens_host, void* out, void* ws, size_t ws_bytes,
-                                   hipStream_t stream);
+                                   int n_q, const int32_t* lens_host, const int32_t* lens_dev, void* out,
+                                   void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * One decode step of a layer (Problem Statement: the new tokens' hidden states are
@@ -324,12 +343,14 @@ int starkv_decode_attention_hidden(const starkv_layer* layer, const starkv_cache
  * starkv_decode_attention (at lengths lens_host), bit for bit; with B * n_q <= 16 new
  * rows the append and the query projection share one kernel launch.
  * X_new: device [B][n_q][d] (dtype); q, out: device [B][n_q][H_q][d_h] (dtype).
- * lens_host: host [B], the lengths after the append.  ws: as for
- * starkv_decode_attention (same B, n_q, lens).  Errors: those of the two calls.
+ * lens_host: host [B], the lengths after the append.  lens_dev: null, or the
+ * device lengths after the append (see "Device lengths"; the new tokens go at
+ * T_b - n_q ..).  ws: as for starkv_decode_attention (same B, n_q, lens).  Errors:
+ * those of the two calls.
  */
 int starkv_decode_step(const starkv_layer* layer, const starkv_cache* cache, const void* X_new, const void* q,
-                       int B, int n_q, const int32_t* lens_host, void* out, void* ws, size_t ws_bytes,
-                       hipStream_t stream);
+                       int B, int n_q, const int32_t* lens_host, const int32_t* lens_dev, void* out, void* ws,
+                       size_t ws_bytes, hipStream_t stream);
 
 /*
  * Rotary position embedding of the keys and queries (the Llama-family layers the STAR-KV summary
@@ -339,10 +360,12 @@ int starkv_decode_step(const starkv_layer* layer, const starkv_cache* cache, con
  * i < d_h / 2 the pair (x_i, x_{i + d_h/2}) of a key at cache position t, or of query j of a
  * chunk of n_q (position T - n_q + j), is rotated by the angle position * theta^(-2 i / d_h).
  * A position-dependent rotation does not commute with the key up-projection (Problem Statement:
- * the reconstruction cost; Methodology section 2: head-wise key factors keep it per head), so a
- * rotary layer attends over reconstructed keys: starkv_decode_attention, starkv_decode_step and
+ * the reconstruction cost; Methodology section 2: head-wise key factors keep it per head).  With
+ * at most 32 query rows per KV head (G n_q <= 32) the decode calls rebuild each 32-token key tile
+ * of a head from its latent inside the score kernel, rotate it and score it there; values stay
+ * in the latent space.  With more rows starkv_decode_attention, starkv_decode_step and
  * starkv_decode_step_noalloc take the path of starkv_prefill_attention (their workspace query
- * returns its size), and starkv_decode_attention_hidden returns EUNSUPPORTED.
+ * returns its size).  starkv_decode_attention_hidden returns EUNSUPPORTED.
  * Errors: EINVAL (null, rotary_dim < 0 or > d_h, theta not finite and positive), EUNSUPPORTED
  * (rotary_dim != d_h, d_h not a multiple of 64, fp32 layers).  Setup call: not concurrent with
  * other calls on the layer.
@@ -387,8 +410,8 @@ int starkv_prefill_attention(const starkv_layer* layer, const starkv_cache* cach
  */
 #define STARKV_NOALLOC_SCRATCH_BYTES (64u << 20)
 int starkv_decode_step_noalloc(const starkv_layer* layer, const starkv_cache* cache, const void* X_new,
-                               const void* q, int B, int n_q, const int32_t* lens_host, void* out,
-                               hipStream_t stream);
+                               const void* q, int B, int n_q, const int32_t* lens_host, const int32_t* lens_dev,
+                               void* out, hipStream_t stream);
 
 /*
  * Rebuild dense keys and values of sequence b, tokens [t0, t1) (Problem

@@ -73,6 +73,9 @@ EXPORTS = ["starkv_abi_version", "starkv_status_string", "starkv_layer_create", 
            "starkv_decode_step_noalloc", "starkv_layer_set_rope", "starkv_prefill_workspace_bytes",
            "starkv_prefill_attention"]
 
+# the ABI these argument lists describe (STARKV_ABI_VERSION of include/starkv.h)
+ABI_VERSION = 2
+
 _lib = None
 
 
@@ -86,6 +89,9 @@ def lib() -> ctypes.CDLL:
     L = ctypes.CDLL(LIB_PATH)
     vp, ci, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     L.starkv_abi_version.restype = ci
+    if L.starkv_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{LIB_PATH} has ABI {L.starkv_abi_version()}, the binding expects {ABI_VERSION}: "
+                           "rebuild it with __graft_entry__.build()")
     L.starkv_status_string.restype = ctypes.c_char_p
     L.starkv_status_string.argtypes = [ci]
     L.starkv_layer_create.argtypes = [ctypes.POINTER(_Desc), ctypes.POINTER(vp)]
@@ -97,21 +103,22 @@ def lib() -> ctypes.CDLL:
     L.starkv_calibrate.argtypes = [vp, vp, ci, vp, vp]
     L.starkv_bind_scales.argtypes = [vp, vp]
     L.starkv_cache_bytes.argtypes = [vp, ci, ci, ctypes.POINTER(sz), ctypes.POINTER(sz)]
-    L.starkv_compress_append.argtypes = [vp, ctypes.POINTER(_Cache), vp, ci, ci, ctypes.POINTER(ctypes.c_int32), vp]
+    L.starkv_compress_append.argtypes = [vp, ctypes.POINTER(_Cache), vp, ci, ci, ctypes.POINTER(ctypes.c_int32), vp,
+                                         vp]
     L.starkv_decode_workspace_bytes.argtypes = [vp, ci, ci, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(sz)]
     L.starkv_decode_attention.argtypes = [vp, ctypes.POINTER(_Cache), vp, ci, ci, ctypes.POINTER(ctypes.c_int32),
-                                          vp, vp, sz, vp]
+                                          vp, vp, vp, sz, vp]
     L.starkv_decode_step.argtypes = [vp, ctypes.POINTER(_Cache), vp, vp, ci, ci, ctypes.POINTER(ctypes.c_int32),
-                                     vp, vp, sz, vp]
+                                     vp, vp, vp, sz, vp]
     L.starkv_decode_step_noalloc.argtypes = [vp, ctypes.POINTER(_Cache), vp, vp, ci, ci,
-                                             ctypes.POINTER(ctypes.c_int32), vp, vp]
+                                             ctypes.POINTER(ctypes.c_int32), vp, vp, vp]
     L.starkv_layer_set_rope.argtypes = [vp, ctypes.c_float, ci]
     L.starkv_prefill_workspace_bytes.argtypes = [vp, ci, ci, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(sz)]
     L.starkv_prefill_attention.argtypes = [vp, ctypes.POINTER(_Cache), vp, ci, ci, ctypes.POINTER(ctypes.c_int32),
                                            vp, vp, sz, vp]
     L.starkv_absorb_query.argtypes = [vp, vp, vp]
     L.starkv_decode_attention_hidden.argtypes = [vp, ctypes.POINTER(_Cache), vp, ci, ci,
-                                                 ctypes.POINTER(ctypes.c_int32), vp, vp, sz, vp]
+                                                 ctypes.POINTER(ctypes.c_int32), vp, vp, vp, sz, vp]
     L.starkv_reconstruct.argtypes = [vp, ctypes.POINTER(_Cache), ci, ci, ci, vp, vp, vp]
     L.starkv_profile_enable.argtypes = [ci]
     L.starkv_profile_read.argtypes = [ctypes.POINTER(_KernelTime), ci, ctypes.POINTER(ci), ci]
@@ -167,6 +174,17 @@ def _lens(lens, B: int) -> np.ndarray:
 
 def _on_device(t, like) -> bool:
     return t.is_cuda and t.device == like.device
+
+
+def _lens_dev(lens_dev, B: int, like):
+    """Device lengths (int32 [B] on the device of the inputs), or None (0 for the call)."""
+    if lens_dev is None:
+        return None
+    import torch
+    _need(isinstance(lens_dev, torch.Tensor) and lens_dev.dtype == torch.int32 and lens_dev.is_contiguous() and
+          tuple(lens_dev.shape) == (B,), f"lens_dev: contiguous int32 tensor [{B}] expected")
+    _need(_on_device(lens_dev, like), f"lens_dev must be on {like.device}")
+    return _ptr(lens_dev)
 
 
 def _stream(stream=None) -> int:
@@ -332,18 +350,20 @@ class Layer:
         _need(ws.is_contiguous() and _on_device(ws, like), "ws: contiguous tensor on the device of the inputs")
         return ws
 
-    def append(self, cache: Cache, X_new, lens: Sequence[int], stream=None) -> None:
-        """Project X_new [B, n_new, d] into the latent and store it after position lens[b]."""
+    def append(self, cache: Cache, X_new, lens: Sequence[int], stream=None, lens_dev=None) -> None:
+        """Project X_new [B, n_new, d] into the latent and store it after position lens[b] (with
+        lens_dev, an int32 device tensor [B]: after min(lens_dev[b], lens[b]) as the kernels read it)."""
         _need(X_new.dtype == self.torch_dtype and X_new.is_contiguous() and X_new.dim() == 3,
               f"X_new: contiguous {self.torch_dtype} tensor [B, n_new, d] expected")
         _need(int(X_new.shape[2]) == self.d, f"X_new shape {tuple(X_new.shape)}: hidden size must be {self.d}")
         B, n_new = int(X_new.shape[0]), int(X_new.shape[1])
         L = _lens(lens, B)
         _need(X_new.is_cuda, "X_new must be a device tensor")
+        ld = _lens_dev(lens_dev, B, X_new)
         self._check_cache(cache, X_new)
         cs = cache.struct()
         _check(self._lib.starkv_compress_append(self._h, ctypes.byref(cs), _ptr(X_new), B, n_new,
-                                                L.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), _stream(stream)),
+                                                L.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), ld, _stream(stream)),
                "starkv_compress_append")
 
     # -- decode
@@ -358,18 +378,22 @@ class Layer:
         self._ws_memo = (key, n.value)
         return n.value
 
-    def decode(self, cache: Cache, q, lens: Sequence[int], out=None, ws=None, stream=None):
-        """Attention of q [B, n_q, H_q, d_h] over the cache (lens include the n_q query tokens)."""
+    def decode(self, cache: Cache, q, lens: Sequence[int], out=None, ws=None, stream=None, lens_dev=None):
+        """Attention of q [B, n_q, H_q, d_h] over the cache (lens include the n_q query tokens).
+        lens_dev: None, or int32 device lengths [B] read when the kernels run; lens is then their
+        upper bound (it sizes the plan and the workspace)."""
         _need(q.dim() == 4, "q: tensor [B, n_q, H_q, d_h] expected")
         L = _lens(lens, int(q.shape[0]))
         B, n_q = self._check_q(q)
+        ld = _lens_dev(lens_dev, B, q)
         self._check_cache(cache, q)
         need = self.workspace_bytes(B, n_q, L)
         ws = self._workspace(ws, need, q)
         out = self._out(out, q.shape, q)
         cs = cache.struct()
         _check(self._lib.starkv_decode_attention(self._h, ctypes.byref(cs), _ptr(q), B, n_q,
-                                                 L.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), _ptr(out), _ptr(ws),
+                                                 L.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), ld, _ptr(out),
+                                                 _ptr(ws),
                                                  int(ws.numel() * ws.element_size()), _stream(stream)),
                "starkv_decode_attention")
         return out
@@ -381,7 +405,7 @@ class Layer:
               f"W_q: contiguous {self.torch_dtype} device tensor {(self.d, self.H_q * self.d_h)} expected")
         _check(self._lib.starkv_absorb_query(self._h, _ptr(W_q), _stream(stream)), "starkv_absorb_query")
 
-    def decode_hidden(self, cache: Cache, x, lens: Sequence[int], out=None, ws=None, stream=None):
+    def decode_hidden(self, cache: Cache, x, lens: Sequence[int], out=None, ws=None, stream=None, lens_dev=None):
         """Attention with the query taken from hidden states x [B, n_q, d] through the absorbed
         query factors; returns out [B, n_q, H_q, d_h]."""
         _need(x.dtype == self.torch_dtype and x.is_contiguous() and x.dim() == 3,
@@ -390,21 +414,23 @@ class Layer:
         B, n_q = int(x.shape[0]), int(x.shape[1])
         L = _lens(lens, B)
         _need(x.is_cuda, "x must be a device tensor")
+        ld = _lens_dev(lens_dev, B, x)
         self._check_cache(cache, x)
         need = self.workspace_bytes(B, n_q, L)
         ws = self._workspace(ws, need, x)
         out = self._out(out, (B, n_q, self.H_q, self.d_h), x)
         cs = cache.struct()
         _check(self._lib.starkv_decode_attention_hidden(self._h, ctypes.byref(cs), _ptr(x), B, n_q,
-                                                        L.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), _ptr(out),
+                                                        L.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), ld,
+                                                        _ptr(out),
                                                         _ptr(ws), int(ws.numel() * ws.element_size()),
                                                         _stream(stream)),
                "starkv_decode_attention_hidden")
         return out
 
-    def step(self, cache: Cache, X_new, q, lens: Sequence[int], out=None, ws=None, stream=None):
+    def step(self, cache: Cache, X_new, q, lens: Sequence[int], out=None, ws=None, stream=None, lens_dev=None):
         """One decode step: append X_new [B, n_q, d] at lens - n_q, then attention of q
-        [B, n_q, H_q, d_h] over lens (the lengths after the append)."""
+        [B, n_q, H_q, d_h] over lens (the lengths after the append).  lens_dev: as for decode."""
         _need(q.dim() == 4, "q: tensor [B, n_q, H_q, d_h] expected")
         B, n_q = int(q.shape[0]), int(q.shape[1])
         _need(X_new.dtype == self.torch_dtype and X_new.is_contiguous(),
@@ -413,18 +439,20 @@ class Layer:
         L = _lens(lens, B)
         self._check_q(q)
         _need(_on_device(X_new, q), f"X_new must be on {q.device}")
+        ld = _lens_dev(lens_dev, B, q)
         self._check_cache(cache, q)
         need = self.workspace_bytes(B, n_q, L)
         ws = self._workspace(ws, need, q)
         out = self._out(out, q.shape, q)
         cs = cache.struct()
         _check(self._lib.starkv_decode_step(self._h, ctypes.byref(cs), _ptr(X_new), _ptr(q), B, n_q,
-                                            L.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), _ptr(out), _ptr(ws),
+                                            L.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), ld, _ptr(out),
+                                            _ptr(ws),
                                             int(ws.numel() * ws.element_size()), _stream(stream)),
                "starkv_decode_step")
         return out
 
-    def step_noalloc(self, cache: Cache, X_new, q, lens: Sequence[int], out, stream=None):
+    def step_noalloc(self, cache: Cache, X_new, q, lens: Sequence[int], out, stream=None, lens_dev=None):
         """starkv_decode_step with the library's static device scratch instead of a workspace: the
         call allocates no device memory (``out`` [B, n_q, H_q, d_h] is the caller's).  Calls that
         overlap on one GPU share the scratch and must be serialised."""
@@ -436,12 +464,13 @@ class Layer:
         L = _lens(lens, B)
         self._check_q(q)
         _need(_on_device(X_new, q), f"X_new must be on {q.device}")
+        ld = _lens_dev(lens_dev, B, q)
         self._check_cache(cache, q)
         _need(out is not None, "out must be given (the call allocates nothing)")
         out = self._out(out, q.shape, q)
         cs = cache.struct()
         _check(self._lib.starkv_decode_step_noalloc(self._h, ctypes.byref(cs), _ptr(X_new), _ptr(q), B, n_q,
-                                                    L.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), _ptr(out),
+                                                    L.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), ld, _ptr(out),
                                                     _stream(stream)),
                "starkv_decode_step_noalloc")
         return out

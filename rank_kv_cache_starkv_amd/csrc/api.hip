@@ -333,10 +333,16 @@ static int check_bound(const Layer& L, bool need_bk) {
   return STARKV_OK;
 }
 
+// Device lengths: 4-byte aligned when given.
+static bool lens_dev_ok(const int32_t* lens_dev) { return ((uintptr_t)lens_dev & 3) == 0; }
+
+// Rotary layers whose decode attends over reconstructed keys and values plan on host lengths only.
+static bool recon_decode(const Layer& L, int n_q) { return L.rope_theta > 0.f && !skv::rope_latent_scores(L, n_q); }
+
 int starkv_compress_append(const starkv_layer* l, const starkv_cache* c, const void* X_new, int B, int n_new,
-                           const int32_t* lens_host, hipStream_t stream) {
+                           const int32_t* lens_host, const int32_t* lens_dev, hipStream_t stream) {
   SKV_GUARD_BEGIN
-  if (!l || !lens_host) return STARKV_EINVAL;
+  if (!l || !lens_host || !lens_dev_ok(lens_dev)) return STARKV_EINVAL;
   if (B <= 0 || B > STARKV_MAX_BATCH || n_new < 0) return B > STARKV_MAX_BATCH ? STARKV_EUNSUPPORTED : STARKV_EINVAL;
   int st = check_cache(l->L, c, B);
   if (st != STARKV_OK) return st;
@@ -349,7 +355,7 @@ int starkv_compress_append(const starkv_layer* l, const starkv_cache* c, const v
   }
   st = check_bound(l->L, false);
   if (st != STARKV_OK) return st;
-  return hip_status(skv::launch_append(l->L, *c, X_new, B, n_new, lens_host, stream));
+  return hip_status(skv::launch_append(l->L, *c, X_new, B, n_new, lens_host, stream, lens_dev, 0));
   SKV_GUARD_END
 }
 
@@ -388,16 +394,18 @@ int starkv_decode_workspace_bytes(const starkv_layer* l, int B, int n_q, const i
 }
 
 int starkv_decode_attention(const starkv_layer* l, const starkv_cache* c, const void* q, int B, int n_q,
-                            const int32_t* lens_host, void* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+                            const int32_t* lens_host, const int32_t* lens_dev, void* out, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
   SKV_GUARD_BEGIN
-  if (!l || !q || !out || !ws) return STARKV_EINVAL;
+  if (!l || !q || !out || !ws || !lens_dev_ok(lens_dev)) return STARKV_EINVAL;
   const Layer& L = l->L;
   int st = check_decode(L, c, B, n_q, lens_host);
   if (st != STARKV_OK) return st;
   st = check_bound(L, true);
   if (st != STARKV_OK) return st;
   if (((uintptr_t)ws & 255) != 0) return STARKV_EINVAL;
-  if (L.rope_theta > 0.f && !skv::rope_latent_scores(L, n_q)) {
+  if (recon_decode(L, n_q)) {
+    if (lens_dev) return STARKV_EUNSUPPORTED;
     if (ws_bytes < skv::prefill_workspace_bytes(L, B, lens_host)) return STARKV_EWORKSPACE;
     return hip_status(skv::launch_prefill(L, *c, q, B, n_q, lens_host, out, ws, stream));
   }
@@ -407,15 +415,16 @@ int starkv_decode_attention(const starkv_layer* l, const starkv_cache* c, const 
   st = get_plan(l, B, n_q, lens_host, c->T_max, ws, &plan, &kts, &seq);
   if (st != STARKV_OK) return st;
   if (ws_bytes < plan.ws_bytes) return STARKV_EWORKSPACE;
+  seq.lens_dev = lens_dev;
   return hip_status(skv::launch_decode(L, plan, kts, seq, q, out, c->k_rows, c->v_tiles, stream));
   SKV_GUARD_END
 }
 
 int starkv_decode_attention_hidden(const starkv_layer* l, const starkv_cache* c, const void* x, int B, int n_q,
-                                   const int32_t* lens_host, void* out, void* ws, size_t ws_bytes,
-                                   hipStream_t stream) {
+                                   const int32_t* lens_host, const int32_t* lens_dev, void* out, void* ws,
+                                   size_t ws_bytes, hipStream_t stream) {
   SKV_GUARD_BEGIN
-  if (!l || !x || !out || !ws) return STARKV_EINVAL;
+  if (!l || !x || !out || !ws || !lens_dev_ok(lens_dev)) return STARKV_EINVAL;
   const Layer& L = l->L;
   int st = check_decode(L, c, B, n_q, lens_host);
   if (st != STARKV_OK) return st;
@@ -430,14 +439,16 @@ int starkv_decode_attention_hidden(const starkv_layer* l, const starkv_cache* c,
   st = get_plan(l, B, n_q, lens_host, c->T_max, ws, &plan, &kts, &seq);
   if (st != STARKV_OK) return st;
   if (ws_bytes < plan.ws_bytes) return STARKV_EWORKSPACE;
+  seq.lens_dev = lens_dev;
   return hip_status(skv::launch_decode(L, plan, kts, seq, x, out, c->k_rows, c->v_tiles, stream, L.d_wqk));
   SKV_GUARD_END
 }
 
 int starkv_decode_step(const starkv_layer* l, const starkv_cache* c, const void* X_new, const void* q, int B,
-                       int n_q, const int32_t* lens_host, void* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+                       int n_q, const int32_t* lens_host, const int32_t* lens_dev, void* out, void* ws,
+                       size_t ws_bytes, hipStream_t stream) {
   SKV_GUARD_BEGIN
-  if (!l || !q || !out || !ws || !X_new) return STARKV_EINVAL;
+  if (!l || !q || !out || !ws || !X_new || !lens_dev_ok(lens_dev)) return STARKV_EINVAL;
   const Layer& L = l->L;
   int st = check_decode(L, c, B, n_q, lens_host);
   if (st != STARKV_OK) return st;
@@ -446,7 +457,8 @@ int starkv_decode_step(const starkv_layer* l, const starkv_cache* c, const void*
   if (((uintptr_t)ws & 255) != 0) return STARKV_EINVAL;
   int32_t lens_pre[STARKV_MAX_BATCH];
   for (int b = 0; b < B; ++b) lens_pre[b] = lens_host[b] - n_q;
-  if (L.rope_theta > 0.f && !skv::rope_latent_scores(L, n_q)) {
+  if (recon_decode(L, n_q)) {
+    if (lens_dev) return STARKV_EUNSUPPORTED;
     if (ws_bytes < skv::prefill_workspace_bytes(L, B, lens_host)) return STARKV_EWORKSPACE;
     const hipError_t e = skv::launch_append(L, *c, X_new, B, n_q, lens_pre, stream);
     if (e != hipSuccess) return STARKV_EHIP;
@@ -458,6 +470,7 @@ int starkv_decode_step(const starkv_layer* l, const starkv_cache* c, const void*
   st = get_plan(l, B, n_q, lens_host, c->T_max, ws, &plan, &kts, &seq);
   if (st != STARKV_OK) return st;
   if (ws_bytes < plan.ws_bytes) return STARKV_EWORKSPACE;
+  seq.lens_dev = lens_dev;
   return hip_status(skv::launch_step(L, *c, plan, kts, seq, X_new, lens_pre, q, out, stream));
   SKV_GUARD_END
 }
@@ -521,9 +534,10 @@ int starkv_prefill_attention(const starkv_layer* l, const starkv_cache* c, const
 }
 
 int starkv_decode_step_noalloc(const starkv_layer* l, const starkv_cache* c, const void* X_new, const void* q,
-                               int B, int n_q, const int32_t* lens_host, void* out, hipStream_t stream) {
+                               int B, int n_q, const int32_t* lens_host, const int32_t* lens_dev, void* out,
+                               hipStream_t stream) {
   SKV_GUARD_BEGIN
-  if (!l || !q || !out || !X_new) return STARKV_EINVAL;
+  if (!l || !q || !out || !X_new || !lens_dev_ok(lens_dev)) return STARKV_EINVAL;
   const Layer& L = l->L;
   int st = check_decode(L, c, B, n_q, lens_host);
   if (st != STARKV_OK) return st;
@@ -534,7 +548,8 @@ int starkv_decode_step_noalloc(const starkv_layer* l, const starkv_cache* c, con
   if (st != STARKV_OK) return st;
   int32_t lens_pre[STARKV_MAX_BATCH];
   for (int b = 0; b < B; ++b) lens_pre[b] = lens_host[b] - n_q;
-  if (L.rope_theta > 0.f && !skv::rope_latent_scores(L, n_q)) {
+  if (recon_decode(L, n_q)) {
+    if (lens_dev) return STARKV_EUNSUPPORTED;
     if (skv::prefill_workspace_bytes(L, B, lens_host) > kScratchBytes) return STARKV_EWORKSPACE;
     const hipError_t e = skv::launch_append(L, *c, X_new, B, n_q, lens_pre, stream);
     if (e != hipSuccess) return STARKV_EHIP;
@@ -546,6 +561,7 @@ int starkv_decode_step_noalloc(const starkv_layer* l, const starkv_cache* c, con
   st = get_plan(l, B, n_q, lens_host, c->T_max, ws, &plan, &kts, &seq);
   if (st != STARKV_OK) return st;
   if (plan.ws_bytes > kScratchBytes) return STARKV_EWORKSPACE;
+  seq.lens_dev = lens_dev;
   return hip_status(skv::launch_step(L, *c, plan, kts, seq, X_new, lens_pre, q, out, stream));
   SKV_GUARD_END
 }

@@ -393,7 +393,7 @@ void fill_gemm_args(const Layer& L, GemmArgs& a, const void* X, int M) {
 }
 
 void fill_append_args(const Layer& L, const starkv_cache& c, GemmArgs& a, const void* X_new, int B, int n_new,
-                      const int32_t* lens) {
+                      const int32_t* lens, const int32_t* lens_dev, int lens_sub) {
   fill_gemm_args(L, a, X_new, B * n_new);
   a.n_new = n_new;
   a.T_max = c.T_max;
@@ -403,6 +403,8 @@ void fill_append_args(const Layer& L, const starkv_cache& c, GemmArgs& a, const 
   a.v_tiles = (uint8_t*)c.v_tiles;
   a.scales = L.scales;
   for (int b = 0; b < B; ++b) a.lens[b] = lens[b];
+  a.lens_dev = lens_dev;
+  a.lens_sub = lens_sub;
 }
 
 hipError_t launch_calibrate(const Layer& L, const void* X_cal, int n_cal, uint16_t* scales_out, hipStream_t s) {
@@ -447,9 +449,9 @@ static hipError_t launch_dma_append(const ProfScope& ps, GemmArgs& a, int M, hip
 }
 
 hipError_t launch_append(const Layer& L, const starkv_cache& c, const void* X_new, int B, int n_new,
-                         const int32_t* lens, hipStream_t s) {
+                         const int32_t* lens, hipStream_t s, const int32_t* lens_dev, int lens_sub) {
   GemmArgs a = {};
-  fill_append_args(L, c, a, X_new, B, n_new, lens);
+  fill_append_args(L, c, a, X_new, B, n_new, lens, lens_dev, lens_sub);
   ProfScope ps("append");
   hipError_t e;
   const bool mix = L.mix();

@@ -259,6 +259,8 @@ int plan_decode(const Layer& L, int B, int n_q, const int32_t* lens, int T_max, 
   }
   seq->uni = uniform ? 1 : 0;
   seq->u_len = lens[0];
+  seq->lens_dev = nullptr;
+  seq->len_lo = n_q;
   seq->u_nch = seq->chunk_off[1];
   seq->u_nspl = seq->split_off[1];
   seq->u_nblk = seq->blk_off[1];
@@ -578,7 +580,10 @@ __global__ __launch_bounds__(256) void k_qproj(QprojArgs a) {
 
 // Sequence bookkeeping of the decode plan: with equal lengths every quantity is a product or a
 // quotient; otherwise it is read from the prefix tables (segment search by the whole wave).
-__device__ __forceinline__ int seq_len(const SeqTable& t, int b) { return t.uni ? t.u_len : t.lens[b]; }
+__device__ __forceinline__ int seq_len(const SeqTable& t, int b) {
+  const int l = t.uni ? t.u_len : t.lens[b];
+  return t.lens_dev ? min(max(t.lens_dev[b], t.len_lo), l) : l;
+}
 __device__ __forceinline__ int seq_chunk0(const SeqTable& t, int b) { return t.uni ? b * t.u_nch : t.chunk_off[b]; }
 __device__ __forceinline__ int seq_nch(const SeqTable& t, int b) {
   return t.uni ? t.u_nch : t.chunk_off[b + 1] - t.chunk_off[b];
@@ -3288,13 +3293,13 @@ hipError_t launch_step(const Layer& L, const starkv_cache& c, const DecodePlan& 
   const int sw = (M <= 8 && L.d % 64 == 0 && !L.pack3) ? 8 : ((M <= 16 && L.d % 32 == 0) ? 16 : 0);
   if (sw == 0 || L.rope_theta > 0.f) {
     // many new rows: the tiled append, then the decode
-    const hipError_t e = launch_append(L, c, X_new, g.B, g.n_q, lens_pre, s);
+    const hipError_t e = launch_append(L, c, X_new, g.B, g.n_q, lens_pre, s, seq.lens_dev, g.n_q);
     if (e != hipSuccess) return e;
     return launch_decode(L, plan, kts, seq, q, out, c.k_rows, c.v_tiles, s);
   }
   StepFrontArgs fa;
   fa.ga = GemmArgs{};
-  fill_append_args(L, c, fa.ga, X_new, g.B, g.n_q, lens_pre);
+  fill_append_args(L, c, fa.ga, X_new, g.B, g.n_q, lens_pre, seq.lens_dev, g.n_q);
   fa.qa = qproj_args(L, plan, kts, q);
   fa.n_app = ceil_div(fa.ga.NS, sw);
   fa.nrg = qproj_row_groups(g);

@@ -30,6 +30,10 @@ struct GemmArgs {
   uint8_t* v_tiles;
   const uint16_t* scales;
   int lens[kMaxB];
+  // lengths read on the device (null: lens): rows go after max(lens_dev[b] - lens_sub, 0),
+  // at most lens[b]
+  const int32_t* lens_dev;
+  int lens_sub;
   // calibrate
   uint32_t* absmax;
   // raw fp32 output [M][NS] (the hidden-state query projection): MODE 2 stores X A_t^T, MODE 4
@@ -76,7 +80,8 @@ __device__ __forceinline__ void load_frag8(const void* base, size_t elem_off, bo
 __device__ __forceinline__ int row_pos(const GemmArgs& a, int m) {
   const int mc = min(m, a.M - 1);
   const int b = mc / a.n_new;
-  const int pos = a.lens[b] + (mc - b * a.n_new);
+  const int l0 = a.lens_dev ? min(max(a.lens_dev[b] - a.lens_sub, 0), a.lens[b]) : a.lens[b];
+  const int pos = l0 + (mc - b * a.n_new);
   return m < a.M ? pos : 0;
 }
 
@@ -396,6 +401,6 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& a, int blk, float (*
 // Host side: argument blocks of the latent GEMM for a layer, and for an append into a cache.
 void fill_gemm_args(const Layer& L, GemmArgs& a, const void* X, int M);
 void fill_append_args(const Layer& L, const starkv_cache& c, GemmArgs& a, const void* X_new, int B, int n_new,
-                      const int32_t* lens);
+                      const int32_t* lens, const int32_t* lens_dev = nullptr, int lens_sub = 0);
 
 }  // namespace skv

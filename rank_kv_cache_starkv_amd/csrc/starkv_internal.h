@@ -143,6 +143,11 @@ struct KtList {
 struct SeqTable {
   // every sequence the same length: positions follow by division (no table reads on the device)
   int uni, u_len, u_nch, u_nspl, u_nblk;
+  // lengths read on the device at run time (null: the planned lengths are the lengths).  The
+  // plan's lengths are then upper bounds: sequence b attends over min(max(lens_dev[b], len_lo),
+  // planned length) tokens, so chunks and splits past that length are empty.
+  const int32_t* lens_dev;
+  int len_lo;
   int lens[kMaxB];
   int chunk_off[kMaxB + 1];  // prefix of 32-token chunks per sequence
   int split_off[kMaxB + 1];  // prefix of value splits per sequence
@@ -219,8 +224,9 @@ hipError_t launch_build_factors(const Layer& L, const float* U_k, const float* V
 
 hipError_t launch_calibrate(const Layer& L, const void* X_cal, int n_cal, uint16_t* scales_out, hipStream_t s);
 
+// lens_dev (optional): rows of sequence b go after max(lens_dev[b] - lens_sub, 0), at most lens[b]
 hipError_t launch_append(const Layer& L, const starkv_cache& c, const void* X_new, int B, int n_new,
-                         const int32_t* lens, hipStream_t s);
+                         const int32_t* lens, hipStream_t s, const int32_t* lens_dev = nullptr, int lens_sub = 0);
 
 hipError_t launch_reconstruct(const Layer& L, const starkv_cache& c, int b, int t0, int t1, void* K_out,
                               void* V_out, hipStream_t s);

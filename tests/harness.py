@@ -302,3 +302,46 @@ def check_output(w: I.Workload, got: np.ndarray, ref: np.ndarray, what: str) -> 
     assert rel <= 2e-2, (what, rel)
     assert per[worst] <= 2e-2, (what, "row, head", divmod(worst, w.H_q), float(per[worst]))
     return rel
+
+
+def compare_cache(run: Run, exact: bool) -> None:
+    """The GPU cache bytes of every oracle sequence against the oracle's: bit-exact with
+    exact-latent conditioning (the bytes the format defines for tokens < T), else decoded codes
+    within one code at rounding boundaries (quantised latents) or the rounding of bf16/fp32."""
+    w = run.w
+    for b in run.oracle_seqs:
+        gk, gv = gpu_seq_cache(run, b)
+        ok, ov = oracle_seq_bytes(run, b)
+        T = int(run.lens[b])
+        if exact and run.fmt.packed:
+            # packed layout: the row bytes the format defines (not the row padding), the outlier
+            # nibble rows at the columns of tokens < T, and the 3-bit stream's plane words at the
+            # bits of tokens < T (a word also holds the tile's later tokens)
+            fmt = run.fmt
+            used = fmt.K4 // 2 + 3 * fmt.K3 // 8
+            np.testing.assert_array_equal(gk[:, :used], ok[:, :used])
+            r3 = fmt.V4 // 2
+            for t in range(0, T, O.TT):
+                n = min(O.TT, T - t)
+                np.testing.assert_array_equal(gv[t // O.TT, :r3, :n], ov[t // O.TT, :r3, :n])
+                words = [np.ascontiguousarray(x[t // O.TT].reshape(-1)[r3 * O.TT: r3 * O.TT + 12 * fmt.V3]).view("<u4")
+                         for x in (gv, ov)]
+                mask = np.uint32(sum(1 << O.token_bit3(j) for j in range(n)))
+                np.testing.assert_array_equal(words[0] & mask, words[1] & mask)
+        elif exact:
+            np.testing.assert_array_equal(gk, ok)
+            # value tiles: compare the columns of tokens < T only
+            for t in range(0, T, O.TT):
+                n = min(O.TT, T - t) * run.fmt.elem
+                np.testing.assert_array_equal(gv[t // O.TT, :, :n], ov[t // O.TT, :, :n])
+        else:
+            kc = O.unpack_key_rows(gk, run.fmt)
+            vc = O.unpack_value_tiles(gv, run.fmt, T)
+            okc, ovc = run.ocache[b].key, run.ocache[b].value
+            if O.is_quantized(w.latent):
+                nd = check_natural_codes(run, b, kc, vc)
+                log(f"  seq {b}: natural-run codes differing by one at rounding boundaries: {nd}/{kc.size + vc.size}")
+            else:
+                tol = 1e-5 if w.latent == "f32" else 2 ** -7
+                np.testing.assert_allclose(kc, okc, rtol=tol, atol=tol * np.abs(okc).max())
+                np.testing.assert_allclose(vc, ovc, rtol=tol, atol=tol * np.abs(ovc).max())

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     L = S.lib()
-    assert L.starkv_abi_version() == 1
+    assert L.starkv_abi_version() == S.ABI_VERSION == 2
     for st in (0, -1, -2, -3, -4, -5, -6, -7):
         assert L.starkv_status_string(st).decode() not in ("", "unknown status")
     assert L.starkv_status_string(-99).decode() == "unknown status"
@@ -129,27 +129,33 @@ def test_hot_calls_reject_bad_arguments_without_launching():
     fake = ctypes.c_void_p(0x1000)
     cache = S._Cache(0x1000, 0x2000, w.B, 4096)
     # no factors bound yet -> ESTATE (after the argument checks pass)
-    assert L.starkv_compress_append(h, ctypes.byref(cache), fake, w.B, 1, lp, None) == -7
-    assert L.starkv_decode_attention(h, ctypes.byref(cache), fake, w.B, 1, lp, fake, ctypes.c_void_p(0x1000),
+    assert L.starkv_compress_append(h, ctypes.byref(cache), fake, w.B, 1, lp, None, None) == -7
+    assert L.starkv_decode_attention(h, ctypes.byref(cache), fake, w.B, 1, lp, None, fake, ctypes.c_void_p(0x1000),
                                      1 << 30, None) == -7
     # argument errors
-    assert L.starkv_compress_append(h, ctypes.byref(cache), fake, w.B, 5000, lp, None) == -3  # capacity
-    assert L.starkv_compress_append(h, ctypes.byref(cache), fake, 0, 1, lp, None) == -1
-    assert L.starkv_compress_append(h, ctypes.byref(cache), fake, 129, 1, lp, None) == -4
-    assert L.starkv_compress_append(h, ctypes.byref(cache), fake, w.B, 0, lp, None) == 0  # no-op
+    assert L.starkv_compress_append(h, ctypes.byref(cache), fake, w.B, 5000, lp, None, None) == -3  # capacity
+    assert L.starkv_compress_append(h, ctypes.byref(cache), fake, 0, 1, lp, None, None) == -1
+    assert L.starkv_compress_append(h, ctypes.byref(cache), fake, 129, 1, lp, None, None) == -4
+    assert L.starkv_compress_append(h, ctypes.byref(cache), fake, w.B, 0, lp, None, None) == 0  # no-op
     bad = S._Cache(0x1000, 0x2000, w.B, 100)  # T_max not a multiple of 32
-    assert L.starkv_compress_append(h, ctypes.byref(bad), fake, w.B, 1, lp, None) == -1
-    assert L.starkv_decode_attention(h, ctypes.byref(cache), fake, w.B, 0, lp, fake, fake, 1 << 30, None) == -1
+    assert L.starkv_compress_append(h, ctypes.byref(bad), fake, w.B, 1, lp, None, None) == -1
+    assert L.starkv_decode_attention(h, ctypes.byref(cache), fake, w.B, 0, lp, None, fake, fake, 1 << 30, None) == -1
     big = np.full(w.B, 5000, np.int32)
     assert L.starkv_decode_attention(h, ctypes.byref(cache), fake, w.B, 1,
-                                     big.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), fake, fake, 1 << 30, None) == -3
-    assert L.starkv_decode_attention(h, ctypes.byref(cache), fake, w.B, 9, lp, fake, fake, 1 << 30, None) == -4  # 32*9 rows
+                                     big.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), None, fake, fake, 1 << 30, None) == -3
+    assert L.starkv_decode_attention(h, ctypes.byref(cache), fake, w.B, 9, lp, None, fake, fake, 1 << 30, None) == -4  # 32*9 rows
     # the fused step: the decode checks, plus a missing X_new
-    assert L.starkv_decode_step(h, ctypes.byref(cache), fake, fake, w.B, 1, lp, fake, fake, 1 << 30, None) == -7
-    assert L.starkv_decode_step(h, ctypes.byref(cache), None, fake, w.B, 1, lp, fake, fake, 1 << 30, None) == -1
-    assert L.starkv_decode_step(h, ctypes.byref(cache), fake, fake, w.B, 0, lp, fake, fake, 1 << 30, None) == -1
+    assert L.starkv_decode_step(h, ctypes.byref(cache), fake, fake, w.B, 1, lp, None, fake, fake, 1 << 30, None) == -7
+    assert L.starkv_decode_step(h, ctypes.byref(cache), None, fake, w.B, 1, lp, None, fake, fake, 1 << 30, None) == -1
+    assert L.starkv_decode_step(h, ctypes.byref(cache), fake, fake, w.B, 0, lp, None, fake, fake, 1 << 30, None) == -1
     assert L.starkv_decode_step(h, ctypes.byref(cache), fake, fake, w.B, 1,
-                                big.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), fake, fake, 1 << 30, None) == -3
+                                big.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), None, fake, fake, 1 << 30, None) == -3
+    # device lengths must be 4-byte aligned
+    odd = ctypes.c_void_p(0x1002)
+    assert L.starkv_compress_append(h, ctypes.byref(cache), fake, w.B, 1, lp, odd, None) == -1
+    assert L.starkv_decode_attention(h, ctypes.byref(cache), fake, w.B, 1, lp, odd, fake, fake, 1 << 30, None) == -1
+    assert L.starkv_decode_step(h, ctypes.byref(cache), fake, fake, w.B, 1, lp, odd, fake, fake, 1 << 30, None) == -1
+    assert L.starkv_decode_step_noalloc(h, ctypes.byref(cache), fake, fake, w.B, 1, lp, odd, fake, None) == -1
     assert L.starkv_reconstruct(h, ctypes.byref(cache), w.B, 0, 1, fake, fake, None) == -1
     assert L.starkv_reconstruct(h, ctypes.byref(cache), 0, 5, 4, fake, fake, None) == -1
     assert L.starkv_calibrate(h, fake, 4, fake, None) == -7

@@ -59,43 +59,7 @@ def _run_mini(cfg, exact, q_scale=1.0):
 
 
 def _compare_cache(run, exact):
-    w = run.w
-    for b in run.oracle_seqs:
-        gk, gv = H.gpu_seq_cache(run, b)
-        ok, ov = H.oracle_seq_bytes(run, b)
-        T = int(run.lens[b])
-        if exact and run.fmt.packed:
-            # packed layout: the row bytes the format defines (not the row padding), the outlier
-            # nibble rows at the columns of tokens < T, and the 3-bit stream's plane words at the
-            # bits of tokens < T (a word also holds the tile's later tokens)
-            fmt = run.fmt
-            used = fmt.K4 // 2 + 3 * fmt.K3 // 8
-            np.testing.assert_array_equal(gk[:, :used], ok[:, :used])
-            r3 = fmt.V4 // 2
-            for t in range(0, T, O.TT):
-                n = min(O.TT, T - t)
-                np.testing.assert_array_equal(gv[t // O.TT, :r3, :n], ov[t // O.TT, :r3, :n])
-                words = [np.ascontiguousarray(x[t // O.TT].reshape(-1)[r3 * O.TT: r3 * O.TT + 12 * fmt.V3]).view("<u4")
-                         for x in (gv, ov)]
-                mask = np.uint32(sum(1 << O.token_bit3(j) for j in range(n)))
-                np.testing.assert_array_equal(words[0] & mask, words[1] & mask)
-        elif exact:
-            np.testing.assert_array_equal(gk, ok)
-            # value tiles: compare the columns of tokens < T only
-            for t in range(0, T, O.TT):
-                n = min(O.TT, T - t) * run.fmt.elem
-                np.testing.assert_array_equal(gv[t // O.TT, :, :n], ov[t // O.TT, :, :n])
-        else:
-            kc = O.unpack_key_rows(gk, run.fmt)
-            vc = O.unpack_value_tiles(gv, run.fmt, T)
-            okc, ovc = run.ocache[b].key, run.ocache[b].value
-            if O.is_quantized(w.latent):
-                nd = H.check_natural_codes(run, b, kc, vc)
-                H.log(f"  seq {b}: natural-run codes differing by one at rounding boundaries: {nd}/{kc.size + vc.size}")
-            else:
-                tol = 1e-5 if w.latent == "f32" else 2 ** -7
-                np.testing.assert_allclose(kc, okc, rtol=tol, atol=tol * np.abs(okc).max())
-                np.testing.assert_allclose(vc, ovc, rtol=tol, atol=tol * np.abs(ovc).max())
+    H.compare_cache(run, exact)
 
 
 @pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, 5, 6])
