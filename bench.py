@@ -26,6 +26,7 @@ from __future__ import annotations
 import argparse
 import csv
 import dataclasses
+import gc
 import glob
 import hashlib
 import json
@@ -42,6 +43,7 @@ sys.path.insert(0, ROOT)
 METRIC = "low-rank KV decode attention queries/s + achieved HBM GB/s vs ~8 TB/s peak"
 HBM_PEAK_GBPS = 8000.0
 MIN_ROTATION_BYTES = 1 << 30
+EAGER_SEG = 32  # eager steps issued between synchronisations
 
 
 def log(msg: str) -> None:
@@ -371,16 +373,26 @@ def measure(w, args, dev, with_cpu: bool, steps: int, warmup: int) -> dict:
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    # eager: one host call per step (append + attention)
-    t_host = time.perf_counter()
-    ev0.record()
-    for i in range(steps):
-        step(warmup + i)
-    ev1.record()
-    t_host = time.perf_counter() - t_host
-    torch.cuda.synchronize()
-    ms_step_eager = ev0.elapsed_time(ev1) / steps
+    # eager: one host call per step (append + attention), issued in segments of EAGER_SEG steps
+    # with a synchronisation between segments, so that the host issue time is the calls' own cost
+    # (when the GPU is the slower side, a long run fills the HIP queue and further launches wait
+    # for free slots).  Python's cyclic collector is paused while timing: a full collection over
+    # this process's objects landing inside the loop showed up as 0.2-0.4 ms/step of host issue.
+    gc.collect()
+    gc.disable()
+    t_host, ms_eager = 0.0, 0.0
+    for i0 in range(0, steps, EAGER_SEG):
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        ev0.record()
+        for i in range(i0, min(steps, i0 + EAGER_SEG)):
+            step(warmup + i)
+        ev1.record()
+        t_host += time.perf_counter() - t0
+        torch.cuda.synchronize()
+        ms_eager += ev0.elapsed_time(ev1)
+    gc.enable()
+    ms_step_eager = ms_eager / steps
     host_us = t_host / steps * 1e6
     log(f"[time] eager: {ms_step_eager * 1000:.2f} us/step (host issue {host_us:.1f} us/step)")
 

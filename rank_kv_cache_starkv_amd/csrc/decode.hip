@@ -273,7 +273,7 @@ int plan_decode(const Layer& L, int B, int n_q, const int32_t* lens, int T_max, 
   const size_t o_p = o; o = align256(o + (size_t)total_chunks * g.M_pad * kTC * esz_p);
   const size_t o_cm = o; o = align256(o + (size_t)total_chunks * g.M_pad * 4);
   const size_t o_cl = o; o = align256(o + (size_t)total_chunks * g.M_pad * 4);
-  const size_t o_zp = o; o = align256(o + (size_t)total_splits * g.M_pad * g.rv_ld * 4);
+  const size_t o_zp = o; o = align256(o + (size_t)total_splits * g.M_pad * g.rv_ld * (L.mix() ? 2 : 4));
   const size_t o_sl = o; o = align256(o + (size_t)total_splits * g.M_pad * 4);
   const size_t o_sm = o; o = align256(o + (size_t)total_splits * g.M_pad * 4);
   const size_t o_zt = o; o = align256(o + (size_t)B * g.M_pad * g.rv_ld * 4);
@@ -285,7 +285,7 @@ int plan_decode(const Layer& L, int B, int n_q, const int32_t* lens, int T_max, 
   w.p = base + o_p;
   w.cm = (float*)(base + o_cm);
   w.cl = (float*)(base + o_cl);
-  w.zp = (float*)(base + o_zp);
+  w.zp = (void*)(base + o_zp);
   w.sl = (float*)(base + o_sl);
   w.sm = (float*)(base + o_sm);
   w.zt = (float*)(base + o_zt);
@@ -312,6 +312,7 @@ struct QprojArgs {
   float* rowp;
   DecodeGeom g;
   int nkt_max;
+  int qp_w;  // rows per workgroup of the query-projection launch
   KtList kts;
 };
 
@@ -321,24 +322,28 @@ __device__ __forceinline__ float ldx(const void* p, size_t i) {
   return bf16_to_f32(((const uint16_t*)p)[i]);
 }
 
-// One workgroup per (sequence, KV head g): the rows of g (its G query heads x n_q queries)
-// are complete here, so the per-row quantisation scale is local.  Each row owns the 16-byte
-// fragment chunks of its column in every K-tile of its column tile; the workgroup writes
-// exactly those chunks (zeros outside g's segment), so no two workgroups write the same bytes.
-constexpr int kQpRB = 8;      // query-projection rows per batch
+// A workgroup takes rows of one KV head g: the rows of g in one sequence are its G query heads
+// x n_q queries, and the workgroup's rows are a range of the flattened (sequence, row) index
+// u = b * G n_q + row, so one workgroup may take the rows of several sequences.  A row's
+// quantisation scale depends on that row alone.  Each row owns the 16-byte fragment chunks of its
+// column in every K-tile of its column tile; the workgroup writes exactly those chunks (zeros
+// outside g's segment), so no two workgroups write the same bytes.
+constexpr int kQpRB = 8;      // query-projection rows per batch (fused step front)
+constexpr int kQpRB16 = 16;   // ... (query-projection launch)
 constexpr int kQpRMAX = 256;  // max rank (<= d_h <= 256)
-struct QprojShared {
-  float qh[kQpRB][kQpRMAX];
-  int8_t hi8[kQpRB][kQpRMAX];
-  int8_t lo8[kQpRB][kQpRMAX];
-  float rho_s[kQpRB];
+template <int RB>
+struct QprojSharedT {
+  float qh[RB][kQpRMAX];
+  int8_t hi8[RB][kQpRMAX];
+  int8_t lo8[RB][kQpRMAX];
+  float rho_s[RB];
 };
+using QprojShared = QprojSharedT<kQpRB>;
 
-// Body of the query projection for workgroup (KV head gk, sequence b, row group rg of nrg) with
-// NT threads.
-template <int DT, int LAT, int NT, bool HID = false>
-__device__ __forceinline__ void qproj_body(const QprojArgs& a, int gk, int b, int rg, int nrg, QprojShared& sh) {
-  constexpr int RB = kQpRB;
+// Body of the query projection for the rows u in [u_lo, u_hi) of KV head gk (u = b G n_q + row of
+// g in sequence b), RB rows per batch, with NT threads.
+template <int DT, int LAT, int NT, bool HID = false, int RB = kQpRB>
+__device__ __forceinline__ void qproj_body(const QprojArgs& a, int gk, int u_lo, int u_hi, QprojSharedT<RB>& sh) {
   constexpr int NWV = NT / 64;
   constexpr int SUB = 4;                            // lanes per dot product
   constexpr int EPL = DT == STARKV_F32 ? 4 : 8;    // elements per 16-byte load
@@ -351,16 +356,14 @@ __device__ __forceinline__ void qproj_body(const QprojArgs& a, int gk, int b, in
   const DecodeGeom& g = a.g;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int rph = g.G * g.n_q;
-  const int rpg = (rph + nrg - 1) / nrg;  // rows of this workgroup
-  const int r_lo = rg * rpg, r_hi = min(rph, r_lo + rpg);
   const int c0 = ld_uniform(a.heads.koff + gk);
   const int r = ld_uniform(a.heads.koff + gk + 1) - c0;
   const int n8g = (LAT == STARKV_LATENT_MIX84) ? ld_uniform(a.heads.n8 + gk) : 0;
   const int o8 = (LAT == STARKV_LATENT_MIX84) ? ld_uniform(a.heads.off8 + gk) : 0;
   const int o4 = (LAT == STARKV_LATENT_MIX84) ? ld_uniform(a.heads.off4 + gk) : 0;
 
-  for (int rb0 = r_lo; rb0 < r_hi; rb0 += RB) {
-    const int nrows = min(RB, r_hi - rb0);
+  for (int ub0 = u_lo; ub0 < u_hi; ub0 += RB) {
+    const int nrows = min(RB, u_hi - ub0);
     __syncthreads();
     // q^[n][k] = (q_n . B_k[c0 + k]) * scale * log2(e)/sqrt(d_h): SUB adjacent lanes per dot
     // product, lane sub taking the 16-byte pieces sub, sub + SUB, ... of the q row and the B_k
@@ -370,18 +373,17 @@ __device__ __forceinline__ void qproj_body(const QprojArgs& a, int gk, int b, in
     for (int ps = tid; ps < nrows * r * SUB; ps += NT) {
       const int p = ps / SUB, sub = ps % SUB;
       const int n = p / r, k = p % r;
+      const int b = (ub0 + n) / rph, lr = (ub0 + n) - b * rph;  // sequence, row of g
       if (HID) {
         // hidden-state query: the projection x_(b, j) . wqk[row of (query head, k)] is in qraw
-        const int i = gk * rph + rb0 + n;
-        const int hh = (i % rph) / g.n_q, j = i % g.n_q;
+        const int hh = lr / g.n_q, j = lr % g.n_q;
         float sc = 1.f;
         if (LAT == STARKV_LATENT_MIX84) sc = f16_to_f32(a.scales[c0 + k]);
         const float v = a.qraw[((size_t)b * g.n_q + j) * ((size_t)g.G * g.n_key) + (size_t)g.G * c0 + hh * r + k];
         if (sub == 0) qh[n][k] = v * sc * g.qscale;
         continue;
       }
-      const int i = gk * rph + rb0 + n;
-      const int hh = (i % rph) / g.n_q, j = i % g.n_q;
+      const int hh = lr / g.n_q, j = lr % g.n_q;
       const size_t qoff = (((size_t)b * g.n_q + j) * g.H_q + gk * g.G + hh) * g.d_h;
       const size_t boff = (size_t)(c0 + k) * g.d_h;
       float acc = 0.f;
@@ -459,7 +461,7 @@ __device__ __forceinline__ void qproj_body(const QprojArgs& a, int gk, int b, in
         sl += __shfl_xor(sl, o, 64);
       }
       if (lane == 0) {
-        const int i = gk * rph + rb0 + n;
+        const int b = (ub0 + n) / rph, i = gk * rph + (ub0 + n) - b * rph;
         float* rp = a.rowp + ((size_t)b * g.M_pad + i) * 4;
         rp[0] = LAT == STARKV_LATENT_MIX84 ? rho_s[n] : 1.f;
         rp[1] = (float)sh;
@@ -471,7 +473,7 @@ __device__ __forceinline__ void qproj_body(const QprojArgs& a, int gk, int b, in
     int pre[RB + 1];  // first item of each row (rows past nrows have none)
     pre[0] = 0;
 #pragma unroll
-    for (int n = 0; n < RB; ++n) pre[n + 1] = pre[n] + (n < nrows ? 4 * a.kts.n[(gk * rph + rb0 + n) >> 4] : 0);
+    for (int n = 0; n < RB; ++n) pre[n + 1] = pre[n] + (n < nrows ? 4 * a.kts.n[(gk * rph + (ub0 + n) % rph) >> 4] : 0);
     for (int it = tid; it < pre[RB]; it += NT) {
       int n = 0, item = it;
 #pragma unroll
@@ -480,7 +482,7 @@ __device__ __forceinline__ void qproj_body(const QprojArgs& a, int gk, int b, in
           n = m;
           item = it - pre[m];
         }
-      const int i = gk * rph + rb0 + n;
+      const int b = (ub0 + n) / rph, i = gk * rph + (ub0 + n) - b * rph;
       const int ct = i >> 4, col = i & 15;
       {
         const int jt = item >> 2, qq = item & 3;
@@ -547,8 +549,9 @@ __device__ __forceinline__ void qproj_body(const QprojArgs& a, int gk, int b, in
       }
     }
   }
-  // the last head also zeroes the chunks of the padding rows of the last column tile
-  if (gk == g.H_kv - 1 && rg == 0) {
+  // the last head also zeroes the chunks of the padding rows of the last column tile, in the
+  // workgroup that holds the sequence's first row
+  for (int b = (u_lo + rph - 1) / rph; gk == g.H_kv - 1 && b * rph < u_hi; ++b) {
     for (int i = g.M_q; i < g.nct * 16; ++i) {
       const int ct = i >> 4, col = i & 15;
       const int nkt = a.kts.n[ct];
@@ -569,10 +572,13 @@ __device__ __forceinline__ void qproj_body(const QprojArgs& a, int gk, int b, in
 
 // HID: the query comes from hidden states; their projection through the absorbed factors is
 // already in a.qraw.
+// Grid (KV head, row group): group y takes the rows u in [y qp_w, (y + 1) qp_w) of the head.
 template <int DT, int LAT, bool HID>
 __global__ __launch_bounds__(256) void k_qproj(QprojArgs a) {
-  __shared__ QprojShared sh;
-  qproj_body<DT, LAT, 256, HID>(a, blockIdx.x, blockIdx.y, blockIdx.z, gridDim.z, sh);
+  __shared__ QprojSharedT<kQpRB16> sh;
+  const int n_u = a.g.B * a.g.G * a.g.n_q;
+  const int u_lo = blockIdx.y * a.qp_w;
+  qproj_body<DT, LAT, 256, HID, kQpRB16>(a, blockIdx.x, u_lo, min(n_u, u_lo + a.qp_w), sh);
 }
 
 // ===========================================================================
@@ -1769,7 +1775,8 @@ struct ValueArgs {
   const void* p;
   const float* cm;
   const float* cl;
-  float* zp;
+  void* zp;  // split partials (fp32, or f16 scaled by zsc: int8/int4 latents)
+  float zsc;  // int8/int4 latents: power-of-two scale of the f16 partials
   float* sl;
   float* sm;
   DecodeGeom g;
@@ -2021,7 +2028,7 @@ __global__ __launch_bounds__(256) void k_values(ValueArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int row = mt * 32 + d32_row(v, q);
-        if (row < g.M_q) a.zp[((size_t)sg * g.M_pad + row) * g.rv_ld + vc] = acc[mt][nt][v];
+        if (row < g.M_q) ((float*)a.zp)[((size_t)sg * g.M_pad + row) * g.rv_ld + vc] = acc[mt][nt][v];
       }
   }
   if (blockIdx.x == 0 && wave == 0 && q == 0) {
@@ -2304,7 +2311,12 @@ __device__ __forceinline__ void values1_run(const ValueArgs& a, int slice, int s
 #pragma unroll
       for (int w = 0; w < 4; ++w) z += fw[vv][w] * sred[((w * NT + t) * 16 + v) * 64 + lane];
       const int row = d32_row(v, q);
-      if (cok && row < g.M_q) a.zp[((size_t)sg * g.M_pad + row) * g.rv_ld + vc] = z;
+      const size_t zi = ((size_t)sg * g.M_pad + row) * g.rv_ld + vc;
+      if (LAT == STARKV_LATENT_MIX84) {
+        if (cok && row < g.M_q) ((uint16_t*)a.zp)[zi] = f32_to_f16(z * a.zsc);
+      } else if (cok && row < g.M_q) {
+        ((float*)a.zp)[zi] = z;
+      }
     }
   }
   if (slice == 0 && wave == 0 && q == 0 && rok) {
@@ -2364,7 +2376,7 @@ __global__ __launch_bounds__(256) void k_values1(ValueArgs a) {
 // rotated by (row / 4) mod 4, which makes the A-fragment reads of 16 consecutive rows hit distinct
 // LDS banks.  Grid as k_values1 (one dimension; the groups of a split run on one XCD).
 template <int LAT, int NMT, int NTW, int D>
-__global__ __launch_bounds__(256) void k_values_mt(ValueArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_values_mt(ValueArgs a) {
   static_assert(LAT != STARKV_LATENT_F32, "fp32 latents use k_values");
   constexpr int MP = 32 * NMT;
   constexpr int esz = LAT == STARKV_LATENT_BF16 ? 2 : 1;
@@ -2575,27 +2587,37 @@ __global__ __launch_bounds__(256) void k_values_mt(ValueArgs a) {
   vm_wait<0>();  // no asynchronous load may still be writing LDS when the workgroup ends
 
   // z partials: lane holds channel r of each N-tile, rows d32_row(v, q) of each row tile
+  int vc[NTW];
+  bool cok[NTW];
 #pragma unroll
   for (int j = 0; j < NTW; ++j) {
-    if (!ntok[j]) continue;
-    int vc;
-    bool cok;
     if (!is4[j]) {
-      vc = blk[j] * 32 + r;
-      cok = vc < (LAT == STARKV_LATENT_MIX84 ? a.n8v : g.r_v);
+      vc[j] = blk[j] * 32 + r;
+      cok[j] = ntok[j] && vc[j] < (LAT == STARKV_LATENT_MIX84 ? a.n8v : g.r_v);
     } else {
       const int w = 2 * ((blk[j] - a.V8 / 32) * 32 + r) + par[j];
-      cok = w < a.n4v;
-      vc = a.n8v + w;
+      cok[j] = ntok[j] && w < a.n4v;
+      vc[j] = a.n8v + w;
     }
-    if (!cok) continue;
+  }
 #pragma unroll
-    for (int mt = 0; mt < NMT; ++mt)
+  for (int mt = 0; mt < NMT; ++mt) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = mt * 32 + d32_row(v, q);
-        if (row < g.M_q) a.zp[((size_t)sg * g.M_pad + row) * g.rv_ld + vc] = acc[j][mt][v];
+    for (int v = 0; v < 16; ++v) {
+      const int row = mt * 32 + d32_row(v, q);
+      if (row >= g.M_q) continue;
+      const size_t z0 = ((size_t)sg * g.M_pad + row) * g.rv_ld;
+      if (LAT == STARKV_LATENT_MIX84) {
+#pragma unroll
+        for (int j = 0; j < NTW; ++j)
+          if (cok[j]) ((uint16_t*)a.zp)[z0 + vc[j]] = f32_to_f16(acc[j][mt][v] * a.zsc);
+      } else {
+#pragma unroll
+        for (int j = 0; j < NTW; ++j)
+          if (cok[j]) ((float*)a.zp)[z0 + vc[j]] = acc[j][mt][v];
       }
+    }
+    __builtin_amdgcn_sched_barrier(0);  // one row tile's conversions at a time (registers)
   }
   if (grp == 0 && wave == 0 && q == 0) {
 #pragma unroll
@@ -2613,7 +2635,8 @@ __global__ __launch_bounds__(256) void k_values_mt(ValueArgs a) {
 // merge + up-projection: out = (sum_s z_s) * scale_v B_v^g / (sum_s l_s)
 
 struct MergeArgs {
-  const float* zp;
+  const void* zp;  // split partials (fp32, or f16 scaled by zsc: int8/int4 latents)
+  float zinv;      // int8/int4 latents: 1 / zsc
   const float* sl;
   const float* sm;
   float* zt;                // [B][M_pad][rv_ld] merged, scaled, normalised value latent
@@ -2627,7 +2650,8 @@ struct MergeArgs {
 
 // Split merge.  Split s weighted its tiles against its own maximum m_s of the row, so with M the
 // largest m_s: z~[c] = (sum_s 2^(m_s - M) z_s[c]) * scale_c / (sum_s 2^(m_s - M) l_s), and zero in
-// the padding channels [r_v, rv_ld).  Workgroup = 4 rows x (256 / nsp) channels of one sequence;
+// the padding channels [r_v, rv_ld).  MIX (int8/int4 latents): the partials are f16, scaled by
+// a power of two (zsc) that keeps them in range; zinv undoes it.  Workgroup = 4 rows x (256 / nsp) channels of one sequence;
 // nsp adjacent lanes (1 or 4) share 4 channels and take every nsp-th split each, all their loads
 // issued at once (NB splits per batch), keep a running maximum (rescaling their sums when it
 // grows), and combine by lane exchange in a fixed order, so the result is deterministic.
@@ -2643,7 +2667,9 @@ __global__ __launch_bounds__(256) void k_zmerge(MergeArgs a) {
   const bool live = i < g.M_q && c < g.rv_ld;
   const int ic = min(i, g.M_q - 1), cc = min(c, g.rv_ld - 4);
   const int s0 = seq_split0(a.seq, b), ns = seq_nsplit(a.seq, b);
-  const float* zc = a.zp + ((size_t)s0 * g.M_pad + ic) * g.rv_ld + cc;
+  const size_t zo = ((size_t)s0 * g.M_pad + ic) * g.rv_ld + cc;
+  const float* zc = (const float*)a.zp + zo;
+  const uint16_t* zh = (const uint16_t*)a.zp + zo;
   const float* lc = a.sl + (size_t)s0 * g.M_pad + ic;
   const float* mc = a.sm + (size_t)s0 * g.M_pad + ic;
   const size_t zs = (size_t)g.M_pad * g.rv_ld;
@@ -2662,7 +2688,12 @@ __global__ __launch_bounds__(256) void k_zmerge(MergeArgs a) {
 #pragma unroll
     for (int u = 0; u < NB; ++u) {
       const int ss = min(s + u * nsp, ns - 1);
-      v[u] = ld16(zc + (size_t)ss * zs);
+      if (MIX) {
+        const u32x2 h = ld8(zh + (size_t)ss * zs);
+        v[u] = u32x4{h[0], h[1], 0, 0};
+      } else {
+        v[u] = ld16(zc + (size_t)ss * zs);
+      }
       lv[u] = lc[(size_t)ss * g.M_pad];
       mv[u] = mc[(size_t)ss * g.M_pad];
     }
@@ -2679,8 +2710,15 @@ __global__ __launch_bounds__(256) void k_zmerge(MergeArgs a) {
     for (int u = 0; u < NB; ++u) {
       if (s + u * nsp < ns) {
         const float w = rel_weight(mv[u], Mn);
+        if (MIX) {
+          const float wz = w * a.zinv;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) z[e] += w * __uint_as_float(v[u][e]);
+          for (int e = 0; e < 4; ++e)
+            z[e] += wz * f16_to_f32((uint16_t)(e & 1 ? v[u][e >> 1] >> 16 : v[u][e >> 1] & 0xFFFF));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) z[e] += w * __uint_as_float(v[u][e]);
+        }
         l += w * lv[u];
       }
     }
@@ -2946,7 +2984,8 @@ __global__ __launch_bounds__(256) void k_upproj(MergeArgs a) {
 // Split merge folded into the up-projection (sequences of at most 4 splits): workgroup = (g,
 // 16-column slice of d_h, 16-row tile of g's rows over all sequences); its eight waves split K =
 // rv_ld in 32-channel chunks.  A lane sums its row's split partials for its 8 channels (in split
-// order, weighted 2^(m_s - M) as in k_zmerge), scales them by scale_c / sum_s 2^(m_s - M) l_s,
+// order, weighted 2^(m_s - M) as in k_zmerge; MIX: f16 partials, times zinv), scales them by
+// scale_c / sum_s 2^(m_s - M) l_s,
 // and feeds the MFMA as k_upproj does.  Padding channels (>= r_v) are zeroed; loads unconditional.
 template <int DT, bool MIX>
 __global__ __launch_bounds__(512) void k_upproj_merge(MergeArgs a) {
@@ -2969,12 +3008,12 @@ __global__ __launch_bounds__(512) void k_upproj_merge(MergeArgs a) {
   const int bb = rr / rph;
   const int ii = gk * rph + rr % rph;
   const int s0 = seq_split0(a.seq, bb), ns = seq_nsplit(a.seq, bb);
-  const float* zs[NSM];
+  size_t zs[NSM];  // element offsets of this lane's partial rows
   float lv[NSM], mv[NSM];
 #pragma unroll
   for (int sx = 0; sx < NSM; ++sx) {
     const size_t sp = (size_t)(s0 + min(sx, ns - 1));
-    zs[sx] = a.zp + (sp * g.M_pad + ii) * g.rv_ld + 8 * qq;
+    zs[sx] = (sp * g.M_pad + ii) * g.rv_ld + 8 * qq;
     lv[sx] = a.sl[sp * g.M_pad + ii];
     mv[sx] = a.sm[sp * g.M_pad + ii];
   }
@@ -2989,6 +3028,7 @@ __global__ __launch_bounds__(512) void k_upproj_merge(MergeArgs a) {
   for (int sx = 0; sx < NSM; ++sx) {
     wsx[sx] = sx < ns ? rel_weight(mv[sx], M) : 0.f;
     l += wsx[sx] * lv[sx];
+    if (MIX) wsx[sx] *= a.zinv;  // the f16 partials are scaled by zsc
   }
   const float il = 1.f / l;
   const int col = gk * g.d_h + nsl * 16 + n;  // B_v^T row of this lane's output column
@@ -3003,8 +3043,12 @@ __global__ __launch_bounds__(512) void k_upproj_merge(MergeArgs a) {
     const int c = 32 * kc + 8 * qq;  // first channel of this lane's 8
 #pragma unroll
     for (int sx = 0; sx < NSM; ++sx) {
-      z[u][sx][0] = ld16(zs[sx] + 32 * kc);
-      z[u][sx][1] = ld16(zs[sx] + 32 * kc + 4);
+      if (MIX) {
+        z[u][sx][0] = ld16((const uint16_t*)a.zp + zs[sx] + 32 * kc);  // 8 halves
+      } else {
+        z[u][sx][0] = ld16((const float*)a.zp + zs[sx] + 32 * kc);
+        z[u][sx][1] = ld16((const float*)a.zp + zs[sx] + 32 * kc + 4);
+      }
     }
     const int cc = c < g.r_v ? c : 0;
     if (DT == STARKV_F32) {
@@ -3027,7 +3071,11 @@ __global__ __launch_bounds__(512) void k_upproj_merge(MergeArgs a) {
     for (int e = 0; e < 8; ++e) {
       float t = 0.f;
 #pragma unroll
-      for (int sx = 0; sx < NSM; ++sx) t += wsx[sx] * __uint_as_float(z[u][sx][e >> 2][e & 3]);
+      for (int sx = 0; sx < NSM; ++sx) {
+        const uint32_t hw = z[u][sx][0][e >> 1];
+        t += wsx[sx] * (MIX ? f16_to_f32((uint16_t)(e & 1 ? hw >> 16 : hw & 0xFFFF))
+                            : __uint_as_float(z[u][sx][e >> 2][e & 3]));
+      }
       float scl = il;
       if (MIX) scl *= f16_to_f32((uint16_t)(e & 1 ? sc[u][e >> 1] >> 16 : sc[u][e >> 1] & 0xFFFF));
       zz[e] = (live && c + e < g.r_v) ? t * scl : 0.f;
@@ -3079,6 +3127,16 @@ __global__ __launch_bounds__(512) void k_upproj_merge(MergeArgs a) {
 
 // ===========================================================================
 
+// Scale of the f16 split partials of int8/int4 layers: a partial sums at most cps * 32 tokens'
+// weights (each at most 1) times codes of at most 127 in magnitude; the largest power of two
+// that keeps that bound within 32768 (half the f16 range).
+static float partial_scale(int cps) {
+  const double bound = (double)cps * kTC * 127.0;
+  int k = 0;
+  while (bound > 32768.0 * std::ldexp(1.0, k)) ++k;
+  return (float)std::ldexp(1.0, -k);
+}
+
 template <int LAT>
 static hipError_t launch_values_nmt(const ProfScope& ps, int nmt, dim3 grid, dim3 block, hipStream_t s,
                                     const ValueArgs& va) {
@@ -3126,6 +3184,7 @@ static hipError_t launch_values1(const ProfScope& ps, int nbw8, int nbw4, dim3 g
 static QprojArgs qproj_args(const Layer& L, const DecodePlan& plan, const KtList& kts, const void* q) {
   QprojArgs qa;
   qa.q = q;
+  qa.qp_w = 1;
   qa.B_k = L.B_k;
   qa.wqk = nullptr;
   qa.qraw = plan.ws.qraw;
@@ -3139,9 +3198,18 @@ static QprojArgs qproj_args(const Layer& L, const DecodePlan& plan, const KtList
   return qa;
 }
 
-// query-projection row groups: few KV heads x sequences spread a head's rows over workgroups
+// query-projection row groups of the fused step front: few KV heads x sequences spread a head's
+// rows over workgroups
 static int qproj_row_groups(const DecodeGeom& g) {
   return std::min(g.G * g.n_q, std::max(1, ceil_div(256, g.H_kv * g.B)));
+}
+
+// rows per workgroup of the query-projection launch: the rows of one KV head in one sequence, split
+// in row groups while there are few KV heads x sequences.  (Workgroups of 16 rows from four
+// sequences, a quarter as many, were slower on MI355X: 34 against 24 us on the 13B-class ragged
+// step, since a thread's dot products run one after another.)
+static int qproj_rows_per_wg(const DecodeGeom& g) {
+  return ceil_div(g.G * g.n_q, qproj_row_groups(g));
 }
 
 // First launch of a fused decode step: the few-token append's workgroups and the query
@@ -3164,8 +3232,15 @@ __global__ __launch_bounds__(256) void k_step_front(StepFrontArgs a) {
   const int blk = blockIdx.x;
   const int H = a.qa.g.H_kv, B = a.qa.g.B;
   const int n_qp = H * B * a.nrg;
-  if (blk < n_qp) qproj_body<DT, LAT, 256>(a.qa, blk % H, (blk / H) % B, blk / (H * B), a.nrg, sh);
-  else skinny_body<DT, SW, LAT == STARKV_LATENT_MIX84, 4>(a.ga, blk - n_qp, red);
+  if (blk < n_qp) {
+    // workgroup (KV head, sequence b, row group rg of nrg): rows rg rpg .. of g in sequence b
+    const int rph = a.qa.g.G * a.qa.g.n_q, rpg = (rph + a.nrg - 1) / a.nrg;
+    const int b = (blk / H) % B, rg = blk / (H * B);
+    const int r0 = min(rph, rg * rpg);
+    qproj_body<DT, LAT, 256>(a.qa, blk % H, b * rph + r0, b * rph + min(rph, r0 + rpg), sh);
+  } else {
+    skinny_body<DT, SW, LAT == STARKV_LATENT_MIX84, 4>(a.ga, blk - n_qp, red);
+  }
 }
 
 template <int SW>
@@ -3269,7 +3344,8 @@ hipError_t launch_decode(const Layer& L, const DecodePlan& plan, const KtList& k
   }
   {
     ProfScope ps("decode_qproj");
-    const dim3 gq(g.H_kv, g.B, qproj_row_groups(g));
+    qa.qp_w = qproj_rows_per_wg(g);
+    const dim3 gq(g.H_kv, ceil_div(g.B * g.G * g.n_q, qa.qp_w));
     if (wqk) {
       if (L.dtype == STARKV_F32) e = launch_k(ps, k_qproj<STARKV_F32, STARKV_LATENT_F32, true>, gq, dim3(256), s, qa);
       else if (L.latent == STARKV_LATENT_BF16) e = launch_k(ps, k_qproj<STARKV_BF16, STARKV_LATENT_BF16, true>, gq, dim3(256), s, qa);
@@ -3381,6 +3457,7 @@ static hipError_t launch_decode_tail(const Layer& L, const DecodePlan& plan, con
   va.g = g;
   va.seq = seq;
   va.cps = w.cps;
+  va.zsc = partial_scale(w.cps);
   va.bpw = w.blocks_per_wg;
   va.NB = L.v_rows / 32;
   va.V8 = L.V8;
@@ -3421,6 +3498,7 @@ static hipError_t launch_decode_tail(const Layer& L, const DecodePlan& plan, con
   // 4. merge + up-projection
   MergeArgs ma;
   ma.zp = w.zp;
+  ma.zinv = 1.f / partial_scale(w.cps);
   ma.sl = w.sl;
   ma.sm = w.sm;
   ma.zt = w.zt;

@@ -169,7 +169,9 @@ struct DecodeWs {
   void* p;          // [total_chunks][M_pad][kTC] probabilities (f16 / bf16 / f32)
   float* cm;        // [total_chunks][M_pad] chunk max (log2 units)
   float* cl;        // [total_chunks][M_pad] chunk sum
-  float* zp;        // [total_splits][M_pad][rv_ld] value-latent partials, weighted against sm
+  void* zp;         // [total_splits][M_pad][rv_ld] value-latent partials: fp32, weighted against
+                    // sm (bf16/fp32 latents); f16, divided by the split's sum sl (int8/int4
+                    // latents: a weighted mean of codes, within the code range)
   float* sl;        // [total_splits][M_pad] split sum of the probabilities, weighted against sm
   float* sm;        // [total_splits][M_pad] split maximum of the base-2 logits (the weights' reference)
   float* zt;        // [B][M_pad][rv_ld] merged value latent (scaled, normalised; zero padding)
