@@ -334,10 +334,21 @@ constexpr int kQpRMAX = 256;  // max rank (<= d_h <= 256)
 template <int RB>
 struct QprojSharedT {
   float qh[RB][kQpRMAX];
-  int8_t hi8[RB][kQpRMAX];
-  int8_t lo8[RB][kQpRMAX];
-  float rho_s[RB];
+  uint32_t amax[RB];  // bits of each row's max |q^| (non-negative floats order as integers)
 };
+
+// Two-part int8 split of a latent query element x of a row with max |q^| = m:
+// x ~ rho (hi + lo / 254), rho = m / 127 (1 for a zero row).
+__device__ __forceinline__ float qrow_rho(uint32_t amax_bits) {
+  const float m = __uint_as_float(amax_bits);
+  return m > 0.f ? m / 127.f : 1.f;
+}
+__device__ __forceinline__ void qsplit(float x, float rho, int& hi, int& lo) {
+  const float h = fminf(fmaxf(__builtin_rintf(x / rho), -127.f), 127.f);
+  const float l = fminf(fmaxf(__builtin_rintf((x - h * rho) * (254.f / rho)), -127.f), 127.f);
+  hi = (int)h;
+  lo = (int)l;
+}
 using QprojShared = QprojSharedT<kQpRB>;
 
 // Body of the query projection for the rows u in [u_lo, u_hi) of KV head gk (u = b G n_q + row of
@@ -350,9 +361,7 @@ __device__ __forceinline__ void qproj_body(const QprojArgs& a, int gk, int u_lo,
   constexpr int NX = 4;                             // 16-byte loads per operand per lane per round
   constexpr int CH = SUB * NX * EPL;                // elements of d_h per load round
   auto& qh = sh.qh;
-  auto& hi8 = sh.hi8;
-  auto& lo8 = sh.lo8;
-  auto& rho_s = sh.rho_s;
+  auto& amax = sh.amax;
   const DecodeGeom& g = a.g;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int rph = g.G * g.n_q;
@@ -364,6 +373,8 @@ __device__ __forceinline__ void qproj_body(const QprojArgs& a, int gk, int u_lo,
 
   for (int ub0 = u_lo; ub0 < u_hi; ub0 += RB) {
     const int nrows = min(RB, u_hi - ub0);
+    __syncthreads();  // the previous batch is done with qh and amax
+    if (tid < RB) amax[tid] = 0u;
     __syncthreads();
     // q^[n][k] = (q_n . B_k[c0 + k]) * scale * log2(e)/sqrt(d_h): SUB adjacent lanes per dot
     // product, lane sub taking the 16-byte pieces sub, sub + SUB, ... of the q row and the B_k
@@ -380,7 +391,11 @@ __device__ __forceinline__ void qproj_body(const QprojArgs& a, int gk, int u_lo,
         float sc = 1.f;
         if (LAT == STARKV_LATENT_MIX84) sc = f16_to_f32(a.scales[c0 + k]);
         const float v = a.qraw[((size_t)b * g.n_q + j) * ((size_t)g.G * g.n_key) + (size_t)g.G * c0 + hh * r + k];
-        if (sub == 0) qh[n][k] = v * sc * g.qscale;
+        if (sub == 0) {
+          const float x = v * sc * g.qscale;
+          qh[n][k] = x;
+          if (LAT == STARKV_LATENT_MIX84) atomicMax(&amax[n], __float_as_uint(fabsf(x)));
+        }
         continue;
       }
       const int hh = lr / g.n_q, j = lr % g.n_q;
@@ -421,39 +436,26 @@ __device__ __forceinline__ void qproj_body(const QprojArgs& a, int gk, int u_lo,
       for (int o = 1; o < SUB; o <<= 1) acc += __shfl_xor(acc, o, 64);
       float sc = 1.f;
       if (LAT == STARKV_LATENT_MIX84) sc = f16_to_f32(a.scales[c0 + k]);
-      if (sub == 0) qh[n][k] = acc * sc * g.qscale;
+      if (sub == 0) {
+        const float x = acc * sc * g.qscale;
+        qh[n][k] = x;
+        if (LAT == STARKV_LATENT_MIX84) atomicMax(&amax[n], __float_as_uint(fabsf(x)));
+      }
     }
     __syncthreads();
-    // per-row scale (int8 path): rho = max|q^| / 127, one wave per row
-    if (LAT == STARKV_LATENT_MIX84) {
-      for (int n = wave; n < nrows; n += NWV) {
-        float m = 0.f;
-        for (int k = lane; k < r; k += 64) m = fmaxf(m, fabsf(qh[n][k]));
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-        if (lane == 0) rho_s[n] = m > 0.f ? m / 127.f : 1.f;
-      }
-      __syncthreads();
-      for (int idx = tid; idx < nrows * r; idx += NT) {
-        const int n = idx / r, k = idx % r;
-        const float rho = rho_s[n], x = qh[n][k];
-        const float hi = fminf(fmaxf(__builtin_rintf(x / rho), -127.f), 127.f);
-        const float lo = fminf(fmaxf(__builtin_rintf((x - hi * rho) * (254.f / rho)), -127.f), 127.f);
-        hi8[n][k] = (int8_t)hi;
-        lo8[n][k] = (int8_t)lo;
-      }
-      __syncthreads();
-    }
     // row parameters: rho and the int4 offset-binary bias terms 8 * sum(int4 codes' weights)
     for (int n = wave; n < nrows; n += NWV) {
       // offset-binary codes: int4 nibbles read as code + 8; packed layout: outlier nibbles
       // code + 8, 3-bit inlier fields code + 4
       int sh = 0, sl = 0;
+      const float rho = LAT == STARKV_LATENT_MIX84 ? qrow_rho(amax[n]) : 1.f;
       if (LAT == STARKV_LATENT_MIX84)
         for (int k = (g.pack3 ? 0 : n8g) + lane; k < r; k += 64) {
           const int wgt = (g.pack3 && k >= n8g) ? 4 : 8;
-          sh += wgt * hi8[n][k];
-          sl += wgt * lo8[n][k];
+          int hi, lo;
+          qsplit(qh[n][k], rho, hi, lo);
+          sh += wgt * hi;
+          sl += wgt * lo;
         }
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) {
@@ -463,7 +465,7 @@ __device__ __forceinline__ void qproj_body(const QprojArgs& a, int gk, int u_lo,
       if (lane == 0) {
         const int b = (ub0 + n) / rph, i = gk * rph + (ub0 + n) - b * rph;
         float* rp = a.rowp + ((size_t)b * g.M_pad + i) * 4;
-        rp[0] = LAT == STARKV_LATENT_MIX84 ? rho_s[n] : 1.f;
+        rp[0] = rho;
         rp[1] = (float)sh;
         rp[2] = (float)sl;
         rp[3] = 0.f;
@@ -491,6 +493,7 @@ __device__ __forceinline__ void qproj_body(const QprojArgs& a, int gk, int u_lo,
         uint8_t* frag = a.qfrag + (((size_t)b * g.nct + ct) * a.nkt_max + jt) * 2048;
         if (LAT == STARKV_LATENT_MIX84) {
           const int P0 = kt * 64 + 16 * qq;
+          const float rho = qrow_rho(amax[n]);
           uint32_t wh[4] = {0, 0, 0, 0}, wl[4] = {0, 0, 0, 0};
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
@@ -513,8 +516,10 @@ __device__ __forceinline__ void qproj_body(const QprojArgs& a, int gk, int u_lo,
               if (u >= o4 && u < o4 + (r - n8g)) k = n8g + (u - o4);
             }
             if (k >= 0) {
-              wh[e >> 2] |= ((uint32_t)(uint8_t)hi8[n][k]) << (8 * (e & 3));
-              wl[e >> 2] |= ((uint32_t)(uint8_t)lo8[n][k]) << (8 * (e & 3));
+              int hi, lo;
+              qsplit(qh[n][k], rho, hi, lo);
+              wh[e >> 2] |= ((uint32_t)(uint8_t)(int8_t)hi) << (8 * (e & 3));
+              wl[e >> 2] |= ((uint32_t)(uint8_t)(int8_t)lo) << (8 * (e & 3));
             }
           }
           st16(frag + ln * 16, u32x4{wh[0], wh[1], wh[2], wh[3]});
@@ -2376,7 +2381,7 @@ __global__ __launch_bounds__(256) void k_values1(ValueArgs a) {
 // rotated by (row / 4) mod 4, which makes the A-fragment reads of 16 consecutive rows hit distinct
 // LDS banks.  Grid as k_values1 (one dimension; the groups of a split run on one XCD).
 template <int LAT, int NMT, int NTW, int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_values_mt(ValueArgs a) {
+__device__ __forceinline__ void values_mt_body(const ValueArgs& a) {
   static_assert(LAT != STARKV_LATENT_F32, "fp32 latents use k_values");
   constexpr int MP = 32 * NMT;
   constexpr int esz = LAT == STARKV_LATENT_BF16 ? 2 : 1;
@@ -2630,6 +2635,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     }
   }
 }
+
+// int8/int4 latents: two workgroups per CU (two waves per SIMD), with the accumulators in the
+// unified register file; bf16 latents: their larger LDS stages allow one workgroup per CU.
+template <int LAT, int NMT, int NTW, int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_values_mt_w2(ValueArgs a) {
+  values_mt_body<LAT, NMT, NTW, D>(a);
+}
+template <int LAT, int NMT, int NTW, int D>
+__global__ __launch_bounds__(256) void k_values_mt_w1(ValueArgs a) {
+  values_mt_body<LAT, NMT, NTW, D>(a);
+}
+template <int LAT, int NMT, int NTW, int D>
+constexpr auto values_mt_kernel() {
+  if constexpr (LAT == STARKV_LATENT_MIX84) return &k_values_mt_w2<LAT, NMT, NTW, D>;
+  else return &k_values_mt_w1<LAT, NMT, NTW, D>;
+}
+template <int LAT, int NMT, int NTW, int D>
+constexpr void (*k_values_mt)(ValueArgs) = values_mt_kernel<LAT, NMT, NTW, D>();
 
 // ===========================================================================
 // merge + up-projection: out = (sum_s z_s) * scale_v B_v^g / (sum_s l_s)
@@ -3335,13 +3358,11 @@ static hipError_t launch_decode_rope(const Layer& L, const DecodePlan& plan, con
   return launch_decode_tail(L, plan, kts, seq, out, k_rows, v_tiles, s, false);
 }
 
-hipError_t launch_decode(const Layer& L, const DecodePlan& plan, const KtList& kts, const SeqTable& seq,
-                         const void* q, void* out, const void* k_rows, const void* v_tiles, hipStream_t s,
-                         const float* wqk) {
+// The query fragments of a decode (and, with wqk, the hidden-state projection before them).
+static hipError_t launch_query_frags(const Layer& L, const DecodePlan& plan, const KtList& kts, const void* q,
+                                     hipStream_t s, const float* wqk) {
   const DecodeGeom& g = plan.g;
   hipError_t e = hipSuccess;
-  if (L.rope_theta > 0.f) return launch_decode_rope(L, plan, kts, seq, q, out, k_rows, v_tiles, s);
-  // 1. query fragments
   QprojArgs qa = qproj_args(L, plan, kts, q);
   qa.wqk = wqk;
   if (wqk) {
@@ -3365,8 +3386,16 @@ hipError_t launch_decode(const Layer& L, const DecodePlan& plan, const KtList& k
       else if (L.latent == STARKV_LATENT_BF16) e = launch_k(ps, k_qproj<STARKV_BF16, STARKV_LATENT_BF16, false>, gq, dim3(256), s, qa);
       else e = launch_k(ps, k_qproj<STARKV_BF16, STARKV_LATENT_MIX84, false>, gq, dim3(256), s, qa);
     }
-    if (e != hipSuccess) return e;
   }
+  return e;
+}
+
+hipError_t launch_decode(const Layer& L, const DecodePlan& plan, const KtList& kts, const SeqTable& seq,
+                         const void* q, void* out, const void* k_rows, const void* v_tiles, hipStream_t s,
+                         const float* wqk) {
+  if (L.rope_theta > 0.f) return launch_decode_rope(L, plan, kts, seq, q, out, k_rows, v_tiles, s);
+  const hipError_t e = launch_query_frags(L, plan, kts, q, s, wqk);
+  if (e != hipSuccess) return e;
   return launch_decode_tail(L, plan, kts, seq, out, k_rows, v_tiles, s);
 }
 
