@@ -294,6 +294,9 @@ def measure(w, args, dev, with_cpu: bool, steps: int, warmup: int) -> dict:
     lens = lens.astype(np.int32)
     lens_pre = (lens - n_q).astype(np.int32)  # each step appends at lens_pre and attends over lens
     T_max = int(-(-int(lens.max()) // 32) * 32)
+    if args.lens_dev:
+        # device lengths: the plan and the cache take a capacity, the kernels read the lengths
+        T_max = max(T_max, int(-(-args.lens_dev // 32) * 32))
     tdt = torch.float32 if w.dtype == "f32" else torch.bfloat16
 
     t0 = time.perf_counter()
@@ -346,13 +349,17 @@ def measure(w, args, dev, with_cpu: bool, steps: int, warmup: int) -> dict:
     X_np = I.as_dtype(I.x_new(w, n_q), w.dtype)
     q = to_dev_bf16(q_np, dev) if w.dtype == "bf16" else torch.from_numpy(q_np).to(dev)
     X_step = to_dev_bf16(X_np, dev) if w.dtype == "bf16" else torch.from_numpy(X_np).to(dev)
-    ws_bytes = max(L.workspace_bytes(w.B, n_q, lens) for L in layers)
+    # with --lens-dev the step is planned at the capacity for every sequence and the kernels take
+    # the lengths from a device array
+    lens_plan = np.full(w.B, T_max, np.int32) if args.lens_dev else lens
+    lens_dev = torch.from_numpy(lens).to(dev) if args.lens_dev else None
+    ws_bytes = max(L.workspace_bytes(w.B, n_q, lens_plan) for L in layers)
     ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
     outs = [torch.empty_like(q) for _ in range(n_layers)]
 
     def step(i):
         li = i % n_layers
-        layers[li].step(caches[li], X_step, q, lens, out=outs[li], ws=ws)
+        layers[li].step(caches[li], X_step, q, lens_plan, out=outs[li], ws=ws, lens_dev=lens_dev)
 
     if args.hidden_query:
         # each layer absorbs its own synthetic W_q [d, H_q d_h]; the step appends, then attends
@@ -446,7 +453,7 @@ def measure(w, args, dev, with_cpu: bool, steps: int, warmup: int) -> dict:
         dom = max((k for k in kern_us if k.startswith("decode_")), key=lambda k: kern_us[k])
         achieved = ab[dom] / (kern_us[dom] * 1e-6) / 1e9
         # counters cover the q path of unrotated layers only
-        traffic = None if args.hidden_query or args.rope else traffic_for(dom, w.name)
+        traffic = None if args.hidden_query or args.rope or args.lens_dev else traffic_for(dom, w.name)
     dec_us = sum(us for k, us in kern_us.items() if k.startswith("decode_"))
     res = {
         "value": w.B * n_q / (ms_step * 1e-3),
@@ -456,7 +463,8 @@ def measure(w, args, dev, with_cpu: bool, steps: int, warmup: int) -> dict:
                    "d_h": w.d_h, "hidden": w.d, "key_rank_sum": int(np.sum(probe.ranks)), "value_rank": probe.r_v,
                    "latent": w.latent, "layers_rotated": n_layers,
                    "query": "hidden states, absorbed W_q B_g^T" if args.hidden_query else "q",
-                   "rope_theta": args.rope or None},
+                   "rope_theta": args.rope or None,
+                   "lens_dev_capacity": T_max if args.lens_dev else None},
         "dtype": {"f32": "f32", "bf16": "bf16", "mix84": "int8/int4 codes, f16 MFMA, fp32 accumulate",
                   "had43": "4-bit/3-bit codes in int8/int4 bytes, f16 MFMA, fp32 accumulate",
                   "had43p": "4-bit/3-bit codes packed (3.2 bits), f16 MFMA, fp32 accumulate"}[w.latent],
@@ -707,6 +715,9 @@ def main() -> int:
                          "HBM rates) instead of the decode step")
     ap.add_argument("--rope", type=float, default=0.0, metavar="THETA",
                     help="rotary layers (base THETA): decode and prefill attend over reconstructed keys")
+    ap.add_argument("--lens-dev", type=int, default=0, metavar="CAP",
+                    help="plan the step at a capacity of CAP tokens per sequence and pass the lengths on "
+                         "the device (starkv_decode_step's lens_dev)")
     ap.add_argument("--copy-probe", action="store_true", help=f"copy {COPY_PROBE_MIB} MiB device to device")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"))
     args = ap.parse_args()

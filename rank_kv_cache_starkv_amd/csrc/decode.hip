@@ -599,6 +599,11 @@ __device__ __forceinline__ int seq_chunk0(const SeqTable& t, int b) { return t.u
 __device__ __forceinline__ int seq_nch(const SeqTable& t, int b) {
   return t.uni ? t.u_nch : t.chunk_off[b + 1] - t.chunk_off[b];
 }
+// chunks that hold tokens below the length the kernels see: the planned count, or with device
+// lengths the chunks of that length (later chunks and the splits made of them are skipped)
+__device__ __forceinline__ int seq_nch_live(const SeqTable& t, int b) {
+  return t.lens_dev ? (seq_len(t, b) + kTC - 1) / kTC : seq_nch(t, b);
+}
 __device__ __forceinline__ int seq_split0(const SeqTable& t, int b) { return t.uni ? b * t.u_nspl : t.split_off[b]; }
 __device__ __forceinline__ int seq_nsplit(const SeqTable& t, int b) {
   return t.uni ? t.u_nspl : t.split_off[b + 1] - t.split_off[b];
@@ -683,6 +688,7 @@ __global__ __launch_bounds__(256) void k_scores(ScoreArgs a) {
   const int b = seq_of_blk(a.seq, g.B, gblk);
   const int t_blk = (gblk - seq_blk0(a.seq, b)) * 128;
   const int len = seq_len(a.seq, b);
+  if (t_blk >= len) return;  // past the device length: no value split reads it (whole workgroup)
   const uint8_t* kbase = a.k_rows + (size_t)b * g.T_max * g.k_row_bytes;
   const int nkt = a.kts.n[ct];
   const int nkw = nkt > wave ? (nkt - wave + 3) / 4 : 0;  // K-tiles of this wave (uniform)
@@ -929,6 +935,7 @@ __global__ __launch_bounds__(256) void k_scores_chunk(ScoreArgs a) {
     while (cg >= seq_chunk0(a.seq, b + 1)) ++b;
     const int t0 = (cg - seq_chunk0(a.seq, b)) * kTC;
     const int len = seq_len(a.seq, b);
+    if (t0 >= len) continue;  // past the device length: no value split reads it
     const uint8_t* kbase = a.k_rows + (size_t)b * g.T_max * g.k_row_bytes;
     const int i = ct * 16 + n;  // query row of this lane's result column
     const bool rowvalid = i < g.M_q;
@@ -1178,13 +1185,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   int ci = c_first;
   int bi = seq_of_chunk(a.seq, g.B, c_first);
   int bi_end = seq_chunk0(a.seq, bi + 1);
+  int bi_len = seq_len(a.seq, bi);
   auto issue = [&](u32x4 kr[KTM][2]) {
-    const bool live = ci < c_end;  // wave-uniform
-    if (live)
+    bool live = ci < c_end;  // wave-uniform
+    if (live) {
       while (ci >= bi_end) {
         ++bi;
         bi_end = seq_chunk0(a.seq, bi + 1);
+        bi_len = seq_len(a.seq, bi);
       }
+      live = (ci - seq_chunk0(a.seq, bi)) * kTC < bi_len;  // (false only past a device length)
+    }
     const __amdgpu_buffer_rsrc_t krs =
         buf_rsrc(a.k_rows + (size_t)bi * g.T_max * g.k_row_bytes, live ? (uint32_t)g.T_max * rb : 0u);
     const uint32_t t0 = (uint32_t)(ci - seq_chunk0(a.seq, bi)) * kTC;
@@ -1222,6 +1233,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       bc0 = bc_end;
       bc_end = seq_chunk0(a.seq, bc + 1);
       bc_len = seq_len(a.seq, bc);
+    }
+    if ((cc - bc0) * kTC >= bc_len) {  // past a device length: no value split reads this chunk
+      cc += 2;
+      return;
     }
     if (bc != bf) {  // the block reaches another sequence (rare): its fragments first
       bf = bc;
@@ -1433,7 +1448,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   const int b = blockIdx.z, gk = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int r = lane & 31, q = lane >> 5;
-  const int nch = seq_nch(a.seq, b), len = seq_len(a.seq, b);
+  const int nch = seq_nch_live(a.seq, b), len = seq_len(a.seq, b);
   const int cbase = blockIdx.x * 4 * a.cpw;
   if (cbase >= nch) return;  // whole workgroup, before any barrier
   const int rows = g.G * g.n_q;  // query rows of this KV head (at most 32)
@@ -1880,8 +1895,9 @@ __global__ __launch_bounds__(256) void k_values(ValueArgs a) {
   const int b = seq_of_split(a.seq, g.B, sg);
   const int s = sg - seq_split0(a.seq, b);
   const int cbase = seq_chunk0(a.seq, b);
-  const int nch = seq_nch(a.seq, b);
+  const int nch = seq_nch_live(a.seq, b);
   const int c_lo = s * a.cps, c_hi = min(c_lo + a.cps, nch);
+  if (c_lo >= nch) return;  // a split past a device length (whole workgroup): the merges skip it
   const int len = seq_len(a.seq, b);
   const int r = lane & 31, q = lane >> 5;
   const bool is4 = (LAT == STARKV_LATENT_MIX84) && (nb >= a.V8 / 32);
@@ -2086,8 +2102,9 @@ __device__ __forceinline__ void values1_run(const ValueArgs& a, int slice, int s
   const int b = seq_of_split(a.seq, g.B, sg);
   const int s = sg - seq_split0(a.seq, b);
   const int cbase = seq_chunk0(a.seq, b);
-  const int nch = seq_nch(a.seq, b);
+  const int nch = seq_nch_live(a.seq, b);
   const int c_lo = s * a.cps, c_hi = min(c_lo + a.cps, nch);
+  if (c_lo >= nch) return;  // a split past a device length (whole workgroup): the merges skip it
   const int len = seq_len(a.seq, b);
   const bool rok = r < g.M_q;
   const size_t prow = (size_t)(rok ? r : 0);
@@ -2410,8 +2427,9 @@ __device__ __forceinline__ void values_mt_body(const ValueArgs& a) {
   if (a.vo.n) b = seq_of_split(a.seq, g.B, sg);
   const int s = sg - seq_split0(a.seq, b);
   const int cbase = seq_chunk0(a.seq, b);
-  const int nch = seq_nch(a.seq, b);
+  const int nch = seq_nch_live(a.seq, b);
   const int c_lo = s * a.cps, c_hi = min(c_lo + a.cps, nch);
+  if (c_lo >= nch) return;  // a split past a device length (whole workgroup): the merges skip it
   const int len = seq_len(a.seq, b);
   const uint32_t ring0 = lds_addr(ring);
 
@@ -2669,6 +2687,7 @@ struct MergeArgs {
   DecodeGeom g;
   SeqTable seq;
   int nsp;  // split merge: lanes sharing 4 channels (1, or 4 for many splits)
+  int cps;  // chunks per split
 };
 
 // Split merge.  Split s weighted its tiles against its own maximum m_s of the row, so with M the
@@ -2689,7 +2708,8 @@ __global__ __launch_bounds__(256) void k_zmerge(MergeArgs a) {
   const int c = blockIdx.x * (256 / nsp) + ((tid & 63) / nsp) * 4;
   const bool live = i < g.M_q && c < g.rv_ld;
   const int ic = min(i, g.M_q - 1), cc = min(c, g.rv_ld - 4);
-  const int s0 = seq_split0(a.seq, b), ns = seq_nsplit(a.seq, b);
+  const int s0 = seq_split0(a.seq, b);
+  const int ns = min(seq_nsplit(a.seq, b), (seq_nch_live(a.seq, b) + a.cps - 1) / a.cps);  // live splits
   const size_t zo = ((size_t)s0 * g.M_pad + ic) * g.rv_ld + cc;
   const float* zc = (const float*)a.zp + zo;
   const uint16_t* zh = (const uint16_t*)a.zp + zo;
@@ -3040,7 +3060,8 @@ __global__ __launch_bounds__(512) void k_upproj_merge(MergeArgs a) {
   const int rr = min((int)blockIdx.y * 16 + n, Rg - 1);  // A-fragment row of this lane
   const int bb = rr / rph;
   const int ii = gk * rph + rr % rph;
-  const int s0 = seq_split0(a.seq, bb), ns = seq_nsplit(a.seq, bb);
+  const int s0 = seq_split0(a.seq, bb);
+  const int ns = min(seq_nsplit(a.seq, bb), (seq_nch_live(a.seq, bb) + a.cps - 1) / a.cps);  // live splits
   size_t zs[NSM];  // element offsets of this lane's partial rows
   float lv[NSM], mv[NSM];
 #pragma unroll
@@ -3538,6 +3559,7 @@ static hipError_t launch_decode_tail(const Layer& L, const DecodePlan& plan, con
   MergeArgs ma;
   ma.zp = w.zp;
   ma.zinv = 1.f / partial_scale(w.cps);
+  ma.cps = w.cps;
   ma.sl = w.sl;
   ma.sm = w.sm;
   ma.zt = w.zt;
