@@ -61,10 +61,14 @@ __global__ __launch_bounds__(64 * NW) void k_latent_gemm(GemmArgs a) {
     b_base[h] = (size_t)(b_ok[h] ? ch : 0) * a.d;
     scb[h] = (MODE == 0 && a.latent == STARKV_LATENT_MIX84) ? scale_bits(a, ch) : (uint16_t)0;
   }
-  // this wave's K-steps (16 each): an NW-th of K
+  // this wave's K-steps (16 each): an NW-th of the workgroup's part of K (one part, or with the
+  // raw output ksplit parts, grid z)
   const int nk = a.d / 16;
-  const int per = (nk + NW - 1) / NW;
-  const int kb = wave * per, ke = min(nk, kb + per);
+  const int ksp = max(a.ksplit, 1);
+  const int pk = (nk + ksp - 1) / ksp;
+  const int k_lo = min(nk, (int)blockIdx.z * pk), k_hi = min(nk, k_lo + pk);
+  const int per = (k_hi - k_lo + NW - 1) / NW;
+  const int kb = k_lo + wave * per, ke = min(k_hi, kb + per);
 
   f32x16 acc[2][2];
 #pragma unroll
@@ -539,17 +543,26 @@ hipError_t launch_hidden_query(const Layer& L, const void* x, int M, const void*
     return launch_ev(bf ? k_latent_gemm_skinny<STARKV_BF16, 16, false, 4> : k_latent_gemm_skinny<STARKV_F32, 16, false, 2>,
                      dim3((a.NS + 15) / 16), dim3(512), s, a, start, stop);
   }
-  // tiled form, one launch: bf16 loads the high and low parts together (MODE 4)
+  // tiled form, one launch: bf16 loads the high and low parts together (MODE 4); K split over
+  // hidden_query_parts workgroups per tile, each storing its own partial sums
   const int n_rt = (M + 63) / 64, n_ct = (a.NS + 63) / 64;
   a.A_t = wqk_hi;
   a.A_t2 = wqk_lo;
+  a.ksplit = hidden_query_parts(M, a.NS);
+  a.out_part = (size_t)M * a.NS;
   a.xmap_rt = n_rt <= 16 ? n_rt : 0;
   if (a.xmap_rt > 0)
     return launch_ev(bf ? k_latent_gemm<STARKV_BF16, 4, 8> : k_latent_gemm<STARKV_F32, 2, 8>,
-                     dim3(8 * n_rt * ((n_ct + 7) / 8)), dim3(512), s, a, start, stop);
-  hipError_t e = launch_ev(bf ? k_latent_gemm<STARKV_BF16, 4, 4> : k_latent_gemm<STARKV_F32, 2, 4>, dim3(n_rt, n_ct),
-                           dim3(256), s, a, start, stop);
+                     dim3(8 * n_rt * ((n_ct + 7) / 8), 1, a.ksplit), dim3(512), s, a, start, stop);
+  hipError_t e = launch_ev(bf ? k_latent_gemm<STARKV_BF16, 4, 4> : k_latent_gemm<STARKV_F32, 2, 4>,
+                           dim3(n_rt, n_ct, a.ksplit), dim3(256), s, a, start, stop);
   return e;
+}
+
+int hidden_query_parts(int M, int NS) {
+  if (M <= 16) return 1;  // the skinny form
+  const int tiles = ((M + 63) / 64) * ((NS + 63) / 64);
+  return std::max(1, std::min(4, 256 / tiles));
 }
 
 }  // namespace skv

@@ -277,7 +277,8 @@ int plan_decode(const Layer& L, int B, int n_q, const int32_t* lens, int T_max, 
   const size_t o_sl = o; o = align256(o + (size_t)total_splits * g.M_pad * 4);
   const size_t o_sm = o; o = align256(o + (size_t)total_splits * g.M_pad * 4);
   const size_t o_zt = o; o = align256(o + (size_t)B * g.M_pad * g.rv_ld * 4);
-  const size_t o_qraw = o; o = align256(o + (size_t)B * n_q * L.G * L.n_key * 4);
+  w.qraw_parts = hidden_query_parts(B * n_q, L.G * L.n_key);
+  const size_t o_qraw = o; o = align256(o + (size_t)w.qraw_parts * B * n_q * L.G * L.n_key * 4);
   P->ws_bytes = o;
   uint8_t* base = (uint8_t*)ws_base;
   w.qfrag = base + o_qfrag;
@@ -305,7 +306,8 @@ struct QprojArgs {
   const void* q;        // queries [B][n_q][H_q][d_h], or hidden states [B][n_q][d] when wqk is set
   const void* B_k;
   const float* wqk;     // absorbed path: non-null (the projection x wqk^T is in qraw)
-  const float* qraw;    // [B n_q][G n_key] hidden-state query projection
+  const float* qraw;    // [qraw_parts][B n_q][G n_key] hidden-state query projection (K parts)
+  int qraw_parts;
   const uint16_t* scales;
   HeadTables heads;
   uint8_t* qfrag;
@@ -390,7 +392,11 @@ __device__ __forceinline__ void qproj_body(const QprojArgs& a, int gk, int u_lo,
         const int hh = lr / g.n_q, j = lr % g.n_q;
         float sc = 1.f;
         if (LAT == STARKV_LATENT_MIX84) sc = f16_to_f32(a.scales[c0 + k]);
-        const float v = a.qraw[((size_t)b * g.n_q + j) * ((size_t)g.G * g.n_key) + (size_t)g.G * c0 + hh * r + k];
+        // the projection's K parts, added in order
+        const size_t part = (size_t)g.B * g.n_q * g.G * g.n_key;
+        const size_t qi = ((size_t)b * g.n_q + j) * ((size_t)g.G * g.n_key) + (size_t)g.G * c0 + hh * r + k;
+        float v = a.qraw[qi];
+        for (int pp = 1; pp < a.qraw_parts; ++pp) v += a.qraw[qi + pp * part];
         if (sub == 0) {
           const float x = v * sc * g.qscale;
           qh[n][k] = x;
@@ -3242,6 +3248,7 @@ static QprojArgs qproj_args(const Layer& L, const DecodePlan& plan, const KtList
   qa.B_k = L.B_k;
   qa.wqk = nullptr;
   qa.qraw = plan.ws.qraw;
+  qa.qraw_parts = plan.ws.qraw_parts;
   qa.scales = L.scales;
   qa.heads = L.heads();
   qa.qfrag = (uint8_t*)plan.ws.qfrag;

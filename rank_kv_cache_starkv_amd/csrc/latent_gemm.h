@@ -40,6 +40,10 @@ struct GemmArgs {
   // stores X (A_t + A_t2)^T with the two parts loaded together
   float* out_f32;
   const void* A_t2;
+  // raw output (MODE 2 / 4) of the tiled GEMM: K split over ksplit parts (grid z), part z storing
+  // its partial sums at out_f32 + z * out_part (0 or 1: one part)
+  int ksplit;
+  size_t out_part;
 };
 
 // MODE 2 / 4 epilogue: out_f32[m][slot] = x for rows < M and slots < NS.
@@ -48,7 +52,7 @@ __device__ __forceinline__ void store_raw(const GemmArgs& a, int slot, const flo
 #pragma unroll
   for (int v = 0; v < R; ++v) {
     if (ms[v] >= a.M || slot >= a.NS) continue;
-    float* o = a.out_f32 + (size_t)ms[v] * a.NS + slot;
+    float* o = a.out_f32 + blockIdx.z * a.out_part + (size_t)ms[v] * a.NS + slot;
     *o = xs[v];
   }
 }

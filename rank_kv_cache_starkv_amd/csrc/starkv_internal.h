@@ -175,7 +175,8 @@ struct DecodeWs {
   float* sl;        // [total_splits][M_pad] split sum of the probabilities, weighted against sm
   float* sm;        // [total_splits][M_pad] split maximum of the base-2 logits (the weights' reference)
   float* zt;        // [B][M_pad][rv_ld] merged value latent (scaled, normalised; zero padding)
-  float* qraw;      // [B n_q][G n_key] hidden-state query projection (absorbed path)
+  float* qraw;      // [qraw_parts][B n_q][G n_key] hidden-state query projection (absorbed path): K parts
+  int qraw_parts;
   int nkt_max;
   int total_chunks, total_splits;
   int cps;          // score chunks per value split
@@ -213,6 +214,9 @@ hipError_t launch_absorb_query(const Layer& L, const void* W_q, float* wqk, hipS
 // timing events start, stop (either may be null) bracket all of its launches.
 hipError_t launch_hidden_query(const Layer& L, const void* x, int M, const void* wqk_hi, const void* wqk_lo,
                                float* out, hipStream_t s, hipEvent_t start, hipEvent_t stop);
+// K parts of that projection for M hidden rows and NS absorbed columns: its output holds that many
+// [M][NS] partial sums one after another (1 for the skinny form of at most 16 rows)
+int hidden_query_parts(int M, int NS);
 
 // A decode step: append n_q new tokens per sequence at lens_pre, then decode attention over
 // plan's lengths (lens_pre + n_q); few new rows run the append and the query projection in one

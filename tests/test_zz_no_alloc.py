@@ -23,23 +23,29 @@ def _bits(t):
     return t.view(torch.int32) if t.dtype == torch.float32 else t.view(torch.int16)
 
 
-def _case(run, w, lens0, step):
+def _case(run, w, lens0, step, slack=0):
     """The step on B = len(lens0) sequences of the run's cache: existing entry point (caller
-    workspace) from a copy of the cache, then the no-alloc one from the same starting bytes."""
+    workspace) from a copy of the cache, then the no-alloc one from the same starting bytes.
+    slack > 0: both calls take the lengths on the device, planned at lens + slack (capped at the
+    cache capacity)."""
     B, n_q = len(lens0), w.n_q
     wb = dataclasses.replace(w, B=B)
     lens = np.asarray(lens0, np.int32) + n_q
+    lens_dev = None
+    if slack:
+        lens_dev = torch.from_numpy(lens.copy()).to(H.DEV)
+        lens = np.minimum(lens + slack, run.cache.T_max).astype(np.int32)
     Xn = H.to_dev(H.hidden(run, I.x_new(wb, n_q, step=step)), w.dtype)
     q = H.to_dev(I.as_dtype(I.queries(wb, step=step), w.dtype), w.dtype)
     k0, v0 = run.cache.k_rows.clone(), run.cache.v_tiles.clone()
     ws = torch.empty((run.GL.workspace_bytes(B, n_q, lens),), dtype=torch.uint8, device=H.DEV)
-    ref = run.GL.step(run.cache, Xn, q, lens, out=torch.empty_like(q), ws=ws)
+    ref = run.GL.step(run.cache, Xn, q, lens, out=torch.empty_like(q), ws=ws, lens_dev=lens_dev)
     torch.cuda.synchronize()
     k_ref, v_ref = run.cache.k_rows.clone(), run.cache.v_tiles.clone()
     run.cache.k_rows.copy_(k0)
     run.cache.v_tiles.copy_(v0)
     out = torch.full_like(q, float("nan"))
-    run.GL.step_noalloc(run.cache, Xn, q, lens, out)
+    run.GL.step_noalloc(run.cache, Xn, q, lens, out, lens_dev=lens_dev)
     torch.cuda.synchronize()
     assert torch.equal(_bits(out), _bits(ref)), "output bits"
     assert torch.equal(run.cache.k_rows, k_ref) and torch.equal(run.cache.v_tiles, v_ref), "cache bytes"
@@ -63,6 +69,20 @@ def test_noalloc_step_matches_workspace_step(cfg):
     assert out1.shape[0] == len(lens0) and out2.shape[0] == 2
     # the oracle's bar for the first sequence of the first call is covered by the workspace
     # step's own parity tests; the two entry points agree bit for bit
+
+
+def test_noalloc_step_with_device_lengths():
+    """The no-alloc step with lengths on the device (planned 200 tokens past them) against the
+    workspace step with the same arguments, bit for bit, on two calls in a row."""
+    w = I.WORKLOADS[2]
+    lens0 = [250, 70, 180]
+    w = dataclasses.replace(w, B=len(lens0))
+    H.log(f"[noalloc lens_dev] cfg=2 lens0={lens0}")
+    run = H.make_layer(w, exact=True)
+    H.calibrate(run)
+    H.prefill(run, lens0, oracle_seqs=[0], T_max=max(lens0) + 2 * w.n_q + 256)
+    _case(run, w, lens0, step=3, slack=200)
+    _case(run, w, [min(x, 40) for x in lens0[:2]], step=4, slack=100)
 
 
 def test_noalloc_refuses_a_step_beyond_its_scratch():
