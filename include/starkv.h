@@ -388,7 +388,8 @@ int starkv_prefill_workspace_bytes(const starkv_layer* layer, int B, int n_q, co
  * head on MFMA (f16, rotated keys), then causal attention with an online softmax over 32-token
  * tiles.  q: device [B][n_q][H_q][d_h] (bf16); out: same shape.  ws: device workspace of
  * starkv_prefill_workspace_bytes (256-byte aligned, no initialisation): the latent and K^, V^ of
- * all sequences (each padded to a multiple of 32 tokens).  bf16 layers only (EUNSUPPORTED for
+ * all sequences (each padded to a multiple of 32 tokens), and for int8/int4 layers an f16 copy of
+ * B_v with the value scales folded in (the value reconstruction multiplies the codes by it).  bf16 layers only (EUNSUPPORTED for
  * fp32).  Reconstructed keys and values are held in f16: their magnitudes must stay within its
  * range.  Errors: EINVAL, ECAPACITY, EWORKSPACE, ESTATE, EUNSUPPORTED, EHIP.
  */

@@ -13,10 +13,13 @@
 //   1. k_deq_latent  the dequantised latent of every cached token, token-major: key channels
 //                    in fp32, xk[t][c] = code * scale_c (or the stored bf16 / fp32 latent); value
 //                    channels as bf16 high and low parts of the same fp32 value, xv_hi[t][c] and
-//                    xv_lo[t][c], rows padded with zeros to a multiple of 64 channels
+//                    xv_lo[t][c], rows padded with zeros to a multiple of 64 channels; int8/int4
+//                    layers (r_v a multiple of 8) store the value codes themselves, exact in f16,
+//                    in xv_hi, and k_scale_bv folds the scales into an f16 copy of B_v^T
 //   2. k_recon       K^_g = xk_g B_g per KV head on MFMA (fp32 latent split into bf16 high and low
 //                    parts), the rotation of the keys at their positions in the epilogue;
-//      k_recon_v     V^ = (xv_hi + xv_lo) B_v for all heads at once, a GEMM whose operand tiles
+//      k_recon_v     V^ = (xv_hi + xv_lo) B_v for all heads at once (int8/int4: codes times the
+//                    scaled B_v, one f16 MFMA instead of two bf16 ones), a GEMM whose operand tiles
 //                    stream through LDS; stored as f16, K^ token-major and V^ transposed (dims x
 //                    tokens)
 //   3. k_flash       causal attention of the query chunk over K^, V^: 32-token key tiles with an
@@ -80,6 +83,7 @@ struct DeqArgs {
   uint16_t* xv_lo;  // [total][rvp]
   int n_lat, n_key, r_v, rvp, H_kv, K8, V8, n8v, k_row_bytes, v_rows, T_max;
   int pack3, K4, V4;  // packed layout: outlier nibbles, then 3-bit planes from K4 / V4
+  int codes;          // int8/int4 values: the codes, in f16, into xv_hi (xv_lo unused)
   SeqBases sb;
 };
 
@@ -114,7 +118,8 @@ __device__ __forceinline__ float deq_key(const DeqArgs& a, int b, int t, int c) 
     return ((const float*)row)[c];
   }
 }
-template <int LAT>
+// CODE (int8/int4): the code alone, without its scale
+template <int LAT, bool CODE = false>
 __device__ __forceinline__ float deq_value(const DeqArgs& a, int b, int t, int cv) {
   const int c = a.n_key + cv;
   if (LAT == STARKV_LATENT_MIX84 && a.pack3) {
@@ -126,14 +131,14 @@ __device__ __forceinline__ float deq_value(const DeqArgs& a, int b, int t, int c
     } else {
       code = val_code3(a.v_tiles, b, t, cv - a.n8v, a.V4, a.v_rows, a.T_max);
     }
-    return (float)code * f16_to_f32(a.scales[c]);
+    return CODE ? (float)code : (float)code * f16_to_f32(a.scales[c]);
   } else if (LAT == STARKV_LATENT_MIX84) {
     const bool i4 = cv >= a.n8v;
     const int w = cv - a.n8v;
     const int vr = i4 ? a.V8 + (w >> 1) : cv;
     const int byte = a.v_tiles[vblock_off(b, vr >> 5, t / kTT, a.v_rows, a.T_max, 1) + (vr & 31) * kTT + t % kTT];
     const int code = i4 ? ((int)(((w & 1) ? byte >> 4 : byte) & 0xF) ^ 8) - 8 : (int)(int8_t)byte;
-    return (float)code * f16_to_f32(a.scales[c]);
+    return CODE ? (float)code : (float)code * f16_to_f32(a.scales[c]);
   } else if (LAT == STARKV_LATENT_BF16) {
     const uint16_t* blk = (const uint16_t*)(a.v_tiles + vblock_off(b, cv >> 5, t / kTT, a.v_rows, a.T_max, 2));
     return bf16_to_f32(blk[(cv & 31) * kTT + t % kTT]);
@@ -158,6 +163,20 @@ __global__ __launch_bounds__(256) void k_deq_latent(DeqArgs a) {
   }
   // value channels in pairs: one 32-bit store of each part per pair
   const int np = a.rvp / 2;
+  if (LAT == STARKV_LATENT_MIX84 && a.codes) {
+#pragma unroll 4
+    for (int idx = threadIdx.x; idx < kRT * np; idx += 256) {
+      const int tl = idx / np, cv = 2 * (idx % np);
+      const int t = t0 + tl;
+      float x0 = deq_value<LAT, true>(a, b, t, min(cv, a.r_v - 1));
+      float x1 = deq_value<LAT, true>(a, b, t, min(cv + 1, a.r_v - 1));
+      x0 = t < len && cv < a.r_v ? x0 : 0.f;
+      x1 = t < len && cv + 1 < a.r_v ? x1 : 0.f;
+      *(uint32_t*)(a.xv_hi + (size_t)(tok0 + tl) * a.rvp + cv) =
+          (uint32_t)f32_to_f16(x0) | ((uint32_t)f32_to_f16(x1) << 16);
+    }
+    return;
+  }
 #pragma unroll 4
   for (int idx = threadIdx.x; idx < kRT * np; idx += 256) {
     const int tl = idx / np, cv = 2 * (idx % np);
@@ -377,10 +396,12 @@ struct ReconVArgs {
   SeqBases sb;
 };
 
-template <int TM, int TN, int NST>
+// CODES: xv_hi holds f16 value codes and B_vt the f16 scaled factors (k_scale_bv): one f16 MFMA
+// per K-step and no low part.
+template <int TM, int TN, int NST, bool CODES = false>
 __global__ __launch_bounds__(256) void k_recon_v(ReconVArgs a) {
   constexpr int XB = TM * 128, WB = TN * 128;  // bytes of the operand tiles of a K block
-  constexpr int SB = 2 * XB + WB;              // bytes of a stage
+  constexpr int SB = (CODES ? 1 : 2) * XB + WB;  // bytes of a stage
   constexpr int LX = TM / 32, LW = TN / 32;    // 16-byte loads per wave per X / W tile
   constexpr int MT = TM / 64, NTT = TN / 64;   // 32 x 32 tiles per wave, rows and columns
   extern __shared__ __align__(16) uint8_t ring_raw[];
@@ -411,12 +432,12 @@ __global__ __launch_bounds__(256) void k_recon_v(ReconVArgs a) {
   const uint32_t ring0 = lds_addr(ring_raw);
   auto issue = [&](int kb, int st) {
     kb = min(kb, nkb - 1);  // past the end: reload the last block (never read)
-    const uint32_t hb = ring0 + st * SB, lb = hb + XB, wb = lb + XB;
+    const uint32_t hb = ring0 + st * SB, lb = hb + XB, wb = CODES ? lb : lb + XB;
 #pragma unroll
     for (int jj = 0; jj < LX; ++jj) {
       const uint32_t slot = 1024 * (LX * wave + jj);
       lds_dma16(a.xv_hi + xoff[jj] + 64 * kb, hb + slot);
-      lds_dma16(a.xv_lo + xoff[jj] + 64 * kb, lb + slot);
+      if (!CODES) lds_dma16(a.xv_lo + xoff[jj] + 64 * kb, lb + slot);
     }
 #pragma unroll
     for (int jj = 0; jj < LW; ++jj)
@@ -448,13 +469,13 @@ __global__ __launch_bounds__(256) void k_recon_v(ReconVArgs a) {
 #pragma unroll
   for (int u = 0; u < NST - 1; ++u) issue(u, u);
   for (int kb = 0; kb < nkb; ++kb) {
-    vm_wait<(2 * LX + LW) * (NST - 2)>();  // this wave's loads of block kb are in
+    vm_wait<((CODES ? 1 : 2) * LX + LW) * (NST - 2)>();  // this wave's loads of block kb are in
     __builtin_amdgcn_s_barrier();            // ... and every wave's; block kb - 1's stage is free
     asm volatile("" ::: "memory");
     issue(kb + NST - 1, (kb + NST - 1) % NST);
     const uint8_t* ht = ring_raw + (kb % NST) * SB;
     const uint8_t* lt = ht + XB;
-    const uint8_t* wt = lt + XB;
+    const uint8_t* wt = CODES ? lt : lt + XB;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int c = 2 * ks + q;
@@ -462,7 +483,7 @@ __global__ __launch_bounds__(256) void k_recon_v(ReconVArgs a) {
 #pragma unroll
       for (int i = 0; i < MT; ++i) {
         xh[i] = *(const u32x4*)(ht + xo[i] + 16 * (c ^ xsw[i]));
-        xl[i] = *(const u32x4*)(lt + xo[i] + 16 * (c ^ xsw[i]));
+        if (!CODES) xl[i] = *(const u32x4*)(lt + xo[i] + 16 * (c ^ xsw[i]));
       }
 #pragma unroll
       for (int j = 0; j < NTT; ++j) wf[j] = *(const u32x4*)(wt + wo[j] + 16 * (c ^ wsw[j]));
@@ -470,8 +491,12 @@ __global__ __launch_bounds__(256) void k_recon_v(ReconVArgs a) {
       for (int i = 0; i < MT; ++i)
 #pragma unroll
         for (int j = 0; j < NTT; ++j) {
-          acc[i][j] = mfma32_bf16(as_bf16x8(xh[i]), as_bf16x8(wf[j]), acc[i][j]);
-          acc[i][j] = mfma32_bf16(as_bf16x8(xl[i]), as_bf16x8(wf[j]), acc[i][j]);
+          if (CODES) {
+            acc[i][j] = mfma32_f16(as_f16x8(xh[i]), as_f16x8(wf[j]), acc[i][j]);
+          } else {
+            acc[i][j] = mfma32_bf16(as_bf16x8(xh[i]), as_bf16x8(wf[j]), acc[i][j]);
+            acc[i][j] = mfma32_bf16(as_bf16x8(xl[i]), as_bf16x8(wf[j]), acc[i][j]);
+          }
         }
     }
   }
@@ -503,6 +528,19 @@ __global__ __launch_bounds__(256) void k_recon_v(ReconVArgs a) {
       }
     }
   }
+}
+
+// B_v^T with the value scales folded in, for the code operand of k_recon_v:
+// out[n][k] = f16(scale_(n_key + k) * B_vt[n][k]) for n < N, k < r_v (2 elements per thread).
+__global__ __launch_bounds__(256) void k_scale_bv(const uint16_t* B_vt, const uint16_t* vscales, int N, int r_v,
+                                                  uint16_t* out) {
+  const size_t i = 2 * ((size_t)blockIdx.x * 256 + threadIdx.x);
+  if (i >= (size_t)N * r_v) return;  // r_v is even (a multiple of 8): pairs stay in one row
+  const int k = (int)(i % r_v);
+  const uint32_t bv = *(const uint32_t*)(B_vt + i);
+  const float x0 = bf16_to_f32((uint16_t)(bv & 0xFFFF)) * f16_to_f32(vscales[k]);
+  const float x1 = bf16_to_f32((uint16_t)(bv >> 16)) * f16_to_f32(vscales[k + 1]);
+  *(uint32_t*)(out + i) = (uint32_t)f32_to_f16(x0) | ((uint32_t)f32_to_f16(x1) << 16);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -729,6 +767,9 @@ struct PrefillWs {
 
 int value_rows_padded(const Layer& L) { return ceil_div(L.r_v, 64) * 64; }
 
+// whether the value reconstruction takes the codes and the scaled B_v (int8/int4, r_v % 8 == 0)
+bool value_codes(const Layer& L) { return L.latent == STARKV_LATENT_MIX84 && (L.r_v & 7) == 0; }
+
 PrefillWs prefill_layout(const Layer& L, int total) {
   PrefillWs w;
   size_t o = 0;
@@ -737,7 +778,9 @@ PrefillWs prefill_layout(const Layer& L, int total) {
   w.o_xvh = o;
   o = align256(o + (size_t)total * value_rows_padded(L) * 2);
   w.o_xvl = o;
-  o = align256(o + (size_t)total * value_rows_padded(L) * 2);
+  // int8/int4 layers with r_v a multiple of 8 keep the f16 scaled B_v^T here instead of a low part
+  o = align256(o + std::max((size_t)total * value_rows_padded(L),
+                            value_codes(L) ? (size_t)L.H_kv * L.d_h * L.r_v : (size_t)0) * 2);
   w.o_kh = o;
   o = align256(o + (size_t)total * L.H_kv * L.d_h * 2);
   w.o_vt = o;
@@ -769,7 +812,20 @@ hipError_t launch_recon_flash(const Layer& L, const ReconArgs& ra, const ReconVA
                                              : launch_lds(ps, k_recon<NT, true, 0, false>, grid_r, dim3(256), lds, s, ra);
     if (e != hipSuccess) return e;
   }
-  if ((L.r_v & 7) == 0) {
+  if (value_codes(L)) {
+    ProfScope ps("prefill_recon_v");
+    constexpr int T = kReconVTile;
+    // the scaled factors into the low-part region, then codes x scaled factors
+    ReconVArgs vc = va;
+    const size_t n_el = (size_t)va.N * L.r_v;
+    hipLaunchKernelGGL(k_scale_bv, dim3((unsigned)((n_el / 2 + 255) / 256)), dim3(256), 0, s, va.B_vt,
+                       L.scales + L.n_key, va.N, L.r_v, (uint16_t*)va.xv_lo);
+    vc.B_vt = va.xv_lo;
+    const dim3 grid(ceil_div(total, T), ceil_div(va.N, T));
+    const hipError_t e = launch_lds(ps, k_recon_v<T, T, kReconVStages, true>, grid, dim3(256),
+                                    (size_t)kReconVStages * 2 * T * 128, s, vc);
+    if (e != hipSuccess) return e;
+  } else if ((L.r_v & 7) == 0) {
     ProfScope ps("prefill_recon_v");
     constexpr int T = kReconVTile;
     const dim3 grid(ceil_div(total, T), ceil_div(va.N, T));
@@ -833,6 +889,7 @@ hipError_t launch_prefill(const Layer& L, const starkv_cache& c, const void* q, 
   da.k_row_bytes = L.k_row_bytes;
   da.v_rows = L.v_rows;
   da.T_max = c.T_max;
+  da.codes = value_codes(L) ? 1 : 0;
   da.sb = sb;
   hipError_t e;
   {

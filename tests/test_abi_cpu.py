@@ -266,7 +266,12 @@ def test_rope_setup_and_prefill_workspace():
     tot = 128 + 64
     n_lat, H_kv, d_h = layer.info["n_lat"], w.H_kv, w.d_h
     al = lambda x: -(-x // 256) * 256  # noqa: E731
-    exp = al(tot * n_lat * 4) + 2 * al(tot * H_kv * d_h * 2)
+    n_key, r_v = layer.info["n_key"], layer.r_v
+    rvp = -(-r_v // 64) * 64
+    # latent (fp32 keys, f16 codes of the values), then the scaled B_v^T of the int8/int4 value
+    # reconstruction (or the values' low part, whichever is larger), then K^ and V^ (f16)
+    exp = (al(tot * n_key * 4) + al(tot * rvp * 2) + al(max(tot * rvp, H_kv * d_h * r_v) * 2)
+           + 2 * al(tot * H_kv * d_h * 2))
     assert layer.prefill_workspace_bytes(2, 7, lens) == exp
     dec = layer.workspace_bytes(2, 1, lens)
     layer.set_rope(10000.0)
