@@ -78,7 +78,7 @@ struct DeqArgs {
   const uint16_t* scales;
   const int* src;  // [n_lat] (head << 16) | index within the head; head = H_kv for value channels
   HeadTables heads;
-  float* xk;       // [total][n_key]
+  float* xk;       // [total][n_key] (int8/int4 layers: f16 codes, [total][n_key] halves)
   uint16_t* xv_hi;  // [total][rvp]
   uint16_t* xv_lo;  // [total][rvp]
   int n_lat, n_key, r_v, rvp, H_kv, K8, V8, n8v, k_row_bytes, v_rows, T_max;
@@ -89,7 +89,8 @@ struct DeqArgs {
 
 // Workgroup = one 32-token tile of one sequence; thread items walk (token, channel) with the
 // channel fastest, so the stores are contiguous.  Tokens past the length get 0.
-template <int LAT>
+// CODE (int8/int4): the code alone, without its scale
+template <int LAT, bool CODE = false>
 __device__ __forceinline__ float deq_key(const DeqArgs& a, int b, int t, int c) {
   const uint8_t* row = a.k_rows + ((size_t)b * a.T_max + t) * a.k_row_bytes;
   if (LAT == STARKV_LATENT_MIX84) {
@@ -111,7 +112,7 @@ __device__ __forceinline__ float deq_key(const DeqArgs& a, int b, int t, int c) 
       const int byte = row[a.K8 + (u >> 1)];
       code = ((int)(((u & 1) ? byte >> 4 : byte) & 0xF) ^ 8) - 8;  // signed nibble
     }
-    return (float)code * f16_to_f32(a.scales[c]);
+    return CODE ? (float)code : (float)code * f16_to_f32(a.scales[c]);
   } else if (LAT == STARKV_LATENT_BF16) {
     return bf16_to_f32(((const uint16_t*)row)[c]);
   } else {
@@ -154,12 +155,23 @@ __global__ __launch_bounds__(256) void k_deq_latent(DeqArgs a) {
   const int t0 = tok0 - a.sb.base[b], len = a.sb.lens[b];
   // no branch around the loads (tokens of the tile past the length are still cache rows below
   // T_max; their values are replaced by 0 after the load), so unrolled iterations overlap
+  if (LAT == STARKV_LATENT_MIX84) {
+    // int8/int4 keys: the codes themselves, exact in f16 (k_recon folds the scales into B_g)
 #pragma unroll 4
-  for (int idx = threadIdx.x; idx < kRT * a.n_key; idx += 256) {
-    const int tl = idx / a.n_key, c = idx % a.n_key;
-    const int t = t0 + tl;
-    const float x = deq_key<LAT>(a, b, t, c);
-    a.xk[(size_t)(tok0 + tl) * a.n_key + c] = t < len ? x : 0.f;
+    for (int idx = threadIdx.x; idx < kRT * a.n_key; idx += 256) {
+      const int tl = idx / a.n_key, c = idx % a.n_key;
+      const int t = t0 + tl;
+      const float x = deq_key<LAT, true>(a, b, t, c);
+      ((uint16_t*)a.xk)[(size_t)(tok0 + tl) * a.n_key + c] = f32_to_f16(t < len ? x : 0.f);
+    }
+  } else {
+#pragma unroll 4
+    for (int idx = threadIdx.x; idx < kRT * a.n_key; idx += 256) {
+      const int tl = idx / a.n_key, c = idx % a.n_key;
+      const int t = t0 + tl;
+      const float x = deq_key<LAT>(a, b, t, c);
+      a.xk[(size_t)(tok0 + tl) * a.n_key + c] = t < len ? x : 0.f;
+    }
   }
   // value channels in pairs: one 32-bit store of each part per pair
   const int np = a.rvp / 2;
@@ -197,7 +209,8 @@ __global__ __launch_bounds__(256) void k_deq_latent(DeqArgs a) {
 // 2. reconstruction of K^ and V^ per KV head (bf16 factors)
 
 struct ReconArgs {
-  const float* xk;       // [total][n_key]
+  const float* xk;       // [total][n_key] (KC: f16 codes)
+  const uint16_t* kscales;  // KC: the key channels' f16 scales
   const uint16_t* xv_hi;  // [total][rvp]
   const uint16_t* xv_lo;
   const uint16_t* B_k;   // [n_key][d_h]
@@ -221,12 +234,14 @@ __device__ __forceinline__ int vt_slot(int t) {
 
 // Workgroup = (128 tokens, KV head g, keys or values), four waves of 32 tokens x all d_h columns
 // (NT = d_h / 32 column tiles of 32x32x16 bf16 MFMA).  The latent row of a token is split into
-// bf16 high and low parts (two MFMAs), so the product is as accurate as fp32 x bf16.  Keys read
+// bf16 high and low parts (two MFMAs), so the product is as accurate as fp32 x bf16.  KC
+// (int8/int4 keys): the latent holds the codes in f16 and the staged B_g rows are scaled by their
+// channel's scale and rounded to f16, one f16 MFMA per K-step.  Keys read
 // B_g transposed from LDS (staged by the workgroup); values (only when r_v is not a multiple of 8:
 // otherwise k_recon_v) read B_v^T rows directly and the latent's parts as stored.  Rotary keys
 // (over the whole head dimension): the pair (e, e + d_h / 2) is rotated by
 // position * theta^(-2 e / d_h), the angle formed and reduced in fp64.
-template <int NT, bool VEC, int KIND, bool ROPE>
+template <int NT, bool VEC, int KIND, bool ROPE, bool KC = false>
 __global__ __launch_bounds__(256) void k_recon(ReconArgs a) {
   extern __shared__ uint16_t bkt[];  // keys: B_g^T [d_h][rpad]
   __shared__ double inv_freq[128];    // rotary keys: theta^(-2 e / d_h), e < d_h / 2
@@ -254,9 +269,12 @@ __global__ __launch_bounds__(256) void k_recon(ReconArgs a) {
         const int i = i0 + 256 * u;
         const int k = i % a.rpad, e8 = i / a.rpad;
         if (i < n16) {
+          const float ks = KC && k < rk ? f16_to_f32(a.kscales[c_lo + k]) : 0.f;
 #pragma unroll
-          for (int j = 0; j < 8; ++j)
-            bkt[(8 * e8 + j) * a.rpad + k] = k < rk ? (uint16_t)(v[u][j >> 1] >> (16 * (j & 1))) : (uint16_t)0;
+          for (int j = 0; j < 8; ++j) {
+            const uint16_t bb = (uint16_t)(v[u][j >> 1] >> (16 * (j & 1)));
+            bkt[(8 * e8 + j) * a.rpad + k] = k < rk ? (KC ? f32_to_f16(bf16_to_f32(bb) * ks) : bb) : (uint16_t)0;
+          }
         }
       }
     }
@@ -273,10 +291,22 @@ __global__ __launch_bounds__(256) void k_recon(ReconArgs a) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[nt][v] = 0.f;
   const float* xr = a.xk + (size_t)tok * a.n_key + c_lo;
+  const uint16_t* xr16 = (const uint16_t*)a.xk + (size_t)tok * a.n_key + c_lo;
   for (int k0 = 0; k0 < rk; k0 += 16) {
     const int kb = k0 + 8 * q;
     bf16x8 ah, al;
-    if (kind == 0) {
+    if (KC) {
+      // f16 codes (channels past the head's rank: 0)
+      uint32_t hw[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t c0 = kb + 2 * i < rk ? xr16[kb + 2 * i] : 0u;
+        const uint32_t c1 = kb + 2 * i + 1 < rk ? xr16[kb + 2 * i + 1] : 0u;
+        hw[i] = c0 | (c1 << 16);
+      }
+      ah = as_bf16x8(u32x4{hw[0], hw[1], hw[2], hw[3]});  // (f16 bits; the MFMA reads them as f16)
+      al = ah;
+    } else if (kind == 0) {
       float xv[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) xv[i] = kb + i < rk ? xr[kb + i] : 0.f;
@@ -317,8 +347,12 @@ __global__ __launch_bounds__(256) void k_recon(ReconArgs a) {
       if (kind == 0) {
         // keys: K^T tiles (rows = head dims, columns = tokens), so that a lane holds runs of 4
         // consecutive dims of one token for the token-major store
-        acc[nt] = mfma32_bf16(as_bf16x8(bw), ah, acc[nt]);
-        acc[nt] = mfma32_bf16(as_bf16x8(bw), al, acc[nt]);
+        if (KC) {
+          acc[nt] = mfma32_f16(as_f16x8(bw), __builtin_bit_cast(f16x8, ah), acc[nt]);
+        } else {
+          acc[nt] = mfma32_bf16(as_bf16x8(bw), ah, acc[nt]);
+          acc[nt] = mfma32_bf16(as_bf16x8(bw), al, acc[nt]);
+        }
       } else {
         acc[nt] = mfma32_bf16(ah, as_bf16x8(bw), acc[nt]);
         acc[nt] = mfma32_bf16(al, as_bf16x8(bw), acc[nt]);
@@ -808,8 +842,13 @@ hipError_t launch_recon_flash(const Layer& L, const ReconArgs& ra, const ReconVA
   const dim3 grid_r(ceil_div(total, 128), L.H_kv);
   {
     ProfScope ps("prefill_recon");
-    const hipError_t e = ra.rope_theta > 0.f ? launch_lds(ps, k_recon<NT, true, 0, true>, grid_r, dim3(256), lds, s, ra)
-                                             : launch_lds(ps, k_recon<NT, true, 0, false>, grid_r, dim3(256), lds, s, ra);
+    const bool kc = L.latent == STARKV_LATENT_MIX84;
+    const hipError_t e =
+        ra.rope_theta > 0.f
+            ? (kc ? launch_lds(ps, k_recon<NT, true, 0, true, true>, grid_r, dim3(256), lds, s, ra)
+                  : launch_lds(ps, k_recon<NT, true, 0, true>, grid_r, dim3(256), lds, s, ra))
+            : (kc ? launch_lds(ps, k_recon<NT, true, 0, false, true>, grid_r, dim3(256), lds, s, ra)
+                  : launch_lds(ps, k_recon<NT, true, 0, false>, grid_r, dim3(256), lds, s, ra));
     if (e != hipSuccess) return e;
   }
   if (value_codes(L)) {
@@ -905,6 +944,7 @@ hipError_t launch_prefill(const Layer& L, const starkv_cache& c, const void* q, 
   for (int g = 0; g < L.H_kv; ++g) rmax = std::max(rmax, L.rk[g]);
   ReconArgs ra;
   ra.xk = xk;
+  ra.kscales = L.scales;
   ra.xv_hi = xvh;
   ra.xv_lo = xvl;
   ra.B_k = (const uint16_t*)L.B_k;
