@@ -104,6 +104,50 @@ def algorithmic_bytes(w, ranks, r_v, lens, n_q, hidden=False):
     return b
 
 
+# dense MFMA peaks of MI355X (TFLOP/s or TOP/s) by the operand type each decode contraction uses
+MFMA_PEAK = {"f32": 157.3, "bf16": 2500.0, "f16": 2500.0, "i8": 5000.0}
+
+
+def algorithmic_flops(w, ranks, r_v, lens, n_q):
+    """Multiply-adds (x2) the decode contractions must do per step, with the MFMA operand type of
+    each: key scores (every query row against its KV head's r_g channels of every cached token),
+    value aggregation (every query row against the r_v value channels of every token) and the
+    up-projection (r_v x d_h per row and head)."""
+    tokens = float(np.sum(lens))
+    G = w.H_q // w.H_kv
+    n_key = int(sum(ranks))
+    quant = w.latent in QUANTIZED
+    t_sc = "f32" if w.latent == "f32" else ("i8" if quant else "bf16")
+    t_v = "f32" if w.latent == "f32" else ("f16" if quant else "bf16")
+    return {
+        "decode_scores": (2.0 * n_q * G * n_key * tokens, t_sc),
+        "decode_values": (2.0 * w.H_q * n_q * r_v * tokens, t_v),
+        "decode_upproj": (2.0 * w.B * n_q * w.H_q * r_v * w.d_h, "f32" if w.latent == "f32" else "bf16"),
+    }
+
+
+def roofline_of(kernel, us, byts, flops, traffic):
+    """Roofline of one kernel: HBM (algorithmic bytes at 8 TB/s) and MFMA (algorithmic flops at
+    the dense peak of its operand type); the bound is the larger of the two ideal times, and both
+    fractions are reported."""
+    t_hbm = byts / (HBM_PEAK_GBPS * 1e9)
+    hbm = {"achieved": byts / (us * 1e-6) / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+           "frac": byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS}
+    r = {"kernel": kernel, "traffic": traffic, "alg_bytes_per_launch": byts, "us_per_launch": us}
+    if flops is not None:
+        fl, ty = flops
+        peak = MFMA_PEAK[ty]
+        t_mfma = fl / (peak * 1e12)
+        mfma = {"achieved": fl / (us * 1e-6) / 1e12, "peak": peak, "unit": "TFLOP/s" if ty != "i8" else "TOP/s",
+                "frac": fl / (us * 1e-6) / 1e12 / peak, "operands": ty}
+        r["alg_flops_per_launch"] = fl
+        r["hbm"] = hbm
+        r["mfma"] = mfma
+        if t_mfma > t_hbm:
+            return {"bound": "mfma", **{k: mfma[k] for k in ("achieved", "peak", "unit", "frac")}, **r}
+    return {"bound": "hbm", **{k: hbm[k] for k in ("achieved", "peak", "unit", "frac")}, **r}
+
+
 def source_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "rank_kv_cache_starkv_amd", "csrc")
@@ -451,9 +495,9 @@ def measure(w, args, dev, with_cpu: bool, steps: int, warmup: int) -> dict:
         traffic = None
     else:
         dom = max((k for k in kern_us if k.startswith("decode_")), key=lambda k: kern_us[k])
-        achieved = ab[dom] / (kern_us[dom] * 1e-6) / 1e9
         # counters cover the q path of unrotated layers only
         traffic = None if args.hidden_query or args.rope or args.lens_dev else traffic_for(dom, w.name)
+        fls = algorithmic_flops(w, probe.ranks, probe.r_v, lens, n_q)
     dec_us = sum(us for k, us in kern_us.items() if k.startswith("decode_"))
     res = {
         "value": w.B * n_q / (ms_step * 1e-3),
@@ -471,9 +515,7 @@ def measure(w, args, dev, with_cpu: bool, steps: int, warmup: int) -> dict:
         "roofline": ({"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": 2500.0, "unit": "TFLOP/s",
                       "frac": achieved / 2500.0, "traffic": None, "alg_flops_per_launch": ab[dom],
                       "us_per_launch": kern_us[dom]} if recon else
-                     {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-                      "alg_bytes_per_launch": ab[dom], "us_per_launch": kern_us[dom]}),
+                     roofline_of(dom, kern_us[dom], ab[dom], fls.get(dom), traffic)),
         "ms_per_step_eager": ms_step_eager,
         "host_issue_us_per_step": host_us,
         "step_hbm_gbps": ab["step"] / (ms_step * 1e-3) / 1e9,
@@ -777,8 +819,9 @@ def main() -> int:
                              "ms_per_step_eager": sr["ms_per_step_eager"],
                              "host_issue_us_per_step": sr["host_issue_us_per_step"],
                              "kv_tokens_per_s": sr["kv_tokens_per_s"], "step_frac": sr["step_frac"],
-                             "roofline": {k: sr["roofline"][k] for k in ("kernel", "achieved", "frac", "traffic",
-                                                                          "us_per_launch")},
+                             "roofline": {k: sr["roofline"][k] for k in ("bound", "kernel", "achieved", "unit", "frac",
+                                                                          "traffic", "us_per_launch", "hbm", "mfma")
+                                          if k in sr["roofline"]},
                              "kernel_us": sr["kernel_us"], "config": sr["config"]}
         result["sub_results"] = subs
     print(json.dumps(result))
