@@ -1350,6 +1350,202 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   vm_wait<0>();  // the trailing loads (at kOOB) have returned before the wave ends
 }
 
+// Key scores of int8/int4 latents with the chunk's key rows staged in LDS once per workgroup.
+// Workgroup = block of nch_wg consecutive 32-token chunks (global numbering, possibly spanning
+// sequences) x every column tile: wave w takes column tile w (nct waves).  The 32 key rows of a
+// chunk are one contiguous span of the cache (32 k_row_bytes bytes); the waves copy it into a
+// ring of NST LDS stages by 16-byte DMA (wave w issues the span's 1 KiB pieces w, w + nct, ...,
+// DPW of them, the surplus repeating the last piece), NST - 1 chunks ahead of use, with one
+// barrier per chunk.  Each wave then reads its K-tiles of the 32 rows from LDS (an int8 lane 16
+// bytes, an int4 lane its exact 8 bytes) and runs the MFMAs, softmax statistics and stores of
+// k_scores_mix.  Every key byte of a chunk crosses from L2 once per workgroup, where the
+// per-column-tile kernel fetched each row's K-tiles once per column tile (whole 64-position
+// K-tiles around each tile's few heads: about three times the key bytes on the 13B-class step).
+constexpr int kScoresLdsStages = 4;
+template <int KTM, int DPW>
+__global__ __launch_bounds__(640) void k_scores_lds(ScoreArgs a) {
+  constexpr int NST = kScoresLdsStages;
+  constexpr int NSTORE = 4;  // vector memory stores per computed chunk (p~ twice, m, l)
+  extern __shared__ __align__(16) uint8_t stg_raw[];
+  const DecodeGeom& g = a.g;
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int NW = g.nct;
+  const int n = lane & 15, qq = lane >> 4;
+  const int c_first = blockIdx.x * a.nch_wg;
+  const int c_end = min(c_first + a.nch_wg, a.total_chunks);
+  if (c_first >= c_end) return;  // whole workgroup
+  const uint32_t rb = (uint32_t)g.k_row_bytes;
+  const uint32_t span = 32u * rb;
+  const int npc = (int)((span + 1023u) >> 10);  // 1 KiB pieces of a chunk's rows
+  const uint32_t sbytes = (uint32_t)npc << 10;  // bytes of one stage
+  const int ct = wave;
+
+  // this lane's DMA: piece j of the wave is span piece min(wave + NW j, npc - 1); lane bytes past
+  // the span reload its last 16 bytes (they land past the rows in the stage and are never read)
+  uint32_t dsrc[DPW], ddst[DPW];
+#pragma unroll
+  for (int j = 0; j < DPW; ++j) {
+    const int pc = min(wave + NW * j, npc - 1);
+    dsrc[j] = min(((uint32_t)pc << 10) + 16u * lane, span - 16u);
+    ddst[j] = (uint32_t)pc << 10;
+  }
+
+  // K-tiles of the column tile: per-lane byte offset in a key row of the lane's 16 int8 codes or
+  // 8 bytes of 16 int4 codes (padding lanes: offset 0; they meet a zero query fragment)
+  const int nkt = a.kts.n[ct];
+  const int ks0 = a.kts.s0[ct], kn0 = a.kts.n0[ct], ks1 = a.kts.s1[ct];
+  uint32_t kofs[KTM];
+  bool k8[KTM];
+#pragma unroll
+  for (int jt = 0; jt < KTM; ++jt) {
+    const int kt = jt < kn0 ? ks0 + jt : ks1 + (jt - kn0);
+    const int P0 = kt * 64 + 16 * qq;
+    const bool on = jt < nkt;
+    k8[jt] = on && P0 < g.K8;
+    const bool i4 = on && P0 >= g.K8 && P0 < g.K8 + g.K4;
+    kofs[jt] = k8[jt] ? (uint32_t)P0 : (i4 ? (uint32_t)(g.K8 + (P0 - g.K8) / 2) : 0u);
+  }
+  const int i = ct * 16 + n;
+  const bool rowvalid = i < g.M_q;
+  const bool tile_full = (ct + 1) * 16 <= g.M_q;
+  const int jq = i % g.n_q;
+
+  // issue side: chunk ci of sequence bi
+  int ci = c_first;
+  int bi = seq_of_chunk(a.seq, g.B, c_first);
+  int bi0 = seq_chunk0(a.seq, bi), bi_end = seq_chunk0(a.seq, bi + 1);
+  const uint32_t ring0 = lds_addr(stg_raw);
+  const uint8_t* last_base = a.k_rows + ((size_t)bi * g.T_max + (size_t)(ci - bi0) * kTC) * rb;
+  auto issue = [&](int st) {
+    if (ci < c_end) {  // wave-uniform
+      while (ci >= bi_end) {
+        ++bi;
+        bi0 = bi_end;
+        bi_end = seq_chunk0(a.seq, bi + 1);
+      }
+      last_base = a.k_rows + ((size_t)bi * g.T_max + (size_t)(ci - bi0) * kTC) * rb;
+    }
+    // (past the block's last chunk: the last chunk's rows again, never read)
+#pragma unroll
+    for (int j = 0; j < DPW; ++j) lds_dma16(last_base + dsrc[j], ring0 + (uint32_t)st * sbytes + ddst[j]);
+    ++ci;
+  };
+
+  // query fragments and row parameters of sequence bb
+  i32x4 fh[KTM], fl[KTM];
+  float rs = 0.f;
+  int ibias = 0;
+  auto load_seq = [&](int bb) {
+    const uint8_t* fbase = a.qfrag + ((size_t)bb * g.nct + ct) * a.nkt_max * 2048;
+#pragma unroll
+    for (int jt = 0; jt < KTM; ++jt) {
+      const int jc = jt < nkt ? jt : 0;
+      fh[jt] = __builtin_bit_cast(i32x4, ld16(fbase + jc * 2048 + lane * 16));
+      fl[jt] = __builtin_bit_cast(i32x4, ld16(fbase + jc * 2048 + 1024 + lane * 16));
+    }
+    const u32x4 rp = ld16(a.rowp + ((size_t)bb * g.M_pad + min(i, g.M_q - 1)) * 4);
+    rs = __uint_as_float(rp[0]) * (1.f / 254.f);
+    ibias = 254 * (int)__uint_as_float(rp[1]) + (int)__uint_as_float(rp[2]);
+  };
+
+  int bc = seq_of_chunk(a.seq, g.B, c_first), bf = -1;
+  int bc0 = seq_chunk0(a.seq, bc), bc_end = seq_chunk0(a.seq, bc + 1), bc_len = seq_len(a.seq, bc);
+
+#pragma unroll
+  for (int u = 0; u < NST - 1; ++u) issue(u);
+  for (int cc = c_first; cc < c_end; ++cc) {
+    const int k = cc - c_first;
+    // this wave's pieces of chunk cc are in, and after the barrier every wave's.  In issue order
+    // (the compiler barriers keep it) each iteration issues its DMA pieces, then the stores of
+    // its chunk (none for a skipped chunk; fragment loads at a sequence start only add to what
+    // follows), so after chunk cc's pieces came at most (NST - 2) DPW pieces and (NST - 1)
+    // NSTORE stores.
+    vm_wait<(NST - 2) * DPW + (NST - 1) * NSTORE>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    issue((k + NST - 1) % NST);  // into the stage chunk cc - 1 used
+    asm volatile("" ::: "memory");
+    while (cc >= bc_end) {
+      ++bc;
+      bc0 = bc_end;
+      bc_end = seq_chunk0(a.seq, bc + 1);
+      bc_len = seq_len(a.seq, bc);
+    }
+    const int t0 = (cc - bc0) * kTC;
+    if (ct >= NW || t0 >= bc_len) continue;  // past a device length: no value split reads this chunk
+    if (bc != bf) {  // first chunk of a sequence in this block: its fragments
+      bf = bc;
+      load_seq(bc);
+    }
+    const uint8_t* st = stg_raw + (size_t)(k % NST) * sbytes;
+    i32x4 ah[2], al[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      ah[tt] = i32x4{0, 0, 0, 0};
+      al[tt] = i32x4{-ibias, -ibias, -ibias, -ibias};
+    }
+#pragma unroll
+    for (int jt = 0; jt < KTM; ++jt) {
+      if (jt < nkt) {  // wave-uniform
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          // 16 bytes at the lane's offset (an int4 lane uses the first 8; the stage has 16
+          // bytes of slack past its last row)
+          const uint8_t* src = st + (uint32_t)(16 * tt + n) * rb + kofs[jt];
+          const u32x2 lo = *(const u32x2*)src;
+          const u32x2 hi = *(const u32x2*)(src + 8);
+          const i32x4 av = k8[jt] ? i32x4{(int)lo[0], (int)lo[1], (int)hi[0], (int)hi[1]} : unpack_int4_group(lo);
+          ah[tt] = mfma16_i8(av, fh[jt], ah[tt]);
+          al[tt] = mfma16_i8(av, fl[jt], al[tt]);
+        }
+      }
+    }
+    float s2[2][4];
+    float m = -INFINITY;
+    if (tile_full && t0 + kTC - 1 <= bc_len - g.n_q) {  // wave-uniform: every row sees every token
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          s2[tt][v] = rs * (float)(254 * ah[tt][v] + al[tt][v]);
+          m = fmaxf(m, s2[tt][v]);
+        }
+    } else {
+      const int lim = rowvalid ? bc_len - g.n_q + jq : -1;  // last token this row sees
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int t = t0 + tt * 16 + 4 * qq + v;
+          s2[tt][v] = t <= lim ? rs * (float)(254 * ah[tt][v] + al[tt][v]) : -INFINITY;
+          m = fmaxf(m, s2[tt][v]);
+        }
+    }
+    m = wave_max_xor(m, 16);
+    m = wave_max_xor(m, 32);
+    const float mref = m == -INFINITY ? 0.f : m;
+    float l = 0.f;
+    const size_t prow = ((size_t)cc * g.M_pad + i) * kTC;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      float e4[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        e4[v] = __builtin_amdgcn_exp2f(s2[tt][v] - mref);
+        l += e4[v];
+      }
+      const uint32_t w0 = (uint32_t)f32_to_f16(e4[0]) | ((uint32_t)f32_to_f16(e4[1]) << 16);
+      const uint32_t w1 = (uint32_t)f32_to_f16(e4[2]) | ((uint32_t)f32_to_f16(e4[3]) << 16);
+      st8((uint16_t*)a.p + prow + tt * 16 + 4 * qq, u32x2{w0, w1});
+    }
+    l = wave_sum_xor(l, 16);
+    l = wave_sum_xor(l, 32);
+    a.cm[(size_t)cc * g.M_pad + i] = m;
+    a.cl[(size_t)cc * g.M_pad + i] = l;
+  }
+  vm_wait<0>();  // the trailing DMA of the ring has landed before the workgroup ends
+}
+
 // Key scores of a rotary layer (keys rotated by position after the key projection): the rotation
 // does not commute with B_g, so each key tile is rebuilt from the latent before the dot product
 // (STAR-KV summary page, Problem Statement: the reconstruction cost; Methodology section 2: the
@@ -3316,6 +3512,32 @@ static hipError_t launch_decode_tail(const Layer& L, const DecodePlan& plan, con
                                      void* out, const void* k_rows, const void* v_tiles, hipStream_t s,
                                      bool scores = true);
 
+// k_scores_lds: DMA pieces per wave per chunk (one of the instantiated counts, at least the
+// chunk's 1 KiB pieces over the nct waves), or 0 when the kernel does not apply (three stages of
+// a chunk's key rows must fit in LDS)
+constexpr int kScoresLdsWgPerCu = 1;
+static int scores_lds_dpw(const DecodeGeom& g) {
+  const int npc = ceil_div(32 * g.k_row_bytes, 1024);
+  if (kScoresLdsStages * (long)npc * 1024 + 16 > 160 * 1024) return 0;
+  const int need = ceil_div(npc, g.nct);
+  for (int d : {2, 3, 4, 6, 8})
+    if (need <= d) return d;
+  return 0;
+}
+
+template <int KTM>
+static hipError_t launch_scores_lds(const ProfScope& ps, int dpw, dim3 grid, dim3 block, size_t lds, hipStream_t s,
+                                    const ScoreArgs& sa) {
+  void* argv[] = {(void*)&sa};
+  const void* k = dpw == 2 ? (const void*)k_scores_lds<KTM, 2>
+                  : dpw == 3 ? (const void*)k_scores_lds<KTM, 3>
+                  : dpw == 4 ? (const void*)k_scores_lds<KTM, 4>
+                  : dpw == 6 ? (const void*)k_scores_lds<KTM, 6>
+                             : (const void*)k_scores_lds<KTM, 8>;
+  if (ps.start() && ps.stop()) return hipExtLaunchKernel(k, grid, block, argv, lds, s, ps.start(), ps.stop(), 0);
+  return hipLaunchKernel(k, grid, block, argv, lds, s);
+}
+
 template <int NT>
 static hipError_t launch_scores_rope(const Layer& L, const ProfScope& ps, dim3 grid, size_t lds, hipStream_t s,
                                      const RopeScoreArgs& ra, bool qc) {
@@ -3487,6 +3709,16 @@ static hipError_t launch_decode_tail(const Layer& L, const DecodePlan& plan, con
         const int n_wg = ceil_div(w.total_chunks, sa.nch_wg);
         if (w.nkt_max <= 6) e = launch_k(ps, k_scores_chunk<STARKV_LATENT_MIX84, 4, true>, dim3(n_wg), dim3(256), s, sa);
         else e = launch_k(ps, k_scores_chunk<STARKV_LATENT_MIX84, 2, true>, dim3(n_wg), dim3(256), s, sa);
+      } else if (g.nct >= 4 && g.nct <= 10 && w.nkt_max <= 8 && scores_lds_dpw(g) > 0) {
+        // many column tiles: each chunk's key rows staged in LDS once, one wave per column tile
+        const int dpw = scores_lds_dpw(g);
+        const int npc = ceil_div(32 * g.k_row_bytes, 1024);
+        const size_t lds = kScoresLdsStages * (size_t)npc * 1024 + 16;
+        sa.nch_wg = std::max(1, ceil_div(w.total_chunks, 256 * kScoresLdsWgPerCu));
+        const dim3 grid(ceil_div(w.total_chunks, sa.nch_wg)), block(64 * g.nct);
+        if (w.nkt_max <= 4) e = launch_scores_lds<4>(ps, dpw, grid, block, lds, s, sa);
+        else if (w.nkt_max <= 6) e = launch_scores_lds<6>(ps, dpw, grid, block, lds, s, sa);
+        else e = launch_scores_lds<8>(ps, dpw, grid, block, lds, s, sa);
       } else if (g.nct >= 4 && w.nkt_max <= 8) {
         // many column tiles: column-tile state in registers while walking blocks of chunks
         sa.nch_wg = 32;  // chunks per block (16 waves' worth of column tiles x 16 chunks each)
