@@ -1453,14 +1453,25 @@ __global__ __launch_bounds__(640) void k_scores_lds(ScoreArgs a) {
 
 #pragma unroll
   for (int u = 0; u < NST - 1; ++u) issue(u);
+  // The wait for chunk cc counts what this wave issued after chunk cc's pieces (the vector
+  // memory counter drains in issue order, and the compiler barriers keep that order): the pieces
+  // of the next NST - 2 chunks ((NST - 2) DPW, in the prologue too) and the stores of the last
+  // NST - 1 iterations (NSTORE for each that computed its chunk, none for a skipped chunk or
+  // before the first iteration; fragment loads at a sequence start come on top, which only makes
+  // the wait stricter).
+  uint32_t hist = 0;  // bit j: iteration k - 1 - j computed its chunk
   for (int cc = c_first; cc < c_end; ++cc) {
     const int k = cc - c_first;
-    // this wave's pieces of chunk cc are in, and after the barrier every wave's.  In issue order
-    // (the compiler barriers keep it) each iteration issues its DMA pieces, then the stores of
-    // its chunk (none for a skipped chunk; fragment loads at a sequence start only add to what
-    // follows), so after chunk cc's pieces came at most (NST - 2) DPW pieces and (NST - 1)
-    // NSTORE stores.
-    vm_wait<(NST - 2) * DPW + (NST - 1) * NSTORE>();
+    asm volatile("" ::: "memory");
+    switch (__builtin_popcount(hist & ((1u << (NST - 1)) - 1u))) {  // wave-uniform
+      case 0: vm_wait<(NST - 2) * DPW>(); break;
+      case 1: vm_wait<(NST - 2) * DPW + NSTORE>(); break;
+      case 2: vm_wait<(NST - 2) * DPW + 2 * NSTORE>(); break;
+      case 3: vm_wait<(NST - 2) * DPW + 3 * NSTORE>(); break;
+      case 4: vm_wait<(NST - 2) * DPW + 4 * NSTORE>(); break;
+      default: vm_wait<(NST - 2) * DPW + 5 * NSTORE>(); break;
+    }
+    hist <<= 1;
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     issue((k + NST - 1) % NST);  // into the stage chunk cc - 1 used
@@ -1473,6 +1484,7 @@ __global__ __launch_bounds__(640) void k_scores_lds(ScoreArgs a) {
     }
     const int t0 = (cc - bc0) * kTC;
     if (ct >= NW || t0 >= bc_len) continue;  // past a device length: no value split reads this chunk
+    hist |= 1u;
     if (bc != bf) {  // first chunk of a sequence in this block: its fragments
       bf = bc;
       load_seq(bc);
