@@ -29,12 +29,6 @@ namespace skv {
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 static int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-static int env_int(const char* name, int dflt) {
-  const char* v = getenv(name);
-  if (!v || !*v) return dflt;
-  return atoi(v);
-}
-
 // Value splits of a ragged batch in XCD order.  The value workgroups go to the eight XCDs in turn
 // by grid position, and each XCD runs its share on its own 32 CUs, so an order that ignores the
 // split lengths can leave one XCD with far more work than another.  Deal the splits (cps chunks
@@ -180,17 +174,14 @@ int plan_decode(const Layer& L, int B, int n_q, const int32_t* lens, int T_max, 
 
   // chunks and splits
   const int NB = L.v_rows / 32;
-  int bpw = NB >= 16 ? 4 : (NB >= 8 ? 2 : 1);
-  bpw = env_int("STARKV_BPW", bpw);
-  if (bpw < 1 || bpw > 4) bpw = 4;
+  const int bpw = NB >= 16 ? 4 : (NB >= 8 ? 2 : 1);
   int n_slices = ceil_div(NB, bpw);
   DecodeWs& w = P->ws;
   // one-M-tile value kernel: slices of up to nbw8 one-N-tile blocks and nbw4 int4 blocks
   {
     // int8 blocks are half the bytes of bf16 ones: bigger slices (measured on MI355X)
-    const int v8 = env_int("STARKV_NBW8", L.mix() ? 4 : 2), v4 = env_int("STARKV_NBW4", 2);
-    w.nbw8 = v8 >= 4 ? 4 : (v8 >= 2 ? 2 : 1);
-    w.nbw4 = v4 >= 2 ? 2 : 1;
+    w.nbw8 = L.mix() ? 4 : 2;
+    w.nbw4 = 2;
   }
   const int nb8 = L.mix() ? L.V8 / 32 : NB;
   w.n_sl8 = ceil_div(nb8, w.nbw8);
@@ -215,7 +206,7 @@ int plan_decode(const Layer& L, int B, int n_q, const int32_t* lens, int T_max, 
     max_chunks = std::max(max_chunks, nc);
   }
   // splits: aim at ~512 value workgroups (two per CU), at least 8 tiles (two per wave) per split
-  const int target_wg = env_int("STARKV_VALUE_WGS", 512);
+  const int target_wg = 512;
   int cps = std::max(8, ceil_div(total_chunks, std::max(1, target_wg / n_slices)));
   cps = std::max(cps, ceil_div(max_chunks, kMaxSplitsPerSeq));
   // at most 4 splits per sequence while that keeps >= 256 value workgroups: longer-lived
@@ -227,8 +218,7 @@ int plan_decode(const Layer& L, int B, int n_q, const int32_t* lens, int T_max, 
   bool uniform = true;
   for (int b = 1; b < B; ++b)
     if (lens[b] != lens[0]) uniform = false;
-  const bool ordered = !uniform && !(g.M_pad > 32 && L.latent == STARKV_LATENT_F32) &&
-                       env_int("STARKV_VORDER", 1) != 0;
+  const bool ordered = !uniform && !(g.M_pad > 32 && L.latent == STARKV_LATENT_F32);
   int cps_lo = std::max(8, ceil_div(max_chunks, kMaxSplitsPerSeq));
   if (B * 4 * n_slices >= 256) cps_lo = std::max(cps_lo, ceil_div(max_chunks, 4));
   bool have_order = false;
@@ -246,8 +236,6 @@ int plan_decode(const Layer& L, int B, int n_q, const int32_t* lens, int T_max, 
       if (c >= max_chunks) break;
     }
   }
-  const int cps_env = env_int("STARKV_CPS", 0);
-  if (cps_env > 0) cps = std::max(cps_env, ceil_div(max_chunks, kMaxSplitsPerSeq));
   P->vo.n = 0;
   if (ordered && order_splits(*seq, B, cps, n_slices, &P->vo) < 0) P->vo.n = 0;
   int total_splits = 0;
@@ -3474,10 +3462,12 @@ static int qproj_row_groups(const DecodeGeom& g) {
 }
 
 // rows per workgroup of the query-projection launch: the rows of one KV head in one sequence, split
-// in row groups while there are few KV heads x sequences.  (Workgroups of 16 rows from four
-// sequences, a quarter as many, were slower on MI355X: 34 against 24 us on the 13B-class ragged
-// step, since a thread's dot products run one after another.)
+// in row groups while there are few KV heads x sequences.  With 2048 or more (KV head, sequence)
+// pairs a workgroup takes the rows of two sequences: half as many workgroups, each running the
+// same chain of dependent steps over twice the dot products (13B-class ragged step: 25.5 ->
+// 21.8 us on MI355X; the rows of four sequences per workgroup, 32.8 us).
 static int qproj_rows_per_wg(const DecodeGeom& g) {
+  if (qproj_row_groups(g) == 1 && g.H_kv * g.B >= 2048) return 2 * g.G * g.n_q;
   return ceil_div(g.G * g.n_q, qproj_row_groups(g));
 }
 
