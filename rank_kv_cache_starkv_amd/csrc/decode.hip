@@ -1398,10 +1398,10 @@ __global__ __launch_bounds__(640) void k_scores_lds(ScoreArgs a) {
   const bool tile_full = (ct + 1) * 16 <= g.M_q;
   const int jq = i % g.n_q;
 
-  // issue side: chunk ci of sequence bi
+  // issue side: chunk ci of sequence bi (of length bi_len)
   int ci = c_first;
   int bi = seq_of_chunk(a.seq, g.B, c_first);
-  int bi0 = seq_chunk0(a.seq, bi), bi_end = seq_chunk0(a.seq, bi + 1);
+  int bi0 = seq_chunk0(a.seq, bi), bi_end = seq_chunk0(a.seq, bi + 1), bi_len = seq_len(a.seq, bi);
   const uint32_t ring0 = lds_addr(stg_raw);
   const uint8_t* last_base = a.k_rows + ((size_t)bi * g.T_max + (size_t)(ci - bi0) * kTC) * rb;
   auto issue = [&](int st) {
@@ -1410,10 +1410,12 @@ __global__ __launch_bounds__(640) void k_scores_lds(ScoreArgs a) {
         ++bi;
         bi0 = bi_end;
         bi_end = seq_chunk0(a.seq, bi + 1);
+        bi_len = seq_len(a.seq, bi);
       }
-      last_base = a.k_rows + ((size_t)bi * g.T_max + (size_t)(ci - bi0) * kTC) * rb;
+      if ((ci - bi0) * kTC < bi_len) last_base = a.k_rows + ((size_t)bi * g.T_max + (size_t)(ci - bi0) * kTC) * rb;
     }
-    // (past the block's last chunk: the last chunk's rows again, never read)
+    // (a chunk past a device length, or past the block's last chunk: the rows of the last live
+    // chunk again, from L2, never read; the stage still takes DPW pieces, as the waits count)
 #pragma unroll
     for (int j = 0; j < DPW; ++j) lds_dma16(last_base + dsrc[j], ring0 + (uint32_t)st * sbytes + ddst[j]);
     ++ci;
